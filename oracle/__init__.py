@@ -1,0 +1,152 @@
+"""CPU oracle of one HAM layer (fp64, token-serial).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path (the
+HIP library and its Python binding) never imports, loads or calls anything here,
+and nothing here imports the product package.
+
+The arithmetic lives in ``ham_oracle.c`` (plain C, double precision); this module
+only compiles it with gcc, converts arrays to float64 and splits independent
+heads over threads.  Source of the method: "Hybrid Associative Memories"
+(arXiv 2603.22325, full-text page) -- §2 for the KV memory, DeltaNet update,
+routing score and gated mix; App. A.1 for the state orientation, the fit-error
+router, masking by original position and generation.
+
+Every function here is pinned by tests/test_oracle_pins.py against closed forms,
+invariants, textbook linear algebra and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ham_oracle.c")
+_LIB = os.path.join(_HERE, "libham_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build() -> str:
+    """Compile ham_oracle.c with gcc (no fast-math: IEEE double throughout)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", _LIB, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.ham_oracle_forward.restype = ctypes.c_int
+        lib.ham_oracle_forward.argtypes = (
+            [ctypes.c_int] * 5 + [ctypes.c_double] * 2 + [P] * 3 + [P] * 3 + [P] * 3
+            + [P] * 2 + [P] * 2 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
+            + [ctypes.c_int, ctypes.c_int])
+        _lib = lib
+        return lib
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
+            v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, S0=None,
+            cache=None, cap=None, t0=0, threads=None):
+    """Run the oracle over all heads.
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
+    S0: [B,H,dk,dv] or None (zeros).  cache: None or dict(Kc, Vc, pos, count) of an
+    existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
+    absolute position of token 0.  Returns a dict of float64 / int arrays:
+    e, routed, o_rnn, o_kv, o, S, Kc, Vc, pos, count.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    beta, g = _f64(beta), _f64(g)
+    qa, ka, va = _f64(q_attn), _f64(k_attn), _f64(v_attn)
+    gr, gk = _f64(gate_rnn), _f64(gate_kv)
+    tau = np.ascontiguousarray(np.asarray(tau, dtype=np.float32).reshape(H))
+    mo = None if mask_override is None else np.ascontiguousarray(
+        np.asarray(mask_override).astype(np.int8))
+    t0a = np.ascontiguousarray(np.broadcast_to(np.asarray(t0, dtype=np.int64), (B,)))
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    S = np.ascontiguousarray(S)
+    if cache is None:
+        cap = T if cap is None else cap
+        Kc = np.zeros((B, H, cap, dk))
+        Vc = np.zeros((B, H, cap, dv))
+        pos = np.full((B, H, cap), -1, dtype=np.int64)
+        count = np.zeros((B, H), dtype=np.int64)
+    else:
+        Kc = np.array(cache["Kc"], dtype=np.float64, copy=True)
+        Vc = np.array(cache["Vc"], dtype=np.float64, copy=True)
+        pos = np.array(cache["pos"], dtype=np.int64, copy=True)
+        count = np.array(cache["count"], dtype=np.int64, copy=True)
+        cap = Kc.shape[2]
+    Kc, Vc, pos, count = (np.ascontiguousarray(a) for a in (Kc, Vc, pos, count))
+    e = np.zeros((B, T, H))
+    routed = np.zeros((B, T, H), dtype=np.int8)
+    o_rnn = np.zeros((B, T, H, dv))
+    o_kv = np.zeros((B, T, H, dv))
+    o = np.zeros((B, T, H, dv))
+
+    lib = _load()
+    nheads = B * H
+    nthr = max(1, min(threads or default_threads(), nheads))
+    bounds = [nheads * i // nthr for i in range(nthr + 1)]
+
+    def run(i):
+        return lib.ham_oracle_forward(
+            B, T, H, dk, dv, float(scale), float(eps),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
+            _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(t0a),
+            _ptr(S), cap, _ptr(Kc), _ptr(Vc), _ptr(pos), _ptr(count),
+            _ptr(e), _ptr(routed), _ptr(o_rnn), _ptr(o_kv), _ptr(o),
+            bounds[i], bounds[i + 1])
+
+    if nthr == 1:
+        rcs = [run(0)]
+    else:
+        with ThreadPoolExecutor(nthr) as ex:
+            rcs = list(ex.map(run, range(nthr)))
+    if any(rc != 0 for rc in rcs):
+        raise RuntimeError("oracle: KV cache capacity exceeded")
+    return dict(e=e, routed=routed, o_rnn=o_rnn, o_kv=o_kv, o=o, S=S, Kc=Kc, Vc=Vc,
+                pos=pos, count=count)
+
+
+def route_stats(out, tau, near_band=1e-5):
+    """Counts, KV usage rho and near-threshold counts from an oracle result.
+
+    rho = sum of routed counts / (B*T*H) ([HAM] §5, KV-usage definition restricted
+    to one layer); n_near[h] = number of tokens of head h with |e - tau_h| < near_band.
+    """
+    e = out["e"]
+    B, T, H = e.shape
+    routed = out["routed"].astype(np.int64)
+    count = routed.sum(axis=1)                      # [B,H]
+    rho = float(count.sum()) / float(B * T * H)
+    tau = np.asarray(tau, dtype=np.float64).reshape(1, 1, H)
+    n_near = (np.abs(e - tau) < near_band).sum(axis=(0, 1))
+    return dict(count=count, rho=rho, n_near=n_near)

@@ -1,0 +1,209 @@
+/*
+ * ham_oracle.c -- plain, slow, token-serial CPU oracle of one HAM layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it.  It shares no code, header or constant with the HIP library.
+ *
+ * Source: "Hybrid Associative Memories" (Lufkin, Figliolia, Millidge,
+ * Krishnamurthy; arXiv 2603.22325, full-text page), cited below as [HAM].
+ *
+ * Everything is double precision.  The caller passes the exact input values
+ * (bf16 inputs are widened exactly).  Each (b,h) head is independent and is
+ * processed strictly in token order; the caller may split the head range over
+ * threads.  No blocking, chunking or reordering beyond the definitions.
+ *
+ * Per head, with the state S stored d_k x d_v ([HAM] App. A.1, "RNN Memory"):
+ *
+ *   alpha_t = exp(g_t)                                  (g_t <= 0 is the log decay)
+ *   p_t     = S_{t-1}^T k_t                             prediction of v_t
+ *             ([HAM] App. A.1 "Router Implementations", fit-error router)
+ *   e_t     = 1 - cos(p_t, v_t)   (cos := 0 if either vector is zero)
+ *             ([HAM] §2 "Prediction Error as Routing Metric")
+ *   routed  = float(e_t) > tau_h   (strict; NaN never routes)
+ *   S_t     = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *             ([HAM] §2 DeltaNet update, one gradient step on 1/2|S k - v|^2,
+ *              with the gated-DeltaNet decay on the whole old state, App. A.1)
+ *   o_rnn_t = S_t^T q_t                                 (post-update readout, [HAM] §2
+ *                                                       linear-attention equation)
+ *   if routed: append (k^a_t, v^a_t, position) to this head's cache
+ *   o_kv_t  = softmax over the cached keys, scale * q^a_t . k_c, of the cached
+ *             values; 0 when the cache is empty           ([HAM] §2 KV-memory
+ *             equation; causality by original position, App. A.1 "FlexAttention
+ *             and Block Masks")
+ *   o_t     = gr_t * rms(o_rnn_t) + gk_t * rms(o_kv_t),  rms(x) = x / sqrt(mean(x^2)+eps)
+ *             ([HAM] §2 headwise norm and gated sum; App. A.1 headwise gating)
+ *
+ * Parity pins for every function here live in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* cosine of two vectors; 0 when either has zero norm.  [HAM] §2 routing score. */
+static double cosine(const double *a, const double *b, int n)
+{
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (int i = 0; i < n; ++i) {
+        ab += a[i] * b[i];
+        aa += a[i] * a[i];
+        bb += b[i] * b[i];
+    }
+    if (aa == 0.0 || bb == 0.0)
+        return 0.0;
+    double c = ab / (sqrt(aa) * sqrt(bb));
+    if (c > 1.0) c = 1.0;
+    if (c < -1.0) c = -1.0;
+    return c;
+}
+
+/* x / sqrt(mean(x^2) + eps), written to y.  [HAM] §2 Norm_h of each readout. */
+static void rms_normalize(const double *x, double *y, int n, double eps)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int i = 0; i < n; ++i)
+        y[i] = x[i] * inv;
+}
+
+/*
+ * One HAM layer over heads [head_begin, head_end) of the flattened B x H grid
+ * (head index = b*H + h), for T new tokens.
+ *
+ * Layouts (row-major): token tensors [B,T,H,d]; per-token scalars [B,T,H];
+ * state S [B,H,dk,dv] (read as the entering state, overwritten with S_T);
+ * cache Kc [B,H,cap,dk], Vc [B,H,cap,dv], pos [B,H,cap], count [B,H]
+ * (read as the entering cache, extended in place).  t0[b] is the absolute
+ * position of token 0 of sequence b.  qa/ka/va: separate attention-path
+ * inputs, or NULL to share q/k/v ([HAM] §2 implementation details: shared
+ * projections).  gate_rnn/gate_kv: NULL means 1.  mask_override: NULL, or a
+ * [B,T,H] array of 0/1 that replaces the threshold decision (the score e is
+ * still computed).  Outputs e, routed, o_rnn, o_kv, o may each be NULL.
+ *
+ * Returns 0, or -3 if a routed token finds the cache full (the head stops there).
+ */
+int ham_oracle_forward(int B, int T, int H, int dk, int dv,
+                       double scale, double eps,
+                       const double *q, const double *k, const double *v,
+                       const double *qa, const double *ka, const double *va,
+                       const double *beta, const double *g, const float *tau,
+                       const double *gate_rnn, const double *gate_kv,
+                       const int8_t *mask_override, const int64_t *t0,
+                       double *S, int cap, double *Kc, double *Vc,
+                       int64_t *pos, int64_t *count,
+                       double *e, int8_t *routed,
+                       double *o_rnn, double *o_kv, double *o,
+                       int head_begin, int head_end)
+{
+    const double *qA = qa ? qa : q;
+    const double *kA = ka ? ka : k;
+    const double *vA = va ? va : v;
+    double *p = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *orn = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *okv = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *tmp1 = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *tmp2 = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *w = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    int status = 0;
+
+    for (int bh = head_begin; bh < head_end; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double *Sh = S + (size_t)bh * dk * dv;
+        double *Kh = Kc + (size_t)bh * cap * dk;
+        double *Vh = Vc + (size_t)bh * cap * dv;
+        int64_t *ph = pos + (size_t)bh * cap;
+        int64_t n = count[bh];
+
+        for (int t = 0; t < T; ++t) {
+            const size_t tok = ((size_t)b * T + t) * H + h;   /* [B,T,H] index */
+            const double *kt = k + tok * dk, *vt = v + tok * dv, *qt = q + tok * dk;
+            const double alpha = exp(g[tok]);
+            const double bt = beta[tok];
+
+            /* prediction p = S_{t-1}^T k_t */
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    acc += Sh[(size_t)i * dv + j] * kt[i];
+                p[j] = acc;
+            }
+            /* routing score and decision (decision taken in fp32, like the GPU) */
+            const double et = 1.0 - cosine(p, vt, dv);
+            int r;
+            if (mask_override)
+                r = mask_override[tok] != 0;
+            else
+                r = ((float)et > tau[h]);
+            if (e) e[tok] = et;
+            if (routed) routed[tok] = (int8_t)r;
+
+            /* gated delta update: S = alpha*S + beta*k*(v - alpha*p)^T
+             * which equals alpha*(I - beta k k^T) S + beta k v^T. */
+            for (int i = 0; i < dk; ++i) {
+                const double bk = bt * kt[i];
+                for (int j = 0; j < dv; ++j)
+                    Sh[(size_t)i * dv + j] = alpha * Sh[(size_t)i * dv + j]
+                                           + bk * (vt[j] - alpha * p[j]);
+            }
+            /* post-update readout o_rnn = S_t^T q_t */
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    acc += Sh[(size_t)i * dv + j] * qt[i];
+                orn[j] = acc;
+            }
+
+            /* append the routed token, ascending original position */
+            if (r) {
+                if (n >= cap) { status = -3; break; }
+                memcpy(Kh + (size_t)n * dk, kA + tok * dk, sizeof(double) * (size_t)dk);
+                memcpy(Vh + (size_t)n * dv, vA + tok * dv, sizeof(double) * (size_t)dv);
+                ph[n] = t0[b] + t;
+                n += 1;
+            }
+
+            /* softmax attention over the cached (routed) keys, all at positions <= t */
+            const double *qat = qA + tok * dk;
+            for (int j = 0; j < dv; ++j) okv[j] = 0.0;
+            if (n > 0) {
+                double m = -INFINITY;
+                for (int64_t c = 0; c < n; ++c) {
+                    double s = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        s += qat[i] * Kh[(size_t)c * dk + i];
+                    w[c] = scale * s;
+                    if (w[c] > m) m = w[c];
+                }
+                double den = 0.0;
+                for (int64_t c = 0; c < n; ++c) {
+                    w[c] = exp(w[c] - m);
+                    den += w[c];
+                }
+                for (int64_t c = 0; c < n; ++c) {
+                    const double wc = w[c] / den;
+                    for (int j = 0; j < dv; ++j)
+                        okv[j] += wc * Vh[(size_t)c * dv + j];
+                }
+            }
+
+            /* headwise RMS norms and the two independent gates */
+            const double gr = gate_rnn ? gate_rnn[tok] : 1.0;
+            const double gk = gate_kv ? gate_kv[tok] : 1.0;
+            rms_normalize(orn, tmp1, dv, eps);
+            rms_normalize(okv, tmp2, dv, eps);
+            for (int j = 0; j < dv; ++j) {
+                if (o_rnn) o_rnn[tok * dv + j] = orn[j];
+                if (o_kv) o_kv[tok * dv + j] = okv[j];
+                if (o) o[tok * dv + j] = gr * tmp1[j] + gk * tmp2[j];
+            }
+        }
+        count[bh] = n;
+        if (status) break;
+    }
+    free(p); free(orn); free(okv); free(tmp1); free(tmp2); free(w);
+    return status;
+}
