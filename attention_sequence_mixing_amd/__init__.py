@@ -1,0 +1,244 @@
+"""HAM (Hybrid Associative Memory) sequence mixer on AMD MI355X.
+
+Python binding of the C ABI in include/ham.h.  This module only marshals
+arguments: it checks shapes and dtypes of torch tensors, allocates outputs and
+scratch with torch (device memory plumbing), and passes raw device pointers and
+the current HIP stream to libham.so.  Every step of the layer runs in the HIP
+kernels of that library; if it is missing, the calls raise.
+
+Method: "Hybrid Associative Memories" (arXiv 2603.22325), §2 and App. A.1.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (HAM_BF16, HAM_CONTINUE, HAM_F32, HAM_FORCE_RECURRENT, HamDims, HamError,
+                   check)
+
+__all__ = ["ham_forward", "ham_decode_step", "ham_route_stats", "ForwardPlan", "DecodePlan",
+           "HamError", "HAM_CONTINUE", "HAM_FORCE_RECURRENT", "library_path"]
+
+library_path = _lib.LIB_PATH
+
+
+def _vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io_code(dtype):
+    if dtype == torch.float32:
+        return HAM_F32
+    if dtype == torch.bfloat16:
+        return HAM_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(name, t, shape, dtype, device):
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0):
+    return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0)
+
+
+class ForwardPlan:
+    """Outputs and scratch for repeated ham_forward calls of one shape.
+
+    Allocation happens once here; each call only enqueues the kernels.
+    """
+
+    def __init__(self, B, T, H, dk, dv, dtype, device, *, cap=None, scale=None,
+                 norm_eps=1e-6, flags=0, t0=0, want_o_rnn=False, want_o_kv=False):
+        device = torch.device(device)
+        self.io = _io_code(dtype)
+        self.dtype, self.device = dtype, device
+        self.cap = T if cap is None else cap
+        self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
+        self.dims = make_dims(B, T, H, dk, dv, self.io, self.scale, norm_eps, self.cap, flags, t0)
+        self.shape = (B, T, H, dk, dv)
+        L = _lib.lib()
+        ws_bytes = L.ham_forward_workspace_size(ctypes.byref(self.dims))
+        if ws_bytes == 0:
+            raise HamError(-1, L.ham_last_error().decode())
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.o = torch.empty((B, T, H, dv), dtype=dtype, device=device)
+        self.o_rnn = torch.empty((B, T, H, dv), dtype=dtype, device=device) if want_o_rnn else None
+        self.o_kv = torch.empty((B, T, H, dv), dtype=dtype, device=device) if want_o_kv else None
+        self.e = torch.empty((B, T, H), dtype=torch.float32, device=device)
+        self.routed = torch.empty((B, T, H), dtype=torch.uint8, device=device)
+        self.S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+        self.Kc = torch.zeros((B, H, self.cap, dk), dtype=dtype, device=device)
+        self.Vc = torch.zeros((B, H, self.cap, dv), dtype=dtype, device=device)
+        self.pos = torch.full((B, H, self.cap), -1, dtype=torch.int32, device=device)
+        self.count = torch.zeros((B, H), dtype=torch.int32, device=device)
+
+    def __call__(self, q, k, v, beta, g, tau, *, q_attn=None, k_attn=None, v_attn=None,
+                 gate_rnn=None, gate_kv=None, S0=None, stream=None):
+        B, T, H, dk, dv = self.shape
+        dev, dt = self.device, self.dtype
+        for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
+            _need(n, t, (B, T, H, dk), dt, dev)
+        for n, t in (("v", v), ("v_attn", v_attn)):
+            _need(n, t, (B, T, H, dv), dt, dev)
+        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
+            _need(n, t, (B, T, H), torch.float32, dev)
+        _need("tau", tau, (H,), torch.float32, dev)
+        _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
+        if q is None or k is None or v is None or beta is None or g is None or tau is None:
+            raise ValueError("q, k, v, beta, g and tau are required")
+        rc = _lib.lib().ham_forward(
+            ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
+            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S0), _vp(self.S),
+            _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv), _vp(self.e), _vp(self.routed),
+            _vp(self.Kc), _vp(self.Vc), _vp(self.pos), _vp(self.count),
+            _vp(self.ws), self.ws.numel(), _stream(stream))
+        check(rc)
+        return self
+
+    def result(self):
+        return dict(o=self.o, o_rnn=self.o_rnn, o_kv=self.o_kv, e=self.e, routed=self.routed,
+                    S=self.S, Kc=self.Kc, Vc=self.Vc, pos=self.pos, count=self.count)
+
+
+def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
+                k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
+                t0=0, force_recurrent=False, want_o_rnn=False, want_o_kv=False, stream=None):
+    """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
+
+    cache: None, or dict(Kc, Vc, pos, count) of an earlier call to continue; it
+    is then extended in place and S0 should be that call's state.  Returns a dict
+    with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if asked).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    flags = (HAM_FORCE_RECURRENT if force_recurrent else 0) | (HAM_CONTINUE if cache is not None else 0)
+    if cache is not None:
+        cap = cache["Kc"].shape[2]
+    plan = ForwardPlan(B, T, H, dk, dv, q.dtype, q.device, cap=cap, scale=scale,
+                       norm_eps=norm_eps, flags=flags, t0=t0, want_o_rnn=want_o_rnn,
+                       want_o_kv=want_o_kv)
+    if cache is not None:
+        plan.Kc = _need("Kc", cache["Kc"], (B, H, plan.cap, dk), q.dtype, q.device)
+        plan.Vc = _need("Vc", cache["Vc"], (B, H, plan.cap, dv), q.dtype, q.device)
+        plan.pos = _need("pos", cache["pos"], (B, H, plan.cap), torch.int32, q.device)
+        plan.count = _need("count", cache["count"], (B, H), torch.int32, q.device)
+    plan(q, k, v, beta, g, tau, q_attn=q_attn, k_attn=k_attn, v_attn=v_attn,
+         gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, stream=stream)
+    return plan.result()
+
+
+class DecodePlan:
+    """Scratch and outputs for repeated ham_decode_step calls on one cache."""
+
+    def __init__(self, B, H, dk, dv, cap, dtype, device, *, scale=None, norm_eps=1e-6,
+                 want_o_rnn=False, want_o_kv=False):
+        device = torch.device(device)
+        self.io = _io_code(dtype)
+        self.dtype, self.device = dtype, device
+        self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
+        self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap)
+        self.shape = (B, H, dk, dv, cap)
+        L = _lib.lib()
+        ws_bytes = L.ham_decode_workspace_size(ctypes.byref(self.dims))
+        if ws_bytes == 0:
+            raise HamError(-1, L.ham_last_error().decode())
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.o = torch.empty((B, H, dv), dtype=dtype, device=device)
+        self.o_rnn = torch.empty((B, H, dv), dtype=dtype, device=device) if want_o_rnn else None
+        self.o_kv = torch.empty((B, H, dv), dtype=dtype, device=device) if want_o_kv else None
+        self.e = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.routed = torch.empty((B, H), dtype=torch.uint8, device=device)
+        self.status = torch.zeros((1,), dtype=torch.int32, device=device)
+
+    def __call__(self, q, k, v, beta, g, tau, S, Kc, Vc, pos, count, t_abs, *, q_attn=None,
+                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, stream=None):
+        B, H, dk, dv, cap = self.shape
+        dev, dt = self.device, self.dtype
+        for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
+            _need(n, t, (B, H, dk), dt, dev)
+        for n, t in (("v", v), ("v_attn", v_attn)):
+            _need(n, t, (B, H, dv), dt, dev)
+        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
+            _need(n, t, (B, H), torch.float32, dev)
+        _need("tau", tau, (H,), torch.float32, dev)
+        _need("S", S, (B, H, dk, dv), torch.float32, dev)
+        _need("Kc", Kc, (B, H, cap, dk), dt, dev)
+        _need("Vc", Vc, (B, H, cap, dv), dt, dev)
+        _need("pos", pos, (B, H, cap), torch.int32, dev)
+        _need("count", count, (B, H), torch.int32, dev)
+        _need("t_abs", t_abs, (B,), torch.int32, dev)
+        rc = _lib.lib().ham_decode_step(
+            ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
+            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S), _vp(Kc), _vp(Vc),
+            _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
+            _vp(self.e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
+            _stream(stream))
+        check(rc)
+        return self
+
+
+def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_eps=1e-6,
+                    q_attn=None, k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None,
+                    want_o_rnn=False, want_o_kv=False, stream=None):
+    """One decode step: q, k, v [B,H,d]; S and cache (dict Kc, Vc, pos, count) are
+    updated in place; t_abs [B] int32 positions.  Returns dict(o, e, routed, status, ...)."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    cap = cache["Kc"].shape[2]
+    plan = DecodePlan(B, H, dk, dv, cap, q.dtype, q.device, scale=scale, norm_eps=norm_eps,
+                      want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
+    plan(q, k, v, beta, g, tau, S, cache["Kc"], cache["Vc"], cache["pos"], cache["count"], t_abs,
+         q_attn=q_attn, k_attn=k_attn, v_attn=v_attn, gate_rnn=gate_rnn, gate_kv=gate_kv,
+         stream=stream)
+    return dict(o=plan.o, o_rnn=plan.o_rnn, o_kv=plan.o_kv, e=plan.e, routed=plan.routed,
+                status=plan.status)
+
+
+def ham_route_stats(k, v, beta, g, tau, *, q=None, S0=None, near_band=1e-5, want_rho=True,
+                    force_recurrent=False, stream=None):
+    """Routing only (RNN scores, threshold, counts).  Returns dict(e, routed, count,
+    n_near, rho); rho is None unless want_rho (which waits for the stream)."""
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    io = _io_code(dt)
+    _need("v", v, (B, T, H, dv), dt, dev)
+    _need("beta", beta, (B, T, H), torch.float32, dev)
+    _need("g", g, (B, T, H), torch.float32, dev)
+    _need("tau", tau, (H,), torch.float32, dev)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    dims = make_dims(B, T, H, dk, dv, io, 1.0, 1e-6, max(T, 1),
+                     HAM_FORCE_RECURRENT if force_recurrent else 0)
+    L = _lib.lib()
+    ws_bytes = L.ham_route_stats_workspace_size(ctypes.byref(dims))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    e = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    routed = torch.empty((B, T, H), dtype=torch.uint8, device=dev)
+    count = torch.empty((B, H), dtype=torch.int32, device=dev)
+    n_near = torch.empty((H,), dtype=torch.int64, device=dev)
+    rho = ctypes.c_double(float("nan"))
+    rc = L.ham_route_stats(ctypes.byref(dims), _vp(q), _vp(k), _vp(v), _vp(beta), _vp(g), _vp(tau),
+                           _vp(S0), _vp(e), _vp(routed), _vp(count), _vp(n_near),
+                           ctypes.c_float(near_band), ctypes.byref(rho) if want_rho else None,
+                           _vp(ws), ws.numel(), _stream(stream))
+    check(rc)
+    return dict(e=e, routed=routed, count=count, n_near=n_near, rho=rho.value if want_rho else None)

@@ -1,0 +1,363 @@
+// ham_api.cpp -- the C ABI declared in include/ham.h: argument checks, scratch
+// layout and the kernel sequence of each entry point.  Every launch goes to the
+// caller's stream; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ham.h"
+#include "ham_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_dims(const ham_dims* d, bool need_T) {
+  if (!d) return fail(HAM_EINVAL, "dims is NULL");
+  if (d->B <= 0 || d->H <= 0 || (need_T && d->T <= 0))
+    return fail(HAM_EINVAL, "B, T and H must be positive (B=%d T=%d H=%d)", d->B, d->T, d->H);
+  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
+    return fail(HAM_EUNSUPPORTED, "dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
+  if (d->io_dtype != HAM_F32 && d->io_dtype != HAM_BF16)
+    return fail(HAM_EUNSUPPORTED, "io_dtype must be HAM_F32 or HAM_BF16 (got %d)", d->io_dtype);
+  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT))
+    return fail(HAM_EUNSUPPORTED, "unknown flag bits 0x%x", d->flags);
+  if (d->cap <= 0) return fail(HAM_EINVAL, "cap must be positive (cap=%d)", d->cap);
+  if (!std::isfinite(d->scale)) return fail(HAM_EINVAL, "scale must be finite");
+  if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(HAM_EINVAL, "norm_eps must be finite and >= 0");
+  if (d->t0 < 0) return fail(HAM_EINVAL, "t0 must be >= 0");
+  const double elems = (double)d->B * (need_T ? d->T : 1) * d->H * (d->dk > d->dv ? d->dk : d->dv);
+  if (elems > 9.0e15) return fail(HAM_EINVAL, "problem too large");
+  return HAM_OK;
+}
+
+#define HAM_REQUIRE(p) \
+  do { if (!(p)) return fail(HAM_EINVAL, "required pointer %s is NULL", #p); } while (0)
+#define HAM_ALIGNED(p) \
+  do { if (!aligned16(p)) return fail(HAM_EINVAL, "pointer %s is not 16-byte aligned", #p); } while (0)
+#define HAM_HIP(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(HAM_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
+struct FwdLayout {
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, total;
+};
+
+FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
+  const size_t BTH = (size_t)d->B * d->T * d->H, BH = (size_t)d->B * d->H;
+  const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
+  FwdLayout L{};
+  size_t off = 0;
+  L.o_rnn32 = off;     off += up256(BTH * d->dv * sizeof(float));
+  L.score = off;       off += up256(BTH * ham::kScoreSlicesMax * sizeof(float4));
+  L.e = off;           off += up256(BTH * sizeof(float));
+  L.routed = off;      off += up256(BTH);
+  L.chunk_count = off; off += up256(BH * nchunk * sizeof(int32_t));
+  L.count_in = off;    off += up256(BH * sizeof(int32_t));
+  L.ntok = off;        off += up256(BTH * sizeof(int32_t));
+  L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
+  L.total = off;
+  return L;
+}
+
+struct DecLayout {
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, total;
+  int nseg;
+};
+
+DecLayout dec_layout(const ham_dims* d) {
+  const size_t BH = (size_t)d->B * d->H;
+  DecLayout L{};
+  L.nseg = (d->cap + ham::kDecodeSeg - 1) / ham::kDecodeSeg;
+  size_t off = 0;
+  L.o_rnn32 = off;     off += up256(BH * d->dv * sizeof(float));
+  L.score = off;       off += up256(BH * ham::kScoreSlicesMax * sizeof(float4));
+  L.e = off;           off += up256(BH * sizeof(float));
+  L.routed = off;      off += up256(BH);
+  L.chunk_count = off; off += up256(BH * sizeof(int32_t));
+  L.count_in = off;    off += up256(BH * sizeof(int32_t));
+  L.part = off;        off += up256(BH * (size_t)L.nseg * (d->dv + 2) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// ---- stage timing (ham_profile_*) ------------------------------------------------
+struct Profiler {
+  std::mutex mu;
+  bool armed = false;
+  int max_calls = 0, used = 0;
+  std::vector<hipEvent_t> ev;      // max_calls x (HAM_PROFILE_STAGES + 1)
+  std::vector<int> kinds, nstage;
+};
+Profiler g_prof;
+
+// One call's recorder: claims a slot when armed; mark() records after a stage.
+struct CallTimer {
+  int slot = -1, stage = 0;
+  hipStream_t s;
+  CallTimer(int kind, hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (!g_prof.armed || g_prof.used >= g_prof.max_calls) return;
+    slot = g_prof.used++;
+    g_prof.kinds[slot] = kind;
+    (void)hipEventRecord(g_prof.ev[(size_t)slot * (HAM_PROFILE_STAGES + 1)], s);
+  }
+  void mark() {
+    if (slot < 0 || stage >= HAM_PROFILE_STAGES) return;
+    ++stage;
+    (void)hipEventRecord(g_prof.ev[(size_t)slot * (HAM_PROFILE_STAGES + 1) + stage], s);
+    g_prof.nstage[slot] = stage;
+  }
+};
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// The RNN pass shared by ham_forward and ham_route_stats; returns the slice count.
+int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slices, CallTimer& tm) {
+  const bool chunked = !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
+                       ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv);
+  if (chunked) {
+    *slices = ham::rnn_chunked_slices(d->dv);
+    HAM_HIP(ham::launch_rnn_chunked(d->io_dtype, d->dk, d->dv, ra, s));
+  } else {
+    *slices = ham::rnn_recurrent_slices(d->dv);
+    HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
+  }
+  tm.mark();
+  return HAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ham_version(void) { return 10000; }
+
+const char* ham_last_error(void) { return g_err.c_str(); }
+
+size_t ham_forward_workspace_size(const ham_dims* d) {
+  if (check_dims(d, true) != HAM_OK) return 0;
+  return fwd_layout(d, false).total;
+}
+
+size_t ham_route_stats_workspace_size(const ham_dims* d) {
+  if (check_dims(d, true) != HAM_OK) return 0;
+  return fwd_layout(d, true).total;
+}
+
+size_t ham_decode_workspace_size(const ham_dims* d) {
+  if (check_dims(d, false) != HAM_OK) return 0;
+  return dec_layout(d).total;
+}
+
+int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
+                const void* q_attn, const void* k_attn, const void* v_attn,
+                const float* beta, const float* g, const float* tau,
+                const float* gate_rnn, const float* gate_kv,
+                const float* S0, float* S_out, void* o, void* o_rnn, void* o_kv,
+                float* e, uint8_t* routed, void* Kc, void* Vc, int32_t* pos, int32_t* count,
+                void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != HAM_OK) return rc;
+  HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g);
+  HAM_REQUIRE(tau); HAM_REQUIRE(S_out); HAM_REQUIRE(o); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc);
+  HAM_REQUIRE(pos); HAM_REQUIRE(count);
+  HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
+  HAM_ALIGNED(v_attn); HAM_ALIGNED(S0); HAM_ALIGNED(S_out); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn);
+  HAM_ALIGNED(o_kv); HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
+  if (!(d->flags & HAM_CONTINUE) && d->cap < d->T)
+    return fail(HAM_ECAPACITY, "cap (%d) < T (%d): the cache cannot hold every token", d->cap, d->T);
+  const FwdLayout L = fwd_layout(d, false);
+  if (!ws || ws_bytes < L.total)
+    return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float* o_rnn32 = at<float>(ws, L.o_rnn32);
+  float4* score = at<float4>(ws, L.score);
+  float* e_buf = e ? e : at<float>(ws, L.e);
+  uint8_t* r_buf = routed ? routed : at<uint8_t>(ws, L.routed);
+  int32_t* chunk_count = at<int32_t>(ws, L.chunk_count);
+  int32_t* count_in = at<int32_t>(ws, L.count_in);
+  int32_t* ntok = at<int32_t>(ws, L.ntok);
+
+  CallTimer tm(0, s);
+  ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, d->B, d->T, d->H};
+  int slices = 0;
+  rc = run_rnn(d, ra, s, &slices, tm);
+  if (rc != HAM_OK) return rc;
+
+  ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count,
+                    (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H};
+  HAM_HIP(ham::launch_route(ro, s));
+  tm.mark();
+
+  ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
+                      Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap};
+  HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
+  tm.mark();
+
+  ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
+                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap};
+  HAM_HIP(ham::launch_attention(d->io_dtype, d->dk, d->dv, aa, s));
+  tm.mark();
+  return HAM_OK;
+}
+
+int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void* v,
+                    const void* q_attn, const void* k_attn, const void* v_attn,
+                    const float* beta, const float* g, const float* tau,
+                    const float* gate_rnn, const float* gate_kv,
+                    float* S, void* Kc, void* Vc, int32_t* pos, int32_t* count,
+                    const int32_t* t_abs, void* o, void* o_rnn, void* o_kv,
+                    float* e, uint8_t* routed, int32_t* status,
+                    void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc != HAM_OK) return rc;
+  HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g);
+  HAM_REQUIRE(tau); HAM_REQUIRE(S); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos);
+  HAM_REQUIRE(count); HAM_REQUIRE(t_abs); HAM_REQUIRE(o);
+  HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
+  HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
+  HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
+  const DecLayout L = dec_layout(d);
+  if (!ws || ws_bytes < L.total)
+    return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float* o_rnn32 = at<float>(ws, L.o_rnn32);
+  float4* score = at<float4>(ws, L.score);
+  float* e_buf = e ? e : at<float>(ws, L.e);
+  uint8_t* r_buf = routed ? routed : at<uint8_t>(ws, L.routed);
+  int32_t* chunk_count = at<int32_t>(ws, L.chunk_count);
+  int32_t* count_in = at<int32_t>(ws, L.count_in);
+  float* part = at<float>(ws, L.part);
+
+  CallTimer tm(1, s);
+  ham::RnnArgs ra{q, k, v, beta, g, S, S, o_rnn32, score, d->B, 1, d->H};
+  HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
+  tm.mark();
+  ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, e_buf, r_buf, chunk_count,
+                    count, count_in, d->B, 1, d->H};
+  HAM_HIP(ham::launch_route(ro, s));
+  tm.mark();
+  ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
+                      Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap};
+  HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
+  tm.mark();
+  ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
+                         ham::kDecodeSeg, L.nseg};
+  HAM_HIP(ham::launch_decode_attn(d->io_dtype, d->dk, d->dv, da, s));
+  tm.mark();
+  ham::DecodeCombineArgs cb{part, count, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps,
+                            d->B, d->H, ham::kDecodeSeg, L.nseg};
+  HAM_HIP(ham::launch_decode_combine(d->io_dtype, d->dv, cb, s));
+  tm.mark();
+  return HAM_OK;
+}
+
+int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void* v,
+                    const float* beta, const float* g, const float* tau, const float* S0,
+                    float* e, uint8_t* routed, int32_t* count, int64_t* n_near, float near_band,
+                    double* rho_host, void* ws, size_t ws_bytes, void* stream) {
+  (void)q;
+  int rc = check_dims(d, true);
+  if (rc != HAM_OK) return rc;
+  HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g); HAM_REQUIRE(tau);
+  HAM_REQUIRE(count);
+  HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(S0); HAM_ALIGNED(ws);
+  if (n_near && !(near_band >= 0.f)) return fail(HAM_EINVAL, "near_band must be >= 0");
+  const FwdLayout L = fwd_layout(d, true);
+  if (!ws || ws_bytes < L.total)
+    return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float4* score = at<float4>(ws, L.score);
+  float* e_buf = e ? e : at<float>(ws, L.e);
+  uint8_t* r_buf = routed ? routed : at<uint8_t>(ws, L.routed);
+  int32_t* chunk_count = at<int32_t>(ws, L.chunk_count);
+  int32_t* count_in = at<int32_t>(ws, L.count_in);
+  float* S_tmp = at<float>(ws, L.state);
+
+  CallTimer tm(2, s);
+  ham::RnnArgs ra{q ? q : k, k, v, beta, g, S0, S_tmp, nullptr, score, d->B, d->T, d->H};
+  int slices = 0;
+  rc = run_rnn(d, ra, s, &slices, tm);
+  if (rc != HAM_OK) return rc;
+  ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count, nullptr, count_in,
+                    d->B, d->T, d->H};
+  HAM_HIP(ham::launch_route(ro, s));
+  tm.mark();
+  ham::StatsArgs sa{e_buf, tau, chunk_count, count, n_near, near_band, d->B, d->T, d->H};
+  HAM_HIP(ham::launch_stats(sa, s));
+  tm.mark();
+  if (rho_host) {
+    std::vector<int32_t> c((size_t)d->B * d->H);
+    HAM_HIP(hipMemcpyAsync(c.data(), count, c.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HAM_HIP(hipStreamSynchronize(s));
+    double tot = 0;
+    for (int32_t x : c) tot += x;
+    *rho_host = tot / ((double)d->B * d->T * d->H);
+  }
+  return HAM_OK;
+}
+
+int ham_profile_start(int max_calls) {
+  if (max_calls <= 0 || max_calls > (1 << 20)) return fail(HAM_EINVAL, "max_calls out of range");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign((size_t)max_calls * (HAM_PROFILE_STAGES + 1), nullptr);
+  for (auto& e : g_prof.ev) HAM_HIP(hipEventCreate(&e));
+  g_prof.kinds.assign(max_calls, -1);
+  g_prof.nstage.assign(max_calls, 0);
+  g_prof.max_calls = max_calls;
+  g_prof.used = 0;
+  g_prof.armed = true;
+  return HAM_OK;
+}
+
+int ham_profile_stop(float* stage_ms, int max_values, int* n_calls, int* kinds) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.armed) return fail(HAM_EINVAL, "profiling is not armed");
+  g_prof.armed = false;
+  const int used = g_prof.used;
+  if (n_calls) *n_calls = used;
+  for (int c = 0; c < used; ++c) {
+    if (kinds) kinds[c] = g_prof.kinds[c];
+    const size_t base = (size_t)c * (HAM_PROFILE_STAGES + 1);
+    const int ns = g_prof.nstage[c];
+    if (ns > 0) HAM_HIP(hipEventSynchronize(g_prof.ev[base + ns]));
+    for (int st = 0; st < HAM_PROFILE_STAGES; ++st) {
+      const long idx = (long)c * HAM_PROFILE_STAGES + st;
+      if (!stage_ms || idx >= max_values) continue;
+      float ms = 0.f;
+      if (st < ns) HAM_HIP(hipEventElapsedTime(&ms, g_prof.ev[base + st], g_prof.ev[base + st + 1]));
+      stage_ms[idx] = ms;
+    }
+  }
+  return HAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,304 @@
+// ham_attn.hip -- causal softmax attention over the compacted KV cache, with the
+// headwise-norm gated mix fused into the epilogue.
+//
+// "Hybrid Associative Memories": softmax retrieval over the stored pairs (§2
+// KV-memory equation), restricted to routed tokens; a query at original position
+// t sees cached keys at original positions <= t (App. A.1 "FlexAttention and
+// Block Masks": causality by original position, padding excluded).  Because the
+// cache is in ascending original position, that set is the prefix c < n_t of the
+// cache, with n_t the number of cached tokens at positions <= t (n_t includes t
+// itself when t is routed).  Mix: o = g_rnn*rms(o_rnn) + g_kv*rms(o_kv) (§2
+// headwise norm and gated sum; App. A.1 headwise gating).
+//
+// One workgroup = 64 queries of one (b,h), 4 waves x 16 queries.  Each wave
+// computes S^T = K Q^T on 16x16 MFMA tiles (keys on rows), so the per-query
+// softmax state lives in the lanes that later hold that query's output column of
+// O^T = V^T P^T: no data movement between the two products.  bf16 uses
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; fp32 uses v_mfma_f32_16x16x4f32.
+#include "ham_common.h"
+#include "ham_internal.h"
+
+namespace ham {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <class IO>
+struct AttnTile;
+template <>
+struct AttnTile<IoBF16> { static constexpr int BN = 64; };
+template <>
+struct AttnTile<IoF32> { static constexpr int BN = 32; };
+
+template <class IO, int DK, int DV>
+struct AttnSmem;
+template <int DK, int DV>
+struct AttnSmem<IoBF16, DK, DV> {
+  static constexpr int BN = 64;
+  static constexpr int KS = DK + 8;   // K row stride (elements), padded
+  static constexpr int VS = BN + 8;   // V^T row stride (elements), padded
+  uint16_t K[BN * KS];
+  uint16_t Vt[DV * VS];
+};
+template <int DK, int DV>
+struct AttnSmem<IoF32, DK, DV> {
+  static constexpr int BN = 32;
+  static constexpr int KS = DK + 4;
+  static constexpr int VS = DV + 4;
+  float K[BN * KS];
+  float V[BN * VS];
+};
+
+// Stage rows [c0, c0+BN) of this head's cache into LDS; rows at or beyond nmax
+// are zero so masked lanes multiply finite values.
+template <int DK, int DV>
+HAM_DEVICE void stage_kv(AttnSmem<IoBF16, DK, DV>& sm, const uint16_t* Kh, const uint16_t* Vh,
+                         int c0, int nmax, int tid) {
+  constexpr int BN = 64, KS = DK + 8, VS = BN + 8;
+  constexpr int KU = DK / 8, VU = DV / 8;
+#pragma unroll
+  for (int u = tid; u < BN * KU; u += 256) {
+    const int row = u / KU, col = (u % KU) * 8;
+    u16x8 x = (u16x8)(0);
+    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Kh + (size_t)(c0 + row) * DK + col);
+    *reinterpret_cast<u16x8*>(&sm.K[row * KS + col]) = x;
+  }
+#pragma unroll
+  for (int u = tid; u < BN * VU; u += 256) {
+    const int row = u / VU, col = (u % VU) * 8;
+    u16x8 x = (u16x8)(0);
+    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Vh + (size_t)(c0 + row) * DV + col);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.Vt[(col + j) * VS + row] = x[j];
+  }
+}
+
+template <int DK, int DV>
+HAM_DEVICE void stage_kv(AttnSmem<IoF32, DK, DV>& sm, const float* Kh, const float* Vh,
+                         int c0, int nmax, int tid) {
+  constexpr int BN = 32, KS = DK + 4, VS = DV + 4;
+  constexpr int KU = DK / 4, VU = DV / 4;
+#pragma unroll
+  for (int u = tid; u < BN * KU; u += 256) {
+    const int row = u / KU, col = (u % KU) * 4;
+    f32x4 x = (f32x4)(0.f);
+    if (c0 + row < nmax) x = *reinterpret_cast<const f32x4*>(Kh + (size_t)(c0 + row) * DK + col);
+    *reinterpret_cast<f32x4*>(&sm.K[row * KS + col]) = x;
+  }
+#pragma unroll
+  for (int u = tid; u < BN * VU; u += 256) {
+    const int row = u / VU, col = (u % VU) * 4;
+    f32x4 x = (f32x4)(0.f);
+    if (c0 + row < nmax) x = *reinterpret_cast<const f32x4*>(Vh + (size_t)(c0 + row) * DV + col);
+    *reinterpret_cast<f32x4*>(&sm.V[row * VS + col]) = x;
+  }
+}
+
+// Query fragments: the B operand of S^T = K Q^T for this lane's query.
+template <int DK>
+struct QFragBF16 { bf16x8 x[DK / 32]; };
+template <int DK>
+struct QFragF32 { float x[DK / 4]; };
+
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  using E = typename IO::elem;
+  constexpr bool kBF16 = (IO::kBytes == 2);
+  constexpr int BN = AttnTile<IO>::BN;
+  constexpr int NT = BN / 16;              // 16-key subtiles per tile
+  constexpr int DT = DV / 16;              // 16-wide d tiles of the output
+  __shared__ AttnSmem<IO, DK, DV> sm;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 4, qn = lane & 15;
+  const int nqb = (a.T + 63) / 64;
+  // longest query blocks first; XCD-aware so one head's blocks share an L2
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqb;
+  const int qb = nqb - 1 - (lin % nqb);
+  const int b = bh / a.H, h = bh % a.H;
+
+  const E* __restrict__ qp = static_cast<const E*>(a.q);
+  const E* __restrict__ Kh = static_cast<const E*>(a.Kc) + (size_t)bh * a.cap * DK;
+  const E* __restrict__ Vh = static_cast<const E*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const int32_t* ntok = a.ntok + (size_t)bh * a.T;
+
+  const int t = qb * 64 + wave * 16 + qn;           // this lane's query
+  const bool tvalid = t < a.T;
+  const int nq = tvalid ? ntok[t] : 0;              // visible keys c < nq
+  const int tlast = min(a.T - 1, qb * 64 + 63);
+  const int nhi = ntok[tlast];                      // keys any query of the block sees
+  const size_t tok = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
+
+  // load this lane's query fragment
+  QFragBF16<DK> qfb;
+  QFragF32<DK> qff;
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      u16x8 x = (u16x8)(0);
+      if (tvalid) x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(qp) + tok * DK + ks * 32 + 8 * g);
+      qfb.x[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < DK / 4; ++ks)
+      qff.x[ks] = tvalid ? reinterpret_cast<const float*>(qp)[tok * DK + ks * 4 + g] : 0.f;
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4)(0.f);
+
+  const int ntiles = (nhi + BN - 1) / BN;
+  for (int it = 0; it < ntiles; ++it) {
+    const int c0 = it * BN;
+    __syncthreads();
+    stage_kv(sm, Kh, Vh, c0, nhi, tid);
+    __syncthreads();
+
+    f32x4 st[NT];
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) {
+      st[kt] = (f32x4)(0.f);
+      if constexpr (kBF16) {
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const u16x8 kx = *reinterpret_cast<const u16x8*>(&sm.K[(kt * 16 + qn) * (DK + 8) + ks * 32 + 8 * g]);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx), qfb.x[ks], st[kt], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DK / 4; ++ks) {
+          const float kx = sm.K[(kt * 16 + qn) * (DK + 4) + ks * 4 + g];
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, qff.x[ks], st[kt], 0, 0, 0);
+        }
+      }
+    }
+    // st[kt][i] = q_t . k_c for c = c0 + kt*16 + 4g + i (this lane's query t)
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cidx = c0 + kt * 16 + 4 * g + i;
+        const float s = (cidx < nq) ? st[kt][i] * sl2 : -INFINITY;
+        st[kt][i] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (st[kt][i] == -INFINITY) ? 0.f : exp2f(st[kt][i] - m_new);
+        st[kt][i] = p;
+        psum += p;
+      }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
+
+    // O^T += V^T P^T
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int u = 0; u < NT / 2; ++u) {
+        u16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = f32_to_bf16(st[2 * u][i]);
+          pb[4 + i] = f32_to_bf16(st[2 * u + 1][i]);
+        }
+        const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vrow = &sm.Vt[(dt * 16 + qn) * (64 + 8)];
+          const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 4 * g);
+          const u16x4 v1 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 16 + 4 * g);
+          u16x8 va;
+          va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+          va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbf, acc[dt], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* vrow = &sm.V[(kt * 16 + 4 * g + i) * (DV + 4)];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[dt * 16 + qn], st[kt][i], acc[dt], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
+  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  // lane holds query t, output dims d = dt*16 + 4g + i
+  float okv[DT][4], orn[DT][4];
+  float ssk = 0.f, ssr = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x4 r4 = (f32x4)(0.f);
+    if (tvalid) r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tok * DV + dt * 16 + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      okv[dt][i] = acc[dt][i] * inv_l;
+      orn[dt][i] = r4[i];
+      ssk += okv[dt][i] * okv[dt][i];
+      ssr += orn[dt][i] * orn[dt][i];
+    }
+  }
+  ssk += __shfl_xor(ssk, 16, kWave);
+  ssk += __shfl_xor(ssk, 32, kWave);
+  ssr += __shfl_xor(ssr, 16, kWave);
+  ssr += __shfl_xor(ssr, 32, kWave);
+  if (!tvalid) return;
+  const size_t tt = ((size_t)b * a.T + t) * a.H + h;
+  const float gr = a.gate_rnn ? a.gate_rnn[tt] : 1.f;
+  const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
+  const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
+  const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
+  E* o = static_cast<E*>(a.o);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
+    const size_t off = tt * DV + dt * 16 + 4 * g;
+    IO::store4(o, off, y);
+    if (a.o_kv) IO::store4(static_cast<E*>(a.o_kv), off, okv[dt]);
+    if (a.o_rnn) IO::store4(static_cast<E*>(a.o_rnn), off, orn[dt]);
+  }
+}
+
+template <class IO, int DK, int DV>
+static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+  const int nqb = (a.T + 63) / 64;
+  hipLaunchKernelGGL((attn_kernel<IO, DK, DV>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s) {
+#define HAM_CASE(IOT, DKV, DVV) \
+  if (dk == DKV && dv == DVV) return launch_attn_t<IOT, DKV, DVV>(a, s);
+  if (io == 0) {
+    HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+  } else {
+    HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+  }
+#undef HAM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ham

@@ -1,0 +1,96 @@
+// ham_common.h -- device helpers shared by the HAM kernels (gfx950 / CDNA4).
+//
+// Wave size is 64.  bf16 values travel as raw uint16 bits; conversions to bf16
+// round to nearest even.  Nothing here is specific to one kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HAM_DEVICE __device__ __forceinline__
+
+namespace ham {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------------
+HAM_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+HAM_DEVICE uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
+  return (uint16_t)(u >> 16);
+}
+
+// ---- element type of q/k/v/cache/outputs ----------------------------------------
+// IoF32: float elements.  IoBF16: bf16 bit patterns (uint16_t).
+struct IoF32 {
+  using elem = float;
+  static constexpr int kBytes = 4;
+  HAM_DEVICE static float load(const elem* p, size_t i) { return p[i]; }
+  HAM_DEVICE static void store(elem* p, size_t i, float x) { p[i] = x; }
+  // 4 consecutive elements (16-byte aligned base + i multiple of 4)
+  HAM_DEVICE static void load4(const elem* p, size_t i, float out[4]) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  }
+  HAM_DEVICE static void store4(elem* p, size_t i, const float x[4]) {
+    f32x4 v; v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    *reinterpret_cast<f32x4*>(p + i) = v;
+  }
+};
+
+struct IoBF16 {
+  using elem = uint16_t;
+  static constexpr int kBytes = 2;
+  HAM_DEVICE static float load(const elem* p, size_t i) { return bf16_to_f32(p[i]); }
+  HAM_DEVICE static void store(elem* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+  HAM_DEVICE static void load4(const elem* p, size_t i, float out[4]) {
+    u16x4 v = *reinterpret_cast<const u16x4*>(p + i);
+    out[0] = bf16_to_f32(v[0]); out[1] = bf16_to_f32(v[1]);
+    out[2] = bf16_to_f32(v[2]); out[3] = bf16_to_f32(v[3]);
+  }
+  HAM_DEVICE static void store4(elem* p, size_t i, const float x[4]) {
+    u16x4 v;
+    v[0] = f32_to_bf16(x[0]); v[1] = f32_to_bf16(x[1]);
+    v[2] = f32_to_bf16(x[2]); v[3] = f32_to_bf16(x[3]);
+    *reinterpret_cast<u16x4*>(p + i) = v;
+  }
+};
+
+// ---- wave-level reductions (xor butterflies over `width` lanes) -----------------
+template <int kWidth>
+HAM_DEVICE float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWidth; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+template <int kWidth>
+HAM_DEVICE float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWidth; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+HAM_DEVICE int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// ---- XCD-aware workgroup order ----------------------------------------------------
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
+// so that each XCD receives a contiguous range of logical ids: neighbouring tiles
+// (for example the query blocks of one head, which share K/V) then meet in the
+// same L2.
+constexpr int kNumXcd = 8;
+HAM_DEVICE int xcd_remap(int hw_id, int n) {
+  int per = n / kNumXcd, rem = n % kNumXcd;
+  int xcd = hw_id % kNumXcd, slot = hw_id / kNumXcd;
+  // XCDs [0, rem) get per+1 ids, the rest get per.
+  int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + slot;
+}
+
+}  // namespace ham

@@ -1,0 +1,122 @@
+// ham_internal.h -- host-side declarations shared by the C ABI and the kernel
+// translation units: argument blocks, workspace layout, launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ham {
+
+// Score partials: every RNN kernel writes, per token and per d_v slice, the
+// three sums (p.v, p.p, v.v) of the prediction p = S_{t-1}^T k_t against v_t.
+// The routing kernel adds the slices and forms the cosine.
+constexpr int kScoreSlicesMax = 8;
+
+struct RnnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const float* S0;      // [B,H,dk,dv] or null (zeros)
+  float* S_out;         // [B,H,dk,dv]
+  float* o_rnn32;       // [B,T,H,dv] fp32 or null (no readout)
+  float4* score;        // [B*H][T][slices]
+  int B, T, H;
+};
+
+struct RouteArgs {
+  const float4* score;  // [B*H][T][slices]
+  int slices;
+  const float* tau;     // [H]
+  float* e;             // [B,T,H]
+  uint8_t* routed;      // [B,T,H]
+  int32_t* chunk_count; // [B*H][nchunk]
+  const int32_t* count; // [B,H] entering count (HAM_CONTINUE) or null
+  int32_t* count_in;    // [B*H] snapshot of the entering count
+  int B, T, H;
+};
+
+struct CompactArgs {
+  const void* k;        // attention-path keys   [B,T,H,dk]
+  const void* v;        // attention-path values [B,T,H,dv]
+  const uint8_t* routed;
+  const int32_t* chunk_count;
+  const int32_t* count_in;
+  void* Kc;             // [B,H,cap,dk]
+  void* Vc;             // [B,H,cap,dv]
+  int32_t* pos;         // [B,H,cap]
+  int32_t* count;       // [B,H] out
+  int32_t* ntok;        // [B*H][T] inclusive visible-key count per token, or null
+  int32_t* status;      // overflow flag or null
+  const int32_t* t_abs; // [B] or null
+  int t0;
+  int B, T, H, cap;
+};
+
+struct StatsArgs {
+  const float* e;
+  const float* tau;
+  const int32_t* chunk_count;
+  int32_t* count;       // [B,H]
+  int64_t* n_near;      // [H] or null
+  float near_band;
+  int B, T, H;
+};
+
+struct AttnArgs {
+  const void* q;        // attention-path queries [B,T,H,dk]
+  const void* Kc;
+  const void* Vc;
+  const int32_t* ntok;  // [B*H][T]
+  const float* o_rnn32; // [B,T,H,dv]
+  const float* gate_rnn;
+  const float* gate_kv;
+  void* o;
+  void* o_rnn;
+  void* o_kv;
+  float scale;
+  float eps;
+  int B, T, H, cap;
+};
+
+struct DecodeAttnArgs {
+  const void* q;        // [B,H,dk]
+  const void* Kc;
+  const void* Vc;
+  const int32_t* count; // [B,H] after the append
+  float* part;          // [B*H][nseg][dv + 2]  (acc..., m, l)
+  float scale;
+  int B, H, cap, seg, nseg;
+};
+
+struct DecodeCombineArgs {
+  const float* part;
+  const int32_t* count;
+  const float* o_rnn32;  // [B,H,dv]
+  const float* gate_rnn;
+  const float* gate_kv;
+  void* o;
+  void* o_rnn;
+  void* o_kv;
+  float eps;
+  int B, H, seg, nseg;
+};
+
+// launchers (return hipGetLastError() of the launch)
+hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
+int rnn_recurrent_slices(int dv);
+hipError_t launch_rnn_chunked(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
+int rnn_chunked_slices(int dv);
+bool rnn_chunked_supported(int io, int dk, int dv);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_compact(int io, int dk, int dv, const CompactArgs& a, hipStream_t s);
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, hipStream_t s);
+hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hipStream_t s);
+
+constexpr int kChunk = 64;         // tokens per routing / compaction chunk
+constexpr int kDecodeSeg = 512;    // keys per split-K segment in decode
+
+}  // namespace ham

@@ -1,0 +1,181 @@
+// ham_route.hip -- routing score, threshold, stream compaction and statistics.
+//
+// "Hybrid Associative Memories": the score e_t = 1 - cos(S_{t-1}^T k_t, v_t)
+// (§2 "Prediction Error as Routing Metric"; App. A.1 fit-error router), the
+// threshold decision (a token enters the KV memory iff its score exceeds tau,
+// App. A.1 "Forward Pass"), the data-dependent KV cache of routed tokens only
+// (§2 KV-memory equation restricted to the routed set; App. A.1 "KV Memory"),
+// and the KV-usage fraction rho (§5).
+//
+// Compaction is deterministic: per 64-token chunk one wave64 ballot gives the
+// chunk's routed count and each token's rank inside the chunk; a chunk's base is
+// the sum of the earlier chunks' counts.  No atomics, so the cache order is the
+// ascending original position on every run.
+#include "ham_common.h"
+#include "ham_internal.h"
+
+namespace ham {
+
+// grid (nchunk, H, B), one wave: lane = token within the chunk.
+__global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
+  const int lane = lane_id();
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.H + h;
+  const int nchunk = gridDim.x;
+  const int t = c * kChunk + lane;
+  const bool valid = t < a.T;
+  bool r = false;
+  if (valid) {
+    const float4* sp = a.score + ((size_t)bh * a.T + t) * a.slices;
+    float pv = 0.f, pp = 0.f, vv = 0.f;
+    for (int s = 0; s < a.slices; ++s) {
+      float4 x = sp[s];
+      pv += x.x; pp += x.y; vv += x.z;
+    }
+    float cs = 0.f;
+    if (pp > 0.f && vv > 0.f) {
+      cs = pv / (sqrtf(pp) * sqrtf(vv));
+      cs = fminf(1.f, fmaxf(-1.f, cs));
+    }
+    const float e = 1.f - cs;
+    r = e > a.tau[h];                 // strict; a NaN score never routes
+    const size_t tok = ((size_t)b * a.T + t) * a.H + h;
+    a.e[tok] = e;
+    a.routed[tok] = (uint8_t)r;
+  }
+  const unsigned long long bal = __ballot(r);
+  if (lane == 0) {
+    a.chunk_count[(size_t)bh * nchunk + c] = __popcll(bal);
+    if (c == 0) a.count_in[bh] = a.count ? a.count[bh] : 0;
+  }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  const int nchunk = (a.T + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(route_kernel, dim3(nchunk, a.H, a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// grid (nchunk, H, B), 256 threads.  Writes the chunk's routed rows to the cache
+// at count_in + base + rank, their positions, the per-token visible-key counts,
+// and (last chunk) the new count.
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
+  using E = typename IO::elem;
+  constexpr int KU = DK * IO::kBytes / 16;    // 16-byte units per key row
+  constexpr int VU = DV * IO::kBytes / 16;
+  __shared__ int s_red[4];
+  __shared__ int s_tok[kChunk];
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.H + h;
+  const int nchunk = gridDim.x;
+
+  int part = 0;
+  for (int i = tid; i < c; i += 256) part += a.chunk_count[(size_t)bh * nchunk + i];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, kWave);
+  if (lane == 0) s_red[wave] = part;
+  __syncthreads();
+  const int base = a.count_in[bh] + s_red[0] + s_red[1] + s_red[2] + s_red[3];
+
+  if (wave == 0) {
+    const int t = c * kChunk + lane;
+    const bool valid = t < a.T;
+    const bool r = valid && a.routed[((size_t)b * a.T + t) * a.H + h];
+    const unsigned long long bal = __ballot(r);
+    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+    if (r) s_tok[rank] = t;
+    if (a.ntok && valid) a.ntok[(size_t)bh * a.T + t] = min(a.cap, base + rank + (int)r);
+    if (lane == 0) s_cnt = __popcll(bal);
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+  const int tpos0 = a.t_abs ? a.t_abs[b] : a.t0;
+
+  const char* kb = static_cast<const char*>(a.k);
+  const char* vb = static_cast<const char*>(a.v);
+  char* Kb = static_cast<char*>(a.Kc);
+  char* Vb = static_cast<char*>(a.Vc);
+  for (int u = tid; u < cnt * (KU + VU); u += 256) {
+    const int i = u / (KU + VU), w = u % (KU + VU);
+    const int slot = base + i;
+    if (slot >= a.cap) continue;
+    const size_t tok = ((size_t)b * a.T + s_tok[i]) * a.H + h;
+    const size_t row = (size_t)bh * a.cap + slot;
+    if (w < KU) {
+      const uint4 x = *reinterpret_cast<const uint4*>(kb + (tok * DK) * IO::kBytes + (size_t)w * 16);
+      *reinterpret_cast<uint4*>(Kb + (row * DK) * IO::kBytes + (size_t)w * 16) = x;
+    } else {
+      const int wv = w - KU;
+      const uint4 x = *reinterpret_cast<const uint4*>(vb + (tok * DV) * IO::kBytes + (size_t)wv * 16);
+      *reinterpret_cast<uint4*>(Vb + (row * DV) * IO::kBytes + (size_t)wv * 16) = x;
+    }
+  }
+  for (int i = tid; i < cnt; i += 256) {
+    const int slot = base + i;
+    if (slot < a.cap) a.pos[(size_t)bh * a.cap + slot] = tpos0 + s_tok[i];
+  }
+  if (tid == 0) {
+    if (base + cnt > a.cap && a.status) *a.status = 1;
+    if (c == nchunk - 1) a.count[bh] = min(a.cap, base + cnt);
+  }
+}
+
+template <class IO, int DK, int DV>
+static hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
+  const int nchunk = (a.T + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL((compact_kernel<IO, DK, DV>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(int io, int dk, int dv, const CompactArgs& a, hipStream_t s) {
+#define HAM_CASE(IOT, DKV, DVV) \
+  if (dk == DKV && dv == DVV) return launch_compact_t<IOT, DKV, DVV>(a, s);
+  if (io == 0) {
+    HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+  } else {
+    HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+  }
+#undef HAM_CASE
+  return hipErrorInvalidValue;
+}
+
+// grid (H), 256 threads: per-head routed counts and near-threshold counts.
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+  __shared__ long long s_red[4];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int h = blockIdx.x;
+  const int nchunk = (a.T + kChunk - 1) / kChunk;
+  for (int b = 0; b < a.B; ++b) {
+    long long part = 0;
+    for (int i = tid; i < nchunk; i += 256) part += a.chunk_count[(size_t)(b * a.H + h) * nchunk + i];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, kWave);
+    if (lane == 0) s_red[wave] = part;
+    __syncthreads();
+    if (tid == 0) a.count[b * a.H + h] = (int32_t)(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    __syncthreads();
+  }
+  if (!a.n_near) return;
+  const float tau = a.tau[h];
+  long long near = 0;
+  const long long n = (long long)a.B * a.T;
+  for (long long i = tid; i < n; i += 256) {
+    const float e = a.e[(size_t)i * a.H + h];
+    near += (fabsf(e - tau) < a.near_band) ? 1 : 0;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) near += __shfl_xor(near, m, kWave);
+  if (lane == 0) s_red[wave] = near;
+  __syncthreads();
+  if (tid == 0) a.n_near[h] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(stats_kernel, dim3(a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ham

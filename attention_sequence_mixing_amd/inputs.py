@@ -3,7 +3,7 @@
 This module holds no arithmetic of the method: it only draws random numbers,
 shapes them like the inputs of one HAM sequence mixer, rounds them to the I/O
 dtype, and picks a routing threshold from a given array of scores.  Both the
-tests (for the oracle and the HIP library alike) and the benchmark use it.
+tests (on both sides of every comparison) and the benchmark use it.
 
 Recipe (every workload): NumPy ``default_rng(seed)`` (PCG64); draws in the
 fixed order q, k, v, beta_raw, g_raw, each in C order ``[B,T,H,d]`` or

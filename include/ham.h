@@ -1,0 +1,205 @@
+/*
+ * ham.h -- C ABI of the HAM (Hybrid Associative Memory) sequence-mixer library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Hybrid Associative Memories" (Lufkin, Figliolia, Millidge,
+ * Krishnamurthy; arXiv 2603.22325), cited as [HAM].  Per (batch b, head h):
+ *
+ *   gated delta-rule RNN ([HAM] §2 DeltaNet update; App. A.1 "RNN Memory"),
+ *   state S in R^{dk x dv}, alpha_t = exp(g_t):
+ *       S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *       o_rnn_t = S_t^T q_t                       (post-update readout)
+ *   routing score ([HAM] §2 "Prediction Error as Routing Metric"; App. A.1
+ *   fit-error router):  e_t = 1 - cos(S_{t-1}^T k_t, v_t)   (cos := 0 for a
+ *   zero vector), token t is routed iff e_t > tau_h (strict, in fp32).
+ *   KV memory of routed tokens only ([HAM] §2 KV-memory equation; App. A.1
+ *   causality by original position): o_kv_t = softmax_c(scale * q_t.Kc[c]) Vc
+ *   over cached entries at original positions <= t; 0 if there are none.
+ *   mix ([HAM] §2 headwise norm and gated sum; App. A.1 headwise gating):
+ *       o_t = gr_t * rms(o_rnn_t) + gk_t * rms(o_kv_t),
+ *       rms(x) = x / sqrt(mean(x^2) + norm_eps).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory.  Scratch memory comes from the
+ *     caller through (ws, ws_bytes), sized by the matching *_workspace_size().
+ *   - Layouts are dense row-major: token tensors [B,T,H,d]; per-token scalars
+ *     [B,T,H] fp32; state [B,H,dk,dv] fp32; KV cache [B,H,cap,d] (io dtype),
+ *     pos [B,H,cap] int32, count [B,H] int32.  Pointers must be 16-byte aligned.
+ *   - io_dtype selects the element type of q, k, v, the attention inputs, the
+ *     cache and the outputs o / o_rnn / o_kv: HAM_F32 (float) or HAM_BF16
+ *     (bfloat16 bits; stores round to nearest even).  beta, g, tau, gates, e and
+ *     the state are always fp32.
+ *   - dk, dv must each be 64 or 128.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work; nothing blocks except ham_route_stats with rho_host != NULL.
+ *   - Return codes: HAM_OK, or a negative HAM_E* code; ham_last_error() then
+ *     returns a thread-local message.  Argument errors are detected on the host
+ *     before anything is enqueued.
+ */
+#ifndef HAM_H
+#define HAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HAM_OK 0
+#define HAM_EINVAL (-1)        /* NULL required pointer, bad size, misalignment */
+#define HAM_EUNSUPPORTED (-2)  /* dk/dv not in {64,128}, unknown dtype or flag */
+#define HAM_ECAPACITY (-3)     /* cap < (tokens already cached) + T */
+#define HAM_EHIP (-4)          /* a HIP launch failed */
+#define HAM_EWORKSPACE (-5)    /* ws NULL or smaller than the *_workspace_size() */
+
+#define HAM_F32 0
+#define HAM_BF16 1
+
+/* flags */
+#define HAM_CONTINUE 1         /* S0 / Kc / Vc / pos / count hold an earlier call's
+                                  state and cache; new entries are appended */
+#define HAM_FORCE_RECURRENT 2  /* run the token-serial RNN kernel even for long T */
+
+typedef struct {
+    int B, T, H;      /* batch, new tokens per sequence, heads                   */
+    int dk, dv;       /* key and value head sizes (64 or 128 each)               */
+    int io_dtype;     /* HAM_F32 or HAM_BF16                                      */
+    float scale;      /* attention logit scale (the usual choice is 1/sqrt(dk))  */
+    float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
+    int cap;          /* KV-cache capacity per (b,h), in tokens                   */
+    int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT                       */
+    int t0;           /* absolute position of token 0 (recorded in pos)          */
+} ham_dims;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int ham_version(void);
+
+/* Thread-local message for the last non-OK return of this thread. */
+const char *ham_last_error(void);
+
+/* Bytes of device scratch ham_forward needs for these dims (0 on bad dims). */
+size_t ham_forward_workspace_size(const ham_dims *dims);
+
+/*
+ * ham_forward -- one HAM layer over T new tokens of B sequences.
+ * [HAM] §2 (all four equations) and App. A.1 (router, masking, generation).
+ *
+ *   q, k, v            [B,T,H,dk|dv] io dtype, required: the RNN inputs.
+ *   q_attn, k_attn, v_attn  attention-path inputs (same shapes), or NULL to
+ *                      share q/k/v (the paper shares the projections).
+ *   beta, g            [B,T,H] fp32, required: write strength and log decay
+ *                      (alpha = exp(g); g must be finite).
+ *   tau                [H] fp32, required: routing threshold per head in e-units
+ *                      (+inf routes nothing: pure gated DeltaNet; -inf routes all).
+ *   gate_rnn, gate_kv  [B,T,H] fp32 or NULL (= 1).
+ *   S0                 [B,H,dk,dv] fp32 entering state, or NULL (= 0).
+ *   S_out              [B,H,dk,dv] fp32, required: state after token T-1.  May
+ *                      alias S0.
+ *   o                  [B,T,H,dv] io dtype, required: mixed output.
+ *   o_rnn, o_kv        [B,T,H,dv] io dtype or NULL: the two readouts before the
+ *                      norms (o_kv = 0 where nothing is visible).
+ *   e                  [B,T,H] fp32 or NULL: routing scores.
+ *   routed             [B,T,H] uint8 or NULL: 1 where routed.
+ *   Kc, Vc, pos, count the per-(b,h) KV cache, required.  Without HAM_CONTINUE
+ *                      count is output only and entries [0,count) are written;
+ *                      with it, count[b,h] (<= cap) entries already exist and
+ *                      new ones are appended.  Entries are in ascending original
+ *                      position; pos holds t0 + t.  Entries >= count are left
+ *                      untouched.
+ *   ws, ws_bytes       device scratch of ham_forward_workspace_size(dims) bytes.
+ * Errors: HAM_EINVAL, HAM_EUNSUPPORTED, HAM_ECAPACITY (cap < T, or with
+ * HAM_CONTINUE cap < T plus the cached tokens -- that part is checked on the
+ * device: appends beyond cap are dropped and count saturates at cap),
+ * HAM_EWORKSPACE, HAM_EHIP.
+ */
+int ham_forward(const ham_dims *dims,
+                const void *q, const void *k, const void *v,
+                const void *q_attn, const void *k_attn, const void *v_attn,
+                const float *beta, const float *g, const float *tau,
+                const float *gate_rnn, const float *gate_kv,
+                const float *S0, float *S_out,
+                void *o, void *o_rnn, void *o_kv,
+                float *e, uint8_t *routed,
+                void *Kc, void *Vc, int32_t *pos, int32_t *count,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of device scratch ham_decode_step needs (dims->T is ignored). */
+size_t ham_decode_workspace_size(const ham_dims *dims);
+
+/*
+ * ham_decode_step -- one new token for each of B sequences ([HAM] App. A.1
+ * "Generation": the state is carried, routed tokens are appended to the cache).
+ * Order within the step: e from S_{t-1}; route; state update; o_rnn; append if
+ * routed; attention over the cache including the new entry; mix.  The result
+ * equals ham_forward over the same token with HAM_CONTINUE.
+ *
+ *   q, k, v (+ optional *_attn)  [B,H,dk|dv] io dtype.
+ *   beta, g, gate_rnn, gate_kv   [B,H] fp32 (gates may be NULL).
+ *   tau                          [H] fp32.
+ *   S                            [B,H,dk,dv] fp32, in/out.
+ *   Kc, Vc, pos, count           cache, in/out (count[b,h] <= cap on entry).
+ *   t_abs                        [B] int32 absolute position of the new token.
+ *   o (required), o_rnn, o_kv    [B,H,dv] io dtype.
+ *   e, routed                    [B,H] or NULL.
+ *   status                       int32 scalar or NULL: set to 1 (never cleared)
+ *                                when a routed token found its cache full; the
+ *                                append is then skipped.
+ */
+int ham_decode_step(const ham_dims *dims,
+                    const void *q, const void *k, const void *v,
+                    const void *q_attn, const void *k_attn, const void *v_attn,
+                    const float *beta, const float *g, const float *tau,
+                    const float *gate_rnn, const float *gate_kv,
+                    float *S, void *Kc, void *Vc, int32_t *pos, int32_t *count,
+                    const int32_t *t_abs,
+                    void *o, void *o_rnn, void *o_kv,
+                    float *e, uint8_t *routed, int32_t *status,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of device scratch ham_route_stats needs. */
+size_t ham_route_stats_workspace_size(const ham_dims *dims);
+
+/*
+ * ham_route_stats -- routing only: the RNN over T tokens (no readout, no
+ * attention), scores, threshold and counts.  KV usage ([HAM] §5, per layer):
+ * rho = sum(count) / (B*T*H).
+ *
+ *   q, k, v, beta, g, tau, S0    as in ham_forward (q is unused; may be NULL).
+ *   e, routed                    optional outputs as in ham_forward.
+ *   count                        [B,H] int32, required: tokens routed per head.
+ *   n_near                       [H] int64 or NULL: tokens with |e - tau_h| <
+ *                                near_band (near-threshold tokens).
+ *   rho_host                     HOST double* or NULL; if set, the call waits for
+ *                                the stream and stores rho there.
+ */
+int ham_route_stats(const ham_dims *dims,
+                    const void *q, const void *k, const void *v,
+                    const float *beta, const float *g, const float *tau,
+                    const float *S0,
+                    float *e, uint8_t *routed, int32_t *count,
+                    int64_t *n_near, float near_band, double *rho_host,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Instrumentation (not part of the method): HIP-event timing of the kernel
+ * stages of the next calls.  ham_profile_start(max_calls) arms recording on the
+ * current device for up to max_calls subsequent ham_forward / ham_decode_step /
+ * ham_route_stats calls (any thread; events are recorded on each call's own
+ * stream around each kernel launch).  ham_profile_stop waits for the recorded
+ * events and writes stage_ms[call * HAM_PROFILE_STAGES + stage] (milliseconds,
+ * 0 for unused stages) for at most max_values values, the number of recorded
+ * calls to *n_calls and each call's entry point to kinds[call] (0 forward,
+ * 1 decode, 2 route_stats; kinds may be NULL).  Stages: forward {rnn, route,
+ * compact, attention}; decode {rnn, route, append, attention, combine};
+ * route_stats {rnn, route, stats}.  Returns HAM_OK, HAM_EINVAL or HAM_EHIP.
+ */
+#define HAM_PROFILE_STAGES 5
+int ham_profile_start(int max_calls);
+int ham_profile_stop(float *stage_ms, int max_values, int *n_calls, int *kinds);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HAM_H */

@@ -51,7 +51,7 @@ def _load():
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
             [ctypes.c_int] * 5 + [ctypes.c_double] * 2 + [P] * 3 + [P] * 3 + [P] * 3
-            + [P] * 2 + [P] * 2 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
+            + [P] * 2 + [P] * 3 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
         return lib
@@ -71,13 +71,14 @@ def default_threads() -> int:
 
 def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
             v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, S0=None,
-            cache=None, cap=None, t0=0, threads=None):
+            cache=None, cap=None, t0=0, emit=None, threads=None):
     """Run the oracle over all heads.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
     S0: [B,H,dk,dv] or None (zeros).  cache: None or dict(Kc, Vc, pos, count) of an
     existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
-    absolute position of token 0.  Returns a dict of float64 / int arrays:
+    absolute position of token 0.  emit: None or [B,T,H] bool; False skips the
+    attention readout and mix of that token (o_kv, o stay 0).  Returns a dict of float64 / int arrays:
     e, routed, o_rnn, o_kv, o, S, Kc, Vc, pos, count.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -89,6 +90,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
     tau = np.ascontiguousarray(np.asarray(tau, dtype=np.float32).reshape(H))
     mo = None if mask_override is None else np.ascontiguousarray(
         np.asarray(mask_override).astype(np.int8))
+    em = None if emit is None else np.ascontiguousarray(np.asarray(emit).astype(np.int8))
     t0a = np.ascontiguousarray(np.broadcast_to(np.asarray(t0, dtype=np.int64), (B,)))
     S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
     S = np.ascontiguousarray(S)
@@ -120,7 +122,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
         return lib.ham_oracle_forward(
             B, T, H, dk, dv, float(scale), float(eps),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
-            _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(t0a),
+            _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(em), _ptr(t0a),
             _ptr(S), cap, _ptr(Kc), _ptr(Vc), _ptr(pos), _ptr(count),
             _ptr(e), _ptr(routed), _ptr(o_rnn), _ptr(o_kv), _ptr(o),
             bounds[i], bounds[i + 1])

@@ -82,7 +82,10 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
  * inputs, or NULL to share q/k/v ([HAM] §2 implementation details: shared
  * projections).  gate_rnn/gate_kv: NULL means 1.  mask_override: NULL, or a
  * [B,T,H] array of 0/1 that replaces the threshold decision (the score e is
- * still computed).  Outputs e, routed, o_rnn, o_kv, o may each be NULL.
+ * still computed).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
+ * attention readout and the mix of that token are skipped (o_kv and o stay as
+ * they were) -- this only saves time when a few sampled tokens are checked.
+ * Outputs e, routed, o_rnn, o_kv, o may each be NULL.
  *
  * Returns 0, or -3 if a routed token finds the cache full (the head stops there).
  */
@@ -92,7 +95,8 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                        const double *qa, const double *ka, const double *va,
                        const double *beta, const double *g, const float *tau,
                        const double *gate_rnn, const double *gate_kv,
-                       const int8_t *mask_override, const int64_t *t0,
+                       const int8_t *mask_override, const int8_t *emit,
+                       const int64_t *t0,
                        double *S, int cap, double *Kc, double *Vc,
                        int64_t *pos, int64_t *count,
                        double *e, int8_t *routed,
@@ -166,6 +170,10 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                 n += 1;
             }
 
+            if (emit && !emit[tok]) {
+                if (o_rnn) memcpy(o_rnn + tok * dv, orn, sizeof(double) * (size_t)dv);
+                continue;
+            }
             /* softmax attention over the cached (routed) keys, all at positions <= t */
             const double *qat = qA + tok * dk;
             for (int j = 0; j < dv; ++j) okv[j] = 0.0;

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol that include/ham.h declares, sizes its workspaces and rejects bad arguments
+before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_sequence_mixing_amd import _lib
+from attention_sequence_mixing_amd._lib import HamDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "ham.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ham_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ham_version() >= 10000
+
+
+def dims(**kw):
+    d = dict(B=2, T=300, H=4, dk=128, dv=128, io_dtype=1, scale=0.088, norm_eps=1e-6, cap=300,
+             flags=0, t0=0)
+    d.update(kw)
+    return HamDims(**d)
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    d = dims()
+    ws = L.ham_forward_workspace_size(ctypes.byref(d))
+    BTH = 2 * 300 * 4
+    assert ws >= BTH * 128 * 4 + BTH * 4 + BTH      # o_rnn fp32 + e + routed at least
+    assert L.ham_route_stats_workspace_size(ctypes.byref(d)) > ws   # adds the state
+    assert L.ham_decode_workspace_size(ctypes.byref(d)) > 0
+    for bad in (dims(dk=96), dims(dv=32), dims(T=0), dims(B=-1), dims(io_dtype=7), dims(cap=0),
+                dims(flags=64)):
+        assert L.ham_forward_workspace_size(ctypes.byref(bad)) == 0
+
+
+def _fwd(d, ptrs=None, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    fake = P(1 << 20)   # an aligned non-NULL host value; never dereferenced by these checks
+    args = [fake] * 23 if ptrs is None else ptrs
+    return _lib.lib().ham_forward(ctypes.byref(d), *args, ws_bytes, None)
+
+
+def _msg():
+    return _lib.lib().ham_last_error().decode()
+
+
+def test_forward_argument_errors():
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    base = [fake] * 23
+    # dims
+    assert _fwd(dims(dk=100)) == _lib.HAM_EUNSUPPORTED
+    assert "dk" in _msg()
+    assert _fwd(dims(B=0)) == _lib.HAM_EINVAL
+    assert _fwd(dims(io_dtype=3)) == _lib.HAM_EUNSUPPORTED
+    assert _fwd(dims(flags=8)) == _lib.HAM_EUNSUPPORTED
+    # required pointers: q k v (0-2), beta g tau (6-8), S_out (12), o (13), Kc Vc pos count (18-21)
+    for i in (0, 1, 2, 6, 7, 8, 12, 13, 18, 19, 20, 21):
+        a = list(base)
+        a[i] = None
+        assert _fwd(dims(), a) == _lib.HAM_EINVAL, i
+        assert "NULL" in _msg()
+    # misaligned
+    a = list(base)
+    a[0] = P((1 << 20) + 2)
+    assert _fwd(dims(), a) == _lib.HAM_EINVAL and "aligned" in _msg()
+    # capacity without continuation
+    assert _fwd(dims(cap=100)) == _lib.HAM_ECAPACITY
+    # workspace
+    a = list(base)
+    a[22] = None
+    assert _fwd(dims(), a) == _lib.HAM_EWORKSPACE
+    assert _fwd(dims(), base, ws_bytes=16) == _lib.HAM_EWORKSPACE
+
+
+def test_decode_and_stats_argument_errors():
+    L = _lib.lib()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    a = [fake] * 24
+    a[15] = None                                       # count
+    assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
+    a = [fake] * 24
+    a[16] = None                                       # t_abs
+    assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
+    a = [fake] * 24
+    assert L.ham_decode_step(ctypes.byref(dims()), *a, 8, None) == _lib.HAM_EWORKSPACE
+    s = [fake] * 11
+    s[9] = None                                        # count
+    assert L.ham_route_stats(ctypes.byref(dims()), *s, ctypes.c_float(1e-5), None, fake,
+                             1 << 40, None) == _lib.HAM_EINVAL
+    s = [fake] * 11
+    assert L.ham_route_stats(ctypes.byref(dims()), *s, ctypes.c_float(-1.0), None, fake,
+                             1 << 40, None) == _lib.HAM_EINVAL
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The library and binding never reference the oracle."""
+    pkg = os.path.join(ROOT, "attention_sequence_mixing_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower(), f
+    with open(_lib.LIB_PATH, "rb") as fh:
+        assert b"ham_oracle" not in fh.read()
