@@ -145,3 +145,26 @@ def make_gates(B, T, H, seed):
     gr = _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
     gk = _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
     return gr, gk
+
+
+def make_inputs_torch(B, T, H, dk, dv=None, *, dtype="bf16", seed=0, device="cuda"):
+    """The same recipe drawn on the device with torch's generator (for workloads too
+    large to draw on the host, e.g. a 32K-token prefix of 32 sequences).  Deterministic
+    for a given device and torch build; not bit-identical to make_inputs."""
+    import torch
+    dv = dk if dv is None else dv
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.to(tdt)
+
+    q = unit((B, T, H, dk))
+    k = unit((B, T, H, dk))
+    v = torch.randn((B, T, H, dv), generator=gen, device=device, dtype=torch.float32).to(tdt)
+    beta = torch.sigmoid(torch.randn((B, T, H), generator=gen, device=device))
+    g = -torch.nn.functional.softplus(torch.randn((B, T, H), generator=gen, device=device))
+    return dict(q=q, k=k, v=v, beta=beta.contiguous(), g=g.contiguous())

@@ -1,0 +1,292 @@
+"""Benchmark of the HAM layer on one MI355X.
+
+Default run (N=1): the layer forward at the 800M-model shape (bf16 I/O, fp32
+state: B=8, H=16, d=128, T=4096, threshold per head for KV usage rho=0.5) timed
+over K steps with inputs resident in HBM; then the decode workload (batch 32,
+H=16, d=128, 32K-token prefix at rho=0.5, 256 decode steps).  Per-kernel times
+come from HIP events recorded by the library on the launch stream; the oracle
+is timed on a bounded sample on the host cores as a CPU baseline.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+CHUNK = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rnn_flops_per_token_head(d, C=CHUNK):
+    """Chunked gated delta rule per token and head (C = 64) plus the fit-error
+    score: Tab. E.11 subtotal per head + the Tab. E.13 selection term."""
+    return 1 + 3.5 * C + C * C / 2 + 6 * C * d + 4 * C * d + 6 * d * d + 12 * d
+
+
+def attn_flops_per_pair(d):
+    """QK^T 2d + softmax 4 + PV 2d per visible (query, key) pair (Tab. E.12)."""
+    return 4 * d + 4
+
+
+def profile_stages(lib, fn, n):
+    import ctypes
+    import torch
+    lib.ham_profile_start(n)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    S = 5
+    buf = (ctypes.c_float * (n * S))()
+    ncalls = ctypes.c_int(0)
+    kinds = (ctypes.c_int * n)()
+    rc = lib.ham_profile_stop(buf, n * S, ctypes.byref(ncalls), kinds)
+    if rc != 0:
+        raise RuntimeError(lib.ham_last_error().decode())
+    arr = np.frombuffer(buf, dtype=np.float32).reshape(n, S)[: ncalls.value]
+    return arr.mean(axis=0)          # ms per stage, averaged over calls
+
+
+def bench_forward(args, dev):
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    from attention_sequence_mixing_amd.inputs import LAYER, make_workload, tau_for_rho
+
+    w = LAYER
+    t0 = time.time()
+    inp = make_workload(w)
+    dt = torch.bfloat16
+    t = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(dt)
+    log(f"[bench] inputs {w.name} drawn in {time.time() - t0:.1f}s")
+    st = ham.ham_route_stats(t["k"], t["v"], t["beta"], t["g"],
+                             torch.full((w.H,), float("inf"), device=dev), want_rho=False)
+    tau_np = tau_for_rho(st["e"].cpu().numpy(), w.rho)
+    tau = torch.from_numpy(tau_np).to(dev)
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, dt, dev, scale=w.attn_scale)
+
+    def step():
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = profile_stages(_lib.lib(), step, args.steps)
+
+    routed = plan.routed
+    count = plan.count
+    rho = float(count.sum().item()) / (w.B * w.T * w.H)
+    n_t = torch.cumsum(routed.to(torch.int64), dim=1)          # visible keys per query
+    pairs = float(n_t.sum().item())
+    BTH = w.B * w.T * w.H
+    d = w.d
+    rnn_flops = BTH * rnn_flops_per_token_head(d)
+    att_flops = pairs * attn_flops_per_pair(d)
+    nroute = float(count.sum().item())
+    # algorithmic bytes (inputs read once, outputs written once)
+    rnn_bytes = BTH * (3 * d * 2 + 8 + 16 * 8 + d * 4)          # q,k,v bf16, beta/g, score partials, o_rnn fp32
+    route_bytes = BTH * (16 * 8 + 4 + 1)
+    compact_bytes = BTH * (1 + 4) + nroute * (2 * (2 * d * 2) + 4)
+    attn_bytes = BTH * (d * 2 + d * 4 + 4 + d * 2) + w.B * w.H * 0 + nroute * 2 * d * 2
+    names = ["rnn", "route", "compact", "attention"]
+    per = []
+    for i, nm in enumerate(names):
+        sec = stages[i] / 1e3
+        if nm == "rnn":
+            per.append(dict(stage=nm, ms=stages[i], bound="alu", unit="TFLOP/s",
+                            achieved=rnn_flops / sec / 1e12, peak=PEAK_FP32_TFLOPS))
+        elif nm == "attention":
+            per.append(dict(stage=nm, ms=stages[i], bound="mfma", unit="TFLOP/s",
+                            achieved=att_flops / sec / 1e12, peak=PEAK_BF16_TFLOPS))
+        else:
+            b = route_bytes if nm == "route" else compact_bytes
+            per.append(dict(stage=nm, ms=stages[i], bound="hbm", unit="GB/s",
+                            achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
+        per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
+    dom = max(per, key=lambda x: x["ms"])
+    return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
+                rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops)
+
+
+def bench_decode(args, dev):
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    from attention_sequence_mixing_amd.inputs import (DECODE_B, DECODE_D, DECODE_H, DECODE_PREFIX,
+                                                      DECODE_STEPS, make_inputs_torch, tau_for_rho)
+    B, H, d, T0, steps = DECODE_B, DECODE_H, DECODE_D, args.decode_prefix or DECODE_PREFIX, DECODE_STEPS
+    cap = T0 + steps
+    dt = torch.bfloat16
+    t0 = time.time()
+    pre = make_inputs_torch(B, T0, H, d, dtype="bf16", seed=4, device=dev)
+    st = ham.ham_route_stats(pre["k"], pre["v"], pre["beta"], pre["g"],
+                             torch.full((H,), float("inf"), device=dev), want_rho=False)
+    tau = torch.from_numpy(tau_for_rho(st["e"].cpu().numpy(), 0.5)).to(dev)
+    del st
+    plan = ham.ForwardPlan(B, T0, H, d, d, dt, dev, cap=cap, scale=d ** -0.5)
+    plan(pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"], tau)
+    torch.cuda.synchronize()
+    log(f"[bench] decode prefill B={B} T={T0} done in {time.time() - t0:.1f}s")
+    del pre
+    S, Kc, Vc, pos, count = plan.S, plan.Kc, plan.Vc, plan.pos, plan.count
+    plan.o = None
+    plan.ws = None
+    torch.cuda.empty_cache()
+    S0, count0 = S.clone(), count.clone()
+    x = make_inputs_torch(steps, B, H, d, dtype="bf16", seed=5, device=dev)   # [steps, B, H, d]
+    dplan = ham.DecodePlan(B, H, d, d, cap, dt, dev, scale=d ** -0.5)
+    t_abs = [torch.full((B,), T0 + s, dtype=torch.int32, device=dev) for s in range(steps)]
+
+    def run_all():
+        for s in range(steps):
+            dplan(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s], tau, S, Kc, Vc, pos,
+                  count, t_abs[s])
+
+    cache_keys0 = float(count0.sum().item())
+    run_all()                               # warm-up pass over the same steps
+    torch.cuda.synchronize()
+    S.copy_(S0); count.copy_(count0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_all()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    cache_keys1 = float(count.sum().item())
+    S.copy_(S0); count.copy_(count0)
+    # per-stage timing over all steps
+    L = _lib.lib()
+    L.ham_profile_start(steps)
+    run_all()
+    torch.cuda.synchronize()
+    import ctypes
+    buf = (ctypes.c_float * (steps * 5))()
+    n = ctypes.c_int(0)
+    L.ham_profile_stop(buf, steps * 5, ctypes.byref(n), None)
+    stg = np.frombuffer(buf, dtype=np.float32).reshape(steps, 5)[: n.value].mean(axis=0)
+    mean_keys = 0.5 * (cache_keys0 + cache_keys1)
+    cache_bytes = mean_keys * 2 * d * 2                     # K and V rows, bf16
+    state_bytes = B * H * d * d * 4 * 2                     # S read + write
+    attn_sec = stg[3] / 1e3
+    roof = dict(stage="decode_attention", ms=float(stg[3]), bound="hbm", unit="GB/s",
+                achieved=cache_bytes / attn_sec / 1e9, peak=PEAK_HBM_GBS)
+    roof["frac"] = roof["achieved"] / PEAK_HBM_GBS
+    return dict(us_per_step=us, tokens_per_s=B / (us / 1e6), steps=steps, prefix=T0,
+                cache_keys_mean=mean_keys, step_bytes=cache_bytes + state_bytes,
+                step_gbs=(cache_bytes + state_bytes) / (us / 1e6) / 1e9,
+                stages_ms=dict(zip(["rnn", "route", "append", "attention", "combine"],
+                                   [float(v) for v in stg])),
+                roofline=roof)
+
+
+def cpu_baseline(res, heads):
+    import oracle
+    w = res["w"]
+    inp = res["inp"]
+    hs = list(range(heads))
+    sub = {n: np.ascontiguousarray(a[0:1, :, hs]) for n, a in inp.items()}
+    tau = res["tau"][hs]
+    threads = min(16, heads, os.cpu_count() or 1)
+    oracle.forward(**{n: a[:, :64] for n, a in sub.items()}, tau=tau, scale=w.attn_scale,
+                   threads=threads)   # compile/load outside the timing
+    t0 = time.perf_counter()
+    oracle.forward(**sub, tau=tau, scale=w.attn_scale, threads=threads)
+    sec = time.perf_counter() - t0
+    tokens = heads * w.T / w.H       # one token = all H heads of one position
+    return dict(value=tokens / sec, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"b=0, heads 0..{heads - 1} of {w.name}, all {w.T} tokens, fp64 C oracle, "
+                       f"{sec:.1f}s; scaled as {heads}/{w.H} of a token per head-token")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-prefix", type=int, default=0)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the HAM layer on a single MI355X "
+              "(heads shard across GPUs without communication; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    p = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {p.name} {getattr(p, 'gcnArchName', '')} CUs={p.multi_processor_count} "
+        f"mem={p.total_memory / 2**30:.0f} GiB")
+    res = bench_forward(args, dev)
+    for s in res["stages"]:
+        log(f"[bench] stage {s['stage']:10s} {s['ms']:8.3f} ms  {s['achieved']:9.1f} {s['unit']} "
+            f"({100 * s['frac']:.1f}% of {s['peak']})")
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(args, dev)
+        log(f"[bench] decode {dec['us_per_step']:.1f} us/step, stages {dec['stages_ms']}")
+    cpu = None if args.no_cpu else cpu_baseline(res, args.cpu_heads)
+    w = res["w"]
+    dom = res["dom"]
+    roof = dict(bound=dom["bound"], achieved=round(dom["achieved"], 3), peak=dom["peak"],
+                unit=dom["unit"], frac=round(dom["frac"], 4), traffic=None, kernel=dom["stage"])
+    out = {
+        "metric": "HAM layer fwd tokens/sec at T=4096, rho_KV=0.5; decode us/token at 32k",
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d": w.d, "rho_kv": w.rho,
+                   "state": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rho_measured": round(res["rho"], 6),
+        "visible_pairs": res["pairs"],
+        "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
+                   for s in res["stages"]],
+        "decode": None if dec is None else {
+            "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
+            "us_per_step": round(dec["us_per_step"], 2), "tokens_per_s": round(dec["tokens_per_s"], 1),
+            "steps": dec["steps"], "stages_ms": {k: round(v, 4) for k, v in dec["stages_ms"].items()},
+            "step_GBps": round(dec["step_gbs"], 1),
+            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec["roofline"].items()}},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
