@@ -60,7 +60,7 @@ def profile_stages(lib, fn, n):
     if rc != 0:
         raise RuntimeError(lib.ham_last_error().decode())
     arr = np.frombuffer(buf, dtype=np.float32).reshape(n, S)[: ncalls.value]
-    return arr.mean(axis=0)          # ms per stage, averaged over calls
+    return [float(x) for x in arr.astype(np.float64).mean(axis=0)]   # ms per stage
 
 
 def bench_forward(args, dev):
@@ -190,7 +190,8 @@ def bench_decode(args, dev):
     buf = (ctypes.c_float * (steps * 5))()
     n = ctypes.c_int(0)
     L.ham_profile_stop(buf, steps * 5, ctypes.byref(n), None)
-    stg = np.frombuffer(buf, dtype=np.float32).reshape(steps, 5)[: n.value].mean(axis=0)
+    stg = [float(x) for x in np.frombuffer(buf, dtype=np.float32).reshape(steps, 5)[: n.value]
+           .astype(np.float64).mean(axis=0)]
     mean_keys = 0.5 * (cache_keys0 + cache_keys1)
     cache_bytes = mean_keys * 2 * d * 2                     # K and V rows, bf16
     state_bytes = B * H * d * d * 4 * 2                     # S read + write
