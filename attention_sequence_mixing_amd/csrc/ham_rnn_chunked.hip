@@ -83,31 +83,33 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
 template <int DK, int NW>
 struct ChunkSmem {
   static constexpr int KS = DK + 8;        // row stride (u16) of K and Q
-  static constexpr int TS = kC + 8;        // row stride (u16) of C-wide bf16 matrices and K^T
+  static constexpr int TS = kC + 8;        // row stride (u16) of K^T
   static constexpr int VS = 16 * NW + 8;   // row stride (u16) of the V slice
-  static constexpr int FS = kC + 1;        // row stride (f32) of C x C fp32 matrices
   uint16_t K[kC * KS];
   uint16_t Q[kC * KS];
   uint16_t Kt[DK * TS];
   uint16_t V[kC * VS];
-  uint16_t A[3][kC * TS];                  // strict_lower(Gamma o K K^T): hi, mid, lo
-  uint16_t Tm[3][kC * TS];                 // (I + diag(beta)A)^-1 diag(beta): hi, mid, lo
-  union {
-    uint16_t QK[2][kC * TS];               // Gamma o Q K^T o lower_incl: hi, mid
-    float L[kC * FS];                      // diag(beta) A, during the inverse only
-  } u;
-  float Tf[kC * FS];                       // (I + L)^-1 in fp32
-  float W[3 * 256];
-  float G[kC], gam[kC], beta[kC], wdec[kC];
+  // MFMA A-operand fragments in lane order, one 16-byte entry per lane:
+  //   A  = strict_lower(Gamma o K K^T)          6 (row-tile, k-step) pairs x 3 splits
+  //   QK = Gamma o Q K^T o lower_incl          6 pairs x 2 splits
+  bf16x8 Af[6][3][kWave];
+  bf16x8 QKf[6][2][kWave];
+  float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
+  float Td[4][16][20];                     // (I + Ld)^-1 diag(beta) per block
+  float G2[kC], gam[kC], beta[kC], wdec[kC];
 };
 
+// Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
+HAM_DEVICE constexpr int pair_index(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 + s : 4 + s; }
+
 // Per-thread register stage of one chunk's inputs (prefetched one chunk ahead).
+// Units are 16 bytes; unit u covers token u % 64 and 8 consecutive elements.
 template <int DK, int NW>
 struct ChunkRegs {
   static constexpr int NT = 64 * NW;
-  static constexpr int KU = kC * (DK / 8);             // 16-byte units of K (and Q)
+  static constexpr int KU = kC * (DK / 8);
   static constexpr int KPT = (KU + NT - 1) / NT;
-  static constexpr int VU = kC * 2 * NW;               // 16-byte units of the V slice
+  static constexpr int VU = kC * 2 * NW;
   static constexpr int VPT = (VU + NT - 1) / NT;
   u16x8 k[KPT], q[KPT], v[VPT];
   float g, beta;
@@ -124,7 +126,7 @@ HAM_DEVICE void load_chunk(const RnnArgs& a, ChunkRegs<DK, NW>& r, int b, int h,
 #pragma unroll
   for (int p = 0; p < R::KPT; ++p) {
     const int u = tid + p * R::NT;
-    const int row = u / (DK / 8), cu = (u % (DK / 8)) * 8;
+    const int row = u % kC, cu = (u / kC) * 8;
     r.k[p] = (u16x8)(0);
     r.q[p] = (u16x8)(0);
     if (u < R::KU && row < nvalid) {
@@ -136,7 +138,7 @@ HAM_DEVICE void load_chunk(const RnnArgs& a, ChunkRegs<DK, NW>& r, int b, int h,
 #pragma unroll
   for (int p = 0; p < R::VPT; ++p) {
     const int u = tid + p * R::NT;
-    const int row = u / (2 * NW), cu = (u % (2 * NW)) * 8;
+    const int row = u % kC, cu = (u / kC) * 8;
     r.v[p] = (u16x8)(0);
     if (u < R::VU && row < nvalid) {
       const size_t tok = ((size_t)b * a.T + t0 + row) * a.H + h;
@@ -160,7 +162,7 @@ HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, i
   for (int p = 0; p < R::KPT; ++p) {
     const int u = tid + p * R::NT;
     if (u < R::KU) {
-      const int row = u / (DK / 8), cu = (u % (DK / 8)) * 8;
+      const int row = u % kC, cu = (u / kC) * 8;
       *reinterpret_cast<u16x8*>(&sm.K[row * SM::KS + cu]) = r.k[p];
       *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
 #pragma unroll
@@ -171,7 +173,7 @@ HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, i
   for (int p = 0; p < R::VPT; ++p) {
     const int u = tid + p * R::NT;
     if (u < R::VU) {
-      const int row = u / (2 * NW), cu = (u % (2 * NW)) * 8;
+      const int row = u % kC, cu = (u / kC) * 8;
       *reinterpret_cast<u16x8*>(&sm.V[row * SM::VS + cu]) = r.v[p];
     }
   }
@@ -184,67 +186,101 @@ HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, i
       if (tid >= off) G += y;
     }
     const float Glast = __shfl(G, kC - 1, kWave);
-    sm.G[tid] = G;
+    sm.G2[tid] = G * 1.4426950408889634f;
     sm.gam[tid] = expf(G);
     sm.wdec[tid] = expf(Glast - G);
     sm.beta[tid] = r.beta;
   }
 }
 
-// T = (I + L)^-1 for strictly lower L (fp32, 64x64, in sm.u.L) by 16x16 blocks:
-// diagonal blocks by forward substitution, then block rows level by level,
-// T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj.
-template <int DK, int NW>
-HAM_DEVICE void invert_unit_lower(ChunkSmem<DK, NW>& sm, int tid) {
+// One (row tile mt, k-step s) fragment of the decayed Gram matrix, computed
+// transposed so that the MFMA output already sits in A-operand order: lane (g,n)
+// ends with entries (t = 16mt + n, j = 32s + 16h + 4g + i) for half h, i = 0..3.
+template <int DK, int NW, bool kQK>
+HAM_DEVICE void gram_fragment(ChunkSmem<DK, NW>& sm, int mt, int s, int g, int n, int lane) {
   using SM = ChunkSmem<DK, NW>;
-  constexpr int NT = 64 * NW, FS = SM::FS;
-  const float* L = sm.u.L;
-  float* Tf = sm.Tf;
-  if (tid < 64) {
-    const int bb = tid >> 4, c = tid & 15;
-    float col[16];
+  constexpr int KS = SM::KS;
+  const uint16_t* rowsT = kQK ? sm.Q : sm.K;
+  float val[2][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = (r == c) ? 1.f : 0.f;
-      const float* lr = L + (16 * bb + r) * FS + 16 * bb;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int jt = 2 * s + hh;
+    f32x4 acc = (f32x4)(0.f);
+    if (jt <= mt) {
 #pragma unroll
-      for (int j = 0; j < r; ++j) s = fmaf(-lr[j], col[j], s);
-      col[r] = s;
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * jt + n) * KS + 32 * ks + 8 * g]));
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[(16 * mt + n) * KS + 32 * ks + 8 * g]));
+        acc = mfma_bf16(af, bf, acc);
+      }
     }
+    const int t = 16 * mt + n;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Tf[(16 * bb + r) * FS + 16 * bb + c] = col[r];
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * jt + 4 * g + i;
+      const bool keep = kQK ? (j <= t) : (j < t);
+      val[hh][i] = keep ? acc[i] * exp2f(sm.G2[t] - sm.G2[j]) : 0.f;
+      if (!kQK && jt == mt) sm.Ld[mt][n][4 * g + i] = sm.beta[t] * val[hh][i];
+    }
   }
-  __syncthreads();
+  const int pi = pair_index(mt, s);
+  if (kQK) {
+    bf16x8 h8, m8;
 #pragma unroll
-  for (int lev = 1; lev < 4; ++lev) {
-    const int nb = 4 - lev;
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      const int i = lev + blk, j = i - lev;
-      float s = 0.f;
-      const float* lr = L + (16 * i + r) * FS;
-      for (int kk = 16 * j; kk < 16 * i; ++kk) s = fmaf(lr[kk], Tf[kk * FS + 16 * j + cc], s);
-      sm.W[blk * 256 + r * 16 + cc] = s;
+    for (int i = 0; i < 8; ++i) {
+      const float x = val[i >> 2][i & 3];
+      const __bf16 xh = to_bf16(x);
+      h8[i] = xh;
+      m8[i] = to_bf16(x - from_bf16(xh));
     }
-    __syncthreads();
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      const int i = lev + blk, j = i - lev;
-      float s = 0.f;
-      const float* tr = Tf + (16 * i + r) * FS + 16 * i;
+    sm.QKf[pi][0][lane] = h8;
+    sm.QKf[pi][1][lane] = m8;
+  } else {
+    bf16x8 h8, m8, l8;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) s = fmaf(tr[kk], sm.W[blk * 256 + kk * 16 + cc], s);
-      Tf[(16 * i + r) * FS + 16 * j + cc] = -s;
+    for (int i = 0; i < 8; ++i) {
+      __bf16 x0, x1, x2;
+      split3(val[i >> 2][i & 3], x0, x1, x2);
+      h8[i] = x0; m8[i] = x1; l8[i] = x2;
     }
-    __syncthreads();
+    sm.Af[pi][0][lane] = h8;
+    sm.Af[pi][1][lane] = m8;
+    sm.Af[pi][2][lane] = l8;
   }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+HAM_DEVICE f32x4 mfma_bf16_k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+HAM_DEVICE void split3x4(const float x[4], bf16x4& h, bf16x4& m, bf16x4& l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __bf16 a, b, c;
+    split3(x[i], a, b, c);
+    h[i] = a; m[i] = b; l[i] = c;
+  }
+}
+
+// Six-term fp32-accurate product accumulation: (ah+am+al)(bh+bm+bl), dropping the
+// terms below 2^-16 relative.
+template <class F, class V>
+HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, const V& bm, const V& bl, f32x4 c) {
+  c = mf(am, bm, c);
+  c = mf(al, bh, c);
+  c = mf(ah, bl, c);
+  c = mf(am, bh, c);
+  c = mf(ah, bm, c);
+  c = mf(ah, bh, c);
+  return c;
 }
 
 template <int DK, int DV, int NW>
 __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   using SM = ChunkSmem<DK, NW>;
-  constexpr int NT = 64 * NW;
-  constexpr int KS = SM::KS, TS = SM::TS, VS = SM::VS, FS = SM::FS;
+  constexpr int KS = SM::KS, TS = SM::TS, VS = SM::VS;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
   constexpr int NSL = DV / 16;    // score slices
@@ -259,6 +295,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const int vcol = wave * 16 + n;
   const int slice = blockIdx.x * NW + wave;
   const bool readout = a.o_rnn32 != nullptr;
+  auto mf32 = [](const bf16x8& x, const bf16x8& y, const f32x4& c) { return mfma_bf16(x, y, c); };
+  auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) { return mfma_bf16_k16(x, y, c); };
 
   // state tiles: S[16*mt + 4g + i][col]
   f32x4 S[MT];
@@ -270,6 +308,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       S[mt][i] = a.S0 ? a.S0[sbase + (size_t)(16 * mt + 4 * g + i) * DV + col] : 0.f;
 
   const int nchunk = (a.T + kC - 1) / kC;
+  const int nfrag = readout ? 12 : 6;
   ChunkRegs<DK, NW> regs;
   load_chunk<DK, DV, NW>(a, regs, b, h, 0, colbase, tid, readout);
 
@@ -281,76 +320,36 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     if (c + 1 < nchunk) load_chunk<DK, DV, NW>(a, regs, b, h, t0 + kC, colbase, tid, readout);
     __syncthreads();
 
-    // ---- A = strict_lower(Gamma o K K^T) (3-way split) and L = diag(beta) A ----
-    for (int tile = wave; tile < 16; tile += NW) {
-      const int mt = tile >> 2, nt = tile & 3;
-      f32x4 acc = (f32x4)(0.f);
-      if (nt <= mt) {
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * mt + n) * KS + 32 * ks + 8 * g]));
-          const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * nt + n) * KS + 32 * ks + 8 * g]));
-          acc = mfma_bf16(af, bf, acc);
-        }
-      }
-      const int j = 16 * nt + n;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g + i;
-        const float val = (j < t) ? acc[i] * expf(sm.G[t] - sm.G[j]) : 0.f;
-        __bf16 x0, x1, x2;
-        split3(val, x0, x1, x2);
-        sm.A[0][t * TS + j] = __builtin_bit_cast(uint16_t, x0);
-        sm.A[1][t * TS + j] = __builtin_bit_cast(uint16_t, x1);
-        sm.A[2][t * TS + j] = __builtin_bit_cast(uint16_t, x2);
-        sm.u.L[t * FS + j] = sm.beta[t] * val;
-      }
-    }
-    __syncthreads();
-    invert_unit_lower<DK, NW>(sm, tid);
-    // T' = T diag(beta), 3-way split, zero above the diagonal
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int t = e >> 6, j = e & 63;
-      const float val = (j <= t) ? sm.Tf[t * FS + j] * sm.beta[j] : 0.f;
-      __bf16 x0, x1, x2;
-      split3(val, x0, x1, x2);
-      sm.Tm[0][t * TS + j] = __builtin_bit_cast(uint16_t, x0);
-      sm.Tm[1][t * TS + j] = __builtin_bit_cast(uint16_t, x1);
-      sm.Tm[2][t * TS + j] = __builtin_bit_cast(uint16_t, x2);
-    }
-    __syncthreads();
-    // ---- Gamma o Q K^T o lower_incl (2-way split), reusing the L storage ----
-    if (readout) {
-      for (int tile = wave; tile < 16; tile += NW) {
-        const int mt = tile >> 2, nt = tile & 3;
-        f32x4 acc = (f32x4)(0.f);
-        if (nt <= mt) {
-#pragma unroll
-          for (int ks = 0; ks < KSD; ++ks) {
-            const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.Q[(16 * mt + n) * KS + 32 * ks + 8 * g]));
-            const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * nt + n) * KS + 32 * ks + 8 * g]));
-            acc = mfma_bf16(af, bf, acc);
-          }
-        }
-        const int j = 16 * nt + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * mt + 4 * g + i;
-          const float val = (j <= t) ? acc[i] * expf(sm.G[t] - sm.G[j]) : 0.f;
-          const __bf16 x0 = to_bf16(val);
-          const __bf16 x1 = to_bf16(val - from_bf16(x0));
-          sm.u.QK[0][t * TS + j] = __builtin_bit_cast(uint16_t, x0);
-          sm.u.QK[1][t * TS + j] = __builtin_bit_cast(uint16_t, x1);
-        }
-      }
+    // ---- decayed Gram fragments, shared through LDS in lane order ----
+    for (int f = wave; f < nfrag; f += NW) {
+      const int pi = f % 6;
+      const int mt = pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3;
+      const int s = pi < 2 ? 0 : (pi - 2) & 1;
+      if (f < 6) gram_fragment<DK, NW, false>(sm, mt, s, g, n, lane);
+      else gram_fragment<DK, NW, true>(sm, mt, s, g, n, lane);
     }
     __syncthreads();
 
-    // ---- state phase: this wave's 16 columns ----
+    // ---- wave 0: inverses of the four diagonal blocks, T'_ii = (I + L_ii)^-1 diag(beta_i) ----
+    if (wave == 0) {
+      const int bb = lane >> 4, cc = lane & 15;
+      float colv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sacc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) sacc = fmaf(-sm.Ld[bb][r][j], colv[j], sacc);
+        colv[r] = sacc;
+      }
+      const float bc = sm.beta[16 * bb + cc];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.Td[bb][r][cc] = colv[r] * bc;
+    }
+
+    // ---- Y_K = K S, Y_Q = Q S (independent of the inverse) ----
     bf16x8 sh[KSD], smd[KSD], sl[KSD];
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) split_pair3(S[2 * ks], S[2 * ks + 1], sh[ks], smd[ks], sl[ks]);
-
     f32x4 P[4], O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -371,7 +370,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
     }
-    // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4], Vr[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -385,59 +383,71 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         O[mt][i] *= gm;
         X[mt][i] = vv - P[mt][i];
       }
-    bf16x8 xh[2], xm[2], xl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) split_pair3(X[2 * s], X[2 * s + 1], xh[s], xm[s], xl[s]);
+    __syncthreads();                          // Td is ready
 
-    // D = T' X   (6 cross terms per k-step; T' is lower triangular)
+    // ---- block forward substitution: D_i = T'_ii (X_i - sum_{j<i} A_ij D_j) ----
+    // dB[s][*]: B-operand fragments (k-step s) of the D blocks solved so far.
+    bf16x8 dB[2][3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int z = 0; z < 3; ++z) dB[s][z] = (bf16x8)(0);
     f32x4 D[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      D[mt] = (f32x4)(0.f);
+    for (int i = 0; i < 4; ++i) {
+      f32x4 R = (f32x4)(0.f);
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s) {
-        const int off = (16 * mt + n) * TS + 32 * s + 4 * g;
-        const bf16x8 th = frag2(&sm.Tm[0][off], &sm.Tm[0][off + 16]);
-        const bf16x8 tm = frag2(&sm.Tm[1][off], &sm.Tm[1][off + 16]);
-        const bf16x8 tl = frag2(&sm.Tm[2][off], &sm.Tm[2][off + 16]);
-        D[mt] = mfma_bf16(tm, xm[s], D[mt]);
-        D[mt] = mfma_bf16(tl, xh[s], D[mt]);
-        D[mt] = mfma_bf16(th, xl[s], D[mt]);
-        D[mt] = mfma_bf16(tm, xh[s], D[mt]);
-        D[mt] = mfma_bf16(th, xm[s], D[mt]);
-        D[mt] = mfma_bf16(th, xh[s], D[mt]);
+      for (int s = 0; s <= (i - 1) / 2 && i > 0; ++s) {
+        const int pi = pair_index(i, s);
+        R = mma6(mf32, sm.Af[pi][0][lane], sm.Af[pi][1][lane], sm.Af[pi][2][lane],
+                 dB[s][0], dB[s][1], dB[s][2], R);
       }
+      float rhs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rhs[e] = X[i][e] - R[e];
+      bf16x4 rh, rm, rl, th, tm, tl;
+      split3x4(rhs, rh, rm, rl);
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.Td[i][n][4 * g]);
+      const float tva[4] = {tv[0], tv[1], tv[2], tv[3]};
+      split3x4(tva, th, tm, tl);
+      D[i] = mma6(mf16, th, tm, tl, rh, rm, rl, (f32x4)(0.f));
+      // the diagonal block's share of A D, for the prediction P
+      const int half = i & 1;
+      bf16x4 dh4, dm4, dl4;
+      const float dva[4] = {D[i][0], D[i][1], D[i][2], D[i][3]};
+      split3x4(dva, dh4, dm4, dl4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dB[i >> 1][0][4 * half + e] = dh4[e];
+        dB[i >> 1][1][4 * half + e] = dm4[e];
+        dB[i >> 1][2][4 * half + e] = dl4[e];
+      }
+      const int pd = pair_index(i, i >> 1);
+      bf16x4 ah4, am4, al4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ah4[e] = sm.Af[pd][0][lane][4 * half + e];
+        am4[e] = sm.Af[pd][1][lane][4 * half + e];
+        al4[e] = sm.Af[pd][2][lane][4 * half + e];
+      }
+      P[i] = mma6(mf16, ah4, am4, al4, dh4, dm4, dl4, P[i] + R);
     }
-    bf16x8 dh[2], dm[2], dl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) split_pair3(D[2 * s], D[2 * s + 1], dh[s], dm[s], dl[s]);
 
-    // P += A D (6 terms), O += (Gamma o Q K^T) D (3 terms)
+    // ---- readout O += (Gamma o Q K^T o lower_incl) D  (bf16 outputs: 3 terms) ----
+    if (readout) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s) {
-        const int off = (16 * mt + n) * TS + 32 * s + 4 * g;
-        const bf16x8 ah = frag2(&sm.A[0][off], &sm.A[0][off + 16]);
-        const bf16x8 am = frag2(&sm.A[1][off], &sm.A[1][off + 16]);
-        const bf16x8 al = frag2(&sm.A[2][off], &sm.A[2][off + 16]);
-        P[mt] = mfma_bf16(am, dm[s], P[mt]);
-        P[mt] = mfma_bf16(al, dh[s], P[mt]);
-        P[mt] = mfma_bf16(ah, dl[s], P[mt]);
-        P[mt] = mfma_bf16(am, dh[s], P[mt]);
-        P[mt] = mfma_bf16(ah, dm[s], P[mt]);
-        P[mt] = mfma_bf16(ah, dh[s], P[mt]);
-        if (readout) {
-          const bf16x8 qh = frag2(&sm.u.QK[0][off], &sm.u.QK[0][off + 16]);
-          const bf16x8 qm = frag2(&sm.u.QK[1][off], &sm.u.QK[1][off + 16]);
-          O[mt] = mfma_bf16(qm, dh[s], O[mt]);
-          O[mt] = mfma_bf16(qh, dm[s], O[mt]);
-          O[mt] = mfma_bf16(qh, dh[s], O[mt]);
+        for (int s = 0; s <= (mt >> 1); ++s) {
+          const int pi = pair_index(mt, s);
+          const bf16x8 qh = sm.QKf[pi][0][lane], qm = sm.QKf[pi][1][lane];
+          O[mt] = mfma_bf16(qm, dB[s][0], O[mt]);
+          O[mt] = mfma_bf16(qh, dB[s][1], O[mt]);
+          O[mt] = mfma_bf16(qh, dB[s][0], O[mt]);
         }
-      }
     }
 
-    // score partials of this 16-column slice, and the readout
+    // ---- score partials of this 16-column slice, and the readout ----
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
 
-    // S <- gamma_C S + K^T diag(exp(G_C - G)) D
+    // ---- S <- gamma_C S + K^T diag(exp(G_C - G)) D ----
     bf16x8 eh[2], em[2], el[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
