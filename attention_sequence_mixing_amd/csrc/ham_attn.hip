@@ -282,6 +282,257 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---- bf16 path: 32 queries per wave, double-buffered K / V^T tiles ---------------
+//
+// A wave owns QT 16-query tiles; every K and V^T fragment it reads from LDS feeds
+// QT MFMAs, which keeps the LDS traffic per MFMA flop at 1/QT of the one-tile
+// layout.  The next key tile is fetched into registers while the current one is
+// consumed, then written to the other LDS buffer; one barrier per tile.  V^T is
+// built with 4-byte loads (two adjacent d of one key; each load instruction of a
+// wave reads 256 contiguous bytes of one row) packed into 16-byte LDS stores of
+// eight consecutive keys.
+template <int DK, int DV, int QT>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
+  constexpr int BMW = 16 * QT, BM = 4 * BMW;
+  constexpr int KS = DK + 8, VS = BN + 8;
+  constexpr int KU = BN * DK / 8, KPT = KU / 256;            // 16-byte K units per thread
+  constexpr int VU = (DV / 2) * (BN / 8), VPT = VU / 256;     // (d pair, 8-key group) units
+  static_assert(KU % 256 == 0 && VU % 256 == 0, "tile does not split evenly");
+  __shared__ uint16_t Ks[2][BN * KS];
+  __shared__ uint16_t Vt[2][DV * VS];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 4, qn = lane & 15;
+  const int nqb = (a.T + BM - 1) / BM;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqb;
+  const int qb = nqb - 1 - (lin % nqb);
+  const int b = bh / a.H, h = bh % a.H;
+
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* Kh = static_cast<const uint16_t*>(a.Kc) + (size_t)bh * a.cap * DK;
+  const uint16_t* Vh = static_cast<const uint16_t*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const int32_t* ntok = a.ntok + (size_t)bh * a.T;
+
+  const int qb0 = qb * BM;
+  const int nlo = ntok[qb0];                               // every query of the block sees c < nlo
+  const int nhi = ntok[min(a.T - 1, qb0 + BM - 1)];        // no query sees c >= nhi
+
+  int tq[QT], nq[QT];
+  bf16x8 qf[QT][KSD];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    tq[qt] = qb0 + wave * BMW + 16 * qt + qn;
+    const bool ok = tq[qt] < a.T;
+    nq[qt] = ok ? ntok[tq[qt]] : 0;
+    const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      u16x8 x = (u16x8)(0);
+      if (ok) x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
+      qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  u16x8 kreg[KPT];
+  uint32_t vreg[VPT][8];
+  auto load_tile = [&](int c0) {
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int u = tid + p * 256;
+      const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
+      kreg[p] = (u16x8)(0);
+      if (c0 + row < nhi) kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)(c0 + row) * DK + col);
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int u = tid + p * 256;
+      const int dp = u % (DV / 2), kg = u / (DV / 2);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int c = c0 + kg * 8 + r;
+        vreg[p][r] = 0u;
+        if (c < nhi) vreg[p][r] = *reinterpret_cast<const uint32_t*>(Vh + (size_t)c * DV + 2 * dp);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int u = tid + p * 256;
+      const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
+      *reinterpret_cast<u16x8*>(&Ks[buf][row * KS + col]) = kreg[p];
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int u = tid + p * 256;
+      const int dp = u % (DV / 2), kg = u / (DV / 2);
+      u16x8 lo, hi;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        lo[r] = (uint16_t)(vreg[p][r] & 0xffffu);
+        hi[r] = (uint16_t)(vreg[p][r] >> 16);
+      }
+      *reinterpret_cast<u16x8*>(&Vt[buf][(2 * dp) * VS + kg * 8]) = lo;
+      *reinterpret_cast<u16x8*>(&Vt[buf][(2 * dp + 1) * VS + kg * 8]) = hi;
+    }
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run[QT], l_run[QT];
+  f32x4 acc[QT][DT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = (f32x4)(0.f);
+  }
+
+  const int ntiles = (nhi + BN - 1) / BN;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int c0 = it * BN;
+    if (it + 1 < ntiles) load_tile(c0 + BN);
+    const uint16_t* K_ = Ks[buf];
+    const uint16_t* V_ = Vt[buf];
+
+    f32x4 st[QT][NKT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) st[qt][kt] = (f32x4)(0.f);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const bf16x8 kx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&K_[(kt * 16 + qn) * KS + ks * 32 + 8 * g]));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
+      }
+
+    const bool full = (c0 + BN) <= nlo;      // no key of this tile is masked for any query
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sv = st[qt][kt][i] * sl2;
+          if (!full && (c0 + kt * 16 + 4 * g + i) >= nq[qt]) sv = -INFINITY;
+          st[qt][kt][i] = sv;
+          tmax = fmaxf(tmax, sv);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run[qt], tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = exp2f(m_run[qt] - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = exp2f(st[qt][kt][i] - m_use);
+          st[qt][kt][i] = pr;
+          psum += pr;
+        }
+      l_run[qt] = l_run[qt] * corr + psum;
+      m_run[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= corr;
+    }
+
+#pragma unroll
+    for (int u = 0; u < NKT / 2; ++u) {
+      bf16x8 pb[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[qt][i] = static_cast<__bf16>(st[qt][2 * u][i]);
+          pb[qt][4 + i] = static_cast<__bf16>(st[qt][2 * u + 1][i]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vrow = &V_[(dt * 16 + qn) * VS];
+        const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 4 * g);
+        const u16x4 v1 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 16 + 4 * g);
+        u16x8 va;
+        va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+        va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[qt], acc[qt][dt], 0, 0, 0);
+      }
+    }
+    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int t = tq[qt];
+    const bool tvalid = t < a.T;
+    const size_t tt = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
+    float okv[DT][4], orn[DT][4];
+    float ssk = 0.f, ssr = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 r4 = (f32x4)(0.f);
+      if (tvalid) r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        okv[dt][i] = acc[qt][dt][i] * inv_l;
+        orn[dt][i] = r4[i];
+        ssk += okv[dt][i] * okv[dt][i];
+        ssr += orn[dt][i] * orn[dt][i];
+      }
+    }
+    ssk += __shfl_xor(ssk, 16, kWave);
+    ssk += __shfl_xor(ssk, 32, kWave);
+    ssr += __shfl_xor(ssr, 16, kWave);
+    ssr += __shfl_xor(ssr, 32, kWave);
+    if (!tvalid) continue;
+    const float gr = a.gate_rnn ? a.gate_rnn[tt] : 1.f;
+    const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
+    const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
+    const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
+    uint16_t* o = static_cast<uint16_t*>(a.o);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
+      const size_t off = tt * DV + dt * 16 + 4 * g;
+      IoBF16::store4(o, off, y);
+      if (a.o_kv) IoBF16::store4(static_cast<uint16_t*>(a.o_kv), off, okv[dt]);
+      if (a.o_rnn) IoBF16::store4(static_cast<uint16_t*>(a.o_rnn), off, orn[dt]);
+    }
+  }
+}
+
+template <int DK, int DV>
+static hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  constexpr int QT = 2, BM = 64 * QT;
+  const int nqb = (a.T + BM - 1) / BM;
+  hipLaunchKernelGGL((attn_bf16_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <class IO, int DK, int DV>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.T + 63) / 64;
@@ -295,7 +546,10 @@ hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
   } else {
-    HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+    if (dk == 64 && dv == 64) return launch_attn_bf16<64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_attn_bf16<64, 128>(a, s);
+    if (dk == 128 && dv == 64) return launch_attn_bf16<128, 64>(a, s);
+    if (dk == 128 && dv == 128) return launch_attn_bf16<128, 128>(a, s);
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;
