@@ -1,0 +1,168 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times, against the CPU oracle on everything it can afford: every routing score,
+routing decision, compaction entry and final state of every head (RNN-only oracle
+pass), and the attention outputs at sampled tokens of sampled heads.
+
+Workloads: the layer at the 800M-model shape (B=8, H=16, d=128, T=4096, bf16 I/O,
+rho = 0.5 and the two rho limits); the long-context case (B=1, H=16, T=32768,
+planted repeated pairs, rho = 0.25); the decode case (batch 32, H=16, d=128,
+32K-token prefix, then decode steps).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import attention_sequence_mixing_amd as ham
+from attention_sequence_mixing_amd.inputs import (LAYER, LONG, DECODE_B, DECODE_D, DECODE_H,
+                                                  DECODE_PREFIX, make_inputs_torch, make_workload,
+                                                  tau_for_rho)
+from parity import E_TOL, NEAR, TOL, np_of, rel_err_slices, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = torch.device("cuda:0")
+INF = np.float32(np.inf)
+
+
+def _rnn_only_oracle(inp, tau, scale, cap=None):
+    """Oracle over all heads with no attention readout (emit all-zero)."""
+    B, T, H, _ = inp["q"].shape
+    return oracle.forward(**inp, tau=tau, scale=scale, cap=cap, emit=np.zeros((B, T, H), np.int8))
+
+
+def _check_all_heads(out, ref, tau):
+    """Scores, routing, compaction and state of every head."""
+    e_gpu = out["e"].cpu().numpy()
+    r_gpu = out["routed"].cpu().numpy().astype(bool)
+    de = np.abs(e_gpu - ref["e"]).max()
+    assert de < E_TOL, f"score error {de:.3e}"
+    H = e_gpu.shape[2]
+    near = np.abs(ref["e"] - np.asarray(tau, np.float64).reshape(1, 1, H)) < NEAR
+    flips = r_gpu != ref["routed"].astype(bool)
+    assert not (flips & ~near).any(), f"{int((flips & ~near).sum())} flips outside the near band"
+    nflip_heads = flips.any(axis=1)                      # [B,H]
+    cnt = out["count"].cpu().numpy()
+    pos = out["pos"].cpu().numpy()
+    Kc, Vc = out["Kc"], out["Vc"]
+    B = cnt.shape[0]
+    for b in range(B):
+        for h in range(H):
+            if nflip_heads[b, h]:
+                # routing differs only inside the band: compaction must be the GPU mask's nonzeros
+                nz = np.nonzero(r_gpu[b, :, h])[0]
+                assert cnt[b, h] == len(nz)
+                assert np.array_equal(pos[b, h, :len(nz)], nz)
+                continue
+            n = int(ref["count"][b, h])
+            assert cnt[b, h] == n
+            assert np.array_equal(pos[b, h, :n], ref["pos"][b, h, :n])
+            assert np.array_equal(np_of(Kc[b, h, :n]), ref["Kc"][b, h, :n])
+            assert np.array_equal(np_of(Vc[b, h, :n]), ref["Vc"][b, h, :n])
+    errS = rel_err_slices(np_of(out["S"]), ref["S"], 1)
+    assert errS < 1e-4, errS
+    return int(flips.sum()), float(de)
+
+
+def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu):
+    """Oracle outputs at sampled tokens of sampled heads (with the GPU mask if it
+    differs from the oracle's inside the near band)."""
+    T = inp["q"].shape[1]
+    rng = np.random.default_rng(seed)
+    worst = {}
+    for (b, h) in heads:
+        sub = {n: np.ascontiguousarray(a[b:b + 1, :, h:h + 1]) for n, a in inp.items()}
+        toks = np.unique(np.concatenate([rng.choice(T, ntok, replace=False), [0, T - 1]]))
+        emit = np.zeros((1, T, 1), np.int8)
+        emit[0, toks, 0] = 1
+        ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit,
+                             mask_override=r_gpu[b:b + 1, :, h:h + 1])
+        for name in ("o", "o_rnn", "o_kv"):
+            x = np_of(out[name][b, toks, h])
+            y = ref[name][0, toks, 0]
+            err = np.abs(x - y).max() / max(np.abs(y).max(), 1e-30)
+            worst[name] = max(worst.get(name, 0.0), float(err))
+            assert err < TOL[dtype], (name, b, h, err)
+    return worst
+
+
+@pytest.mark.parametrize("rho", [0.5, 0.0, 1.0])
+def test_layer_fullsize(rho):
+    w = LAYER
+    inp = make_workload(w)
+    scale = w.attn_scale
+    tau0 = np.full(w.H, INF, np.float32)
+    base = _rnn_only_oracle(inp, tau0, scale)
+    tau = tau_for_rho(base["e"], rho)
+    ref = _rnn_only_oracle(inp, tau, scale)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    nflip, de = _check_all_heads(out, ref, tau)
+    r_gpu = out["routed"].cpu().numpy()
+    got_rho = float(out["count"].sum()) / (w.B * w.T * w.H)
+    assert abs(got_rho - rho) <= (nflip + 1) / (w.B * w.T * w.H)
+    worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 0), (3, 7), (7, 15)], 24,
+                                   torch.bfloat16, 40, r_gpu)
+    print(f"layer rho={rho}: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
+
+
+def test_long_context_fullsize():
+    w = LONG
+    inp = make_workload(w)
+    scale = w.attn_scale
+    base = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(base["e"], w.rho)
+    ref = _rnn_only_oracle(inp, tau, scale)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    nflip, de = _check_all_heads(out, ref, tau)
+    worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 0), (0, 9)], 16, torch.bfloat16, 41,
+                                   out["routed"].cpu().numpy())
+    print(f"long: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
+
+
+def test_decode_fullsize_sampled_heads():
+    B, H, d, T0, steps = DECODE_B, DECODE_H, DECODE_D, DECODE_PREFIX, 8
+    scale = d ** -0.5
+    tau = np.full(H, 1.0, np.float32)        # a fixed threshold near the median score
+    pre = make_inputs_torch(B, T0, H, d, dtype="bf16", seed=4, device=DEV)
+    x = make_inputs_torch(steps, B, H, d, dtype="bf16", seed=5, device=DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+    plan = ham.ForwardPlan(B, T0, H, d, d, torch.bfloat16, DEV, cap=T0 + steps, scale=scale)
+    plan(pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"], tau_d)
+    dplan = ham.DecodePlan(B, H, d, d, T0 + steps, torch.bfloat16, DEV, scale=scale)
+    outs, es, rs = [], [], []
+    for s in range(steps):
+        dplan(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s], tau_d, plan.S, plan.Kc,
+              plan.Vc, plan.pos, plan.count, torch.full((B,), T0 + s, dtype=torch.int32, device=DEV))
+        outs.append(np_of(dplan.o)); es.append(dplan.e.cpu().numpy()); rs.append(dplan.routed.cpu().numpy())
+    torch.cuda.synchronize()
+    assert int(dplan.status.item()) == 0
+    e_pre = plan.e.cpu().numpy()
+    r_pre = plan.routed.cpu().numpy()
+    for (b, h) in [(0, 0), (5, 3), (17, 11), (31, 15)]:
+        sub = {n: np.concatenate([np_of(pre[n][b:b + 1, :, h:h + 1]),
+                                  np_of(x[n][:, b, h]).reshape((1, steps, 1) + x[n].shape[3:])], axis=1)
+               for n in ("q", "k", "v", "beta", "g")}
+        T = T0 + steps
+        emit = np.zeros((1, T, 1), np.int8)
+        emit[0, T0:, 0] = 1
+        e_all = np.concatenate([e_pre[b, :, h], np.array([e[b, h] for e in es])])
+        r_all = np.concatenate([r_pre[b, :, h], np.array([r[b, h] for r in rs])]).astype(np.int8)
+        ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit)
+        assert np.abs(e_all - ref["e"][0, :, 0]).max() < E_TOL
+        near = np.abs(ref["e"][0, :, 0] - tau[h]) < NEAR
+        assert not ((r_all.astype(bool) != ref["routed"][0, :, 0].astype(bool)) & ~near).any()
+        if not np.array_equal(r_all, ref["routed"][0, :, 0]):
+            ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit,
+                                 mask_override=r_all.reshape(1, T, 1))
+        assert int(plan.count[b, h].item()) == int(ref["count"][0, 0])
+        o_dec = np.stack([o[b, h] for o in outs])
+        y = ref["o"][0, T0:, 0]
+        err = np.abs(o_dec - y).max() / np.abs(y).max()
+        assert err < TOL[torch.bfloat16], (b, h, err)
+        errS = np.abs(np_of(plan.S[b, h]) - ref["S"][0, 0]).max() / np.abs(ref["S"][0, 0]).max()
+        assert errS < 1e-4, errS
