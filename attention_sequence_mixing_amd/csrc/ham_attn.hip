@@ -291,11 +291,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // built with 4-byte loads (two adjacent d of one key; each load instruction of a
 // wave reads 256 contiguous bytes of one row) packed into 16-byte LDS stores of
 // eight consecutive keys.
+//
+// Softmax: the running maximum is kept in log2 units of the scaled logits
+// (scale > 0, so the maximum of the raw scores gives it); the accumulators are
+// rescaled only when some query's maximum grows by more than 2^8, otherwise the
+// stale maximum is kept (probabilities up to 2^8 are exact enough in fp32/bf16 and
+// the final division by the running sum cancels the common factor).
+constexpr float kLazyRescale = 8.0f;
+
 template <int DK, int DV, int QT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
   constexpr int BMW = 16 * QT, BM = 4 * BMW;
-  constexpr int KS = DK + 8, VS = BN + 8;
+  constexpr int KS = DK + 8, VS = BN + 4;
   constexpr int KU = BN * DK / 8, KPT = KU / 256;            // 16-byte K units per thread
   constexpr int VU = (DV / 2) * (BN / 8), VPT = VU / 256;     // (d pair, 8-key group) units
   static_assert(KU % 256 == 0 && VU % 256 == 0, "tile does not split evenly");
@@ -329,21 +337,23 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
-      u16x8 x = (u16x8)(0);
-      if (ok) x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
+      u16x8 x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
       qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
+  // Tile staging.  Rows at or beyond nhi are never visible: K rows there are read
+  // from a clamped in-range row and masked through the scores; V rows are zeroed
+  // so that p = 0 multiplies finite values.
   u16x8 kreg[KPT];
   uint32_t vreg[VPT][8];
+  const int rmax = a.cap - 1;
   auto load_tile = [&](int c0) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
       const int u = tid + p * 256;
       const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
-      kreg[p] = (u16x8)(0);
-      if (c0 + row < nhi) kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)(c0 + row) * DK + col);
+      kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)min(c0 + row, rmax) * DK + col);
     }
 #pragma unroll
     for (int p = 0; p < VPT; ++p) {
@@ -352,8 +362,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int c = c0 + kg * 8 + r;
-        vreg[p][r] = 0u;
-        if (c < nhi) vreg[p][r] = *reinterpret_cast<const uint32_t*>(Vh + (size_t)c * DV + 2 * dp);
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(Vh + (size_t)min(c, rmax) * DV + 2 * dp);
+        vreg[p][r] = (c < nhi) ? x : 0u;
       }
     }
   };
@@ -379,8 +389,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  const float sl2 = a.scale * kLog2e;
-  float m_run[QT], l_run[QT];
+  const float sl2 = a.scale * kLog2e;        // > 0
+  float m_run[QT], l_run[QT];                // m_run in scaled log2 units
   f32x4 acc[QT][DT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -418,37 +428,52 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
           st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
       }
 
-    const bool full = (c0 + BN) <= nlo;      // no key of this tile is masked for any query
+    if ((c0 + BN) > nlo) {                   // some key of this tile is masked for some query
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((c0 + kt * 16 + 4 * g + i) >= nq[qt]) st[qt][kt][i] = -INFINITY;
+    }
+    bool grow = false;
+    float m_new[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv = st[qt][kt][i] * sl2;
-          if (!full && (c0 + kt * 16 + 4 * g + i) >= nq[qt]) sv = -INFINITY;
-          st[qt][kt][i] = sv;
-          tmax = fmaxf(tmax, sv);
-        }
+        tmax = fmaxf(tmax, fmaxf(fmaxf(st[qt][kt][0], st[qt][kt][1]), fmaxf(st[qt][kt][2], st[qt][kt][3])));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[qt], tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = exp2f(m_run[qt] - m_use);
+      m_new[qt] = tmax * sl2;
+      grow |= m_new[qt] > m_run[qt] + kLazyRescale;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mn = fmaxf(m_run[qt], m_new[qt]);
+        const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - mn);
+        l_run[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= corr;
+        m_run[qt] = mn;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = exp2f(st[qt][kt][i] - m_use);
+          const float pr = __builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], sl2, mneg));
           st[qt][kt][i] = pr;
           psum += pr;
         }
-      l_run[qt] = l_run[qt] * corr + psum;
-      m_run[qt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= corr;
+      l_run[qt] += psum;
     }
 
 #pragma unroll
@@ -492,8 +517,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     float ssk = 0.f, ssr = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      f32x4 r4 = (f32x4)(0.f);
-      if (tvalid) r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+      const f32x4 r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         okv[dt][i] = acc[qt][dt][i] * inv_l;

@@ -20,12 +20,8 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 // ---- bf16 <-> fp32 ---------------------------------------------------------------
 HAM_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-HAM_DEVICE uint16_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
-  return (uint16_t)(u >> 16);
-}
+// nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950)
+HAM_DEVICE uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 
 // ---- element type of q/k/v/cache/outputs ----------------------------------------
 // IoF32: float elements.  IoBF16: bf16 bit patterns (uint16_t).

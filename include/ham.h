@@ -66,7 +66,7 @@ typedef struct {
     int B, T, H;      /* batch, new tokens per sequence, heads                   */
     int dk, dv;       /* key and value head sizes (64 or 128 each)               */
     int io_dtype;     /* HAM_F32 or HAM_BF16                                      */
-    float scale;      /* attention logit scale (the usual choice is 1/sqrt(dk))  */
+    float scale;      /* attention logit scale, > 0 (usually 1/sqrt(dk))         */
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
     int cap;          /* KV-cache capacity per (b,h), in tokens                   */
     int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT                       */

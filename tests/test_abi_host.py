@@ -69,6 +69,8 @@ def test_forward_argument_errors():
     assert _fwd(dims(B=0)) == _lib.HAM_EINVAL
     assert _fwd(dims(io_dtype=3)) == _lib.HAM_EUNSUPPORTED
     assert _fwd(dims(flags=8)) == _lib.HAM_EUNSUPPORTED
+    assert _fwd(dims(scale=0.0)) == _lib.HAM_EINVAL and "scale" in _msg()
+    assert _fwd(dims(scale=-1.0)) == _lib.HAM_EINVAL
     # required pointers: q k v (0-2), beta g tau (6-8), S_out (12), o (13), Kc Vc pos count (18-21)
     for i in (0, 1, 2, 6, 7, 8, 12, 13, 18, 19, 20, 21):
         a = list(base)
