@@ -75,6 +75,17 @@ HAM_DEVICE float wave_max(float x) {
 
 HAM_DEVICE int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15), result in every lane of
+// the row: swap neighbours, swap pairs (quad permutes), then mirror within 8 and 16
+// lanes.  Pure VALU (no LDS crossbar traffic).
+HAM_DEVICE float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
 // ---- XCD-aware workgroup order ----------------------------------------------------
 // The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical ids: neighbouring tiles

@@ -84,11 +84,10 @@ template <int DK, int NW>
 struct ChunkSmem {
   static constexpr int KS = DK + 8;        // row stride (u16) of K and Q
   static constexpr int TS = kC + 8;        // row stride (u16) of K^T
-  static constexpr int VS = 16 * NW + 8;   // row stride (u16) of the V slice
   uint16_t K[kC * KS];
   uint16_t Q[kC * KS];
   uint16_t Kt[DK * TS];
-  uint16_t V[kC * VS];
+  uint16_t Vt[16 * NW * TS];               // this workgroup's V columns, transposed
   // MFMA A-operand fragments in lane order, one 16-byte entry per lane:
   //   A  = strict_lower(Gamma o K K^T)          6 (row-tile, k-step) pairs x 3 splits
   //   QK = Gamma o Q K^T o lower_incl          6 pairs x 2 splits
@@ -96,22 +95,31 @@ struct ChunkSmem {
   bf16x8 QKf[6][2][kWave];
   float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
   float Td[4][16][20];                     // (I + Ld)^-1 diag(beta) per block
-  float G2[kC], gam[kC], beta[kC], wdec[kC];
+  alignas(16) float G2[kC];
+  alignas(16) float gam[kC];
+  alignas(16) float beta[kC];
+  alignas(16) float wdec[kC];
 };
 
 // Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
 HAM_DEVICE constexpr int pair_index(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 + s : 4 + s; }
 
 // Per-thread register stage of one chunk's inputs (prefetched one chunk ahead).
-// Units are 16 bytes; unit u covers token u % 64 and 8 consecutive elements.
+// K and V are fetched as (adjacent pair of elements, 8 consecutive tokens) units
+// with 4-byte loads -- a wave's load instruction reads contiguous bytes of one
+// token row -- so that the transposed copies K^T and V^T are written with 16-byte
+// stores.  Q only needs its row-major copy (16-byte units, token-major).
 template <int DK, int NW>
 struct ChunkRegs {
   static constexpr int NT = 64 * NW;
-  static constexpr int KU = kC * (DK / 8);
+  static constexpr int KU = (DK / 2) * (kC / 8);        // (d pair, token group) units of K
   static constexpr int KPT = (KU + NT - 1) / NT;
-  static constexpr int VU = kC * 2 * NW;
+  static constexpr int QU = kC * (DK / 8);              // 16-byte units of Q
+  static constexpr int QPT = (QU + NT - 1) / NT;
+  static constexpr int VU = (8 * NW) * (kC / 8);        // (column pair, token group) units of V
   static constexpr int VPT = (VU + NT - 1) / NT;
-  u16x8 k[KPT], q[KPT], v[VPT];
+  uint32_t k[KPT][8], v[VPT][8];
+  u16x8 q[QPT];
   float g, beta;
 };
 
@@ -123,34 +131,75 @@ HAM_DEVICE void load_chunk(const RnnArgs& a, ChunkRegs<DK, NW>& r, int b, int h,
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   const int nvalid = min(kC, a.T - t0);
+  const size_t rowstride = (size_t)a.H;                 // tokens are H rows apart
+  const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
+  static_assert(R::KU % R::NT == 0 && R::VU % R::NT == 0 && R::QU % R::NT == 0, "uneven staging");
+  if (nvalid == kC) {                       // full chunk: no per-load conditions
 #pragma unroll
-  for (int p = 0; p < R::KPT; ++p) {
-    const int u = tid + p * R::NT;
-    const int row = u % kC, cu = (u / kC) * 8;
-    r.k[p] = (u16x8)(0);
-    r.q[p] = (u16x8)(0);
-    if (u < R::KU && row < nvalid) {
-      const size_t tok = ((size_t)b * a.T + t0 + row) * a.H + h;
-      r.k[p] = *reinterpret_cast<const u16x8*>(k + tok * DK + cu);
-      if (readout) r.q[p] = *reinterpret_cast<const u16x8*>(q + tok * DK + cu);
+    for (int p = 0; p < R::KPT; ++p) {
+      const int u = tid + p * R::NT;
+      const int dp = u % (DK / 2), tg = u / (DK / 2);
+      const uint16_t* src = k + (tok0 + (size_t)(tg * 8) * rowstride) * DK + 2 * dp;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        r.k[p][j] = *reinterpret_cast<const uint32_t*>(src + (size_t)j * rowstride * DK);
     }
-  }
 #pragma unroll
-  for (int p = 0; p < R::VPT; ++p) {
-    const int u = tid + p * R::NT;
-    const int row = u % kC, cu = (u / kC) * 8;
-    r.v[p] = (u16x8)(0);
-    if (u < R::VU && row < nvalid) {
-      const size_t tok = ((size_t)b * a.T + t0 + row) * a.H + h;
-      r.v[p] = *reinterpret_cast<const u16x8*>(v + tok * DV + colbase + cu);
+    for (int p = 0; p < R::VPT; ++p) {
+      const int u = tid + p * R::NT;
+      const int cp = u % (8 * NW), tg = u / (8 * NW);
+      const uint16_t* src = v + (tok0 + (size_t)(tg * 8) * rowstride) * DV + colbase + 2 * cp;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        r.v[p][j] = *reinterpret_cast<const uint32_t*>(src + (size_t)j * rowstride * DV);
+    }
+    if (readout) {
+#pragma unroll
+      for (int p = 0; p < R::QPT; ++p) {
+        const int u = tid + p * R::NT;
+        const int row = u % kC, cu = (u / kC) * 8;
+        r.q[p] = *reinterpret_cast<const u16x8*>(q + (tok0 + row * rowstride) * DK + cu);
+      }
+    }
+  } else {                                  // tail chunk: zero the rows past T
+#pragma unroll
+    for (int p = 0; p < R::KPT; ++p) {
+      const int u = tid + p * R::NT;
+      const int dp = u % (DK / 2), tg = u / (DK / 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = tg * 8 + j;
+        r.k[p][j] = 0u;
+        if (row < nvalid)
+          r.k[p][j] = *reinterpret_cast<const uint32_t*>(k + (tok0 + row * rowstride) * DK + 2 * dp);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < R::VPT; ++p) {
+      const int u = tid + p * R::NT;
+      const int cp = u % (8 * NW), tg = u / (8 * NW);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = tg * 8 + j;
+        r.v[p][j] = 0u;
+        if (row < nvalid)
+          r.v[p][j] = *reinterpret_cast<const uint32_t*>(v + (tok0 + row * rowstride) * DV + colbase + 2 * cp);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < R::QPT; ++p) {
+      const int u = tid + p * R::NT;
+      const int row = u % kC, cu = (u / kC) * 8;
+      r.q[p] = (u16x8)(0);
+      if (readout && row < nvalid)
+        r.q[p] = *reinterpret_cast<const u16x8*>(q + (tok0 + row * rowstride) * DK + cu);
     }
   }
   r.g = 0.f;
   r.beta = 0.f;
   if (tid < kC && tid < nvalid) {
-    const size_t tok = ((size_t)b * a.T + t0 + tid) * a.H + h;
-    r.g = a.g[tok];
-    r.beta = a.beta[tok];
+    r.g = a.g[tok0 + tid * rowstride];
+    r.beta = a.beta[tok0 + tid * rowstride];
   }
 }
 
@@ -161,20 +210,40 @@ HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, i
 #pragma unroll
   for (int p = 0; p < R::KPT; ++p) {
     const int u = tid + p * R::NT;
-    if (u < R::KU) {
-      const int row = u % kC, cu = (u / kC) * 8;
-      *reinterpret_cast<u16x8*>(&sm.K[row * SM::KS + cu]) = r.k[p];
-      *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
+    {
+      const int dp = u % (DK / 2), tg = u / (DK / 2);
+      u16x8 lo, hi;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.Kt[(cu + j) * SM::TS + row] = r.k[p][j];
+      for (int j = 0; j < 8; ++j) {
+        lo[j] = (uint16_t)(r.k[p][j] & 0xffffu);
+        hi[j] = (uint16_t)(r.k[p][j] >> 16);
+        *reinterpret_cast<uint32_t*>(&sm.K[(tg * 8 + j) * SM::KS + 2 * dp]) = r.k[p][j];
+      }
+      *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp) * SM::TS + tg * 8]) = lo;
+      *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp + 1) * SM::TS + tg * 8]) = hi;
     }
   }
 #pragma unroll
   for (int p = 0; p < R::VPT; ++p) {
     const int u = tid + p * R::NT;
-    if (u < R::VU) {
+    {
+      const int cp = u % (8 * NW), tg = u / (8 * NW);
+      u16x8 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo[j] = (uint16_t)(r.v[p][j] & 0xffffu);
+        hi[j] = (uint16_t)(r.v[p][j] >> 16);
+      }
+      *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp) * SM::TS + tg * 8]) = lo;
+      *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp + 1) * SM::TS + tg * 8]) = hi;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < R::QPT; ++p) {
+    const int u = tid + p * R::NT;
+    {
       const int row = u % kC, cu = (u / kC) * 8;
-      *reinterpret_cast<u16x8*>(&sm.V[row * SM::VS + cu]) = r.v[p];
+      *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
     }
   }
   if (tid < kC) {
@@ -215,11 +284,13 @@ HAM_DEVICE void gram_fragment(ChunkSmem<DK, NW>& sm, int mt, int s, int g, int n
       }
     }
     const int t = 16 * mt + n;
+    const float gt = sm.G2[t];
+    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G2[16 * jt + 4 * g]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * jt + 4 * g + i;
       const bool keep = kQK ? (j <= t) : (j < t);
-      val[hh][i] = keep ? acc[i] * exp2f(sm.G2[t] - sm.G2[j]) : 0.f;
+      val[hh][i] = keep ? acc[i] * __builtin_amdgcn_exp2f(gt - gj[i]) : 0.f;
       if (!kQK && jt == mt) sm.Ld[mt][n][4 * g + i] = sm.beta[t] * val[hh][i];
     }
   }
@@ -280,7 +351,7 @@ HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, 
 template <int DK, int DV, int NW>
 __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   using SM = ChunkSmem<DK, NW>;
-  constexpr int KS = SM::KS, TS = SM::TS, VS = SM::VS;
+  constexpr int KS = SM::KS, TS = SM::TS;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
   constexpr int NSL = DV / 16;    // score slices
@@ -321,7 +392,10 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     __syncthreads();
 
     // ---- decayed Gram fragments, shared through LDS in lane order ----
-    for (int f = wave; f < nfrag; f += NW) {
+#pragma unroll
+    for (int rep = 0; rep < (12 + NW - 1) / NW; ++rep) {
+      const int f = wave + rep * NW;
+      if (f >= nfrag) break;
       const int pi = f % 6;
       const int mt = pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3;
       const int s = pi < 2 ? 0 : (pi - 2) & 1;
@@ -336,10 +410,11 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       float colv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float sacc = (r == cc) ? 1.f : 0.f;
+        // four independent partial sums shorten the dependent chain of each row
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < r; ++j) sacc = fmaf(-sm.Ld[bb][r][j], colv[j], sacc);
-        colv[r] = sacc;
+        for (int j = 0; j < r; ++j) part[j & 3] = fmaf(sm.Ld[bb][r][j], colv[j], part[j & 3]);
+        colv[r] = ((r == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
       }
       const float bc = sm.beta[16 * bb + cc];
 #pragma unroll
@@ -347,42 +422,44 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
 
     // ---- Y_K = K S, Y_Q = Q S (independent of the inverse) ----
-    bf16x8 sh[KSD], smd[KSD], sl[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) split_pair3(S[2 * ks], S[2 * ks + 1], sh[ks], smd[ks], sl[ks]);
     f32x4 P[4], O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       P[mt] = (f32x4)(0.f);
       O[mt] = (f32x4)(0.f);
+    }
 #pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
+    for (int ks = 0; ks < KSD; ++ks) {
+      bf16x8 sh, smd, sl;
+      split_pair3(S[2 * ks], S[2 * ks + 1], sh, smd, sl);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
         const uint16_t* kr = &sm.K[(16 * mt + n) * KS + 32 * ks + 4 * g];
         const bf16x8 af = frag2(kr, kr + 16);
-        P[mt] = mfma_bf16(af, sl[ks], P[mt]);
-        P[mt] = mfma_bf16(af, smd[ks], P[mt]);
-        P[mt] = mfma_bf16(af, sh[ks], P[mt]);
+        P[mt] = mfma_bf16(af, sl, P[mt]);
+        P[mt] = mfma_bf16(af, smd, P[mt]);
+        P[mt] = mfma_bf16(af, sh, P[mt]);
         if (readout) {
           const uint16_t* qr = &sm.Q[(16 * mt + n) * KS + 32 * ks + 4 * g];
           const bf16x8 qf = frag2(qr, qr + 16);
-          O[mt] = mfma_bf16(qf, smd[ks], O[mt]);
-          O[mt] = mfma_bf16(qf, sh[ks], O[mt]);
+          O[mt] = mfma_bf16(qf, smd, O[mt]);
+          O[mt] = mfma_bf16(qf, sh, O[mt]);
         }
       }
     }
-    f32x4 X[4], Vr[4];
+    f32x4 X[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[16 * mt + 4 * g]);
+      const u16x4 v4 = *reinterpret_cast<const u16x4*>(&sm.Vt[vcol * TS + 16 * mt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g + i;
-        const float gm = sm.gam[t];
-        const float vv = bf16_to_f32(sm.V[t * VS + vcol]);
-        Vr[mt][i] = vv;
-        P[mt][i] *= gm;
-        O[mt][i] *= gm;
+        const float vv = bf16_to_f32(v4[i]);
+        P[mt][i] *= gm[i];
+        O[mt][i] *= gm[i];
         X[mt][i] = vv - P[mt][i];
       }
+    }
     __syncthreads();                          // Td is ready
 
     // ---- block forward substitution: D_i = T'_ii (X_i - sum_{j<i} A_ij D_j) ----
@@ -449,14 +526,15 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 
     // ---- score partials of this 16-column slice, and the readout ----
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const u16x4 v4 = *reinterpret_cast<const u16x4*>(&sm.Vt[vcol * TS + 16 * mt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * g + i;
-        float pv = P[mt][i] * Vr[mt][i], pp = P[mt][i] * P[mt][i], vv = Vr[mt][i] * Vr[mt][i];
-        pv = wave_sum<16>(pv);
-        pp = wave_sum<16>(pp);
-        vv = wave_sum<16>(vv);
+        const float vr = bf16_to_f32(v4[i]);
+        const float pv = row16_sum(P[mt][i] * vr);
+        const float pp = row16_sum(P[mt][i] * P[mt][i]);
+        const float vv = row16_sum(vr * vr);
         if (t < nvalid) {
           if (n == 0)
             a.score[((size_t)bh * a.T + t0 + t) * NSL + slice] = make_float4(pv, pp, vv, 0.f);
@@ -464,16 +542,19 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
             a.o_rnn32[(((size_t)b * a.T + t0 + t) * a.H + h) * DV + col] = O[mt][i];
         }
       }
+    }
 
     // ---- S <- gamma_C S + K^T diag(exp(G_C - G)) D ----
     bf16x8 eh[2], em[2], el[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float w0[4], w1[4];
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&sm.wdec[32 * s + 4 * g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&sm.wdec[32 * s + 16 + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        w0[i] = sm.wdec[32 * s + 4 * g + i];
-        w1[i] = sm.wdec[32 * s + 16 + 4 * g + i];
+        w0[i] = wa[i];
+        w1[i] = wb[i];
       }
       split_pair3(D[2 * s], D[2 * s + 1], eh[s], em[s], el[s], w0, w1);
     }
@@ -504,14 +585,10 @@ hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Four waves (64 state columns) per workgroup: the per-chunk prep work is split
+// four ways, which sets the latency of the sequential chunk loop.
 template <int DK, int DV>
-hipError_t launch_dims(const RnnArgs& a, hipStream_t s) {
-  // widest workgroup that still gives every CU a workgroup
-  const long heads = (long)a.B * a.H;
-  if (heads * (DV / 64) >= 256) return launch_t<DK, DV, 4>(a, s);
-  if (heads * (DV / 32) >= 256) return launch_t<DK, DV, 2>(a, s);
-  return launch_t<DK, DV, 1>(a, s);
-}
+hipError_t launch_dims(const RnnArgs& a, hipStream_t s) { return launch_t<DK, DV, 4>(a, s); }
 
 }  // namespace
 
