@@ -62,7 +62,7 @@ int check_dims(const ham_dims* d, bool need_T) {
 
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
 struct FwdLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, prep, total;
 };
 
 FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
@@ -78,6 +78,8 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.count_in = off;    off += up256(BH * sizeof(int32_t));
   L.ntok = off;        off += up256(BTH * sizeof(int32_t));
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
+  L.prep = off;
+  if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += BH * nchunk * ham::kPrepRecordBytes;
   L.total = off;
   return L;
 }
@@ -204,7 +206,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   int32_t* ntok = at<int32_t>(ws, L.ntok);
 
   CallTimer tm(0, s);
-  ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, d->B, d->T, d->H};
+  ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, at<char>(ws, L.prep), d->B, d->T, d->H};
   int slices = 0;
   rc = run_rnn(d, ra, s, &slices, tm);
   if (rc != HAM_OK) return rc;
@@ -256,7 +258,7 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   float* part = at<float>(ws, L.part);
 
   CallTimer tm(1, s);
-  ham::RnnArgs ra{q, k, v, beta, g, S, S, o_rnn32, score, d->B, 1, d->H};
+  ham::RnnArgs ra{q, k, v, beta, g, S, S, o_rnn32, score, nullptr, d->B, 1, d->H};
   HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
   tm.mark();
   ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, e_buf, r_buf, chunk_count,
@@ -302,7 +304,8 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   float* S_tmp = at<float>(ws, L.state);
 
   CallTimer tm(2, s);
-  ham::RnnArgs ra{q ? q : k, k, v, beta, g, S0, S_tmp, nullptr, score, d->B, d->T, d->H};
+  ham::RnnArgs ra{q ? q : k, k, v, beta, g, S0, S_tmp, nullptr, score, at<char>(ws, L.prep),
+                  d->B, d->T, d->H};
   int slices = 0;
   rc = run_rnn(d, ra, s, &slices, tm);
   if (rc != HAM_OK) return rc;

@@ -22,8 +22,12 @@ struct RnnArgs {
   float* S_out;         // [B,H,dk,dv]
   float* o_rnn32;       // [B,T,H,dv] fp32 or null (no readout)
   float4* score;        // [B*H][T][slices]
+  void* prep;           // chunked path: per-chunk records [B*H][nchunk][kPrepRecordBytes]
   int B, T, H;
 };
+
+// Bytes of one chunk record written by the chunked path's prep kernel.
+constexpr size_t kPrepRecordBytes = 35840;
 
 struct RouteArgs {
   const float4* score;  // [B*H][T][slices]

@@ -36,7 +36,7 @@
 #include "ham_internal.h"
 
 namespace ham {
-namespace {
+namespace chunked {
 
 constexpr int kC = 64;   // chunk length
 
@@ -80,29 +80,227 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Chunk record written by the prep kernel and streamed by the state kernel (all
+// offsets in bytes; 16-byte lane entries are in MFMA operand order):
+//   [0, 18432)       A  fragments: 6 (row tile, k-step) pairs x 3 splits x 64 lanes
+//   [18432, 30720)   QK fragments: 6 pairs x 2 splits x 64 lanes
+//   [30720, 34816)   T'_ii = (I + diag(beta) A_ii)^-1 diag(beta): 4 blocks x 64 lanes,
+//                    lane (g,n) holds row n, columns 4g..4g+3 (fp32)
+//   [34816, 35072)   gamma_t = exp(G_t)                (fp32 x 64)
+//   [35072, 35328)   w_t = exp(G_last - G_t)           (fp32 x 64)
+//   [35328, 35840)   padding to whole 1 KiB blocks
+constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 34816, kRecW = 35072;
+constexpr int kRecBlocks = (int)(kPrepRecordBytes / 1024);
+static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
+
+// Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
+HAM_DEVICE constexpr int pair_index(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 + s : 4 + s; }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+HAM_DEVICE f32x4 mfma_bf16_k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+HAM_DEVICE void split3x4(const float x[4], bf16x4& h, bf16x4& m, bf16x4& l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __bf16 a, b, c;
+    split3(x[i], a, b, c);
+    h[i] = a; m[i] = b; l[i] = c;
+  }
+}
+
+// Six-term fp32-accurate product accumulation: (ah+am+al)(bh+bm+bl), dropping the
+// terms below 2^-16 relative.
+template <class F, class V>
+HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, const V& bm, const V& bl, f32x4 c) {
+  c = mf(am, bm, c);
+  c = mf(al, bh, c);
+  c = mf(ah, bl, c);
+  c = mf(am, bh, c);
+  c = mf(ah, bm, c);
+  c = mf(ah, bh, c);
+  return c;
+}
+
+// ---------------------------------------------------------------------------------
+// Prep kernel: one workgroup (4 waves) per (b, h, chunk); chunks are independent.
+// Decayed Gram matrices (S2), their diagonal-block inverses (S3), gamma and the
+// state-update decays (S1).
+template <int DK>
+struct PrepSmem {
+  static constexpr int KS = DK + 8;
+  uint16_t K[kC * KS];
+  uint16_t Q[kC * KS];
+  float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
+  alignas(16) float Td[4][16][20];         // (I + Ld)^-1 diag(beta)
+  alignas(16) float G2[kC];
+  alignas(16) float beta[kC];
+};
+
+// One (row tile mt, k-step s) fragment of a decayed Gram matrix, computed
+// transposed so that the MFMA output already sits in A-operand order: lane (g,n)
+// ends with entries (t = 16mt + n, j = 32s + 16h + 4g + i) for half h, i = 0..3.
+template <int DK, bool kQK>
+HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g, int n, int lane) {
+  constexpr int KS = PrepSmem<DK>::KS;
+  const uint16_t* rowsT = kQK ? sm.Q : sm.K;
+  float val[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int jt = 2 * s + hh;
+    f32x4 acc = (f32x4)(0.f);
+    if (jt <= mt) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * jt + n) * KS + 32 * ks + 8 * g]));
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[(16 * mt + n) * KS + 32 * ks + 8 * g]));
+        acc = mfma_bf16(af, bf, acc);
+      }
+    }
+    const int t = 16 * mt + n;
+    const float gt = sm.G2[t];
+    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G2[16 * jt + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * jt + 4 * g + i;
+      const bool keep = kQK ? (j <= t) : (j < t);
+      val[hh][i] = keep ? acc[i] * __builtin_amdgcn_exp2f(gt - gj[i]) : 0.f;
+      if (!kQK && jt == mt) sm.Ld[mt][n][4 * g + i] = sm.beta[t] * val[hh][i];
+    }
+  }
+  const int pi = pair_index(mt, s);
+  if (kQK) {
+    bf16x8 h8, m8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = val[i >> 2][i & 3];
+      const __bf16 xh = to_bf16(x);
+      h8[i] = xh;
+      m8[i] = to_bf16(x - from_bf16(xh));
+    }
+    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecQK) + pi * 2 * kWave + lane;
+    dst[0] = h8;
+    dst[kWave] = m8;
+  } else {
+    bf16x8 h8, m8, l8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __bf16 x0, x1, x2;
+      split3(val[i >> 2][i & 3], x0, x1, x2);
+      h8[i] = x0; m8[i] = x1; l8[i] = x2;
+    }
+    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecA) + pi * 3 * kWave + lane;
+    dst[0] = h8;
+    dst[kWave] = m8;
+    dst[2 * kWave] = l8;
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
+  using SM = PrepSmem<DK>;
+  constexpr int KS = SM::KS;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nchunk = gridDim.x;
+  const int t0 = c * kC;
+  const int nvalid = min(kC, a.T - t0);
+  const bool readout = a.o_rnn32 != nullptr;
+  char* rec = static_cast<char*>(a.prep) + ((size_t)(b * a.H + h) * nchunk + c) * kPrepRecordBytes;
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k);
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
+
+  // stage K and Q rows (16-byte units, token-major), zero past T
+  for (int u = tid; u < kC * (DK / 8); u += 256) {
+    const int row = u % kC, cu = (u / kC) * 8;
+    u16x8 kx = (u16x8)(0), qx = (u16x8)(0);
+    if (row < nvalid) {
+      const size_t off = (tok0 + (size_t)row * a.H) * DK + cu;
+      kx = *reinterpret_cast<const u16x8*>(kp + off);
+      if (readout) qx = *reinterpret_cast<const u16x8*>(qp + off);
+    }
+    *reinterpret_cast<u16x8*>(&sm.K[row * KS + cu]) = kx;
+    *reinterpret_cast<u16x8*>(&sm.Q[row * KS + cu]) = qx;
+  }
+  if (wave == 0) {
+    float gv = 0.f, bv = 0.f;
+    if (lane < nvalid) {
+      gv = a.g[tok0 + (size_t)lane * a.H];
+      bv = a.beta[tok0 + (size_t)lane * a.H];
+    }
+    // inclusive prefix sum of the log decays over the chunk
+    float G = gv;
+#pragma unroll
+    for (int off = 1; off < kC; off <<= 1) {
+      const float y = __shfl_up(G, off, kWave);
+      if (lane >= off) G += y;
+    }
+    const float Glast = __shfl(G, kC - 1, kWave);
+    sm.G2[lane] = G * 1.4426950408889634f;
+    sm.beta[lane] = bv;
+    reinterpret_cast<float*>(rec + kRecGam)[lane] = expf(G);
+    reinterpret_cast<float*>(rec + kRecW)[lane] = expf(Glast - G);
+  }
+  __syncthreads();
+
+  const int nfrag = readout ? 12 : 6;
+#pragma unroll
+  for (int rep = 0; rep < 3; ++rep) {
+    const int f = wave + rep * 4;
+    if (f >= nfrag) break;
+    const int pi = f % 6;
+    const int mt = pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3;
+    const int s = pi < 2 ? 0 : (pi - 2) & 1;
+    if (f < 6) gram_fragment<DK, false>(sm, rec, mt, s, g, n, lane);
+    else gram_fragment<DK, true>(sm, rec, mt, s, g, n, lane);
+  }
+  __syncthreads();
+
+  // inverses of the four diagonal blocks by forward substitution (lane = block, column)
+  if (wave == 0) {
+    const int bb = lane >> 4, cc = lane & 15;
+    float colv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < r; ++j) part[j & 3] = fmaf(sm.Ld[bb][r][j], colv[j], part[j & 3]);
+      colv[r] = ((r == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
+    }
+    const float bc = sm.beta[16 * bb + cc];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.Td[bb][r][cc] = colv[r] * bc;
+  }
+  __syncthreads();
+  {
+    // lane order: entry (block i, lane (g,n)) = row n, columns 4g..4g+3
+    const int i = tid >> 6;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Td[i][n][4 * g]);
+    reinterpret_cast<f32x4*>(rec + kRecTd)[i * kWave + lane] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// State kernel: one workgroup = NW waves = 16*NW state columns of one head, walking
+// the chunks in order.  The chunk record is streamed into LDS one chunk ahead with
+// direct global-to-LDS loads; K, Q, K^T and this workgroup's V^T columns are staged
+// from registers prefetched one chunk ahead.
 template <int DK, int NW>
 struct ChunkSmem {
   static constexpr int KS = DK + 8;        // row stride (u16) of K and Q
-  static constexpr int TS = kC + 8;        // row stride (u16) of K^T
+  static constexpr int TS = kC + 8;        // row stride (u16) of K^T and V^T
   uint16_t K[kC * KS];
   uint16_t Q[kC * KS];
   uint16_t Kt[DK * TS];
   uint16_t Vt[16 * NW * TS];               // this workgroup's V columns, transposed
-  // MFMA A-operand fragments in lane order, one 16-byte entry per lane:
-  //   A  = strict_lower(Gamma o K K^T)          6 (row-tile, k-step) pairs x 3 splits
-  //   QK = Gamma o Q K^T o lower_incl          6 pairs x 2 splits
-  bf16x8 Af[6][3][kWave];
-  bf16x8 QKf[6][2][kWave];
-  float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
-  float Td[4][16][20];                     // (I + Ld)^-1 diag(beta) per block
-  alignas(16) float G2[kC];
-  alignas(16) float gam[kC];
-  alignas(16) float beta[kC];
-  alignas(16) float wdec[kC];
+  alignas(16) char rec[2][kPrepRecordBytes];
 };
-
-// Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
-HAM_DEVICE constexpr int pair_index(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 + s : 4 + s; }
 
 // Per-thread register stage of one chunk's inputs (prefetched one chunk ahead).
 // K and V are fetched as (adjacent pair of elements, 8 consecutive tokens) units
@@ -120,7 +318,6 @@ struct ChunkRegs {
   static constexpr int VPT = (VU + NT - 1) / NT;
   uint32_t k[KPT][8], v[VPT][8];
   u16x8 q[QPT];
-  float g, beta;
 };
 
 template <int DK, int DV, int NW>
@@ -195,12 +392,6 @@ HAM_DEVICE void load_chunk(const RnnArgs& a, ChunkRegs<DK, NW>& r, int b, int h,
         r.q[p] = *reinterpret_cast<const u16x8*>(q + (tok0 + row * rowstride) * DK + cu);
     }
   }
-  r.g = 0.f;
-  r.beta = 0.f;
-  if (tid < kC && tid < nvalid) {
-    r.g = a.g[tok0 + tid * rowstride];
-    r.beta = a.beta[tok0 + tid * rowstride];
-  }
 }
 
 template <int DK, int NW>
@@ -210,142 +401,36 @@ HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, i
 #pragma unroll
   for (int p = 0; p < R::KPT; ++p) {
     const int u = tid + p * R::NT;
-    {
-      const int dp = u % (DK / 2), tg = u / (DK / 2);
-      u16x8 lo, hi;
+    const int dp = u % (DK / 2), tg = u / (DK / 2);
+    u16x8 lo, hi;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lo[j] = (uint16_t)(r.k[p][j] & 0xffffu);
-        hi[j] = (uint16_t)(r.k[p][j] >> 16);
-        *reinterpret_cast<uint32_t*>(&sm.K[(tg * 8 + j) * SM::KS + 2 * dp]) = r.k[p][j];
-      }
-      *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp) * SM::TS + tg * 8]) = lo;
-      *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp + 1) * SM::TS + tg * 8]) = hi;
+    for (int j = 0; j < 8; ++j) {
+      lo[j] = (uint16_t)(r.k[p][j] & 0xffffu);
+      hi[j] = (uint16_t)(r.k[p][j] >> 16);
+      *reinterpret_cast<uint32_t*>(&sm.K[(tg * 8 + j) * SM::KS + 2 * dp]) = r.k[p][j];
     }
+    *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp) * SM::TS + tg * 8]) = lo;
+    *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp + 1) * SM::TS + tg * 8]) = hi;
   }
 #pragma unroll
   for (int p = 0; p < R::VPT; ++p) {
     const int u = tid + p * R::NT;
-    {
-      const int cp = u % (8 * NW), tg = u / (8 * NW);
-      u16x8 lo, hi;
+    const int cp = u % (8 * NW), tg = u / (8 * NW);
+    u16x8 lo, hi;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lo[j] = (uint16_t)(r.v[p][j] & 0xffffu);
-        hi[j] = (uint16_t)(r.v[p][j] >> 16);
-      }
-      *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp) * SM::TS + tg * 8]) = lo;
-      *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp + 1) * SM::TS + tg * 8]) = hi;
+    for (int j = 0; j < 8; ++j) {
+      lo[j] = (uint16_t)(r.v[p][j] & 0xffffu);
+      hi[j] = (uint16_t)(r.v[p][j] >> 16);
     }
+    *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp) * SM::TS + tg * 8]) = lo;
+    *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp + 1) * SM::TS + tg * 8]) = hi;
   }
 #pragma unroll
   for (int p = 0; p < R::QPT; ++p) {
     const int u = tid + p * R::NT;
-    {
-      const int row = u % kC, cu = (u / kC) * 8;
-      *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
-    }
+    const int row = u % kC, cu = (u / kC) * 8;
+    *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
   }
-  if (tid < kC) {
-    // inclusive prefix sum of the log decays over the chunk (wave 0)
-    float G = r.g;
-#pragma unroll
-    for (int off = 1; off < kC; off <<= 1) {
-      const float y = __shfl_up(G, off, kWave);
-      if (tid >= off) G += y;
-    }
-    const float Glast = __shfl(G, kC - 1, kWave);
-    sm.G2[tid] = G * 1.4426950408889634f;
-    sm.gam[tid] = expf(G);
-    sm.wdec[tid] = expf(Glast - G);
-    sm.beta[tid] = r.beta;
-  }
-}
-
-// One (row tile mt, k-step s) fragment of the decayed Gram matrix, computed
-// transposed so that the MFMA output already sits in A-operand order: lane (g,n)
-// ends with entries (t = 16mt + n, j = 32s + 16h + 4g + i) for half h, i = 0..3.
-template <int DK, int NW, bool kQK>
-HAM_DEVICE void gram_fragment(ChunkSmem<DK, NW>& sm, int mt, int s, int g, int n, int lane) {
-  using SM = ChunkSmem<DK, NW>;
-  constexpr int KS = SM::KS;
-  const uint16_t* rowsT = kQK ? sm.Q : sm.K;
-  float val[2][4];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int jt = 2 * s + hh;
-    f32x4 acc = (f32x4)(0.f);
-    if (jt <= mt) {
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * jt + n) * KS + 32 * ks + 8 * g]));
-        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[(16 * mt + n) * KS + 32 * ks + 8 * g]));
-        acc = mfma_bf16(af, bf, acc);
-      }
-    }
-    const int t = 16 * mt + n;
-    const float gt = sm.G2[t];
-    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G2[16 * jt + 4 * g]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * jt + 4 * g + i;
-      const bool keep = kQK ? (j <= t) : (j < t);
-      val[hh][i] = keep ? acc[i] * __builtin_amdgcn_exp2f(gt - gj[i]) : 0.f;
-      if (!kQK && jt == mt) sm.Ld[mt][n][4 * g + i] = sm.beta[t] * val[hh][i];
-    }
-  }
-  const int pi = pair_index(mt, s);
-  if (kQK) {
-    bf16x8 h8, m8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = val[i >> 2][i & 3];
-      const __bf16 xh = to_bf16(x);
-      h8[i] = xh;
-      m8[i] = to_bf16(x - from_bf16(xh));
-    }
-    sm.QKf[pi][0][lane] = h8;
-    sm.QKf[pi][1][lane] = m8;
-  } else {
-    bf16x8 h8, m8, l8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __bf16 x0, x1, x2;
-      split3(val[i >> 2][i & 3], x0, x1, x2);
-      h8[i] = x0; m8[i] = x1; l8[i] = x2;
-    }
-    sm.Af[pi][0][lane] = h8;
-    sm.Af[pi][1][lane] = m8;
-    sm.Af[pi][2][lane] = l8;
-  }
-}
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-HAM_DEVICE f32x4 mfma_bf16_k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-HAM_DEVICE void split3x4(const float x[4], bf16x4& h, bf16x4& m, bf16x4& l) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __bf16 a, b, c;
-    split3(x[i], a, b, c);
-    h[i] = a; m[i] = b; l[i] = c;
-  }
-}
-
-// Six-term fp32-accurate product accumulation: (ah+am+al)(bh+bm+bl), dropping the
-// terms below 2^-16 relative.
-template <class F, class V>
-HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, const V& bm, const V& bl, f32x4 c) {
-  c = mf(am, bm, c);
-  c = mf(al, bh, c);
-  c = mf(ah, bl, c);
-  c = mf(am, bh, c);
-  c = mf(ah, bm, c);
-  c = mf(ah, bh, c);
-  return c;
 }
 
 template <int DK, int DV, int NW>
@@ -379,49 +464,40 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       S[mt][i] = a.S0 ? a.S0[sbase + (size_t)(16 * mt + 4 * g + i) * DV + col] : 0.f;
 
   const int nchunk = (a.T + kC - 1) / kC;
-  const int nfrag = readout ? 12 : 6;
+  const char* recs = static_cast<const char*>(a.prep) + (size_t)bh * nchunk * kPrepRecordBytes;
+  // direct global-to-LDS copy of one chunk record (1 KiB per wave instruction); the
+  // builtin exists only in the device compilation pass
+#if defined(__HIP_DEVICE_COMPILE__)
+#define HAM_FETCH_RECORD(BUF, REC)                                                         \
+  for (int blk = wave; blk < kRecBlocks; blk += NW)                                        \
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((REC) + blk * 1024 + lane * 16), \
+                                     &sm.rec[(BUF)][blk * 1024], 16, 0, 0)
+#else
+#define HAM_FETCH_RECORD(BUF, REC) (void)(REC)
+#endif
   ChunkRegs<DK, NW> regs;
   load_chunk<DK, DV, NW>(a, regs, b, h, 0, colbase, tid, readout);
+  HAM_FETCH_RECORD(0, recs);
 
   for (int c = 0; c < nchunk; ++c) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
+    __builtin_amdgcn_s_waitcnt(0);            // this chunk's registers and record have arrived
     __syncthreads();                          // the previous chunk's LDS readers are done
     store_chunk<DK, NW>(sm, regs, tid);
-    if (c + 1 < nchunk) load_chunk<DK, DV, NW>(a, regs, b, h, t0 + kC, colbase, tid, readout);
-    __syncthreads();
-
-    // ---- decayed Gram fragments, shared through LDS in lane order ----
-#pragma unroll
-    for (int rep = 0; rep < (12 + NW - 1) / NW; ++rep) {
-      const int f = wave + rep * NW;
-      if (f >= nfrag) break;
-      const int pi = f % 6;
-      const int mt = pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3;
-      const int s = pi < 2 ? 0 : (pi - 2) & 1;
-      if (f < 6) gram_fragment<DK, NW, false>(sm, mt, s, g, n, lane);
-      else gram_fragment<DK, NW, true>(sm, mt, s, g, n, lane);
+    if (c + 1 < nchunk) {
+      load_chunk<DK, DV, NW>(a, regs, b, h, t0 + kC, colbase, tid, readout);
+      HAM_FETCH_RECORD((c + 1) & 1, recs + (size_t)(c + 1) * kPrepRecordBytes);
     }
     __syncthreads();
+    const char* rec = sm.rec[c & 1];
+    const bf16x8* Af = reinterpret_cast<const bf16x8*>(rec + kRecA);
+    const bf16x8* QKf = reinterpret_cast<const bf16x8*>(rec + kRecQK);
+    const f32x4* Tdf = reinterpret_cast<const f32x4*>(rec + kRecTd);
+    const float* gam = reinterpret_cast<const float*>(rec + kRecGam);
+    const float* wdec = reinterpret_cast<const float*>(rec + kRecW);
 
-    // ---- wave 0: inverses of the four diagonal blocks, T'_ii = (I + L_ii)^-1 diag(beta_i) ----
-    if (wave == 0) {
-      const int bb = lane >> 4, cc = lane & 15;
-      float colv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // four independent partial sums shorten the dependent chain of each row
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < r; ++j) part[j & 3] = fmaf(sm.Ld[bb][r][j], colv[j], part[j & 3]);
-        colv[r] = ((r == cc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
-      }
-      const float bc = sm.beta[16 * bb + cc];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Td[bb][r][cc] = colv[r] * bc;
-    }
-
-    // ---- Y_K = K S, Y_Q = Q S (independent of the inverse) ----
+    // ---- Y_K = K S, Y_Q = Q S ----
     f32x4 P[4], O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -447,10 +523,11 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
     }
+    // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[16 * mt + 4 * g]);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(&gam[16 * mt + 4 * g]);
       const u16x4 v4 = *reinterpret_cast<const u16x4*>(&sm.Vt[vcol * TS + 16 * mt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -460,7 +537,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         X[mt][i] = vv - P[mt][i];
       }
     }
-    __syncthreads();                          // Td is ready
 
     // ---- block forward substitution: D_i = T'_ii (X_i - sum_{j<i} A_ij D_j) ----
     // dB[s][*]: B-operand fragments (k-step s) of the D blocks solved so far.
@@ -476,15 +552,15 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
       for (int s = 0; s <= (i - 1) / 2 && i > 0; ++s) {
         const int pi = pair_index(i, s);
-        R = mma6(mf32, sm.Af[pi][0][lane], sm.Af[pi][1][lane], sm.Af[pi][2][lane],
-                 dB[s][0], dB[s][1], dB[s][2], R);
+        R = mma6(mf32, Af[(pi * 3 + 0) * kWave + lane], Af[(pi * 3 + 1) * kWave + lane],
+                 Af[(pi * 3 + 2) * kWave + lane], dB[s][0], dB[s][1], dB[s][2], R);
       }
       float rhs[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) rhs[e] = X[i][e] - R[e];
       bf16x4 rh, rm, rl, th, tm, tl;
       split3x4(rhs, rh, rm, rl);
-      const f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.Td[i][n][4 * g]);
+      const f32x4 tv = Tdf[i * kWave + lane];
       const float tva[4] = {tv[0], tv[1], tv[2], tv[3]};
       split3x4(tva, th, tm, tl);
       D[i] = mma6(mf16, th, tm, tl, rh, rm, rl, (f32x4)(0.f));
@@ -500,12 +576,15 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         dB[i >> 1][2][4 * half + e] = dl4[e];
       }
       const int pd = pair_index(i, i >> 1);
+      const bf16x8 afh = Af[(pd * 3 + 0) * kWave + lane];
+      const bf16x8 afm = Af[(pd * 3 + 1) * kWave + lane];
+      const bf16x8 afl = Af[(pd * 3 + 2) * kWave + lane];
       bf16x4 ah4, am4, al4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        ah4[e] = sm.Af[pd][0][lane][4 * half + e];
-        am4[e] = sm.Af[pd][1][lane][4 * half + e];
-        al4[e] = sm.Af[pd][2][lane][4 * half + e];
+        ah4[e] = afh[4 * half + e];
+        am4[e] = afm[4 * half + e];
+        al4[e] = afl[4 * half + e];
       }
       P[i] = mma6(mf16, ah4, am4, al4, dh4, dm4, dl4, P[i] + R);
     }
@@ -517,7 +596,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
         for (int s = 0; s <= (mt >> 1); ++s) {
           const int pi = pair_index(mt, s);
-          const bf16x8 qh = sm.QKf[pi][0][lane], qm = sm.QKf[pi][1][lane];
+          const bf16x8 qh = QKf[(pi * 2 + 0) * kWave + lane], qm = QKf[(pi * 2 + 1) * kWave + lane];
           O[mt] = mfma_bf16(qm, dB[s][0], O[mt]);
           O[mt] = mfma_bf16(qh, dB[s][1], O[mt]);
           O[mt] = mfma_bf16(qh, dB[s][0], O[mt]);
@@ -549,8 +628,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float w0[4], w1[4];
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&sm.wdec[32 * s + 4 * g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&sm.wdec[32 * s + 16 + 4 * g]);
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 4 * g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 16 + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         w0[i] = wa[i];
@@ -558,7 +637,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       }
       split_pair3(D[2 * s], D[2 * s + 1], eh[s], em[s], el[s], w0, w1);
     }
-    const float gl = sm.gam[kC - 1];
+    const float gl = gam[kC - 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       S[mt] *= gl;
@@ -576,21 +655,27 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) a.S_out[sbase + (size_t)(16 * mt + 4 * g + i) * DV + col] = S[mt][i];
+#undef HAM_FETCH_RECORD
 }
 
 template <int DK, int DV, int NW>
 hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
+  const int nchunk = (a.T + kC - 1) / kC;
+  hipLaunchKernelGGL((rnn_prep_kernel<DK>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(DV / (16 * NW), a.H, a.B);
   hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
-// Four waves (64 state columns) per workgroup: the per-chunk prep work is split
-// four ways, which sets the latency of the sequential chunk loop.
+// Four waves (64 state columns) per workgroup.
 template <int DK, int DV>
 hipError_t launch_dims(const RnnArgs& a, hipStream_t s) { return launch_t<DK, DV, 4>(a, s); }
 
-}  // namespace
+}  // namespace chunked
+
+using chunked::launch_dims;
 
 bool rnn_chunked_supported(int io, int dk, int dv) {
   return io == 1 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
