@@ -33,6 +33,7 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int check_dims(const ham_dims* d, bool need_T) {
   if (!d) return fail(HAM_EINVAL, "dims is NULL");
+  if (d->H > 4096) return fail(HAM_EUNSUPPORTED, "H must be <= 4096 (H=%d)", d->H);
   if (d->B <= 0 || d->H <= 0 || (need_T && d->T <= 0))
     return fail(HAM_EINVAL, "B, T and H must be positive (B=%d T=%d H=%d)", d->B, d->T, d->H);
   if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))

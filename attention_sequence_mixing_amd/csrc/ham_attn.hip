@@ -344,26 +344,50 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // Tile staging.  Rows at or beyond nhi are never visible: K rows there are read
   // from a clamped in-range row and masked through the scores; V rows are zeroed
-  // so that p = 0 multiplies finite values.
+  // so that p = 0 multiplies finite values.  Per-thread byte offsets are fixed;
+  // each tile only moves the (wave-uniform) base.  Only a tile that reaches nhi
+  // needs the clamps.
   u16x8 kreg[KPT];
   uint32_t vreg[VPT][8];
+  uint32_t koff[KPT], voff[VPT];
+#pragma unroll
+  for (int p = 0; p < KPT; ++p) {
+    const int u = tid + p * 256;
+    koff[p] = (uint32_t)(((u / (DK / 8)) * DK + (u % (DK / 8)) * 8) * 2);
+  }
+#pragma unroll
+  for (int p = 0; p < VPT; ++p) {
+    const int u = tid + p * 256;
+    voff[p] = (uint32_t)(((u / (DV / 2)) * 8 * DV + 2 * (u % (DV / 2))) * 2);
+  }
   const int rmax = a.cap - 1;
   auto load_tile = [&](int c0) {
+    const char* kt = reinterpret_cast<const char*>(Kh + (size_t)c0 * DK);
+    const char* vt = reinterpret_cast<const char*>(Vh + (size_t)c0 * DV);
+    if (c0 + BN <= nhi) {
 #pragma unroll
-    for (int p = 0; p < KPT; ++p) {
-      const int u = tid + p * 256;
-      const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
-      kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)min(c0 + row, rmax) * DK + col);
-    }
+      for (int p = 0; p < KPT; ++p) kreg[p] = *reinterpret_cast<const u16x8*>(kt + koff[p]);
 #pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const int u = tid + p * 256;
-      const int dp = u % (DV / 2), kg = u / (DV / 2);
+      for (int p = 0; p < VPT; ++p)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int c = c0 + kg * 8 + r;
-        const uint32_t x = *reinterpret_cast<const uint32_t*>(Vh + (size_t)min(c, rmax) * DV + 2 * dp);
-        vreg[p][r] = (c < nhi) ? x : 0u;
+        for (int r = 0; r < 8; ++r) vreg[p][r] = *reinterpret_cast<const uint32_t*>(vt + voff[p] + r * DV * 2);
+    } else {
+#pragma unroll
+      for (int p = 0; p < KPT; ++p) {
+        const int u = tid + p * 256;
+        const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
+        kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)min(c0 + row, rmax) * DK + col);
+      }
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) {
+        const int u = tid + p * 256;
+        const int dp = u % (DV / 2), kg = u / (DV / 2);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int c = c0 + kg * 8 + r;
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(Vh + (size_t)min(c, rmax) * DV + 2 * dp);
+          vreg[p][r] = (c < nhi) ? x : 0u;
+        }
       }
     }
   };

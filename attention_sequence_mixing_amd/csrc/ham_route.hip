@@ -7,29 +7,36 @@
 // (§2 KV-memory equation restricted to the routed set; App. A.1 "KV Memory"),
 // and the KV-usage fraction rho (§5).
 //
-// Compaction is deterministic: per 64-token chunk one wave64 ballot gives the
-// chunk's routed count and each token's rank inside the chunk; a chunk's base is
-// the sum of the earlier chunks' counts.  No atomics, so the cache order is the
-// ascending original position on every run.
+// Compaction is deterministic: per 64-token chunk one wave64 ballot gives each
+// token's rank inside the chunk; a chunk's base is the sum of the earlier chunks'
+// routed counts (integer sums, so their order does not matter).  No global atomics:
+// the cache order is the ascending original position on every run.
 #include "ham_common.h"
 #include "ham_internal.h"
 
 namespace ham {
 
-// grid (nchunk, H, B), one wave: lane = token within the chunk.
-__global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
-  const int lane = lane_id();
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int bh = b * a.H + h;
+// grid (nchunk, B), 256 threads: all heads of one 64-token chunk.  Thread index
+// runs head-fastest so that e and routed ([B,T,H]) are written contiguously; the
+// per-head routed counts of the chunk are integer sums in LDS (order-independent).
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  extern __shared__ int s_cnt[];            // [H]
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x, b = blockIdx.y;
   const int nchunk = gridDim.x;
-  const int t = c * kChunk + lane;
-  const bool valid = t < a.T;
-  bool r = false;
-  if (valid) {
+  const int H = a.H;
+  for (int h = tid; h < H; h += 256) s_cnt[h] = 0;
+  __syncthreads();
+  const int t0 = c * kChunk;
+  const int nv = min(kChunk, a.T - t0);
+  for (int idx = tid; idx < nv * H; idx += 256) {
+    const int tl = idx / H, h = idx % H;
+    const int t = t0 + tl;
+    const int bh = b * H + h;
     const float4* sp = a.score + ((size_t)bh * a.T + t) * a.slices;
     float pv = 0.f, pp = 0.f, vv = 0.f;
     for (int s = 0; s < a.slices; ++s) {
-      float4 x = sp[s];
+      const float4 x = sp[s];
       pv += x.x; pp += x.y; vv += x.z;
     }
     float cs = 0.f;
@@ -38,21 +45,23 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
       cs = fminf(1.f, fmaxf(-1.f, cs));
     }
     const float e = 1.f - cs;
-    r = e > a.tau[h];                 // strict; a NaN score never routes
-    const size_t tok = ((size_t)b * a.T + t) * a.H + h;
+    const bool r = e > a.tau[h];            // strict; a NaN score never routes
+    const size_t tok = ((size_t)b * a.T + t) * H + h;
     a.e[tok] = e;
     a.routed[tok] = (uint8_t)r;
+    if (r) atomicAdd(&s_cnt[h], 1);
   }
-  const unsigned long long bal = __ballot(r);
-  if (lane == 0) {
-    a.chunk_count[(size_t)bh * nchunk + c] = __popcll(bal);
+  __syncthreads();
+  for (int h = tid; h < H; h += 256) {
+    const int bh = b * H + h;
+    a.chunk_count[(size_t)bh * nchunk + c] = s_cnt[h];
     if (c == 0) a.count_in[bh] = a.count ? a.count[bh] : 0;
   }
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(route_kernel, dim3(nchunk, a.H, a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(route_kernel, dim3(nchunk, a.B), dim3(256), a.H * sizeof(int), s, a);
   return hipGetLastError();
 }
 
