@@ -573,6 +573,309 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// ---- bf16 path v4: direct-to-LDS tile ring ----------------------------------------
+//
+// 8 waves x 32 queries per workgroup.  K and V tiles (64 keys) are copied from HBM
+// into LDS with direct global-to-LDS loads (no staging registers) into a 3-stage
+// ring, two tiles ahead of the one being consumed.  Both tiles are row-major with
+// the 16-byte chunks of each row XOR-swizzled by the row index (chunk c of row r
+// sits at chunk slot c ^ (r mod chunks-per-row)), which keeps the fragment reads
+// free of bank conflicts.  K fragments (A operand of S^T = K Q^T) are 16-byte
+// reads; V^T fragments (A operand of O^T = V^T P^T) use the transposing LDS read:
+// for each 16-lane group, lane r addresses V[k0 + r/4][d0 + 4(r mod 4) .. +3] and
+// lane i receives V[k0 + j][d0 + i] for j = 0..3.
+template <int D>
+HAM_DEVICE int swz_off(int row, int chunk) {            // byte offset in a tile
+  constexpr int NCH = D / 8;
+  return row * (D * 2) + ((chunk ^ (row & (NCH - 1))) << 4);
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+
+HAM_DEVICE short4v lds_read_tr16(const char* base, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)((__attribute__((address_space(3))) const char*)base + byte_off));
+#else
+  (void)base; (void)byte_off;
+  return short4v{0, 0, 0, 0};
+#endif
+}
+
+template <int DK, int DV, int QT>
+__global__ __launch_bounds__(512, 1) void attn_bf16_v4_kernel(AttnArgs a) {
+  constexpr int NWV = 8;                                   // waves per workgroup
+  constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
+  constexpr int BMW = 16 * QT, BM = NWV * BMW;
+  constexpr int KB = BN * DK * 2, VB = BN * DV * 2;        // tile bytes
+  constexpr int KI = KB / 1024, VI = VB / 1024;            // 1 KiB load instructions per tile
+  static_assert((KI + VI) % NWV == 0, "tile loads must split evenly over the waves");
+  constexpr int LPW = (KI + VI) / NWV;                     // load instructions per wave per tile
+  constexpr int NST = 4;                                   // ring stages
+  __shared__ __attribute__((aligned(16))) char ring[NST][KB + VB];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 4, qn = lane & 15;
+  const int nqb = (a.T + BM - 1) / BM;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqb;
+  const int qb = nqb - 1 - (lin % nqb);
+  const int b = bh / a.H, h = bh % a.H;
+
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* Kh = static_cast<const uint16_t*>(a.Kc) + (size_t)bh * a.cap * DK;
+  const uint16_t* Vh = static_cast<const uint16_t*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const int32_t* ntok = a.ntok + (size_t)bh * a.T;
+
+  const int qb0 = qb * BM;
+  const int nlo = ntok[qb0];
+  const int nhi = ntok[min(a.T - 1, qb0 + BM - 1)];
+
+  int tq[QT], nq[QT];
+  bf16x8 qf[QT][KSD];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    tq[qt] = qb0 + wave * BMW + 16 * qt + qn;
+    const bool ok = tq[qt] < a.T;
+    nq[qt] = ok ? ntok[tq[qt]] : 0;
+    const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+      qf[qt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g));
+  }
+
+  // Direct loads of one tile into ring stage `st`.  Instruction i of this wave covers
+  // 1 KiB of the stage; lane l writes its 16 bytes at i*1024 + 16*l, which holds
+  // chunk (slot ^ swizzle) of tile row r.  Rows at or beyond nhi read row nhi-1
+  // (finite values; those keys are masked through the scores).
+  const int rlast = nhi - 1;
+  auto issue_tile = [&](int it, int st) {
+    const int c0 = it * BN;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int i = wave * LPW + k;                      // instruction index within the tile
+      const int pos = i * 1024 + lane * 16;              // byte position in the stage
+      const bool isK = i < KI;
+      const int D = isK ? DK : DV;
+      const int rb = D * 2;
+      const int tp = isK ? pos : pos - KB;
+      const int r = tp / rb, slot = (tp % rb) >> 4;
+      const int nch = D / 8;
+      const int chunk = slot ^ (r & (nch - 1));
+      const int row = min(c0 + r, rlast);
+      const uint16_t* src = isK ? Kh + (size_t)row * DK + chunk * 8 : Vh + (size_t)row * DV + chunk * 8;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), &ring[st][i * 1024], 16, 0, 0);
+#else
+      (void)src;
+#endif
+    }
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run[QT], l_run[QT];
+  f32x4 acc[QT][DT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = (f32x4)(0.f);
+  }
+
+  // Per-lane fragment offsets inside a stage.  The swizzle term only depends on the
+  // lane (row mod chunks-per-row is fixed by the lane), so each fragment address is
+  // stage base + one of these + a compile-time constant.
+  constexpr int RBK = DK * 2, RBV = DV * 2, NCHK = DK / 8, NCHV = DV / 8;
+  int koff[KSD], voff[DT];
+  const int r4 = qn >> 2, c4 = qn & 3;
+#pragma unroll
+  for (int ks = 0; ks < KSD; ++ks) koff[ks] = qn * RBK + (((ks * 4 + g) ^ (qn & (NCHK - 1))) << 4);
+  {
+    const int ry = 4 * g + r4;                             // tile row of this lane's V run (mod 16)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      voff[dt] = KB + ry * RBV + (((2 * dt + (c4 >> 1)) ^ (ry & (NCHV - 1))) << 4) + (c4 & 1) * 8;
+  }
+
+  const int ntiles = (nhi + BN - 1) / BN;
+  __builtin_amdgcn_s_waitcnt(0);                          // query fragments are in
+  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(1, 1);
+
+  f32x4 st[QT][NKT];
+  // S^T = K Q^T for the tile in `stage`
+  auto do_scores = [&](int stage) {
+    const char* Kt = ring[stage];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) st[qt][kt] = (f32x4)(0.f);
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Kt + koff[ks] + kt * 16 * RBK);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
+      }
+  };
+  // masks, online softmax (lazy rescale) and O^T += V^T P^T for tile `it`
+  auto do_softmax_pv = [&](int it, int stage) {
+    const int c0 = it * BN;
+    if ((c0 + BN) > nlo) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((c0 + kt * 16 + 4 * g + i) >= nq[qt]) st[qt][kt][i] = -INFINITY;
+    }
+    // The running maximum is common to the four lanes of a query; a lane-local
+    // maximum decides whether it must grow, and only then is the row maximum
+    // formed across lanes.
+    bool grow = false;
+    float m_loc[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(st[qt][kt][0], st[qt][kt][1]), fmaxf(st[qt][kt][2], st[qt][kt][3])));
+      m_loc[qt] = tmax * sl2;
+      grow |= m_loc[qt] > m_run[qt] + kLazyRescale;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float mrow = fmaxf(m_loc[qt], __shfl_xor(m_loc[qt], 16, kWave));
+        mrow = fmaxf(mrow, __shfl_xor(mrow, 32, kWave));
+        const float mn = fmaxf(m_run[qt], mrow);
+        const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - mn);
+        l_run[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= corr;
+        m_run[qt] = mn;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], sl2, mneg));
+          st[qt][kt][i] = pr;
+          psum += pr;
+        }
+      l_run[qt] += psum;
+    }
+    const char* Kt = ring[stage];
+#pragma unroll
+    for (int u = 0; u < NKT / 2; ++u) {
+      bf16x8 pb[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[qt][i] = static_cast<__bf16>(st[qt][2 * u][i]);
+          pb[qt][4 + i] = static_cast<__bf16>(st[qt][2 * u + 1][i]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const short4v lo = lds_read_tr16(Kt, voff[dt] + 32 * u * RBV);
+        const short4v hi = lds_read_tr16(Kt, voff[dt] + (32 * u + 16) * RBV);
+        short8v va;
+        va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
+        va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[qt], acc[qt][dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Waves w and w+4 share a SIMD.  Waves 4..7 run half a step behind: in step it
+  // they finish tile it-1 (softmax, V) and then start tile it (scores), so their
+  // VALU phase overlaps the MFMA phase of their SIMD partner.  Tiles in use in
+  // step it: it-1, it (ring stages), it+1 and it+2 in flight -> four stages.
+  const bool lag = wave >= 4;
+  for (int it = 0; it <= ntiles; ++it) {
+    if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0xF70 | LPW);   // tile it has landed
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 2 < ntiles) issue_tile(it + 2, (it + 2) % NST);
+    if (!lag) {
+      if (it < ntiles) {
+        do_scores(it % NST);
+        do_softmax_pv(it, it % NST);
+      }
+    } else {
+      if (it >= 1) do_softmax_pv(it - 1, (it - 1) % NST);
+      if (it < ntiles) do_scores(it % NST);
+    }
+  }
+
+  // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int t = tq[qt];
+    const bool tvalid = t < a.T;
+    const size_t tt = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
+    float okv[DT][4], orn[DT][4];
+    float ssk = 0.f, ssr = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 r4v = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        okv[dt][i] = acc[qt][dt][i] * inv_l;
+        orn[dt][i] = r4v[i];
+        ssk += okv[dt][i] * okv[dt][i];
+        ssr += orn[dt][i] * orn[dt][i];
+      }
+    }
+    ssk += __shfl_xor(ssk, 16, kWave);
+    ssk += __shfl_xor(ssk, 32, kWave);
+    ssr += __shfl_xor(ssr, 16, kWave);
+    ssr += __shfl_xor(ssr, 32, kWave);
+    if (!tvalid) continue;
+    const float gr = a.gate_rnn ? a.gate_rnn[tt] : 1.f;
+    const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
+    const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
+    const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
+    uint16_t* o = static_cast<uint16_t*>(a.o);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
+      const size_t off = tt * DV + dt * 16 + 4 * g;
+      IoBF16::store4(o, off, y);
+      if (a.o_kv) IoBF16::store4(static_cast<uint16_t*>(a.o_kv), off, okv[dt]);
+      if (a.o_rnn) IoBF16::store4(static_cast<uint16_t*>(a.o_rnn), off, orn[dt]);
+    }
+  }
+}
+
+template <int DK, int DV>
+static hipError_t launch_attn_bf16_v4(const AttnArgs& a, hipStream_t s) {
+  constexpr int QT = 2, BM = 8 * 16 * QT;
+  const int nqb = (a.T + BM - 1) / BM;
+  hipLaunchKernelGGL((attn_bf16_v4_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DK, int DV>
 static hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 2, BM = 64 * QT;
@@ -594,10 +897,10 @@ hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
   } else {
-    if (dk == 64 && dv == 64) return launch_attn_bf16<64, 64>(a, s);
-    if (dk == 64 && dv == 128) return launch_attn_bf16<64, 128>(a, s);
-    if (dk == 128 && dv == 64) return launch_attn_bf16<128, 64>(a, s);
-    if (dk == 128 && dv == 128) return launch_attn_bf16<128, 128>(a, s);
+    if (dk == 64 && dv == 64) return launch_attn_bf16_v4<64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_attn_bf16_v4<64, 128>(a, s);
+    if (dk == 128 && dv == 64) return launch_attn_bf16_v4<128, 64>(a, s);
+    if (dk == 128 && dv == 128) return launch_attn_bf16_v4<128, 128>(a, s);
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;
