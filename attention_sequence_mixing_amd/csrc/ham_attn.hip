@@ -14,7 +14,8 @@
 // computes S^T = K Q^T on 16x16 MFMA tiles (keys on rows), so the per-query
 // softmax state lives in the lanes that later hold that query's output column of
 // O^T = V^T P^T: no data movement between the two products.  bf16 uses
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; fp32 uses v_mfma_f32_16x16x4f32.
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation (attn_bf16_v4_kernel); fp32 I/O
+// uses v_mfma_f32_16x16x4f32 (attn_kernel).
 #include "ham_common.h"
 #include "ham_internal.h"
 
@@ -282,302 +283,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// ---- bf16 path: 32 queries per wave, double-buffered K / V^T tiles ---------------
-//
-// A wave owns QT 16-query tiles; every K and V^T fragment it reads from LDS feeds
-// QT MFMAs, which keeps the LDS traffic per MFMA flop at 1/QT of the one-tile
-// layout.  The next key tile is fetched into registers while the current one is
-// consumed, then written to the other LDS buffer; one barrier per tile.  V^T is
-// built with 4-byte loads (two adjacent d of one key; each load instruction of a
-// wave reads 256 contiguous bytes of one row) packed into 16-byte LDS stores of
-// eight consecutive keys.
-//
-// Softmax: the running maximum is kept in log2 units of the scaled logits
-// (scale > 0, so the maximum of the raw scores gives it); the accumulators are
-// rescaled only when some query's maximum grows by more than 2^8, otherwise the
-// stale maximum is kept (probabilities up to 2^8 are exact enough in fp32/bf16 and
-// the final division by the running sum cancels the common factor).
+// Softmax of the bf16 path: the running maximum is kept in log2 units of the scaled
+// logits (scale > 0, so the maximum of the raw scores gives it).  The accumulators
+// are rescaled only when some query's maximum grows by more than 8 (a factor 2^8);
+// otherwise the stale maximum is kept: probabilities up to 2^8 are exact enough in
+// fp32 and bf16, and the final division by the running sum cancels the common factor.
 constexpr float kLazyRescale = 8.0f;
 
-template <int DK, int DV, int QT>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
-  constexpr int BMW = 16 * QT, BM = 4 * BMW;
-  constexpr int KS = DK + 8, VS = BN + 4;
-  constexpr int KU = BN * DK / 8, KPT = KU / 256;            // 16-byte K units per thread
-  constexpr int VU = (DV / 2) * (BN / 8), VPT = VU / 256;     // (d pair, 8-key group) units
-  static_assert(KU % 256 == 0 && VU % 256 == 0, "tile does not split evenly");
-  __shared__ uint16_t Ks[2][BN * KS];
-  __shared__ uint16_t Vt[2][DV * VS];
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int g = lane >> 4, qn = lane & 15;
-  const int nqb = (a.T + BM - 1) / BM;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nqb;
-  const int qb = nqb - 1 - (lin % nqb);
-  const int b = bh / a.H, h = bh % a.H;
-
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* Kh = static_cast<const uint16_t*>(a.Kc) + (size_t)bh * a.cap * DK;
-  const uint16_t* Vh = static_cast<const uint16_t*>(a.Vc) + (size_t)bh * a.cap * DV;
-  const int32_t* ntok = a.ntok + (size_t)bh * a.T;
-
-  const int qb0 = qb * BM;
-  const int nlo = ntok[qb0];                               // every query of the block sees c < nlo
-  const int nhi = ntok[min(a.T - 1, qb0 + BM - 1)];        // no query sees c >= nhi
-
-  int tq[QT], nq[QT];
-  bf16x8 qf[QT][KSD];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    tq[qt] = qb0 + wave * BMW + 16 * qt + qn;
-    const bool ok = tq[qt] < a.T;
-    nq[qt] = ok ? ntok[tq[qt]] : 0;
-    const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      u16x8 x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // Tile staging.  Rows at or beyond nhi are never visible: K rows there are read
-  // from a clamped in-range row and masked through the scores; V rows are zeroed
-  // so that p = 0 multiplies finite values.  Per-thread byte offsets are fixed;
-  // each tile only moves the (wave-uniform) base.  Only a tile that reaches nhi
-  // needs the clamps.
-  u16x8 kreg[KPT];
-  uint32_t vreg[VPT][8];
-  uint32_t koff[KPT], voff[VPT];
-#pragma unroll
-  for (int p = 0; p < KPT; ++p) {
-    const int u = tid + p * 256;
-    koff[p] = (uint32_t)(((u / (DK / 8)) * DK + (u % (DK / 8)) * 8) * 2);
-  }
-#pragma unroll
-  for (int p = 0; p < VPT; ++p) {
-    const int u = tid + p * 256;
-    voff[p] = (uint32_t)(((u / (DV / 2)) * 8 * DV + 2 * (u % (DV / 2))) * 2);
-  }
-  const int rmax = a.cap - 1;
-  auto load_tile = [&](int c0) {
-    const char* kt = reinterpret_cast<const char*>(Kh + (size_t)c0 * DK);
-    const char* vt = reinterpret_cast<const char*>(Vh + (size_t)c0 * DV);
-    if (c0 + BN <= nhi) {
-#pragma unroll
-      for (int p = 0; p < KPT; ++p) kreg[p] = *reinterpret_cast<const u16x8*>(kt + koff[p]);
-#pragma unroll
-      for (int p = 0; p < VPT; ++p)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) vreg[p][r] = *reinterpret_cast<const uint32_t*>(vt + voff[p] + r * DV * 2);
-    } else {
-#pragma unroll
-      for (int p = 0; p < KPT; ++p) {
-        const int u = tid + p * 256;
-        const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
-        kreg[p] = *reinterpret_cast<const u16x8*>(Kh + (size_t)min(c0 + row, rmax) * DK + col);
-      }
-#pragma unroll
-      for (int p = 0; p < VPT; ++p) {
-        const int u = tid + p * 256;
-        const int dp = u % (DV / 2), kg = u / (DV / 2);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int c = c0 + kg * 8 + r;
-          const uint32_t x = *reinterpret_cast<const uint32_t*>(Vh + (size_t)min(c, rmax) * DV + 2 * dp);
-          vreg[p][r] = (c < nhi) ? x : 0u;
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPT; ++p) {
-      const int u = tid + p * 256;
-      const int row = u / (DK / 8), col = (u % (DK / 8)) * 8;
-      *reinterpret_cast<u16x8*>(&Ks[buf][row * KS + col]) = kreg[p];
-    }
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const int u = tid + p * 256;
-      const int dp = u % (DV / 2), kg = u / (DV / 2);
-      u16x8 lo, hi;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        lo[r] = (uint16_t)(vreg[p][r] & 0xffffu);
-        hi[r] = (uint16_t)(vreg[p][r] >> 16);
-      }
-      *reinterpret_cast<u16x8*>(&Vt[buf][(2 * dp) * VS + kg * 8]) = lo;
-      *reinterpret_cast<u16x8*>(&Vt[buf][(2 * dp + 1) * VS + kg * 8]) = hi;
-    }
-  };
-
-  const float sl2 = a.scale * kLog2e;        // > 0
-  float m_run[QT], l_run[QT];                // m_run in scaled log2 units
-  f32x4 acc[QT][DT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = (f32x4)(0.f);
-  }
-
-  const int ntiles = (nhi + BN - 1) / BN;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int c0 = it * BN;
-    if (it + 1 < ntiles) load_tile(c0 + BN);
-    const uint16_t* K_ = Ks[buf];
-    const uint16_t* V_ = Vt[buf];
-
-    f32x4 st[QT][NKT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) st[qt][kt] = (f32x4)(0.f);
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        const bf16x8 kx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&K_[(kt * 16 + qn) * KS + ks * 32 + 8 * g]));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
-      }
-
-    if ((c0 + BN) > nlo) {                   // some key of this tile is masked for some query
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((c0 + kt * 16 + 4 * g + i) >= nq[qt]) st[qt][kt][i] = -INFINITY;
-    }
-    bool grow = false;
-    float m_new[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(st[qt][kt][0], st[qt][kt][1]), fmaxf(st[qt][kt][2], st[qt][kt][3])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      m_new[qt] = tmax * sl2;
-      grow |= m_new[qt] > m_run[qt] + kLazyRescale;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float mn = fmaxf(m_run[qt], m_new[qt]);
-        const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - mn);
-        l_run[qt] *= corr;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= corr;
-        m_run[qt] = mn;
-      }
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], sl2, mneg));
-          st[qt][kt][i] = pr;
-          psum += pr;
-        }
-      l_run[qt] += psum;
-    }
-
-#pragma unroll
-    for (int u = 0; u < NKT / 2; ++u) {
-      bf16x8 pb[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[qt][i] = static_cast<__bf16>(st[qt][2 * u][i]);
-          pb[qt][4 + i] = static_cast<__bf16>(st[qt][2 * u + 1][i]);
-        }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vrow = &V_[(dt * 16 + qn) * VS];
-        const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 4 * g);
-        const u16x4 v1 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 16 + 4 * g);
-        u16x8 va;
-        va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
-        va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[qt], acc[qt][dt], 0, 0, 0);
-      }
-    }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, kWave);
-    l_tot += __shfl_xor(l_tot, 32, kWave);
-    const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int t = tq[qt];
-    const bool tvalid = t < a.T;
-    const size_t tt = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
-    float okv[DT][4], orn[DT][4];
-    float ssk = 0.f, ssr = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        okv[dt][i] = acc[qt][dt][i] * inv_l;
-        orn[dt][i] = r4[i];
-        ssk += okv[dt][i] * okv[dt][i];
-        ssr += orn[dt][i] * orn[dt][i];
-      }
-    }
-    ssk += __shfl_xor(ssk, 16, kWave);
-    ssk += __shfl_xor(ssk, 32, kWave);
-    ssr += __shfl_xor(ssr, 16, kWave);
-    ssr += __shfl_xor(ssr, 32, kWave);
-    if (!tvalid) continue;
-    const float gr = a.gate_rnn ? a.gate_rnn[tt] : 1.f;
-    const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
-    const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
-    const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
-    uint16_t* o = static_cast<uint16_t*>(a.o);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      float y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
-      const size_t off = tt * DV + dt * 16 + 4 * g;
-      IoBF16::store4(o, off, y);
-      if (a.o_kv) IoBF16::store4(static_cast<uint16_t*>(a.o_kv), off, okv[dt]);
-      if (a.o_rnn) IoBF16::store4(static_cast<uint16_t*>(a.o_rnn), off, orn[dt]);
-    }
-  }
-}
-
-// ---- bf16 path v4: direct-to-LDS tile ring ----------------------------------------
+// ---- bf16 path: direct-to-LDS tile ring ---------------------------------------------
 //
-// 8 waves x 32 queries per workgroup.  K and V tiles (64 keys) are copied from HBM
-// into LDS with direct global-to-LDS loads (no staging registers) into a 3-stage
-// ring, two tiles ahead of the one being consumed.  Both tiles are row-major with
+// 4 waves x 32 queries per workgroup, two workgroups per CU.  K and V tiles (64
+// keys) are copied from HBM into LDS with direct global-to-LDS loads (no staging
+// registers) into a 2-stage ring, one tile ahead of the one being consumed.  Both tiles are row-major with
 // the 16-byte chunks of each row XOR-swizzled by the row index (chunk c of row r
 // sits at chunk slot c ^ (r mod chunks-per-row)), which keeps the fragment reads
 // free of bank conflicts.  K fragments (A operand of S^T = K Q^T) are 16-byte
@@ -605,23 +322,25 @@ HAM_DEVICE short4v lds_read_tr16(const char* base, int byte_off) {
 }
 
 template <int DK, int DV, int QT>
-__global__ __launch_bounds__(512, 1) void attn_bf16_v4_kernel(AttnArgs a) {
-  constexpr int NWV = 8;                                   // waves per workgroup
+__global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
+  constexpr int NWV = 4;                                   // waves per workgroup
   constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
   constexpr int BMW = 16 * QT, BM = NWV * BMW;
   constexpr int KB = BN * DK * 2, VB = BN * DV * 2;        // tile bytes
   constexpr int KI = KB / 1024, VI = VB / 1024;            // 1 KiB load instructions per tile
   static_assert((KI + VI) % NWV == 0, "tile loads must split evenly over the waves");
   constexpr int LPW = (KI + VI) / NWV;                     // load instructions per wave per tile
-  constexpr int NST = 4;                                   // ring stages
+  constexpr int NST = 2;                                   // ring stages
   __shared__ __attribute__((aligned(16))) char ring[NST][KB + VB];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, qn = lane & 15;
   const int nqb = (a.T + BM - 1) / BM;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nqb;
-  const int qb = nqb - 1 - (lin % nqb);
+  // global longest-first: all heads' last query block first
+  const int lin = blockIdx.x;
+  const int nbh = gridDim.x / nqb;
+  const int bh = lin % nbh;
+  const int qb = nqb - 1 - (lin / nbh);
   const int b = bh / a.H, h = bh % a.H;
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
@@ -703,7 +422,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_v4_kernel(AttnArgs a) {
   const int ntiles = (nhi + BN - 1) / BN;
   __builtin_amdgcn_s_waitcnt(0);                          // query fragments are in
   if (ntiles > 0) issue_tile(0, 0);
-  if (ntiles > 1) issue_tile(1, 1);
 
   f32x4 st[QT][NKT];
   // S^T = K Q^T for the tile in `stage`
@@ -802,25 +520,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_v4_kernel(AttnArgs a) {
     }
   };
 
-  // Waves w and w+4 share a SIMD.  Waves 4..7 run half a step behind: in step it
-  // they finish tile it-1 (softmax, V) and then start tile it (scores), so their
-  // VALU phase overlaps the MFMA phase of their SIMD partner.  Tiles in use in
-  // step it: it-1, it (ring stages), it+1 and it+2 in flight -> four stages.
-  const bool lag = wave >= 4;
-  for (int it = 0; it <= ntiles; ++it) {
-    if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0xF70 | LPW);   // tile it has landed
-    else __builtin_amdgcn_s_waitcnt(0);
+  // Step it: tile it has landed (wait, then barrier: every wave is also done with
+  // tile it-1, whose stage the next load overwrites); fetch tile it+1; consume it.
+  for (int it = 0; it < ntiles; ++it) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 2 < ntiles) issue_tile(it + 2, (it + 2) % NST);
-    if (!lag) {
-      if (it < ntiles) {
-        do_scores(it % NST);
-        do_softmax_pv(it, it % NST);
-      }
-    } else {
-      if (it >= 1) do_softmax_pv(it - 1, (it - 1) % NST);
-      if (it < ntiles) do_scores(it % NST);
-    }
+    if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) % NST);
+    do_scores(it % NST);
+    do_softmax_pv(it, it % NST);
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
@@ -870,17 +577,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_v4_kernel(AttnArgs a) {
 
 template <int DK, int DV>
 static hipError_t launch_attn_bf16_v4(const AttnArgs& a, hipStream_t s) {
-  constexpr int QT = 2, BM = 8 * 16 * QT;
+  constexpr int QT = 2, BM = 4 * 16 * QT;
   const int nqb = (a.T + BM - 1) / BM;
-  hipLaunchKernelGGL((attn_bf16_v4_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(512), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int DK, int DV>
-static hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  constexpr int QT = 2, BM = 64 * QT;
-  const int nqb = (a.T + BM - 1) / BM;
-  hipLaunchKernelGGL((attn_bf16_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16_v4_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
