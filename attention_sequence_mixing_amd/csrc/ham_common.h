@@ -86,6 +86,28 @@ HAM_DEVICE float row16_sum(float x) {
   return x;
 }
 
+// Transposed sum over the 16 lanes of a DPP row: every lane holds 16 values x[0..15];
+// lane n of the row ends with the row total of x[n].  Four exchange steps with the
+// partners n^8 (row rotate by 8), n^7 (half-row mirror), n^2 and n^1 (quad permutes);
+// at each step a lane keeps the half of its remaining values selected by one bit of
+// n and receives its partner's partial sums of that half.  15 exchanges instead of
+// the 64 of sixteen separate row sums.
+template <int kCtrl>
+HAM_DEVICE float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+HAM_DEVICE float row16_transpose_sum(const float (&x)[16], int n) {
+  float y[8], z[4], w[2];
+  const bool b3 = n & 8, b2 = n & 4, b1 = n & 2, b0 = n & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = (b3 ? x[j + 8] : x[j]) + dpp_mov<0x128>(b3 ? x[j] : x[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = (b2 ? y[j + 4] : y[j]) + dpp_mov<0x141>(b2 ? y[j] : y[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) w[j] = (b1 ? z[j + 2] : z[j]) + dpp_mov<0x4E>(b1 ? z[j] : z[j + 2]);
+  return (b0 ? w[1] : w[0]) + dpp_mov<0xB1>(b0 ? w[0] : w[1]);
+}
+
 // ---- XCD-aware workgroup order ----------------------------------------------------
 // The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical ids: neighbouring tiles

@@ -85,13 +85,12 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
 // offsets in bytes; 16-byte lane entries are in MFMA operand order):
 //   [0, 18432)       A  fragments: 6 (row tile, k-step) pairs x 3 splits x 64 lanes
 //   [18432, 30720)   QK fragments: 6 pairs x 2 splits x 64 lanes
-//   [30720, 34816)   T'_ii = (I + diag(beta) A_ii)^-1 diag(beta): 4 blocks x 64 lanes,
-//                    lane (g,n) holds row n, columns 4g..4g+3 (fp32)
-//   [34816, 35072)   gamma_t = exp(G_t)                (fp32 x 64)
-//   [35072, 35328)   w_t = exp(G_last - G_t)           (fp32 x 64)
-//   [35328, 35840)   padding to whole 1 KiB blocks
-constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 34816, kRecW = 35072;
-constexpr int kRecBlocks = (int)(kPrepRecordBytes / 1024);
+//   [30720, 36864)   T'_ii = (I + diag(beta) A_ii)^-1 diag(beta): 4 blocks x 3 splits
+//                    x 64 lanes of 4 bf16; lane (g,n) holds row n, columns 4g..4g+3
+//   [36864, 37120)   gamma_t = exp(G_t)                (fp32 x 64)
+//   [37120, 37376)   w_t = exp(G_last - G_t)           (fp32 x 64)
+//   [37376, 37888)   padding to whole 1 KiB blocks
+constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 36864, kRecW = 37120;
 static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
 
 // Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
@@ -279,225 +278,222 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
   }
   __syncthreads();
   {
-    // lane order: entry (block i, lane (g,n)) = row n, columns 4g..4g+3
+    // lane order: entry (block i, split z, lane (g,n)) = row n, columns 4g..4g+3
     const int i = tid >> 6;
     const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Td[i][n][4 * g]);
-    reinterpret_cast<f32x4*>(rec + kRecTd)[i * kWave + lane] = x;
+    const float xa[4] = {x[0], x[1], x[2], x[3]};
+    bf16x4 th, tm, tl;
+    split3x4(xa, th, tm, tl);
+    bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecTd) + (i * 3) * kWave + lane;
+    dst[0] = th;
+    dst[kWave] = tm;
+    dst[2 * kWave] = tl;
   }
 }
 
 // ---------------------------------------------------------------------------------
 // State kernel: one workgroup = NW waves = 16*NW state columns of one head, walking
-// the chunks in order.  The chunk record is streamed into LDS one chunk ahead with
-// direct global-to-LDS loads; K, Q, K^T and this workgroup's V^T columns are staged
-// from registers prefetched one chunk ahead.
-template <int DK, int NW>
-struct ChunkSmem {
-  static constexpr int KS = DK + 8;        // row stride (u16) of K and Q
-  static constexpr int TS = kC + 8;        // row stride (u16) of K^T and V^T
-  uint16_t K[kC * KS];
-  uint16_t Q[kC * KS];
-  uint16_t Kt[DK * TS];
-  uint16_t Vt[16 * NW * TS];               // this workgroup's V columns, transposed
-  alignas(16) char rec[2][kPrepRecordBytes];
-};
+// the chunks in order.  Each chunk's K, Q, the workgroup's V columns and the chunk
+// record are copied into LDS with direct global-to-LDS loads, one chunk ahead, into
+// a two-stage buffer.  K, Q and V stay row-major with their 16-byte chunks
+// XOR-swizzled by row; K^T and V-column fragments come from the transposing LDS
+// read (for a 16-lane group, lane r addresses X[k0 + r/4][d0 + 4(r mod 4) .. +3]
+// and lane i receives X[k0 + j][d0 + i], j = 0..3).
+typedef short short4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Per-thread register stage of one chunk's inputs (prefetched one chunk ahead).
-// K and V are fetched as (adjacent pair of elements, 8 consecutive tokens) units
-// with 4-byte loads -- a wave's load instruction reads contiguous bytes of one
-// token row -- so that the transposed copies K^T and V^T are written with 16-byte
-// stores.  Q only needs its row-major copy (16-byte units, token-major).
-template <int DK, int NW>
-struct ChunkRegs {
-  static constexpr int NT = 64 * NW;
-  static constexpr int KU = (DK / 2) * (kC / 8);        // (d pair, token group) units of K
-  static constexpr int KPT = (KU + NT - 1) / NT;
-  static constexpr int QU = kC * (DK / 8);              // 16-byte units of Q
-  static constexpr int QPT = (QU + NT - 1) / NT;
-  static constexpr int VU = (8 * NW) * (kC / 8);        // (column pair, token group) units of V
-  static constexpr int VPT = (VU + NT - 1) / NT;
-  uint32_t k[KPT][8], v[VPT][8];
-  u16x8 q[QPT];
-};
+// 8-byte transposing LDS read (for a 16-lane group, lane r addresses
+// X[k0 + r/4][d0 + 4(r mod 4) .. +3] and lane i receives X[k0 + j][d0 + i], j = 0..3).
+HAM_DEVICE u32x2 lds_tr16(const char* base, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) short4s lds_short4;
+  const short4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)((__attribute__((address_space(3))) const char*)base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+#else
+  (void)base; (void)byte_off;
+  return u32x2{};
+#endif
+}
 
-template <int DK, int DV, int NW>
-HAM_DEVICE void load_chunk(const RnnArgs& a, ChunkRegs<DK, NW>& r, int b, int h, int t0, int colbase,
-                           int tid, bool readout) {
-  using R = ChunkRegs<DK, NW>;
-  const uint16_t* k = static_cast<const uint16_t*>(a.k);
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* v = static_cast<const uint16_t*>(a.v);
-  const int nvalid = min(kC, a.T - t0);
-  const size_t rowstride = (size_t)a.H;                 // tokens are H rows apart
-  const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
-  static_assert(R::KU % R::NT == 0 && R::VU % R::NT == 0 && R::QU % R::NT == 0, "uneven staging");
-  if (nvalid == kC) {                       // full chunk: no per-load conditions
-#pragma unroll
-    for (int p = 0; p < R::KPT; ++p) {
-      const int u = tid + p * R::NT;
-      const int dp = u % (DK / 2), tg = u / (DK / 2);
-      const uint16_t* src = k + (tok0 + (size_t)(tg * 8) * rowstride) * DK + 2 * dp;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        r.k[p][j] = *reinterpret_cast<const uint32_t*>(src + (size_t)j * rowstride * DK);
-    }
-#pragma unroll
-    for (int p = 0; p < R::VPT; ++p) {
-      const int u = tid + p * R::NT;
-      const int cp = u % (8 * NW), tg = u / (8 * NW);
-      const uint16_t* src = v + (tok0 + (size_t)(tg * 8) * rowstride) * DV + colbase + 2 * cp;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        r.v[p][j] = *reinterpret_cast<const uint32_t*>(src + (size_t)j * rowstride * DV);
-    }
-    if (readout) {
-#pragma unroll
-      for (int p = 0; p < R::QPT; ++p) {
-        const int u = tid + p * R::NT;
-        const int row = u % kC, cu = (u / kC) * 8;
-        r.q[p] = *reinterpret_cast<const u16x8*>(q + (tok0 + row * rowstride) * DK + cu);
-      }
-    }
-  } else {                                  // tail chunk: zero the rows past T
-#pragma unroll
-    for (int p = 0; p < R::KPT; ++p) {
-      const int u = tid + p * R::NT;
-      const int dp = u % (DK / 2), tg = u / (DK / 2);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = tg * 8 + j;
-        r.k[p][j] = 0u;
-        if (row < nvalid)
-          r.k[p][j] = *reinterpret_cast<const uint32_t*>(k + (tok0 + row * rowstride) * DK + 2 * dp);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < R::VPT; ++p) {
-      const int u = tid + p * R::NT;
-      const int cp = u % (8 * NW), tg = u / (8 * NW);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = tg * 8 + j;
-        r.v[p][j] = 0u;
-        if (row < nvalid)
-          r.v[p][j] = *reinterpret_cast<const uint32_t*>(v + (tok0 + row * rowstride) * DV + colbase + 2 * cp);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < R::QPT; ++p) {
-      const int u = tid + p * R::NT;
-      const int row = u % kC, cu = (u / kC) * 8;
-      r.q[p] = (u16x8)(0);
-      if (readout && row < nvalid)
-        r.q[p] = *reinterpret_cast<const u16x8*>(q + (tok0 + row * rowstride) * DK + cu);
-    }
-  }
+HAM_DEVICE u32x4 cat(const u32x2& a, const u32x2& b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3); }
+HAM_DEVICE bf16x8 as8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
+HAM_DEVICE bf16x4 as4(const u32x2& x) { return __builtin_bit_cast(bf16x4, x); }
+
+// two floats -> two bf16 (nearest even) in one dword, low half first
+HAM_DEVICE uint32_t pk_bf16(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+}
+// (x0, x1) = hi + mid + lo elementwise, each term a packed bf16 pair; the
+// residuals are exact in fp32.
+HAM_DEVICE void split3_pk(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = pk_bf16(x0, x1);
+  float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  m = pk_bf16(r0, r1);
+  r0 -= __uint_as_float(m << 16);
+  r1 -= __uint_as_float(m & 0xffff0000u);
+  l = pk_bf16(r0, r1);
+}
+// four values (one accumulator's rows) -> three 4-element bf16 terms
+HAM_DEVICE void split4(const f32x4& x, u32x2& h, u32x2& m, u32x2& l) {
+  uint32_t h0, m0, l0, h1, m1, l1;
+  split3_pk(x[0], x[1], h0, m0, l0);
+  split3_pk(x[2], x[3], h1, m1, l1);
+  h = u32x2{h0, h1};
+  m = u32x2{m0, m1};
+  l = u32x2{l0, l1};
 }
 
 template <int DK, int NW>
-HAM_DEVICE void store_chunk(ChunkSmem<DK, NW>& sm, const ChunkRegs<DK, NW>& r, int tid) {
-  using R = ChunkRegs<DK, NW>;
-  using SM = ChunkSmem<DK, NW>;
-#pragma unroll
-  for (int p = 0; p < R::KPT; ++p) {
-    const int u = tid + p * R::NT;
-    const int dp = u % (DK / 2), tg = u / (DK / 2);
-    u16x8 lo, hi;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo[j] = (uint16_t)(r.k[p][j] & 0xffffu);
-      hi[j] = (uint16_t)(r.k[p][j] >> 16);
-      *reinterpret_cast<uint32_t*>(&sm.K[(tg * 8 + j) * SM::KS + 2 * dp]) = r.k[p][j];
-    }
-    *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp) * SM::TS + tg * 8]) = lo;
-    *reinterpret_cast<u16x8*>(&sm.Kt[(2 * dp + 1) * SM::TS + tg * 8]) = hi;
-  }
-#pragma unroll
-  for (int p = 0; p < R::VPT; ++p) {
-    const int u = tid + p * R::NT;
-    const int cp = u % (8 * NW), tg = u / (8 * NW);
-    u16x8 lo, hi;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo[j] = (uint16_t)(r.v[p][j] & 0xffffu);
-      hi[j] = (uint16_t)(r.v[p][j] >> 16);
-    }
-    *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp) * SM::TS + tg * 8]) = lo;
-    *reinterpret_cast<u16x8*>(&sm.Vt[(2 * cp + 1) * SM::TS + tg * 8]) = hi;
-  }
-#pragma unroll
-  for (int p = 0; p < R::QPT; ++p) {
-    const int u = tid + p * R::NT;
-    const int row = u % kC, cu = (u / kC) * 8;
-    *reinterpret_cast<u16x8*>(&sm.Q[row * SM::KS + cu]) = r.q[p];
-  }
-}
+struct ChunkLayout {
+  static constexpr int RK = DK * 2;                  // bytes per K / Q row
+  static constexpr int NCK = DK / 8;                 // 16-byte chunks per K / Q row
+  static constexpr int RV = NW * 16 * 2;             // bytes per V-slice row
+  static constexpr int NCV = NW * 2;
+  static constexpr int KB = kC * RK, VB = kC * RV;
+  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_V = 2 * KB, OFF_R = 2 * KB + VB;
+  static constexpr int STAGE = OFF_R + (int)kPrepRecordBytes;
+  static constexpr int KI = KB / 1024 / NW;          // 1 KiB loads per wave: K (and Q), V
+  static constexpr int VI = VB / 1024 / NW;
+  static constexpr int RI = (int)(kPrepRecordBytes / 1024);
+  static_assert(KB % (1024 * NW) == 0 && VB % (1024 * NW) == 0, "tiles must split evenly over the waves");
+  static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
+  // byte offset of 16-byte chunk c of row r in a tile with nch chunks per row,
+  // chunks XOR-swizzled by row
+  HAM_DEVICE static int swz(int r, int c, int rowbytes, int nch) { return r * rowbytes + ((c ^ (r & (nch - 1))) << 4); }
+};
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool RO>
 __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
-  using SM = ChunkSmem<DK, NW>;
-  constexpr int KS = SM::KS, TS = SM::TS;
+  using LY = ChunkLayout<DK, NW>;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
   constexpr int NSL = DV / 16;    // score slices
-  __shared__ SM sm;
+  __shared__ __attribute__((aligned(16))) char smem[2][LY::STAGE];
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.H + h;
   const int colbase = blockIdx.x * 16 * NW;
   const int col = colbase + wave * 16 + n;
-  const int vcol = wave * 16 + n;
   const int slice = blockIdx.x * NW + wave;
-  const bool readout = a.o_rnn32 != nullptr;
-  auto mf32 = [](const bf16x8& x, const bf16x8& y, const f32x4& c) { return mfma_bf16(x, y, c); };
-  auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) { return mfma_bf16_k16(x, y, c); };
+  auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, y, c, 0, 0, 0);
+  };
 
-  // state tiles: S[16*mt + 4g + i][col]
+  // State tiles: element i of tile mt in lane (g, n) is S[srow(mt, g, i)][col] with
+  // srow = 32 (mt/2) + 8g + 4 (mt mod 2) + i.  With this row order the k-slots
+  // 8g..8g+7 of a 32-row step (tiles 2ks, 2ks+1) are the consecutive rows
+  // 32ks + 8g .. +7, so the matching K and Q operands are single 16-byte reads.
+  auto srow = [&](int mt, int i) { return 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i; };
   f32x4 S[MT];
   const size_t sbase = (size_t)bh * DK * DV;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[mt][i] = a.S0 ? a.S0[sbase + (size_t)(16 * mt + 4 * g + i) * DV + col] : 0.f;
+    for (int i = 0; i < 4; ++i) S[mt][i] = 0.f;
+  if (a.S0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[mt][i] = a.S0[sbase + (size_t)srow(mt, i) * DV + col];
+  }
 
   const int nchunk = (a.T + kC - 1) / kC;
   const char* recs = static_cast<const char*>(a.prep) + (size_t)bh * nchunk * kPrepRecordBytes;
-  // direct global-to-LDS copy of one chunk record (1 KiB per wave instruction); the
-  // builtin exists only in the device compilation pass
-#if defined(__HIP_DEVICE_COMPILE__)
-#define HAM_FETCH_RECORD(BUF, REC)                                                         \
-  for (int blk = wave; blk < kRecBlocks; blk += NW)                                        \
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((REC) + blk * 1024 + lane * 16), \
-                                     &sm.rec[(BUF)][blk * 1024], 16, 0, 0)
-#else
-#define HAM_FETCH_RECORD(BUF, REC) (void)(REC)
-#endif
-  ChunkRegs<DK, NW> regs;
-  load_chunk<DK, DV, NW>(a, regs, b, h, 0, colbase, tid, readout);
-  HAM_FETCH_RECORD(0, recs);
+  const char* kbase = static_cast<const char*>(a.k);
+  const char* qbase = static_cast<const char*>(a.q);
+  const char* vbase = static_cast<const char*>(a.v);
 
+  // Direct loads.  Wave w issues the 1 KiB blocks w, w + NW, ... of each tile; lane
+  // l writes the 16 bytes at 16 l of the block.  The source offset of a lane (bytes
+  // from the chunk's first token row of this head) depends on the chunk only through
+  // the clamp of rows past T to the last valid token (finite values whose write
+  // vectors are zero because beta = 0 there), so full chunks reuse precomputed ones.
+  auto k_off = [&](int j, int tlast) {
+    const int tp = (wave + NW * j) * 1024 + lane * 16;
+    const int r = tp / LY::RK, c = ((tp % LY::RK) >> 4) ^ (r & (LY::NCK - 1));
+    return (uint32_t)(min(r, tlast) * a.H * (DK * 2) + c * 16);
+  };
+  auto v_off = [&](int j, int tlast) {
+    const int tp = (wave + NW * j) * 1024 + lane * 16;
+    const int r = tp / LY::RV, c = ((tp % LY::RV) >> 4) ^ (r & (LY::NCV - 1));
+    return (uint32_t)(min(r, tlast) * a.H * (DV * 2) + colbase * 2 + c * 16);
+  };
+  uint32_t koff[LY::KI], voff[LY::VI];
+#pragma unroll
+  for (int j = 0; j < LY::KI; ++j) koff[j] = k_off(j, kC - 1);
+#pragma unroll
+  for (int j = 0; j < LY::VI; ++j) voff[j] = v_off(j, kC - 1);
+
+  auto issue_chunk = [&](int cc, int st) {
+    const int t0 = cc * kC;
+    const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
+    const char* kc = kbase + tok0 * (DK * 2);
+    const char* qc = qbase + tok0 * (DK * 2);
+    const char* vc = vbase + tok0 * (DV * 2);
+    const char* rc = recs + (size_t)cc * kPrepRecordBytes;
+    const uint32_t lo = (uint32_t)lane * 16u;
+    const bool full = t0 + kC <= a.T;
+    char* dst = smem[st];
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int j = 0; j < LY::KI; ++j) {
+      const uint32_t ko = full ? koff[j] : k_off(j, a.T - 1 - t0);
+      const int blk = (wave + NW * j) * 1024;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + ko), dst + LY::OFF_K + blk, 16, 0, 0);
+      if (RO) __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qc + ko), dst + LY::OFF_Q + blk, 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < LY::VI; ++j) {
+      const uint32_t vo = full ? voff[j] : v_off(j, a.T - 1 - t0);
+      const int blk = (wave + NW * j) * 1024;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < (LY::RI + NW - 1) / NW; ++j) {
+      const int blk = (wave + NW * j) * 1024;
+      if (wave + NW * j < LY::RI)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rc + blk + lo), dst + LY::OFF_R + blk, 16, 0, 0);
+    }
+#else
+    (void)kc; (void)qc; (void)vc; (void)rc; (void)lo; (void)full; (void)dst;
+#endif
+  };
+
+  // per-lane output offsets (elements) from the chunk's first token row: the
+  // readout of tokens 4g + 16mt + i, and the score partials of token s_tok (the
+  // token whose row totals this lane ends with after the transposed reduction)
+  const uint32_t o_lane = (uint32_t)((4 * g * a.H + h) * DV + col);
+  const int s_tok = 16 * (n >> 2) + 4 * g + (n & 3);
+  const uint32_t s_lane = (uint32_t)(s_tok * NSL + slice);
+
+  issue_chunk(0, 0);
   for (int c = 0; c < nchunk; ++c) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
-    __builtin_amdgcn_s_waitcnt(0);            // this chunk's registers and record have arrived
-    __syncthreads();                          // the previous chunk's LDS readers are done
-    store_chunk<DK, NW>(sm, regs, tid);
-    if (c + 1 < nchunk) {
-      load_chunk<DK, DV, NW>(a, regs, b, h, t0 + kC, colbase, tid, readout);
-      HAM_FETCH_RECORD((c + 1) & 1, recs + (size_t)(c + 1) * kPrepRecordBytes);
-    }
-    __syncthreads();
-    const char* rec = sm.rec[c & 1];
-    const bf16x8* Af = reinterpret_cast<const bf16x8*>(rec + kRecA);
-    const bf16x8* QKf = reinterpret_cast<const bf16x8*>(rec + kRecQK);
-    const f32x4* Tdf = reinterpret_cast<const f32x4*>(rec + kRecTd);
+    __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
+    __syncthreads();                          // ... for every wave; the other stage is free
+    if (c + 1 < nchunk) issue_chunk(c + 1, (c + 1) & 1);
+    const char* stg = smem[c & 1];
+    const char* Ks = stg + LY::OFF_K;
+    const char* Qs = stg + LY::OFF_Q;
+    const char* Vs = stg + LY::OFF_V;
+    const char* rec = stg + LY::OFF_R;
+    const u32x4* Af = reinterpret_cast<const u32x4*>(rec + kRecA);
+    const u32x4* QKf = reinterpret_cast<const u32x4*>(rec + kRecQK);
+    const u32x2* Tdf = reinterpret_cast<const u32x2*>(rec + kRecTd);
     const float* gam = reinterpret_cast<const float*>(rec + kRecGam);
     const float* wdec = reinterpret_cast<const float*>(rec + kRecW);
 
     // ---- Y_K = K S, Y_Q = Q S ----
+    // A operand of row tile mt, k-step ks: token row 16mt+n, d = 32ks+8g..+7, the
+    // 16-byte chunk 4ks + g of the row.
     f32x4 P[4], O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -506,45 +502,54 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
-      bf16x8 sh, smd, sl;
-      split_pair3(S[2 * ks], S[2 * ks + 1], sh, smd, sl);
+      u32x2 h0, m0, l0, h1, m1, l1;
+      split4(S[2 * ks], h0, m0, l0);
+      split4(S[2 * ks + 1], h1, m1, l1);
+      const bf16x8 sh = as8(cat(h0, h1)), smd = as8(cat(m0, m1)), sl = as8(cat(l0, l1));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const uint16_t* kr = &sm.K[(16 * mt + n) * KS + 32 * ks + 4 * g];
-        const bf16x8 af = frag2(kr, kr + 16);
+        const int oa = LY::swz(16 * mt + n, 4 * ks + g, LY::RK, LY::NCK);
+        const bf16x8 af = as8(*reinterpret_cast<const u32x4*>(Ks + oa));
         P[mt] = mfma_bf16(af, sl, P[mt]);
         P[mt] = mfma_bf16(af, smd, P[mt]);
         P[mt] = mfma_bf16(af, sh, P[mt]);
-        if (readout) {
-          const uint16_t* qr = &sm.Q[(16 * mt + n) * KS + 32 * ks + 4 * g];
-          const bf16x8 qf = frag2(qr, qr + 16);
+        if (RO) {
+          const bf16x8 qf = as8(*reinterpret_cast<const u32x4*>(Qs + oa));
           O[mt] = mfma_bf16(qf, smd, O[mt]);
           O[mt] = mfma_bf16(qf, sh, O[mt]);
         }
       }
     }
+    // this lane's V values V[16mt + 4g + i][wave*16 + n], by transposing reads
+    const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
+    auto v4_at = [&](int mt) {
+      const int r = 16 * mt + 4 * g + vr;
+      const u32x2 x = lds_tr16(Vs, LY::swz(r, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
+      f32x4 f;
+      f[0] = __uint_as_float(x[0] << 16);
+      f[1] = __uint_as_float(x[0] & 0xffff0000u);
+      f[2] = __uint_as_float(x[1] << 16);
+      f[3] = __uint_as_float(x[1] & 0xffff0000u);
+      return f;
+    };
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const f32x4 gm = *reinterpret_cast<const f32x4*>(&gam[16 * mt + 4 * g]);
-      const u16x4 v4 = *reinterpret_cast<const u16x4*>(&sm.Vt[vcol * TS + 16 * mt + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vv = bf16_to_f32(v4[i]);
-        P[mt][i] *= gm[i];
-        O[mt][i] *= gm[i];
-        X[mt][i] = vv - P[mt][i];
-      }
+      const f32x4 v4 = v4_at(mt);
+      P[mt] *= gm;
+      if (RO) O[mt] *= gm;
+      X[mt] = v4 - P[mt];
     }
 
     // ---- block forward substitution: D_i = T'_ii (X_i - sum_{j<i} A_ij D_j) ----
-    // dB[s][*]: B-operand fragments (k-step s) of the D blocks solved so far.
-    bf16x8 dB[2][3];
+    // dB[s][z]: B-operand fragments (k-step s, term z) of the D blocks solved so far.
+    u32x4 dB[2][3];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int z = 0; z < 3; ++z) dB[s][z] = (bf16x8)(0);
+      for (int z = 0; z < 3; ++z) dB[s][z] = (u32x4)(0u);
     f32x4 D[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -552,99 +557,97 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
       for (int s = 0; s <= (i - 1) / 2 && i > 0; ++s) {
         const int pi = pair_index(i, s);
-        R = mma6(mf32, Af[(pi * 3 + 0) * kWave + lane], Af[(pi * 3 + 1) * kWave + lane],
-                 Af[(pi * 3 + 2) * kWave + lane], dB[s][0], dB[s][1], dB[s][2], R);
+        R = mma6(mfma_bf16, as8(Af[(pi * 3 + 0) * kWave + lane]), as8(Af[(pi * 3 + 1) * kWave + lane]),
+                 as8(Af[(pi * 3 + 2) * kWave + lane]), as8(dB[s][0]), as8(dB[s][1]), as8(dB[s][2]), R);
       }
-      float rhs[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rhs[e] = X[i][e] - R[e];
-      bf16x4 rh, rm, rl, th, tm, tl;
-      split3x4(rhs, rh, rm, rl);
-      const f32x4 tv = Tdf[i * kWave + lane];
-      const float tva[4] = {tv[0], tv[1], tv[2], tv[3]};
-      split3x4(tva, th, tm, tl);
-      D[i] = mma6(mf16, th, tm, tl, rh, rm, rl, (f32x4)(0.f));
+      u32x2 rh, rm, rl;
+      split4(X[i] - R, rh, rm, rl);
+      D[i] = mma6(mf16, as4(Tdf[(i * 3 + 0) * kWave + lane]), as4(Tdf[(i * 3 + 1) * kWave + lane]),
+                  as4(Tdf[(i * 3 + 2) * kWave + lane]), as4(rh), as4(rm), as4(rl), (f32x4)(0.f));
       // the diagonal block's share of A D, for the prediction P
       const int half = i & 1;
-      bf16x4 dh4, dm4, dl4;
-      const float dva[4] = {D[i][0], D[i][1], D[i][2], D[i][3]};
-      split3x4(dva, dh4, dm4, dl4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dB[i >> 1][0][4 * half + e] = dh4[e];
-        dB[i >> 1][1][4 * half + e] = dm4[e];
-        dB[i >> 1][2][4 * half + e] = dl4[e];
-      }
+      u32x2 dh, dm, dl;
+      split4(D[i], dh, dm, dl);
+      dB[i >> 1][0][2 * half] = dh[0]; dB[i >> 1][0][2 * half + 1] = dh[1];
+      dB[i >> 1][1][2 * half] = dm[0]; dB[i >> 1][1][2 * half + 1] = dm[1];
+      dB[i >> 1][2][2 * half] = dl[0]; dB[i >> 1][2][2 * half + 1] = dl[1];
       const int pd = pair_index(i, i >> 1);
-      const bf16x8 afh = Af[(pd * 3 + 0) * kWave + lane];
-      const bf16x8 afm = Af[(pd * 3 + 1) * kWave + lane];
-      const bf16x8 afl = Af[(pd * 3 + 2) * kWave + lane];
-      bf16x4 ah4, am4, al4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ah4[e] = afh[4 * half + e];
-        am4[e] = afm[4 * half + e];
-        al4[e] = afl[4 * half + e];
-      }
-      P[i] = mma6(mf16, ah4, am4, al4, dh4, dm4, dl4, P[i] + R);
+      const u32x2* Ah = reinterpret_cast<const u32x2*>(rec + kRecA) + 2 * ((pd * 3) * kWave + lane) + half;
+      P[i] = mma6(mf16, as4(Ah[0]), as4(Ah[2 * kWave]), as4(Ah[4 * kWave]), as4(dh), as4(dm), as4(dl), P[i] + R);
     }
 
     // ---- readout O += (Gamma o Q K^T o lower_incl) D  (bf16 outputs: 3 terms) ----
-    if (readout) {
+    if (RO) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int s = 0; s <= (mt >> 1); ++s) {
           const int pi = pair_index(mt, s);
-          const bf16x8 qh = QKf[(pi * 2 + 0) * kWave + lane], qm = QKf[(pi * 2 + 1) * kWave + lane];
-          O[mt] = mfma_bf16(qm, dB[s][0], O[mt]);
-          O[mt] = mfma_bf16(qh, dB[s][1], O[mt]);
-          O[mt] = mfma_bf16(qh, dB[s][0], O[mt]);
+          const bf16x8 qh = as8(QKf[(pi * 2 + 0) * kWave + lane]), qm = as8(QKf[(pi * 2 + 1) * kWave + lane]);
+          O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
+          O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
+          O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
         }
     }
 
     // ---- score partials of this 16-column slice, and the readout ----
+    const bool full = nvalid == kC;
+    {
+      float xpv[16], xpp[16], xvv[16];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const u16x4 v4 = *reinterpret_cast<const u16x4*>(&sm.Vt[vcol * TS + 16 * mt + 4 * g]);
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 v4 = v4_at(mt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g + i;
-        const float vr = bf16_to_f32(v4[i]);
-        const float pv = row16_sum(P[mt][i] * vr);
-        const float pp = row16_sum(P[mt][i] * P[mt][i]);
-        const float vv = row16_sum(vr * vr);
-        if (t < nvalid) {
-          if (n == 0)
-            a.score[((size_t)bh * a.T + t0 + t) * NSL + slice] = make_float4(pv, pp, vv, 0.f);
-          if (readout)
-            a.o_rnn32[(((size_t)b * a.T + t0 + t) * a.H + h) * DV + col] = O[mt][i];
+        for (int i = 0; i < 4; ++i) {
+          xpv[4 * mt + i] = P[mt][i] * v4[i];
+          xpp[4 * mt + i] = P[mt][i] * P[mt][i];
+          xvv[4 * mt + i] = v4[i] * v4[i];
         }
       }
+      const float pv = row16_transpose_sum(xpv, n);
+      const float pp = row16_transpose_sum(xpp, n);
+      const float vv = row16_transpose_sum(xvv, n);
+      float4* sc = a.score + ((size_t)bh * a.T + t0) * NSL;
+      if (full || s_tok < nvalid) sc[s_lane] = make_float4(pv, pp, vv, 0.f);
+    }
+    if (RO) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tr = 16 * mt + i;                 // token = tr + 4g
+          float* oc = a.o_rnn32 + ((size_t)b * a.T + t0 + tr) * a.H * DV;
+          if (full || tr + 4 * g < nvalid) oc[o_lane] = O[mt][i];
+        }
     }
 
     // ---- S <- gamma_C S + K^T diag(exp(G_C - G)) D ----
     bf16x8 eh[2], em[2], el[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float w0[4], w1[4];
       const f32x4 wa = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 4 * g]);
       const f32x4 wb = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 16 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0[i] = wa[i];
-        w1[i] = wb[i];
-      }
-      split_pair3(D[2 * s], D[2 * s + 1], eh[s], em[s], el[s], w0, w1);
+      u32x2 h0, m0, l0, h1, m1, l1;
+      split4(D[2 * s] * wa, h0, m0, l0);
+      split4(D[2 * s + 1] * wb, h1, m1, l1);
+      eh[s] = as8(cat(h0, h1));
+      em[s] = as8(cat(m0, m1));
+      el[s] = as8(cat(l0, l1));
     }
     const float gl = gam[kC - 1];
+    const int kr4 = n >> 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       S[mt] *= gl;
+      // K^T fragment: output lane 4c + i needs column srow(mt, c, i); lane (k, c) of
+      // the transposing read addresses row k, columns srow(mt, c, 0..3)
+      const int dcol = 32 * (mt >> 1) + 8 * (n & 3) + 4 * (mt & 1);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint16_t* kr = &sm.Kt[(16 * mt + n) * TS + 32 * s + 4 * g];
-        const bf16x8 kf = frag2(kr, kr + 16);
+        const int ra = 32 * s + 4 * g + kr4, rb = ra + 16;
+        const u32x2 ka = lds_tr16(Ks, LY::swz(ra, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
+        const u32x2 kb = lds_tr16(Ks, LY::swz(rb, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
+        const bf16x8 kf = as8(cat(ka, kb));
         S[mt] = mfma_bf16(kf, el[s], S[mt]);
         S[mt] = mfma_bf16(kf, em[s], S[mt]);
         S[mt] = mfma_bf16(kf, eh[s], S[mt]);
@@ -654,10 +657,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a.S_out[sbase + (size_t)(16 * mt + 4 * g + i) * DV + col] = S[mt][i];
-#undef HAM_FETCH_RECORD
+    for (int i = 0; i < 4; ++i) a.S_out[sbase + (size_t)srow(mt, i) * DV + col] = S[mt][i];
 }
-
 template <int DK, int DV, int NW>
 hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kC - 1) / kC;
@@ -665,7 +666,10 @@ hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(DV / (16 * NW), a.H, a.B);
-  hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW>), grid, dim3(64 * NW), 0, s, a);
+  if (a.o_rnn32)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true>), grid, dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
