@@ -139,14 +139,18 @@ template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 // The RNN pass shared by ham_forward and ham_route_stats; returns the slice count.
+// Two timer stages: the chunk prep (empty on the token-serial path) and the state pass.
 int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slices, CallTimer& tm) {
   const bool chunked = !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
                        ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv);
   if (chunked) {
     *slices = ham::rnn_chunked_slices(d->dv);
-    HAM_HIP(ham::launch_rnn_chunked(d->io_dtype, d->dk, d->dv, ra, s));
+    HAM_HIP(ham::launch_rnn_chunked_prep(d->io_dtype, d->dk, ra, s));
+    tm.mark();
+    HAM_HIP(ham::launch_rnn_chunked_state(d->io_dtype, d->dk, d->dv, ra, s));
   } else {
     *slices = ham::rnn_recurrent_slices(d->dv);
+    tm.mark();
     HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
   }
   tm.mark();

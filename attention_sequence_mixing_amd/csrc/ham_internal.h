@@ -110,7 +110,9 @@ struct DecodeCombineArgs {
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
 int rnn_recurrent_slices(int dv);
-hipError_t launch_rnn_chunked(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
+// chunked path: prep (per-chunk records, chunks in parallel), then the state pass
+hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t s);
+hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
 int rnn_chunked_slices(int dv);
 bool rnn_chunked_supported(int io, int dk, int dv);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

@@ -372,7 +372,11 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
   constexpr int NSL = DV / 16;    // score slices
-  __shared__ __attribute__((aligned(16))) char smem[2][LY::STAGE];
+  // Two stages as separate LDS objects: the chunk loop is unrolled by two, so
+  // every access names its stage statically and the compiler can tell that reads
+  // of the current stage do not depend on the direct loads into the other one.
+  __shared__ __attribute__((aligned(16))) char stage0[LY::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[LY::STAGE];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
   for (int j = 0; j < LY::VI; ++j) voff[j] = v_off(j, kC - 1);
 
-  auto issue_chunk = [&](int cc, int st) {
+  auto issue_chunk = [&](int cc, char* dst) {
     const int t0 = cc * kC;
     const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
     const char* kc = kbase + tok0 * (DK * 2);
@@ -440,7 +444,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const char* rc = recs + (size_t)cc * kPrepRecordBytes;
     const uint32_t lo = (uint32_t)lane * 16u;
     const bool full = t0 + kC <= a.T;
-    char* dst = smem[st];
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int j = 0; j < LY::KI; ++j) {
@@ -473,17 +476,33 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const int s_tok = 16 * (n >> 2) + 4 * g + (n & 3);
   const uint32_t s_lane = (uint32_t)(s_tok * NSL + slice);
 
-  issue_chunk(0, 0);
-  for (int c = 0; c < nchunk; ++c) {
+  auto chunk_step = [&](int c, const char* stg, char* nxt) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
     __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
     __syncthreads();                          // ... for every wave; the other stage is free
-    if (c + 1 < nchunk) issue_chunk(c + 1, (c + 1) & 1);
-    const char* stg = smem[c & 1];
+    // This lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads), taken
+    // before the next chunk's direct loads are issued: the compiler orders every
+    // later transposing read after those loads.
+    const char* Vs = stg + LY::OFF_V;
+    u32x2 vraw[4];
+    {
+      const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        vraw[mt] = lds_tr16(Vs, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
+    }
+    auto v4_at = [&](int mt) {
+      f32x4 f;
+      f[0] = __uint_as_float(vraw[mt][0] << 16);
+      f[1] = __uint_as_float(vraw[mt][0] & 0xffff0000u);
+      f[2] = __uint_as_float(vraw[mt][1] << 16);
+      f[3] = __uint_as_float(vraw[mt][1] & 0xffff0000u);
+      return f;
+    };
+    if (c + 1 < nchunk) issue_chunk(c + 1, nxt);
     const char* Ks = stg + LY::OFF_K;
     const char* Qs = stg + LY::OFF_Q;
-    const char* Vs = stg + LY::OFF_V;
     const char* rec = stg + LY::OFF_R;
     const u32x4* Af = reinterpret_cast<const u32x4*>(rec + kRecA);
     const u32x4* QKf = reinterpret_cast<const u32x4*>(rec + kRecQK);
@@ -500,38 +519,38 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       P[mt] = (f32x4)(0.f);
       O[mt] = (f32x4)(0.f);
     }
+    // fragments of k-step ks are read one step ahead of their products
+    u32x4 kf[2][4], qf[2][4];
+    auto load_frags = [&](int ks, int buf) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int oa = LY::swz(16 * mt + n, 4 * ks + g, LY::RK, LY::NCK);
+        kf[buf][mt] = *reinterpret_cast<const u32x4*>(Ks + oa);
+        if (RO) qf[buf][mt] = *reinterpret_cast<const u32x4*>(Qs + oa);
+      }
+    };
+    load_frags(0, 0);
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
+      if (ks + 1 < KSD) load_frags(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);      // keep those reads ahead of this step's products
       u32x2 h0, m0, l0, h1, m1, l1;
       split4(S[2 * ks], h0, m0, l0);
       split4(S[2 * ks + 1], h1, m1, l1);
       const bf16x8 sh = as8(cat(h0, h1)), smd = as8(cat(m0, m1)), sl = as8(cat(l0, l1));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int oa = LY::swz(16 * mt + n, 4 * ks + g, LY::RK, LY::NCK);
-        const bf16x8 af = as8(*reinterpret_cast<const u32x4*>(Ks + oa));
+        const bf16x8 af = as8(kf[ks & 1][mt]);
         P[mt] = mfma_bf16(af, sl, P[mt]);
         P[mt] = mfma_bf16(af, smd, P[mt]);
         P[mt] = mfma_bf16(af, sh, P[mt]);
         if (RO) {
-          const bf16x8 qf = as8(*reinterpret_cast<const u32x4*>(Qs + oa));
-          O[mt] = mfma_bf16(qf, smd, O[mt]);
-          O[mt] = mfma_bf16(qf, sh, O[mt]);
+          const bf16x8 qa = as8(qf[ks & 1][mt]);
+          O[mt] = mfma_bf16(qa, smd, O[mt]);
+          O[mt] = mfma_bf16(qa, sh, O[mt]);
         }
       }
     }
-    // this lane's V values V[16mt + 4g + i][wave*16 + n], by transposing reads
-    const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
-    auto v4_at = [&](int mt) {
-      const int r = 16 * mt + 4 * g + vr;
-      const u32x2 x = lds_tr16(Vs, LY::swz(r, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
-      f32x4 f;
-      f[0] = __uint_as_float(x[0] << 16);
-      f[1] = __uint_as_float(x[0] & 0xffff0000u);
-      f[2] = __uint_as_float(x[1] << 16);
-      f[3] = __uint_as_float(x[1] & 0xffff0000u);
-      return f;
-    };
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
@@ -611,14 +630,20 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       if (full || s_tok < nvalid) sc[s_lane] = make_float4(pv, pp, vv, 0.f);
     }
     if (RO) {
+      float* oc = a.o_rnn32 + ((size_t)b * a.T + t0) * a.H * DV;
+      const uint32_t rs = (uint32_t)(a.H * DV);
+      if (full) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tr = 16 * mt + i;                 // token = tr + 4g
-          float* oc = a.o_rnn32 + ((size_t)b * a.T + t0 + tr) * a.H * DV;
-          if (full || tr + 4 * g < nvalid) oc[o_lane] = O[mt][i];
-        }
+          for (int i = 0; i < 4; ++i) oc[o_lane + (uint32_t)(16 * mt + i) * rs] = O[mt][i];
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * mt + i + 4 * g < nvalid) oc[o_lane + (uint32_t)(16 * mt + i) * rs] = O[mt][i];
+      }
     }
 
     // ---- S <- gamma_C S + K^T diag(exp(G_C - G)) D ----
@@ -647,24 +672,35 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         const int ra = 32 * s + 4 * g + kr4, rb = ra + 16;
         const u32x2 ka = lds_tr16(Ks, LY::swz(ra, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
         const u32x2 kb = lds_tr16(Ks, LY::swz(rb, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
-        const bf16x8 kf = as8(cat(ka, kb));
-        S[mt] = mfma_bf16(kf, el[s], S[mt]);
-        S[mt] = mfma_bf16(kf, em[s], S[mt]);
-        S[mt] = mfma_bf16(kf, eh[s], S[mt]);
+        const bf16x8 kt = as8(cat(ka, kb));
+        S[mt] = mfma_bf16(kt, el[s], S[mt]);
+        S[mt] = mfma_bf16(kt, em[s], S[mt]);
+        S[mt] = mfma_bf16(kt, eh[s], S[mt]);
       }
     }
+  };
+
+  issue_chunk(0, stage0);
+  for (int c = 0; c < nchunk; c += 2) {
+    chunk_step(c, stage0, stage1);
+    if (c + 1 < nchunk) chunk_step(c + 1, stage1, stage0);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) a.S_out[sbase + (size_t)srow(mt, i) * DV + col] = S[mt][i];
 }
-template <int DK, int DV, int NW>
-hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
+template <int DK>
+hipError_t launch_prep_t(const RnnArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kC - 1) / kC;
   hipLaunchKernelGGL((rnn_prep_kernel<DK>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// Four waves (64 state columns) per workgroup.
+template <int DK, int DV>
+hipError_t launch_state_t(const RnnArgs& a, hipStream_t s) {
+  constexpr int NW = 4;
   dim3 grid(DV / (16 * NW), a.H, a.B);
   if (a.o_rnn32)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true>), grid, dim3(64 * NW), 0, s, a);
@@ -673,13 +709,7 @@ hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Four waves (64 state columns) per workgroup.
-template <int DK, int DV>
-hipError_t launch_dims(const RnnArgs& a, hipStream_t s) { return launch_t<DK, DV, 4>(a, s); }
-
 }  // namespace chunked
-
-using chunked::launch_dims;
 
 bool rnn_chunked_supported(int io, int dk, int dv) {
   return io == 1 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
@@ -687,12 +717,19 @@ bool rnn_chunked_supported(int io, int dk, int dv) {
 
 int rnn_chunked_slices(int dv) { return dv / 16; }
 
-hipError_t launch_rnn_chunked(int io, int dk, int dv, const RnnArgs& a, hipStream_t s) {
+hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t s) {
   if (io != 1) return hipErrorInvalidValue;
-  if (dk == 64 && dv == 64) return launch_dims<64, 64>(a, s);
-  if (dk == 64 && dv == 128) return launch_dims<64, 128>(a, s);
-  if (dk == 128 && dv == 64) return launch_dims<128, 64>(a, s);
-  if (dk == 128 && dv == 128) return launch_dims<128, 128>(a, s);
+  if (dk == 64) return chunked::launch_prep_t<64>(a, s);
+  if (dk == 128) return chunked::launch_prep_t<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hipStream_t s) {
+  if (io != 1) return hipErrorInvalidValue;
+  if (dk == 64 && dv == 64) return chunked::launch_state_t<64, 64>(a, s);
+  if (dk == 64 && dv == 128) return chunked::launch_state_t<64, 128>(a, s);
+  if (dk == 128 && dv == 64) return chunked::launch_state_t<128, 64>(a, s);
+  if (dk == 128 && dv == 128) return chunked::launch_state_t<128, 128>(a, s);
   return hipErrorInvalidValue;
 }
 

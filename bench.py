@@ -40,18 +40,28 @@ def rnn_flops_per_token_head(d, C=CHUNK):
     return 1 + 3.5 * C + C * C / 2 + 6 * C * d + 4 * C * d + 6 * d * d + 12 * d
 
 
+def rnn_prep_flops_per_token_head(d, C=CHUNK):
+    """The Tab. E.11 rows done by the chunk-parallel prep kernel: g cumsum,
+    compute A (C(2d + 3.5) per token), invert A (C^2/2) and the Q K^T half of the
+    output row (2 C d)."""
+    return 1 + 3.5 * C + C * C / 2 + 2 * C * d + 2 * C * d
+
+
+def rnn_state_flops_per_token_head(d, C=CHUNK):
+    """The rest of Tab. E.11 (recompute w/u 4Cd, the state recurrence 4d^2, the
+    output's 2d^2 + 2Cd) plus the 12d selection term of Tab. E.13: the state kernel."""
+    return rnn_flops_per_token_head(d, C) - rnn_prep_flops_per_token_head(d, C)
+
+
 def attn_flops_per_pair(d):
     """QK^T 2d + softmax 4 + PV 2d per visible (query, key) pair (Tab. E.12)."""
     return 4 * d + 4
 
 
-def profile_stages(lib, fn, n):
+def collect_stages(lib, n):
+    """Stage times (ms, mean over the recorded calls) from the library's HIP events,
+    which it records on the launch stream around each kernel of the armed calls."""
     import ctypes
-    import torch
-    lib.ham_profile_start(n)
-    for _ in range(n):
-        fn()
-    torch.cuda.synchronize()
     S = 5
     buf = (ctypes.c_float * (n * S))()
     ncalls = ctypes.c_int(0)
@@ -89,6 +99,10 @@ def bench_forward(args, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed steps themselves carry the per-kernel HIP events (recorded by the
+    # library on the launch stream, which is torch's current stream here).
+    lib = _lib.lib()
+    lib.ham_profile_start(args.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     e0.record()
@@ -98,7 +112,7 @@ def bench_forward(args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms = e0.elapsed_time(e1) / args.steps
-    stages = profile_stages(_lib.lib(), step, args.steps)
+    stages = collect_stages(lib, args.steps)
 
     routed = plan.routed
     count = plan.count
@@ -108,25 +122,27 @@ def bench_forward(args, dev):
     BTH = w.B * w.T * w.H
     d = w.d
     rnn_flops = BTH * rnn_flops_per_token_head(d)
+    state_flops = BTH * rnn_state_flops_per_token_head(d)
     att_flops = pairs * attn_flops_per_pair(d)
     nroute = float(count.sum().item())
     # algorithmic bytes (inputs read once, outputs written once)
-    rnn_bytes = BTH * (3 * d * 2 + 8 + 16 * 8 + d * 4)          # q,k,v bf16, beta/g, score partials, o_rnn fp32
-    route_bytes = BTH * (16 * 8 + 4 + 1)
+    prep_bytes = BTH * (2 * d * 2 + 8)                          # q, k bf16; beta, g fp32
+    route_bytes = BTH * (16 * 8 + 4 + 1)                        # score partials in; e, routed out
     compact_bytes = BTH * (1 + 4) + nroute * (2 * (2 * d * 2) + 4)
-    attn_bytes = BTH * (d * 2 + d * 4 + 4 + d * 2) + w.B * w.H * 0 + nroute * 2 * d * 2
-    names = ["rnn", "route", "compact", "attention"]
+    # Each kernel is priced against the roof of the arithmetic it runs: the prep
+    # kernel's Gram products are a small share of its HBM traffic (67 FLOP/B); the
+    # state kernel and attention run bf16 MFMA (the state kernel's fp32-accurate
+    # products as split bf16 terms; only algorithmic FLOPs are counted).
+    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
     per = []
     for i, nm in enumerate(names):
         sec = stages[i] / 1e3
-        if nm == "rnn":
-            per.append(dict(stage=nm, ms=stages[i], bound="alu", unit="TFLOP/s",
-                            achieved=rnn_flops / sec / 1e12, peak=PEAK_FP32_TFLOPS))
-        elif nm == "attention":
+        if nm in ("rnn_state", "attention"):
+            f = state_flops if nm == "rnn_state" else att_flops
             per.append(dict(stage=nm, ms=stages[i], bound="mfma", unit="TFLOP/s",
-                            achieved=att_flops / sec / 1e12, peak=PEAK_BF16_TFLOPS))
+                            achieved=f / sec / 1e12, peak=PEAK_BF16_TFLOPS))
         else:
-            b = route_bytes if nm == "route" else compact_bytes
+            b = {"rnn_prep": prep_bytes, "route": route_bytes, "compact": compact_bytes}[nm]
             per.append(dict(stage=nm, ms=stages[i], bound="hbm", unit="GB/s",
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
@@ -173,25 +189,16 @@ def bench_decode(args, dev):
     run_all()                               # warm-up pass over the same steps
     torch.cuda.synchronize()
     S.copy_(S0); count.copy_(count0)
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)            # per-kernel HIP events on the timed steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     run_all()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    stg = collect_stages(lib, steps)
     cache_keys1 = float(count.sum().item())
-    S.copy_(S0); count.copy_(count0)
-    # per-stage timing over all steps
-    L = _lib.lib()
-    L.ham_profile_start(steps)
-    run_all()
-    torch.cuda.synchronize()
-    import ctypes
-    buf = (ctypes.c_float * (steps * 5))()
-    n = ctypes.c_int(0)
-    L.ham_profile_stop(buf, steps * 5, ctypes.byref(n), None)
-    stg = [float(x) for x in np.frombuffer(buf, dtype=np.float32).reshape(steps, 5)[: n.value]
-           .astype(np.float64).mean(axis=0)]
     mean_keys = 0.5 * (cache_keys0 + cache_keys1)
     cache_bytes = mean_keys * 2 * d * 2                     # K and V rows, bf16
     state_bytes = B * H * d * d * 4 * 2                     # S read + write
@@ -207,23 +214,29 @@ def bench_decode(args, dev):
                 roofline=roof)
 
 
-def cpu_baseline(res, heads):
+def cpu_baseline(res, nbatch):
+    """The fp64 C oracle, as it stands, on the first nbatch sequences of the same
+    workload and threshold (all heads, all tokens), threads over heads."""
     import oracle
     w = res["w"]
     inp = res["inp"]
-    hs = list(range(heads))
-    sub = {n: np.ascontiguousarray(a[0:1, :, hs]) for n, a in inp.items()}
-    tau = res["tau"][hs]
-    threads = min(16, heads, os.cpu_count() or 1)
-    oracle.forward(**{n: a[:, :64] for n, a in sub.items()}, tau=tau, scale=w.attn_scale,
-                   threads=threads)   # compile/load outside the timing
+    nb = max(1, min(nbatch, w.B))
+    sub = {n: np.ascontiguousarray(a[0:nb]) for n, a in inp.items()}
+    tau = res["tau"]
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, w.H * nb, avail))
+    oracle.forward(**{n: a[:1, :64] for n, a in sub.items()}, tau=tau, scale=w.attn_scale,
+                   threads=threads)   # load outside the timing
     t0 = time.perf_counter()
     oracle.forward(**sub, tau=tau, scale=w.attn_scale, threads=threads)
     sec = time.perf_counter() - t0
-    tokens = heads * w.T / w.H       # one token = all H heads of one position
+    tokens = nb * w.T
     return dict(value=tokens / sec, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"b=0, heads 0..{heads - 1} of {w.name}, all {w.T} tokens, fp64 C oracle, "
-                       f"{sec:.1f}s; scaled as {heads}/{w.H} of a token per head-token")
+                sample=f"sequences 0..{nb - 1} of {w.name} (all {w.H} heads, all {w.T} tokens, "
+                       f"same tau), fp64 C oracle, {sec:.1f}s wall on {threads} threads")
 
 
 def main():
@@ -233,7 +246,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-prefix", type=int, default=0)
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-batch", type=int, default=8,
+                    help="sequences of the layer workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -253,7 +267,7 @@ def main():
     if not args.no_decode:
         dec = bench_decode(args, dev)
         log(f"[bench] decode {dec['us_per_step']:.1f} us/step, stages {dec['stages_ms']}")
-    cpu = None if args.no_cpu else cpu_baseline(res, args.cpu_heads)
+    cpu = None if args.no_cpu else cpu_baseline(res, args.cpu_batch)
     w = res["w"]
     dom = res["dom"]
     roof = dict(bound=dom["bound"], achieved=round(dom["achieved"], 3), peak=dom["peak"],

@@ -191,9 +191,11 @@ int ham_route_stats(const ham_dims *dims,
  * events and writes stage_ms[call * HAM_PROFILE_STAGES + stage] (milliseconds,
  * 0 for unused stages) for at most max_values values, the number of recorded
  * calls to *n_calls and each call's entry point to kinds[call] (0 forward,
- * 1 decode, 2 route_stats; kinds may be NULL).  Stages: forward {rnn, route,
- * compact, attention}; decode {rnn, route, append, attention, combine};
- * route_stats {rnn, route, stats}.  Returns HAM_OK, HAM_EINVAL or HAM_EHIP.
+ * 1 decode, 2 route_stats; kinds may be NULL).  Stages: forward {rnn_prep,
+ * rnn_state, route, compact, attention}; decode {rnn, route, append, attention,
+ * combine}; route_stats {rnn_prep, rnn_state, route, stats}.  rnn_prep is the
+ * chunk-parallel part of the chunked recurrence (0 on the token-serial path).
+ * Returns HAM_OK, HAM_EINVAL or HAM_EHIP.
  */
 #define HAM_PROFILE_STAGES 5
 int ham_profile_start(int max_calls);
