@@ -85,12 +85,13 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
 // offsets in bytes; 16-byte lane entries are in MFMA operand order):
 //   [0, 18432)       A  fragments: 6 (row tile, k-step) pairs x 3 splits x 64 lanes
 //   [18432, 30720)   QK fragments: 6 pairs x 2 splits x 64 lanes
-//   [30720, 36864)   T'_ii = (I + diag(beta) A_ii)^-1 diag(beta): 4 blocks x 3 splits
-//                    x 64 lanes of 4 bf16; lane (g,n) holds row n, columns 4g..4g+3
-//   [36864, 37120)   gamma_t = exp(G_t)                (fp32 x 64)
-//   [37120, 37376)   w_t = exp(G_last - G_t)           (fp32 x 64)
-//   [37376, 37888)   padding to whole 1 KiB blocks
-constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 36864, kRecW = 37120;
+//   [30720, 43008)   T'_I = (I + diag(beta) A_II)^-1 diag(beta) of the two 32-token
+//                    diagonal blocks: 2 blocks x 2 row tiles x 3 splits x 64 lanes, in
+//                    the same operand order as the A fragments
+//   [43008, 43264)   gamma_t = exp(G_t)                (fp32 x 64)
+//   [43264, 43520)   w_t = exp(G_last - G_t)           (fp32 x 64)
+//   [43520, 44032)   padding to whole 1 KiB blocks
+constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 43008, kRecW = 43264;
 static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
 
 // Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
@@ -135,6 +136,9 @@ struct PrepSmem {
   uint16_t Q[kC * KS];
   float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
   alignas(16) float Td[4][16][20];         // (I + Ld)^-1 diag(beta)
+  float Aoff[2][16][17];                   // A blocks (rows 16-block 2I+1, cols 16-block 2I)
+  float W[2][16][17];                      // Aoff T'_{2I}
+  alignas(16) float Off[2][16][20];        // -T'_{2I+1} Aoff T'_{2I}
   alignas(16) float G2[kC];
   alignas(16) float beta[kC];
 };
@@ -168,6 +172,7 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
       const bool keep = kQK ? (j <= t) : (j < t);
       val[hh][i] = keep ? acc[i] * __builtin_amdgcn_exp2f(gt - gj[i]) : 0.f;
       if (!kQK && jt == mt) sm.Ld[mt][n][4 * g + i] = sm.beta[t] * val[hh][i];
+      if (!kQK && (mt & 1) && jt == mt - 1) sm.Aoff[mt >> 1][n][4 * g + i] = val[hh][i];
     }
   }
   const int pi = pair_index(mt, s);
@@ -277,14 +282,39 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
     for (int r = 0; r < 16; ++r) sm.Td[bb][r][cc] = colv[r] * bc;
   }
   __syncthreads();
+  // 32-token diagonal blocks: T'_I = [[T'_{2I}, 0], [-T'_{2I+1} A_{2I+1,2I} T'_{2I}, T'_{2I+1}]]
+  // (block inverse of the unit lower-triangular I + diag(beta) A, times diag(beta))
+  for (int idx = tid; idx < 512; idx += 256) {
+    const int I = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+    float acc = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) acc = fmaf(sm.Aoff[I][r][k2], sm.Td[2 * I][k2][cc], acc);
+    sm.W[I][r][cc] = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 512; idx += 256) {
+    const int I = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+    float acc = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) acc = fmaf(sm.Td[2 * I + 1][r][k2], sm.W[I][k2][cc], acc);
+    sm.Off[I][r][cc] = -acc;
+  }
+  __syncthreads();
   {
-    // lane order: entry (block i, split z, lane (g,n)) = row n, columns 4g..4g+3
-    const int i = tid >> 6;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Td[i][n][4 * g]);
-    const float xa[4] = {x[0], x[1], x[2], x[3]};
-    bf16x4 th, tm, tl;
-    split3x4(xa, th, tm, tl);
-    bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecTd) + (i * 3) * kWave + lane;
+    // wave (I, r): row tile r of block I; lane (g,n) holds row n, columns 4g..4g+3
+    // (k-slots 0..3) and 16+4g..16+4g+3 (k-slots 4..7) of the 32 block columns
+    const int I = wave >> 1, r = wave & 1;
+    f32x4 lo, hi;
+    if (r == 0) {
+      lo = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I][n][4 * g]);
+      hi = (f32x4)(0.f);
+    } else {
+      lo = *reinterpret_cast<const f32x4*>(&sm.Off[I][n][4 * g]);
+      hi = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I + 1][n][4 * g]);
+    }
+    bf16x8 th, tm, tl;
+    split_pair3(lo, hi, th, tm, tl);
+    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecTd) + (wave * 3) * kWave + lane;
     dst[0] = th;
     dst[kWave] = tm;
     dst[2 * kWave] = tl;
@@ -354,7 +384,8 @@ struct ChunkLayout {
   static constexpr int RV = NW * 16 * 2;             // bytes per V-slice row
   static constexpr int NCV = NW * 2;
   static constexpr int KB = kC * RK, VB = kC * RV;
-  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_V = 2 * KB, OFF_R = 2 * KB + VB;
+  // a stage holds K, Q and the chunk record; the V slice has one buffer of its own
+  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_R = 2 * KB;
   static constexpr int STAGE = OFF_R + (int)kPrepRecordBytes;
   static constexpr int KI = KB / 1024 / NW;          // 1 KiB loads per wave: K (and Q), V
   static constexpr int VI = VB / 1024 / NW;
@@ -377,18 +408,21 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // of the current stage do not depend on the direct loads into the other one.
   __shared__ __attribute__((aligned(16))) char stage0[LY::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[LY::STAGE];
+  __shared__ __attribute__((aligned(16))) char vbuf[LY::VB];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int bh = b * a.H + h;
-  const int colbase = blockIdx.x * 16 * NW;
+  // 1-D grid of (head, column block) pairs, renumbered so that the column blocks
+  // of one head run on the same XCD and share its L2 (they read the same K, Q and
+  // chunk records).
+  constexpr int NCB = DV / (16 * NW);                       // column blocks per head
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int cb = lin % NCB, bh = lin / NCB;
+  const int h = bh % a.H, b = bh / a.H;
+  const int colbase = cb * 16 * NW;
   const int col = colbase + wave * 16 + n;
-  const int slice = blockIdx.x * NW + wave;
-  auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, y, c, 0, 0, 0);
-  };
+  const int slice = cb * NW + wave;
 
   // State tiles: element i of tile mt in lane (g, n) is S[srow(mt, g, i)][col] with
   // srow = 32 (mt/2) + 8g + 4 (mt mod 2) + i.  With this row order the k-slots
@@ -414,7 +448,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const char* qbase = static_cast<const char*>(a.q);
   const char* vbase = static_cast<const char*>(a.v);
 
-  // Direct loads.  Wave w issues the 1 KiB blocks w, w + NW, ... of each tile; lane
+  // Direct loads of chunk cc: K, Q and the record into the stage dst, the V slice
+  // into its single buffer.  Wave w issues the 1 KiB blocks w, w + NW, ... of each tile; lane
   // l writes the 16 bytes at 16 l of the block.  The source offset of a lane (bytes
   // from the chunk's first token row of this head) depends on the chunk only through
   // the clamp of rows past T to the last valid token (finite values whose write
@@ -456,7 +491,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     for (int j = 0; j < LY::VI; ++j) {
       const uint32_t vo = full ? voff[j] : v_off(j, a.T - 1 - t0);
       const int blk = (wave + NW * j) * 1024;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), vbuf + blk, 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < (LY::RI + NW - 1) / NW; ++j) {
@@ -479,19 +514,18 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   auto chunk_step = [&](int c, const char* stg, char* nxt) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
-    __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
+    __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles, record and V have arrived
     __syncthreads();                          // ... for every wave; the other stage is free
-    // This lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads), taken
-    // before the next chunk's direct loads are issued: the compiler orders every
-    // later transposing read after those loads.
-    const char* Vs = stg + LY::OFF_V;
+    // This lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads); the
+    // second barrier frees the V buffer for the next chunk.
     u32x2 vraw[4];
     {
       const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        vraw[mt] = lds_tr16(Vs, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
+        vraw[mt] = lds_tr16(vbuf, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
     }
+    __syncthreads();
     auto v4_at = [&](int mt) {
       f32x4 f;
       f[0] = __uint_as_float(vraw[mt][0] << 16);
@@ -506,7 +540,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const char* rec = stg + LY::OFF_R;
     const u32x4* Af = reinterpret_cast<const u32x4*>(rec + kRecA);
     const u32x4* QKf = reinterpret_cast<const u32x4*>(rec + kRecQK);
-    const u32x2* Tdf = reinterpret_cast<const u32x2*>(rec + kRecTd);
     const float* gam = reinterpret_cast<const float*>(rec + kRecGam);
     const float* wdec = reinterpret_cast<const float*>(rec + kRecW);
 
@@ -562,38 +595,44 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       X[mt] = v4 - P[mt];
     }
 
-    // ---- block forward substitution: D_i = T'_ii (X_i - sum_{j<i} A_ij D_j) ----
-    // dB[s][z]: B-operand fragments (k-step s, term z) of the D blocks solved so far.
+    // ---- block forward substitution over the two 32-token blocks ----
+    //   D_0 = T'_0 X_0,   D_1 = T'_1 (X_1 - A_10 D_0),   P += A D (strictly lower A)
+    // dB[s][z]: B-operand fragments (k-step s, term z) of D rows 32s..32s+31.
+    const u32x4* T32 = reinterpret_cast<const u32x4*>(rec + kRecTd);
+    auto A_at = [&](int mt, int s, int z) { return as8(Af[(pair_index(mt, s) * 3 + z) * kWave + lane]); };
     u32x4 dB[2][3];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int z = 0; z < 3; ++z) dB[s][z] = (u32x4)(0u);
     f32x4 D[4];
+    auto solve_block = [&](int I, const f32x4& x0, const f32x4& x1) {
+      u32x2 h0, m0, l0, h1, m1, l1;
+      split4(x0, h0, m0, l0);
+      split4(x1, h1, m1, l1);
+      const bf16x8 rh = as8(cat(h0, h1)), rm = as8(cat(m0, m1)), rl = as8(cat(l0, l1));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 R = (f32x4)(0.f);
-#pragma unroll
-      for (int s = 0; s <= (i - 1) / 2 && i > 0; ++s) {
-        const int pi = pair_index(i, s);
-        R = mma6(mfma_bf16, as8(Af[(pi * 3 + 0) * kWave + lane]), as8(Af[(pi * 3 + 1) * kWave + lane]),
-                 as8(Af[(pi * 3 + 2) * kWave + lane]), as8(dB[s][0]), as8(dB[s][1]), as8(dB[s][2]), R);
+      for (int r = 0; r < 2; ++r) {
+        const u32x4* t = T32 + ((I * 2 + r) * 3) * kWave + lane;
+        D[2 * I + r] = mma6(mfma_bf16, as8(t[0]), as8(t[kWave]), as8(t[2 * kWave]), rh, rm, rl, (f32x4)(0.f));
       }
-      u32x2 rh, rm, rl;
-      split4(X[i] - R, rh, rm, rl);
-      D[i] = mma6(mf16, as4(Tdf[(i * 3 + 0) * kWave + lane]), as4(Tdf[(i * 3 + 1) * kWave + lane]),
-                  as4(Tdf[(i * 3 + 2) * kWave + lane]), as4(rh), as4(rm), as4(rl), (f32x4)(0.f));
-      // the diagonal block's share of A D, for the prediction P
-      const int half = i & 1;
-      u32x2 dh, dm, dl;
-      split4(D[i], dh, dm, dl);
-      dB[i >> 1][0][2 * half] = dh[0]; dB[i >> 1][0][2 * half + 1] = dh[1];
-      dB[i >> 1][1][2 * half] = dm[0]; dB[i >> 1][1][2 * half + 1] = dm[1];
-      dB[i >> 1][2][2 * half] = dl[0]; dB[i >> 1][2][2 * half + 1] = dl[1];
-      const int pd = pair_index(i, i >> 1);
-      const u32x2* Ah = reinterpret_cast<const u32x2*>(rec + kRecA) + 2 * ((pd * 3) * kWave + lane) + half;
-      P[i] = mma6(mf16, as4(Ah[0]), as4(Ah[2 * kWave]), as4(Ah[4 * kWave]), as4(dh), as4(dm), as4(dl), P[i] + R);
-    }
+      split4(D[2 * I], h0, m0, l0);
+      split4(D[2 * I + 1], h1, m1, l1);
+      dB[I][0] = cat(h0, h1);
+      dB[I][1] = cat(m0, m1);
+      dB[I][2] = cat(l0, l1);
+    };
+    solve_block(0, X[0], X[1]);
+    const f32x4 R2 = mma6(mfma_bf16, A_at(2, 0, 0), A_at(2, 0, 1), A_at(2, 0, 2),
+                          as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), (f32x4)(0.f));
+    const f32x4 R3 = mma6(mfma_bf16, A_at(3, 0, 0), A_at(3, 0, 1), A_at(3, 0, 2),
+                          as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), (f32x4)(0.f));
+    solve_block(1, X[2] - R2, X[3] - R3);
+    // the prediction P = gamma K S + A D
+    P[0] = mma6(mfma_bf16, A_at(0, 0, 0), A_at(0, 0, 1), A_at(0, 0, 2),
+                as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), P[0]);
+    P[1] = mma6(mfma_bf16, A_at(1, 0, 0), A_at(1, 0, 1), A_at(1, 0, 2),
+                as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), P[1]);
+    P[2] = mma6(mfma_bf16, A_at(2, 1, 0), A_at(2, 1, 1), A_at(2, 1, 2),
+                as8(dB[1][0]), as8(dB[1][1]), as8(dB[1][2]), P[2] + R2);
+    P[3] = mma6(mfma_bf16, A_at(3, 1, 0), A_at(3, 1, 1), A_at(3, 1, 2),
+                as8(dB[1][0]), as8(dB[1][1]), as8(dB[1][2]), P[3] + R3);
 
     // ---- readout O += (Gamma o Q K^T o lower_incl) D  (bf16 outputs: 3 terms) ----
     if (RO) {
@@ -701,7 +740,7 @@ hipError_t launch_prep_t(const RnnArgs& a, hipStream_t s) {
 template <int DK, int DV>
 hipError_t launch_state_t(const RnnArgs& a, hipStream_t s) {
   constexpr int NW = 4;
-  dim3 grid(DV / (16 * NW), a.H, a.B);
+  dim3 grid((DV / (16 * NW)) * a.H * a.B);
   if (a.o_rnn32)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true>), grid, dim3(64 * NW), 0, s, a);
   else

@@ -34,6 +34,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def copy_calibration(dev):
+    """A plain device copy of known size (1 GiB read, 1 GiB written), three times:
+    the reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 copies of {n} bytes")
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_layer_bf16_B8_H16_T4096_d128.md")
+
+
+def measured_traffic(kernel_prefix):
+    """HBM bytes per launch of a kernel from the committed counter summary, or None
+    when there is no summary for it or the kernel source changed since (the summary
+    records the SHA-256 of the source file it was taken with)."""
+    import hashlib
+    import re
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m = re.search(r"^traffic\s+" + re.escape(kernel_prefix) + r"\s+(\S+)\s+(\d+)\s+(\S+)\s*$", text, re.M)
+    if not m:
+        return None
+    src, nbytes, sha = m.group(1), int(m.group(2)), m.group(3)
+    path = os.path.join(ROOT, src)
+    if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != sha:
+        return None
+    return nbytes
+
+
 def rnn_flops_per_token_head(d, C=CHUNK):
     """Chunked gated delta rule per token and head (C = 64) plus the fit-error
     score: Tab. E.11 subtotal per head + the Tab. E.13 selection term."""
@@ -249,6 +286,8 @@ def main():
     ap.add_argument("--cpu-batch", type=int, default=8,
                     help="sequences of the layer workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the HAM layer on a single MI355X "
@@ -256,6 +295,9 @@ def main():
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
     p = torch.cuda.get_device_properties(dev)
     log(f"[bench] device {p.name} {getattr(p, 'gcnArchName', '')} CUs={p.multi_processor_count} "
         f"mem={p.total_memory / 2**30:.0f} GiB")
@@ -270,8 +312,9 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(res, args.cpu_batch)
     w = res["w"]
     dom = res["dom"]
+    traffic = measured_traffic(dom["stage"])
     roof = dict(bound=dom["bound"], achieved=round(dom["achieved"], 3), peak=dom["peak"],
-                unit=dom["unit"], frac=round(dom["frac"], 4), traffic=None, kernel=dom["stage"])
+                unit=dom["unit"], frac=round(dom["frac"], 4), traffic=traffic, kernel=dom["stage"])
     out = {
         "metric": "HAM layer fwd tokens/sec at T=4096, rho_KV=0.5; decode us/token at 32k",
         "value": round(res["tokens_per_s"], 1),
