@@ -56,7 +56,6 @@ def measured_traffic(kernel_prefix):
     """HBM bytes per launch of a kernel from the committed counter summary, or None
     when there is no summary for it or the kernel source changed since (the summary
     records the SHA-256 of the source file it was taken with)."""
-    import hashlib
     import re
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
@@ -65,10 +64,22 @@ def measured_traffic(kernel_prefix):
     if not m:
         return None
     src, nbytes, sha = m.group(1), int(m.group(2)), m.group(3)
-    path = os.path.join(ROOT, src)
-    if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != sha:
+    if kernel_source_sha(src) != sha:
         return None
     return nbytes
+
+
+def kernel_source_sha(src):
+    """SHA-256 over a kernel's source file and the two shared device headers."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_sequence_mixing_amd", "csrc")
+    for path in (os.path.join(ROOT, src), os.path.join(csrc, "ham_common.h"),
+                 os.path.join(csrc, "ham_internal.h")):
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def rnn_flops_per_token_head(d, C=CHUNK):
