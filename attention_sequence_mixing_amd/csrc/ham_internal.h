@@ -27,7 +27,7 @@ struct RnnArgs {
 };
 
 // Bytes of one chunk record written by the chunked path's prep kernel.
-constexpr size_t kPrepRecordBytes = 44032;
+constexpr size_t kPrepRecordBytes = 35840;
 
 struct RouteArgs {
   const float4* score;  // [B*H][T][slices]

@@ -82,20 +82,31 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
 
 // ---------------------------------------------------------------------------------
 // Chunk record written by the prep kernel and streamed by the state kernel (all
-// offsets in bytes; 16-byte lane entries are in MFMA operand order):
-//   [0, 18432)       A  fragments: 6 (row tile, k-step) pairs x 3 splits x 64 lanes
-//   [18432, 30720)   QK fragments: 6 pairs x 2 splits x 64 lanes
-//   [30720, 43008)   T'_I = (I + diag(beta) A_II)^-1 diag(beta) of the two 32-token
-//                    diagonal blocks: 2 blocks x 2 row tiles x 3 splits x 64 lanes, in
-//                    the same operand order as the A fragments
-//   [43008, 43264)   gamma_t = exp(G_t)                (fp32 x 64)
-//   [43264, 43520)   w_t = exp(G_last - G_t)           (fp32 x 64)
-//   [43520, 44032)   padding to whole 1 KiB blocks
-constexpr int kRecA = 0, kRecQK = 18432, kRecTd = 30720, kRecGam = 43008, kRecW = 43264;
-static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
+// offsets in bytes; lane entries are in MFMA operand order).  A and Gamma o QK^T are
+// stored as (row tile mt, 32-column step s) pairs with s <= mt/2; the pairs (0,0)
+// and (2,1) reach past the diagonal, so only their first 16 columns are nonzero and
+// they are kept as 16-wide fragments (8 bytes per lane), as is the first row tile
+// of each 32x32 block inverse.
+//   [0, 12288)       A, full pairs (1,0) (2,0) (3,0) (3,1): 3 bf16 terms x 64 lanes x 16 B
+//   [12288, 15360)   A, half pairs (0,0) (2,1): 3 terms x 64 lanes x 8 B
+//   [15360, 23552)   Gamma o QK^T, full pairs: 2 terms x 64 x 16 B
+//   [23552, 25600)   Gamma o QK^T, half pairs: 2 terms x 64 x 8 B
+//   [25600, 31744)   T'_I = (I + diag(beta) A_II)^-1 diag(beta), 32x32 block I = 0, 1,
+//                    second row tile: 3 terms x 64 x 16 B
+//   [31744, 34816)   first row tile of T'_I (its 16 nonzero columns): 3 terms x 64 x 8 B
+//   [34816, 35072)   gamma_t = exp(G_t)                (fp32 x 64)
+//   [35072, 35328)   w_t = exp(G_last - G_t)           (fp32 x 64)
+//   [35328, 35840)   padding to whole 1 KiB blocks
+constexpr int kRecA = 0, kRecAh = 12288, kRecQK = 15360, kRecQKh = 23552, kRecT = 25600, kRecTh = 31744,
+              kRecGam = 34816, kRecW = 35072;
+static_assert(kPrepRecordBytes % 1024 == 0 && kRecW + 256 <= (int)kPrepRecordBytes, "record layout");
 
 // Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
 HAM_DEVICE constexpr int pair_index(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 + s : 4 + s; }
+// pairs (0,0) and (2,1) have 16 nonzero columns; slots within the full / half groups
+HAM_DEVICE constexpr bool pair_is_half(int pi) { return pi == 0 || pi == 3; }
+HAM_DEVICE constexpr int full_slot(int pi) { return pi == 1 ? 0 : pi == 2 ? 1 : pi == 4 ? 2 : 3; }
+HAM_DEVICE constexpr int half_slot(int pi) { return pi == 0 ? 0 : 1; }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -185,9 +196,15 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
       h8[i] = xh;
       m8[i] = to_bf16(x - from_bf16(xh));
     }
-    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecQK) + pi * 2 * kWave + lane;
-    dst[0] = h8;
-    dst[kWave] = m8;
+    if (pair_is_half(pi)) {
+      bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecQKh) + half_slot(pi) * 2 * kWave + lane;
+      dst[0] = __builtin_shufflevector(h8, h8, 0, 1, 2, 3);
+      dst[kWave] = __builtin_shufflevector(m8, m8, 0, 1, 2, 3);
+    } else {
+      bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecQK) + full_slot(pi) * 2 * kWave + lane;
+      dst[0] = h8;
+      dst[kWave] = m8;
+    }
   } else {
     bf16x8 h8, m8, l8;
 #pragma unroll
@@ -196,10 +213,17 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
       split3(val[i >> 2][i & 3], x0, x1, x2);
       h8[i] = x0; m8[i] = x1; l8[i] = x2;
     }
-    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecA) + pi * 3 * kWave + lane;
-    dst[0] = h8;
-    dst[kWave] = m8;
-    dst[2 * kWave] = l8;
+    if (pair_is_half(pi)) {
+      bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecAh) + half_slot(pi) * 3 * kWave + lane;
+      dst[0] = __builtin_shufflevector(h8, h8, 0, 1, 2, 3);
+      dst[kWave] = __builtin_shufflevector(m8, m8, 0, 1, 2, 3);
+      dst[2 * kWave] = __builtin_shufflevector(l8, l8, 0, 1, 2, 3);
+    } else {
+      bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecA) + full_slot(pi) * 3 * kWave + lane;
+      dst[0] = h8;
+      dst[kWave] = m8;
+      dst[2 * kWave] = l8;
+    }
   }
 }
 
@@ -304,20 +328,25 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
     // wave (I, r): row tile r of block I; lane (g,n) holds row n, columns 4g..4g+3
     // (k-slots 0..3) and 16+4g..16+4g+3 (k-slots 4..7) of the 32 block columns
     const int I = wave >> 1, r = wave & 1;
-    f32x4 lo, hi;
-    if (r == 0) {
-      lo = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I][n][4 * g]);
-      hi = (f32x4)(0.f);
-    } else {
-      lo = *reinterpret_cast<const f32x4*>(&sm.Off[I][n][4 * g]);
-      hi = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I + 1][n][4 * g]);
+    if (r == 0) {                         // [T'_{2I}, 0]: the 16 nonzero columns
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I][n][4 * g]);
+      const float xa[4] = {lo[0], lo[1], lo[2], lo[3]};
+      bf16x4 th, tm, tl;
+      split3x4(xa, th, tm, tl);
+      bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecTh) + (I * 3) * kWave + lane;
+      dst[0] = th;
+      dst[kWave] = tm;
+      dst[2 * kWave] = tl;
+    } else {                              // [-T'_{2I+1} A T'_{2I}, T'_{2I+1}]
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.Off[I][n][4 * g]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.Td[2 * I + 1][n][4 * g]);
+      bf16x8 th, tm, tl;
+      split_pair3(lo, hi, th, tm, tl);
+      bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecT) + (I * 3) * kWave + lane;
+      dst[0] = th;
+      dst[kWave] = tm;
+      dst[2 * kWave] = tl;
     }
-    bf16x8 th, tm, tl;
-    split_pair3(lo, hi, th, tm, tl);
-    bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecTd) + (wave * 3) * kWave + lane;
-    dst[0] = th;
-    dst[kWave] = tm;
-    dst[2 * kWave] = tl;
   }
 }
 
@@ -384,8 +413,8 @@ struct ChunkLayout {
   static constexpr int RV = NW * 16 * 2;             // bytes per V-slice row
   static constexpr int NCV = NW * 2;
   static constexpr int KB = kC * RK, VB = kC * RV;
-  // a stage holds K, Q and the chunk record; the V slice has one buffer of its own
-  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_R = 2 * KB;
+  // a stage holds K, Q, the workgroup's V columns and the chunk record
+  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_V = 2 * KB, OFF_R = 2 * KB + VB;
   static constexpr int STAGE = OFF_R + (int)kPrepRecordBytes;
   static constexpr int KI = KB / 1024 / NW;          // 1 KiB loads per wave: K (and Q), V
   static constexpr int VI = VB / 1024 / NW;
@@ -408,7 +437,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // of the current stage do not depend on the direct loads into the other one.
   __shared__ __attribute__((aligned(16))) char stage0[LY::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[LY::STAGE];
-  __shared__ __attribute__((aligned(16))) char vbuf[LY::VB];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -448,8 +476,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const char* qbase = static_cast<const char*>(a.q);
   const char* vbase = static_cast<const char*>(a.v);
 
-  // Direct loads of chunk cc: K, Q and the record into the stage dst, the V slice
-  // into its single buffer.  Wave w issues the 1 KiB blocks w, w + NW, ... of each tile; lane
+  // Direct loads of chunk cc into the stage dst.  Wave w issues the 1 KiB blocks
+  // w, w + NW, ... of each tile; lane
   // l writes the 16 bytes at 16 l of the block.  The source offset of a lane (bytes
   // from the chunk's first token row of this head) depends on the chunk only through
   // the clamp of rows past T to the last valid token (finite values whose write
@@ -491,7 +519,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     for (int j = 0; j < LY::VI; ++j) {
       const uint32_t vo = full ? voff[j] : v_off(j, a.T - 1 - t0);
       const int blk = (wave + NW * j) * 1024;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), vbuf + blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < (LY::RI + NW - 1) / NW; ++j) {
@@ -514,18 +542,17 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   auto chunk_step = [&](int c, const char* stg, char* nxt) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
-    __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles, record and V have arrived
+    __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
     __syncthreads();                          // ... for every wave; the other stage is free
-    // This lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads); the
-    // second barrier frees the V buffer for the next chunk.
+    // this lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads)
     u32x2 vraw[4];
     {
+      const char* Vs = stg + LY::OFF_V;
       const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        vraw[mt] = lds_tr16(vbuf, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
+        vraw[mt] = lds_tr16(Vs, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
     }
-    __syncthreads();
     auto v4_at = [&](int mt) {
       f32x4 f;
       f[0] = __uint_as_float(vraw[mt][0] << 16);
@@ -539,7 +566,9 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const char* Qs = stg + LY::OFF_Q;
     const char* rec = stg + LY::OFF_R;
     const u32x4* Af = reinterpret_cast<const u32x4*>(rec + kRecA);
+    const u32x2* Afh = reinterpret_cast<const u32x2*>(rec + kRecAh);
     const u32x4* QKf = reinterpret_cast<const u32x4*>(rec + kRecQK);
+    const u32x2* QKfh = reinterpret_cast<const u32x2*>(rec + kRecQKh);
     const float* gam = reinterpret_cast<const float*>(rec + kRecGam);
     const float* wdec = reinterpret_cast<const float*>(rec + kRecW);
 
@@ -598,8 +627,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     // ---- block forward substitution over the two 32-token blocks ----
     //   D_0 = T'_0 X_0,   D_1 = T'_1 (X_1 - A_10 D_0),   P += A D (strictly lower A)
     // dB[s][z]: B-operand fragments (k-step s, term z) of D rows 32s..32s+31.
-    const u32x4* T32 = reinterpret_cast<const u32x4*>(rec + kRecTd);
-    auto A_at = [&](int mt, int s, int z) { return as8(Af[(pair_index(mt, s) * 3 + z) * kWave + lane]); };
+    const u32x4* Tf = reinterpret_cast<const u32x4*>(rec + kRecT);
+    const u32x2* Tfh = reinterpret_cast<const u32x2*>(rec + kRecTh);
+    auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) { return mfma_bf16_k16(x, y, c); };
+    auto lo4 = [](const u32x4& x) { return as4(u32x2{x[0], x[1]}); };
+    auto A_at = [&](int mt, int s, int z) { return as8(Af[(full_slot(pair_index(mt, s)) * 3 + z) * kWave + lane]); };
+    auto Ah_at = [&](int mt, int s, int z) { return as4(Afh[(half_slot(pair_index(mt, s)) * 3 + z) * kWave + lane]); };
     u32x4 dB[2][3];
     f32x4 D[4];
     auto solve_block = [&](int I, const f32x4& x0, const f32x4& x1) {
@@ -607,10 +640,14 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       split4(x0, h0, m0, l0);
       split4(x1, h1, m1, l1);
       const bf16x8 rh = as8(cat(h0, h1)), rm = as8(cat(m0, m1)), rl = as8(cat(l0, l1));
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const u32x4* t = T32 + ((I * 2 + r) * 3) * kWave + lane;
-        D[2 * I + r] = mma6(mfma_bf16, as8(t[0]), as8(t[kWave]), as8(t[2 * kWave]), rh, rm, rl, (f32x4)(0.f));
+      {
+        const u32x2* t = Tfh + (I * 3) * kWave + lane;          // first row tile: 16 columns
+        D[2 * I] = mma6(mf16, as4(t[0]), as4(t[kWave]), as4(t[2 * kWave]), as4(h0), as4(m0), as4(l0),
+                        (f32x4)(0.f));
+      }
+      {
+        const u32x4* t = Tf + (I * 3) * kWave + lane;
+        D[2 * I + 1] = mma6(mfma_bf16, as8(t[0]), as8(t[kWave]), as8(t[2 * kWave]), rh, rm, rl, (f32x4)(0.f));
       }
       split4(D[2 * I], h0, m0, l0);
       split4(D[2 * I + 1], h1, m1, l1);
@@ -625,12 +662,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
                           as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), (f32x4)(0.f));
     solve_block(1, X[2] - R2, X[3] - R3);
     // the prediction P = gamma K S + A D
-    P[0] = mma6(mfma_bf16, A_at(0, 0, 0), A_at(0, 0, 1), A_at(0, 0, 2),
-                as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), P[0]);
+    P[0] = mma6(mf16, Ah_at(0, 0, 0), Ah_at(0, 0, 1), Ah_at(0, 0, 2),
+                lo4(dB[0][0]), lo4(dB[0][1]), lo4(dB[0][2]), P[0]);
     P[1] = mma6(mfma_bf16, A_at(1, 0, 0), A_at(1, 0, 1), A_at(1, 0, 2),
                 as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), P[1]);
-    P[2] = mma6(mfma_bf16, A_at(2, 1, 0), A_at(2, 1, 1), A_at(2, 1, 2),
-                as8(dB[1][0]), as8(dB[1][1]), as8(dB[1][2]), P[2] + R2);
+    P[2] = mma6(mf16, Ah_at(2, 1, 0), Ah_at(2, 1, 1), Ah_at(2, 1, 2),
+                lo4(dB[1][0]), lo4(dB[1][1]), lo4(dB[1][2]), P[2] + R2);
     P[3] = mma6(mfma_bf16, A_at(3, 1, 0), A_at(3, 1, 1), A_at(3, 1, 2),
                 as8(dB[1][0]), as8(dB[1][1]), as8(dB[1][2]), P[3] + R3);
 
@@ -641,10 +678,19 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
         for (int s = 0; s <= (mt >> 1); ++s) {
           const int pi = pair_index(mt, s);
-          const bf16x8 qh = as8(QKf[(pi * 2 + 0) * kWave + lane]), qm = as8(QKf[(pi * 2 + 1) * kWave + lane]);
-          O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
-          O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
-          O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
+          if (pair_is_half(pi)) {
+            const bf16x4 qh = as4(QKfh[(half_slot(pi) * 2 + 0) * kWave + lane]);
+            const bf16x4 qm = as4(QKfh[(half_slot(pi) * 2 + 1) * kWave + lane]);
+            O[mt] = mf16(qm, lo4(dB[s][0]), O[mt]);
+            O[mt] = mf16(qh, lo4(dB[s][1]), O[mt]);
+            O[mt] = mf16(qh, lo4(dB[s][0]), O[mt]);
+          } else {
+            const bf16x8 qh = as8(QKf[(full_slot(pi) * 2 + 0) * kWave + lane]);
+            const bf16x8 qm = as8(QKf[(full_slot(pi) * 2 + 1) * kWave + lane]);
+            O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
+            O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
+            O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
+          }
         }
     }
 
