@@ -17,11 +17,44 @@ namespace ham {
 
 constexpr float kLog2eD = 1.4426950408889634f;
 
+// Raw cache rows: a lane holds N consecutive elements of a row as loaded (bf16
+// bit patterns or floats) and converts them when they are used.
+template <class IO, int N>
+struct RawRun;
+template <int N>
+struct RawRun<IoBF16, N> {                    // 16-byte runs (8-byte when N = 4)
+  static_assert(N % 8 == 0 || N == 4, "run length");
+  static constexpr int W = N % 8 == 0 ? 8 : 4;
+  typedef uint16_t vec __attribute__((ext_vector_type(W)));
+  vec x[N / W];
+  HAM_DEVICE void load(const uint16_t* p) {
+#pragma unroll
+    for (int i = 0; i < N / W; ++i) x[i] = *reinterpret_cast<const vec*>(p + W * i);
+  }
+  HAM_DEVICE float operator[](int i) const { return bf16_to_f32(x[i / W][i % W]); }
+};
+template <int N>
+struct RawRun<IoF32, N> {
+  static_assert(N % 4 == 0, "16-byte runs");
+  f32x4 x[N / 4];
+  HAM_DEVICE void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) x[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+  }
+  HAM_DEVICE float operator[](int i) const { return x[i >> 2][i & 3]; }
+};
+
+// grid (nseg, H, B), 256 threads: one workgroup streams one segment of a head's
+// cache.  16 lane groups of 16 lanes; a lane group takes U keys per step (a lane
+// holds d/16 elements of each row, 16-byte loads), forms their scores with a row
+// reduction, and applies the U keys with one running-maximum update (blocked
+// online softmax).  Keys past the end of the segment load the last valid row and
+// get probability 0.
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   using E = typename IO::elem;
   constexpr int KE = DK / 16, VE = DV / 16;   // elements per lane per row
-  constexpr int U = 4;                        // keys in flight per lane group
+  constexpr int U = 8;                        // keys per lane group per step
   __shared__ float s_m[16], s_l[16];
   __shared__ float s_acc[16][DV];
 
@@ -50,34 +83,38 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   for (int i = 0; i < VE; ++i) acc[i] = 0.f;
 
   for (int c = s0 + grp; c < s1; c += 16 * U) {
-    float kx[U][KE], vx[U][VE];
+    RawRun<IO, KE> kx[U];
+    RawRun<IO, VE> vx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int cc = c + 16 * u;
-      if (cc < s1) {
-#pragma unroll
-        for (int i = 0; i < KE; i += 4) IO::load4(Kh, (size_t)cc * DK + i, kx[u] + i);
-#pragma unroll
-        for (int i = 0; i < VE; i += 4) IO::load4(Vh, (size_t)cc * DV + i, vx[u] + i);
-      }
+      const int cc = min(c + 16 * u, s1 - 1);
+      kx[u].load(Kh + (size_t)cc * DK);
+      vx[u].load(Vh + (size_t)cc * DV);
     }
+    float sc[U];
+    float bm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int cc = c + 16 * u;
-      if (cc < s1) {                           // uniform within the 16-lane group
-        float s = 0.f;
+      float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < KE; ++i) s = fmaf(qv[i], kx[u][i], s);
-        s = wave_sum<16>(s);
-        const float mn = fmaxf(m, s);
-        const float corr = exp2f(m - mn);
-        const float p = exp2f(s - mn);
-        l = l * corr + p;
-#pragma unroll
-        for (int i = 0; i < VE; ++i) acc[i] = fmaf(p, vx[u][i], acc[i] * corr);
-        m = mn;
-      }
+      for (int i = 0; i < KE; ++i) s = fmaf(qv[i], kx[u][i], s);
+      s = row16_sum(s);
+      sc[u] = (c + 16 * u < s1) ? s : -INFINITY;
+      bm = fmaxf(bm, sc[u]);
     }
+    const float mn = fmaxf(m, bm);            // finite: key c is always valid
+    const float corr = __builtin_amdgcn_exp2f(m - mn);
+    l *= corr;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = __builtin_amdgcn_exp2f(sc[u] - mn);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[i] = fmaf(p, vx[u][i], acc[i]);
+    }
+    m = mn;
   }
   // merge the 16 lane groups
   if (sub == 0) { s_m[grp] = m; s_l[grp] = l; }
@@ -134,11 +171,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeCombineArgs a)
   const int n = a.count[bh];
   const int used = (n + a.seg - 1) / a.seg;
   const float* part = a.part + (size_t)bh * a.nseg * (DV + 2);
+  // segment maxima read by the lanes in parallel
   float M = -INFINITY;
-  for (int s = 0; s < used; ++s) M = fmaxf(M, part[(size_t)s * (DV + 2) + DV]);
+  for (int s = lane; s < used; s += 64) M = fmaxf(M, part[(size_t)s * (DV + 2) + DV]);
+  M = wave_max<64>(M);
   float L = 0.f, okv[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) okv[i] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < used; ++s) {
     const float* ps = part + (size_t)s * (DV + 2);
     const float w = exp2f(ps[DV] - M);

@@ -123,6 +123,6 @@ hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, h
 hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hipStream_t s);
 
 constexpr int kChunk = 64;         // tokens per routing / compaction chunk
-constexpr int kDecodeSeg = 512;    // keys per split-K segment in decode
+constexpr int kDecodeSeg = 1024;   // keys per split-K segment in decode
 
 }  // namespace ham
