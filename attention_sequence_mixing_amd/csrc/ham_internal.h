@@ -21,7 +21,7 @@ struct RnnArgs {
   const float* S0;      // [B,H,dk,dv] or null (zeros)
   float* S_out;         // [B,H,dk,dv]
   float* o_rnn32;       // [B,T,H,dv] fp32 or null (no readout)
-  float4* score;        // [B*H][T][slices]
+  float4* score;        // [B,T,H][slices]
   void* prep;           // chunked path: per-chunk records [B*H][nchunk][kPrepRecordBytes]
   int B, T, H;
 };
@@ -30,7 +30,7 @@ struct RnnArgs {
 constexpr size_t kPrepRecordBytes = 35840;
 
 struct RouteArgs {
-  const float4* score;  // [B*H][T][slices]
+  const float4* score;  // [B,T,H][slices]
   int slices;
   const float* tau;     // [H]
   float* e;             // [B,T,H]

@@ -537,7 +537,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // token whose row totals this lane ends with after the transposed reduction)
   const uint32_t o_lane = (uint32_t)((4 * g * a.H + h) * DV + col);
   const int s_tok = 16 * (n >> 2) + 4 * g + (n & 3);
-  const uint32_t s_lane = (uint32_t)(s_tok * NSL + slice);
+  const uint32_t s_lane = (uint32_t)(s_tok * a.H * NSL + slice);
 
   auto chunk_step = [&](int c, const char* stg, char* nxt) {
     const int t0 = c * kC;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       const float pv = row16_transpose_sum(xpv, n);
       const float pp = row16_transpose_sum(xpp, n);
       const float vv = row16_transpose_sum(xvv, n);
-      float4* sc = a.score + ((size_t)bh * a.T + t0) * NSL;
+      float4* sc = a.score + (((size_t)b * a.T + t0) * a.H + h) * NSL;
       if (full || s_tok < nvalid) sc[s_lane] = make_float4(pv, pp, vv, 0.f);
     }
     if (RO) {

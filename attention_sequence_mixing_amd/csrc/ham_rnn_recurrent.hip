@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
       pp += __shfl_xor(pp, msk, kWave);
       vv += __shfl_xor(vv, msk, kWave);
     }
-    if (lane == 0) a.score[((size_t)bh * a.T + t) * NS + slice] = make_float4(pv, pp, vv, 0.f);
+    if (lane == 0) a.score[tok * NS + slice] = make_float4(pv, pp, vv, 0.f);
 
     // S <- alpha*S + k * beta*(v_j - alpha*p_j)
     const float w = beta * (vj - alpha * p);

@@ -19,8 +19,12 @@ namespace ham {
 // grid (nchunk, B), 256 threads: all heads of one 64-token chunk.  Thread index
 // runs head-fastest so that e and routed ([B,T,H]) are written contiguously; the
 // per-head routed counts of the chunk are integer sums in LDS (order-independent).
+// NS (score slices per token) is a compile-time constant so that every slice load
+// of a thread is in flight at once.
+template <int NS>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   extern __shared__ int s_cnt[];            // [H]
+  constexpr int PER = 4;                    // (token, head) pairs per thread and pass
   const int tid = threadIdx.x;
   const int c = blockIdx.x, b = blockIdx.y;
   const int nchunk = gridDim.x;
@@ -29,27 +33,39 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __syncthreads();
   const int t0 = c * kChunk;
   const int nv = min(kChunk, a.T - t0);
-  for (int idx = tid; idx < nv * H; idx += 256) {
-    const int tl = idx / H, h = idx % H;
-    const int t = t0 + tl;
-    const int bh = b * H + h;
-    const float4* sp = a.score + ((size_t)bh * a.T + t) * a.slices;
-    float pv = 0.f, pp = 0.f, vv = 0.f;
-    for (int s = 0; s < a.slices; ++s) {
-      const float4 x = sp[s];
-      pv += x.x; pp += x.y; vv += x.z;
+  const int npair = nv * H;
+  for (int base = 0; base < npair; base += 256 * PER) {
+    float4 x[PER][NS];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = min(base + tid + 256 * j, npair - 1);
+      const int tl = idx / H, h = idx - tl * H;
+      const float4* sp = a.score + (((size_t)b * a.T + t0 + tl) * H + h) * NS;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) x[j][s] = sp[s];
     }
-    float cs = 0.f;
-    if (pp > 0.f && vv > 0.f) {
-      cs = pv / (sqrtf(pp) * sqrtf(vv));
-      cs = fminf(1.f, fmaxf(-1.f, cs));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = base + tid + 256 * j;
+      if (idx >= npair) break;
+      const int tl = idx / H, h = idx - tl * H;
+      float pv = 0.f, pp = 0.f, vv = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        pv += x[j][s].x; pp += x[j][s].y; vv += x[j][s].z;
+      }
+      float cs = 0.f;
+      if (pp > 0.f && vv > 0.f) {
+        cs = pv / (sqrtf(pp) * sqrtf(vv));
+        cs = fminf(1.f, fmaxf(-1.f, cs));
+      }
+      const float e = 1.f - cs;
+      const bool r = e > a.tau[h];          // strict; a NaN score never routes
+      const size_t tok = ((size_t)b * a.T + t0 + tl) * H + h;
+      a.e[tok] = e;
+      a.routed[tok] = (uint8_t)r;
+      if (r) atomicAdd(&s_cnt[h], 1);
     }
-    const float e = 1.f - cs;
-    const bool r = e > a.tau[h];            // strict; a NaN score never routes
-    const size_t tok = ((size_t)b * a.T + t) * H + h;
-    a.e[tok] = e;
-    a.routed[tok] = (uint8_t)r;
-    if (r) atomicAdd(&s_cnt[h], 1);
   }
   __syncthreads();
   for (int h = tid; h < H; h += 256) {
@@ -61,7 +77,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(route_kernel, dim3(nchunk, a.B), dim3(256), a.H * sizeof(int), s, a);
+  const dim3 grid(nchunk, a.B);
+  const size_t lds = a.H * sizeof(int);
+  if (a.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, a);
+  else if (a.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
