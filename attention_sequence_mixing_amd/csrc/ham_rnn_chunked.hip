@@ -498,7 +498,10 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
   for (int j = 0; j < LY::VI; ++j) voff[j] = v_off(j, kC - 1);
 
-  auto issue_chunk = [&](int cc, char* dst) {
+  // part 1: K, Q and V tiles; part 2: the chunk record.  The two parts are issued
+  // at different points of the chunk (measured: issuing all loads at once stalls
+  // the loop more than spreading them).
+  auto issue_chunk = [&](int cc, char* dst, int part) {
     const int t0 = cc * kC;
     const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
     const char* kc = kbase + tok0 * (DK * 2);
@@ -508,6 +511,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const uint32_t lo = (uint32_t)lane * 16u;
     const bool full = t0 + kC <= a.T;
 #if defined(__HIP_DEVICE_COMPILE__)
+    if (part & 1) {
 #pragma unroll
     for (int j = 0; j < LY::KI; ++j) {
       const uint32_t ko = full ? koff[j] : k_off(j, a.T - 1 - t0);
@@ -521,11 +525,14 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       const int blk = (wave + NW * j) * 1024;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
     }
+    }
+    if (part & 2) {
 #pragma unroll
     for (int j = 0; j < (LY::RI + NW - 1) / NW; ++j) {
       const int blk = (wave + NW * j) * 1024;
       if (wave + NW * j < LY::RI)
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rc + blk + lo), dst + LY::OFF_R + blk, 16, 0, 0);
+    }
     }
 #else
     (void)kc; (void)qc; (void)vc; (void)rc; (void)lo; (void)full; (void)dst;
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       f[3] = __uint_as_float(vraw[mt][1] & 0xffff0000u);
       return f;
     };
-    if (c + 1 < nchunk) issue_chunk(c + 1, nxt);
+    if (c + 1 < nchunk) issue_chunk(c + 1, nxt, 1);   // the next chunk's tiles
     const char* Ks = stg + LY::OFF_K;
     const char* Qs = stg + LY::OFF_Q;
     const char* rec = stg + LY::OFF_R;
@@ -613,6 +620,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
     }
+    if (c + 1 < nchunk) issue_chunk(c + 1, nxt, 2);   // the next chunk's record
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
@@ -765,7 +773,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
   };
 
-  issue_chunk(0, stage0);
+  issue_chunk(0, stage0, 3);
   for (int c = 0; c < nchunk; c += 2) {
     chunk_step(c, stage0, stage1);
     if (c + 1 < nchunk) chunk_step(c + 1, stage1, stage0);
