@@ -224,3 +224,61 @@ def test_rho_sweep_small():
         want = 2 * int(round(rho * 2 * 256))          # round(rho*B*T) per head, 2 heads
         got = int(out["count"].sum())
         assert abs(got - want) <= res["nflip"], (rho, got, want)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv", [
+    (1, 63, 1, 128, 128), (1, 64, 2, 64, 64), (2, 65, 1, 64, 128), (1, 127, 2, 128, 64),
+    (1, 128, 1, 128, 128), (2, 129, 3, 64, 64), (3, 150, 5, 128, 128), (1, 257, 7, 64, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_boundaries(B, T, H, dk, dv, dtype):
+    """Lengths on either side of the 64-token chunk and 64/128-query blocks (the
+    token-serial path below 65 tokens, the chunked path above), several head counts."""
+    seed = 40 + T + H
+    inp = make_inputs(B, T, H, dk, dv, dtype="f32" if dtype == torch.float32 else "bf16", seed=seed)
+    scale = dk ** -0.5
+    tau = _tau(inp, 0.5, scale)
+    out = _run(inp, tau, dtype, scale=scale)
+    check_forward(out, inp, tau, dtype, scale=scale)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_from_empty_state(dtype):
+    """Decode steps from a zero state and an empty cache equal one forward call;
+    with tau = +inf nothing is cached and o_kv stays 0."""
+    B, H, d, T = 2, 3, 64, 20
+    inp = make_inputs(B, T, H, d, dtype="f32" if dtype == torch.float32 else "bf16", seed=33)
+    scale = d ** -0.5
+    for tau in (_tau(inp, 0.5, scale), np.full(H, INF, np.float32)):
+        ref = oracle.forward(**inp, tau=tau, scale=scale, cap=T)
+        t = to_dev(inp, dtype, DEV)
+        tau_d = torch.from_numpy(tau).to(DEV)
+        S = torch.zeros((B, H, d, d), device=DEV)
+        Kc = torch.zeros((B, H, T, d), dtype=dtype, device=DEV)
+        Vc = torch.zeros((B, H, T, d), dtype=dtype, device=DEV)
+        pos = torch.full((B, H, T), -1, dtype=torch.int32, device=DEV)
+        count = torch.zeros((B, H), dtype=torch.int32, device=DEV)
+        plan = ham.DecodePlan(B, H, d, d, T, dtype, DEV, scale=scale, want_o_kv=True)
+        es, rs, os_, okv = [], [], [], []
+        for s in range(T):
+            x = {n: t[n][:, s].contiguous() for n in t}
+            plan(x["q"], x["k"], x["v"], x["beta"], x["g"], tau_d, S, Kc, Vc, pos, count,
+                 torch.full((B,), s, dtype=torch.int32, device=DEV))
+            es.append(plan.e.cpu().numpy()); rs.append(plan.routed.cpu().numpy())
+            os_.append(np_of(plan.o)); okv.append(np_of(plan.o_kv))
+        torch.cuda.synchronize()
+        e_all, r_all = np.stack(es, 1), np.stack(rs, 1)
+        nflip = check_routing(e_all, r_all, ref, tau)
+        if nflip:
+            ref = oracle.forward(**inp, tau=tau, scale=scale, cap=T, mask_override=r_all)
+        assert np.all(e_all[:, 0] == 1.0)               # zero state: cosine 0 by definition
+        assert rel_err_slices(np.stack(os_, 1), ref["o"], 2) < TOL[dtype]
+        assert np.array_equal(count.cpu().numpy(), ref["count"])
+        if np.isinf(tau).all():
+            assert int(count.sum()) == 0 and float(np.abs(np.stack(okv, 1)).max()) == 0.0
+        else:
+            assert rel_err_slices(np.stack(okv, 1), ref["o_kv"], 2) < TOL[dtype]
+            got_pos = pos.cpu().numpy()
+            for b in range(B):
+                for h in range(H):
+                    n = int(ref["count"][b, h])
+                    assert np.array_equal(got_pos[b, h, :n], ref["pos"][b, h, :n])
