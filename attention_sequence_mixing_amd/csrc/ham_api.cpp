@@ -43,6 +43,8 @@ int check_dims(const ham_dims* d, bool need_T) {
   if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT))
     return fail(HAM_EUNSUPPORTED, "unknown flag bits 0x%x", d->flags);
   if (d->cap <= 0) return fail(HAM_EINVAL, "cap must be positive (cap=%d)", d->cap);
+  // the attention kernels address one head's cache rows with 32-bit byte offsets
+  if (d->cap > (1 << 22)) return fail(HAM_EUNSUPPORTED, "cap must be <= 4194304 (cap=%d)", d->cap);
   if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return fail(HAM_EINVAL, "scale must be finite and > 0");
   if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(HAM_EINVAL, "norm_eps must be finite and >= 0");
   if (d->t0 < 0) return fail(HAM_EINVAL, "t0 must be >= 0");

@@ -10,12 +10,12 @@
 // itself when t is routed).  Mix: o = g_rnn*rms(o_rnn) + g_kv*rms(o_kv) (§2
 // headwise norm and gated sum; App. A.1 headwise gating).
 //
-// One workgroup = 64 queries of one (b,h), 4 waves x 16 queries.  Each wave
-// computes S^T = K Q^T on 16x16 MFMA tiles (keys on rows), so the per-query
-// softmax state lives in the lanes that later hold that query's output column of
-// O^T = V^T P^T: no data movement between the two products.  bf16 uses
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation (attn_bf16_v4_kernel); fp32 I/O
-// uses v_mfma_f32_16x16x4f32 (attn_kernel).
+// Each wave computes S^T = K Q^T on 16x16 MFMA tiles (keys on rows), so the
+// per-query softmax state lives in the lanes that later hold that query's output
+// column of O^T = V^T P^T: no data movement between the two products.  bf16 I/O
+// (attn_bf16_v5_kernel): 4 waves x 32 queries of one (b,h) per workgroup on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  fp32 I/O (attn_kernel): 4
+// waves x 16 queries on v_mfma_f32_16x16x4f32.
 #include "ham_common.h"
 #include "ham_internal.h"
 
@@ -283,30 +283,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Softmax of the bf16 path: the running maximum is kept in log2 units of the scaled
-// logits (scale > 0, so the maximum of the raw scores gives it).  The accumulators
-// are rescaled only when some query's maximum grows by more than 8 (a factor 2^8);
-// otherwise the stale maximum is kept: probabilities up to 2^8 are exact enough in
-// fp32 and bf16, and the final division by the running sum cancels the common factor.
+// Softmax of the bf16 path: the running maximum m is kept in log2 units of the
+// scaled logits.  A tile's probabilities are first formed against the stale m;
+// their row sum bounds the largest of them, so when no query's sum exceeds
+// 2^12 every probability is at most 2^12 and the tile is accepted as is (fp32 and
+// bf16 hold such values exactly enough, and the final division by the running sum
+// cancels the common factor).  Otherwise the tile's scores are formed again and
+// the exact path runs: row maxima across the four lanes of a query, rescale of the
+// accumulators, probabilities against the new maximum.  The first tile of a block
+// always takes the exact path.
+constexpr float kLazySum = 4096.0f;
 constexpr float kLazyRescale = 8.0f;
 
 // ---- bf16 path: direct-to-LDS tile ring ---------------------------------------------
 //
 // 4 waves x 32 queries per workgroup, two workgroups per CU.  K and V tiles (64
-// keys) are copied from HBM into LDS with direct global-to-LDS loads (no staging
-// registers) into a 2-stage ring, one tile ahead of the one being consumed.  Both tiles are row-major with
-// the 16-byte chunks of each row XOR-swizzled by the row index (chunk c of row r
-// sits at chunk slot c ^ (r mod chunks-per-row)), which keeps the fragment reads
-// free of bank conflicts.  K fragments (A operand of S^T = K Q^T) are 16-byte
-// reads; V^T fragments (A operand of O^T = V^T P^T) use the transposing LDS read:
-// for each 16-lane group, lane r addresses V[k0 + r/4][d0 + 4(r mod 4) .. +3] and
-// lane i receives V[k0 + j][d0 + i] for j = 0..3.
-template <int D>
-HAM_DEVICE int swz_off(int row, int chunk) {            // byte offset in a tile
-  constexpr int NCH = D / 8;
-  return row * (D * 2) + ((chunk ^ (row & (NCH - 1))) << 4);
-}
-
+// keys) are copied from HBM into LDS by buffer loads that write LDS directly (no
+// staging registers) into a 2-stage ring, one tile ahead of the one being
+// consumed.  The buffer descriptors are rebuilt per tile in scalar registers with
+// the tile's first row as base and the rows still visible to the block as range,
+// so rows past the last visible key read as zero without per-lane clamping; the
+// per-lane offsets are fixed for the whole kernel.  Tiles are row-major with the
+// 16-byte chunks of each row XOR-swizzled: in K, chunk c of row r sits at slot
+// c ^ (r mod chunks-per-row); in V at slot c ^ 2(r mod chunks-per-row/2), which
+// keeps both fragment reads free of bank conflicts.  K fragments (A operand of
+// S^T = K Q^T) are 16-byte reads; V^T fragments (A operand of O^T = V^T P^T) use
+// the transposing LDS read: for each 16-lane group, lane r addresses
+// V[k0 + r/4][d0 + 4(r mod 4) .. +3] and lane i receives V[k0 + j][d0 + i] for
+// j = 0..3.
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 
@@ -321,8 +325,26 @@ HAM_DEVICE short4v lds_read_tr16(const char* base, int byte_off) {
 #endif
 }
 
+// Chunk slot swizzles of the K and V tiles (D = row length in elements).
+template <int D>
+HAM_DEVICE int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D>
+HAM_DEVICE int swz_v(int r) { return 2 * (r & (D / 16 - 1)); }
+
+// One 16-byte-per-lane buffer load from `base` + voff with `range_bytes` valid bytes,
+// written to LDS at `lds` + 16 * lane; offsets at or past the range read zero.
+HAM_DEVICE void buffer_to_lds(const void* base, int range_bytes, int voff, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                               range_bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#else
+  (void)base; (void)range_bytes; (void)voff; (void)lds;
+#endif
+}
+
 template <int DK, int DV, int QT>
-__global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   constexpr int NWV = 4;                                   // waves per workgroup
   constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
   constexpr int BMW = 16 * QT, BM = NWV * BMW;
@@ -330,10 +352,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
   constexpr int KI = KB / 1024, VI = VB / 1024;            // 1 KiB load instructions per tile
   static_assert((KI + VI) % NWV == 0, "tile loads must split evenly over the waves");
   constexpr int LPW = (KI + VI) / NWV;                     // load instructions per wave per tile
-  constexpr int NST = 2;                                   // ring stages
-  __shared__ __attribute__((aligned(16))) char ring[NST][KB + VB];
+  constexpr int RBK = DK * 2, RBV = DV * 2;                // row bytes
+  // two ring stages as separate LDS objects, so that reads of one stage are known
+  // not to alias the direct loads in flight into the other
+  __shared__ __attribute__((aligned(16))) char stage0[KB + VB];
+  __shared__ __attribute__((aligned(16))) char stage1[KB + VB];
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, qn = lane & 15;
   const int nqb = (a.T + BM - 1) / BM;
   // global longest-first: all heads' last query block first
@@ -344,8 +370,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
   const int b = bh / a.H, h = bh % a.H;
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* Kh = static_cast<const uint16_t*>(a.Kc) + (size_t)bh * a.cap * DK;
-  const uint16_t* Vh = static_cast<const uint16_t*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const char* Kh = static_cast<const char*>(a.Kc) + (size_t)bh * a.cap * RBK;
+  const char* Vh = static_cast<const char*>(a.Vc) + (size_t)bh * a.cap * RBV;
   const int32_t* ntok = a.ntok + (size_t)bh * a.T;
 
   const int qb0 = qb * BM;
@@ -365,31 +391,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
       qf[qt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g));
   }
 
-  // Direct loads of one tile into ring stage `st`.  Instruction i of this wave covers
-  // 1 KiB of the stage; lane l writes its 16 bytes at i*1024 + 16*l, which holds
-  // chunk (slot ^ swizzle) of tile row r.  Rows at or beyond nhi read row nhi-1
-  // (finite values; those keys are masked through the scores).
-  const int rlast = nhi - 1;
-  auto issue_tile = [&](int it, int st) {
+  // Tile loads: 1 KiB instruction i covers bytes [i*1024, i*1024 + 1024) of a stage
+  // (K rows first, then V rows); wave w issues i = 4k + w.  Lane l writes 16 bytes at
+  // i*1024 + 16*l, which hold chunk (slot ^ swizzle) of its tile row.  The swizzle
+  // repeats every PK (PV) instructions, a divisor of 4, so one per-lane offset per
+  // tensor serves all of a wave's loads; the rest of each instruction's offset goes
+  // into the descriptor base.
+  static_assert(KI % NWV == 0, "K and V loads must not share a wave step");
+  constexpr int PK = (DK / 8) * RBK / 1024 > 1 ? (DK / 8) * RBK / 1024 : 1;
+  constexpr int PV = (DV / 16) * RBV / 1024 > 1 ? (DV / 16) * RBV / 1024 : 1;
+  static_assert(NWV % PK == 0 && NWV % PV == 0, "swizzle period must divide the wave count");
+  const int jK = wave % PK, jV = wave % PV;
+  int ldK, ldV;
+  {
+    const int pk = jK * 1024 + lane * 16, rk = pk / RBK;
+    ldK = rk * RBK + ((((pk % RBK) >> 4) ^ swz_k<DK>(rk)) << 4);
+    const int pv = jV * 1024 + lane * 16, rv = pv / RBV;
+    ldV = rv * RBV + ((((pv % RBV) >> 4) ^ swz_v<DV>(rv)) << 4);
+  }
+  auto issue_tile = [&](int it, char* st) {
     const int c0 = it * BN;
+    const int rows = nhi - c0;                             // > 0 for every issued tile
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
-      const int i = wave * LPW + k;                      // instruction index within the tile
-      const int pos = i * 1024 + lane * 16;              // byte position in the stage
-      const bool isK = i < KI;
-      const int D = isK ? DK : DV;
-      const int rb = D * 2;
-      const int tp = isK ? pos : pos - KB;
-      const int r = tp / rb, slot = (tp % rb) >> 4;
-      const int nch = D / 8;
-      const int chunk = slot ^ (r & (nch - 1));
-      const int row = min(c0 + r, rlast);
-      const uint16_t* src = isK ? Kh + (size_t)row * DK + chunk * 8 : Vh + (size_t)row * DV + chunk * 8;
-#if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), &ring[st][i * 1024], 16, 0, 0);
-#else
-      (void)src;
-#endif
+      if (k < KI / NWV) {
+        const int i = k * NWV + wave, sh = (i - jK) * 1024;
+        buffer_to_lds(Kh + (size_t)c0 * RBK + sh, max(rows * RBK - sh, 0), ldK, st + i * 1024);
+      } else {
+        const int i = (k - KI / NWV) * NWV + wave, sh = (i - jV) * 1024;
+        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV, st + KB + i * 1024);
+      }
     }
   };
 
@@ -404,29 +435,25 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = (f32x4)(0.f);
   }
 
-  // Per-lane fragment offsets inside a stage.  The swizzle term only depends on the
-  // lane (row mod chunks-per-row is fixed by the lane), so each fragment address is
-  // stage base + one of these + a compile-time constant.
-  constexpr int RBK = DK * 2, RBV = DV * 2, NCHK = DK / 8, NCHV = DV / 8;
+  // Per-lane fragment offsets inside a stage (the swizzle terms depend only on the lane).
   int koff[KSD], voff[DT];
   const int r4 = qn >> 2, c4 = qn & 3;
 #pragma unroll
-  for (int ks = 0; ks < KSD; ++ks) koff[ks] = qn * RBK + (((ks * 4 + g) ^ (qn & (NCHK - 1))) << 4);
+  for (int ks = 0; ks < KSD; ++ks) koff[ks] = qn * RBK + (((ks * 4 + g) ^ swz_k<DK>(qn)) << 4);
   {
     const int ry = 4 * g + r4;                             // tile row of this lane's V run (mod 16)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      voff[dt] = KB + ry * RBV + (((2 * dt + (c4 >> 1)) ^ (ry & (NCHV - 1))) << 4) + (c4 & 1) * 8;
+      voff[dt] = KB + ry * RBV + (((2 * dt + (c4 >> 1)) ^ swz_v<DV>(ry)) << 4) + (c4 & 1) * 8;
   }
 
   const int ntiles = (nhi + BN - 1) / BN;
   __builtin_amdgcn_s_waitcnt(0);                          // query fragments are in
-  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 0) issue_tile(0, stage0);
 
   f32x4 st[QT][NKT];
   // S^T = K Q^T for the tile in `stage`
-  auto do_scores = [&](int stage) {
-    const char* Kt = ring[stage];
+  auto do_scores = [&](const char* Kt) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -441,9 +468,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
           st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
       }
   };
-  // masks, online softmax (lazy rescale) and O^T += V^T P^T for tile `it`
-  auto do_softmax_pv = [&](int it, int stage) {
-    const int c0 = it * BN;
+  // keys at or past a query's visible count get -inf
+  auto do_mask = [&](int c0) {
     if ((c0 + BN) > nlo) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -453,9 +479,41 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
           for (int i = 0; i < 4; ++i)
             if ((c0 + kt * 16 + 4 * g + i) >= nq[qt]) st[qt][kt][i] = -INFINITY;
     }
-    // The running maximum is common to the four lanes of a query; a lane-local
-    // maximum decides whether it must grow, and only then is the row maximum
-    // formed across lanes.
+  };
+  // probabilities against the current maximum, rounded to bf16: the B operand of
+  // O^T += V^T P^T.  Within each 32-key half u, B's row k = 8g + j holds key
+  // 32u + 4g + j (j < 4) or 32u + 16 + 4g + j - 4 (j >= 4); the V^T fragments
+  // follow the same order.
+  bf16x8 pb[NKT / 2][QT];
+  auto do_probs = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
+#pragma unroll
+      for (int u = 0; u < NKT / 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[u][qt][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[qt][2 * u][i], sl2, mneg)));
+          pb[u][qt][4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[qt][2 * u + 1][i], sl2, mneg)));
+        }
+    }
+  };
+  // the tile's row sums of those probabilities, formed on MFMA as 1^T P^T: every
+  // lane receives its query's sum over all 64 keys
+  auto do_rowsum = [&](float (&ls)[QT]) {
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = static_cast<__bf16>(1.0f);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      f32x4 r = (f32x4)(0.f);
+#pragma unroll
+      for (int u = 0; u < NKT / 2; ++u) r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[u][qt], r, 0, 0, 0);
+      ls[qt] = r[0];
+    }
+  };
+  // exact path: row maxima, rescale, probabilities against the new maximum
+  auto do_exact = [&]() {
     bool grow = false;
     float m_loc[QT];
 #pragma unroll
@@ -480,61 +538,69 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
         m_run[qt] = mn;
       }
     }
+    do_probs();
+    float ls[QT];
+    do_rowsum(ls);
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(st[qt][kt][i], sl2, mneg));
-          st[qt][kt][i] = pr;
-          psum += pr;
-        }
-      l_run[qt] += psum;
-    }
-    const char* Kt = ring[stage];
+    for (int qt = 0; qt < QT; ++qt) l_run[qt] += ls[qt];
+  };
+  // O^T += V^T P^T for the tile in `stage`
+  auto do_pv = [&](const char* Vt) {
 #pragma unroll
     for (int u = 0; u < NKT / 2; ++u) {
-      bf16x8 pb[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[qt][i] = static_cast<__bf16>(st[qt][2 * u][i]);
-          pb[qt][4 + i] = static_cast<__bf16>(st[qt][2 * u + 1][i]);
-        }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const short4v lo = lds_read_tr16(Kt, voff[dt] + 32 * u * RBV);
-        const short4v hi = lds_read_tr16(Kt, voff[dt] + (32 * u + 16) * RBV);
+        const short4v lo = lds_read_tr16(Vt, voff[dt] + 32 * u * RBV);
+        const short4v hi = lds_read_tr16(Vt, voff[dt] + (32 * u + 16) * RBV);
         short8v va;
         va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
         va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
         const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[qt], acc[qt][dt], 0, 0, 0);
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u][qt], acc[qt][dt], 0, 0, 0);
       }
     }
   };
 
-  // Step it: tile it has landed (wait, then barrier: every wave is also done with
-  // tile it-1, whose stage the next load overwrites); fetch tile it+1; consume it.
-  for (int it = 0; it < ntiles; ++it) {
+  // Step it: tile it has landed in `cur` (wait, then barrier: every wave is also
+  // done with tile it-1, whose stage `nxt` the next load overwrites); fetch tile
+  // it+1 into `nxt`; consume tile it.
+  auto step = [&](int it, char* cur, char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) % NST);
-    do_scores(it % NST);
-    do_softmax_pv(it, it % NST);
+    if (it + 1 < ntiles) issue_tile(it + 1, nxt);
+    do_scores(cur);
+    do_mask(it * BN);
+    bool exact = (it == 0);
+    if (!exact) {
+      do_probs();
+      float ls[QT];
+      do_rowsum(ls);
+      bool over = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) over |= ls[qt] > kLazySum;
+      if (__any(over)) {
+        exact = true;
+        do_scores(cur);
+        do_mask(it * BN);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) l_run[qt] += ls[qt];
+      }
+    }
+    if (exact) do_exact();
+    do_pv(cur);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, stage0, stage1);
+    if (it + 1 < ntiles) step(it + 1, stage1, stage0);
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, kWave);
-    l_tot += __shfl_xor(l_tot, 32, kWave);
+    const float l_tot = l_run[qt];                       // full row sum in every lane
     const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     const int t = tq[qt];
     const bool tvalid = t < a.T;
@@ -576,10 +642,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v4_kernel(AttnArgs a) {
 }
 
 template <int DK, int DV>
-static hipError_t launch_attn_bf16_v4(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_attn_bf16_v5(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 2, BM = 4 * 16 * QT;
   const int nqb = (a.T + BM - 1) / BM;
-  hipLaunchKernelGGL((attn_bf16_v4_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -596,10 +662,10 @@ hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
   } else {
-    if (dk == 64 && dv == 64) return launch_attn_bf16_v4<64, 64>(a, s);
-    if (dk == 64 && dv == 128) return launch_attn_bf16_v4<64, 128>(a, s);
-    if (dk == 128 && dv == 64) return launch_attn_bf16_v4<128, 64>(a, s);
-    if (dk == 128 && dv == 128) return launch_attn_bf16_v4<128, 128>(a, s);
+    if (dk == 64 && dv == 64) return launch_attn_bf16_v5<64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_attn_bf16_v5<64, 128>(a, s);
+    if (dk == 128 && dv == 64) return launch_attn_bf16_v5<128, 64>(a, s);
+    if (dk == 128 && dv == 128) return launch_attn_bf16_v5<128, 128>(a, s);
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;

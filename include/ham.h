@@ -68,7 +68,7 @@ typedef struct {
     int io_dtype;     /* HAM_F32 or HAM_BF16                                      */
     float scale;      /* attention logit scale, > 0 (usually 1/sqrt(dk))         */
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
-    int cap;          /* KV-cache capacity per (b,h), in tokens                   */
+    int cap;          /* KV-cache capacity per (b,h), in tokens, 1..4194304       */
     int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT                       */
     int t0;           /* absolute position of token 0 (recorded in pos)          */
 } ham_dims;
