@@ -81,6 +81,8 @@ def test_forward_argument_errors():
     a = list(base)
     a[0] = P((1 << 20) + 2)
     assert _fwd(dims(), a) == _lib.HAM_EINVAL and "aligned" in _msg()
+    assert _fwd(dims(cap=(1 << 22) + 1)) == _lib.HAM_EUNSUPPORTED and "cap" in _msg()
+    assert _fwd(dims(T=0)) == _lib.HAM_EINVAL
     # capacity without continuation
     assert _fwd(dims(cap=100)) == _lib.HAM_ECAPACITY
     # workspace
