@@ -51,7 +51,7 @@ def _load():
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
             [ctypes.c_int] * 5 + [ctypes.c_double] * 2 + [P] * 3 + [P] * 3 + [P] * 3
-            + [P] * 2 + [P] * 3 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
+            + [P] * 2 + [P] * 4 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
         return lib
@@ -70,14 +70,16 @@ def default_threads() -> int:
 
 
 def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
-            v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, S0=None,
-            cache=None, cap=None, t0=0, emit=None, threads=None):
+            v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, router_score=None,
+            S0=None, cache=None, cap=None, t0=0, emit=None, threads=None):
     """Run the oracle over all heads.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
     S0: [B,H,dk,dv] or None (zeros).  cache: None or dict(Kc, Vc, pos, count) of an
     existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
-    absolute position of token 0.  emit: None or [B,T,H] bool; False skips the
+    absolute position of token 0.  router_score: None or [B,T,H] float32 scores of a
+    learned router that replace the fit-error score (the decision is score > tau).
+    emit: None or [B,T,H] bool; False skips the
     attention readout and mix of that token (o_kv, o stay 0).  Returns a dict of float64 / int arrays:
     e, routed, o_rnn, o_kv, o, S, Kc, Vc, pos, count.
     """
@@ -90,6 +92,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
     tau = np.ascontiguousarray(np.asarray(tau, dtype=np.float32).reshape(H))
     mo = None if mask_override is None else np.ascontiguousarray(
         np.asarray(mask_override).astype(np.int8))
+    rs = None if router_score is None else np.ascontiguousarray(
+        np.asarray(router_score, dtype=np.float32).reshape(B, T, H))
     em = None if emit is None else np.ascontiguousarray(np.asarray(emit).astype(np.int8))
     t0a = np.ascontiguousarray(np.broadcast_to(np.asarray(t0, dtype=np.int64), (B,)))
     S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
@@ -122,7 +126,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
         return lib.ham_oracle_forward(
             B, T, H, dk, dv, float(scale), float(eps),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
-            _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(em), _ptr(t0a),
+            _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(rs), _ptr(em),
+            _ptr(t0a),
             _ptr(S), cap, _ptr(Kc), _ptr(Vc), _ptr(pos), _ptr(count),
             _ptr(e), _ptr(routed), _ptr(o_rnn), _ptr(o_kv), _ptr(o),
             bounds[i], bounds[i + 1])
@@ -136,6 +141,30 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
         raise RuntimeError("oracle: KV cache capacity exceeded")
     return dict(e=e, routed=routed, o_rnn=o_rnn, o_kv=o_kv, o=o, S=S, Kc=Kc, Vc=Vc,
                 pos=pos, count=count)
+
+
+def select_tau(e, rho):
+    """Per-head threshold for a target KV fraction rho ([HAM] §5: rho_KV, the share of
+    a layer's tokens kept in the KV cache; App. A.1 "Forward Pass": a token is stored
+    when its score exceeds the threshold).  For head h the N = B*T scores e[:, :, h]
+    are sorted ascending (NaN last); k = round(rho * N) (Python's round: nearest,
+    ties to even); tau = +inf for k = 0, -inf for k = N, otherwise the float32 nearest
+    to the midpoint of the (N-k)-th and (N-k+1)-th smallest scores, so that exactly k
+    scores exceed it when those two differ.  Returns float32 [H]."""
+    e = np.asarray(e, dtype=np.float32)
+    B, T, H = e.shape
+    N = B * T
+    k = int(round(rho * N))
+    out = np.empty(H, dtype=np.float32)
+    for h in range(H):
+        if k == 0:
+            out[h] = np.inf
+        elif k == N:
+            out[h] = -np.inf
+        else:
+            s = np.sort(e[:, :, h].reshape(-1).astype(np.float64))
+            out[h] = np.float32(0.5 * (s[N - k - 1] + s[N - k]))
+    return out
 
 
 def route_stats(out, tau, near_band=1e-5):

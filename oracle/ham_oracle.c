@@ -21,6 +21,11 @@
  *   e_t     = 1 - cos(p_t, v_t)   (cos := 0 if either vector is zero)
  *             ([HAM] §2 "Prediction Error as Routing Metric")
  *   routed  = float(e_t) > tau_h   (strict; NaN never routes)
+ *             With a learned input router the score is instead the caller's
+ *             e_t = router_score_t (sigma(W_r x_t) or sigma(MLP(x_t)), computed
+ *             outside the layer; [HAM] App. A.1 "Router Implementations", input
+ *             router, and "Forward Pass": scale s = 1 for learned routers); the
+ *             RNN still reads every token.
  *   S_t     = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
  *             ([HAM] §2 DeltaNet update, one gradient step on 1/2|S k - v|^2,
  *              with the gated-DeltaNet decay on the whole old state, App. A.1)
@@ -82,7 +87,8 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
  * inputs, or NULL to share q/k/v ([HAM] §2 implementation details: shared
  * projections).  gate_rnn/gate_kv: NULL means 1.  mask_override: NULL, or a
  * [B,T,H] array of 0/1 that replaces the threshold decision (the score e is
- * still computed).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
+ * still computed).  router_score: NULL, or a [B,T,H] fp32 array of routing
+ * scores that replaces the fit-error score (e is then a copy of it).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
  * attention readout and the mix of that token are skipped (o_kv and o stay as
  * they were) -- this only saves time when a few sampled tokens are checked.
  * Outputs e, routed, o_rnn, o_kv, o may each be NULL.
@@ -95,8 +101,8 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                        const double *qa, const double *ka, const double *va,
                        const double *beta, const double *g, const float *tau,
                        const double *gate_rnn, const double *gate_kv,
-                       const int8_t *mask_override, const int8_t *emit,
-                       const int64_t *t0,
+                       const int8_t *mask_override, const float *router_score,
+                       const int8_t *emit, const int64_t *t0,
                        double *S, int cap, double *Kc, double *Vc,
                        int64_t *pos, int64_t *count,
                        double *e, int8_t *routed,
@@ -136,7 +142,7 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                 p[j] = acc;
             }
             /* routing score and decision (decision taken in fp32, like the GPU) */
-            const double et = 1.0 - cosine(p, vt, dv);
+            const double et = router_score ? (double)router_score[tok] : 1.0 - cosine(p, vt, dv);
             int r;
             if (mask_override)
                 r = mask_override[tok] != 0;

@@ -280,3 +280,85 @@ def test_capacity_overflow_is_an_error():
     inp = make_inputs(1, 20, 1, 8, seed=18)
     with pytest.raises(RuntimeError):
         oracle.forward(**inp, tau=np.array([-INF]), scale=0.5, cap=5)
+
+
+# --- learned-router scores and the threshold for a target fraction ------------------
+def test_router_scores_route_by_score_and_leave_the_rnn_alone():
+    """With a learned router the decision is score > tau on the caller's scores; the
+    RNN (state, readout) is the same as without routing; the KV readout is a dense
+    softmax over the keys whose score clears tau."""
+    rng = np.random.default_rng(41)
+    B, T, H, d = 2, 60, 2, 16
+    inp = make_inputs(B, T, H, d, seed=41)
+    rs = rng.random((B, T, H), dtype=np.float32)           # sigma(.) of a router lies in (0, 1)
+    tau = np.array([0.4, 0.7], np.float32)
+    out = oracle.forward(**inp, tau=tau, scale=0.25, router_score=rs)
+    base = oracle.forward(**inp, tau=np.full(H, INF), scale=0.25)
+    np.testing.assert_array_equal(out["routed"], (rs > tau[None, None, :]).astype(np.int8))
+    np.testing.assert_array_equal(out["e"], rs.astype(np.float64))
+    np.testing.assert_array_equal(out["o_rnn"], base["o_rnn"])
+    np.testing.assert_array_equal(out["S"], base["S"])
+    for b in range(B):
+        for h in range(H):
+            m = rs[b, :, h] > tau[h]
+            allowed = np.tril(np.ones((T, T), bool)) & m[None, :]
+            ref = masked_softmax_attention(inp["q"][b, :, h].astype(np.float64), inp["k"][b, :, h].astype(np.float64),
+                                           inp["v"][b, :, h].astype(np.float64), allowed, 0.25)
+            np.testing.assert_allclose(out["o_kv"][b, :, h], ref, rtol=1e-12, atol=1e-12)
+            assert out["pos"][b, h, :m.sum()].tolist() == np.nonzero(m)[0].tolist()
+
+
+def test_router_scores_equal_to_the_fit_error_reproduce_the_default_path():
+    B, T, H, d = 1, 50, 2, 16
+    inp = make_inputs(B, T, H, d, seed=42)
+    base = oracle.forward(**inp, tau=np.full(H, INF), scale=0.25)
+    tau = tau_for_rho(base["e"], 0.5)
+    ref = oracle.forward(**inp, tau=tau, scale=0.25)
+    out = oracle.forward(**inp, tau=tau, scale=0.25, router_score=ref["e"].astype(np.float32))
+    np.testing.assert_array_equal(out["routed"], ref["routed"])
+    for n in ("o", "o_kv", "o_rnn", "S", "Kc", "Vc", "pos", "count"):
+        np.testing.assert_array_equal(out[n], ref[n])
+
+
+def test_select_tau_brute_force():
+    """Counting pins: exactly k = round(rho*N) scores exceed tau when the scores are
+    distinct, tau sits strictly between the two order statistics around the cut, and
+    k = 0 / k = N give +inf / -inf."""
+    rng = np.random.default_rng(43)
+    for (B, T, H) in ((1, 7, 1), (2, 50, 3), (3, 101, 2)):
+        e = rng.standard_normal((B, T, H)).astype(np.float32)
+        N = B * T
+        for rho in (0.0, 0.01, 0.1, 0.25, 0.5, 0.77, 0.99, 1.0):
+            tau = oracle.select_tau(e, rho)
+            k = int(round(rho * N))
+            for h in range(H):
+                x = e[:, :, h].reshape(-1)
+                if k == 0:
+                    assert tau[h] == np.inf
+                elif k == N:
+                    assert tau[h] == -np.inf
+                else:
+                    assert int((x > tau[h]).sum()) == k
+                    below = np.sort(x)[N - k - 1]
+                    above = np.sort(x)[N - k]
+                    assert below <= tau[h] <= above and below < above
+
+
+def test_select_tau_ties_nan_and_rounding():
+    # ties: every score equal -> tau is that value and nothing exceeds it
+    e = np.full((1, 10, 1), 0.25, np.float32)
+    assert oracle.select_tau(e, 0.5)[0] == np.float32(0.25)
+    # NaN sorts above every number and never routes: with 3 NaNs among 8 scores and
+    # k = 5 the NaNs take the top three ranks, the cut lies between 0.5 and 0.7, and
+    # only the two numbers above it exceed tau
+    x = np.array([0.1, np.nan, 0.5, 0.3, np.nan, 0.9, 0.7, np.nan], np.float32).reshape(1, 8, 1)
+    tau = oracle.select_tau(x, 5 / 8)
+    assert tau[0] == np.float32(0.5 * (np.float64(np.float32(0.5)) + np.float64(np.float32(0.7))))
+    assert int((x > tau[0]).sum()) == 2
+    # k = round(rho*N) with ties to even: N = 2, rho = 0.25 -> 0.5 -> 0 (+inf); rho = 0.75 -> 1.5 -> 2 (-inf)
+    y = np.array([1.0, 2.0], np.float32).reshape(1, 2, 1)
+    assert oracle.select_tau(y, 0.25)[0] == np.inf
+    assert oracle.select_tau(y, 0.75)[0] == -np.inf
+    # the midpoint is formed in double and rounded once to float32
+    z = np.array([1.0, np.nextafter(np.float32(1.0), np.float32(2.0))], np.float32).reshape(1, 2, 1)
+    assert oracle.select_tau(z, 0.5)[0] == np.float32(0.5 * (1.0 + np.float64(z[0, 1, 0])))
