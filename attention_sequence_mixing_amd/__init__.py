@@ -16,11 +16,12 @@ import math
 import torch
 
 from . import _lib
-from ._lib import (HAM_BF16, HAM_CONTINUE, HAM_F32, HAM_FORCE_RECURRENT, HamDims, HamError,
-                   check)
+from ._lib import (HAM_BF16, HAM_CONTINUE, HAM_EXTERNAL_SCORES, HAM_F32, HAM_FORCE_RECURRENT,
+                   HamDims, HamError, check)
 
-__all__ = ["ham_forward", "ham_decode_step", "ham_route_stats", "ForwardPlan", "DecodePlan",
-           "HamError", "HAM_CONTINUE", "HAM_FORCE_RECURRENT", "library_path"]
+__all__ = ["ham_forward", "ham_decode_step", "ham_route_stats", "ham_select_tau", "ForwardPlan",
+           "DecodePlan", "HamError", "HAM_CONTINUE", "HAM_FORCE_RECURRENT", "HAM_EXTERNAL_SCORES",
+           "library_path"]
 
 library_path = _lib.LIB_PATH
 
@@ -92,7 +93,10 @@ class ForwardPlan:
         self.count = torch.zeros((B, H), dtype=torch.int32, device=device)
 
     def __call__(self, q, k, v, beta, g, tau, *, q_attn=None, k_attn=None, v_attn=None,
-                 gate_rnn=None, gate_kv=None, S0=None, stream=None):
+                 gate_rnn=None, gate_kv=None, S0=None, router_scores=None, stream=None):
+        """router_scores: [B,T,H] float32 scores of a learned router, which then replace
+        the RNN's prediction error as the routing score (needs the plan to have been
+        made with flags including HAM_EXTERNAL_SCORES)."""
         B, T, H, dk, dv = self.shape
         dev, dt = self.device, self.dtype
         for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
@@ -105,6 +109,11 @@ class ForwardPlan:
         _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
         if q is None or k is None or v is None or beta is None or g is None or tau is None:
             raise ValueError("q, k, v, beta, g and tau are required")
+        ext = bool(self.dims.flags & HAM_EXTERNAL_SCORES)
+        if ext != (router_scores is not None):
+            raise ValueError("router_scores must be given exactly when the plan has HAM_EXTERNAL_SCORES")
+        if ext:
+            self.e = _need("router_scores", router_scores, (B, T, H), torch.float32, dev)
         rc = _lib.lib().ham_forward(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
             _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S0), _vp(self.S),
@@ -121,16 +130,21 @@ class ForwardPlan:
 
 def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
-                t0=0, force_recurrent=False, want_o_rnn=False, want_o_kv=False, stream=None):
+                t0=0, force_recurrent=False, router_scores=None, want_o_rnn=False,
+                want_o_kv=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
 
     cache: None, or dict(Kc, Vc, pos, count) of an earlier call to continue; it
-    is then extended in place and S0 should be that call's state.  Returns a dict
-    with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if asked).
+    is then extended in place and S0 should be that call's state.  router_scores:
+    None, or [B,T,H] float32 scores of a learned router that replace the RNN's
+    prediction error as the routing score (tau then in the router's units).
+    Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
+    asked); e is the routing score used.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    flags = (HAM_FORCE_RECURRENT if force_recurrent else 0) | (HAM_CONTINUE if cache is not None else 0)
+    flags = ((HAM_FORCE_RECURRENT if force_recurrent else 0) | (HAM_CONTINUE if cache is not None else 0)
+             | (HAM_EXTERNAL_SCORES if router_scores is not None else 0))
     if cache is not None:
         cap = cache["Kc"].shape[2]
     plan = ForwardPlan(B, T, H, dk, dv, q.dtype, q.device, cap=cap, scale=scale,
@@ -142,7 +156,7 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
         plan.pos = _need("pos", cache["pos"], (B, H, plan.cap), torch.int32, q.device)
         plan.count = _need("count", cache["count"], (B, H), torch.int32, q.device)
     plan(q, k, v, beta, g, tau, q_attn=q_attn, k_attn=k_attn, v_attn=v_attn,
-         gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, stream=stream)
+         gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, router_scores=router_scores, stream=stream)
     return plan.result()
 
 
@@ -170,7 +184,10 @@ class DecodePlan:
         self.status = torch.zeros((1,), dtype=torch.int32, device=device)
 
     def __call__(self, q, k, v, beta, g, tau, S, Kc, Vc, pos, count, t_abs, *, q_attn=None,
-                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, stream=None):
+                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, router_scores=None,
+                 stream=None):
+        """router_scores: None, or [B,H] float32 learned-router scores of the new tokens,
+        which then replace the RNN's prediction error as the routing score."""
         B, H, dk, dv, cap = self.shape
         dev, dt = self.device, self.dtype
         for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
@@ -186,11 +203,14 @@ class DecodePlan:
         _need("pos", pos, (B, H, cap), torch.int32, dev)
         _need("count", count, (B, H), torch.int32, dev)
         _need("t_abs", t_abs, (B,), torch.int32, dev)
+        _need("router_scores", router_scores, (B, H), torch.float32, dev)
+        self.dims.flags = HAM_EXTERNAL_SCORES if router_scores is not None else 0
+        e = router_scores if router_scores is not None else self.e
         rc = _lib.lib().ham_decode_step(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
             _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S), _vp(Kc), _vp(Vc),
             _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
-            _vp(self.e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
+            _vp(e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
             _stream(stream))
         check(rc)
         return self
@@ -242,3 +262,18 @@ def ham_route_stats(k, v, beta, g, tau, *, q=None, S0=None, near_band=1e-5, want
                            _vp(ws), ws.numel(), _stream(stream))
     check(rc)
     return dict(e=e, routed=routed, count=count, n_near=n_near, rho=rho.value if want_rho else None)
+
+
+def ham_select_tau(e, rho, *, out=None, stream=None):
+    """Per-head threshold [H] float32 that routes round(rho*B*T) of each head's scores
+    e [B,T,H] (float32, on the GPU): the midpoint of the two order statistics around
+    the cut; +inf for rho*N rounding to 0, -inf for N."""
+    B, T, H = e.shape
+    _need("e", e, (B, T, H), torch.float32, e.device)
+    tau = torch.empty((H,), dtype=torch.float32, device=e.device) if out is None else out
+    _need("out", tau, (H,), torch.float32, e.device)
+    dims = make_dims(B, T, H, 64, 64, HAM_F32, 1.0, 1e-6, max(T, 1))
+    rc = _lib.lib().ham_select_tau(ctypes.byref(dims), _vp(e), ctypes.c_double(float(rho)), _vp(tau),
+                                   _stream(stream))
+    check(rc)
+    return tau

@@ -13,12 +13,12 @@ LIB_PATH = os.path.join(HERE, "libham.so")
 
 HAM_OK, HAM_EINVAL, HAM_EUNSUPPORTED, HAM_ECAPACITY, HAM_EHIP, HAM_EWORKSPACE = 0, -1, -2, -3, -4, -5
 HAM_F32, HAM_BF16 = 0, 1
-HAM_CONTINUE, HAM_FORCE_RECURRENT = 1, 2
+HAM_CONTINUE, HAM_FORCE_RECURRENT, HAM_EXTERNAL_SCORES = 1, 2, 4
 
 # every symbol include/ham.h declares
 EXPORTS = ("ham_version", "ham_last_error", "ham_forward_workspace_size", "ham_forward",
            "ham_decode_workspace_size", "ham_decode_step", "ham_route_stats_workspace_size",
-           "ham_route_stats", "ham_profile_start", "ham_profile_stop")
+           "ham_route_stats", "ham_select_tau", "ham_profile_start", "ham_profile_stop")
 HAM_PROFILE_STAGES = 5
 
 
@@ -65,6 +65,8 @@ def lib():
     L.ham_decode_step.argtypes = [D] + [P] * 24 + [Z, P]
     L.ham_route_stats.restype = I
     L.ham_route_stats.argtypes = [D] + [P] * 11 + [ctypes.c_float, P, P, Z, P]
+    L.ham_select_tau.restype = I
+    L.ham_select_tau.argtypes = [D, P, ctypes.c_double, P, P]
     L.ham_profile_start.restype = I
     L.ham_profile_start.argtypes = [I]
     L.ham_profile_stop.restype = I

@@ -40,7 +40,7 @@ int check_dims(const ham_dims* d, bool need_T) {
     return fail(HAM_EUNSUPPORTED, "dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
   if (d->io_dtype != HAM_F32 && d->io_dtype != HAM_BF16)
     return fail(HAM_EUNSUPPORTED, "io_dtype must be HAM_F32 or HAM_BF16 (got %d)", d->io_dtype);
-  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT))
+  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES))
     return fail(HAM_EUNSUPPORTED, "unknown flag bits 0x%x", d->flags);
   if (d->cap <= 0) return fail(HAM_EINVAL, "cap must be positive (cap=%d)", d->cap);
   // the attention kernels address one head's cache rows with 32-bit byte offsets
@@ -197,6 +197,8 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
   HAM_ALIGNED(v_attn); HAM_ALIGNED(S0); HAM_ALIGNED(S_out); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn);
   HAM_ALIGNED(o_kv); HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
+  const bool ext = (d->flags & HAM_EXTERNAL_SCORES) != 0;
+  if (ext && !e) return fail(HAM_EINVAL, "HAM_EXTERNAL_SCORES needs the scores in e (NULL)");
   if (!(d->flags & HAM_CONTINUE) && d->cap < d->T)
     return fail(HAM_ECAPACITY, "cap (%d) < T (%d): the cache cannot hold every token", d->cap, d->T);
   const FwdLayout L = fwd_layout(d, false);
@@ -218,8 +220,9 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   rc = run_rnn(d, ra, s, &slices, tm);
   if (rc != HAM_OK) return rc;
 
-  ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count,
-                    (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H};
+  ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
+                    (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H,
+                    ext ? e : nullptr};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
 
@@ -251,6 +254,8 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
   HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
   HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
+  const bool ext = (d->flags & HAM_EXTERNAL_SCORES) != 0;
+  if (ext && !e) return fail(HAM_EINVAL, "HAM_EXTERNAL_SCORES needs the scores in e (NULL)");
   const DecLayout L = dec_layout(d);
   if (!ws || ws_bytes < L.total)
     return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
@@ -268,8 +273,8 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   ham::RnnArgs ra{q, k, v, beta, g, S, S, o_rnn32, score, nullptr, d->B, 1, d->H};
   HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
   tm.mark();
-  ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, e_buf, r_buf, chunk_count,
-                    count, count_in, d->B, 1, d->H};
+  ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, ext ? nullptr : e_buf, r_buf,
+                    chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
@@ -294,6 +299,9 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   (void)q;
   int rc = check_dims(d, true);
   if (rc != HAM_OK) return rc;
+  if (d->flags & HAM_EXTERNAL_SCORES)
+    return fail(HAM_EUNSUPPORTED, "ham_route_stats takes its scores from the RNN; use ham_select_tau "
+                                  "on learned-router scores");
   HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g); HAM_REQUIRE(tau);
   HAM_REQUIRE(count);
   HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(S0); HAM_ALIGNED(ws);
@@ -331,6 +339,19 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
     for (int32_t x : c) tot += x;
     *rho_host = tot / ((double)d->B * d->T * d->H);
   }
+  return HAM_OK;
+}
+
+int ham_select_tau(const ham_dims* d, const float* e, double rho, float* tau, void* stream) {
+  if (!d) return fail(HAM_EINVAL, "dims is NULL");
+  if (d->B <= 0 || d->T <= 0 || d->H <= 0)
+    return fail(HAM_EINVAL, "B, T and H must be positive (B=%d T=%d H=%d)", d->B, d->T, d->H);
+  if ((long long)d->B * d->T > 2147483647LL) return fail(HAM_EINVAL, "B*T must be < 2^31");
+  if (!(rho >= 0.0 && rho <= 1.0)) return fail(HAM_EINVAL, "rho must lie in [0, 1]");
+  HAM_REQUIRE(e); HAM_REQUIRE(tau);
+  const long long N = (long long)d->B * d->T;
+  const long long k = (long long)std::nearbyint(rho * (double)N);   // ties to even
+  HAM_HIP(ham::launch_select_tau(e, d->B, d->T, d->H, k, tau, static_cast<hipStream_t>(stream)));
   return HAM_OK;
 }
 

@@ -39,6 +39,8 @@ struct RouteArgs {
   const int32_t* count; // [B,H] entering count (HAM_CONTINUE) or null
   int32_t* count_in;    // [B*H] snapshot of the entering count
   int B, T, H;
+  const float* e_in;    // [B,T,H] caller's routing scores (learned router) or null;
+                        // when set, score/slices are unused and e is not written
 };
 
 struct CompactArgs {
@@ -118,6 +120,7 @@ bool rnn_chunked_supported(int io, int dk, int dv);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_compact(int io, int dk, int dv, const CompactArgs& a, hipStream_t s);
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, float* tau, hipStream_t s);
 hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hipStream_t s);

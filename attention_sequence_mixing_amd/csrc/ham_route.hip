@@ -20,7 +20,8 @@ namespace ham {
 // runs head-fastest so that e and routed ([B,T,H]) are written contiguously; the
 // per-head routed counts of the chunk are integer sums in LDS (order-independent).
 // NS (score slices per token) is a compile-time constant so that every slice load
-// of a thread is in flight at once.
+// of a thread is in flight at once.  NS = 0: the scores are the caller's (a learned
+// input router's sigma(W_r x_t), App. A.1 "Router Implementations"), read from e_in.
 template <int NS>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   extern __shared__ int s_cnt[];            // [H]
@@ -35,34 +36,43 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   const int nv = min(kChunk, a.T - t0);
   const int npair = nv * H;
   for (int base = 0; base < npair; base += 256 * PER) {
-    float4 x[PER][NS];
+    float4 x[PER][NS > 0 ? NS : 1];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int idx = min(base + tid + 256 * j, npair - 1);
       const int tl = idx / H, h = idx - tl * H;
-      const float4* sp = a.score + (((size_t)b * a.T + t0 + tl) * H + h) * NS;
+      if constexpr (NS > 0) {
+        const float4* sp = a.score + (((size_t)b * a.T + t0 + tl) * H + h) * NS;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) x[j][s] = sp[s];
+        for (int s = 0; s < NS; ++s) x[j][s] = sp[s];
+      } else {
+        x[j][0].x = a.e_in[((size_t)b * a.T + t0 + tl) * H + h];
+      }
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int idx = base + tid + 256 * j;
       if (idx >= npair) break;
       const int tl = idx / H, h = idx - tl * H;
-      float pv = 0.f, pp = 0.f, vv = 0.f;
+      float e;
+      if constexpr (NS > 0) {
+        float pv = 0.f, pp = 0.f, vv = 0.f;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        pv += x[j][s].x; pp += x[j][s].y; vv += x[j][s].z;
+        for (int s = 0; s < NS; ++s) {
+          pv += x[j][s].x; pp += x[j][s].y; vv += x[j][s].z;
+        }
+        float cs = 0.f;
+        if (pp > 0.f && vv > 0.f) {
+          cs = pv / (sqrtf(pp) * sqrtf(vv));
+          cs = fminf(1.f, fmaxf(-1.f, cs));
+        }
+        e = 1.f - cs;
+      } else {
+        e = x[j][0].x;
       }
-      float cs = 0.f;
-      if (pp > 0.f && vv > 0.f) {
-        cs = pv / (sqrtf(pp) * sqrtf(vv));
-        cs = fminf(1.f, fmaxf(-1.f, cs));
-      }
-      const float e = 1.f - cs;
       const bool r = e > a.tau[h];          // strict; a NaN score never routes
       const size_t tok = ((size_t)b * a.T + t0 + tl) * H + h;
-      a.e[tok] = e;
+      if constexpr (NS > 0) a.e[tok] = e;
       a.routed[tok] = (uint8_t)r;
       if (r) atomicAdd(&s_cnt[h], 1);
     }
@@ -79,7 +89,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kChunk - 1) / kChunk;
   const dim3 grid(nchunk, a.B);
   const size_t lds = a.H * sizeof(int);
-  if (a.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, a);
+  if (a.e_in) hipLaunchKernelGGL(route_kernel<0>, grid, dim3(256), lds, s, a);
+  else if (a.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, a);
   else if (a.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
@@ -204,6 +215,103 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(stats_kernel, dim3(a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- threshold for a target KV fraction ---------------------------------------------
+// "Hybrid Associative Memories" §5 (rho_KV, the fraction of a layer's tokens kept in
+// the KV cache) and App. A.1 "Forward Pass" (a token is stored when its score exceeds
+// the threshold).  For head h with N = B*T scores and k of them to keep, tau is the
+// float nearest to the midpoint of the (N-k)-th and (N-k+1)-th smallest scores.
+//
+// One workgroup per head finds both order statistics exactly by radix select on
+// order-preserving 32-bit keys (sign-magnitude floats mapped to unsigned order; every
+// NaN maps to the largest key, so NaN sorts above all numbers): four 8-bit digit
+// passes with LDS histograms (integer counts, so the result does not depend on the
+// order of the atomic adds) give the lower statistic; one more pass counts the keys
+// at or below it and takes the smallest key above it, which gives the upper one.
+HAM_DEVICE uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if (x != x) return 0xFFFFFFFFu;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+HAM_DEVICE float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__global__ __launch_bounds__(1024) void select_tau_kernel(const float* __restrict__ e, int B, int T, int H,
+                                                          long long k, float* __restrict__ tau) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit, s_below;
+  __shared__ uint32_t s_le[32], s_min[32];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const long long N = (long long)B * T;
+  if (k <= 0 || k >= N) {
+    if (tid == 0) tau[h] = (k <= 0) ? INFINITY : -INFINITY;
+    return;
+  }
+  const uint32_t n = (uint32_t)N;
+  auto key_at = [&](uint32_t i) { return order_key(e[(size_t)i * H + h]); };   // i = b*T + t
+  // lower statistic: rank r = N-k-1 (0-based) of the ascending order
+  uint32_t r = (uint32_t)(N - k - 1), prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += 1024) {
+      const uint32_t key = key_at(i);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // 256 bins, 4 per lane: inclusive scan over lanes of the lane sums
+      uint32_t c[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[lane * 4 + j]; sum += c[j]; }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const uint32_t y = __shfl_up(incl, m, kWave);
+        if (lane >= m) incl += y;
+      }
+      uint32_t run = incl - sum;                 // count in bins before this lane's
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run <= r && r < run + c[j]) { s_digit = (uint32_t)(lane * 4 + j); s_below = run; }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+    r -= s_below;
+    prefix |= s_digit << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t k1 = prefix;
+  // upper statistic: rank N-k; equal to the lower one when more than N-k keys are <= it
+  uint32_t le = 0, mn = 0xFFFFFFFFu;
+  for (uint32_t i = tid; i < n; i += 1024) {
+    const uint32_t key = key_at(i);
+    le += (key <= k1);
+    if (key > k1) mn = min(mn, key);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    le += __shfl_xor(le, m, kWave);
+    mn = min(mn, (uint32_t)__shfl_xor(mn, m, kWave));
+  }
+  if (lane == 0) { s_le[wave] = le; s_min[wave] = mn; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t L = 0, M = 0xFFFFFFFFu;
+    for (int w = 0; w < 16; ++w) { L += s_le[w]; M = min(M, s_min[w]); }
+    const uint32_t k2 = (L > (uint32_t)(N - k)) ? k1 : M;
+    const double mid = 0.5 * ((double)key_value(k1) + (double)key_value(k2));
+    tau[h] = (float)mid;
+  }
+}
+
+hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, float* tau, hipStream_t s) {
+  hipLaunchKernelGGL(select_tau_kernel, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
   return hipGetLastError();
 }
 

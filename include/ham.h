@@ -61,6 +61,13 @@ extern "C" {
 #define HAM_CONTINUE 1         /* S0 / Kc / Vc / pos / count hold an earlier call's
                                   state and cache; new entries are appended */
 #define HAM_FORCE_RECURRENT 2  /* run the token-serial RNN kernel even for long T */
+#define HAM_EXTERNAL_SCORES 4  /* e is an input: the routing scores of a learned input
+                                  router (sigma(W_r x_t) or sigma(MLP(x_t)), computed by
+                                  the caller; [HAM] App. A.1 "Router Implementations",
+                                  scale s = 1 in "Forward Pass") replace the RNN's
+                                  prediction error; tau is in the same units.  The RNN
+                                  still reads every token.  ham_forward and
+                                  ham_decode_step only. */
 
 typedef struct {
     int B, T, H;      /* batch, new tokens per sequence, heads                   */
@@ -69,7 +76,7 @@ typedef struct {
     float scale;      /* attention logit scale, > 0 (usually 1/sqrt(dk))         */
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
     int cap;          /* KV-cache capacity per (b,h), in tokens, 1..4194304       */
-    int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT                       */
+    int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES  */
     int t0;           /* absolute position of token 0 (recorded in pos)          */
 } ham_dims;
 
@@ -100,7 +107,9 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  *   o                  [B,T,H,dv] io dtype, required: mixed output.
  *   o_rnn, o_kv        [B,T,H,dv] io dtype or NULL: the two readouts before the
  *                      norms (o_kv = 0 where nothing is visible).
- *   e                  [B,T,H] fp32 or NULL: routing scores.
+ *   e                  [B,T,H] fp32 or NULL: routing scores (output).  With
+ *                      HAM_EXTERNAL_SCORES it is a required input: the caller's
+ *                      scores, read and not written.
  *   routed             [B,T,H] uint8 or NULL: 1 where routed.
  *   Kc, Vc, pos, count the per-(b,h) KV cache, required.  Without HAM_CONTINUE
  *                      count is output only and entries [0,count) are written;
@@ -142,7 +151,8 @@ size_t ham_decode_workspace_size(const ham_dims *dims);
  *   Kc, Vc, pos, count           cache, in/out (count[b,h] <= cap on entry).
  *   t_abs                        [B] int32 absolute position of the new token.
  *   o (required), o_rnn, o_kv    [B,H,dv] io dtype.
- *   e, routed                    [B,H] or NULL.
+ *   e, routed                    [B,H] or NULL (with HAM_EXTERNAL_SCORES, e is
+ *                                the required input score of the new token).
  *   status                       int32 scalar or NULL: set to 1 (never cleared)
  *                                when a routed token found its cache full; the
  *                                append is then skipped.
@@ -173,6 +183,8 @@ size_t ham_route_stats_workspace_size(const ham_dims *dims);
  *                                near_band (near-threshold tokens).
  *   rho_host                     HOST double* or NULL; if set, the call waits for
  *                                the stream and stores rho there.
+ * HAM_EXTERNAL_SCORES is not accepted (HAM_EUNSUPPORTED): with a learned router
+ * the scores do not come from the RNN; ham_select_tau sets a threshold on them.
  */
 int ham_route_stats(const ham_dims *dims,
                     const void *q, const void *k, const void *v,
@@ -181,6 +193,27 @@ int ham_route_stats(const ham_dims *dims,
                     float *e, uint8_t *routed, int32_t *count,
                     int64_t *n_near, float near_band, double *rho_host,
                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ham_select_tau -- per-head threshold for a target KV fraction rho ([HAM] §5:
+ * rho_KV, the share of a layer's tokens kept in the KV cache; App. A.1 "Forward
+ * Pass": a token is stored when its score exceeds the threshold; one threshold
+ * per head here).  For head h, with the N = B*T scores e[:, :, h] and k = rho*N
+ * rounded to the nearest integer (ties to even):
+ *   tau[h] = +inf when k = 0, -inf when k = N, and otherwise the float nearest to
+ *   the midpoint (formed in double) of the (N-k)-th and (N-k+1)-th smallest
+ *   scores, NaN sorting above every number.  Exactly k scores then exceed tau[h]
+ *   when those two differ; NaN scores never route.
+ *
+ *   dims   B, T, H (other fields are not read; B*T <= 2^31 - 1).
+ *   e      [B,T,H] fp32 device scores (fit-error or learned-router units).
+ *   rho    in [0, 1].
+ *   tau    [H] fp32 device output.
+ * No workspace; one workgroup per head (exact radix select, deterministic).
+ * Errors: HAM_EINVAL (NULL pointer, B/T/H <= 0, B*T too large, rho outside
+ * [0, 1] or NaN, misaligned pointer), HAM_EHIP.
+ */
+int ham_select_tau(const ham_dims *dims, const float *e, double rho, float *tau, void *stream);
 
 /*
  * Instrumentation (not part of the method): HIP-event timing of the kernel

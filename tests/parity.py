@@ -65,9 +65,12 @@ def check_routing(e_gpu, r_gpu, ref, tau):
 
 
 def check_forward(out, inp, tau, dtype, *, scale, ref=None, gates=None, attn=None, S0=None,
-                  cache=None, t0=0, eps=1e-6, check_outputs=("o", "o_rnn", "o_kv"), cap=None):
-    """Full comparison of one ham_forward result against the oracle."""
-    okw = dict(scale=scale, eps=eps, S0=S0, cache=cache, t0=t0, cap=cap)
+                  cache=None, t0=0, eps=1e-6, check_outputs=("o", "o_rnn", "o_kv"), cap=None,
+                  router_score=None):
+    """Full comparison of one ham_forward result against the oracle.  With learned-router
+    scores both sides compare the same float32 score with the same threshold, so the
+    routing must match exactly (no near-threshold exemption)."""
+    okw = dict(scale=scale, eps=eps, S0=S0, cache=cache, t0=t0, cap=cap, router_score=router_score)
     if gates is not None:
         okw.update(gate_rnn=gates[0], gate_kv=gates[1])
     if attn is not None:
@@ -77,6 +80,9 @@ def check_forward(out, inp, tau, dtype, *, scale, ref=None, gates=None, attn=Non
     e_gpu = out["e"].cpu().numpy()
     r_gpu = out["routed"].cpu().numpy()
     nflip = check_routing(e_gpu, r_gpu, ref, tau)
+    if router_score is not None:
+        assert np.array_equal(e_gpu, np.asarray(router_score, np.float32))
+        assert nflip == 0 and np.array_equal(r_gpu.astype(bool), ref["routed"].astype(bool))
     if nflip:
         ref = oracle.forward(**inp, tau=tau, mask_override=r_gpu, **okw)
     tol = TOL[dtype]

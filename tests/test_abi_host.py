@@ -123,3 +123,28 @@ def test_product_path_has_no_oracle_dependency():
                 assert "oracle" not in txt.lower(), f
     with open(_lib.LIB_PATH, "rb") as fh:
         assert b"ham_oracle" not in fh.read()
+
+
+def test_select_tau_and_external_score_errors():
+    L = _lib.lib()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    d = dims(B=2, T=100, H=3)
+    assert L.ham_select_tau(ctypes.byref(d), fake, ctypes.c_double(1.5), fake, None) == _lib.HAM_EINVAL
+    assert "rho" in _msg()
+    assert L.ham_select_tau(ctypes.byref(d), fake, ctypes.c_double(float("nan")), fake, None) == _lib.HAM_EINVAL
+    assert L.ham_select_tau(ctypes.byref(d), None, ctypes.c_double(0.5), fake, None) == _lib.HAM_EINVAL
+    assert L.ham_select_tau(ctypes.byref(dims(B=0)), fake, ctypes.c_double(0.5), fake, None) == _lib.HAM_EINVAL
+    assert L.ham_select_tau(ctypes.byref(dims(B=65536, T=65536)), fake, ctypes.c_double(0.5), fake,
+                            None) == _lib.HAM_EINVAL
+    # external scores need e
+    base = [fake] * 23
+    a = list(base)
+    a[16] = None                                       # e
+    assert _fwd(dims(flags=_lib.HAM_EXTERNAL_SCORES), a) == _lib.HAM_EINVAL and "EXTERNAL" in _msg()
+    a = [fake] * 24
+    a[20] = None                                       # e of the decode step
+    assert L.ham_decode_step(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *a, 1 << 40, None) == _lib.HAM_EINVAL
+    s = [fake] * 11
+    assert L.ham_route_stats(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *s, ctypes.c_float(1e-5), None,
+                             fake, 1 << 40, None) == _lib.HAM_EUNSUPPORTED
