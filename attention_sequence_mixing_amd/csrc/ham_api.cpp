@@ -215,6 +215,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   int32_t* ntok = at<int32_t>(ws, L.ntok);
 
   CallTimer tm(0, s);
+  // with learned-router scores the RNN's score partials are computed and left unused
   ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, at<char>(ws, L.prep), d->B, d->T, d->H};
   int slices = 0;
   rc = run_rnn(d, ra, s, &slices, tm);

@@ -230,6 +230,7 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
 // passes with LDS histograms (integer counts, so the result does not depend on the
 // order of the atomic adds) give the lower statistic; one more pass counts the keys
 // at or below it and takes the smallest key above it, which gives the upper one.
+// Heads of up to 32768 scores keep their keys in LDS for all five passes.
 HAM_DEVICE uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
   if (x != x) return 0xFFFFFFFFu;
@@ -239,11 +240,15 @@ HAM_DEVICE float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+constexpr int kSelectLdsKeys = 32768;     // a head's keys are staged in LDS up to this many
+
+template <bool STAGED>
 __global__ __launch_bounds__(1024) void select_tau_kernel(const float* __restrict__ e, int B, int T, int H,
                                                           long long k, float* __restrict__ tau) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_digit, s_below;
   __shared__ uint32_t s_le[32], s_min[32];
+  __shared__ uint32_t s_keys[STAGED ? kSelectLdsKeys : 1];
   const int h = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const long long N = (long long)B * T;
   if (k <= 0 || k >= N) {
@@ -251,7 +256,12 @@ __global__ __launch_bounds__(1024) void select_tau_kernel(const float* __restric
     return;
   }
   const uint32_t n = (uint32_t)N;
-  auto key_at = [&](uint32_t i) { return order_key(e[(size_t)i * H + h]); };   // i = b*T + t
+  // i = b*T + t; with STAGED the keys are read from HBM once and kept in LDS
+  if constexpr (STAGED) {
+    for (uint32_t i = tid; i < n; i += 1024) s_keys[i] = order_key(e[(size_t)i * H + h]);
+    __syncthreads();
+  }
+  auto key_at = [&](uint32_t i) { return STAGED ? s_keys[i] : order_key(e[(size_t)i * H + h]); };
   // lower statistic: rank r = N-k-1 (0-based) of the ascending order
   uint32_t r = (uint32_t)(N - k - 1), prefix = 0, pmask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(1024) void select_tau_kernel(const float* __restric
 }
 
 hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, float* tau, hipStream_t s) {
-  hipLaunchKernelGGL(select_tau_kernel, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
+  if ((long long)B * T <= kSelectLdsKeys)
+    hipLaunchKernelGGL(select_tau_kernel<true>, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
+  else
+    hipLaunchKernelGGL(select_tau_kernel<false>, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
   return hipGetLastError();
 }
 

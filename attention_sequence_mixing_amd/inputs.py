@@ -139,6 +139,14 @@ def tau_for_rho(e: np.ndarray, rho: float) -> np.ndarray:
     return tau
 
 
+def make_router_scores(B, T, H, seed):
+    """Synthetic learned-router scores [B,T,H] float32 in (0, 1): sigmoid(N(0,1)) per
+    token and head, standing in for sigma(W_r x_t) of a trained input router (no
+    weights exist for it here)."""
+    rng = np.random.default_rng(seed + 500)
+    return _sigmoid(rng.standard_normal((B, T, H), dtype=np.float32))
+
+
 def make_gates(B, T, H, seed):
     """Optional per-(t,h) mixing gates in (0,1), drawn as sigmoid(N(0,1))."""
     rng = np.random.default_rng(seed + 1000)

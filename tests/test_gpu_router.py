@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import attention_sequence_mixing_amd as ham
-from attention_sequence_mixing_amd.inputs import make_inputs, make_gates
+from attention_sequence_mixing_amd.inputs import make_inputs, make_gates, make_router_scores
 from parity import check_forward, np_of, rel_err_slices, to_dev, TOL
 
 pytestmark = pytest.mark.gpu
@@ -23,8 +23,7 @@ DEV = torch.device("cuda:0")
 def _router_scores(B, T, H, seed):
     """Scores in (0, 1) like sigma(W_r x); a few are set exactly to the threshold
     afterwards by the tests (ties do not route)."""
-    rng = np.random.default_rng(seed + 500)
-    return (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    return make_router_scores(B, T, H, seed).copy()
 
 
 @pytest.mark.parametrize("B,T,H,dk,dv", [(2, 200, 3, 128, 128), (1, 65, 2, 64, 128),
@@ -97,6 +96,7 @@ def _select_cases():
     cases.append(("nan_inf_zeros", x))
     cases.append(("pair", np.array([[[1.0], [2.0]]], np.float32)))
     cases.append(("layer_shape", rng.random((8, 4096, 16)).astype(np.float32) * 2.0))
+    cases.append(("above_lds_staging", rng.standard_normal((2, 20011, 3)).astype(np.float32)))
     return cases
 
 
