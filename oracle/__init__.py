@@ -50,7 +50,7 @@ def _load():
         P = ctypes.c_void_p
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
-            [ctypes.c_int] * 5 + [ctypes.c_double] * 2 + [P] * 3 + [P] * 3 + [P] * 3
+            [ctypes.c_int] * 5 + [ctypes.c_double] * 3 + [P] * 3 + [P] * 3 + [P] * 3
             + [P] * 2 + [P] * 4 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
@@ -69,7 +69,7 @@ def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
+def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=None, k_attn=None,
             v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, router_score=None,
             S0=None, cache=None, cap=None, t0=0, emit=None, threads=None):
     """Run the oracle over all heads.
@@ -77,7 +77,9 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
     S0: [B,H,dk,dv] or None (zeros).  cache: None or dict(Kc, Vc, pos, count) of an
     existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
-    absolute position of token 0.  router_score: None or [B,T,H] float32 scores of a
+    absolute position of token 0.  rope_base: 0, or the RoPE base applied to the
+    attention-path query and key at their positions (the cache holds rotated keys).
+    router_score: None or [B,T,H] float32 scores of a
     learned router that replace the fit-error score (the decision is score > tau).
     emit: None or [B,T,H] bool; False skips the
     attention readout and mix of that token (o_kv, o stay 0).  Returns a dict of float64 / int arrays:
@@ -124,7 +126,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, q_attn=None, k_attn=None,
 
     def run(i):
         return lib.ham_oracle_forward(
-            B, T, H, dk, dv, float(scale), float(eps),
+            B, T, H, dk, dv, float(scale), float(eps), float(rope_base),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
             _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(rs), _ptr(em),
             _ptr(t0a),

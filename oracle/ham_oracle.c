@@ -32,6 +32,10 @@
  *   o_rnn_t = S_t^T q_t                                 (post-update readout, [HAM] §2
  *                                                       linear-attention equation)
  *   if routed: append (k^a_t, v^a_t, position) to this head's cache
+ *   (with a rotary base b > 0 the attention-path query and key are rotated at
+ *    their original positions first: RoPE, [HAM] §4 "RoPE with a base of 500K for
+ *    all inputs to self-attention", citing Su et al.'s RoFormer: consecutive
+ *    pairs (x_2i, x_2i+1) turned by the angle position * b^(-2i/d_k))
  *   o_kv_t  = softmax over the cached keys, scale * q^a_t . k_c, of the cached
  *             values; 0 when the cache is empty           ([HAM] §2 KV-memory
  *             equation; causality by original position, App. A.1 "FlexAttention
@@ -46,6 +50,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* RoPE ([HAM] §4: base 500K for all inputs to self-attention; RoFormer, Su et al.):
+ * y_2i = x_2i cos(a_i) - x_2i+1 sin(a_i), y_2i+1 = x_2i sin(a_i) + x_2i+1 cos(a_i),
+ * a_i = pos * base^(-2i/d).  y may not alias x. */
+static void rope_rotate(const double *x, double *y, int d, double pos, double base)
+{
+    for (int i = 0; i < d / 2; ++i) {
+        const double a = pos * pow(base, -2.0 * i / d);
+        const double c = cos(a), s = sin(a);
+        y[2 * i] = x[2 * i] * c - x[2 * i + 1] * s;
+        y[2 * i + 1] = x[2 * i] * s + x[2 * i + 1] * c;
+    }
+}
 
 /* cosine of two vectors; 0 when either has zero norm.  [HAM] §2 routing score. */
 static double cosine(const double *a, const double *b, int n)
@@ -91,12 +108,14 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
  * scores that replaces the fit-error score (e is then a copy of it).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
  * attention readout and the mix of that token are skipped (o_kv and o stay as
  * they were) -- this only saves time when a few sampled tokens are checked.
+ * rope_base: 0 for none, else the rotary base applied to the attention-path
+ * query and key at their absolute positions (the cache then holds rotated keys).
  * Outputs e, routed, o_rnn, o_kv, o may each be NULL.
  *
  * Returns 0, or -3 if a routed token finds the cache full (the head stops there).
  */
 int ham_oracle_forward(int B, int T, int H, int dk, int dv,
-                       double scale, double eps,
+                       double scale, double eps, double rope_base,
                        const double *q, const double *k, const double *v,
                        const double *qa, const double *ka, const double *va,
                        const double *beta, const double *g, const float *tau,
@@ -118,6 +137,7 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
     double *tmp1 = (double *)malloc(sizeof(double) * (size_t)dv);
     double *tmp2 = (double *)malloc(sizeof(double) * (size_t)dv);
     double *w = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    double *qrot = (double *)malloc(sizeof(double) * (size_t)dk);
     int status = 0;
 
     for (int bh = head_begin; bh < head_end; ++bh) {
@@ -170,7 +190,10 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
             /* append the routed token, ascending original position */
             if (r) {
                 if (n >= cap) { status = -3; break; }
-                memcpy(Kh + (size_t)n * dk, kA + tok * dk, sizeof(double) * (size_t)dk);
+                if (rope_base > 0.0)
+                    rope_rotate(kA + tok * dk, Kh + (size_t)n * dk, dk, (double)(t0[b] + t), rope_base);
+                else
+                    memcpy(Kh + (size_t)n * dk, kA + tok * dk, sizeof(double) * (size_t)dk);
                 memcpy(Vh + (size_t)n * dv, vA + tok * dv, sizeof(double) * (size_t)dv);
                 ph[n] = t0[b] + t;
                 n += 1;
@@ -182,6 +205,10 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
             }
             /* softmax attention over the cached (routed) keys, all at positions <= t */
             const double *qat = qA + tok * dk;
+            if (rope_base > 0.0) {
+                rope_rotate(qat, qrot, dk, (double)(t0[b] + t), rope_base);
+                qat = qrot;
+            }
             for (int j = 0; j < dv; ++j) okv[j] = 0.0;
             if (n > 0) {
                 double m = -INFINITY;
@@ -218,6 +245,6 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
         count[bh] = n;
         if (status) break;
     }
-    free(p); free(orn); free(okv); free(tmp1); free(tmp2); free(w);
+    free(p); free(orn); free(okv); free(tmp1); free(tmp2); free(w); free(qrot);
     return status;
 }
