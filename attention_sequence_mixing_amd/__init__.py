@@ -57,8 +57,8 @@ def _need(name, t, shape, dtype, device):
     return t
 
 
-def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0):
-    return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0)
+def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0):
+    return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0, float(rope_base))
 
 
 class ForwardPlan:
@@ -68,13 +68,14 @@ class ForwardPlan:
     """
 
     def __init__(self, B, T, H, dk, dv, dtype, device, *, cap=None, scale=None,
-                 norm_eps=1e-6, flags=0, t0=0, want_o_rnn=False, want_o_kv=False):
+                 norm_eps=1e-6, flags=0, t0=0, rope_base=0.0, want_o_rnn=False, want_o_kv=False):
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.cap = T if cap is None else cap
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
-        self.dims = make_dims(B, T, H, dk, dv, self.io, self.scale, norm_eps, self.cap, flags, t0)
+        self.dims = make_dims(B, T, H, dk, dv, self.io, self.scale, norm_eps, self.cap, flags, t0,
+                              rope_base)
         self.shape = (B, T, H, dk, dv)
         L = _lib.lib()
         ws_bytes = L.ham_forward_workspace_size(ctypes.byref(self.dims))
@@ -130,7 +131,7 @@ class ForwardPlan:
 
 def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
-                t0=0, force_recurrent=False, router_scores=None, want_o_rnn=False,
+                t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, want_o_rnn=False,
                 want_o_kv=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
 
@@ -138,7 +139,8 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
     is then extended in place and S0 should be that call's state.  router_scores:
     None, or [B,T,H] float32 scores of a learned router that replace the RNN's
     prediction error as the routing score (tau then in the router's units).
-    Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
+    rope_base: 0, or the RoPE base for the attention-path query and key (the cache
+    then holds rotated keys).  Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
     asked); e is the routing score used.
     """
     B, T, H, dk = q.shape
@@ -148,8 +150,8 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
     if cache is not None:
         cap = cache["Kc"].shape[2]
     plan = ForwardPlan(B, T, H, dk, dv, q.dtype, q.device, cap=cap, scale=scale,
-                       norm_eps=norm_eps, flags=flags, t0=t0, want_o_rnn=want_o_rnn,
-                       want_o_kv=want_o_kv)
+                       norm_eps=norm_eps, flags=flags, t0=t0, rope_base=rope_base,
+                       want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     if cache is not None:
         plan.Kc = _need("Kc", cache["Kc"], (B, H, plan.cap, dk), q.dtype, q.device)
         plan.Vc = _need("Vc", cache["Vc"], (B, H, plan.cap, dv), q.dtype, q.device)
@@ -164,12 +166,12 @@ class DecodePlan:
     """Scratch and outputs for repeated ham_decode_step calls on one cache."""
 
     def __init__(self, B, H, dk, dv, cap, dtype, device, *, scale=None, norm_eps=1e-6,
-                 want_o_rnn=False, want_o_kv=False):
+                 rope_base=0.0, want_o_rnn=False, want_o_kv=False):
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
-        self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap)
+        self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap, rope_base=rope_base)
         self.shape = (B, H, dk, dv, cap)
         L = _lib.lib()
         ws_bytes = L.ham_decode_workspace_size(ctypes.byref(self.dims))
@@ -218,14 +220,15 @@ class DecodePlan:
 
 def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_eps=1e-6,
                     q_attn=None, k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None,
-                    want_o_rnn=False, want_o_kv=False, stream=None):
+                    rope_base=0.0, want_o_rnn=False, want_o_kv=False, stream=None):
     """One decode step: q, k, v [B,H,d]; S and cache (dict Kc, Vc, pos, count) are
-    updated in place; t_abs [B] int32 positions.  Returns dict(o, e, routed, status, ...)."""
+    updated in place; t_abs [B] int32 positions (also the RoPE positions when
+    rope_base > 0).  Returns dict(o, e, routed, status, ...)."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     cap = cache["Kc"].shape[2]
     plan = DecodePlan(B, H, dk, dv, cap, q.dtype, q.device, scale=scale, norm_eps=norm_eps,
-                      want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
+                      rope_base=rope_base, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     plan(q, k, v, beta, g, tau, S, cache["Kc"], cache["Vc"], cache["pos"], cache["count"], t_abs,
          q_attn=q_attn, k_attn=k_attn, v_attn=v_attn, gate_rnn=gate_rnn, gate_kv=gate_kv,
          stream=stream)

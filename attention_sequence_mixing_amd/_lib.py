@@ -26,7 +26,8 @@ class HamDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("io_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
-                ("cap", ctypes.c_int), ("flags", ctypes.c_int), ("t0", ctypes.c_int)]
+                ("cap", ctypes.c_int), ("flags", ctypes.c_int), ("t0", ctypes.c_int),
+                ("rope_base", ctypes.c_float)]
 
 
 class HamError(RuntimeError):

@@ -48,6 +48,8 @@ int check_dims(const ham_dims* d, bool need_T) {
   if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return fail(HAM_EINVAL, "scale must be finite and > 0");
   if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(HAM_EINVAL, "norm_eps must be finite and >= 0");
   if (d->t0 < 0) return fail(HAM_EINVAL, "t0 must be >= 0");
+  if (!std::isfinite(d->rope_base) || d->rope_base < 0.f)
+    return fail(HAM_EINVAL, "rope_base must be 0 (none) or a finite positive base");
   const double elems = (double)d->B * (need_T ? d->T : 1) * d->H * (d->dk > d->dv ? d->dk : d->dv);
   if (elems > 9.0e15) return fail(HAM_EINVAL, "problem too large");
   return HAM_OK;
@@ -65,7 +67,7 @@ int check_dims(const ham_dims* d, bool need_T) {
 
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
 struct FwdLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, prep, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, rope, prep, total;
 };
 
 FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
@@ -81,6 +83,7 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.count_in = off;    off += up256(BH * sizeof(int32_t));
   L.ntok = off;        off += up256(BTH * sizeof(int32_t));
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
+  L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (d->dk / 2) * sizeof(float2)) : 0;
   L.prep = off;
   if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += BH * nchunk * ham::kPrepRecordBytes;
   L.total = off;
@@ -227,13 +230,17 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
 
+  // rotary table of the new tokens' positions (read by the key and query rotations)
+  float2* rope = d->rope_base > 0.f ? at<float2>(ws, L.rope) : nullptr;
+  if (rope) HAM_HIP(ham::launch_rope_table(rope, d->t0, d->T, d->dk, (double)d->rope_base, s));
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
-                      Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap};
+                      Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap,
+                      rope, 0.0};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
 
   ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
-                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap};
+                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope};
   HAM_HIP(ham::launch_attention(d->io_dtype, d->dk, d->dv, aa, s));
   tm.mark();
   return HAM_OK;
@@ -279,11 +286,12 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
-                      Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap};
+                      Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap,
+                      nullptr, (double)d->rope_base};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
   ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
-                         ham::kDecodeSeg, L.nseg};
+                         ham::kDecodeSeg, L.nseg, t_abs, (double)d->rope_base};
   HAM_HIP(ham::launch_decode_attn(d->io_dtype, d->dk, d->dv, da, s));
   tm.mark();
   ham::DecodeCombineArgs cb{part, count, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps,

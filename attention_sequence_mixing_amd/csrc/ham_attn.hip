@@ -133,17 +133,39 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // load this lane's query fragment
   QFragBF16<DK> qfb;
   QFragF32<DK> qff;
+  // with a rotary table the query is turned at its position first (pairs of
+  // consecutive elements; the table row of local token t)
+  const float2* rrow = a.rope ? a.rope + (size_t)(tvalid ? t : 0) * (DK / 2) : nullptr;
   if constexpr (kBF16) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
       u16x8 x = (u16x8)(0);
       if (tvalid) x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(qp) + tok * DK + ks * 32 + 8 * g);
+      if (rrow) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
+          rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
+          x[2 * j] = f32_to_bf16(x0);
+          x[2 * j + 1] = f32_to_bf16(x1);
+        }
+      }
       qfb.x[ks] = __builtin_bit_cast(bf16x8, x);
     }
   } else {
+    const float* qf = reinterpret_cast<const float*>(qp) + tok * DK;
 #pragma unroll
-    for (int ks = 0; ks < DK / 4; ++ks)
-      qff.x[ks] = tvalid ? reinterpret_cast<const float*>(qp)[tok * DK + ks * 4 + g] : 0.f;
+    for (int ks = 0; ks < DK / 4; ++ks) {
+      const int d = ks * 4 + g;
+      float x = tvalid ? qf[d] : 0.f;
+      if (rrow && tvalid) {
+        // element d of pair d/2; its partner is d ^ 1
+        const float y = qf[d ^ 1];
+        const float2 cs = rrow[d >> 1];
+        x = (d & 1) ? (y * cs.y + x * cs.x) : (x * cs.x - y * cs.y);
+      }
+      qff.x[ks] = x;
+    }
   }
 
   const float sl2 = a.scale * kLog2e;
@@ -386,9 +408,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     const bool ok = tq[qt] < a.T;
     nq[qt] = ok ? ntok[tq[qt]] : 0;
     const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
+    // with a rotary table the query is turned at its position (consecutive pairs)
+    const float2* rrow = a.rope ? a.rope + (size_t)(ok ? tq[qt] : 0) * (DK / 2) : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g));
+    for (int ks = 0; ks < KSD; ++ks) {
+      u16x8 x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
+      if (rrow) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
+          rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
+          x[2 * j] = f32_to_bf16(x0);
+          x[2 * j + 1] = f32_to_bf16(x1);
+        }
+      }
+      qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
+    }
   }
 
   // Tile loads: 1 KiB instruction i covers bytes [i*1024, i*1024 + 1024) of a stage

@@ -108,6 +108,25 @@ HAM_DEVICE float row16_transpose_sum(const float (&x)[16], int n) {
   return (b0 ? w[1] : w[0]) + dpp_mov<0xB1>(b0 ? w[0] : w[1]);
 }
 
+// ---- rotary position embedding ------------------------------------------------------
+// "Hybrid Associative Memories" §4: RoPE with base 500K on all inputs to
+// self-attention (RoFormer, Su et al.): pair (x_2i, x_2i+1) of a d-dimensional vector
+// at absolute position pos turns by pos * base^(-2i/d).  The angle is formed and
+// reduced to [-pi, pi] in double precision (at positions in the millions a float
+// angle would be off by a good fraction of a radian), then cos and sin are rounded
+// to float.
+HAM_DEVICE float2 rope_cs(double pos, int i, int d, double base) {
+  const double a = pos * exp(-2.0 * (double)i / (double)d * log(base));
+  const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+  return make_float2((float)cos(r), (float)sin(r));
+}
+HAM_DEVICE void rope_pair(float& x0, float& x1, float2 cs) {
+  const float y0 = x0 * cs.x - x1 * cs.y;
+  const float y1 = x0 * cs.y + x1 * cs.x;
+  x0 = y0;
+  x1 = y1;
+}
+
 // ---- XCD-aware workgroup order ----------------------------------------------------
 // The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical ids: neighbouring tiles

@@ -11,6 +11,8 @@
 // token's rank inside the chunk; a chunk's base is the sum of the earlier chunks'
 // routed counts (integer sums, so their order does not matter).  No global atomics:
 // the cache order is the ascending original position on every run.
+#include <algorithm>
+
 #include "ham_common.h"
 #include "ham_internal.h"
 
@@ -145,7 +147,39 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     const size_t tok = ((size_t)b * a.T + s_tok[i]) * a.H + h;
     const size_t row = (size_t)bh * a.cap + slot;
     if (w < KU) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kb + (tok * DK) * IO::kBytes + (size_t)w * 16);
+      uint4 x = *reinterpret_cast<const uint4*>(kb + (tok * DK) * IO::kBytes + (size_t)w * 16);
+      if (a.rope || a.rope_base > 0.0) {
+        // this 16-byte unit holds the pairs starting at element e0 of the key
+        constexpr int EU = 16 / IO::kBytes;
+        const int e0 = w * EU;
+        float f[EU];
+        if constexpr (IO::kBytes == 2) {
+          const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(wd[j] << 16);
+            f[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+          }
+        } else {
+          f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+          f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+        }
+#pragma unroll
+        for (int j = 0; j < EU / 2; ++j) {
+          const int pi = e0 / 2 + j;
+          const float2 cs = a.rope ? a.rope[(size_t)s_tok[i] * (DK / 2) + pi]
+                                   : rope_cs((double)(tpos0 + s_tok[i]), pi, DK, a.rope_base);
+          rope_pair(f[2 * j], f[2 * j + 1], cs);
+        }
+        if constexpr (IO::kBytes == 2) {
+          uint32_t wd[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wd[j] = (uint32_t)f32_to_bf16(f[2 * j]) | ((uint32_t)f32_to_bf16(f[2 * j + 1]) << 16);
+          x = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        } else {
+          x = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+        }
+      }
       *reinterpret_cast<uint4*>(Kb + (row * DK) * IO::kBytes + (size_t)w * 16) = x;
     } else {
       const int wv = w - KU;
@@ -325,6 +359,23 @@ hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, f
     hipLaunchKernelGGL(select_tau_kernel<true>, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
   else
     hipLaunchKernelGGL(select_tau_kernel<false>, dim3(H), dim3(1024), 0, s, e, B, T, H, k, tau);
+  return hipGetLastError();
+}
+
+// (cos, sin) of the rotary angles of positions t0 .. t0+T-1, pair-fastest ([T][dk/2]).
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* table, int t0, int T, int dk, double base) {
+  const int half = dk / 2;
+  const long long n = (long long)T * half;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int t = (int)(i / half), p = (int)(i % half);
+    table[i] = rope_cs((double)t0 + t, p, dk, base);
+  }
+}
+
+hipError_t launch_rope_table(float2* table, int t0, int T, int dk, double base, hipStream_t s) {
+  const long long n = (long long)T * (dk / 2);
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, table, t0, T, dk, base);
   return hipGetLastError();
 }
 

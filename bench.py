@@ -196,9 +196,42 @@ def bench_forward(args, dev):
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
     router = bench_router(args, dev, w, t)
+    rope = bench_rope(args, dev, w, t, tau)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router)
+                router=router, rope=rope)
+
+
+def bench_rope(args, dev, w, t, tau, base=500000.0):
+    """The same layer with rotary position embedding (base 500K) on the attention
+    query and key: the fit-error routing and threshold are unchanged."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale,
+                           rope_base=base)
+
+    def step():
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    lib.ham_profile_start(args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = collect_stages(lib, args.steps)
+    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
+    log(f"[bench] rope {base:g}: {ms:.3f} ms/step, stages {dict(zip(names, [round(x, 4) for x in stages]))}")
+    return dict(workload=f"{w.name}_rope{int(base)}", ms_per_step=round(ms, 4),
+                tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
 
 
 def bench_router(args, dev, w, t):
@@ -395,6 +428,7 @@ def main():
         "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
                    for s in res["stages"]],
         "learned_router": res["router"],
+        "rope": res["rope"],
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
             "us_per_step": round(dec["us_per_step"], 2), "tokens_per_s": round(dec["tokens_per_s"], 1),

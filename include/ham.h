@@ -78,6 +78,13 @@ typedef struct {
     int cap;          /* KV-cache capacity per (b,h), in tokens, 1..4194304       */
     int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES  */
     int t0;           /* absolute position of token 0 (recorded in pos)          */
+    float rope_base;  /* 0, or the base of a rotary position embedding (RoPE)
+                         applied to the attention-path query and key at their
+                         absolute positions: [HAM] §4 uses base 500000 for all
+                         inputs to self-attention.  Pairs of consecutive elements
+                         (x_2i, x_2i+1) turn by pos * rope_base^(-2i/dk) (RoFormer);
+                         the cache then holds rotated keys.  The RNN path is not
+                         rotated.                                                 */
 } ham_dims;
 
 /* Library version (major*10000 + minor*100 + patch). */

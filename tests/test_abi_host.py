@@ -48,6 +48,20 @@ def test_workspace_sizes():
         assert L.ham_forward_workspace_size(ctypes.byref(bad)) == 0
 
 
+def test_rope_workspace_and_base_checks():
+    """A rotary base adds one table of T x dk/2 (cos, sin) float pairs to the forward
+    workspace; a negative, infinite or NaN base is rejected."""
+    L = _lib.lib()
+    ws0 = L.ham_forward_workspace_size(ctypes.byref(dims()))
+    ws1 = L.ham_forward_workspace_size(ctypes.byref(dims(rope_base=500000.0)))
+    assert ws1 - ws0 >= 300 * 64 * 8
+    assert L.ham_decode_workspace_size(ctypes.byref(dims(rope_base=10000.0))) > 0
+    for bad in (-1.0, float("nan"), float("inf")):
+        for fn in (L.ham_forward_workspace_size, L.ham_decode_workspace_size):
+            assert fn(ctypes.byref(dims(rope_base=bad))) == 0
+            assert "rope_base" in _msg()
+
+
 def _fwd(d, ptrs=None, ws_bytes=1 << 40):
     P = ctypes.c_void_p
     fake = P(1 << 20)   # an aligned non-NULL host value; never dereferenced by these checks
