@@ -91,7 +91,7 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
 }
 
 struct DecLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, rope, total;
   int nseg;
 };
 
@@ -107,6 +107,7 @@ DecLayout dec_layout(const ham_dims* d) {
   L.chunk_count = off; off += up256(BH * sizeof(int32_t));
   L.count_in = off;    off += up256(BH * sizeof(int32_t));
   L.part = off;        off += up256(BH * (size_t)L.nseg * (d->dv + 2) * sizeof(float));
+  L.rope = off;        off += d->rope_base > 0.f ? up256((size_t)d->B * (d->dk / 2) * sizeof(float2)) : 0;
   L.total = off;
   return L;
 }
@@ -232,10 +233,10 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
 
   // rotary table of the new tokens' positions (read by the key and query rotations)
   float2* rope = d->rope_base > 0.f ? at<float2>(ws, L.rope) : nullptr;
-  if (rope) HAM_HIP(ham::launch_rope_table(rope, d->t0, d->T, d->dk, (double)d->rope_base, s));
+  if (rope) HAM_HIP(ham::launch_rope_table(rope, nullptr, d->t0, d->T, d->dk, (double)d->rope_base, s));
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
                       Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap,
-                      rope, 0.0};
+                      rope};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
 
@@ -285,13 +286,16 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
                     chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
+  // rotary table of the new tokens' positions t_abs[b] (key and query rotations)
+  float2* rope = d->rope_base > 0.f ? at<float2>(ws, L.rope) : nullptr;
+  if (rope) HAM_HIP(ham::launch_rope_table(rope, t_abs, 0, d->B, d->dk, (double)d->rope_base, s));
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
                       Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap,
-                      nullptr, (double)d->rope_base};
+                      rope};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
   ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
-                         ham::kDecodeSeg, L.nseg, t_abs, (double)d->rope_base};
+                         ham::kDecodeSeg, L.nseg, rope};
   HAM_HIP(ham::launch_decode_attn(d->io_dtype, d->dk, d->dv, da, s));
   tm.mark();
   ham::DecodeCombineArgs cb{part, count, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps,

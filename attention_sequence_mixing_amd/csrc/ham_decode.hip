@@ -74,11 +74,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   float qv[KE];
 #pragma unroll
   for (int i = 0; i < KE; i += 4) IO::load4(qp, i, qv + i);
-  if (a.rope_base > 0.0) {
+  if (a.rope) {
     // the new token's query turned at its absolute position (consecutive pairs)
-    const double pos = (double)a.t_abs[b];
+    const float2* rrow = a.rope + (size_t)b * (DK / 2) + sub * (KE / 2);
 #pragma unroll
-    for (int j = 0; j < KE / 2; ++j) rope_pair(qv[2 * j], qv[2 * j + 1], rope_cs(pos, sub * KE / 2 + j, DK, a.rope_base));
+    for (int j = 0; j < KE / 2; ++j) rope_pair(qv[2 * j], qv[2 * j + 1], rrow[j]);
   }
   const float sl2 = a.scale * kLog2eD;
 #pragma unroll

@@ -58,8 +58,8 @@ struct CompactArgs {
   const int32_t* t_abs; // [B] or null
   int t0;
   int B, T, H, cap;
-  const float2* rope;   // [T][dk/2] (cos, sin) of the new tokens' key rotations, or null
-  double rope_base;     // > 0 without a table: angles formed here at t_abs (decode)
+  const float2* rope;   // (cos, sin) of the key rotations, or null: [T][dk/2] rows of the
+                        // new tokens (forward), or [B][dk/2] rows at t_abs[b] (decode)
 };
 
 struct StatsArgs {
@@ -97,8 +97,7 @@ struct DecodeAttnArgs {
   float* part;          // [B*H][nseg][dv + 2]  (acc..., m, l)
   float scale;
   int B, H, cap, seg, nseg;
-  const int32_t* t_abs; // [B] positions of the new tokens (query rotation)
-  double rope_base;     // 0: no rotary embedding
+  const float2* rope;   // [B][dk/2] (cos, sin) of the query rotation at t_abs[b], or null
 };
 
 struct DecodeCombineArgs {
@@ -129,7 +128,8 @@ hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, f
 hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hipStream_t s);
-hipError_t launch_rope_table(float2* table, int t0, int T, int dk, double base, hipStream_t s);
+hipError_t launch_rope_table(float2* table, const int32_t* t_abs, int t0, int rows, int dk,
+                             double base, hipStream_t s);
 
 constexpr int kChunk = 64;         // tokens per routing / compaction chunk
 constexpr int kDecodeSeg = 1024;   // keys per split-K segment in decode

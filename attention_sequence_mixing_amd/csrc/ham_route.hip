@@ -100,8 +100,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 
 // grid (nchunk, H, B), 256 threads.  Writes the chunk's routed rows to the cache
 // at count_in + base + rank, their positions, the per-token visible-key counts,
-// and (last chunk) the new count.
-template <class IO, int DK, int DV>
+// and (last chunk) the new count.  ROPE: the key rows are turned by the rotary
+// table on the way (a.rope; row of local token t in a forward, row b in decode).
+template <class IO, int DK, int DV, bool ROPE>
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   using E = typename IO::elem;
   constexpr int KU = DK * IO::kBytes / 16;    // 16-byte units per key row
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     const size_t row = (size_t)bh * a.cap + slot;
     if (w < KU) {
       uint4 x = *reinterpret_cast<const uint4*>(kb + (tok * DK) * IO::kBytes + (size_t)w * 16);
-      if (a.rope || a.rope_base > 0.0) {
+      if constexpr (ROPE) {
         // this 16-byte unit holds the pairs starting at element e0 of the key
         constexpr int EU = 16 / IO::kBytes;
         const int e0 = w * EU;
@@ -167,8 +168,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
 #pragma unroll
         for (int j = 0; j < EU / 2; ++j) {
           const int pi = e0 / 2 + j;
-          const float2 cs = a.rope ? a.rope[(size_t)s_tok[i] * (DK / 2) + pi]
-                                   : rope_cs((double)(tpos0 + s_tok[i]), pi, DK, a.rope_base);
+          const float2 cs = a.rope[(size_t)(a.t_abs ? b : s_tok[i]) * (DK / 2) + pi];
           rope_pair(f[2 * j], f[2 * j + 1], cs);
         }
         if constexpr (IO::kBytes == 2) {
@@ -200,7 +200,10 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
 template <class IO, int DK, int DV>
 static hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL((compact_kernel<IO, DK, DV>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
+  if (a.rope)
+    hipLaunchKernelGGL((compact_kernel<IO, DK, DV, true>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((compact_kernel<IO, DK, DV, false>), dim3(nchunk, a.H, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -362,20 +365,24 @@ hipError_t launch_select_tau(const float* e, int B, int T, int H, long long k, f
   return hipGetLastError();
 }
 
-// (cos, sin) of the rotary angles of positions t0 .. t0+T-1, pair-fastest ([T][dk/2]).
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* table, int t0, int T, int dk, double base) {
+// (cos, sin) of the rotary angles, pair-fastest ([rows][dk/2]); row r is position
+// t_abs[r] when t_abs is given, else t0 + r.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* table, const int32_t* t_abs, int t0,
+                                                         int rows, int dk, double base) {
   const int half = dk / 2;
-  const long long n = (long long)T * half;
+  const long long n = (long long)rows * half;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    const int t = (int)(i / half), p = (int)(i % half);
-    table[i] = rope_cs((double)t0 + t, p, dk, base);
+    const int r = (int)(i / half), p = (int)(i % half);
+    const double pos = t_abs ? (double)t_abs[r] : (double)t0 + r;
+    table[i] = rope_cs(pos, p, dk, base);
   }
 }
 
-hipError_t launch_rope_table(float2* table, int t0, int T, int dk, double base, hipStream_t s) {
-  const long long n = (long long)T * (dk / 2);
+hipError_t launch_rope_table(float2* table, const int32_t* t_abs, int t0, int rows, int dk,
+                             double base, hipStream_t s) {
+  const long long n = (long long)rows * (dk / 2);
   const int blocks = (int)std::min<long long>((n + 255) / 256, 65536);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, table, t0, T, dk, base);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, table, t_abs, t0, rows, dk, base);
   return hipGetLastError();
 }
 

@@ -370,8 +370,10 @@ def cpu_baseline(res, nbatch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU clock takes some tens of milliseconds of load to settle: fewer than ~20
+    # warmup steps of the layer leave the first timed steps at a lower clock
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-prefix", type=int, default=0)
     ap.add_argument("--cpu-batch", type=int, default=8,

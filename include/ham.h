@@ -84,7 +84,9 @@ typedef struct {
                          inputs to self-attention.  Pairs of consecutive elements
                          (x_2i, x_2i+1) turn by pos * rope_base^(-2i/dk) (RoFormer);
                          the cache then holds rotated keys.  The RNN path is not
-                         rotated.                                                 */
+                         rotated.  Angles are formed and reduced in double
+                         precision; their (cos, sin) pairs are kept as floats in
+                         a workspace table and the rotation runs in float.      */
 } ham_dims;
 
 /* Library version (major*10000 + minor*100 + patch). */
