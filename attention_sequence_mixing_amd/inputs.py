@@ -155,6 +155,34 @@ def make_gates(B, T, H, seed):
     return gr, gk
 
 
+def doc_start_from_lengths(lengths, t0=0):
+    """[T] int32 absolute start position of each token's document for one packed
+    sequence made of documents of the given lengths, beginning at position t0."""
+    out, s = [], t0
+    for n in lengths:
+        out.append(np.full(int(n), s, np.int32))
+        s += int(n)
+    return np.concatenate(out) if out else np.zeros(0, np.int32)
+
+
+def make_doc_lengths(T, mean_len, seed):
+    """Document lengths of one packed sequence of T tokens: geometric lengths with
+    the given mean (at least 1), the last document cut to fill T exactly."""
+    rng = np.random.default_rng(seed + 2000)
+    lengths, left = [], T
+    while left > 0:
+        n = min(left, int(rng.geometric(1.0 / max(mean_len, 1.0))))
+        lengths.append(n)
+        left -= n
+    return lengths
+
+
+def make_doc_start(B, T, mean_len, seed, t0=0):
+    """[B,T] int32 document starts of B packed sequences (geometric lengths)."""
+    return np.stack([doc_start_from_lengths(make_doc_lengths(T, mean_len, seed + 7 * b), t0)
+                     for b in range(B)])
+
+
 def make_inputs_torch(B, T, H, dk, dv=None, *, dtype="bf16", seed=0, device="cuda"):
     """The same recipe drawn on the device with torch's generator (for workloads too
     large to draw on the host, e.g. a 32K-token prefix of 32 sequences).  Deterministic

@@ -51,7 +51,7 @@ def _load():
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
             [ctypes.c_int] * 5 + [ctypes.c_double] * 3 + [P] * 3 + [P] * 3 + [P] * 3
-            + [P] * 2 + [P] * 4 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
+            + [P] * 2 + [P] * 5 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
         return lib
@@ -71,7 +71,7 @@ def default_threads() -> int:
 
 def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=None, k_attn=None,
             v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, router_score=None,
-            S0=None, cache=None, cap=None, t0=0, emit=None, threads=None):
+            S0=None, cache=None, cap=None, t0=0, doc_start=None, emit=None, threads=None):
     """Run the oracle over all heads.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
@@ -79,6 +79,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
     absolute position of token 0.  rope_base: 0, or the RoPE base applied to the
     attention-path query and key at their positions (the cache holds rotated keys).
+    doc_start: None or [B,T] int, the absolute position where each token's document
+    begins in a packed batch (attention only to cached keys at positions >= it).
     router_score: None or [B,T,H] float32 scores of a
     learned router that replace the fit-error score (the decision is score > tau).
     emit: None or [B,T,H] bool; False skips the
@@ -98,6 +100,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
         np.asarray(router_score, dtype=np.float32).reshape(B, T, H))
     em = None if emit is None else np.ascontiguousarray(np.asarray(emit).astype(np.int8))
     t0a = np.ascontiguousarray(np.broadcast_to(np.asarray(t0, dtype=np.int64), (B,)))
+    dc = None if doc_start is None else np.ascontiguousarray(
+        np.asarray(doc_start, dtype=np.int64).reshape(B, T))
     S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
     S = np.ascontiguousarray(S)
     if cache is None:
@@ -129,7 +133,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
             B, T, H, dk, dv, float(scale), float(eps), float(rope_base),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
             _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(rs), _ptr(em),
-            _ptr(t0a),
+            _ptr(t0a), _ptr(dc),
             _ptr(S), cap, _ptr(Kc), _ptr(Vc), _ptr(pos), _ptr(count),
             _ptr(e), _ptr(routed), _ptr(o_rnn), _ptr(o_kv), _ptr(o),
             bounds[i], bounds[i + 1])

@@ -37,9 +37,15 @@
  *    all inputs to self-attention", citing Su et al.'s RoFormer: consecutive
  *    pairs (x_2i, x_2i+1) turned by the angle position * b^(-2i/d_k))
  *   o_kv_t  = softmax over the cached keys, scale * q^a_t . k_c, of the cached
- *             values; 0 when the cache is empty           ([HAM] §2 KV-memory
+ *             values; 0 when no cached key is visible     ([HAM] §2 KV-memory
  *             equation; causality by original position, App. A.1 "FlexAttention
  *             and Block Masks")
+ *             Same-document masking (same passage): in a packed sequence each
+ *             document is a contiguous range of positions, and doc_start[b,t] is
+ *             the position where token t's document begins.  A cached key is
+ *             visible to the query only when its position is >= doc_start (it
+ *             belongs to the same document; documents may span calls).  Only the
+ *             attention is masked: the RNN and the routing read every token.
  *   o_t     = gr_t * rms(o_rnn_t) + gk_t * rms(o_kv_t),  rms(x) = x / sqrt(mean(x^2)+eps)
  *             ([HAM] §2 headwise norm and gated sum; App. A.1 headwise gating)
  *
@@ -121,7 +127,7 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                        const double *beta, const double *g, const float *tau,
                        const double *gate_rnn, const double *gate_kv,
                        const int8_t *mask_override, const float *router_score,
-                       const int8_t *emit, const int64_t *t0,
+                       const int8_t *emit, const int64_t *t0, const int64_t *doc_start,
                        double *S, int cap, double *Kc, double *Vc,
                        int64_t *pos, int64_t *count,
                        double *e, int8_t *routed,
@@ -210,24 +216,31 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                 qat = qrot;
             }
             for (int j = 0; j < dv; ++j) okv[j] = 0.0;
-            if (n > 0) {
+            {
+                /* first position of this token's document (none: the whole cache) */
+                const int64_t ds = doc_start ? doc_start[(size_t)b * T + t] : INT64_MIN;
                 double m = -INFINITY;
+                int64_t nvis = 0;
                 for (int64_t c = 0; c < n; ++c) {
+                    if (ph[c] < ds) { w[c] = -INFINITY; continue; }   /* another document */
                     double s = 0.0;
                     for (int i = 0; i < dk; ++i)
                         s += qat[i] * Kh[(size_t)c * dk + i];
                     w[c] = scale * s;
                     if (w[c] > m) m = w[c];
+                    nvis += 1;
                 }
-                double den = 0.0;
-                for (int64_t c = 0; c < n; ++c) {
-                    w[c] = exp(w[c] - m);
-                    den += w[c];
-                }
-                for (int64_t c = 0; c < n; ++c) {
-                    const double wc = w[c] / den;
-                    for (int j = 0; j < dv; ++j)
-                        okv[j] += wc * Vh[(size_t)c * dv + j];
+                if (nvis > 0) {
+                    double den = 0.0;
+                    for (int64_t c = 0; c < n; ++c) {
+                        w[c] = (w[c] == -INFINITY) ? 0.0 : exp(w[c] - m);
+                        den += w[c];
+                    }
+                    for (int64_t c = 0; c < n; ++c) {
+                        const double wc = w[c] / den;
+                        for (int j = 0; j < dv; ++j)
+                            okv[j] += wc * Vh[(size_t)c * dv + j];
+                    }
                 }
             }
 
