@@ -94,10 +94,13 @@ class ForwardPlan:
         self.count = torch.zeros((B, H), dtype=torch.int32, device=device)
 
     def __call__(self, q, k, v, beta, g, tau, *, q_attn=None, k_attn=None, v_attn=None,
-                 gate_rnn=None, gate_kv=None, S0=None, router_scores=None, stream=None):
+                 gate_rnn=None, gate_kv=None, S0=None, router_scores=None, doc_start=None,
+                 stream=None):
         """router_scores: [B,T,H] float32 scores of a learned router, which then replace
         the RNN's prediction error as the routing score (needs the plan to have been
-        made with flags including HAM_EXTERNAL_SCORES)."""
+        made with flags including HAM_EXTERNAL_SCORES).  doc_start: [B,T] int32
+        absolute start position of each token's document in a packed batch (the
+        attention then sees only keys of the same document), or None."""
         B, T, H, dk, dv = self.shape
         dev, dt = self.device, self.dtype
         for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
@@ -108,6 +111,7 @@ class ForwardPlan:
             _need(n, t, (B, T, H), torch.float32, dev)
         _need("tau", tau, (H,), torch.float32, dev)
         _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
+        _need("doc_start", doc_start, (B, T), torch.int32, dev)
         if q is None or k is None or v is None or beta is None or g is None or tau is None:
             raise ValueError("q, k, v, beta, g and tau are required")
         ext = bool(self.dims.flags & HAM_EXTERNAL_SCORES)
@@ -117,7 +121,7 @@ class ForwardPlan:
             self.e = _need("router_scores", router_scores, (B, T, H), torch.float32, dev)
         rc = _lib.lib().ham_forward(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
-            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S0), _vp(self.S),
+            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start), _vp(S0), _vp(self.S),
             _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv), _vp(self.e), _vp(self.routed),
             _vp(self.Kc), _vp(self.Vc), _vp(self.pos), _vp(self.count),
             _vp(self.ws), self.ws.numel(), _stream(stream))
@@ -131,8 +135,8 @@ class ForwardPlan:
 
 def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
-                t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, want_o_rnn=False,
-                want_o_kv=False, stream=None):
+                t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, doc_start=None,
+                want_o_rnn=False, want_o_kv=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
 
     cache: None, or dict(Kc, Vc, pos, count) of an earlier call to continue; it
@@ -140,7 +144,8 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
     None, or [B,T,H] float32 scores of a learned router that replace the RNN's
     prediction error as the routing score (tau then in the router's units).
     rope_base: 0, or the RoPE base for the attention-path query and key (the cache
-    then holds rotated keys).  Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
+    then holds rotated keys).  doc_start: None, or [B,T] int32 absolute start
+    positions of the tokens' documents (same-document masking of a packed batch).  Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
     asked); e is the routing score used.
     """
     B, T, H, dk = q.shape
@@ -158,7 +163,8 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
         plan.pos = _need("pos", cache["pos"], (B, H, plan.cap), torch.int32, q.device)
         plan.count = _need("count", cache["count"], (B, H), torch.int32, q.device)
     plan(q, k, v, beta, g, tau, q_attn=q_attn, k_attn=k_attn, v_attn=v_attn,
-         gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, router_scores=router_scores, stream=stream)
+         gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, router_scores=router_scores,
+         doc_start=doc_start, stream=stream)
     return plan.result()
 
 
@@ -187,9 +193,10 @@ class DecodePlan:
 
     def __call__(self, q, k, v, beta, g, tau, S, Kc, Vc, pos, count, t_abs, *, q_attn=None,
                  k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, router_scores=None,
-                 stream=None):
+                 doc_start=None, stream=None):
         """router_scores: None, or [B,H] float32 learned-router scores of the new tokens,
-        which then replace the RNN's prediction error as the routing score."""
+        which then replace the RNN's prediction error as the routing score.
+        doc_start: None, or [B] int32 absolute start of each new token's document."""
         B, H, dk, dv, cap = self.shape
         dev, dt = self.device, self.dtype
         for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
@@ -206,11 +213,13 @@ class DecodePlan:
         _need("count", count, (B, H), torch.int32, dev)
         _need("t_abs", t_abs, (B,), torch.int32, dev)
         _need("router_scores", router_scores, (B, H), torch.float32, dev)
+        _need("doc_start", doc_start, (B,), torch.int32, dev)
         self.dims.flags = HAM_EXTERNAL_SCORES if router_scores is not None else 0
         e = router_scores if router_scores is not None else self.e
         rc = _lib.lib().ham_decode_step(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
-            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(S), _vp(Kc), _vp(Vc),
+            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start), _vp(S),
+            _vp(Kc), _vp(Vc),
             _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
             _vp(e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
             _stream(stream))
@@ -220,7 +229,7 @@ class DecodePlan:
 
 def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_eps=1e-6,
                     q_attn=None, k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None,
-                    rope_base=0.0, want_o_rnn=False, want_o_kv=False, stream=None):
+                    rope_base=0.0, doc_start=None, want_o_rnn=False, want_o_kv=False, stream=None):
     """One decode step: q, k, v [B,H,d]; S and cache (dict Kc, Vc, pos, count) are
     updated in place; t_abs [B] int32 positions (also the RoPE positions when
     rope_base > 0).  Returns dict(o, e, routed, status, ...)."""
@@ -231,7 +240,7 @@ def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_
                       rope_base=rope_base, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     plan(q, k, v, beta, g, tau, S, cache["Kc"], cache["Vc"], cache["pos"], cache["count"], t_abs,
          q_attn=q_attn, k_attn=k_attn, v_attn=v_attn, gate_rnn=gate_rnn, gate_kv=gate_kv,
-         stream=stream)
+         doc_start=doc_start, stream=stream)
     return dict(o=plan.o, o_rnn=plan.o_rnn, o_kv=plan.o_kv, e=plan.e, routed=plan.routed,
                 status=plan.status)
 

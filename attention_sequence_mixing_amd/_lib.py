@@ -61,9 +61,9 @@ def lib():
         f.restype = Z
         f.argtypes = [D]
     L.ham_forward.restype = I
-    L.ham_forward.argtypes = [D] + [P] * 23 + [Z, P]
+    L.ham_forward.argtypes = [D] + [P] * 24 + [Z, P]
     L.ham_decode_step.restype = I
-    L.ham_decode_step.argtypes = [D] + [P] * 24 + [Z, P]
+    L.ham_decode_step.argtypes = [D] + [P] * 25 + [Z, P]
     L.ham_route_stats.restype = I
     L.ham_route_stats.argtypes = [D] + [P] * 11 + [ctypes.c_float, P, P, Z, P]
     L.ham_select_tau.restype = I

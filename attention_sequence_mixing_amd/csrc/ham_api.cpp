@@ -67,7 +67,7 @@ int check_dims(const ham_dims* d, bool need_T) {
 
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
 struct FwdLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, state, rope, prep, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, lo, state, rope, prep, total;
 };
 
 FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
@@ -82,6 +82,7 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.chunk_count = off; off += up256(BH * nchunk * sizeof(int32_t));
   L.count_in = off;    off += up256(BH * sizeof(int32_t));
   L.ntok = off;        off += up256(BTH * sizeof(int32_t));
+  L.lo = off;          off += with_state ? 0 : up256(BTH * sizeof(int32_t));
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
   L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (d->dk / 2) * sizeof(float2)) : 0;
   L.prep = off;
@@ -91,7 +92,7 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
 }
 
 struct DecLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, rope, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, rope, lo, total;
   int nseg;
 };
 
@@ -108,6 +109,7 @@ DecLayout dec_layout(const ham_dims* d) {
   L.count_in = off;    off += up256(BH * sizeof(int32_t));
   L.part = off;        off += up256(BH * (size_t)L.nseg * (d->dv + 2) * sizeof(float));
   L.rope = off;        off += d->rope_base > 0.f ? up256((size_t)d->B * (d->dk / 2) * sizeof(float2)) : 0;
+  L.lo = off;          off += up256(BH * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -167,7 +169,7 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
 
 extern "C" {
 
-int ham_version(void) { return 10000; }
+int ham_version(void) { return 10100; }
 
 const char* ham_last_error(void) { return g_err.c_str(); }
 
@@ -189,7 +191,7 @@ size_t ham_decode_workspace_size(const ham_dims* d) {
 int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
                 const void* q_attn, const void* k_attn, const void* v_attn,
                 const float* beta, const float* g, const float* tau,
-                const float* gate_rnn, const float* gate_kv,
+                const float* gate_rnn, const float* gate_kv, const int32_t* doc_start,
                 const float* S0, float* S_out, void* o, void* o_rnn, void* o_kv,
                 float* e, uint8_t* routed, void* Kc, void* Vc, int32_t* pos, int32_t* count,
                 void* ws, size_t ws_bytes, void* stream) {
@@ -240,8 +242,14 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
 
+  // same-document masking: each query's first visible cache entry
+  int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
+  if (lo) {
+    ham::DocLoArgs da{doc_start, ntok, count_in, nullptr, pos, lo, d->t0, d->B, d->T, d->H, d->cap};
+    HAM_HIP(ham::launch_doc_lo(da, s));
+  }
   ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
-                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope};
+                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope, lo};
   HAM_HIP(ham::launch_attention(d->io_dtype, d->dk, d->dv, aa, s));
   tm.mark();
   return HAM_OK;
@@ -250,7 +258,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
 int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void* v,
                     const void* q_attn, const void* k_attn, const void* v_attn,
                     const float* beta, const float* g, const float* tau,
-                    const float* gate_rnn, const float* gate_kv,
+                    const float* gate_rnn, const float* gate_kv, const int32_t* doc_start,
                     float* S, void* Kc, void* Vc, int32_t* pos, int32_t* count,
                     const int32_t* t_abs, void* o, void* o_rnn, void* o_kv,
                     float* e, uint8_t* routed, int32_t* status,
@@ -294,8 +302,13 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
                       rope};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
+  int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
+  if (lo) {
+    ham::DocLoArgs dl{doc_start, nullptr, nullptr, count, pos, lo, 0, d->B, 1, d->H, d->cap};
+    HAM_HIP(ham::launch_doc_lo(dl, s));
+  }
   ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
-                         ham::kDecodeSeg, L.nseg, rope};
+                         ham::kDecodeSeg, L.nseg, rope, lo};
   HAM_HIP(ham::launch_decode_attn(d->io_dtype, d->dk, d->dv, da, s));
   tm.mark();
   ham::DecodeCombineArgs cb{part, count, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps,

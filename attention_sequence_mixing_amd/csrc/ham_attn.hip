@@ -128,6 +128,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int nq = tvalid ? ntok[t] : 0;              // visible keys c < nq
   const int tlast = min(a.T - 1, qb * 64 + 63);
   const int nhi = ntok[tlast];                      // keys any query of the block sees
+  // same-document masking: visible keys are lq <= c < nq; the block starts at the
+  // tile of its smallest lq
+  const int lq = (a.lo && tvalid) ? a.lo[(size_t)bh * a.T + t] : 0;
+  __shared__ int s_lomin[4];
+  int it0 = 0;
+  if (a.lo) {
+    int m = tvalid ? lq : 0x7fffffff;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = min(m, __shfl_xor(m, o, kWave));
+    if (lane == 0) s_lomin[wave] = m;
+    __syncthreads();
+    it0 = min(min(s_lomin[0], s_lomin[1]), min(s_lomin[2], s_lomin[3])) / AttnTile<IO>::BN;
+  }
   const size_t tok = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
 
   // load this lane's query fragment
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4)(0.f);
 
   const int ntiles = (nhi + BN - 1) / BN;
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = it0; it < ntiles; ++it) {
     const int c0 = it * BN;
     __syncthreads();
     stage_kv(sm, Kh, Vh, c0, nhi, tid);
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int cidx = c0 + kt * 16 + 4 * g + i;
-        const float s = (cidx < nq) ? st[kt][i] * sl2 : -INFINITY;
+        const float s = (cidx >= lq && cidx < nq) ? st[kt][i] * sl2 : -INFINITY;
         st[kt][i] = s;
         tmax = fmaxf(tmax, s);
       }
@@ -365,7 +378,12 @@ HAM_DEVICE void buffer_to_lds(const void* base, int range_bytes, int voff, char*
 #endif
 }
 
-template <int DK, int DV, int QT>
+// DOC: same-document masking (a.lo set): query t sees keys lo_t <= c < ntok_t; the
+// block starts at the tile of its smallest lo.  The queries' (lo, ntok) ranges wait
+// in LDS for the tiles that need a mask (registers are at their limit here), and a
+// wave in which a row meets its first visible key after the block's first tile
+// takes the exact path then.
+template <int DK, int DV, int QT, bool DOC>
 __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   constexpr int NWV = 4;                                   // waves per workgroup
   constexpr int BN = 64, NKT = BN / 16, DT = DV / 16, KSD = DK / 32;
@@ -483,8 +501,34 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   }
 
   const int ntiles = (nhi + BN - 1) / BN;
+  int it0 = 0, lmax = 0;                                  // first tile; largest lo
+  __shared__ int2 s_rng[DOC ? BM : 1];                    // (lo, ntok) of the block's queries
+  if constexpr (DOC) {
+    __shared__ int s_lo[2][NWV];
+    int mn = 0x7fffffff, mx = 0;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int l = tq[qt] < a.T ? a.lo[(size_t)bh * a.T + tq[qt]] : 0;
+      s_rng[wave * BMW + 16 * qt + qn] = make_int2(l, nq[qt]);
+      if (tq[qt] < a.T) {
+        mn = min(mn, l);
+        mx = max(mx, l);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      mn = min(mn, __shfl_xor(mn, o, kWave));
+      mx = max(mx, __shfl_xor(mx, o, kWave));
+    }
+    if (lane == 0) { s_lo[0][wave] = mn; s_lo[1][wave] = mx; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) { mn = min(mn, s_lo[0][w]); mx = max(mx, s_lo[1][w]); }
+    it0 = __builtin_amdgcn_readfirstlane(mn / BN);
+    lmax = __builtin_amdgcn_readfirstlane(mx);
+  }
   __builtin_amdgcn_s_waitcnt(0);                          // query fragments are in
-  if (ntiles > 0) issue_tile(0, stage0);
+  if (it0 < ntiles) issue_tile(it0, stage0);
 
   f32x4 st[QT][NKT];
   // S^T = K Q^T for the tile in `stage`
@@ -505,7 +549,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   };
   // keys at or past a query's visible count get -inf
   auto do_mask = [&](int c0) {
-    if ((c0 + BN) > nlo) {
+    if constexpr (DOC) {
+      if ((c0 + BN) > nlo || c0 < lmax) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int2 r = s_rng[wave * BMW + 16 * qt + qn];
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = c0 + kt * 16 + 4 * g + i;
+              if (c < r.x || c >= r.y) st[qt][kt][i] = -INFINITY;
+            }
+        }
+      }
+    } else if ((c0 + BN) > nlo) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -607,7 +665,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     if (it + 1 < ntiles) issue_tile(it + 1, nxt);
     do_scores(cur);
     do_mask(it * BN);
-    bool exact = (it == 0);
+    // the first tile is exact; with document masks, every tile in which a row meets
+    // its first visible key is (the row has no running maximum before it)
+    bool exact = !DOC && it == 0;
     if (!exact) {
       do_probs();
       float ls[QT];
@@ -615,6 +675,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       bool over = false;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) over |= ls[qt] > kLazySum;
+      if constexpr (DOC) {
+        const int c0 = it * BN;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          if (m_run[qt] == -INFINITY) {
+            const int2 r = s_rng[wave * BMW + 16 * qt + qn];
+            over |= r.x < r.y && r.x < c0 + BN && r.y > c0;
+          }
+      }
       if (__any(over)) {
         exact = true;
         do_scores(cur);
@@ -627,7 +696,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     if (exact) do_exact();
     do_pv(cur);
   };
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = it0; it < ntiles; it += 2) {
     step(it, stage0, stage1);
     if (it + 1 < ntiles) step(it + 1, stage1, stage0);
   }
@@ -680,7 +749,10 @@ template <int DK, int DV>
 static hipError_t launch_attn_bf16_v5(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 2, BM = 4 * 16 * QT;
   const int nqb = (a.T + BM - 1) / BM;
-  hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  if (a.lo)
+    hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT, true>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT, false>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

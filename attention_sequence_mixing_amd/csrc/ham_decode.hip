@@ -64,9 +64,16 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.H + h;
   const int n = a.count[bh];
-  const int s0 = seg * a.seg;
-  if (s0 >= n) return;
-  const int s1 = min(n, s0 + a.seg);
+  if (seg * a.seg >= n) return;
+  const int s1 = min(n, seg * a.seg + a.seg);
+  // same-document masking: entries before lo belong to earlier documents
+  const int s0 = a.lo ? max(seg * a.seg, a.lo[bh]) : seg * a.seg;
+  if (s0 >= s1) {                             // nothing visible in this segment
+    float* out = a.part + ((size_t)bh * a.nseg + seg) * (DV + 2);
+    for (int d = threadIdx.x; d < DV; d += 256) out[d] = 0.f;
+    if (threadIdx.x == 0) { out[DV] = -INFINITY; out[DV + 1] = 0.f; }
+    return;
+  }
 
   const E* qp = static_cast<const E*>(a.q) + (size_t)bh * DK + sub * KE;
   const E* Kh = static_cast<const E*>(a.Kc) + (size_t)bh * a.cap * DK + sub * KE;
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeCombineArgs a)
 #pragma unroll 4
   for (int s = 0; s < used; ++s) {
     const float* ps = part + (size_t)s * (DV + 2);
-    const float w = exp2f(ps[DV] - M);
+    const float w = (ps[DV] == -INFINITY) ? 0.f : exp2f(ps[DV] - M);
     L += ps[DV + 1] * w;
 #pragma unroll
     for (int i = 0; i < PL; ++i) okv[i] += ps[lane * PL + i] * w;

@@ -87,6 +87,8 @@ struct AttnArgs {
   float eps;
   int B, T, H, cap;
   const float2* rope;   // [T][dk/2] (cos, sin) of the query rotations, or null
+  const int32_t* lo;    // [B*H][T] first visible cache entry per query (same-document
+                        // masking: keys c in [lo, ntok) are visible), or null (0)
 };
 
 struct DecodeAttnArgs {
@@ -98,6 +100,22 @@ struct DecodeAttnArgs {
   float scale;
   int B, H, cap, seg, nseg;
   const float2* rope;   // [B][dk/2] (cos, sin) of the query rotation at t_abs[b], or null
+  const int32_t* lo;    // [B*H] first visible cache entry (same-document masking), or null
+};
+
+// Same-document masking: the first cache entry each query may see, the number of
+// entries at positions before the query's document start (clamped to the query's
+// visible count).  Forward (ntok set): token t of a call starting at t0; decode
+// (ntok null, T = 1): the new token, after its append.
+struct DocLoArgs {
+  const int32_t* doc_start; // [B,T] absolute document start per token
+  const int32_t* ntok;      // [B*H][T] inclusive visible counts, or null (decode)
+  const int32_t* count_in;  // [B*H] entries before this call (forward)
+  const int32_t* count;     // [B*H] entries after the append (decode)
+  const int32_t* pos;       // [B*H][cap] ascending positions
+  int32_t* lo;              // [B*H][T] out
+  int t0;
+  int B, T, H, cap;
 };
 
 struct DecodeCombineArgs {
@@ -130,6 +148,7 @@ hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, h
 hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float2* table, const int32_t* t_abs, int t0, int rows, int dk,
                              double base, hipStream_t s);
+hipError_t launch_doc_lo(const DocLoArgs& a, hipStream_t s);
 
 constexpr int kChunk = 64;         // tokens per routing / compaction chunk
 constexpr int kDecodeSeg = 1024;   // keys per split-K segment in decode

@@ -386,4 +386,40 @@ hipError_t launch_rope_table(float2* table, const int32_t* t_abs, int t0, int ro
   return hipGetLastError();
 }
 
+// Same-document masking: lo = entries at positions < the query's document start.
+// Entries are in ascending position; those of this call are counted by ntok (the
+// inclusive count after local token j is ntok[j]), earlier ones by a binary search.
+HAM_DEVICE int count_before(const int32_t* p, int n, long long ds) {
+  int l = 0, r = n;
+  while (l < r) {
+    const int m = (l + r) >> 1;
+    if ((long long)p[m] < ds) l = m + 1; else r = m;
+  }
+  return l;
+}
+
+// grid (ceil(T/256), H, B), 256 threads: one query per thread.
+__global__ __launch_bounds__(256) void doc_lo_kernel(DocLoArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (t >= a.T) return;
+  const int bh = b * a.H + h;
+  const long long ds = a.doc_start[(size_t)b * a.T + t];
+  const int32_t* ph = a.pos + (size_t)bh * a.cap;
+  int lo;
+  if (a.ntok) {
+    const int32_t* nt = a.ntok + (size_t)bh * a.T;
+    const long long j = ds - (long long)a.t0;          // local index of the start
+    lo = (j >= 1) ? nt[(int)min(j - 1, (long long)t)] : count_before(ph, a.count_in[bh], ds);
+    lo = min(lo, nt[t]);
+  } else {
+    lo = count_before(ph, a.count[bh], ds);
+  }
+  a.lo[(size_t)bh * a.T + t] = lo;
+}
+
+hipError_t launch_doc_lo(const DocLoArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(doc_lo_kernel, dim3((a.T + 255) / 256, a.H, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace ham

@@ -110,6 +110,15 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  *   tau                [H] fp32, required: routing threshold per head in e-units
  *                      (+inf routes nothing: pure gated DeltaNet; -inf routes all).
  *   gate_rnn, gate_kv  [B,T,H] fp32 or NULL (= 1).
+ *   doc_start          [B,T] int32 or NULL: same-document masking of a packed
+ *                      batch ([HAM] App. A.1 "FlexAttention and Block Masks").
+ *                      doc_start[b,t] is the absolute position where token t's
+ *                      document begins; the token attends only to cached keys
+ *                      at positions >= it (keys of earlier calls included, so a
+ *                      document may span calls).  Only the attention is masked:
+ *                      the RNN, the routing and the cache see every token.
+ *                      Any values are accepted; a start after the token's own
+ *                      position leaves it no key (o_kv = 0).
  *   S0                 [B,H,dk,dv] fp32 entering state, or NULL (= 0).
  *   S_out              [B,H,dk,dv] fp32, required: state after token T-1.  May
  *                      alias S0.
@@ -137,6 +146,7 @@ int ham_forward(const ham_dims *dims,
                 const void *q_attn, const void *k_attn, const void *v_attn,
                 const float *beta, const float *g, const float *tau,
                 const float *gate_rnn, const float *gate_kv,
+                const int32_t *doc_start,
                 const float *S0, float *S_out,
                 void *o, void *o_rnn, void *o_kv,
                 float *e, uint8_t *routed,
@@ -155,6 +165,9 @@ size_t ham_decode_workspace_size(const ham_dims *dims);
  *
  *   q, k, v (+ optional *_attn)  [B,H,dk|dv] io dtype.
  *   beta, g, gate_rnn, gate_kv   [B,H] fp32 (gates may be NULL).
+ *   doc_start                    [B] int32 or NULL: absolute start position of
+ *                                the new token's document (same-document
+ *                                masking, as in ham_forward).
  *   tau                          [H] fp32.
  *   S                            [B,H,dk,dv] fp32, in/out.
  *   Kc, Vc, pos, count           cache, in/out (count[b,h] <= cap on entry).
@@ -171,6 +184,7 @@ int ham_decode_step(const ham_dims *dims,
                     const void *q_attn, const void *k_attn, const void *v_attn,
                     const float *beta, const float *g, const float *tau,
                     const float *gate_rnn, const float *gate_kv,
+                    const int32_t *doc_start,
                     float *S, void *Kc, void *Vc, int32_t *pos, int32_t *count,
                     const int32_t *t_abs,
                     void *o, void *o_rnn, void *o_kv,

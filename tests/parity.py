@@ -70,12 +70,12 @@ def check_routing(e_gpu, r_gpu, ref, tau):
 
 def check_forward(out, inp, tau, dtype, *, scale, ref=None, gates=None, attn=None, S0=None,
                   cache=None, t0=0, eps=1e-6, check_outputs=("o", "o_rnn", "o_kv"), cap=None,
-                  router_score=None, rope_base=0.0):
+                  router_score=None, rope_base=0.0, doc_start=None):
     """Full comparison of one ham_forward result against the oracle.  With learned-router
     scores both sides compare the same float32 score with the same threshold, so the
     routing must match exactly (no near-threshold exemption)."""
     okw = dict(scale=scale, eps=eps, S0=S0, cache=cache, t0=t0, cap=cap, router_score=router_score,
-               rope_base=rope_base)
+               rope_base=rope_base, doc_start=doc_start)
     if gates is not None:
         okw.update(gate_rnn=gates[0], gate_kv=gates[1])
     if attn is not None:

@@ -65,7 +65,7 @@ def test_rope_workspace_and_base_checks():
 def _fwd(d, ptrs=None, ws_bytes=1 << 40):
     P = ctypes.c_void_p
     fake = P(1 << 20)   # an aligned non-NULL host value; never dereferenced by these checks
-    args = [fake] * 23 if ptrs is None else ptrs
+    args = [fake] * 24 if ptrs is None else ptrs
     return _lib.lib().ham_forward(ctypes.byref(d), *args, ws_bytes, None)
 
 
@@ -76,7 +76,7 @@ def _msg():
 def test_forward_argument_errors():
     P = ctypes.c_void_p
     fake = P(1 << 20)
-    base = [fake] * 23
+    base = [fake] * 24
     # dims
     assert _fwd(dims(dk=100)) == _lib.HAM_EUNSUPPORTED
     assert "dk" in _msg()
@@ -85,8 +85,8 @@ def test_forward_argument_errors():
     assert _fwd(dims(flags=8)) == _lib.HAM_EUNSUPPORTED
     assert _fwd(dims(scale=0.0)) == _lib.HAM_EINVAL and "scale" in _msg()
     assert _fwd(dims(scale=-1.0)) == _lib.HAM_EINVAL
-    # required pointers: q k v (0-2), beta g tau (6-8), S_out (12), o (13), Kc Vc pos count (18-21)
-    for i in (0, 1, 2, 6, 7, 8, 12, 13, 18, 19, 20, 21):
+    # required pointers: q k v (0-2), beta g tau (6-8), S_out (13), o (14), Kc Vc pos count (19-22)
+    for i in (0, 1, 2, 6, 7, 8, 13, 14, 19, 20, 21, 22):
         a = list(base)
         a[i] = None
         assert _fwd(dims(), a) == _lib.HAM_EINVAL, i
@@ -101,7 +101,7 @@ def test_forward_argument_errors():
     assert _fwd(dims(cap=100)) == _lib.HAM_ECAPACITY
     # workspace
     a = list(base)
-    a[22] = None
+    a[23] = None
     assert _fwd(dims(), a) == _lib.HAM_EWORKSPACE
     assert _fwd(dims(), base, ws_bytes=16) == _lib.HAM_EWORKSPACE
 
@@ -110,13 +110,13 @@ def test_decode_and_stats_argument_errors():
     L = _lib.lib()
     P = ctypes.c_void_p
     fake = P(1 << 20)
-    a = [fake] * 24
-    a[15] = None                                       # count
+    a = [fake] * 25
+    a[16] = None                                       # count
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
-    a = [fake] * 24
-    a[16] = None                                       # t_abs
+    a = [fake] * 25
+    a[17] = None                                       # t_abs
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
-    a = [fake] * 24
+    a = [fake] * 25
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 8, None) == _lib.HAM_EWORKSPACE
     s = [fake] * 11
     s[9] = None                                        # count
@@ -152,12 +152,12 @@ def test_select_tau_and_external_score_errors():
     assert L.ham_select_tau(ctypes.byref(dims(B=65536, T=65536)), fake, ctypes.c_double(0.5), fake,
                             None) == _lib.HAM_EINVAL
     # external scores need e
-    base = [fake] * 23
+    base = [fake] * 24
     a = list(base)
-    a[16] = None                                       # e
+    a[17] = None                                       # e
     assert _fwd(dims(flags=_lib.HAM_EXTERNAL_SCORES), a) == _lib.HAM_EINVAL and "EXTERNAL" in _msg()
-    a = [fake] * 24
-    a[20] = None                                       # e of the decode step
+    a = [fake] * 25
+    a[21] = None                                       # e of the decode step
     assert L.ham_decode_step(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *a, 1 << 40, None) == _lib.HAM_EINVAL
     s = [fake] * 11
     assert L.ham_route_stats(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *s, ctypes.c_float(1e-5), None,

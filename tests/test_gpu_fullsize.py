@@ -4,7 +4,8 @@ routing decision, compaction entry and final state of every head (RNN-only oracl
 pass), and the attention outputs at sampled tokens of sampled heads.
 
 Workloads: the layer at the 800M-model shape (B=8, H=16, d=128, T=4096, bf16 I/O,
-rho = 0.5 and the two rho limits; rho = 0.5 with RoPE base 500K); the long-context case (B=1, H=16, T=32768,
+rho = 0.5 and the two rho limits; rho = 0.5 with RoPE base 500K; rho = 0.5 over packed
+documents with same-document masking and RoPE); the long-context case (B=1, H=16, T=32768,
 planted repeated pairs, rho = 0.25); the decode case (batch 32, H=16, d=128,
 32K-token prefix, then decode steps).
 """
@@ -15,8 +16,8 @@ import torch
 import oracle
 import attention_sequence_mixing_amd as ham
 from attention_sequence_mixing_amd.inputs import (LAYER, LONG, DECODE_B, DECODE_D, DECODE_H,
-                                                  DECODE_PREFIX, make_inputs_torch, make_workload,
-                                                  tau_for_rho)
+                                                  DECODE_PREFIX, make_doc_start, make_inputs_torch,
+                                                  make_workload, tau_for_rho)
 from parity import E_TOL, NEAR, TOL, np_of, rel_err_slices, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -69,7 +70,8 @@ def _check_all_heads(out, ref, tau, kc_tol=None):
     return int(flips.sum()), float(de)
 
 
-def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu, rope_base=0.0):
+def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu, rope_base=0.0,
+                           doc_start=None):
     """Oracle outputs at sampled tokens of sampled heads (with the GPU mask if it
     differs from the oracle's inside the near band)."""
     T = inp["q"].shape[1]
@@ -81,7 +83,8 @@ def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu
         emit = np.zeros((1, T, 1), np.int8)
         emit[0, toks, 0] = 1
         ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit,
-                             mask_override=r_gpu[b:b + 1, :, h:h + 1], rope_base=rope_base)
+                             mask_override=r_gpu[b:b + 1, :, h:h + 1], rope_base=rope_base,
+                             doc_start=None if doc_start is None else doc_start[b:b + 1])
         for name in ("o", "o_rnn", "o_kv"):
             x = np_of(out[name][b, toks, h])
             y = ref[name][0, toks, 0]
@@ -130,6 +133,29 @@ def test_layer_fullsize_rope():
     worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 0), (4, 9), (7, 15)], 24,
                                    torch.bfloat16, 42, out["routed"].cpu().numpy(), rope_base=base)
     print(f"layer rope: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
+
+
+def test_layer_fullsize_packed_documents():
+    """The layer at rho = 0.5 over packed batches (geometric document lengths, mean
+    1024 tokens) with same-document masking and RoPE base 500K."""
+    w = LAYER
+    inp = make_workload(w)
+    scale = w.attn_scale
+    ds = make_doc_start(w.B, w.T, 1024, 43)
+    base_e = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(base_e["e"], 0.5)
+    ref = _rnn_only_oracle(inp, tau, scale, rope_base=500000.0)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, rope_base=500000.0,
+                          doc_start=torch.from_numpy(ds.astype(np.int32)).to(DEV),
+                          want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    nflip, de = _check_all_heads(out, ref, tau, kc_tol=8e-3)
+    worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 1), (2, 8), (6, 14)], 32,
+                                   torch.bfloat16, 44, out["routed"].cpu().numpy(),
+                                   rope_base=500000.0, doc_start=ds)
+    print(f"layer packed: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
 
 
 def test_long_context_fullsize():
