@@ -195,11 +195,13 @@ def bench_forward(args, dev):
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
-    router = bench_router(args, dev, w, t)
-    from attention_sequence_mixing_amd.inputs import make_doc_start
-    rope = bench_variant(args, dev, w, t, tau, "rope500000", rope_base=500000.0)
-    packed = bench_variant(args, dev, w, t, tau, "packed_docs_mean1024_rope500000", rope_base=500000.0,
-                           doc_start=make_doc_start(w.B, w.T, 1024, w.seed))
+    router = rope = packed = None
+    if not args.main_only:
+        from attention_sequence_mixing_amd.inputs import make_doc_start
+        router = bench_router(args, dev, w, t)
+        rope = bench_variant(args, dev, w, t, tau, "rope500000", rope_base=500000.0)
+        packed = bench_variant(args, dev, w, t, tau, "packed_docs_mean1024_rope500000",
+                               rope_base=500000.0, doc_start=make_doc_start(w.B, w.T, 1024, w.seed))
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
                 router=router, rope=rope, packed=packed)
@@ -237,6 +239,51 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None):
     return dict(workload=f"{w.name}_{label}", ms_per_step=round(ms, 4),
                 tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
                 stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
+
+
+def bench_router(args, dev, w, t):
+    """The same layer routed by learned-router scores (synthetic sigmoid(N(0,1)) per
+    token-head, as inputs.make_router_scores draws them): the threshold for the target
+    fraction comes from ham_select_tau on the GPU."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    from attention_sequence_mixing_amd.inputs import make_router_scores
+    rs = torch.from_numpy(make_router_scores(w.B, w.T, w.H, w.seed)).to(dev)
+    tau = ham.ham_select_tau(rs, w.rho)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nsel = 20
+    e0.record()
+    for _ in range(nsel):
+        ham.ham_select_tau(rs, w.rho, out=tau)
+    e1.record()
+    torch.cuda.synchronize()
+    sel_us = e0.elapsed_time(e1) / nsel * 1e3
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale,
+                           flags=ham.HAM_EXTERNAL_SCORES)
+
+    def step():
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, router_scores=rs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    lib.ham_profile_start(args.steps)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = collect_stages(lib, args.steps)
+    rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
+    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
+    log(f"[bench] learned router: {ms:.3f} ms/step, select_tau {sel_us:.1f} us, rho {rho:.4f}, "
+        f"stages {dict(zip(names, [round(x, 4) for x in stages]))}")
+    return dict(workload=f"{w.name}_learned_router", ms_per_step=round(ms, 4),
+                tokens_per_s=round(w.B * w.T / (ms / 1e3), 1), rho_measured=round(rho, 6),
+                select_tau_us=round(sel_us, 2), stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
 
 
 def bench_decode(args, dev):
@@ -335,6 +382,8 @@ def main():
     # warmup steps of the layer leave the first timed steps at a lower clock
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the layer forward (no learned-router, RoPE or packed-document legs)")
     ap.add_argument("--decode-prefix", type=int, default=0)
     ap.add_argument("--cpu-batch", type=int, default=8,
                     help="sequences of the layer workload the CPU oracle baseline runs")
