@@ -140,16 +140,26 @@ HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, 
 // Prep kernel: one workgroup (4 waves) per (b, h, chunk); chunks are independent.
 // Decayed Gram matrices (S2), their diagonal-block inverses (S3), gamma and the
 // state-update decays (S1).
+// 39 KiB at d_k = 128, so four workgroups share a CU: K and Q rows are unpadded with
+// their 16-byte chunks XOR-swizzled by row, and the block-inverse scratch reuses Q's
+// space once the Gram fragments are done.
 template <int DK>
 struct PrepSmem {
-  static constexpr int KS = DK + 8;
-  uint16_t K[kC * KS];
-  uint16_t Q[kC * KS];
+  static constexpr int NCH = DK / 8;       // 16-byte chunks per K / Q row
+  // element offset of chunk c of row r: the 16 rows one fragment read touches fall in
+  // different banks
+  HAM_DEVICE static int at(int r, int c) { return r * DK + ((c ^ (r & (NCH - 1))) << 3); }
+  uint16_t K[kC * DK];
+  union {
+    uint16_t Q[kC * DK];                   // until the Gram fragments are done
+    struct {
+      alignas(16) float Td[4][16][20];     // (I + Ld)^-1 diag(beta)
+      float W[2][16][17];                  // Aoff T'_{2I}
+      alignas(16) float Off[2][16][20];    // -T'_{2I+1} Aoff T'_{2I}
+    };
+  };
   float Ld[4][16][17];                     // diagonal 16x16 blocks of diag(beta) A
-  alignas(16) float Td[4][16][20];         // (I + Ld)^-1 diag(beta)
   float Aoff[2][16][17];                   // A blocks (rows 16-block 2I+1, cols 16-block 2I)
-  float W[2][16][17];                      // Aoff T'_{2I}
-  alignas(16) float Off[2][16][20];        // -T'_{2I+1} Aoff T'_{2I}
   alignas(16) float G2[kC];
   alignas(16) float beta[kC];
 };
@@ -159,7 +169,7 @@ struct PrepSmem {
 // ends with entries (t = 16mt + n, j = 32s + 16h + 4g + i) for half h, i = 0..3.
 template <int DK, bool kQK>
 HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g, int n, int lane) {
-  constexpr int KS = PrepSmem<DK>::KS;
+  using SM = PrepSmem<DK>;
   const uint16_t* rowsT = kQK ? sm.Q : sm.K;
   float val[2][4];
 #pragma unroll
@@ -169,8 +179,8 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
     if (jt <= mt) {
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[(16 * jt + n) * KS + 32 * ks + 8 * g]));
-        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[(16 * mt + n) * KS + 32 * ks + 8 * g]));
+        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[SM::at(16 * jt + n, 4 * ks + g)]));
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[SM::at(16 * mt + n, 4 * ks + g)]));
         acc = mfma_bf16(af, bf, acc);
       }
     }
@@ -230,7 +240,6 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
 template <int DK>
 __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
   using SM = PrepSmem<DK>;
-  constexpr int KS = SM::KS;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -253,8 +262,8 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
       kx = *reinterpret_cast<const u16x8*>(kp + off);
       if (readout) qx = *reinterpret_cast<const u16x8*>(qp + off);
     }
-    *reinterpret_cast<u16x8*>(&sm.K[row * KS + cu]) = kx;
-    *reinterpret_cast<u16x8*>(&sm.Q[row * KS + cu]) = qx;
+    *reinterpret_cast<u16x8*>(&sm.K[SM::at(row, cu >> 3)]) = kx;
+    *reinterpret_cast<u16x8*>(&sm.Q[SM::at(row, cu >> 3)]) = qx;
   }
   if (wave == 0) {
     float gv = 0.f, bv = 0.f;

@@ -126,3 +126,30 @@ def test_select_tau_then_route_hits_the_fraction():
         for h in range(H):
             if len(np.unique(e[:, :, h])) == B * T:
                 assert int(st2["count"][:, h].sum()) == k
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_router_one_routed_set_per_layer(dtype):
+    """A learned router gives one score per token (sigma(W_r x_t) has no head index);
+    broadcast over the heads with one threshold, every head routes the same tokens:
+    the layer keeps one routed set (the per-layer T_KV of the memory accounting,
+    App. E.4), each head caching its own k and v of those tokens."""
+    B, T, H, d = 2, 230, 4, 64
+    inp = make_inputs(B, T, H, d, dtype="f32" if dtype == torch.float32 else "bf16", seed=72)
+    one = make_router_scores(B, T, 1, 72)
+    rs = np.ascontiguousarray(np.broadcast_to(one, (B, T, H)))
+    tau1 = oracle.select_tau(one, 0.3)
+    tau = np.full(H, tau1[0], np.float32)
+    t = to_dev(inp, dtype, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=d ** -0.5, router_scores=torch.from_numpy(rs).to(DEV),
+                          want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    r = out["routed"].cpu().numpy().astype(bool)
+    assert (r == r[:, :, :1]).all()
+    cnt = out["count"].cpu().numpy()
+    assert (cnt == cnt[:, :1]).all() and int(cnt[0, 0]) == int((one[0, :, 0] > tau1[0]).sum())
+    pos = out["pos"].cpu().numpy()
+    for b in range(B):
+        assert (pos[b, :, :cnt[b, 0]] == pos[b, :1, :cnt[b, 0]]).all()
+    check_forward(out, inp, tau, dtype, scale=d ** -0.5, router_score=rs)
