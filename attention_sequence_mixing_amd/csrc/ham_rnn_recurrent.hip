@@ -4,39 +4,48 @@
 // 1/2|S k - v|^2; readout S_t^T q_t) with the gated-DeltaNet decay of App. A.1,
 // and the fit-error score of §2 / App. A.1 ("Router Implementations").
 //
-// One wave owns a 16-column slice of the fp32 state S (dk x dv) of one head and
-// walks the tokens in order.  Lane = 4*c + r: column j0+c, rows [r*dk/4, (r+1)*dk/4).
-// Columns of S evolve independently under S <- alpha (I - beta k k^T) S + beta k v^T,
-// so slices need no communication; the routing score only needs three sums per
-// token, written per slice as partials.  This is the decode-step kernel and the
-// forward path for short sequences.
+// One wave owns 64 columns of the fp32 state S (dk x dv) of one head and walks the
+// tokens in order.  Lane (rh, cp) = (lane / 32, lane mod 32) holds columns 2cp, 2cp+1
+// of the wave's block for rows [rh*dk/2, (rh+1)*dk/2), so each row's 64 columns are
+// one contiguous 256-byte run of float2 loads.  Columns of S evolve independently
+// under S <- alpha (I - beta k k^T) S + beta k v^T, so waves need no communication;
+// the routing score only needs three sums per token, written as partials per
+// 16-column slice.  k_t and q_t are staged in LDS as floats each token (every lane
+// reads them; the reads broadcast).  This is the decode-step kernel and the forward
+// path for short sequences and fp32 I/O.
 #include "ham_common.h"
 #include "ham_internal.h"
 
 namespace ham {
 
+constexpr int kRecCols = 64;              // state columns per wave
+
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
+  static_assert(DV % kRecCols == 0, "whole 64-column blocks");
   using E = typename IO::elem;
-  constexpr int RPL = DK / 4;             // rows per lane
-  constexpr int NS = DV / 16;             // slices per head
+  constexpr int RH = DK / 2;               // rows per lane
+  constexpr int NS = DV / 16;              // score slices per head
+  __shared__ float4 ks4[DK / 4], qs4[DK / 4];
+  float* ks = reinterpret_cast<float*>(ks4);
+  float* qs = reinterpret_cast<float*>(qs4);
   const int lane = lane_id();
-  const int c = lane >> 2, r = lane & 3;
-  const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int j = slice * 16 + c;
+  const int rh = lane >> 5, cp = lane & 31;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int j0 = blk * kRecCols + 2 * cp;  // this lane's first column
   const int bh = b * a.H + h;
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
 
-  float S[RPL];
-  const size_t sbase = (size_t)bh * DK * DV;
+  float2 S[RH];
+  const size_t sbase = (size_t)bh * DK * DV + (size_t)(rh * RH) * DV + j0;
   if (a.S0) {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) S[m] = a.S0[sbase + (size_t)(r * RPL + m) * DV + j];
+    for (int m = 0; m < RH; ++m) S[m] = *reinterpret_cast<const float2*>(a.S0 + sbase + (size_t)m * DV);
   } else {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) S[m] = 0.f;
+    for (int m = 0; m < RH; ++m) S[m] = make_float2(0.f, 0.f);
   }
 
   const bool readout = a.o_rnn32 != nullptr;
@@ -44,52 +53,77 @@ __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
     const size_t tok = ((size_t)b * a.T + t) * a.H + h;
     const float alpha = expf(a.g[tok]);
     const float beta = a.beta[tok];
-    float kr[RPL];
-#pragma unroll
-    for (int m = 0; m < RPL; m += 4) IO::load4(k, tok * DK + r * RPL + m, kr + m);
-    const float vj = IO::load(v, tok * DV + j);
+    for (int e = lane; e < DK; e += 64) {
+      ks[e] = IO::load(k, tok * DK + e);
+      if (readout) qs[e] = IO::load(q, tok * DK + e);
+    }
+    const float v0 = IO::load(v, tok * DV + j0), v1 = IO::load(v, tok * DV + j0 + 1);
+    __syncthreads();
+    const float4* kr = ks4 + rh * (RH / 4);
 
-    // prediction p_j = sum_i S[i][j] k_i   (S_{t-1}^T k_t)
-    float p = 0.f;
+    // prediction p_j = sum_i S[i][j] k_i   (S_{t-1}^T k_t), two chains per column
+    float pa0 = 0.f, pa1 = 0.f, pb0 = 0.f, pb1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) p = fmaf(S[m], kr[m], p);
-    p = wave_sum<4>(p);
+    for (int m = 0; m < RH; m += 4) {
+      const float4 kk = kr[m / 4];
+      pa0 = fmaf(S[m].x, kk.x, pa0);     pa1 = fmaf(S[m].y, kk.x, pa1);
+      pb0 = fmaf(S[m + 1].x, kk.y, pb0); pb1 = fmaf(S[m + 1].y, kk.y, pb1);
+      pa0 = fmaf(S[m + 2].x, kk.z, pa0); pa1 = fmaf(S[m + 2].y, kk.z, pa1);
+      pb0 = fmaf(S[m + 3].x, kk.w, pb0); pb1 = fmaf(S[m + 3].y, kk.w, pb1);
+    }
+    float p0 = pa0 + pb0, p1 = pa1 + pb1;
+    p0 += __shfl_xor(p0, 32, kWave);       // the other half of the rows
+    p1 += __shfl_xor(p1, 32, kWave);
 
-    // score partials over this slice's 16 columns (lanes of one column agree)
-    float pv = p * vj, pp = p * p, vv = vj * vj;
+    // score partials over each 16-column slice (8 lanes of column pairs)
+    float pv = p0 * v0 + p1 * v1, pp = p0 * p0 + p1 * p1, vv = v0 * v0 + v1 * v1;
 #pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) {
+    for (int msk = 1; msk < 8; msk <<= 1) {
       pv += __shfl_xor(pv, msk, kWave);
       pp += __shfl_xor(pp, msk, kWave);
       vv += __shfl_xor(vv, msk, kWave);
     }
-    if (lane == 0) a.score[tok * NS + slice] = make_float4(pv, pp, vv, 0.f);
+    if (rh == 0 && (cp & 7) == 0)
+      a.score[tok * NS + blk * (kRecCols / 16) + (cp >> 3)] = make_float4(pv, pp, vv, 0.f);
 
     // S <- alpha*S + k * beta*(v_j - alpha*p_j)
-    const float w = beta * (vj - alpha * p);
+    const float w0 = beta * (v0 - alpha * p0), w1 = beta * (v1 - alpha * p1);
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) S[m] = fmaf(kr[m], w, alpha * S[m]);
+    for (int m = 0; m < RH; m += 4) {
+      const float4 kk = kr[m / 4];
+      S[m].x = fmaf(kk.x, w0, alpha * S[m].x);         S[m].y = fmaf(kk.x, w1, alpha * S[m].y);
+      S[m + 1].x = fmaf(kk.y, w0, alpha * S[m + 1].x); S[m + 1].y = fmaf(kk.y, w1, alpha * S[m + 1].y);
+      S[m + 2].x = fmaf(kk.z, w0, alpha * S[m + 2].x); S[m + 2].y = fmaf(kk.z, w1, alpha * S[m + 2].y);
+      S[m + 3].x = fmaf(kk.w, w0, alpha * S[m + 3].x); S[m + 3].y = fmaf(kk.w, w1, alpha * S[m + 3].y);
+    }
 
     if (readout) {
-      float qr[RPL];
+      const float4* qr = qs4 + rh * (RH / 4);
+      float oa0 = 0.f, oa1 = 0.f, ob0 = 0.f, ob1 = 0.f;
 #pragma unroll
-      for (int m = 0; m < RPL; m += 4) IO::load4(q, tok * DK + r * RPL + m, qr + m);
-      float o = 0.f;
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) o = fmaf(S[m], qr[m], o);
-      o = wave_sum<4>(o);
-      if (r == 0) a.o_rnn32[tok * DV + j] = o;
+      for (int m = 0; m < RH; m += 4) {
+        const float4 qq = qr[m / 4];
+        oa0 = fmaf(S[m].x, qq.x, oa0);     oa1 = fmaf(S[m].y, qq.x, oa1);
+        ob0 = fmaf(S[m + 1].x, qq.y, ob0); ob1 = fmaf(S[m + 1].y, qq.y, ob1);
+        oa0 = fmaf(S[m + 2].x, qq.z, oa0); oa1 = fmaf(S[m + 2].y, qq.z, oa1);
+        ob0 = fmaf(S[m + 3].x, qq.w, ob0); ob1 = fmaf(S[m + 3].y, qq.w, ob1);
+      }
+      float o0 = oa0 + ob0, o1 = oa1 + ob1;
+      o0 += __shfl_xor(o0, 32, kWave);
+      o1 += __shfl_xor(o1, 32, kWave);
+      if (rh == 0) *reinterpret_cast<float2*>(a.o_rnn32 + tok * DV + j0) = make_float2(o0, o1);
     }
+    __syncthreads();                       // k, q of the next token overwrite LDS
   }
 #pragma unroll
-  for (int m = 0; m < RPL; ++m) a.S_out[sbase + (size_t)(r * RPL + m) * DV + j] = S[m];
+  for (int m = 0; m < RH; ++m) *reinterpret_cast<float2*>(a.S_out + sbase + (size_t)m * DV) = S[m];
 }
 
 int rnn_recurrent_slices(int dv) { return dv / 16; }
 
 template <class IO, int DK, int DV>
 static hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
-  dim3 grid(DV / 16, a.H, a.B);
+  dim3 grid(DV / kRecCols, a.H, a.B);
   hipLaunchKernelGGL((rnn_recurrent_kernel<IO, DK, DV>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
