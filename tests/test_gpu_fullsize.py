@@ -16,8 +16,8 @@ import torch
 import oracle
 import attention_sequence_mixing_amd as ham
 from attention_sequence_mixing_amd.inputs import (LAYER, LONG, DECODE_B, DECODE_D, DECODE_H,
-                                                  DECODE_PREFIX, make_doc_start, make_inputs_torch,
-                                                  make_workload, tau_for_rho)
+                                                  DECODE_PREFIX, make_doc_start, make_inputs,
+                                                  make_inputs_torch, make_workload, tau_for_rho)
 from parity import E_TOL, NEAR, TOL, np_of, rel_err_slices, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -217,3 +217,47 @@ def test_decode_fullsize_sampled_heads():
         assert err < TOL[torch.bfloat16], (b, h, err)
         errS = np.abs(np_of(plan.S[b, h]) - ref["S"][0, 0]).max() / np.abs(ref["S"][0, 0]).max()
         assert errS < 1e-4, errS
+
+
+def test_decode_maximum_capacity_many_segments():
+    """The largest cache the boundary accepts (cap = 4 194 304 entries per head, 2 GiB
+    per K and V array here) with a ragged 70 001-token prefix, head 0 routing every
+    token (70 001 cached keys: 69 split-K segments, more than one combine pass over
+    the 64 lanes) and head 1 at a finite threshold; then decode steps against the
+    oracle (attention outputs only at the decode steps)."""
+    B, H, d, T0, steps = 1, 2, 128, 70001, 3
+    cap = 4194304
+    T = T0 + steps
+    scale = d ** -0.5
+    inp = make_inputs(B, T, H, d, dtype="bf16", seed=45)
+    tau = np.array([-np.inf, 1.0], np.float32)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+    pre = {n: x[:, :T0].contiguous() for n, x in t.items()}
+    plan = ham.ForwardPlan(B, T0, H, d, d, torch.bfloat16, DEV, cap=cap, scale=scale)
+    plan(pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"], tau_d)
+    dplan = ham.DecodePlan(B, H, d, d, cap, torch.bfloat16, DEV, scale=scale)
+    outs, rs, es = [], [], []
+    for s in range(steps):
+        x = {n: t[n][:, T0 + s].contiguous() for n in t}
+        dplan(x["q"], x["k"], x["v"], x["beta"], x["g"], tau_d, plan.S, plan.Kc, plan.Vc, plan.pos,
+              plan.count, torch.full((B,), T0 + s, dtype=torch.int32, device=DEV))
+        outs.append(np_of(dplan.o)); rs.append(dplan.routed.cpu().numpy()); es.append(dplan.e.cpu().numpy())
+    torch.cuda.synchronize()
+    assert int(dplan.status.item()) == 0
+    r_all = np.concatenate([plan.routed.cpu().numpy(), np.stack(rs, 1)], 1)
+    e_all = np.concatenate([plan.e.cpu().numpy(), np.stack(es, 1)], 1)
+    assert r_all[:, :, 0].all()
+    emit = np.zeros((B, T, H), np.int8)
+    emit[:, T0:] = 1
+    ref = oracle.forward(**inp, tau=tau, scale=scale, cap=T, emit=emit)    # cap >= every count
+    assert np.abs(e_all - ref["e"]).max() < E_TOL
+    near = np.abs(ref["e"] - tau.reshape(1, 1, H).astype(np.float64)) < NEAR
+    assert not ((r_all.astype(bool) != ref["routed"].astype(bool)) & ~near).any()
+    if not np.array_equal(r_all.astype(bool), ref["routed"].astype(bool)):
+        ref = oracle.forward(**inp, tau=tau, scale=scale, cap=T, emit=emit, mask_override=r_all)
+    cnt = plan.count.cpu().numpy()
+    assert np.array_equal(cnt, ref["count"]) and int(cnt[0, 0]) == T
+    got = np.stack(outs, 1)
+    assert rel_err_slices(got, ref["o"][:, T0:], 2) < TOL[torch.bfloat16]
+    assert rel_err_slices(np_of(plan.S), ref["S"], 1) < 1e-4
