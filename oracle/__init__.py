@@ -74,7 +74,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
             S0=None, cache=None, cap=None, t0=0, doc_start=None, emit=None, threads=None):
     """Run the oracle over all heads.
 
-    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] (float32, e-units).
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] per head, or [B,T,H]
+    per token and head (a threshold schedule along the sequence); float32, e-units.
     S0: [B,H,dk,dv] or None (zeros).  cache: None or dict(Kc, Vc, pos, count) of an
     existing cache to continue ([B,H,cap,d], [B,H,cap], [B,H]).  t0: int or [B]
     absolute position of token 0.  rope_base: 0, or the RoPE base applied to the
@@ -93,7 +94,9 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     beta, g = _f64(beta), _f64(g)
     qa, ka, va = _f64(q_attn), _f64(k_attn), _f64(v_attn)
     gr, gk = _f64(gate_rnn), _f64(gate_kv)
-    tau = np.ascontiguousarray(np.asarray(tau, dtype=np.float32).reshape(H))
+    tau = np.asarray(tau, dtype=np.float32)
+    tau = np.ascontiguousarray(np.broadcast_to(tau.reshape(H) if tau.size == H else tau.reshape(B, T, H),
+                                               (B, T, H)))
     mo = None if mask_override is None else np.ascontiguousarray(
         np.asarray(mask_override).astype(np.int8))
     rs = None if router_score is None else np.ascontiguousarray(
@@ -177,13 +180,15 @@ def route_stats(out, tau, near_band=1e-5):
     """Counts, KV usage rho and near-threshold counts from an oracle result.
 
     rho = sum of routed counts / (B*T*H) ([HAM] §5, KV-usage definition restricted
-    to one layer); n_near[h] = number of tokens of head h with |e - tau_h| < near_band.
+    to one layer); n_near[h] = number of tokens of head h with |e - tau| < near_band (tau per
+    head [H] or per token and head [B,T,H]).
     """
     e = out["e"]
     B, T, H = e.shape
     routed = out["routed"].astype(np.int64)
     count = routed.sum(axis=1)                      # [B,H]
     rho = float(count.sum()) / float(B * T * H)
-    tau = np.asarray(tau, dtype=np.float64).reshape(1, 1, H)
+    tau = np.asarray(tau, dtype=np.float64)
+    tau = tau.reshape(1, 1, H) if tau.size == H else tau.reshape(B, T, H)
     n_near = (np.abs(e - tau) < near_band).sum(axis=(0, 1))
     return dict(count=count, rho=rho, n_near=n_near)

@@ -20,7 +20,10 @@
  *             ([HAM] App. A.1 "Router Implementations", fit-error router)
  *   e_t     = 1 - cos(p_t, v_t)   (cos := 0 if either vector is zero)
  *             ([HAM] §2 "Prediction Error as Routing Metric")
- *   routed  = float(e_t) > tau_h   (strict; NaN never routes)
+ *   routed  = float(e_t) > tau_{t,h}   (strict; NaN never routes).  The threshold
+ *             is given per token and head: a constant per head, or a schedule along
+ *             the sequence ([HAM] §6: the growth of the KV cache can follow a target
+ *             schedule along the sequence, set at test time).
  *             With a learned input router the score is instead the caller's
  *             e_t = router_score_t (sigma(W_r x_t) or sigma(MLP(x_t)), computed
  *             outside the layer; [HAM] App. A.1 "Router Implementations", input
@@ -173,7 +176,7 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
             if (mask_override)
                 r = mask_override[tok] != 0;
             else
-                r = ((float)et > tau[h]);
+                r = ((float)et > tau[tok]);
             if (e) e[tok] = et;
             if (routed) routed[tok] = (int8_t)r;
 

@@ -61,7 +61,9 @@ def check_routing(e_gpu, r_gpu, ref, tau):
     e_ref = ref["e"]
     de = np.abs(e_gpu - e_ref)
     assert de.max() < E_TOL, f"score error {de.max():.3e}"
-    near = np.abs(e_ref - np.asarray(tau, np.float64).reshape(1, 1, H)) < NEAR
+    t = np.asarray(tau, np.float64)
+    t = t.reshape(1, 1, H) if t.size == H else t.reshape(e_ref.shape)   # per head or per token
+    near = np.abs(e_ref - t) < NEAR
     flips = (r_gpu.astype(bool) != ref["routed"].astype(bool))
     bad = flips & ~near
     assert not bad.any(), f"{int(bad.sum())} routing flips outside the near band"

@@ -507,3 +507,41 @@ def test_doc_mask_continuation_and_degenerate_starts():
                           doc_start=np.arange(T)[None] + 1)
     assert not late["o_kv"].any()
     np.testing.assert_array_equal(late["o_rnn"], none["o_rnn"])
+
+
+# --- threshold schedules along the sequence ([HAM] §6 growth-rate control) ----------
+def test_tau_schedule_is_positional():
+    """A per-token threshold: +inf before position 40 and -inf from it routes exactly
+    the tokens from 40 on, in every head; the RNN side does not change."""
+    B, T, H, d = 2, 70, 3, 8
+    inp = make_inputs(B, T, H, d, seed=140)
+    sched = np.full((B, T, H), np.inf, np.float32)
+    sched[:, 40:] = -np.inf
+    out = oracle.forward(**inp, tau=sched, scale=0.5)
+    assert (out["routed"][:, :40] == 0).all() and (out["routed"][:, 40:] == 1).all()
+    np.testing.assert_array_equal(out["count"], np.full((B, H), T - 40))
+    np.testing.assert_array_equal(out["pos"][:, :, :T - 40], np.broadcast_to(np.arange(40, T), (B, H, T - 40)))
+    plain = oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5)
+    np.testing.assert_array_equal(out["o_rnn"], plain["o_rnn"])
+    np.testing.assert_array_equal(out["e"], plain["e"])
+
+
+def test_tau_schedule_equals_calls_with_constant_thresholds():
+    """A schedule that is tau_a on positions [0, 33) and tau_b after it equals a call with
+    tau_a over the first 33 tokens continued by a call with tau_b."""
+    B, T, H, d = 1, 90, 2, 8
+    inp = make_inputs(B, T, H, d, seed=141)
+    e = oracle.forward(**inp, tau=np.full(H, INF, np.float32), scale=0.5)["e"]
+    ta, tb = tau_for_rho(e[:, :33], 0.7), tau_for_rho(e[:, 33:], 0.2)
+    sched = np.empty((B, T, H), np.float32)
+    sched[:, :33] = ta
+    sched[:, 33:] = tb
+    one = oracle.forward(**inp, tau=sched, scale=0.5, cap=T)
+    p1 = {k: np.ascontiguousarray(x[:, :33]) for k, x in inp.items()}
+    p2 = {k: np.ascontiguousarray(x[:, 33:]) for k, x in inp.items()}
+    r1 = oracle.forward(**p1, tau=ta, scale=0.5, cap=T)
+    r2 = oracle.forward(**p2, tau=tb, scale=0.5, S0=r1["S"], t0=33,
+                        cache={n: r1[n] for n in ("Kc", "Vc", "pos", "count")})
+    np.testing.assert_array_equal(one["routed"], np.concatenate([r1["routed"], r2["routed"]], 1))
+    np.testing.assert_allclose(one["o"], np.concatenate([r1["o"], r2["o"]], 1), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(one["count"], r2["count"])
