@@ -17,11 +17,11 @@ import torch
 
 from . import _lib
 from ._lib import (HAM_BF16, HAM_CONTINUE, HAM_EXTERNAL_SCORES, HAM_F32, HAM_FORCE_RECURRENT,
-                   HamDims, HamError, check)
+                   HAM_TAU_PER_TOKEN, HamDims, HamError, check)
 
 __all__ = ["ham_forward", "ham_decode_step", "ham_route_stats", "ham_select_tau", "ForwardPlan",
            "DecodePlan", "HamError", "HAM_CONTINUE", "HAM_FORCE_RECURRENT", "HAM_EXTERNAL_SCORES",
-           "library_path"]
+           "HAM_TAU_PER_TOKEN", "library_path"]
 
 library_path = _lib.LIB_PATH
 
@@ -55,6 +55,18 @@ def _need(name, t, shape, dtype, device):
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     return t
+
+
+def _tau_flag(tau, per_token_shape, dev):
+    """0 for a per-head threshold [H], HAM_TAU_PER_TOKEN for one per token and head."""
+    if tau is None:
+        raise ValueError("tau is required")
+    H = per_token_shape[-1]
+    if tuple(tau.shape) == tuple(per_token_shape):
+        _need("tau", tau, per_token_shape, torch.float32, dev)
+        return HAM_TAU_PER_TOKEN
+    _need("tau", tau, (H,), torch.float32, dev)
+    return 0
 
 
 def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0):
@@ -109,7 +121,8 @@ class ForwardPlan:
             _need(n, t, (B, T, H, dv), dt, dev)
         for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
             _need(n, t, (B, T, H), torch.float32, dev)
-        _need("tau", tau, (H,), torch.float32, dev)
+        tf = _tau_flag(tau, (B, T, H), dev)
+        self.dims.flags = (self.dims.flags & ~HAM_TAU_PER_TOKEN) | tf
         _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
         _need("doc_start", doc_start, (B, T), torch.int32, dev)
         if q is None or k is None or v is None or beta is None or g is None or tau is None:
@@ -138,6 +151,9 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
                 t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, doc_start=None,
                 want_o_rnn=False, want_o_kv=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
+
+    tau: [H] float32 thresholds per head, or [B,T,H] per token and head (a schedule
+    along the sequence that steers how the cache grows).
 
     cache: None, or dict(Kc, Vc, pos, count) of an earlier call to continue; it
     is then extended in place and S0 should be that call's state.  router_scores:
@@ -205,7 +221,7 @@ class DecodePlan:
             _need(n, t, (B, H, dv), dt, dev)
         for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
             _need(n, t, (B, H), torch.float32, dev)
-        _need("tau", tau, (H,), torch.float32, dev)
+        tf = _tau_flag(tau, (B, H), dev)
         _need("S", S, (B, H, dk, dv), torch.float32, dev)
         _need("Kc", Kc, (B, H, cap, dk), dt, dev)
         _need("Vc", Vc, (B, H, cap, dv), dt, dev)
@@ -214,7 +230,7 @@ class DecodePlan:
         _need("t_abs", t_abs, (B,), torch.int32, dev)
         _need("router_scores", router_scores, (B, H), torch.float32, dev)
         _need("doc_start", doc_start, (B,), torch.int32, dev)
-        self.dims.flags = HAM_EXTERNAL_SCORES if router_scores is not None else 0
+        self.dims.flags = (HAM_EXTERNAL_SCORES if router_scores is not None else 0) | tf
         e = router_scores if router_scores is not None else self.e
         rc = _lib.lib().ham_decode_step(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
@@ -230,7 +246,7 @@ class DecodePlan:
 def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_eps=1e-6,
                     q_attn=None, k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None,
                     rope_base=0.0, doc_start=None, want_o_rnn=False, want_o_kv=False, stream=None):
-    """One decode step: q, k, v [B,H,d]; S and cache (dict Kc, Vc, pos, count) are
+    """One decode step: q, k, v [B,H,d]; tau [H] or [B,H]; S and cache (dict Kc, Vc, pos, count) are
     updated in place; t_abs [B] int32 positions (also the RoPE positions when
     rope_base > 0).  Returns dict(o, e, routed, status, ...)."""
     B, H, dk = q.shape
@@ -256,10 +272,10 @@ def ham_route_stats(k, v, beta, g, tau, *, q=None, S0=None, near_band=1e-5, want
     _need("v", v, (B, T, H, dv), dt, dev)
     _need("beta", beta, (B, T, H), torch.float32, dev)
     _need("g", g, (B, T, H), torch.float32, dev)
-    _need("tau", tau, (H,), torch.float32, dev)
+    tf = _tau_flag(tau, (B, T, H), dev)
     _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
     dims = make_dims(B, T, H, dk, dv, io, 1.0, 1e-6, max(T, 1),
-                     HAM_FORCE_RECURRENT if force_recurrent else 0)
+                     (HAM_FORCE_RECURRENT if force_recurrent else 0) | tf)
     L = _lib.lib()
     ws_bytes = L.ham_route_stats_workspace_size(ctypes.byref(dims))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

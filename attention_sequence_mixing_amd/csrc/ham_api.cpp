@@ -40,7 +40,7 @@ int check_dims(const ham_dims* d, bool need_T) {
     return fail(HAM_EUNSUPPORTED, "dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
   if (d->io_dtype != HAM_F32 && d->io_dtype != HAM_BF16)
     return fail(HAM_EUNSUPPORTED, "io_dtype must be HAM_F32 or HAM_BF16 (got %d)", d->io_dtype);
-  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES))
+  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES | HAM_TAU_PER_TOKEN))
     return fail(HAM_EUNSUPPORTED, "unknown flag bits 0x%x", d->flags);
   if (d->cap <= 0) return fail(HAM_EINVAL, "cap must be positive (cap=%d)", d->cap);
   // the attention kernels address one head's cache rows with 32-bit byte offsets
@@ -229,7 +229,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
 
   ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
                     (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H,
-                    ext ? e : nullptr};
+                    ext ? e : nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
 
@@ -291,7 +291,8 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   HAM_HIP(ham::launch_rnn_recurrent(d->io_dtype, d->dk, d->dv, ra, s));
   tm.mark();
   ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, ext ? nullptr : e_buf, r_buf,
-                    chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr};
+                    chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr,
+                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   // rotary table of the new tokens' positions t_abs[b] (key and query rotations)
@@ -351,10 +352,11 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   rc = run_rnn(d, ra, s, &slices, tm);
   if (rc != HAM_OK) return rc;
   ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count, nullptr, count_in,
-                    d->B, d->T, d->H};
+                    d->B, d->T, d->H, nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
-  ham::StatsArgs sa{e_buf, tau, chunk_count, count, n_near, near_band, d->B, d->T, d->H};
+  ham::StatsArgs sa{e_buf, tau, chunk_count, count, n_near, near_band, d->B, d->T, d->H,
+                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
   HAM_HIP(ham::launch_stats(sa, s));
   tm.mark();
   if (rho_host) {

@@ -32,7 +32,7 @@ constexpr size_t kPrepRecordBytes = 35840;
 struct RouteArgs {
   const float4* score;  // [B,T,H][slices]
   int slices;
-  const float* tau;     // [H]
+  const float* tau;     // [H], or [B,T,H] with tau_per_token
   float* e;             // [B,T,H]
   uint8_t* routed;      // [B,T,H]
   int32_t* chunk_count; // [B*H][nchunk]
@@ -41,6 +41,7 @@ struct RouteArgs {
   int B, T, H;
   const float* e_in;    // [B,T,H] caller's routing scores (learned router) or null;
                         // when set, score/slices are unused and e is not written
+  int tau_per_token;    // tau is [B,T,H] (a threshold schedule along the sequence)
 };
 
 struct CompactArgs {
@@ -70,6 +71,7 @@ struct StatsArgs {
   int64_t* n_near;      // [H] or null
   float near_band;
   int B, T, H;
+  int tau_per_token;    // tau is [B,T,H]
 };
 
 struct AttnArgs {

@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       } else {
         e = x[j][0].x;
       }
-      const bool r = e > a.tau[h];          // strict; a NaN score never routes
       const size_t tok = ((size_t)b * a.T + t0 + tl) * H + h;
+      const bool r = e > a.tau[a.tau_per_token ? tok : (size_t)h];   // strict; NaN never routes
       if constexpr (NS > 0) a.e[tok] = e;
       a.routed[tok] = (uint8_t)r;
       if (r) atomicAdd(&s_cnt[h], 1);
@@ -236,12 +236,12 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
     __syncthreads();
   }
   if (!a.n_near) return;
-  const float tau = a.tau[h];
   long long near = 0;
   const long long n = (long long)a.B * a.T;
   for (long long i = tid; i < n; i += 256) {
-    const float e = a.e[(size_t)i * a.H + h];
-    near += (fabsf(e - tau) < a.near_band) ? 1 : 0;
+    const size_t tok = (size_t)i * a.H + h;
+    const float e = a.e[tok];
+    near += (fabsf(e - a.tau[a.tau_per_token ? tok : (size_t)h]) < a.near_band) ? 1 : 0;
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) near += __shfl_xor(near, m, kWave);

@@ -68,6 +68,12 @@ extern "C" {
                                   prediction error; tau is in the same units.  The RNN
                                   still reads every token.  ham_forward and
                                   ham_decode_step only. */
+#define HAM_TAU_PER_TOKEN 8    /* tau holds one threshold per token and head:
+                                  [B,T,H] (ham_forward, ham_route_stats) or [B,H]
+                                  (ham_decode_step) instead of [H].  A schedule
+                                  along the sequence steers how the KV cache grows
+                                  ([HAM] §6: growth-rate control by a target
+                                  schedule, set at test time). */
 
 typedef struct {
     int B, T, H;      /* batch, new tokens per sequence, heads                   */
@@ -76,7 +82,8 @@ typedef struct {
     float scale;      /* attention logit scale, > 0 (usually 1/sqrt(dk))         */
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
     int cap;          /* KV-cache capacity per (b,h), in tokens, 1..4194304       */
-    int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES  */
+    int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES
+                         | HAM_TAU_PER_TOKEN                                      */
     int t0;           /* absolute position of token 0 (recorded in pos)          */
     float rope_base;  /* 0, or the base of a rotary position embedding (RoPE)
                          applied to the attention-path query and key at their
@@ -108,7 +115,8 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  *   beta, g            [B,T,H] fp32, required: write strength and log decay
  *                      (alpha = exp(g); g must be finite).
  *   tau                [H] fp32, required: routing threshold per head in e-units
- *                      (+inf routes nothing: pure gated DeltaNet; -inf routes all).
+ *                      (+inf routes nothing: pure gated DeltaNet; -inf routes all);
+ *                      [B,T,H] with HAM_TAU_PER_TOKEN.
  *   gate_rnn, gate_kv  [B,T,H] fp32 or NULL (= 1).
  *   doc_start          [B,T] int32 or NULL: same-document masking of a packed
  *                      batch ([HAM] App. A.1 "FlexAttention and Block Masks").
@@ -168,7 +176,7 @@ size_t ham_decode_workspace_size(const ham_dims *dims);
  *   doc_start                    [B] int32 or NULL: absolute start position of
  *                                the new token's document (same-document
  *                                masking, as in ham_forward).
- *   tau                          [H] fp32.
+ *   tau                          [H] fp32 ([B,H] with HAM_TAU_PER_TOKEN).
  *   S                            [B,H,dk,dv] fp32, in/out.
  *   Kc, Vc, pos, count           cache, in/out (count[b,h] <= cap on entry).
  *   t_abs                        [B] int32 absolute position of the new token.

@@ -82,7 +82,7 @@ def test_forward_argument_errors():
     assert "dk" in _msg()
     assert _fwd(dims(B=0)) == _lib.HAM_EINVAL
     assert _fwd(dims(io_dtype=3)) == _lib.HAM_EUNSUPPORTED
-    assert _fwd(dims(flags=8)) == _lib.HAM_EUNSUPPORTED
+    assert _fwd(dims(flags=16)) == _lib.HAM_EUNSUPPORTED
     assert _fwd(dims(scale=0.0)) == _lib.HAM_EINVAL and "scale" in _msg()
     assert _fwd(dims(scale=-1.0)) == _lib.HAM_EINVAL
     # required pointers: q k v (0-2), beta g tau (6-8), S_out (13), o (14), Kc Vc pos count (19-22)
