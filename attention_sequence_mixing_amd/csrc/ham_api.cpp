@@ -3,6 +3,7 @@
 // caller's stream; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -65,9 +66,36 @@ int check_dims(const ham_dims* d, bool need_T) {
     if (e_ != hipSuccess) return fail(HAM_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+bool use_chunked(const ham_dims* d) {
+  return !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
+         ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv);
+}
+
+// Segments of the chunked state pass.  Its workgroups (one per 64 state columns of a
+// head) walk the chunks in order, one per CU; with few heads most CUs would idle, so
+// the chunk sequence is cut into segments that run side by side: each segment's
+// zero-start state B_p and transition A_p (the same pass with V = 0 from S = I), the
+// entering states S_in[p+1] = A_p S_in[p] + B_p, then the full pass per segment.  Used
+// when the heads' column blocks fill at most half the CUs and every segment keeps at
+// least 8 chunks.
+struct SegPlan {
+  int nseg, per;        // segments, chunks per segment (the last may hold fewer)
+};
+SegPlan seg_plan(const ham_dims* d) {
+  const int nchunk = (d->T + ham::kChunk - 1) / ham::kChunk;
+  if (!use_chunked(d)) return {1, nchunk};
+  const long long nwg = (long long)d->B * d->H * (d->dv / 64);
+  if (nwg > 128) return {1, nchunk};
+  const long long p = std::max<long long>(1, std::min<long long>(256 / nwg, nchunk / 8));
+  const int per = (int)((nchunk + p - 1) / p);
+  return {(nchunk + per - 1) / per, per};                  // every segment non-empty
+}
+
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
 struct FwdLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, lo, state, rope, prep, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, lo, state, rope, prep;
+  size_t seg_a, seg_b, seg_s, total;
+  SegPlan seg;
 };
 
 FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
@@ -86,7 +114,12 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
   L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (d->dk / 2) * sizeof(float2)) : 0;
   L.prep = off;
-  if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += BH * nchunk * ham::kPrepRecordBytes;
+  if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += up256(BH * nchunk * ham::kPrepRecordBytes);
+  L.seg = seg_plan(d);
+  const size_t P = (size_t)L.seg.nseg;
+  L.seg_a = off;       off += P > 1 ? up256((P - 1) * BH * d->dk * d->dk * sizeof(float)) : 0;
+  L.seg_b = off;       off += P > 1 ? up256((P - 1) * BH * d->dk * d->dv * sizeof(float)) : 0;
+  L.seg_s = off;       off += P > 1 ? up256(P * BH * d->dk * d->dv * sizeof(float)) : 0;
   L.total = off;
   return L;
 }
@@ -148,14 +181,35 @@ T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws)
 
 // The RNN pass shared by ham_forward and ham_route_stats; returns the slice count.
 // Two timer stages: the chunk prep (empty on the token-serial path) and the state pass.
-int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slices, CallTimer& tm) {
-  const bool chunked = !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
-                       ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv);
-  if (chunked) {
+int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slices, CallTimer& tm,
+            const FwdLayout& L, void* ws) {
+  if (use_chunked(d)) {
     *slices = ham::rnn_chunked_slices(d->dv);
     HAM_HIP(ham::launch_rnn_chunked_prep(d->io_dtype, d->dk, ra, s));
     tm.mark();
-    HAM_HIP(ham::launch_rnn_chunked_state(d->io_dtype, d->dk, d->dv, ra, s));
+    const int P = L.seg.nseg, per = L.seg.per;
+    if (P == 1) {
+      HAM_HIP(ham::launch_rnn_chunked_state(d->io_dtype, d->dk, d->dv, ra, s));
+    } else {
+      const size_t BH = (size_t)d->B * d->H;
+      float* Am = at<float>(ws, L.seg_a);
+      float* Bm = at<float>(ws, L.seg_b);
+      float* Sin = at<float>(ws, L.seg_s);
+      // zero-start states and transitions of segments 0 .. P-2
+      ham::RnnArgs rb = ra;
+      rb.S0 = nullptr; rb.S_out = Bm; rb.o_rnn32 = nullptr;
+      rb.seg_chunks = per; rb.seg_stride = BH * d->dk * d->dv;
+      HAM_HIP(ham::launch_rnn_chunked_state_seg(d->io_dtype, d->dk, d->dv, 1, P - 1, rb, s));
+      ham::RnnArgs rh = rb;
+      rh.S_out = Am; rh.seg_stride = BH * d->dk * d->dk;
+      HAM_HIP(ham::launch_rnn_chunked_state_seg(d->io_dtype, d->dk, d->dk, 2, P - 1, rh, s));
+      ham::SegArgs sg{ra.S0, Am, Bm, Sin, d->B, d->H, P};
+      HAM_HIP(ham::launch_seg_combine(d->dk, d->dv, sg, s));
+      // the full pass, every segment from its entering state
+      ham::RnnArgs rf = ra;
+      rf.S0 = Sin; rf.seg_chunks = per; rf.seg_stride = BH * d->dk * d->dv;
+      HAM_HIP(ham::launch_rnn_chunked_state_seg(d->io_dtype, d->dk, d->dv, 0, P, rf, s));
+    }
   } else {
     *slices = ham::rnn_recurrent_slices(d->dv);
     tm.mark();
@@ -224,7 +278,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   // with learned-router scores the RNN's score partials are computed and left unused
   ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, at<char>(ws, L.prep), d->B, d->T, d->H};
   int slices = 0;
-  rc = run_rnn(d, ra, s, &slices, tm);
+  rc = run_rnn(d, ra, s, &slices, tm, L, ws);
   if (rc != HAM_OK) return rc;
 
   ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
@@ -349,7 +403,7 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   ham::RnnArgs ra{q ? q : k, k, v, beta, g, S0, S_tmp, nullptr, score, at<char>(ws, L.prep),
                   d->B, d->T, d->H};
   int slices = 0;
-  rc = run_rnn(d, ra, s, &slices, tm);
+  rc = run_rnn(d, ra, s, &slices, tm, L, ws);
   if (rc != HAM_OK) return rc;
   ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count, nullptr, count_in,
                     d->B, d->T, d->H, nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};

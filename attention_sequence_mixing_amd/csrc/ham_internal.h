@@ -24,6 +24,21 @@ struct RnnArgs {
   float4* score;        // [B,T,H][slices]
   void* prep;           // chunked path: per-chunk records [B*H][nchunk][kPrepRecordBytes]
   int B, T, H;
+  // chunked state pass over segments of the chunk sequence (0: one segment).  Segment p
+  // covers chunks [p*seg_chunks, (p+1)*seg_chunks), starts from S0 + p*seg_stride and
+  // ends in S_out + p*seg_stride (full pass: only the last segment stores S_out there).
+  int seg_chunks;
+  size_t seg_stride;
+};
+
+// Entering states of the segments of a segmented state pass: S_in[0] = S0 (or 0),
+// S_in[p+1] = A_p S_in[p] + B_p, with A_p [dk x dk] and B_p [dk x dv] per head.
+struct SegArgs {
+  const float* S0;      // [B,H,dk,dv] or null
+  const float* A;       // [P-1][B,H,dk,dk]
+  const float* Bm;      // [P-1][B,H,dk,dv]
+  float* S_in;          // [P][B,H,dk,dv]
+  int B, H, P;
 };
 
 // Bytes of one chunk record written by the chunked path's prep kernel.
@@ -139,6 +154,11 @@ int rnn_recurrent_slices(int dv);
 // chunked path: prep (per-chunk records, chunks in parallel), then the state pass
 hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t s);
 hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
+// Segmented state pass: mode 0 full (scores, readout when o_rnn32 is set), 1 final
+// state only, 2 homogeneous (V = 0, S0 = I, dv = dk: the segment's transition).
+hipError_t launch_rnn_chunked_state_seg(int io, int dk, int dv, int mode, int nseg, const RnnArgs& a,
+                                        hipStream_t s);
+hipError_t launch_seg_combine(int dk, int dv, const SegArgs& a, hipStream_t s);
 int rnn_chunked_slices(int dv);
 bool rnn_chunked_supported(int io, int dk, int dv);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

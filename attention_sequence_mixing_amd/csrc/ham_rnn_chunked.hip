@@ -435,8 +435,14 @@ struct ChunkLayout {
   HAM_DEVICE static int swz(int r, int c, int rowbytes, int nch) { return r * rowbytes + ((c ^ (r & (nch - 1))) << 4); }
 };
 
-template <int DK, int DV, int NW, bool RO>
+// MODE 0: the full pass (score partials; readout when RO).  MODE 1: the final state
+// only.  MODE 2: the homogeneous pass (V = 0 from S0 = I, DV = DK), whose final
+// "state" is the product of the chunk transitions of a segment.  With a.seg_chunks
+// set, the grid covers several segments of the chunk sequence (see RnnArgs).
+template <int DK, int DV, int NW, bool RO, int MODE>
 __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
+  static_assert(MODE == 0 || !RO, "the readout belongs to the full pass");
+  static_assert(MODE != 2 || DK == DV, "the transition is dk x dk");
   using LY = ChunkLayout<DK, NW>;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
@@ -455,7 +461,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // chunk records).
   constexpr int NCB = DV / (16 * NW);                       // column blocks per head
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int cb = lin % NCB, bh = lin / NCB;
+  const int cb = lin % NCB, rest = lin / NCB;
+  const int bh = rest % (a.B * a.H), seg = rest / (a.B * a.H);
   const int h = bh % a.H, b = bh / a.H;
   const int colbase = cb * 16 * NW;
   const int col = colbase + wave * 16 + n;
@@ -468,18 +475,21 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   auto srow = [&](int mt, int i) { return 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i; };
   f32x4 S[MT];
   const size_t sbase = (size_t)bh * DK * DV;
+  const size_t soff = (size_t)seg * a.seg_stride;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[mt][i] = 0.f;
-  if (a.S0) {
+    for (int i = 0; i < 4; ++i) S[mt][i] = (MODE == 2 && srow(mt, i) == col) ? 1.f : 0.f;
+  if (MODE != 2 && a.S0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[mt][i] = a.S0[sbase + (size_t)srow(mt, i) * DV + col];
+      for (int i = 0; i < 4; ++i) S[mt][i] = a.S0[soff + sbase + (size_t)srow(mt, i) * DV + col];
   }
 
   const int nchunk = (a.T + kC - 1) / kC;
+  const int c_begin = a.seg_chunks ? seg * a.seg_chunks : 0;
+  const int c_end = a.seg_chunks ? min(nchunk, c_begin + a.seg_chunks) : nchunk;
   const char* recs = static_cast<const char*>(a.prep) + (size_t)bh * nchunk * kPrepRecordBytes;
   const char* kbase = static_cast<const char*>(a.k);
   const char* qbase = static_cast<const char*>(a.q);
@@ -528,11 +538,13 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + ko), dst + LY::OFF_K + blk, 16, 0, 0);
       if (RO) __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qc + ko), dst + LY::OFF_Q + blk, 16, 0, 0);
     }
+    if (MODE != 2) {
 #pragma unroll
     for (int j = 0; j < LY::VI; ++j) {
       const uint32_t vo = full ? voff[j] : v_off(j, a.T - 1 - t0);
       const int blk = (wave + NW * j) * 1024;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
+    }
     }
     }
     if (part & 2) {
@@ -561,8 +573,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
     __syncthreads();                          // ... for every wave; the other stage is free
     // this lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads)
-    u32x2 vraw[4];
-    {
+    u32x2 vraw[4] = {};
+    if (MODE != 2) {
       const char* Vs = stg + LY::OFF_V;
       const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
 #pragma unroll
@@ -577,7 +589,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       f[3] = __uint_as_float(vraw[mt][1] & 0xffff0000u);
       return f;
     };
-    if (c + 1 < nchunk) issue_chunk(c + 1, nxt, 1);   // the next chunk's tiles
+    if (c + 1 < c_end) issue_chunk(c + 1, nxt, 1);    // the next chunk's tiles
     const char* Ks = stg + LY::OFF_K;
     const char* Qs = stg + LY::OFF_Q;
     const char* rec = stg + LY::OFF_R;
@@ -629,7 +641,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
     }
-    if (c + 1 < nchunk) issue_chunk(c + 1, nxt, 2);   // the next chunk's record
+    if (c + 1 < c_end) issue_chunk(c + 1, nxt, 2);    // the next chunk's record
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
@@ -696,11 +708,18 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         for (int s = 0; s <= (mt >> 1); ++s) {
           const int pi = pair_index(mt, s);
           if (pair_is_half(pi)) {
-            const bf16x4 qh = as4(QKfh[(half_slot(pi) * 2 + 0) * kWave + lane]);
-            const bf16x4 qm = as4(QKfh[(half_slot(pi) * 2 + 1) * kWave + lane]);
-            O[mt] = mf16(qm, lo4(dB[s][0]), O[mt]);
-            O[mt] = mf16(qh, lo4(dB[s][1]), O[mt]);
-            O[mt] = mf16(qh, lo4(dB[s][0]), O[mt]);
+            // the pair's 16 nonzero columns in k-slots 0..3 of a 32-wide step.  Not the
+            // 16x16x16 product: O[2] takes it right after the (2,0) pair's 16x16x32
+            // products on the same accumulator, and that back-to-back pairing of the two
+            // shapes gave wrong rows 4g, 4g+1 (g = 0, 1) of the tile at d_k = 64 in some
+            // builds; with one shape throughout, every build checked gives exact rows.
+            const u32x2 qh2 = QKfh[(half_slot(pi) * 2 + 0) * kWave + lane];
+            const u32x2 qm2 = QKfh[(half_slot(pi) * 2 + 1) * kWave + lane];
+            const bf16x8 qh = as8(u32x4{qh2[0], qh2[1], 0u, 0u});
+            const bf16x8 qm = as8(u32x4{qm2[0], qm2[1], 0u, 0u});
+            O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
+            O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
+            O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
           } else {
             const bf16x8 qh = as8(QKf[(full_slot(pi) * 2 + 0) * kWave + lane]);
             const bf16x8 qm = as8(QKf[(full_slot(pi) * 2 + 1) * kWave + lane]);
@@ -713,7 +732,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 
     // ---- score partials of this 16-column slice, and the readout ----
     const bool full = nvalid == kC;
-    {
+    if (MODE == 0) {
       float xpv[16], xpp[16], xvv[16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -782,15 +801,61 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
   };
 
-  issue_chunk(0, stage0, 3);
-  for (int c = 0; c < nchunk; c += 2) {
+  issue_chunk(c_begin, stage0, 3);
+  for (int c = c_begin; c < c_end; c += 2) {
     chunk_step(c, stage0, stage1);
-    if (c + 1 < nchunk) chunk_step(c + 1, stage1, stage0);
+    if (c + 1 < c_end) chunk_step(c + 1, stage1, stage0);
   }
+  // the full pass stores the state after the last chunk (its last segment only); the
+  // partial passes store each segment's result in its own block
+  if (MODE != 0 || c_end == nchunk) {
+    float* so = a.S_out + (MODE != 0 ? soff : 0) + sbase;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a.S_out[sbase + (size_t)srow(mt, i) * DV + col] = S[mt][i];
+      for (int i = 0; i < 4; ++i) so[(size_t)srow(mt, i) * DV + col] = S[mt][i];
+  }
+}
+
+// S_in of every segment: grid (DV/16, H, B), 256 threads; a workgroup carries 16
+// state columns of one head through the segments (S_in[p+1] = A_p S_in[p] + B_p in
+// fp32), each thread 8 of the dk x 16 entries.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
+  __shared__ float Sc[DK][16];
+  constexpr int PER = DK * 16 / 256;          // entries per thread: one row, PER columns
+  const int tid = threadIdx.x;
+  const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.H + h;
+  const int row = tid / (16 / PER), c0 = (tid % (16 / PER)) * PER;
+  const size_t BH = (size_t)a.B * a.H;
+  const size_t sb = (size_t)bh * DK * DV + (size_t)row * DV + cb * 16 + c0;
+  float cur[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) cur[j] = a.S0 ? a.S0[sb + j] : 0.f;
+  for (int p = 0; p < a.P; ++p) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) a.S_in[(size_t)p * BH * DK * DV + sb + j] = cur[j];
+    if (p + 1 == a.P) break;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) Sc[row][c0 + j] = cur[j];
+    __syncthreads();
+    const float* Ap = a.A + (size_t)p * BH * DK * DK + (size_t)bh * DK * DK + (size_t)row * DK;
+    const float* Bp = a.Bm + (size_t)p * BH * DK * DV + sb;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cur[j] = Bp[j];
+    for (int k = 0; k < DK; k += 4) {
+      const float4 ak = *reinterpret_cast<const float4*>(Ap + k);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        cur[j] = fmaf(ak.x, Sc[k][c0 + j], cur[j]);
+        cur[j] = fmaf(ak.y, Sc[k + 1][c0 + j], cur[j]);
+        cur[j] = fmaf(ak.z, Sc[k + 2][c0 + j], cur[j]);
+        cur[j] = fmaf(ak.w, Sc[k + 3][c0 + j], cur[j]);
+      }
+    }
+    __syncthreads();                          // Sc is rewritten by the next segment
+  }
 }
 template <int DK>
 hipError_t launch_prep_t(const RnnArgs& a, hipStream_t s) {
@@ -799,15 +864,21 @@ hipError_t launch_prep_t(const RnnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Four waves (64 state columns) per workgroup.
+// Four waves (64 state columns) per workgroup; nseg segments of the chunk sequence.
 template <int DK, int DV>
-hipError_t launch_state_t(const RnnArgs& a, hipStream_t s) {
+hipError_t launch_state_t(const RnnArgs& a, int mode, int nseg, hipStream_t s) {
   constexpr int NW = 4;
-  dim3 grid((DV / (16 * NW)) * a.H * a.B);
-  if (a.o_rnn32)
-    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true>), grid, dim3(64 * NW), 0, s, a);
+  dim3 grid((DV / (16 * NW)) * a.H * a.B * nseg);
+  if (mode == 0 && a.o_rnn32)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true, 0>), grid, dim3(64 * NW), 0, s, a);
+  else if (mode == 0)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false, 0>), grid, dim3(64 * NW), 0, s, a);
+  else if (mode == 1)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false, 1>), grid, dim3(64 * NW), 0, s, a);
+  else if constexpr (DK == DV)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DK, NW, false, 2>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false>), grid, dim3(64 * NW), 0, s, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -826,13 +897,28 @@ hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hipStream_t s) {
-  if (io != 1) return hipErrorInvalidValue;
-  if (dk == 64 && dv == 64) return chunked::launch_state_t<64, 64>(a, s);
-  if (dk == 64 && dv == 128) return chunked::launch_state_t<64, 128>(a, s);
-  if (dk == 128 && dv == 64) return chunked::launch_state_t<128, 64>(a, s);
-  if (dk == 128 && dv == 128) return chunked::launch_state_t<128, 128>(a, s);
+hipError_t launch_rnn_chunked_state_seg(int io, int dk, int dv, int mode, int nseg, const RnnArgs& a,
+                                        hipStream_t s) {
+  if (io != 1 || nseg < 1 || (mode == 2 && dk != dv)) return hipErrorInvalidValue;
+  if (dk == 64 && dv == 64) return chunked::launch_state_t<64, 64>(a, mode, nseg, s);
+  if (dk == 64 && dv == 128) return chunked::launch_state_t<64, 128>(a, mode, nseg, s);
+  if (dk == 128 && dv == 64) return chunked::launch_state_t<128, 64>(a, mode, nseg, s);
+  if (dk == 128 && dv == 128) return chunked::launch_state_t<128, 128>(a, mode, nseg, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hipStream_t s) {
+  return launch_rnn_chunked_state_seg(io, dk, dv, 0, 1, a, s);
+}
+
+hipError_t launch_seg_combine(int dk, int dv, const SegArgs& a, hipStream_t s) {
+  const dim3 grid(dv / 16, a.H, a.B);
+  if (dk == 64 && dv == 64) hipLaunchKernelGGL((chunked::seg_combine_kernel<64, 64>), grid, dim3(256), 0, s, a);
+  else if (dk == 64 && dv == 128) hipLaunchKernelGGL((chunked::seg_combine_kernel<64, 128>), grid, dim3(256), 0, s, a);
+  else if (dk == 128 && dv == 64) hipLaunchKernelGGL((chunked::seg_combine_kernel<128, 64>), grid, dim3(256), 0, s, a);
+  else if (dk == 128 && dv == 128) hipLaunchKernelGGL((chunked::seg_combine_kernel<128, 128>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace ham
