@@ -241,6 +241,47 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None):
                 stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
 
 
+def bench_long(args, dev, steps=10, warmup=10):
+    """The long-context forward (B=1, H=16, T=32768, planted pairs, rho = 0.25): with 16
+    heads the chunked state pass runs in segments side by side."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    from attention_sequence_mixing_amd.inputs import LONG, make_workload, tau_for_rho
+    w = LONG
+    inp = make_workload(w)
+    t = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    st = ham.ham_route_stats(t["k"], t["v"], t["beta"], t["g"],
+                             torch.full((w.H,), float("inf"), device=dev), want_rho=False)
+    tau = torch.from_numpy(tau_for_rho(st["e"].cpu().numpy(), w.rho)).to(dev)
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale)
+
+    def step():
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stages = collect_stages(lib, steps)
+    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
+    rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
+    log(f"[bench] long context: {ms:.3f} ms/step, stages {dict(zip(names, [round(x, 4) for x in stages]))}")
+    return dict(workload=w.name, ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                rho_measured=round(rho, 6), steps=steps, warmup=warmup,
+                stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
+
+
 def bench_router(args, dev, w, t):
     """The same layer routed by learned-router scores (synthetic sigmoid(N(0,1)) per
     token-head, as inputs.make_router_scores draws them): the threshold for the target
@@ -407,6 +448,7 @@ def main():
     for s in res["stages"]:
         log(f"[bench] stage {s['stage']:10s} {s['ms']:8.3f} ms  {s['achieved']:9.1f} {s['unit']} "
             f"({100 * s['frac']:.1f}% of {s['peak']})")
+    long_ctx = None if args.main_only else bench_long(args, dev)
     dec = None
     if not args.no_decode:
         dec = bench_decode(args, dev)
@@ -441,6 +483,7 @@ def main():
         "learned_router": res["router"],
         "rope": res["rope"],
         "packed_docs": res["packed"],
+        "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
             "us_per_step": round(dec["us_per_step"], 2), "tokens_per_s": round(dec["tokens_per_s"], 1),
