@@ -817,19 +817,21 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   }
 }
 
-// S_in of every segment: grid (DV/16, H, B), 256 threads; a workgroup carries 16
-// state columns of one head through the segments (S_in[p+1] = A_p S_in[p] + B_p in
-// fp32), each thread 8 of the dk x 16 entries.
+// S_in of every segment: grid (DV/4, H, B), 256 threads; a workgroup carries 4 state
+// columns of one head through the segments (S_in[p+1] = A_p S_in[p] + B_p in fp32;
+// every step needs all dk rows of the previous one, so a head's columns split over
+// workgroups and its rows do not), each thread DK/64 of the dk x 4 entries.
+constexpr int kSegCols = 4;
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
-  __shared__ float Sc[DK][16];
-  constexpr int PER = DK * 16 / 256;          // entries per thread: one row, PER columns
+  __shared__ float Sc[DK][kSegCols];
+  constexpr int PER = DK * kSegCols / 256;    // entries per thread: one row, PER columns
   const int tid = threadIdx.x;
   const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.H + h;
-  const int row = tid / (16 / PER), c0 = (tid % (16 / PER)) * PER;
+  const int row = tid / (kSegCols / PER), c0 = (tid % (kSegCols / PER)) * PER;
   const size_t BH = (size_t)a.B * a.H;
-  const size_t sb = (size_t)bh * DK * DV + (size_t)row * DV + cb * 16 + c0;
+  const size_t sb = (size_t)bh * DK * DV + (size_t)row * DV + cb * kSegCols + c0;
   float cur[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) cur[j] = a.S0 ? a.S0[sb + j] : 0.f;
@@ -842,21 +844,26 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
     __syncthreads();
     const float* Ap = a.A + (size_t)p * BH * DK * DK + (size_t)bh * DK * DK + (size_t)row * DK;
     const float* Bp = a.Bm + (size_t)p * BH * DK * DV + sb;
+    float acc[PER][2];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) cur[j] = Bp[j];
+    for (int j = 0; j < PER; ++j) { acc[j][0] = Bp[j]; acc[j][1] = 0.f; }
+#pragma unroll 4
     for (int k = 0; k < DK; k += 4) {
       const float4 ak = *reinterpret_cast<const float4*>(Ap + k);
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        cur[j] = fmaf(ak.x, Sc[k][c0 + j], cur[j]);
-        cur[j] = fmaf(ak.y, Sc[k + 1][c0 + j], cur[j]);
-        cur[j] = fmaf(ak.z, Sc[k + 2][c0 + j], cur[j]);
-        cur[j] = fmaf(ak.w, Sc[k + 3][c0 + j], cur[j]);
+        acc[j][0] = fmaf(ak.x, Sc[k][c0 + j], acc[j][0]);
+        acc[j][1] = fmaf(ak.y, Sc[k + 1][c0 + j], acc[j][1]);
+        acc[j][0] = fmaf(ak.z, Sc[k + 2][c0 + j], acc[j][0]);
+        acc[j][1] = fmaf(ak.w, Sc[k + 3][c0 + j], acc[j][1]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cur[j] = acc[j][0] + acc[j][1];
     __syncthreads();                          // Sc is rewritten by the next segment
   }
 }
+
 template <int DK>
 hipError_t launch_prep_t(const RnnArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kC - 1) / kC;
@@ -912,7 +919,7 @@ hipError_t launch_rnn_chunked_state(int io, int dk, int dv, const RnnArgs& a, hi
 }
 
 hipError_t launch_seg_combine(int dk, int dv, const SegArgs& a, hipStream_t s) {
-  const dim3 grid(dv / 16, a.H, a.B);
+  const dim3 grid(dv / chunked::kSegCols, a.H, a.B);
   if (dk == 64 && dv == 64) hipLaunchKernelGGL((chunked::seg_combine_kernel<64, 64>), grid, dim3(256), 0, s, a);
   else if (dk == 64 && dv == 128) hipLaunchKernelGGL((chunked::seg_combine_kernel<64, 128>), grid, dim3(256), 0, s, a);
   else if (dk == 128 && dv == 64) hipLaunchKernelGGL((chunked::seg_combine_kernel<128, 64>), grid, dim3(256), 0, s, a);
