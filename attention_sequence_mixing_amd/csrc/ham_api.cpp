@@ -303,7 +303,7 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
     HAM_HIP(ham::launch_doc_lo(da, s));
   }
   ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
-                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope, lo};
+                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope, use_chunked(d) ? 1 : 0, lo};
   HAM_HIP(ham::launch_attention(d->io_dtype, d->dk, d->dv, aa, s));
   tm.mark();
   return HAM_OK;

@@ -659,10 +659,35 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // Step it: tile it has landed in `cur` (wait, then barrier: every wave is also
   // done with tile it-1, whose stage `nxt` the next load overwrites); fetch tile
   // it+1 into `nxt`; consume tile it.
+  // The RNN readout rows of the block (bf16, from the chunked state pass) are copied
+  // into the stage the last tile leaves free while that tile is consumed: wave w
+  // fetches the rows of its own 32 queries, 16-byte chunks XOR-swizzled by row, so
+  // the epilogue reads them from LDS without waiting on memory.
+  constexpr int OCH = DV * 2 / 16;                         // 16-byte chunks per row
+  constexpr int OWB = BMW * DV * 2;                        // one wave's rows, bytes
+  // (not with document masks: that variant has no registers to spare for it)
+  constexpr bool kOrnnLds = !DOC && NWV * OWB <= KB + VB;  // they fit in a stage
+  const char* ornn_st = nullptr;
+  auto issue_ornn = [&](char* st) {
+    const int rstride = a.H * DV * 2;
+    const char* base = reinterpret_cast<const char*>(a.o_rnn32) + (((size_t)b * a.T + qb0) * a.H + h) * DV * 2;
+    const int range = max(0, min(a.T - qb0, BM)) * rstride;   // rows past T read zero
+#pragma unroll
+    for (int j = 0; j < OCH / 2; ++j) {
+      const int r = wave * BMW + j * (64 / OCH) + lane / OCH;
+      const int c = (lane % OCH) ^ (r & (OCH - 1));
+      buffer_to_lds(base, range, r * rstride + c * 16, st + wave * OWB + j * 1024);
+    }
+  };
   auto step = [&](int it, char* cur, char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < ntiles) issue_tile(it + 1, nxt);
+    if (it + 1 < ntiles) {
+      issue_tile(it + 1, nxt);
+    } else if (kOrnnLds && a.ornn_bf16) {
+      issue_ornn(nxt);
+      ornn_st = nxt;
+    }
     do_scores(cur);
     do_mask(it * BN);
     // the first tile is exact; with document masks, every tile in which a row meets
@@ -702,6 +727,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
+  if (kOrnnLds && ornn_st) __builtin_amdgcn_s_waitcnt(0);   // this wave's readout rows are in LDS
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l_tot = l_run[qt];                       // full row sum in every lane
@@ -713,7 +739,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     float ssk = 0.f, ssr = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 r4v = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+      f32x4 r4v;
+      if (kOrnnLds && ornn_st) {
+        // row 16 qt + n of this wave's rows; columns dt*16 + 4g .. +3 are half of chunk 2dt + g/2
+        const int rr = 16 * qt + qn;
+        const int c = (2 * dt + (g >> 1)) ^ ((wave * BMW + rr) & (OCH - 1));
+        const u16x4 x = *reinterpret_cast<const u16x4*>(ornn_st + wave * OWB + rr * (DV * 2) + c * 16 + (g & 1) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r4v[i] = bf16_to_f32(x[i]);
+      } else if (a.ornn_bf16) {
+        const u16x4 x = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(a.o_rnn32) +
+                                                         tt * DV + dt * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r4v[i] = bf16_to_f32(x[i]);
+      } else {
+        r4v = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         okv[dt][i] = acc[qt][dt][i] * inv_l;

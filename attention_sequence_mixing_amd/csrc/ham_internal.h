@@ -20,7 +20,8 @@ struct RnnArgs {
   const float* g;
   const float* S0;      // [B,H,dk,dv] or null (zeros)
   float* S_out;         // [B,H,dk,dv]
-  float* o_rnn32;       // [B,T,H,dv] fp32 or null (no readout)
+  float* o_rnn32;       // [B,T,H,dv] fp32 (token-serial kernel) or bf16 bits (chunked state
+                        // pass, bf16 I/O only), or null (no readout)
   float4* score;        // [B,T,H][slices]
   void* prep;           // chunked path: per-chunk records [B*H][nchunk][kPrepRecordBytes]
   int B, T, H;
@@ -94,7 +95,7 @@ struct AttnArgs {
   const void* Kc;
   const void* Vc;
   const int32_t* ntok;  // [B*H][T]
-  const float* o_rnn32; // [B,T,H,dv]
+  const float* o_rnn32; // [B,T,H,dv] fp32, or bf16 bits with ornn_bf16
   const float* gate_rnn;
   const float* gate_kv;
   void* o;
@@ -104,6 +105,7 @@ struct AttnArgs {
   float eps;
   int B, T, H, cap;
   const float2* rope;   // [T][dk/2] (cos, sin) of the query rotations, or null
+  int ornn_bf16;        // o_rnn32 holds bf16 values (written by the chunked state pass)
   const int32_t* lo;    // [B*H][T] first visible cache entry per query (same-document
                         // masking: keys c in [lo, ntok) are visible), or null (0)
 };

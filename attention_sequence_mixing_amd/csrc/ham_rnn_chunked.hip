@@ -751,19 +751,21 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       if (full || s_tok < nvalid) sc[s_lane] = make_float4(pv, pp, vv, 0.f);
     }
     if (RO) {
-      float* oc = a.o_rnn32 + ((size_t)b * a.T + t0) * a.H * DV;
+      // the readout feeds the bf16 mix and the bf16 o_rnn output: stored as bf16
+      uint16_t* oc = reinterpret_cast<uint16_t*>(a.o_rnn32) + ((size_t)b * a.T + t0) * a.H * DV;
       const uint32_t rs = (uint32_t)(a.H * DV);
       if (full) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oc[o_lane + (uint32_t)(16 * mt + i) * rs] = O[mt][i];
+          for (int i = 0; i < 4; ++i) oc[o_lane + (uint32_t)(16 * mt + i) * rs] = f32_to_bf16(O[mt][i]);
       } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (16 * mt + i + 4 * g < nvalid) oc[o_lane + (uint32_t)(16 * mt + i) * rs] = O[mt][i];
+            if (16 * mt + i + 4 * g < nvalid)
+              oc[o_lane + (uint32_t)(16 * mt + i) * rs] = f32_to_bf16(O[mt][i]);
       }
     }
 
