@@ -7,14 +7,16 @@
 // Block Masks": causality by original position, padding excluded).  Because the
 // cache is in ascending original position, that set is the prefix c < n_t of the
 // cache, with n_t the number of cached tokens at positions <= t (n_t includes t
-// itself when t is routed).  Mix: o = g_rnn*rms(o_rnn) + g_kv*rms(o_kv) (§2
-// headwise norm and gated sum; App. A.1 headwise gating).
+// itself when t is routed).  With same-document masking (App. A.1 "FlexAttention
+// and Block Masks", packed batches) the visible set is cut to keys of t's own document,
+// which is the cache range [lo_t, n_t).  Mix: o = g_rnn*rms(o_rnn) +
+// g_kv*rms(o_kv) (§2 headwise norm and gated sum; App. A.1 headwise gating).
 //
 // Each wave computes S^T = K Q^T on 16x16 MFMA tiles (keys on rows), so the
 // per-query softmax state lives in the lanes that later hold that query's output
 // column of O^T = V^T P^T: no data movement between the two products.  bf16 I/O
 // (attn_bf16_v5_kernel): 4 waves x 32 queries of one (b,h) per workgroup on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  fp32 I/O (attn_kernel): 4
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  fp32 I/O (attn_f32_kernel): 4
 // waves x 16 queries on v_mfma_f32_16x16x4f32.
 #include "ham_common.h"
 #include "ham_internal.h"
@@ -23,25 +25,9 @@ namespace ham {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <class IO>
-struct AttnTile;
-template <>
-struct AttnTile<IoBF16> { static constexpr int BN = 64; };
-template <>
-struct AttnTile<IoF32> { static constexpr int BN = 32; };
-
-template <class IO, int DK, int DV>
-struct AttnSmem;
+// LDS tile of the fp32 kernel: BN cache rows of K and V, rows padded by 4 floats.
 template <int DK, int DV>
-struct AttnSmem<IoBF16, DK, DV> {
-  static constexpr int BN = 64;
-  static constexpr int KS = DK + 8;   // K row stride (elements), padded
-  static constexpr int VS = BN + 8;   // V^T row stride (elements), padded
-  uint16_t K[BN * KS];
-  uint16_t Vt[DV * VS];
-};
-template <int DK, int DV>
-struct AttnSmem<IoF32, DK, DV> {
+struct AttnSmemF32 {
   static constexpr int BN = 32;
   static constexpr int KS = DK + 4;
   static constexpr int VS = DV + 4;
@@ -52,31 +38,9 @@ struct AttnSmem<IoF32, DK, DV> {
 // Stage rows [c0, c0+BN) of this head's cache into LDS; rows at or beyond nmax
 // are zero so masked lanes multiply finite values.
 template <int DK, int DV>
-HAM_DEVICE void stage_kv(AttnSmem<IoBF16, DK, DV>& sm, const uint16_t* Kh, const uint16_t* Vh,
+HAM_DEVICE void stage_kv(AttnSmemF32<DK, DV>& sm, const float* Kh, const float* Vh,
                          int c0, int nmax, int tid) {
-  constexpr int BN = 64, KS = DK + 8, VS = BN + 8;
-  constexpr int KU = DK / 8, VU = DV / 8;
-#pragma unroll
-  for (int u = tid; u < BN * KU; u += 256) {
-    const int row = u / KU, col = (u % KU) * 8;
-    u16x8 x = (u16x8)(0);
-    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Kh + (size_t)(c0 + row) * DK + col);
-    *reinterpret_cast<u16x8*>(&sm.K[row * KS + col]) = x;
-  }
-#pragma unroll
-  for (int u = tid; u < BN * VU; u += 256) {
-    const int row = u / VU, col = (u % VU) * 8;
-    u16x8 x = (u16x8)(0);
-    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Vh + (size_t)(c0 + row) * DV + col);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm.Vt[(col + j) * VS + row] = x[j];
-  }
-}
-
-template <int DK, int DV>
-HAM_DEVICE void stage_kv(AttnSmem<IoF32, DK, DV>& sm, const float* Kh, const float* Vh,
-                         int c0, int nmax, int tid) {
-  constexpr int BN = 32, KS = DK + 4, VS = DV + 4;
+  constexpr int BN = AttnSmemF32<DK, DV>::BN, KS = DK + 4, VS = DV + 4;
   constexpr int KU = DK / 4, VU = DV / 4;
 #pragma unroll
   for (int u = tid; u < BN * KU; u += 256) {
@@ -94,20 +58,13 @@ HAM_DEVICE void stage_kv(AttnSmem<IoF32, DK, DV>& sm, const float* Kh, const flo
   }
 }
 
-// Query fragments: the B operand of S^T = K Q^T for this lane's query.
-template <int DK>
-struct QFragBF16 { bf16x8 x[DK / 32]; };
-template <int DK>
-struct QFragF32 { float x[DK / 4]; };
-
-template <class IO, int DK, int DV>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  using E = typename IO::elem;
-  constexpr bool kBF16 = (IO::kBytes == 2);
-  constexpr int BN = AttnTile<IO>::BN;
+// fp32 I/O: 4 waves x 16 queries of one (b,h) per workgroup, exact online softmax.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+  constexpr int BN = AttnSmemF32<DK, DV>::BN;
   constexpr int NT = BN / 16;              // 16-key subtiles per tile
   constexpr int DT = DV / 16;              // 16-wide d tiles of the output
-  __shared__ AttnSmem<IO, DK, DV> sm;
+  __shared__ AttnSmemF32<DK, DV> sm;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, qn = lane & 15;
@@ -118,9 +75,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int qb = nqb - 1 - (lin % nqb);
   const int b = bh / a.H, h = bh % a.H;
 
-  const E* __restrict__ qp = static_cast<const E*>(a.q);
-  const E* __restrict__ Kh = static_cast<const E*>(a.Kc) + (size_t)bh * a.cap * DK;
-  const E* __restrict__ Vh = static_cast<const E*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const float* __restrict__ qp = static_cast<const float*>(a.q);
+  const float* __restrict__ Kh = static_cast<const float*>(a.Kc) + (size_t)bh * a.cap * DK;
+  const float* __restrict__ Vh = static_cast<const float*>(a.Vc) + (size_t)bh * a.cap * DV;
   const int32_t* ntok = a.ntok + (size_t)bh * a.T;
 
   const int t = qb * 64 + wave * 16 + qn;           // this lane's query
@@ -139,45 +96,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int o = 1; o < 64; o <<= 1) m = min(m, __shfl_xor(m, o, kWave));
     if (lane == 0) s_lomin[wave] = m;
     __syncthreads();
-    it0 = min(min(s_lomin[0], s_lomin[1]), min(s_lomin[2], s_lomin[3])) / AttnTile<IO>::BN;
+    it0 = min(min(s_lomin[0], s_lomin[1]), min(s_lomin[2], s_lomin[3])) / BN;
   }
   const size_t tok = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
 
-  // load this lane's query fragment
-  QFragBF16<DK> qfb;
-  QFragF32<DK> qff;
-  // with a rotary table the query is turned at its position first (pairs of
-  // consecutive elements; the table row of local token t)
+  // this lane's query fragment: the B operand of S^T = K Q^T.  With a rotary
+  // table the query is turned at its position first (pairs of consecutive
+  // elements; the table row of local token t).
+  float qf[DK / 4];
   const float2* rrow = a.rope ? a.rope + (size_t)(tvalid ? t : 0) * (DK / 2) : nullptr;
-  if constexpr (kBF16) {
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      u16x8 x = (u16x8)(0);
-      if (tvalid) x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(qp) + tok * DK + ks * 32 + 8 * g);
-      if (rrow) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
-          rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
-          x[2 * j] = f32_to_bf16(x0);
-          x[2 * j + 1] = f32_to_bf16(x1);
-        }
-      }
-      qfb.x[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  } else {
-    const float* qf = reinterpret_cast<const float*>(qp) + tok * DK;
+  {
+    const float* qrow = qp + tok * DK;
 #pragma unroll
     for (int ks = 0; ks < DK / 4; ++ks) {
       const int d = ks * 4 + g;
-      float x = tvalid ? qf[d] : 0.f;
+      float x = tvalid ? qrow[d] : 0.f;
       if (rrow && tvalid) {
         // element d of pair d/2; its partner is d ^ 1
-        const float y = qf[d ^ 1];
+        const float y = qrow[d ^ 1];
         const float2 cs = rrow[d >> 1];
         x = (d & 1) ? (y * cs.y + x * cs.x) : (x * cs.x - y * cs.y);
       }
-      qff.x[ks] = x;
+      qf[ks] = x;
     }
   }
 
@@ -198,18 +138,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
       st[kt] = (f32x4)(0.f);
-      if constexpr (kBF16) {
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const u16x8 kx = *reinterpret_cast<const u16x8*>(&sm.K[(kt * 16 + qn) * (DK + 8) + ks * 32 + 8 * g]);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx), qfb.x[ks], st[kt], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < DK / 4; ++ks) {
-          const float kx = sm.K[(kt * 16 + qn) * (DK + 4) + ks * 4 + g];
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, qff.x[ks], st[kt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < DK / 4; ++ks) {
+        const float kx = sm.K[(kt * 16 + qn) * (DK + 4) + ks * 4 + g];
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, qf[ks], st[kt], 0, 0, 0);
       }
     }
     // st[kt][i] = q_t . k_c for c = c0 + kt*16 + 4g + i (this lane's query t)
@@ -242,38 +174,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
 
     // O^T += V^T P^T
-    if constexpr (kBF16) {
 #pragma unroll
-      for (int u = 0; u < NT / 2; ++u) {
-        u16x8 pb;
+    for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = f32_to_bf16(st[2 * u][i]);
-          pb[4 + i] = f32_to_bf16(st[2 * u + 1][i]);
-        }
-        const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
+      for (int i = 0; i < 4; ++i) {
+        const float* vrow = &sm.V[(kt * 16 + 4 * g + i) * (DV + 4)];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vrow = &sm.Vt[(dt * 16 + qn) * (64 + 8)];
-          const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 4 * g);
-          const u16x4 v1 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 16 + 4 * g);
-          u16x8 va;
-          va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
-          va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbf, acc[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[dt * 16 + qn], st[kt][i], acc[dt], 0, 0, 0);
       }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float* vrow = &sm.V[(kt * 16 + 4 * g + i) * (DV + 4)];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[dt * 16 + qn], st[kt][i], acc[dt], 0, 0, 0);
-        }
-    }
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
@@ -305,16 +214,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
   const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
   const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
-  E* o = static_cast<E*>(a.o);
+  float* o = static_cast<float*>(a.o);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
     const size_t off = tt * DV + dt * 16 + 4 * g;
-    IO::store4(o, off, y);
-    if (a.o_kv) IO::store4(static_cast<E*>(a.o_kv), off, okv[dt]);
-    if (a.o_rnn) IO::store4(static_cast<E*>(a.o_rnn), off, orn[dt]);
+    IoF32::store4(o, off, y);
+    if (a.o_kv) IoF32::store4(static_cast<float*>(a.o_kv), off, okv[dt]);
+    if (a.o_rnn) IoF32::store4(static_cast<float*>(a.o_rnn), off, orn[dt]);
   }
 }
 
@@ -797,25 +706,25 @@ static hipError_t launch_attn_bf16_v5(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class IO, int DK, int DV>
-static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+template <int DK, int DV>
+static hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.T + 63) / 64;
-  hipLaunchKernelGGL((attn_kernel<IO, DK, DV>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_f32_kernel<DK, DV>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s) {
-#define HAM_CASE(IOT, DKV, DVV) \
-  if (dk == DKV && dv == DVV) return launch_attn_t<IOT, DKV, DVV>(a, s);
   if (io == 0) {
-    HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+    if (dk == 64 && dv == 64) return launch_attn_f32<64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_attn_f32<64, 128>(a, s);
+    if (dk == 128 && dv == 64) return launch_attn_f32<128, 64>(a, s);
+    if (dk == 128 && dv == 128) return launch_attn_f32<128, 128>(a, s);
   } else {
     if (dk == 64 && dv == 64) return launch_attn_bf16_v5<64, 64>(a, s);
     if (dk == 64 && dv == 128) return launch_attn_bf16_v5<64, 128>(a, s);
     if (dk == 128 && dv == 64) return launch_attn_bf16_v5<128, 64>(a, s);
     if (dk == 128 && dv == 128) return launch_attn_bf16_v5<128, 128>(a, s);
   }
-#undef HAM_CASE
   return hipErrorInvalidValue;
 }
 
