@@ -69,8 +69,9 @@ def _tau_flag(tau, per_token_shape, dev):
     return 0
 
 
-def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0):
-    return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0, float(rope_base))
+def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0, route_block=0):
+    return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0, float(rope_base),
+                   int(route_block))
 
 
 class ForwardPlan:
@@ -80,14 +81,15 @@ class ForwardPlan:
     """
 
     def __init__(self, B, T, H, dk, dv, dtype, device, *, cap=None, scale=None,
-                 norm_eps=1e-6, flags=0, t0=0, rope_base=0.0, want_o_rnn=False, want_o_kv=False):
+                 norm_eps=1e-6, flags=0, t0=0, rope_base=0.0, route_block=0, want_o_rnn=False,
+                 want_o_kv=False):
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.cap = T if cap is None else cap
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
         self.dims = make_dims(B, T, H, dk, dv, self.io, self.scale, norm_eps, self.cap, flags, t0,
-                              rope_base)
+                              rope_base, route_block)
         self.shape = (B, T, H, dk, dv)
         L = _lib.lib()
         ws_bytes = L.ham_forward_workspace_size(ctypes.byref(self.dims))
@@ -149,7 +151,7 @@ class ForwardPlan:
 def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
                 t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, doc_start=None,
-                want_o_rnn=False, want_o_kv=False, stream=None):
+                route_block=0, want_o_rnn=False, want_o_kv=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
 
     tau: [H] float32 thresholds per head, or [B,T,H] per token and head (a schedule
@@ -161,8 +163,12 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
     prediction error as the routing score (tau then in the router's units).
     rope_base: 0, or the RoPE base for the attention-path query and key (the cache
     then holds rotated keys).  doc_start: None, or [B,T] int32 absolute start
-    positions of the tokens' documents (same-document masking of a packed batch).  Returns a dict with o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if
-    asked); e is the routing score used.
+    positions of the tokens' documents (same-document masking of a packed batch).
+    route_block: 0 (per-token routing), or 2..64 (a power of two) for block-contiguous
+    routing: aligned blocks route whole on their mean score and become visible from
+    their last token on; t0 and T must then be multiples of it.  Returns a dict with
+    o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if asked); e is the routing
+    score used.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -172,7 +178,7 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
         cap = cache["Kc"].shape[2]
     plan = ForwardPlan(B, T, H, dk, dv, q.dtype, q.device, cap=cap, scale=scale,
                        norm_eps=norm_eps, flags=flags, t0=t0, rope_base=rope_base,
-                       want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
+                       route_block=route_block, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     if cache is not None:
         plan.Kc = _need("Kc", cache["Kc"], (B, H, plan.cap, dk), q.dtype, q.device)
         plan.Vc = _need("Vc", cache["Vc"], (B, H, plan.cap, dv), q.dtype, q.device)
@@ -188,12 +194,16 @@ class DecodePlan:
     """Scratch and outputs for repeated ham_decode_step calls on one cache."""
 
     def __init__(self, B, H, dk, dv, cap, dtype, device, *, scale=None, norm_eps=1e-6,
-                 rope_base=0.0, want_o_rnn=False, want_o_kv=False):
+                 rope_base=0.0, route_block=0, want_o_rnn=False, want_o_kv=False):
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
-        self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap, rope_base=rope_base)
+        self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap, rope_base=rope_base,
+                              route_block=route_block)
+        # block-contiguous routing: the open block's running score sum per (b, h)
+        self.block_score = (torch.zeros((B, H), dtype=torch.float32, device=device)
+                            if route_block > 1 else None)
         self.shape = (B, H, dk, dv, cap)
         L = _lib.lib()
         ws_bytes = L.ham_decode_workspace_size(ctypes.byref(self.dims))
@@ -209,10 +219,12 @@ class DecodePlan:
 
     def __call__(self, q, k, v, beta, g, tau, S, Kc, Vc, pos, count, t_abs, *, q_attn=None,
                  k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, router_scores=None,
-                 doc_start=None, stream=None):
+                 doc_start=None, block_score=None, stream=None):
         """router_scores: None, or [B,H] float32 learned-router scores of the new tokens,
         which then replace the RNN's prediction error as the routing score.
-        doc_start: None, or [B] int32 absolute start of each new token's document."""
+        doc_start: None, or [B] int32 absolute start of each new token's document.
+        block_score: with block-contiguous routing, the [B,H] float32 running score sum
+        of the open blocks (default: the plan's own, zero at creation)."""
         B, H, dk, dv, cap = self.shape
         dev, dt = self.device, self.dtype
         for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
@@ -230,12 +242,15 @@ class DecodePlan:
         _need("t_abs", t_abs, (B,), torch.int32, dev)
         _need("router_scores", router_scores, (B, H), torch.float32, dev)
         _need("doc_start", doc_start, (B,), torch.int32, dev)
+        if block_score is None:
+            block_score = self.block_score
+        _need("block_score", block_score, (B, H), torch.float32, dev)
         self.dims.flags = (HAM_EXTERNAL_SCORES if router_scores is not None else 0) | tf
         e = router_scores if router_scores is not None else self.e
         rc = _lib.lib().ham_decode_step(
             ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
-            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start), _vp(S),
-            _vp(Kc), _vp(Vc),
+            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start),
+            _vp(block_score), _vp(S), _vp(Kc), _vp(Vc),
             _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
             _vp(e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
             _stream(stream))
@@ -245,26 +260,34 @@ class DecodePlan:
 
 def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_eps=1e-6,
                     q_attn=None, k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None,
-                    rope_base=0.0, doc_start=None, want_o_rnn=False, want_o_kv=False, stream=None):
+                    rope_base=0.0, doc_start=None, route_block=0, want_o_rnn=False, want_o_kv=False,
+                    stream=None):
     """One decode step: q, k, v [B,H,d]; tau [H] or [B,H]; S and cache (dict Kc, Vc, pos, count) are
     updated in place; t_abs [B] int32 positions (also the RoPE positions when
-    rope_base > 0).  Returns dict(o, e, routed, status, ...)."""
+    rope_base > 0).  With route_block > 1 the cache dict also carries the open
+    blocks' score sums as cache["block_score"] ([B,H] float32, added as zeros if
+    missing).  Returns dict(o, e, routed, status, ...)."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     cap = cache["Kc"].shape[2]
     plan = DecodePlan(B, H, dk, dv, cap, q.dtype, q.device, scale=scale, norm_eps=norm_eps,
-                      rope_base=rope_base, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
+                      rope_base=rope_base, route_block=route_block, want_o_rnn=want_o_rnn,
+                      want_o_kv=want_o_kv)
+    if route_block > 1 and "block_score" not in cache:
+        cache["block_score"] = plan.block_score
     plan(q, k, v, beta, g, tau, S, cache["Kc"], cache["Vc"], cache["pos"], cache["count"], t_abs,
          q_attn=q_attn, k_attn=k_attn, v_attn=v_attn, gate_rnn=gate_rnn, gate_kv=gate_kv,
-         doc_start=doc_start, stream=stream)
+         doc_start=doc_start, block_score=cache.get("block_score") if route_block > 1 else None,
+         stream=stream)
     return dict(o=plan.o, o_rnn=plan.o_rnn, o_kv=plan.o_kv, e=plan.e, routed=plan.routed,
                 status=plan.status)
 
 
 def ham_route_stats(k, v, beta, g, tau, *, q=None, S0=None, near_band=1e-5, want_rho=True,
-                    force_recurrent=False, stream=None):
+                    force_recurrent=False, route_block=0, stream=None):
     """Routing only (RNN scores, threshold, counts).  Returns dict(e, routed, count,
-    n_near, rho); rho is None unless want_rho (which waits for the stream)."""
+    n_near, rho); rho is None unless want_rho (which waits for the stream).  With
+    route_block > 1 (block-contiguous routing) n_near is not computed (None)."""
     B, T, H, dk = k.shape
     dv = v.shape[-1]
     dev, dt = k.device, k.dtype
@@ -275,14 +298,14 @@ def ham_route_stats(k, v, beta, g, tau, *, q=None, S0=None, near_band=1e-5, want
     tf = _tau_flag(tau, (B, T, H), dev)
     _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
     dims = make_dims(B, T, H, dk, dv, io, 1.0, 1e-6, max(T, 1),
-                     (HAM_FORCE_RECURRENT if force_recurrent else 0) | tf)
+                     (HAM_FORCE_RECURRENT if force_recurrent else 0) | tf, route_block=route_block)
     L = _lib.lib()
     ws_bytes = L.ham_route_stats_workspace_size(ctypes.byref(dims))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     e = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     routed = torch.empty((B, T, H), dtype=torch.uint8, device=dev)
     count = torch.empty((B, H), dtype=torch.int32, device=dev)
-    n_near = torch.empty((H,), dtype=torch.int64, device=dev)
+    n_near = torch.empty((H,), dtype=torch.int64, device=dev) if route_block <= 1 else None
     rho = ctypes.c_double(float("nan"))
     rc = L.ham_route_stats(ctypes.byref(dims), _vp(q), _vp(k), _vp(v), _vp(beta), _vp(g), _vp(tau),
                            _vp(S0), _vp(e), _vp(routed), _vp(count), _vp(n_near),

@@ -27,7 +27,7 @@ class HamDims(ctypes.Structure):
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("io_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
                 ("cap", ctypes.c_int), ("flags", ctypes.c_int), ("t0", ctypes.c_int),
-                ("rope_base", ctypes.c_float)]
+                ("rope_base", ctypes.c_float), ("route_block", ctypes.c_int)]
 
 
 class HamError(RuntimeError):
@@ -63,7 +63,7 @@ def lib():
     L.ham_forward.restype = I
     L.ham_forward.argtypes = [D] + [P] * 24 + [Z, P]
     L.ham_decode_step.restype = I
-    L.ham_decode_step.argtypes = [D] + [P] * 25 + [Z, P]
+    L.ham_decode_step.argtypes = [D] + [P] * 26 + [Z, P]
     L.ham_route_stats.restype = I
     L.ham_route_stats.argtypes = [D] + [P] * 11 + [ctypes.c_float, P, P, Z, P]
     L.ham_select_tau.restype = I

@@ -51,6 +51,12 @@ int check_dims(const ham_dims* d, bool need_T) {
   if (d->t0 < 0) return fail(HAM_EINVAL, "t0 must be >= 0");
   if (!std::isfinite(d->rope_base) || d->rope_base < 0.f)
     return fail(HAM_EINVAL, "rope_base must be 0 (none) or a finite positive base");
+  if (d->route_block < 0 || d->route_block > ham::kChunk || (d->route_block & (d->route_block - 1)))
+    return fail(HAM_EUNSUPPORTED, "route_block must be 0, 1 or a power of two up to %d (route_block=%d)",
+                ham::kChunk, d->route_block);
+  if (need_T && d->route_block > 1 && (d->t0 % d->route_block || d->T % d->route_block))
+    return fail(HAM_EINVAL, "with route_block=%d, t0 (%d) and T (%d) must be multiples of it (whole blocks)",
+                d->route_block, d->t0, d->T);
   const double elems = (double)d->B * (need_T ? d->T : 1) * d->H * (d->dk > d->dv ? d->dk : d->dv);
   if (elems > 9.0e15) return fail(HAM_EINVAL, "problem too large");
   return HAM_OK;
@@ -65,6 +71,9 @@ int check_dims(const ham_dims* d, bool need_T) {
     hipError_t e_ = (expr);                                                             \
     if (e_ != hipSuccess) return fail(HAM_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+
+// block size of block-contiguous routing, or 0 for per-token routing
+int route_blk(const ham_dims* d) { return d->route_block > 1 ? d->route_block : 0; }
 
 bool use_chunked(const ham_dims* d) {
   return !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
@@ -223,7 +232,7 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
 
 extern "C" {
 
-int ham_version(void) { return 10100; }
+int ham_version(void) { return 10200; }
 
 const char* ham_last_error(void) { return g_err.c_str(); }
 
@@ -283,7 +292,8 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
 
   ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
                     (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H,
-                    ext ? e : nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
+                    ext ? e : nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d), nullptr,
+                    nullptr};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
 
@@ -292,14 +302,15 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   if (rope) HAM_HIP(ham::launch_rope_table(rope, nullptr, d->t0, d->T, d->dk, (double)d->rope_base, s));
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
                       Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap,
-                      rope};
+                      rope, route_blk(d)};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
 
   // same-document masking: each query's first visible cache entry
   int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
   if (lo) {
-    ham::DocLoArgs da{doc_start, ntok, count_in, nullptr, pos, lo, d->t0, d->B, d->T, d->H, d->cap};
+    ham::DocLoArgs da{doc_start, ntok, count_in, count, pos, lo, d->t0, d->B, d->T, d->H, d->cap,
+                      route_blk(d)};
     HAM_HIP(ham::launch_doc_lo(da, s));
   }
   ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
@@ -313,7 +324,7 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
                     const void* q_attn, const void* k_attn, const void* v_attn,
                     const float* beta, const float* g, const float* tau,
                     const float* gate_rnn, const float* gate_kv, const int32_t* doc_start,
-                    float* S, void* Kc, void* Vc, int32_t* pos, int32_t* count,
+                    float* block_score, float* S, void* Kc, void* Vc, int32_t* pos, int32_t* count,
                     const int32_t* t_abs, void* o, void* o_rnn, void* o_kv,
                     float* e, uint8_t* routed, int32_t* status,
                     void* ws, size_t ws_bytes, void* stream) {
@@ -322,6 +333,7 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g);
   HAM_REQUIRE(tau); HAM_REQUIRE(S); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos);
   HAM_REQUIRE(count); HAM_REQUIRE(t_abs); HAM_REQUIRE(o);
+  if (route_blk(d)) HAM_REQUIRE(block_score);
   HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
   HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
   HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
@@ -346,7 +358,7 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   tm.mark();
   ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, ext ? nullptr : e_buf, r_buf,
                     chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr,
-                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
+                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d), block_score, t_abs};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   // rotary table of the new tokens' positions t_abs[b] (key and query rotations)
@@ -354,12 +366,12 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   if (rope) HAM_HIP(ham::launch_rope_table(rope, t_abs, 0, d->B, d->dk, (double)d->rope_base, s));
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
                       Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap,
-                      rope};
+                      rope, route_blk(d)};
   HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
   tm.mark();
   int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
   if (lo) {
-    ham::DocLoArgs dl{doc_start, nullptr, nullptr, count, pos, lo, 0, d->B, 1, d->H, d->cap};
+    ham::DocLoArgs dl{doc_start, nullptr, nullptr, count, pos, lo, 0, d->B, 1, d->H, d->cap, 0};
     HAM_HIP(ham::launch_doc_lo(dl, s));
   }
   ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
@@ -387,6 +399,8 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   HAM_REQUIRE(count);
   HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(S0); HAM_ALIGNED(ws);
   if (n_near && !(near_band >= 0.f)) return fail(HAM_EINVAL, "near_band must be >= 0");
+  if (n_near && route_blk(d))
+    return fail(HAM_EUNSUPPORTED, "n_near counts per-token scores; pass NULL with route_block > 1");
   const FwdLayout L = fwd_layout(d, true);
   if (!ws || ws_bytes < L.total)
     return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
@@ -406,7 +420,8 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   rc = run_rnn(d, ra, s, &slices, tm, L, ws);
   if (rc != HAM_OK) return rc;
   ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count, nullptr, count_in,
-                    d->B, d->T, d->H, nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0};
+                    d->B, d->T, d->H, nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d),
+                    nullptr, nullptr};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   ham::StatsArgs sa{e_buf, tau, chunk_count, count, n_near, near_band, d->B, d->T, d->H,

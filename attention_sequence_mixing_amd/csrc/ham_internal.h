@@ -58,6 +58,12 @@ struct RouteArgs {
   const float* e_in;    // [B,T,H] caller's routing scores (learned router) or null;
                         // when set, score/slices are unused and e is not written
   int tau_per_token;    // tau is [B,T,H] (a threshold schedule along the sequence)
+  // block-contiguous routing (blk > 1): whole aligned blocks of blk tokens route
+  // on their mean score.  Forward: the call covers whole blocks.  Decode (t_abs
+  // set, T = 1): blk_acc [B,H] carries the open block's score sum.
+  int blk;
+  float* blk_acc;
+  const int32_t* t_abs;
 };
 
 struct CompactArgs {
@@ -70,13 +76,14 @@ struct CompactArgs {
   void* Vc;             // [B,H,cap,dv]
   int32_t* pos;         // [B,H,cap]
   int32_t* count;       // [B,H] out
-  int32_t* ntok;        // [B*H][T] inclusive visible-key count per token, or null
+  int32_t* ntok;        // [B*H][T] visible-key count per token, or null
   int32_t* status;      // overflow flag or null
   const int32_t* t_abs; // [B] or null
   int t0;
   int B, T, H, cap;
   const float2* rope;   // (cos, sin) of the key rotations, or null: [T][dk/2] rows of the
                         // new tokens (forward), or [B][dk/2] rows at t_abs[b] (decode)
+  int blk;              // block-contiguous routing: block size (> 1), else 0
 };
 
 struct StatsArgs {
@@ -128,13 +135,14 @@ struct DecodeAttnArgs {
 // (ntok null, T = 1): the new token, after its append.
 struct DocLoArgs {
   const int32_t* doc_start; // [B,T] absolute document start per token
-  const int32_t* ntok;      // [B*H][T] inclusive visible counts, or null (decode)
+  const int32_t* ntok;      // [B*H][T] visible counts per query, or null (decode)
   const int32_t* count_in;  // [B*H] entries before this call (forward)
-  const int32_t* count;     // [B*H] entries after the append (decode)
+  const int32_t* count;     // [B*H] entries after the append (decode; forward with blk)
   const int32_t* pos;       // [B*H][cap] ascending positions
   int32_t* lo;              // [B*H][T] out
   int t0;
   int B, T, H, cap;
+  int blk;                  // block-contiguous routing: ntok is not an inclusive count
 };
 
 struct DecodeCombineArgs {

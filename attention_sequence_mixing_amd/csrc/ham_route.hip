@@ -73,10 +73,45 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         e = x[j][0].x;
       }
       const size_t tok = ((size_t)b * a.T + t0 + tl) * H + h;
-      const bool r = e > a.tau[a.tau_per_token ? tok : (size_t)h];   // strict; NaN never routes
       if constexpr (NS > 0) a.e[tok] = e;
+      if (a.blk > 1) continue;                                       // decided per block below
+      const bool r = e > a.tau[a.tau_per_token ? tok : (size_t)h];   // strict; NaN never routes
       a.routed[tok] = (uint8_t)r;
       if (r) atomicAdd(&s_cnt[h], 1);
+    }
+  }
+  if (a.blk > 1) {
+    // Block-contiguous routing ("Hybrid Associative Memories" §7): a block routes
+    // whole on the mean of its scores, summed in token order in fp32 and scaled by
+    // 1/blk (exact, blk a power of two), against tau at its last token.
+    __syncthreads();                          // the scores stored above are visible
+    const float* es = NS > 0 ? a.e : a.e_in;
+    const float inv = 1.f / (float)a.blk;
+    if (a.t_abs) {
+      // decode (T = 1): the open block's sum carries over in blk_acc; the block is
+      // decided at its last token
+      for (int h = tid; h < H; h += 256) {
+        const size_t tok = (size_t)b * H + h;
+        const int j = (int)((unsigned)a.t_abs[b] % (unsigned)a.blk);
+        const float sum = (j == 0 ? 0.f : a.blk_acc[tok]) + es[tok];
+        a.blk_acc[tok] = sum;
+        const bool r = j == a.blk - 1 && sum * inv > a.tau[a.tau_per_token ? tok : (size_t)h];
+        a.routed[tok] = (uint8_t)r;
+        if (r) s_cnt[h] = a.blk;
+      }
+    } else {
+      // forward: the chunk holds whole blocks (t0 and T are multiples of blk)
+      const int nb = nv / a.blk;
+      for (int idx = tid; idx < nb * H; idx += 256) {
+        const int j = idx / H, h = idx - j * H;
+        const size_t tok0 = ((size_t)b * a.T + t0 + j * a.blk) * H + h;
+        float sum = 0.f;
+        for (int i = 0; i < a.blk; ++i) sum += es[tok0 + (size_t)i * H];
+        const size_t tlast = tok0 + (size_t)(a.blk - 1) * H;
+        const bool r = sum * inv > a.tau[a.tau_per_token ? tlast : (size_t)h];
+        for (int i = 0; i < a.blk; ++i) a.routed[tok0 + (size_t)i * H] = (uint8_t)r;
+        if (r) atomicAdd(&s_cnt[h], a.blk);
+      }
     }
   }
   __syncthreads();
@@ -109,7 +144,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   constexpr int VU = DV * IO::kBytes / 16;
   __shared__ int s_red[4];
   __shared__ int s_tok[kChunk];
-  __shared__ int s_cnt;
+  __shared__ int s_cnt, s_rcnt;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.H + h;
@@ -123,19 +158,36 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   __syncthreads();
   const int base = a.count_in[bh] + s_red[0] + s_red[1] + s_red[2] + s_red[3];
 
+  // Decode with block-contiguous routing: the new token joins its open block in
+  // the row count + (t_abs mod blk), past count (invisible until the block is
+  // decided); a routed block is committed at its last token.
+  const bool pend = a.blk > 1 && a.t_abs;
   if (wave == 0) {
     const int t = c * kChunk + lane;
     const bool valid = t < a.T;
     const bool r = valid && a.routed[((size_t)b * a.T + t) * a.H + h];
-    const unsigned long long bal = __ballot(r);
+    const bool w = pend ? valid : r;                     // rows written
+    const unsigned long long bal = __ballot(w);
+    const unsigned long long balr = __ballot(r);
     const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (r) s_tok[rank] = t;
-    if (a.ntok && valid) a.ntok[(size_t)bh * a.T + t] = min(a.cap, base + rank + (int)r);
-    if (lane == 0) s_cnt = __popcll(bal);
+    if (w) s_tok[rank] = t;
+    if (a.ntok && valid) {
+      // a query sees the routed tokens up to itself; with blocks, only those of the
+      // blocks that end at or before it (blocks align with the chunk's lanes)
+      int n = base + rank + (int)r;
+      if (a.blk > 1 && (lane & (a.blk - 1)) != a.blk - 1)
+        n = base + __popcll(bal & ((1ull << (lane & ~(a.blk - 1))) - 1ull));
+      a.ntok[(size_t)bh * a.T + t] = min(a.cap, n);
+    }
+    if (lane == 0) {
+      s_cnt = __popcll(bal);
+      s_rcnt = __popcll(balr);
+    }
   }
   __syncthreads();
   const int cnt = s_cnt;
   const int tpos0 = a.t_abs ? a.t_abs[b] : a.t0;
+  const int slot0 = pend ? base + (int)((unsigned)tpos0 % (unsigned)a.blk) : base;
 
   const char* kb = static_cast<const char*>(a.k);
   const char* vb = static_cast<const char*>(a.v);
@@ -143,7 +195,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   char* Vb = static_cast<char*>(a.Vc);
   for (int u = tid; u < cnt * (KU + VU); u += 256) {
     const int i = u / (KU + VU), w = u % (KU + VU);
-    const int slot = base + i;
+    const int slot = slot0 + i;
     if (slot >= a.cap) continue;
     const size_t tok = ((size_t)b * a.T + s_tok[i]) * a.H + h;
     const size_t row = (size_t)bh * a.cap + slot;
@@ -188,12 +240,12 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     }
   }
   for (int i = tid; i < cnt; i += 256) {
-    const int slot = base + i;
+    const int slot = slot0 + i;
     if (slot < a.cap) a.pos[(size_t)bh * a.cap + slot] = tpos0 + s_tok[i];
   }
   if (tid == 0) {
-    if (base + cnt > a.cap && a.status) *a.status = 1;
-    if (c == nchunk - 1) a.count[bh] = min(a.cap, base + cnt);
+    if (slot0 + cnt > a.cap && a.status) *a.status = 1;
+    if (c == nchunk - 1) a.count[bh] = min(a.cap, base + (pend ? (s_rcnt ? a.blk : 0) : cnt));
   }
 }
 
@@ -406,7 +458,10 @@ __global__ __launch_bounds__(256) void doc_lo_kernel(DocLoArgs a) {
   const long long ds = a.doc_start[(size_t)b * a.T + t];
   const int32_t* ph = a.pos + (size_t)bh * a.cap;
   int lo;
-  if (a.ntok) {
+  if (a.ntok && a.blk > 1) {
+    // block routing: ntok counts only decided blocks, so search the whole cache
+    lo = min(count_before(ph, a.count[bh], ds), a.ntok[(size_t)bh * a.T + t]);
+  } else if (a.ntok) {
     const int32_t* nt = a.ntok + (size_t)bh * a.T;
     const long long j = ds - (long long)a.t0;          // local index of the start
     lo = (j >= 1) ? nt[(int)min(j - 1, (long long)t)] : count_before(ph, a.count_in[bh], ds);

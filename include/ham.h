@@ -11,7 +11,8 @@
  *       o_rnn_t = S_t^T q_t                       (post-update readout)
  *   routing score ([HAM] §2 "Prediction Error as Routing Metric"; App. A.1
  *   fit-error router):  e_t = 1 - cos(S_{t-1}^T k_t, v_t)   (cos := 0 for a
- *   zero vector), token t is routed iff e_t > tau_h (strict, in fp32).
+ *   zero vector), token t is routed iff e_t > tau_h (strict, in fp32); or,
+ *   with ham_dims.route_block, whole blocks on their mean score.
  *   KV memory of routed tokens only ([HAM] §2 KV-memory equation; App. A.1
  *   causality by original position): o_kv_t = softmax_c(scale * q_t.Kc[c]) Vc
  *   over cached entries at original positions <= t; 0 if there are none.
@@ -94,6 +95,22 @@ typedef struct {
                          rotated.  Angles are formed and reduced in double
                          precision; their (cos, sin) pairs are kept as floats in
                          a workspace table and the rotation runs in float.      */
+    int route_block;  /* 0 or 1: every token is routed on its own score.  2, 4,
+                         8, 16, 32 or 64: block-contiguous routing ([HAM] §7:
+                         sending contiguous blocks of tokens to the KV cache
+                         against the random access of per-token routing).  The
+                         positions are cut into aligned blocks of route_block
+                         tokens; a block enters the cache whole when the mean
+                         of its tokens' scores (summed in token order in fp32,
+                         then scaled by 1/route_block) exceeds tau (taken at
+                         the block's last token with HAM_TAU_PER_TOKEN), else
+                         none of it does.  The decision needs the whole block,
+                         so a block becomes visible to the attention from its
+                         last token on: a query sees the cached blocks that end
+                         at or before it.  With route_block = 1 this is the
+                         per-token rule.  ham_forward and ham_route_stats take
+                         whole blocks (t0 and T multiples of route_block);
+                         ham_decode_step keeps the open block pending.        */
 } ham_dims;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -147,7 +164,8 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  * Errors: HAM_EINVAL, HAM_EUNSUPPORTED, HAM_ECAPACITY (cap < T, or with
  * HAM_CONTINUE cap < T plus the cached tokens -- that part is checked on the
  * device: appends beyond cap are dropped and count saturates at cap),
- * HAM_EWORKSPACE, HAM_EHIP.
+ * HAM_EWORKSPACE, HAM_EHIP.  With route_block > 1, t0 and T must be multiples
+ * of it (HAM_EINVAL).
  */
 int ham_forward(const ham_dims *dims,
                 const void *q, const void *k, const void *v,
@@ -186,13 +204,25 @@ size_t ham_decode_workspace_size(const ham_dims *dims);
  *   status                       int32 scalar or NULL: set to 1 (never cleared)
  *                                when a routed token found its cache full; the
  *                                append is then skipped.
+ *   block_score                  [B,H] fp32, in/out, required when
+ *                                dims->route_block > 1 (else ignored, may be
+ *                                NULL): the running score sum of each sequence's
+ *                                open block.  Block-contiguous routing in decode:
+ *                                every token of the open block is written to the
+ *                                cache row count + (t_abs mod route_block), past
+ *                                count, so it stays invisible; at the block's last
+ *                                token the block is decided and, if routed, count
+ *                                grows by route_block before that token attends.
+ *                                routed is then 1 only at the last token of a
+ *                                routed block.  A row that would land at or past
+ *                                cap is dropped and status is set.
  */
 int ham_decode_step(const ham_dims *dims,
                     const void *q, const void *k, const void *v,
                     const void *q_attn, const void *k_attn, const void *v_attn,
                     const float *beta, const float *g, const float *tau,
                     const float *gate_rnn, const float *gate_kv,
-                    const int32_t *doc_start,
+                    const int32_t *doc_start, float *block_score,
                     float *S, void *Kc, void *Vc, int32_t *pos, int32_t *count,
                     const int32_t *t_abs,
                     void *o, void *o_rnn, void *o_kv,

@@ -50,7 +50,7 @@ def _load():
         P = ctypes.c_void_p
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
-            [ctypes.c_int] * 5 + [ctypes.c_double] * 3 + [P] * 3 + [P] * 3 + [P] * 3
+            [ctypes.c_int] * 5 + [ctypes.c_double] * 3 + [ctypes.c_int] + [P] * 3 + [P] * 3 + [P] * 3
             + [P] * 2 + [P] * 5 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
@@ -71,7 +71,8 @@ def default_threads() -> int:
 
 def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=None, k_attn=None,
             v_attn=None, gate_rnn=None, gate_kv=None, mask_override=None, router_score=None,
-            S0=None, cache=None, cap=None, t0=0, doc_start=None, emit=None, threads=None):
+            S0=None, cache=None, cap=None, t0=0, doc_start=None, emit=None, route_block=0,
+            threads=None):
     """Run the oracle over all heads.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta, g: [B,T,H]; tau: [H] per head, or [B,T,H]
@@ -85,7 +86,11 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     router_score: None or [B,T,H] float32 scores of a
     learned router that replace the fit-error score (the decision is score > tau).
     emit: None or [B,T,H] bool; False skips the
-    attention readout and mix of that token (o_kv, o stay 0).  Returns a dict of float64 / int arrays:
+    attention readout and mix of that token (o_kv, o stay 0).  route_block: 0 or 1
+    (per-token routing), or n > 1 for block-contiguous routing ([HAM] §7): aligned
+    blocks of n positions route whole on float(mean of their scores) > tau at the
+    block's last token and enter the cache at that token (t0 must be a multiple of
+    n; a block still open at the end stays unrouted).  Returns a dict of float64 / int arrays:
     e, routed, o_rnn, o_kv, o, S, Kc, Vc, pos, count.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -133,7 +138,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
 
     def run(i):
         return lib.ham_oracle_forward(
-            B, T, H, dk, dv, float(scale), float(eps), float(rope_base),
+            B, T, H, dk, dv, float(scale), float(eps), float(rope_base), int(route_block),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
             _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(rs), _ptr(em),
             _ptr(t0a), _ptr(dc),
@@ -146,6 +151,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     else:
         with ThreadPoolExecutor(nthr) as ex:
             rcs = list(ex.map(run, range(nthr)))
+    if any(rc == -1 for rc in rcs):
+        raise ValueError("oracle: t0 must be a multiple of route_block")
     if any(rc != 0 for rc in rcs):
         raise RuntimeError("oracle: KV cache capacity exceeded")
     return dict(e=e, routed=routed, o_rnn=o_rnn, o_kv=o_kv, o=o, S=S, Kc=Kc, Vc=Vc,

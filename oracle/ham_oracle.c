@@ -34,6 +34,16 @@
  *              with the gated-DeltaNet decay on the whole old state, App. A.1)
  *   o_rnn_t = S_t^T q_t                                 (post-update readout, [HAM] §2
  *                                                       linear-attention equation)
+ *   Block-contiguous routing ([HAM] §7 proposes sending contiguous blocks of tokens
+ *   to the KV cache instead of single tokens; the pages give no rule, so this
+ *   reading is ours): with route_block = n > 1 the positions are cut into aligned
+ *   blocks of n tokens; at a block's last token the block's mean score,
+ *   float(sum of its e / n) compared in fp32, decides for the whole block against
+ *   tau at that last token, and the n tokens are then appended together.  Until
+ *   then they are not in the cache, so a query sees a routed block from the
+ *   block's last token on (causal: the decision reads no later token).  n = 1 is
+ *   the per-token rule.  A call starts at a block boundary; a block left open at
+ *   the end of the call stays unrouted.
  *   if routed: append (k^a_t, v^a_t, position) to this head's cache
  *   (with a rotary base b > 0 the attention-path query and key are rotated at
  *    their original positions first: RoPE, [HAM] §4 "RoPE with a base of 500K for
@@ -119,12 +129,16 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
  * they were) -- this only saves time when a few sampled tokens are checked.
  * rope_base: 0 for none, else the rotary base applied to the attention-path
  * query and key at their absolute positions (the cache then holds rotated keys).
+ * route_block: 0 or 1 for per-token routing, else the block size of
+ * block-contiguous routing (every t0[b] a multiple of it).  With mask_override,
+ * a block's decision is the override at its last token.
  * Outputs e, routed, o_rnn, o_kv, o may each be NULL.
  *
- * Returns 0, or -3 if a routed token finds the cache full (the head stops there).
+ * Returns 0, -1 if a t0[b] is not a multiple of route_block, or -3 if a routed
+ * token finds the cache full (the head stops there).
  */
 int ham_oracle_forward(int B, int T, int H, int dk, int dv,
-                       double scale, double eps, double rope_base,
+                       double scale, double eps, double rope_base, int route_block,
                        const double *q, const double *k, const double *v,
                        const double *qa, const double *ka, const double *va,
                        const double *beta, const double *g, const float *tau,
@@ -148,6 +162,10 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
     double *w = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
     double *qrot = (double *)malloc(sizeof(double) * (size_t)dk);
     int status = 0;
+    const int nb = route_block > 1 ? route_block : 1;
+    for (int b = 0; b < B; ++b)
+        if (t0[b] % nb != 0) status = -1;
+    if (status) head_end = head_begin;
 
     for (int bh = head_begin; bh < head_end; ++bh) {
         const int b = bh / H, h = bh % H;
@@ -156,6 +174,7 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
         double *Vh = Vc + (size_t)bh * cap * dv;
         int64_t *ph = pos + (size_t)bh * cap;
         int64_t n = count[bh];
+        double bsum = 0.0;                       /* score sum of the open block */
 
         for (int t = 0; t < T; ++t) {
             const size_t tok = ((size_t)b * T + t) * H + h;   /* [B,T,H] index */
@@ -173,12 +192,21 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
             /* routing score and decision (decision taken in fp32, like the GPU) */
             const double et = router_score ? (double)router_score[tok] : 1.0 - cosine(p, vt, dv);
             int r;
-            if (mask_override)
+            const int j = (int)((t0[b] + t) % nb);   /* place in its block */
+            if (j == 0) bsum = 0.0;
+            bsum += et;
+            if (j != nb - 1)
+                r = 0;                                   /* the block is still open */
+            else if (mask_override)
                 r = mask_override[tok] != 0;
             else
-                r = ((float)et > tau[tok]);
+                r = ((float)(bsum / nb) > tau[tok]);
             if (e) e[tok] = et;
-            if (routed) routed[tok] = (int8_t)r;
+            if (routed) {
+                routed[tok] = (int8_t)r;
+                if (j == nb - 1)                         /* the whole block shares it */
+                    for (int i = 1; i < nb; ++i) routed[tok - (size_t)i * H] = (int8_t)r;
+            }
 
             /* gated delta update: S = alpha*S + beta*k*(v - alpha*p)^T
              * which equals alpha*(I - beta k k^T) S + beta k v^T. */
@@ -196,16 +224,21 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                 orn[j] = acc;
             }
 
-            /* append the routed token, ascending original position */
+            /* append the routed token (with blocks: the whole block, at its last
+             * token), ascending original position */
             if (r) {
-                if (n >= cap) { status = -3; break; }
-                if (rope_base > 0.0)
-                    rope_rotate(kA + tok * dk, Kh + (size_t)n * dk, dk, (double)(t0[b] + t), rope_base);
-                else
-                    memcpy(Kh + (size_t)n * dk, kA + tok * dk, sizeof(double) * (size_t)dk);
-                memcpy(Vh + (size_t)n * dv, vA + tok * dv, sizeof(double) * (size_t)dv);
-                ph[n] = t0[b] + t;
-                n += 1;
+                for (int ta = t - (nb - 1); ta <= t; ++ta) {
+                    const size_t tk = ((size_t)b * T + ta) * H + h;
+                    if (n >= cap) { status = -3; break; }
+                    if (rope_base > 0.0)
+                        rope_rotate(kA + tk * dk, Kh + (size_t)n * dk, dk, (double)(t0[b] + ta), rope_base);
+                    else
+                        memcpy(Kh + (size_t)n * dk, kA + tk * dk, sizeof(double) * (size_t)dk);
+                    memcpy(Vh + (size_t)n * dv, vA + tk * dv, sizeof(double) * (size_t)dv);
+                    ph[n] = t0[b] + ta;
+                    n += 1;
+                }
+                if (status) break;
             }
 
             if (emit && !emit[tok]) {

@@ -110,13 +110,13 @@ def test_decode_and_stats_argument_errors():
     L = _lib.lib()
     P = ctypes.c_void_p
     fake = P(1 << 20)
-    a = [fake] * 25
-    a[16] = None                                       # count
+    a = [fake] * 26
+    a[17] = None                                       # count
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
-    a = [fake] * 25
-    a[17] = None                                       # t_abs
+    a = [fake] * 26
+    a[18] = None                                       # t_abs
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 1 << 40, None) == _lib.HAM_EINVAL
-    a = [fake] * 25
+    a = [fake] * 26
     assert L.ham_decode_step(ctypes.byref(dims()), *a, 8, None) == _lib.HAM_EWORKSPACE
     s = [fake] * 11
     s[9] = None                                        # count
@@ -156,9 +156,33 @@ def test_select_tau_and_external_score_errors():
     a = list(base)
     a[17] = None                                       # e
     assert _fwd(dims(flags=_lib.HAM_EXTERNAL_SCORES), a) == _lib.HAM_EINVAL and "EXTERNAL" in _msg()
-    a = [fake] * 25
-    a[21] = None                                       # e of the decode step
+    a = [fake] * 26
+    a[22] = None                                       # e of the decode step
     assert L.ham_decode_step(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *a, 1 << 40, None) == _lib.HAM_EINVAL
     s = [fake] * 11
     assert L.ham_route_stats(ctypes.byref(dims(flags=_lib.HAM_EXTERNAL_SCORES)), *s, ctypes.c_float(1e-5), None,
                              fake, 1 << 40, None) == _lib.HAM_EUNSUPPORTED
+
+
+def test_route_block_checks():
+    """Block-contiguous routing: the block size is 0, 1 or a power of two up to 64;
+    a forward (and route_stats) call covers whole blocks; the decode step needs the
+    open blocks' score sums; route_stats does not count near-threshold tokens then."""
+    L = _lib.lib()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    for bad in (3, 12, 128, -1):
+        assert L.ham_forward_workspace_size(ctypes.byref(dims(route_block=bad))) == 0
+        assert "route_block" in _msg()
+        assert _fwd(dims(route_block=bad)) == _lib.HAM_EUNSUPPORTED
+    for ok in (0, 1, 2, 4, 16, 64):
+        assert L.ham_forward_workspace_size(ctypes.byref(dims(T=320, cap=320, route_block=ok))) > 0
+    assert _fwd(dims(T=300, route_block=16)) == _lib.HAM_EINVAL and "multiples" in _msg()
+    assert _fwd(dims(T=320, cap=320, t0=8, route_block=16)) == _lib.HAM_EINVAL
+    a = [fake] * 26
+    a[12] = None                                       # block_score
+    assert L.ham_decode_step(ctypes.byref(dims(route_block=16)), *a, 1 << 40, None) == _lib.HAM_EINVAL
+    assert "block_score" in _msg()
+    s = [fake] * 11
+    assert L.ham_route_stats(ctypes.byref(dims(T=320, cap=320, route_block=16)), *s, ctypes.c_float(1e-5),
+                             None, fake, 1 << 40, None) == _lib.HAM_EUNSUPPORTED

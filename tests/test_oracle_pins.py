@@ -545,3 +545,76 @@ def test_tau_schedule_equals_calls_with_constant_thresholds():
     np.testing.assert_array_equal(one["routed"], np.concatenate([r1["routed"], r2["routed"]], 1))
     np.testing.assert_allclose(one["o"], np.concatenate([r1["o"], r2["o"]], 1), rtol=1e-12, atol=1e-13)
     np.testing.assert_array_equal(one["count"], r2["count"])
+
+
+# --- block-contiguous routing ("Hybrid Associative Memories" §7) -------------------
+def _block_visibility(routed_tok, n, T):
+    """allowed[t, j]: key j is cached and its block (aligned, n positions, local t0 a
+    multiple of n) ends at or before query t."""
+    j = np.arange(T)
+    end = (j // n) * n + n - 1
+    return routed_tok[None, :].astype(bool) & (end[None, :] <= j[:, None])
+
+
+@pytest.mark.parametrize("n,T,t0,rho", [(4, 37, 8, 0.5), (16, 64, 0, 0.3), (8, 50, 16, 1.0),
+                                        (2, 21, 6, 0.0)])
+def test_block_routing_dense_reference(n, T, t0, rho):
+    """The routed set is the set of whole blocks whose mean score (the per-token e,
+    which routing does not change) exceeds tau; a block still open at the end stays
+    out; o_kv equals a dense masked softmax over cached keys whose block ends at or
+    before the query; the RNN side is that of per-token routing."""
+    B, H, d = 2, 2, 8
+    inp = make_inputs(B, T, H, d, seed=120 + n)
+    free = oracle.forward(**inp, tau=np.full(H, INF, np.float32), scale=0.5, t0=t0)
+    nb = T // n
+    means = free["e"][:, :nb * n].reshape(B, nb, n, H).mean(axis=2)          # [B, nb, H]
+    if rho == 0.0:
+        tau = np.full(H, INF, np.float32)
+    elif rho == 1.0:
+        tau = np.full(H, -INF, np.float32)
+    else:
+        tau = np.array([np.quantile(means[:, :, h], 1 - rho) for h in range(H)], np.float32)
+        assert np.abs(means.astype(np.float32) - tau[None, None, :]).min() > 1e-7
+    out = oracle.forward(**inp, tau=tau, scale=0.5, t0=t0, route_block=n)
+    want = np.zeros((B, T, H), np.int8)
+    want[:, :nb * n] = np.repeat((means.astype(np.float32) > tau[None, None, :]), n, axis=1)
+    np.testing.assert_array_equal(out["routed"], want)
+    for name in ("e", "o_rnn", "S"):
+        np.testing.assert_array_equal(out[name], free[name])
+    for b in range(B):
+        for h in range(H):
+            m = want[b, :, h]
+            allowed = _block_visibility(m, n, T)
+            ref = masked_softmax_attention(inp["q"][b, :, h].astype(np.float64), inp["k"][b, :, h].astype(np.float64),
+                                           inp["v"][b, :, h].astype(np.float64), allowed, 0.5)
+            np.testing.assert_allclose(out["o_kv"][b, :, h], ref, rtol=1e-12, atol=1e-12)
+            nz = np.nonzero(m)[0]
+            cnt = out["count"][b, h]
+            assert cnt == len(nz) and cnt % n == 0
+            assert out["pos"][b, h, :cnt].tolist() == (t0 + nz).tolist()
+            np.testing.assert_array_equal(out["Vc"][b, h, :cnt], inp["v"][b, nz, h])
+
+
+def test_block_routing_override_and_continuation():
+    """A block's decision can be forced at its last token (the override elsewhere is
+    ignored); two calls split at a block boundary equal one call; a call must start
+    at a block boundary."""
+    B, T, H, d, n = 1, 48, 2, 8, 8
+    inp = make_inputs(B, T, H, d, seed=131)
+    rng = np.random.default_rng(131)
+    dec = rng.random((B, T // n, H)) < 0.5
+    mo = rng.integers(0, 2, (B, T, H)).astype(np.int8)          # noise off the last tokens
+    mo[:, n - 1::n] = dec
+    out = oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5, mask_override=mo, route_block=n)
+    np.testing.assert_array_equal(out["routed"], np.repeat(dec, n, axis=1).astype(np.int8))
+    tau = np.array([0.9, 1.0], np.float32)
+    one = oracle.forward(**inp, tau=tau, scale=0.5, route_block=n, cap=T)
+    T1 = 24
+    a = oracle.forward(**{k: x[:, :T1] for k, x in inp.items()}, tau=tau, scale=0.5, route_block=n, cap=T)
+    bpart = oracle.forward(**{k: x[:, T1:] for k, x in inp.items()}, tau=tau, scale=0.5, route_block=n,
+                           S0=a["S"], cache={k: a[k] for k in ("Kc", "Vc", "pos", "count")}, t0=T1)
+    for name in ("o", "o_kv", "routed", "e"):
+        np.testing.assert_allclose(np.concatenate([a[name], bpart[name]], 1), one[name], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(bpart["count"], one["count"])
+    with pytest.raises(ValueError):
+        oracle.forward(**inp, tau=tau, scale=0.5, route_block=n, t0=4)
