@@ -195,27 +195,33 @@ def bench_forward(args, dev):
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
-    router = rope = packed = None
+    router = rope = packed = blocks = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
         router = bench_router(args, dev, w, t)
         rope = bench_variant(args, dev, w, t, tau, "rope500000", rope_base=500000.0)
         packed = bench_variant(args, dev, w, t, tau, "packed_docs_mean1024_rope500000",
                                rope_base=500000.0, doc_start=make_doc_start(w.B, w.T, 1024, w.seed))
+        # block-contiguous routing: 64-token blocks, tau per head for half of the
+        # blocks on their mean score
+        nb = 64
+        means = st["e"].view(w.B, w.T // nb, nb, w.H).mean(dim=2).contiguous()
+        tau_b = ham.ham_select_tau(means, w.rho)
+        blocks = bench_variant(args, dev, w, t, tau_b, f"block_routing{nb}", route_block=nb)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router, rope=rope, packed=packed)
+                router=router, rope=rope, packed=packed, blocks=blocks)
 
 
-def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None):
-    """The same layer with the fit-error routing and threshold unchanged, plus RoPE on
-    the attention query and key (rope_base > 0) and/or same-document masking of
-    packed sequences (doc_start [B,T])."""
+def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0):
+    """The same layer with the fit-error routing, plus RoPE on the attention query and
+    key (rope_base > 0), same-document masking of packed sequences (doc_start [B,T])
+    and/or block-contiguous routing (route_block > 1, with its own tau)."""
     import torch
     import attention_sequence_mixing_amd as ham
     from attention_sequence_mixing_amd import _lib
     plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale,
-                           rope_base=rope_base)
+                           rope_base=rope_base, route_block=route_block)
     ds = None if doc_start is None else torch.from_numpy(doc_start.astype(np.int32)).to(dev)
 
     def step():
@@ -235,9 +241,11 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None):
     ms = e0.elapsed_time(e1) / args.steps
     stages = collect_stages(lib, args.steps)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
-    log(f"[bench] {label}: {ms:.3f} ms/step, stages {dict(zip(names, [round(x, 4) for x in stages]))}")
+    rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
+    log(f"[bench] {label}: {ms:.3f} ms/step, rho {rho:.4f}, "
+        f"stages {dict(zip(names, [round(x, 4) for x in stages]))}")
     return dict(workload=f"{w.name}_{label}", ms_per_step=round(ms, 4),
-                tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                tokens_per_s=round(w.B * w.T / (ms / 1e3), 1), rho_measured=round(rho, 6),
                 stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
 
 
@@ -483,6 +491,7 @@ def main():
         "learned_router": res["router"],
         "rope": res["rope"],
         "packed_docs": res["packed"],
+        "block_routing": res["blocks"],
         "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
