@@ -5,7 +5,8 @@ pass), and the attention outputs at sampled tokens of sampled heads.
 
 Workloads: the layer at the 800M-model shape (B=8, H=16, d=128, T=4096, bf16 I/O,
 rho = 0.5 and the two rho limits; rho = 0.5 with RoPE base 500K; rho = 0.5 over packed
-documents with same-document masking and RoPE); the long-context case (B=1, H=16, T=32768,
+documents with same-document masking and RoPE; rho = 0.5 of 64-token blocks with
+block-contiguous routing); the long-context case (B=1, H=16, T=32768,
 planted repeated pairs, rho = 0.25); the decode case (batch 32, H=16, d=128,
 32K-token prefix, then decode steps).
 """
@@ -18,29 +19,31 @@ import attention_sequence_mixing_amd as ham
 from attention_sequence_mixing_amd.inputs import (LAYER, LONG, DECODE_B, DECODE_D, DECODE_H,
                                                   DECODE_PREFIX, make_doc_start, make_inputs,
                                                   make_inputs_torch, make_workload, tau_for_rho)
-from parity import E_TOL, NEAR, TOL, np_of, rel_err_slices, to_dev
+from parity import E_TOL, NEAR, TOL, block_means, np_of, rel_err_slices, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = torch.device("cuda:0")
 INF = np.float32(np.inf)
 
 
-def _rnn_only_oracle(inp, tau, scale, cap=None, rope_base=0.0):
+def _rnn_only_oracle(inp, tau, scale, cap=None, rope_base=0.0, route_block=0):
     """Oracle over all heads with no attention readout (emit all-zero)."""
     B, T, H, _ = inp["q"].shape
     return oracle.forward(**inp, tau=tau, scale=scale, cap=cap, emit=np.zeros((B, T, H), np.int8),
-                          rope_base=rope_base)
+                          rope_base=rope_base, route_block=route_block)
 
 
-def _check_all_heads(out, ref, tau, kc_tol=None):
+def _check_all_heads(out, ref, tau, kc_tol=None, route_block=0):
     """Scores, routing, compaction and state of every head.  kc_tol: None for
-    bit-exact cached keys, else the per-slice relative tolerance (rotated keys)."""
+    bit-exact cached keys, else the per-slice relative tolerance (rotated keys).
+    route_block > 1: the near band applies to block means."""
     e_gpu = out["e"].cpu().numpy()
     r_gpu = out["routed"].cpu().numpy().astype(bool)
     de = np.abs(e_gpu - ref["e"]).max()
     assert de < E_TOL, f"score error {de:.3e}"
     H = e_gpu.shape[2]
-    near = np.abs(ref["e"] - np.asarray(tau, np.float64).reshape(1, 1, H)) < NEAR
+    score = ref["e"] if route_block <= 1 else block_means(ref["e"], route_block)
+    near = np.abs(score - np.asarray(tau, np.float64).reshape(1, 1, H)) < NEAR
     flips = r_gpu != ref["routed"].astype(bool)
     assert not (flips & ~near).any(), f"{int((flips & ~near).sum())} flips outside the near band"
     nflip_heads = flips.any(axis=1)                      # [B,H]
@@ -71,7 +74,7 @@ def _check_all_heads(out, ref, tau, kc_tol=None):
 
 
 def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu, rope_base=0.0,
-                           doc_start=None):
+                           doc_start=None, route_block=0):
     """Oracle outputs at sampled tokens of sampled heads (with the GPU mask if it
     differs from the oracle's inside the near band)."""
     T = inp["q"].shape[1]
@@ -84,7 +87,8 @@ def _check_sampled_outputs(out, inp, tau, scale, heads, ntok, dtype, seed, r_gpu
         emit[0, toks, 0] = 1
         ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit,
                              mask_override=r_gpu[b:b + 1, :, h:h + 1], rope_base=rope_base,
-                             doc_start=None if doc_start is None else doc_start[b:b + 1])
+                             doc_start=None if doc_start is None else doc_start[b:b + 1],
+                             route_block=route_block)
         for name in ("o", "o_rnn", "o_kv"):
             x = np_of(out[name][b, toks, h])
             y = ref[name][0, toks, 0]
@@ -156,6 +160,30 @@ def test_layer_fullsize_packed_documents():
                                    torch.bfloat16, 44, out["routed"].cpu().numpy(),
                                    rope_base=500000.0, doc_start=ds)
     print(f"layer packed: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
+
+
+def test_layer_fullsize_block_routing():
+    """The layer with 64-token block-contiguous routing, tau per head for half of the
+    blocks on their mean score (the benchmark's block-routing leg)."""
+    w = LAYER
+    n = 64
+    inp = make_workload(w)
+    scale = w.attn_scale
+    base_e = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(block_means(base_e["e"], n)[:, ::n], 0.5)
+    ref = _rnn_only_oracle(inp, tau, scale, route_block=n)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, route_block=n, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    nflip, de = _check_all_heads(out, ref, tau, route_block=n)
+    r_gpu = out["routed"].cpu().numpy()
+    assert np.array_equal(r_gpu, np.repeat(r_gpu[:, n - 1::n], n, axis=1))
+    got_rho = float(out["count"].sum()) / (w.B * w.T * w.H)
+    assert abs(got_rho - 0.5) <= (nflip + n) / (w.B * w.T * w.H)
+    worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 2), (5, 11), (7, 15)], 24,
+                                   torch.bfloat16, 45, r_gpu, route_block=n)
+    print(f"layer blocks: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
 
 
 def test_long_context_fullsize():
