@@ -69,9 +69,20 @@ def _tau_flag(tau, per_token_shape, dev):
     return 0
 
 
-def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0, route_block=0):
+def make_dims(B, T, H, dk, dv, io, scale, eps, cap, flags=0, t0=0, rope_base=0.0, route_block=0,
+              kv=None):
+    """kv: None, or (kv_heads, dk_kv, dv_kv) of attention heads with their own geometry."""
+    kh, kdk, kdv = kv if kv is not None else (0, 0, 0)
     return HamDims(B, T, H, dk, dv, io, float(scale), float(eps), cap, flags, t0, float(rope_base),
-                   int(route_block))
+                   int(route_block), int(kh), int(kdk), int(kdv))
+
+
+def _kv_geometry(H, dk, dv, kv):
+    """(kv_heads, dk_kv, dv_kv), defaulting to the RNN heads' geometry."""
+    if kv is None:
+        return H, dk, dv
+    kh, kdk, kdv = kv
+    return kh or H, kdk or dk, kdv or dv
 
 
 class ForwardPlan:
@@ -81,16 +92,22 @@ class ForwardPlan:
     """
 
     def __init__(self, B, T, H, dk, dv, dtype, device, *, cap=None, scale=None,
-                 norm_eps=1e-6, flags=0, t0=0, rope_base=0.0, route_block=0, want_o_rnn=False,
-                 want_o_kv=False):
+                 norm_eps=1e-6, flags=0, t0=0, rope_base=0.0, route_block=0, kv_heads=0, dk_kv=0,
+                 dv_kv=0, want_o_rnn=False, want_o_kv=False):
+        """kv_heads, dk_kv, dv_kv: attention (KV) heads with their own geometry (0: the
+        RNN heads'); the cache, gate_kv, o_kv and q_attn/k_attn/v_attn are then shaped
+        [.., kv_heads, dk_kv|dv_kv]."""
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.cap = T if cap is None else cap
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
+        kv = (kv_heads, dk_kv, dv_kv)
         self.dims = make_dims(B, T, H, dk, dv, self.io, self.scale, norm_eps, self.cap, flags, t0,
-                              rope_base, route_block)
+                              rope_base, route_block, kv)
         self.shape = (B, T, H, dk, dv)
+        self.kv = _kv_geometry(H, dk, dv, kv)
+        HK, DKK, DVK = self.kv
         L = _lib.lib()
         ws_bytes = L.ham_forward_workspace_size(ctypes.byref(self.dims))
         if ws_bytes == 0:
@@ -98,14 +115,14 @@ class ForwardPlan:
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.o = torch.empty((B, T, H, dv), dtype=dtype, device=device)
         self.o_rnn = torch.empty((B, T, H, dv), dtype=dtype, device=device) if want_o_rnn else None
-        self.o_kv = torch.empty((B, T, H, dv), dtype=dtype, device=device) if want_o_kv else None
+        self.o_kv = torch.empty((B, T, HK, DVK), dtype=dtype, device=device) if want_o_kv else None
         self.e = torch.empty((B, T, H), dtype=torch.float32, device=device)
         self.routed = torch.empty((B, T, H), dtype=torch.uint8, device=device)
         self.S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
-        self.Kc = torch.zeros((B, H, self.cap, dk), dtype=dtype, device=device)
-        self.Vc = torch.zeros((B, H, self.cap, dv), dtype=dtype, device=device)
-        self.pos = torch.full((B, H, self.cap), -1, dtype=torch.int32, device=device)
-        self.count = torch.zeros((B, H), dtype=torch.int32, device=device)
+        self.Kc = torch.zeros((B, HK, self.cap, DKK), dtype=dtype, device=device)
+        self.Vc = torch.zeros((B, HK, self.cap, DVK), dtype=dtype, device=device)
+        self.pos = torch.full((B, HK, self.cap), -1, dtype=torch.int32, device=device)
+        self.count = torch.zeros((B, HK), dtype=torch.int32, device=device)
 
     def __call__(self, q, k, v, beta, g, tau, *, q_attn=None, k_attn=None, v_attn=None,
                  gate_rnn=None, gate_kv=None, S0=None, router_scores=None, doc_start=None,
@@ -116,13 +133,17 @@ class ForwardPlan:
         absolute start position of each token's document in a packed batch (the
         attention then sees only keys of the same document), or None."""
         B, T, H, dk, dv = self.shape
+        HK, DKK, DVK = self.kv
         dev, dt = self.device, self.dtype
-        for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
+        for n, t in (("q", q), ("k", k)):
             _need(n, t, (B, T, H, dk), dt, dev)
-        for n, t in (("v", v), ("v_attn", v_attn)):
-            _need(n, t, (B, T, H, dv), dt, dev)
-        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
+        _need("v", v, (B, T, H, dv), dt, dev)
+        for n, t in (("q_attn", q_attn), ("k_attn", k_attn)):
+            _need(n, t, (B, T, HK, DKK), dt, dev)
+        _need("v_attn", v_attn, (B, T, HK, DVK), dt, dev)
+        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn)):
             _need(n, t, (B, T, H), torch.float32, dev)
+        _need("gate_kv", gate_kv, (B, T, HK), torch.float32, dev)
         tf = _tau_flag(tau, (B, T, H), dev)
         self.dims.flags = (self.dims.flags & ~HAM_TAU_PER_TOKEN) | tf
         _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
@@ -176,14 +197,18 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
              | (HAM_EXTERNAL_SCORES if router_scores is not None else 0))
     if cache is not None:
         cap = cache["Kc"].shape[2]
+    # the attention heads take the geometry of the attention-path inputs
+    HK, DKK, DVK = (q_attn.shape[2], q_attn.shape[3], v_attn.shape[3]) if (
+        q_attn is not None and v_attn is not None) else (H, dk, dv)
     plan = ForwardPlan(B, T, H, dk, dv, q.dtype, q.device, cap=cap, scale=scale,
                        norm_eps=norm_eps, flags=flags, t0=t0, rope_base=rope_base,
-                       route_block=route_block, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
+                       route_block=route_block, kv_heads=HK, dk_kv=DKK, dv_kv=DVK,
+                       want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     if cache is not None:
-        plan.Kc = _need("Kc", cache["Kc"], (B, H, plan.cap, dk), q.dtype, q.device)
-        plan.Vc = _need("Vc", cache["Vc"], (B, H, plan.cap, dv), q.dtype, q.device)
-        plan.pos = _need("pos", cache["pos"], (B, H, plan.cap), torch.int32, q.device)
-        plan.count = _need("count", cache["count"], (B, H), torch.int32, q.device)
+        plan.Kc = _need("Kc", cache["Kc"], (B, HK, plan.cap, DKK), q.dtype, q.device)
+        plan.Vc = _need("Vc", cache["Vc"], (B, HK, plan.cap, DVK), q.dtype, q.device)
+        plan.pos = _need("pos", cache["pos"], (B, HK, plan.cap), torch.int32, q.device)
+        plan.count = _need("count", cache["count"], (B, HK), torch.int32, q.device)
     plan(q, k, v, beta, g, tau, q_attn=q_attn, k_attn=k_attn, v_attn=v_attn,
          gate_rnn=gate_rnn, gate_kv=gate_kv, S0=S0, router_scores=router_scores,
          doc_start=doc_start, stream=stream)
@@ -194,13 +219,16 @@ class DecodePlan:
     """Scratch and outputs for repeated ham_decode_step calls on one cache."""
 
     def __init__(self, B, H, dk, dv, cap, dtype, device, *, scale=None, norm_eps=1e-6,
-                 rope_base=0.0, route_block=0, want_o_rnn=False, want_o_kv=False):
+                 rope_base=0.0, route_block=0, kv_heads=0, dk_kv=0, dv_kv=0, want_o_rnn=False,
+                 want_o_kv=False):
         device = torch.device(device)
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
+        kv = (kv_heads, dk_kv, dv_kv)
         self.dims = make_dims(B, 1, H, dk, dv, self.io, self.scale, norm_eps, cap, rope_base=rope_base,
-                              route_block=route_block)
+                              route_block=route_block, kv=kv)
+        self.kv = _kv_geometry(H, dk, dv, kv)
         # block-contiguous routing: the open block's running score sum per (b, h)
         self.block_score = (torch.zeros((B, H), dtype=torch.float32, device=device)
                             if route_block > 1 else None)
@@ -212,7 +240,8 @@ class DecodePlan:
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, dv), dtype=dtype, device=device)
         self.o_rnn = torch.empty((B, H, dv), dtype=dtype, device=device) if want_o_rnn else None
-        self.o_kv = torch.empty((B, H, dv), dtype=dtype, device=device) if want_o_kv else None
+        self.o_kv = (torch.empty((B, self.kv[0], self.kv[2]), dtype=dtype, device=device)
+                     if want_o_kv else None)
         self.e = torch.empty((B, H), dtype=torch.float32, device=device)
         self.routed = torch.empty((B, H), dtype=torch.uint8, device=device)
         self.status = torch.zeros((1,), dtype=torch.int32, device=device)
@@ -226,19 +255,23 @@ class DecodePlan:
         block_score: with block-contiguous routing, the [B,H] float32 running score sum
         of the open blocks (default: the plan's own, zero at creation)."""
         B, H, dk, dv, cap = self.shape
+        HK, DKK, DVK = self.kv
         dev, dt = self.device, self.dtype
-        for n, t in (("q", q), ("k", k), ("q_attn", q_attn), ("k_attn", k_attn)):
+        for n, t in (("q", q), ("k", k)):
             _need(n, t, (B, H, dk), dt, dev)
-        for n, t in (("v", v), ("v_attn", v_attn)):
-            _need(n, t, (B, H, dv), dt, dev)
-        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn), ("gate_kv", gate_kv)):
+        _need("v", v, (B, H, dv), dt, dev)
+        for n, t in (("q_attn", q_attn), ("k_attn", k_attn)):
+            _need(n, t, (B, HK, DKK), dt, dev)
+        _need("v_attn", v_attn, (B, HK, DVK), dt, dev)
+        for n, t in (("beta", beta), ("g", g), ("gate_rnn", gate_rnn)):
             _need(n, t, (B, H), torch.float32, dev)
+        _need("gate_kv", gate_kv, (B, HK), torch.float32, dev)
         tf = _tau_flag(tau, (B, H), dev)
         _need("S", S, (B, H, dk, dv), torch.float32, dev)
-        _need("Kc", Kc, (B, H, cap, dk), dt, dev)
-        _need("Vc", Vc, (B, H, cap, dv), dt, dev)
-        _need("pos", pos, (B, H, cap), torch.int32, dev)
-        _need("count", count, (B, H), torch.int32, dev)
+        _need("Kc", Kc, (B, HK, cap, DKK), dt, dev)
+        _need("Vc", Vc, (B, HK, cap, DVK), dt, dev)
+        _need("pos", pos, (B, HK, cap), torch.int32, dev)
+        _need("count", count, (B, HK), torch.int32, dev)
         _need("t_abs", t_abs, (B,), torch.int32, dev)
         _need("router_scores", router_scores, (B, H), torch.float32, dev)
         _need("doc_start", doc_start, (B,), torch.int32, dev)
@@ -270,9 +303,11 @@ def ham_decode_step(q, k, v, beta, g, tau, S, cache, t_abs, *, scale=None, norm_
     B, H, dk = q.shape
     dv = v.shape[-1]
     cap = cache["Kc"].shape[2]
+    HK, DKK, DVK = (q_attn.shape[1], q_attn.shape[2], v_attn.shape[2]) if (
+        q_attn is not None and v_attn is not None) else (H, dk, dv)
     plan = DecodePlan(B, H, dk, dv, cap, q.dtype, q.device, scale=scale, norm_eps=norm_eps,
-                      rope_base=rope_base, route_block=route_block, want_o_rnn=want_o_rnn,
-                      want_o_kv=want_o_kv)
+                      rope_base=rope_base, route_block=route_block, kv_heads=HK, dk_kv=DKK,
+                      dv_kv=DVK, want_o_rnn=want_o_rnn, want_o_kv=want_o_kv)
     if route_block > 1 and "block_score" not in cache:
         cache["block_score"] = plan.block_score
     plan(q, k, v, beta, g, tau, S, cache["Kc"], cache["Vc"], cache["pos"], cache["count"], t_abs,

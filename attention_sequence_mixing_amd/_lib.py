@@ -27,7 +27,8 @@ class HamDims(ctypes.Structure):
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("io_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
                 ("cap", ctypes.c_int), ("flags", ctypes.c_int), ("t0", ctypes.c_int),
-                ("rope_base", ctypes.c_float), ("route_block", ctypes.c_int)]
+                ("rope_base", ctypes.c_float), ("route_block", ctypes.c_int),
+                ("kv_heads", ctypes.c_int), ("dk_kv", ctypes.c_int), ("dv_kv", ctypes.c_int)]
 
 
 class HamError(RuntimeError):

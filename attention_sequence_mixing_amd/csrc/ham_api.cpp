@@ -51,6 +51,19 @@ int check_dims(const ham_dims* d, bool need_T) {
   if (d->t0 < 0) return fail(HAM_EINVAL, "t0 must be >= 0");
   if (!std::isfinite(d->rope_base) || d->rope_base < 0.f)
     return fail(HAM_EINVAL, "rope_base must be 0 (none) or a finite positive base");
+  if (d->kv_heads < 0 || d->dk_kv < 0 || d->dv_kv < 0)
+    return fail(HAM_EINVAL, "kv_heads, dk_kv and dv_kv must be >= 0 (0: as the RNN heads)");
+  {
+    const int HK = d->kv_heads > 0 ? d->kv_heads : d->H;
+    const int DKK = d->dk_kv > 0 ? d->dk_kv : d->dk, DVK = d->dv_kv > 0 ? d->dv_kv : d->dv;
+    if ((DKK != 64 && DKK != 128) || (DVK != 64 && DVK != 128))
+      return fail(HAM_EUNSUPPORTED, "dk_kv and dv_kv must be 64 or 128 (dk_kv=%d dv_kv=%d)", DKK, DVK);
+    if (HK % d->H)
+      return fail(HAM_EUNSUPPORTED, "kv_heads (%d) must be a multiple of H (%d)", HK, d->H);
+    if ((long long)HK * DVK != (long long)d->H * d->dv)
+      return fail(HAM_EUNSUPPORTED, "the KV heads' values must tile the RNN heads' output: kv_heads*dv_kv "
+                                    "(%d*%d) != H*dv (%d*%d)", HK, DVK, d->H, d->dv);
+  }
   if (d->route_block < 0 || d->route_block > ham::kChunk || (d->route_block & (d->route_block - 1)))
     return fail(HAM_EUNSUPPORTED, "route_block must be 0, 1 or a power of two up to %d (route_block=%d)",
                 ham::kChunk, d->route_block);
@@ -74,6 +87,14 @@ int check_dims(const ham_dims* d, bool need_T) {
 
 // block size of block-contiguous routing, or 0 for per-token routing
 int route_blk(const ham_dims* d) { return d->route_block > 1 ? d->route_block : 0; }
+
+// geometry of the attention (KV) heads; "split": another head count than the RNN's,
+// so the mix of the two readouts runs in its own kernel
+int kv_heads(const ham_dims* d) { return d->kv_heads > 0 ? d->kv_heads : d->H; }
+int dk_kv(const ham_dims* d) { return d->dk_kv > 0 ? d->dk_kv : d->dk; }
+int dv_kv(const ham_dims* d) { return d->dv_kv > 0 ? d->dv_kv : d->dv; }
+bool split_heads(const ham_dims* d) { return kv_heads(d) != d->H; }
+bool own_attn_inputs(const ham_dims* d) { return split_heads(d) || dk_kv(d) != d->dk; }
 
 bool use_chunked(const ham_dims* d) {
   return !(d->flags & HAM_FORCE_RECURRENT) && d->T > ham::kChunk &&
@@ -102,13 +123,14 @@ SegPlan seg_plan(const ham_dims* d) {
 
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
 struct FwdLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, lo, state, rope, prep;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, ntok, lo, state, rope, prep, okv32;
   size_t seg_a, seg_b, seg_s, total;
   SegPlan seg;
 };
 
 FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   const size_t BTH = (size_t)d->B * d->T * d->H, BH = (size_t)d->B * d->H;
+  const size_t BTK = (size_t)d->B * d->T * kv_heads(d), BK = (size_t)d->B * kv_heads(d);
   const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
   FwdLayout L{};
   size_t off = 0;
@@ -117,11 +139,12 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.e = off;           off += up256(BTH * sizeof(float));
   L.routed = off;      off += up256(BTH);
   L.chunk_count = off; off += up256(BH * nchunk * sizeof(int32_t));
-  L.count_in = off;    off += up256(BH * sizeof(int32_t));
-  L.ntok = off;        off += up256(BTH * sizeof(int32_t));
-  L.lo = off;          off += with_state ? 0 : up256(BTH * sizeof(int32_t));
+  L.count_in = off;    off += up256(BK * sizeof(int32_t));
+  L.ntok = off;        off += up256(BTK * sizeof(int32_t));
+  L.lo = off;          off += with_state ? 0 : up256(BTK * sizeof(int32_t));
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
-  L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (d->dk / 2) * sizeof(float2)) : 0;
+  L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (dk_kv(d) / 2) * sizeof(float2)) : 0;
+  L.okv32 = off;       off += (!with_state && split_heads(d)) ? up256(BTH * d->dv * sizeof(float)) : 0;
   L.prep = off;
   if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += up256(BH * nchunk * ham::kPrepRecordBytes);
   L.seg = seg_plan(d);
@@ -134,12 +157,12 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
 }
 
 struct DecLayout {
-  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, rope, lo, total;
+  size_t o_rnn32, score, e, routed, chunk_count, count_in, part, rope, lo, okv32, total;
   int nseg;
 };
 
 DecLayout dec_layout(const ham_dims* d) {
-  const size_t BH = (size_t)d->B * d->H;
+  const size_t BH = (size_t)d->B * d->H, BK = (size_t)d->B * kv_heads(d);
   DecLayout L{};
   L.nseg = (d->cap + ham::kDecodeSeg - 1) / ham::kDecodeSeg;
   size_t off = 0;
@@ -148,10 +171,11 @@ DecLayout dec_layout(const ham_dims* d) {
   L.e = off;           off += up256(BH * sizeof(float));
   L.routed = off;      off += up256(BH);
   L.chunk_count = off; off += up256(BH * sizeof(int32_t));
-  L.count_in = off;    off += up256(BH * sizeof(int32_t));
-  L.part = off;        off += up256(BH * (size_t)L.nseg * (d->dv + 2) * sizeof(float));
-  L.rope = off;        off += d->rope_base > 0.f ? up256((size_t)d->B * (d->dk / 2) * sizeof(float2)) : 0;
-  L.lo = off;          off += up256(BH * sizeof(int32_t));
+  L.count_in = off;    off += up256(BK * sizeof(int32_t));
+  L.part = off;        off += up256(BK * (size_t)L.nseg * (dv_kv(d) + 2) * sizeof(float));
+  L.rope = off;        off += d->rope_base > 0.f ? up256((size_t)d->B * (dk_kv(d) / 2) * sizeof(float2)) : 0;
+  L.lo = off;          off += up256(BK * sizeof(int32_t));
+  L.okv32 = off;       off += split_heads(d) ? up256(BH * d->dv * sizeof(float)) : 0;
   L.total = off;
   return L;
 }
@@ -232,7 +256,7 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
 
 extern "C" {
 
-int ham_version(void) { return 10200; }
+int ham_version(void) { return 10300; }
 
 const char* ham_last_error(void) { return g_err.c_str(); }
 
@@ -268,6 +292,9 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   HAM_ALIGNED(o_kv); HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
   const bool ext = (d->flags & HAM_EXTERNAL_SCORES) != 0;
   if (ext && !e) return fail(HAM_EINVAL, "HAM_EXTERNAL_SCORES needs the scores in e (NULL)");
+  if (own_attn_inputs(d) && !(q_attn && k_attn && v_attn))
+    return fail(HAM_EINVAL, "the KV heads' geometry differs from the RNN heads': q_attn, k_attn and "
+                            "v_attn are required");
   if (!(d->flags & HAM_CONTINUE) && d->cap < d->T)
     return fail(HAM_ECAPACITY, "cap (%d) < T (%d): the cache cannot hold every token", d->cap, d->T);
   const FwdLayout L = fwd_layout(d, false);
@@ -293,29 +320,41 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
                     (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H,
                     ext ? e : nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d), nullptr,
-                    nullptr};
+                    nullptr, kv_heads(d)};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
 
   // rotary table of the new tokens' positions (read by the key and query rotations)
   float2* rope = d->rope_base > 0.f ? at<float2>(ws, L.rope) : nullptr;
-  if (rope) HAM_HIP(ham::launch_rope_table(rope, nullptr, d->t0, d->T, d->dk, (double)d->rope_base, s));
+  if (rope) HAM_HIP(ham::launch_rope_table(rope, nullptr, d->t0, d->T, dk_kv(d), (double)d->rope_base, s));
+  // one cache per KV head, following the routing of its RNN head
+  const int HK = kv_heads(d);
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
-                      Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, d->H, d->cap,
-                      rope, route_blk(d)};
-  HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
+                      Kc, Vc, pos, count, ntok, nullptr, nullptr, d->t0, d->B, d->T, HK, d->cap,
+                      rope, route_blk(d), d->H};
+  HAM_HIP(ham::launch_compact(d->io_dtype, dk_kv(d), dv_kv(d), ca, s));
   tm.mark();
 
   // same-document masking: each query's first visible cache entry
   int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
   if (lo) {
-    ham::DocLoArgs da{doc_start, ntok, count_in, count, pos, lo, d->t0, d->B, d->T, d->H, d->cap,
+    ham::DocLoArgs da{doc_start, ntok, count_in, count, pos, lo, d->t0, d->B, d->T, HK, d->cap,
                       route_blk(d)};
     HAM_HIP(ham::launch_doc_lo(da, s));
   }
-  ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv,
-                   d->scale, d->norm_eps, d->B, d->T, d->H, d->cap, rope, use_chunked(d) ? 1 : 0, lo};
-  HAM_HIP(ham::launch_attention(d->io_dtype, d->dk, d->dv, aa, s));
+  // With KV heads of another geometry the attention writes its readout to scratch and
+  // the mix of the two headwise-normalised readouts runs afterwards.
+  const bool split = split_heads(d);
+  float* okv32 = split ? at<float>(ws, L.okv32) : nullptr;
+  ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, split ? nullptr : o_rnn32, gate_rnn, gate_kv, o,
+                   o_rnn, o_kv, d->scale, d->norm_eps, d->B, d->T, HK, d->cap, rope,
+                   (!split && use_chunked(d)) ? 1 : 0, lo, okv32};
+  HAM_HIP(ham::launch_attention(d->io_dtype, dk_kv(d), dv_kv(d), aa, s));
+  if (split) {
+    ham::MixArgs mx{o_rnn32, okv32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps, d->B * d->T, d->H,
+                    HK / d->H, use_chunked(d) ? 1 : 0};
+    HAM_HIP(ham::launch_mix(d->io_dtype, d->dv, mx, s));
+  }
   tm.mark();
   return HAM_OK;
 }
@@ -334,6 +373,9 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   HAM_REQUIRE(tau); HAM_REQUIRE(S); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos);
   HAM_REQUIRE(count); HAM_REQUIRE(t_abs); HAM_REQUIRE(o);
   if (route_blk(d)) HAM_REQUIRE(block_score);
+  if (own_attn_inputs(d) && !(q_attn && k_attn && v_attn))
+    return fail(HAM_EINVAL, "the KV heads' geometry differs from the RNN heads': q_attn, k_attn and "
+                            "v_attn are required");
   HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
   HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
   HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
@@ -358,29 +400,37 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
   tm.mark();
   ham::RouteArgs ro{score, ham::rnn_recurrent_slices(d->dv), tau, ext ? nullptr : e_buf, r_buf,
                     chunk_count, count, count_in, d->B, 1, d->H, ext ? e : nullptr,
-                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d), block_score, t_abs};
+                    (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d), block_score, t_abs, kv_heads(d)};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   // rotary table of the new tokens' positions t_abs[b] (key and query rotations)
   float2* rope = d->rope_base > 0.f ? at<float2>(ws, L.rope) : nullptr;
-  if (rope) HAM_HIP(ham::launch_rope_table(rope, t_abs, 0, d->B, d->dk, (double)d->rope_base, s));
+  if (rope) HAM_HIP(ham::launch_rope_table(rope, t_abs, 0, d->B, dk_kv(d), (double)d->rope_base, s));
+  const int HK = kv_heads(d);
   ham::CompactArgs ca{k_attn ? k_attn : k, v_attn ? v_attn : v, r_buf, chunk_count, count_in,
-                      Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, d->H, d->cap,
-                      rope, route_blk(d)};
-  HAM_HIP(ham::launch_compact(d->io_dtype, d->dk, d->dv, ca, s));
+                      Kc, Vc, pos, count, nullptr, status, t_abs, 0, d->B, 1, HK, d->cap,
+                      rope, route_blk(d), d->H};
+  HAM_HIP(ham::launch_compact(d->io_dtype, dk_kv(d), dv_kv(d), ca, s));
   tm.mark();
   int32_t* lo = doc_start ? at<int32_t>(ws, L.lo) : nullptr;
   if (lo) {
-    ham::DocLoArgs dl{doc_start, nullptr, nullptr, count, pos, lo, 0, d->B, 1, d->H, d->cap, 0};
+    ham::DocLoArgs dl{doc_start, nullptr, nullptr, count, pos, lo, 0, d->B, 1, HK, d->cap, 0};
     HAM_HIP(ham::launch_doc_lo(dl, s));
   }
-  ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, d->H, d->cap,
+  ham::DecodeAttnArgs da{q_attn ? q_attn : q, Kc, Vc, count, part, d->scale, d->B, HK, d->cap,
                          ham::kDecodeSeg, L.nseg, rope, lo};
-  HAM_HIP(ham::launch_decode_attn(d->io_dtype, d->dk, d->dv, da, s));
+  HAM_HIP(ham::launch_decode_attn(d->io_dtype, dk_kv(d), dv_kv(d), da, s));
   tm.mark();
+  const bool split = split_heads(d);
+  float* okv32 = split ? at<float>(ws, L.okv32) : nullptr;
   ham::DecodeCombineArgs cb{part, count, o_rnn32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps,
-                            d->B, d->H, ham::kDecodeSeg, L.nseg};
-  HAM_HIP(ham::launch_decode_combine(d->io_dtype, d->dv, cb, s));
+                            d->B, HK, ham::kDecodeSeg, L.nseg, okv32};
+  HAM_HIP(ham::launch_decode_combine(d->io_dtype, dv_kv(d), cb, s));
+  if (split) {
+    ham::MixArgs mx{o_rnn32, okv32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps, d->B, d->H,
+                    HK / d->H, 0};
+    HAM_HIP(ham::launch_mix(d->io_dtype, d->dv, mx, s));
+  }
   tm.mark();
   return HAM_OK;
 }
@@ -421,7 +471,7 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
   if (rc != HAM_OK) return rc;
   ham::RouteArgs ro{score, slices, tau, e_buf, r_buf, chunk_count, nullptr, count_in,
                     d->B, d->T, d->H, nullptr, (d->flags & HAM_TAU_PER_TOKEN) ? 1 : 0, route_blk(d),
-                    nullptr, nullptr};
+                    nullptr, nullptr, 0};
   HAM_HIP(ham::launch_route(ro, s));
   tm.mark();
   ham::StatsArgs sa{e_buf, tau, chunk_count, count, n_near, near_band, d->B, d->T, d->H,

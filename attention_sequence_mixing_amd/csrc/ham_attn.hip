@@ -189,6 +189,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
   const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (a.okv32) {
+    // KV heads of another geometry than the RNN's: the readout alone, mixed later
+    if (tvalid) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(a.okv32 + tok * DV + dt * 16 + 4 * g) = acc[dt] * inv_l;
+    }
+    return;
+  }
   // lane holds query t, output dims d = dt*16 + 4g + i
   float okv[DT][4], orn[DT][4];
   float ssk = 0.f, ssr = 0.f;
@@ -644,6 +653,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     const int t = tq[qt];
     const bool tvalid = t < a.T;
     const size_t tt = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
+    if (a.okv32) {
+      // KV heads of another geometry than the RNN's: the readout alone, mixed later
+      if (tvalid) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(a.okv32 + tt * DV + dt * 16 + 4 * g) = acc[qt][dt] * inv_l;
+      }
+      continue;
+    }
     float okv[DT][4], orn[DT][4];
     float ssk = 0.f, ssr = 0.f;
 #pragma unroll
@@ -703,6 +721,56 @@ static hipError_t launch_attn_bf16_v5(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT, true>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT, false>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Gated sum of the headwise-normalised readouts when the KV heads have another
+// geometry than the RNN heads ("Hybrid Associative Memories" §2 headwise norm and
+// gated sum, App. A.1 headwise gating; §4 model setup: twice the RNN heads, half
+// their size, the value columns of a KV head pair tiling one RNN head's).  One wave
+// per (token, RNN head), DV/64 columns per lane: the RNN norm runs over the wave,
+// each KV head's over the 64/R lanes that hold its columns.
+template <class IO, int DV, int R>
+__global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
+  using E = typename IO::elem;
+  constexpr int PL = DV / 64, LK = 64 / R;
+  const int lane = lane_id();
+  const long long u = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, RNN head)
+  if (u >= (long long)a.ntok * a.H) return;                            // whole waves
+  const long long tok = u / a.H;
+  const int h = (int)(u - tok * a.H);
+  const int j = h * R + lane / LK;                                      // this lane's KV head
+  const size_t base = (size_t)u * DV + lane * PL;                       // same flat index both sides
+  float orn[PL], okv[PL], ssr = 0.f, ssk = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    orn[i] = a.ornn_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.o_rnn32)[base + i])
+                         : a.o_rnn32[base + i];
+    okv[i] = a.okv32[base + i];
+    ssr += orn[i] * orn[i];
+    ssk += okv[i] * okv[i];
+  }
+  ssr = wave_sum<64>(ssr);
+#pragma unroll
+  for (int m = 1; m < LK; m <<= 1) ssk += __shfl_xor(ssk, m, kWave);
+  const float gr = a.gate_rnn ? a.gate_rnn[u] : 1.f;
+  const float gk = a.gate_kv ? a.gate_kv[(size_t)tok * (a.H * R) + j] : 1.f;
+  const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
+  const float ik = gk / sqrtf(ssk / (float)(DV / R) + a.eps);
+  E* o = static_cast<E*>(a.o);
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    IO::store(o, base + i, orn[i] * ir + okv[i] * ik);
+    if (a.o_kv) IO::store(static_cast<E*>(a.o_kv), base + i, okv[i]);
+    if (a.o_rnn) IO::store(static_cast<E*>(a.o_rnn), base + i, orn[i]);
+  }
+}
+
+hipError_t launch_mix(int io, int dv, const MixArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((long long)a.ntok * a.H + 3) / 4));
+  if (dv != 128 || a.r != 2) return hipErrorInvalidValue;
+  if (io == 0) hipLaunchKernelGGL((mix_kernel<IoF32, 128, 2>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((mix_kernel<IoBF16, 128, 2>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

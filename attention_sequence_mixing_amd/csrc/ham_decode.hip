@@ -200,6 +200,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeCombineArgs a)
     for (int i = 0; i < PL; ++i) okv[i] += ps[lane * PL + i] * w;
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  if (a.okv32) {
+    // KV heads of another geometry than the RNN's: the readout alone, mixed later
+#pragma unroll
+    for (int i = 0; i < PL; ++i) a.okv32[(size_t)bh * DV + lane * PL + i] = okv[i] * inv;
+    return;
+  }
   float orn[PL], ssr = 0.f, ssk = 0.f;
 #pragma unroll
   for (int i = 0; i < PL; ++i) {

@@ -64,6 +64,7 @@ struct RouteArgs {
   int blk;
   float* blk_acc;
   const int32_t* t_abs;
+  int Hkv;              // KV heads (count, count_in are [B,Hkv]); 0: H
 };
 
 struct CompactArgs {
@@ -84,6 +85,8 @@ struct CompactArgs {
   const float2* rope;   // (cos, sin) of the key rotations, or null: [T][dk/2] rows of the
                         // new tokens (forward), or [B][dk/2] rows at t_abs[b] (decode)
   int blk;              // block-contiguous routing: block size (> 1), else 0
+  int Hr;               // RNN heads (routed, chunk_count); H counts the KV heads, each
+                        // taking the routing of RNN head h / (H / Hr); 0: H
 };
 
 struct StatsArgs {
@@ -115,6 +118,9 @@ struct AttnArgs {
   int ornn_bf16;        // o_rnn32 holds bf16 values (written by the chunked state pass)
   const int32_t* lo;    // [B*H][T] first visible cache entry per query (same-document
                         // masking: keys c in [lo, ntok) are visible), or null (0)
+  float* okv32;         // KV heads of another geometry than the RNN's: the attention
+                        // readout [B,T,H,dv] fp32 goes here and the mix is left to the
+                        // mix kernel (o_rnn32, o, o_rnn, o_kv unused); else null
 };
 
 struct DecodeAttnArgs {
@@ -156,10 +162,27 @@ struct DecodeCombineArgs {
   void* o_kv;
   float eps;
   int B, H, seg, nseg;
+  float* okv32;          // as AttnArgs::okv32: [B,H,dv] fp32 readout, mix left out
+};
+
+// Gated sum of the two headwise-normalised readouts when the KV heads have another
+// geometry than the RNN heads: r = Hkv / H KV heads of dv / r columns per RNN head.
+struct MixArgs {
+  const float* o_rnn32; // [B,T,H,dv] fp32, or bf16 bits with ornn_bf16
+  const float* okv32;   // [B,T,Hkv,dv/r] fp32 (the same flat layout)
+  const float* gate_rnn;// [B,T,H] or null
+  const float* gate_kv; // [B,T,Hkv] or null
+  void* o;              // [B,T,H,dv] io dtype
+  void* o_rnn;          // [B,T,H,dv] or null
+  void* o_kv;           // [B,T,Hkv,dv/r] or null
+  float eps;
+  int ntok, H, r;       // ntok = B*T
+  int ornn_bf16;
 };
 
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
+hipError_t launch_mix(int io, int dv, const MixArgs& a, hipStream_t s);
 int rnn_recurrent_slices(int dv);
 // chunked path: prep (per-chunk records, chunks in parallel), then the state pass
 hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t s);

@@ -115,10 +115,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  for (int h = tid; h < H; h += 256) {
-    const int bh = b * H + h;
-    a.chunk_count[(size_t)bh * nchunk + c] = s_cnt[h];
-    if (c == 0) a.count_in[bh] = a.count ? a.count[bh] : 0;
+  for (int h = tid; h < H; h += 256) a.chunk_count[(size_t)(b * H + h) * nchunk + c] = s_cnt[h];
+  if (c == 0) {
+    // entering count of every cache (one per KV head)
+    const int HK = a.Hkv ? a.Hkv : H;
+    for (int h = tid; h < HK; h += 256) a.count_in[b * HK + h] = a.count ? a.count[b * HK + h] : 0;
   }
 }
 
@@ -149,9 +150,12 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.H + h;
   const int nchunk = gridDim.x;
+  // the RNN head whose routing this cache follows
+  const int Hr = a.Hr ? a.Hr : a.H;
+  const int hr = h / (a.H / Hr), bhr = b * Hr + hr;
 
   int part = 0;
-  for (int i = tid; i < c; i += 256) part += a.chunk_count[(size_t)bh * nchunk + i];
+  for (int i = tid; i < c; i += 256) part += a.chunk_count[(size_t)bhr * nchunk + i];
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, kWave);
   if (lane == 0) s_red[wave] = part;
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
   if (wave == 0) {
     const int t = c * kChunk + lane;
     const bool valid = t < a.T;
-    const bool r = valid && a.routed[((size_t)b * a.T + t) * a.H + h];
+    const bool r = valid && a.routed[((size_t)b * a.T + t) * Hr + hr];
     const bool w = pend ? valid : r;                     // rows written
     const unsigned long long bal = __ballot(w);
     const unsigned long long balr = __ballot(r);

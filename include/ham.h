@@ -31,7 +31,10 @@
  *     cache and the outputs o / o_rnn / o_kv: HAM_F32 (float) or HAM_BF16
  *     (bfloat16 bits; stores round to nearest even).  beta, g, tau, gates, e and
  *     the state are always fp32.
- *   - dk, dv must each be 64 or 128.
+ *   - dk, dv must each be 64 or 128 (likewise dk_kv, dv_kv).  "KV heads" below
+ *     are the attention heads: kv_heads of them (default H) with sizes dk_kv,
+ *     dv_kv (default dk, dv); the cache, gate_kv, o_kv and the attention-path
+ *     inputs are shaped by them.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *     enqueues work; nothing blocks except ham_route_stats with rho_host != NULL.
  *   - Return codes: HAM_OK, or a negative HAM_E* code; ham_last_error() then
@@ -111,6 +114,22 @@ typedef struct {
                          per-token rule.  ham_forward and ham_route_stats take
                          whole blocks (t0 and T multiples of route_block);
                          ham_decode_step keeps the open block pending.        */
+    int kv_heads;     /* 0 (= H), or the number of attention (KV) heads: a
+                         multiple r of H.  The paper's layers have twice as many
+                         KV heads as RNN heads, each half the RNN head's size
+                         ([HAM] §4 model setup: RNN heads 256/384, KV heads
+                         128/192, the value size chosen to match the RNN's
+                         output; App. E Tab. E.1: h_KV = d_QK/128 = 2 h_RNN).  KV head j takes the routing of RNN
+                         head j / r (its cache holds the same positions) and its
+                         own attention-path q, k, v; the outputs of KV heads
+                         r*h .. r*h+r-1 lie side by side over the columns of RNN
+                         head h, so kv_heads * dv_kv must equal H * dv.  Each
+                         side is RMS-normalised per head of its own size and
+                         gated per head before the sum.                       */
+    int dk_kv, dv_kv; /* 0 (= dk, dv), or the KV heads' key and value sizes (64
+                         or 128).  When kv_heads != H or dk_kv != dk, the
+                         attention-path inputs q_attn, k_attn, v_attn are
+                         required ([B,T,kv_heads,dk_kv|dv_kv]).              */
 } ham_dims;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -127,14 +146,15 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  * [HAM] §2 (all four equations) and App. A.1 (router, masking, generation).
  *
  *   q, k, v            [B,T,H,dk|dv] io dtype, required: the RNN inputs.
- *   q_attn, k_attn, v_attn  attention-path inputs (same shapes), or NULL to
- *                      share q/k/v (the paper shares the projections).
+ *   q_attn, k_attn, v_attn  attention-path inputs [B,T,kv_heads,dk_kv|dv_kv], or
+ *                      NULL to share q/k/v (the paper shares the projections;
+ *                      required when the KV heads' geometry differs).
  *   beta, g            [B,T,H] fp32, required: write strength and log decay
  *                      (alpha = exp(g); g must be finite).
  *   tau                [H] fp32, required: routing threshold per head in e-units
  *                      (+inf routes nothing: pure gated DeltaNet; -inf routes all);
  *                      [B,T,H] with HAM_TAU_PER_TOKEN.
- *   gate_rnn, gate_kv  [B,T,H] fp32 or NULL (= 1).
+ *   gate_rnn, gate_kv  [B,T,H] and [B,T,kv_heads] fp32, or NULL (= 1).
  *   doc_start          [B,T] int32 or NULL: same-document masking of a packed
  *                      batch ([HAM] App. A.1 "FlexAttention and Block Masks").
  *                      doc_start[b,t] is the absolute position where token t's
@@ -148,13 +168,15 @@ size_t ham_forward_workspace_size(const ham_dims *dims);
  *   S_out              [B,H,dk,dv] fp32, required: state after token T-1.  May
  *                      alias S0.
  *   o                  [B,T,H,dv] io dtype, required: mixed output.
- *   o_rnn, o_kv        [B,T,H,dv] io dtype or NULL: the two readouts before the
- *                      norms (o_kv = 0 where nothing is visible).
+ *   o_rnn, o_kv        [B,T,H,dv] and [B,T,kv_heads,dv_kv] io dtype or NULL: the
+ *                      two readouts before the norms (o_kv = 0 where nothing
+ *                      is visible).
  *   e                  [B,T,H] fp32 or NULL: routing scores (output).  With
  *                      HAM_EXTERNAL_SCORES it is a required input: the caller's
  *                      scores, read and not written.
  *   routed             [B,T,H] uint8 or NULL: 1 where routed.
- *   Kc, Vc, pos, count the per-(b,h) KV cache, required.  Without HAM_CONTINUE
+ *   Kc, Vc, pos, count the per-(b, KV head) cache [B,kv_heads,cap,dk_kv|dv_kv],
+ *                      [B,kv_heads,cap], [B,kv_heads], required.  Without HAM_CONTINUE
  *                      count is output only and entries [0,count) are written;
  *                      with it, count[b,h] (<= cap) entries already exist and
  *                      new ones are appended.  Entries are in ascending original
@@ -189,16 +211,19 @@ size_t ham_decode_workspace_size(const ham_dims *dims);
  * routed; attention over the cache including the new entry; mix.  The result
  * equals ham_forward over the same token with HAM_CONTINUE.
  *
- *   q, k, v (+ optional *_attn)  [B,H,dk|dv] io dtype.
- *   beta, g, gate_rnn, gate_kv   [B,H] fp32 (gates may be NULL).
+ *   q, k, v (+ optional *_attn)  [B,H,dk|dv] io dtype ([B,kv_heads,dk_kv|dv_kv]
+ *                                for the attention-path inputs).
+ *   beta, g, gate_rnn, gate_kv   [B,H] fp32 ([B,kv_heads] for gate_kv; gates may
+ *                                be NULL).
  *   doc_start                    [B] int32 or NULL: absolute start position of
  *                                the new token's document (same-document
  *                                masking, as in ham_forward).
  *   tau                          [H] fp32 ([B,H] with HAM_TAU_PER_TOKEN).
  *   S                            [B,H,dk,dv] fp32, in/out.
- *   Kc, Vc, pos, count           cache, in/out (count[b,h] <= cap on entry).
+ *   Kc, Vc, pos, count           cache of the KV heads, in/out (count <= cap on
+ *                                entry).
  *   t_abs                        [B] int32 absolute position of the new token.
- *   o (required), o_rnn, o_kv    [B,H,dv] io dtype.
+ *   o (required), o_rnn, o_kv    [B,H,dv], [B,H,dv], [B,kv_heads,dv_kv] io dtype.
  *   e, routed                    [B,H] or NULL (with HAM_EXTERNAL_SCORES, e is
  *                                the required input score of the new token).
  *   status                       int32 scalar or NULL: set to 1 (never cleared)

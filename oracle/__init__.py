@@ -50,7 +50,7 @@ def _load():
         P = ctypes.c_void_p
         lib.ham_oracle_forward.restype = ctypes.c_int
         lib.ham_oracle_forward.argtypes = (
-            [ctypes.c_int] * 5 + [ctypes.c_double] * 3 + [ctypes.c_int] + [P] * 3 + [P] * 3 + [P] * 3
+            [ctypes.c_int] * 8 + [ctypes.c_double] * 3 + [ctypes.c_int] + [P] * 3 + [P] * 3 + [P] * 3
             + [P] * 2 + [P] * 5 + [P, ctypes.c_int, P, P, P, P] + [P] * 5
             + [ctypes.c_int, ctypes.c_int])
         _lib = lib
@@ -90,7 +90,11 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     (per-token routing), or n > 1 for block-contiguous routing ([HAM] §7): aligned
     blocks of n positions route whole on float(mean of their scores) > tau at the
     block's last token and enter the cache at that token (t0 must be a multiple of
-    n; a block still open at the end stays unrouted).  Returns a dict of float64 / int arrays:
+    n; a block still open at the end stays unrouted).  Attention heads of their own
+    geometry ([HAM] §4 model setup: twice the RNN heads, half their size): given by
+    q_attn [B,T,Hk,dkk] and v_attn [B,T,Hk,dvk] with Hk = r*H and r*dvk = dv; KV head
+    r*h + i follows RNN head h's routing; gate_kv is then [B,T,Hk], the cache and o_kv
+    are per KV head.  Returns a dict of float64 / int arrays:
     e, routed, o_rnn, o_kv, o, S, Kc, Vc, pos, count.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -99,6 +103,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     beta, g = _f64(beta), _f64(g)
     qa, ka, va = _f64(q_attn), _f64(k_attn), _f64(v_attn)
     gr, gk = _f64(gate_rnn), _f64(gate_kv)
+    Hk, dkk, dvk = (qa.shape[2], qa.shape[3], va.shape[3]) if (qa is not None and va is not None) \
+        else (H, dk, dv)
     tau = np.asarray(tau, dtype=np.float32)
     tau = np.ascontiguousarray(np.broadcast_to(tau.reshape(H) if tau.size == H else tau.reshape(B, T, H),
                                                (B, T, H)))
@@ -114,10 +120,10 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     S = np.ascontiguousarray(S)
     if cache is None:
         cap = T if cap is None else cap
-        Kc = np.zeros((B, H, cap, dk))
-        Vc = np.zeros((B, H, cap, dv))
-        pos = np.full((B, H, cap), -1, dtype=np.int64)
-        count = np.zeros((B, H), dtype=np.int64)
+        Kc = np.zeros((B, Hk, cap, dkk))
+        Vc = np.zeros((B, Hk, cap, dvk))
+        pos = np.full((B, Hk, cap), -1, dtype=np.int64)
+        count = np.zeros((B, Hk), dtype=np.int64)
     else:
         Kc = np.array(cache["Kc"], dtype=np.float64, copy=True)
         Vc = np.array(cache["Vc"], dtype=np.float64, copy=True)
@@ -128,7 +134,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
     e = np.zeros((B, T, H))
     routed = np.zeros((B, T, H), dtype=np.int8)
     o_rnn = np.zeros((B, T, H, dv))
-    o_kv = np.zeros((B, T, H, dv))
+    o_kv = np.zeros((B, T, Hk, dvk))
     o = np.zeros((B, T, H, dv))
 
     lib = _load()
@@ -138,7 +144,7 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
 
     def run(i):
         return lib.ham_oracle_forward(
-            B, T, H, dk, dv, float(scale), float(eps), float(rope_base), int(route_block),
+            B, T, H, dk, dv, Hk, dkk, dvk, float(scale), float(eps), float(rope_base), int(route_block),
             _ptr(q), _ptr(k), _ptr(v), _ptr(qa), _ptr(ka), _ptr(va),
             _ptr(beta), _ptr(g), _ptr(tau), _ptr(gr), _ptr(gk), _ptr(mo), _ptr(rs), _ptr(em),
             _ptr(t0a), _ptr(dc),
@@ -152,7 +158,8 @@ def forward(q, k, v, beta, g, tau, *, scale, eps=1e-6, rope_base=0.0, q_attn=Non
         with ThreadPoolExecutor(nthr) as ex:
             rcs = list(ex.map(run, range(nthr)))
     if any(rc == -1 for rc in rcs):
-        raise ValueError("oracle: t0 must be a multiple of route_block")
+        raise ValueError("oracle: t0 must be a multiple of route_block, and the attention heads "
+                         "must tile the RNN heads (Hk = r*H, r*dvk = dv, own q/k/v_attn)")
     if any(rc != 0 for rc in rcs):
         raise RuntimeError("oracle: KV cache capacity exceeded")
     return dict(e=e, routed=routed, o_rnn=o_rnn, o_kv=o_kv, o=o, S=S, Kc=Kc, Vc=Vc,

@@ -112,19 +112,29 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
 }
 
 /*
- * One HAM layer over heads [head_begin, head_end) of the flattened B x H grid
+ * One HAM layer over RNN heads [head_begin, head_end) of the flattened B x H grid
  * (head index = b*H + h), for T new tokens.
  *
- * Layouts (row-major): token tensors [B,T,H,d]; per-token scalars [B,T,H];
- * state S [B,H,dk,dv] (read as the entering state, overwritten with S_T);
- * cache Kc [B,H,cap,dk], Vc [B,H,cap,dv], pos [B,H,cap], count [B,H]
- * (read as the entering cache, extended in place).  t0[b] is the absolute
- * position of token 0 of sequence b.  qa/ka/va: separate attention-path
- * inputs, or NULL to share q/k/v ([HAM] §2 implementation details: shared
- * projections).  gate_rnn/gate_kv: NULL means 1.  mask_override: NULL, or a
- * [B,T,H] array of 0/1 that replaces the threshold decision (the score e is
- * still computed).  router_score: NULL, or a [B,T,H] fp32 array of routing
- * scores that replaces the fit-error score (e is then a copy of it).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
+ * Attention (KV) heads: Hk of them (0 = H) with key/value sizes dkk, dvk (0 = dk,
+ * dv); Hk = r*H.  KV head j = r*h + i follows the routing of RNN head h and holds
+ * its own cache; the values of KV heads r*h .. r*h+r-1 lie side by side over the
+ * dv = r*dvk output columns of RNN head h ([HAM] §4 model setup: twice the RNN
+ * heads at half their size, the value size chosen to match the RNN's output;
+ * App. E Tab. E.1).  Each side is RMS-normalised per head of its own size and
+ * gated per head (gate_kv per KV head) before the sum.
+ *
+ * Layouts (row-major): RNN token tensors [B,T,H,d]; attention-path tensors
+ * [B,T,Hk,dkk|dvk]; per-token scalars [B,T,H] (gate_kv [B,T,Hk]); state S
+ * [B,H,dk,dv] (read as the entering state, overwritten with S_T); cache Kc
+ * [B,Hk,cap,dkk], Vc [B,Hk,cap,dvk], pos [B,Hk,cap], count [B,Hk] (read as the
+ * entering cache, extended in place); o_kv [B,T,Hk,dvk]; o, o_rnn [B,T,H,dv].
+ * t0[b] is the absolute position of token 0 of sequence b.  qa/ka/va: separate
+ * attention-path inputs, or NULL to share q/k/v (only with the RNN's geometry;
+ * [HAM] §2 implementation details: shared projections).  gate_rnn/gate_kv: NULL
+ * means 1.  mask_override: NULL, or a [B,T,H] array of 0/1 that replaces the
+ * threshold decision (the score e is still computed).  router_score: NULL, or a
+ * [B,T,H] fp32 array of routing scores that replaces the fit-error score (e is
+ * then a copy of it).  emit: NULL, or a [B,T,H] 0/1 array; where it is 0 the
  * attention readout and the mix of that token are skipped (o_kv and o stay as
  * they were) -- this only saves time when a few sampled tokens are checked.
  * rope_base: 0 for none, else the rotary base applied to the attention-path
@@ -134,10 +144,10 @@ static void rms_normalize(const double *x, double *y, int n, double eps)
  * a block's decision is the override at its last token.
  * Outputs e, routed, o_rnn, o_kv, o may each be NULL.
  *
- * Returns 0, -1 if a t0[b] is not a multiple of route_block, or -3 if a routed
- * token finds the cache full (the head stops there).
+ * Returns 0, -1 if a t0[b] is not a multiple of route_block or the head geometry
+ * is inconsistent, or -3 if a routed token finds the cache full (the head stops).
  */
-int ham_oracle_forward(int B, int T, int H, int dk, int dv,
+int ham_oracle_forward(int B, int T, int H, int dk, int dv, int Hk, int dkk, int dvk,
                        double scale, double eps, double rope_base, int route_block,
                        const double *q, const double *k, const double *v,
                        const double *qa, const double *ka, const double *va,
@@ -151,16 +161,24 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                        double *o_rnn, double *o_kv, double *o,
                        int head_begin, int head_end)
 {
+    if (Hk <= 0) Hk = H;
+    if (dkk <= 0) dkk = dk;
+    if (dvk <= 0) dvk = dv;
+    const int r = Hk / H;
+    const int own = (Hk != H || dkk != dk || dvk != dv);
+    if (Hk % H != 0 || r * dvk != dv || (own && !(qa && ka && va)))
+        return -1;
     const double *qA = qa ? qa : q;
     const double *kA = ka ? ka : k;
     const double *vA = va ? va : v;
     double *p = (double *)malloc(sizeof(double) * (size_t)dv);
     double *orn = (double *)malloc(sizeof(double) * (size_t)dv);
-    double *okv = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *okv = (double *)malloc(sizeof(double) * (size_t)dv);    /* r heads of dvk */
     double *tmp1 = (double *)malloc(sizeof(double) * (size_t)dv);
     double *tmp2 = (double *)malloc(sizeof(double) * (size_t)dv);
     double *w = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
-    double *qrot = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *qrot = (double *)malloc(sizeof(double) * (size_t)dkk);
+    int64_t *n = (int64_t *)malloc(sizeof(int64_t) * (size_t)r);
     int status = 0;
     const int nb = route_block > 1 ? route_block : 1;
     for (int b = 0; b < B; ++b)
@@ -170,10 +188,8 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
     for (int bh = head_begin; bh < head_end; ++bh) {
         const int b = bh / H, h = bh % H;
         double *Sh = S + (size_t)bh * dk * dv;
-        double *Kh = Kc + (size_t)bh * cap * dk;
-        double *Vh = Vc + (size_t)bh * cap * dv;
-        int64_t *ph = pos + (size_t)bh * cap;
-        int64_t n = count[bh];
+        for (int i = 0; i < r; ++i)
+            n[i] = count[(size_t)b * Hk + (size_t)h * r + i];
         double bsum = 0.0;                       /* score sum of the open block */
 
         for (int t = 0; t < T; ++t) {
@@ -191,21 +207,21 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
             }
             /* routing score and decision (decision taken in fp32, like the GPU) */
             const double et = router_score ? (double)router_score[tok] : 1.0 - cosine(p, vt, dv);
-            int r;
-            const int j = (int)((t0[b] + t) % nb);   /* place in its block */
-            if (j == 0) bsum = 0.0;
+            int rt;
+            const int jb = (int)((t0[b] + t) % nb);  /* place in its block */
+            if (jb == 0) bsum = 0.0;
             bsum += et;
-            if (j != nb - 1)
-                r = 0;                                   /* the block is still open */
+            if (jb != nb - 1)
+                rt = 0;                                  /* the block is still open */
             else if (mask_override)
-                r = mask_override[tok] != 0;
+                rt = mask_override[tok] != 0;
             else
-                r = ((float)(bsum / nb) > tau[tok]);
+                rt = ((float)(bsum / nb) > tau[tok]);
             if (e) e[tok] = et;
             if (routed) {
-                routed[tok] = (int8_t)r;
-                if (j == nb - 1)                         /* the whole block shares it */
-                    for (int i = 1; i < nb; ++i) routed[tok - (size_t)i * H] = (int8_t)r;
+                routed[tok] = (int8_t)rt;
+                if (jb == nb - 1)                        /* the whole block shares it */
+                    for (int i = 1; i < nb; ++i) routed[tok - (size_t)i * H] = (int8_t)rt;
             }
 
             /* gated delta update: S = alpha*S + beta*k*(v - alpha*p)^T
@@ -224,76 +240,89 @@ int ham_oracle_forward(int B, int T, int H, int dk, int dv,
                 orn[j] = acc;
             }
 
-            /* append the routed token (with blocks: the whole block, at its last
-             * token), ascending original position */
-            if (r) {
-                for (int ta = t - (nb - 1); ta <= t; ++ta) {
-                    const size_t tk = ((size_t)b * T + ta) * H + h;
-                    if (n >= cap) { status = -3; break; }
-                    if (rope_base > 0.0)
-                        rope_rotate(kA + tk * dk, Kh + (size_t)n * dk, dk, (double)(t0[b] + ta), rope_base);
-                    else
-                        memcpy(Kh + (size_t)n * dk, kA + tk * dk, sizeof(double) * (size_t)dk);
-                    memcpy(Vh + (size_t)n * dv, vA + tk * dv, sizeof(double) * (size_t)dv);
-                    ph[n] = t0[b] + ta;
-                    n += 1;
+            /* per KV head of this RNN head: append, then attend */
+            for (int jj = 0; jj < r; ++jj) {
+                const size_t hk = (size_t)b * Hk + (size_t)h * r + jj;   /* [B,Hk] index */
+                double *Kh = Kc + hk * cap * dkk;
+                double *Vh = Vc + hk * cap * dvk;
+                int64_t *ph = pos + hk * cap;
+                /* append the routed token (with blocks: the whole block, at its last
+                 * token), ascending original position */
+                if (rt) {
+                    for (int ta = t - (nb - 1); ta <= t; ++ta) {
+                        const size_t tk = ((size_t)b * T + ta) * Hk + (size_t)h * r + jj;
+                        if (n[jj] >= cap) { status = -3; break; }
+                        if (rope_base > 0.0)
+                            rope_rotate(kA + tk * dkk, Kh + (size_t)n[jj] * dkk, dkk,
+                                        (double)(t0[b] + ta), rope_base);
+                        else
+                            memcpy(Kh + (size_t)n[jj] * dkk, kA + tk * dkk, sizeof(double) * (size_t)dkk);
+                        memcpy(Vh + (size_t)n[jj] * dvk, vA + tk * dvk, sizeof(double) * (size_t)dvk);
+                        ph[n[jj]] = t0[b] + ta;
+                        n[jj] += 1;
+                    }
+                    if (status) break;
                 }
-                if (status) break;
-            }
-
-            if (emit && !emit[tok]) {
-                if (o_rnn) memcpy(o_rnn + tok * dv, orn, sizeof(double) * (size_t)dv);
-                continue;
-            }
-            /* softmax attention over the cached (routed) keys, all at positions <= t */
-            const double *qat = qA + tok * dk;
-            if (rope_base > 0.0) {
-                rope_rotate(qat, qrot, dk, (double)(t0[b] + t), rope_base);
-                qat = qrot;
-            }
-            for (int j = 0; j < dv; ++j) okv[j] = 0.0;
-            {
+                if (emit && !emit[tok]) continue;
+                /* softmax attention over the cached (routed) keys, all at positions <= t */
+                const size_t tka = ((size_t)b * T + t) * Hk + (size_t)h * r + jj;
+                const double *qat = qA + tka * dkk;
+                if (rope_base > 0.0) {
+                    rope_rotate(qat, qrot, dkk, (double)(t0[b] + t), rope_base);
+                    qat = qrot;
+                }
+                double *ok = okv + (size_t)jj * dvk;
+                for (int j = 0; j < dvk; ++j) ok[j] = 0.0;
                 /* first position of this token's document (none: the whole cache) */
                 const int64_t ds = doc_start ? doc_start[(size_t)b * T + t] : INT64_MIN;
                 double m = -INFINITY;
                 int64_t nvis = 0;
-                for (int64_t c = 0; c < n; ++c) {
+                for (int64_t c = 0; c < n[jj]; ++c) {
                     if (ph[c] < ds) { w[c] = -INFINITY; continue; }   /* another document */
-                    double s = 0.0;
-                    for (int i = 0; i < dk; ++i)
-                        s += qat[i] * Kh[(size_t)c * dk + i];
-                    w[c] = scale * s;
+                    double sc = 0.0;
+                    for (int i = 0; i < dkk; ++i)
+                        sc += qat[i] * Kh[(size_t)c * dkk + i];
+                    w[c] = scale * sc;
                     if (w[c] > m) m = w[c];
                     nvis += 1;
                 }
                 if (nvis > 0) {
                     double den = 0.0;
-                    for (int64_t c = 0; c < n; ++c) {
+                    for (int64_t c = 0; c < n[jj]; ++c) {
                         w[c] = (w[c] == -INFINITY) ? 0.0 : exp(w[c] - m);
                         den += w[c];
                     }
-                    for (int64_t c = 0; c < n; ++c) {
+                    for (int64_t c = 0; c < n[jj]; ++c) {
                         const double wc = w[c] / den;
-                        for (int j = 0; j < dv; ++j)
-                            okv[j] += wc * Vh[(size_t)c * dv + j];
+                        for (int j = 0; j < dvk; ++j)
+                            ok[j] += wc * Vh[(size_t)c * dvk + j];
                     }
                 }
             }
+            if (status) break;
 
-            /* headwise RMS norms and the two independent gates */
+            if (emit && !emit[tok]) {
+                if (o_rnn) memcpy(o_rnn + tok * dv, orn, sizeof(double) * (size_t)dv);
+                continue;
+            }
+            /* headwise RMS norms (each side per head of its own size) and the gates */
             const double gr = gate_rnn ? gate_rnn[tok] : 1.0;
-            const double gk = gate_kv ? gate_kv[tok] : 1.0;
             rms_normalize(orn, tmp1, dv, eps);
-            rms_normalize(okv, tmp2, dv, eps);
-            for (int j = 0; j < dv; ++j) {
-                if (o_rnn) o_rnn[tok * dv + j] = orn[j];
-                if (o_kv) o_kv[tok * dv + j] = okv[j];
-                if (o) o[tok * dv + j] = gr * tmp1[j] + gk * tmp2[j];
+            for (int jj = 0; jj < r; ++jj)
+                rms_normalize(okv + (size_t)jj * dvk, tmp2 + (size_t)jj * dvk, dvk, eps);
+            for (int c = 0; c < dv; ++c) {
+                const int jj = c / dvk;
+                const size_t tka = ((size_t)b * T + t) * Hk + (size_t)h * r + jj;
+                const double gk = gate_kv ? gate_kv[tka] : 1.0;
+                if (o_rnn) o_rnn[tok * dv + c] = orn[c];
+                if (o_kv) o_kv[tka * dvk + (c - jj * dvk)] = okv[c];
+                if (o) o[tok * dv + c] = gr * tmp1[c] + gk * tmp2[c];
             }
         }
-        count[bh] = n;
+        for (int i = 0; i < r; ++i)
+            count[(size_t)b * Hk + (size_t)h * r + i] = n[i];
         if (status) break;
     }
-    free(p); free(orn); free(okv); free(tmp1); free(tmp2); free(w); free(qrot);
+    free(p); free(orn); free(okv); free(tmp1); free(tmp2); free(w); free(qrot); free(n);
     return status;
 }

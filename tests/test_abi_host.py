@@ -186,3 +186,27 @@ def test_route_block_checks():
     s = [fake] * 11
     assert L.ham_route_stats(ctypes.byref(dims(T=320, cap=320, route_block=16)), *s, ctypes.c_float(1e-5),
                              None, fake, 1 << 40, None) == _lib.HAM_EUNSUPPORTED
+
+
+def test_kv_head_geometry_checks():
+    """Attention heads of their own geometry: a multiple of H, sizes 64 or 128, value
+    columns tiling the RNN heads' output, and their own q/k/v inputs."""
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.ham_forward_workspace_size(ctypes.byref(dims(kv_heads=8, dv_kv=64))) > 0
+    assert L.ham_forward_workspace_size(ctypes.byref(dims(kv_heads=8, dv_kv=64))) > \
+        L.ham_forward_workspace_size(ctypes.byref(dims()))           # the readout scratch
+    assert L.ham_decode_workspace_size(ctypes.byref(dims(kv_heads=8, dk_kv=64, dv_kv=64))) > 0
+    for bad, code in ((dims(kv_heads=6, dv_kv=64), _lib.HAM_EUNSUPPORTED),     # not a multiple of H
+                      (dims(kv_heads=8), _lib.HAM_EUNSUPPORTED),               # 8*128 != 4*128
+                      (dims(dk_kv=96), _lib.HAM_EUNSUPPORTED),
+                      (dims(kv_heads=-1), _lib.HAM_EINVAL)):
+        assert L.ham_forward_workspace_size(ctypes.byref(bad)) == 0
+        assert _fwd(bad) == code
+    a = [fake] * 24
+    a[3] = None                                        # q_attn
+    assert _fwd(dims(kv_heads=8, dv_kv=64), a) == _lib.HAM_EINVAL and "q_attn" in _msg()
+    assert _fwd(dims(dk_kv=64), a) == _lib.HAM_EINVAL
+    d = [fake] * 26
+    d[5] = None                                        # v_attn of the decode step
+    assert L.ham_decode_step(ctypes.byref(dims(kv_heads=8, dv_kv=64)), *d, 1 << 40, None) == _lib.HAM_EINVAL

@@ -1,0 +1,158 @@
+"""GPU parity of attention heads with their own geometry.
+
+"Hybrid Associative Memories" §4 (model setup) and App. E Tab. E.1: the HAM layer has
+twice as many KV heads as RNN heads, each half the RNN head's size (RNN 256/384, KV
+128/192), the KV value size chosen so that the KV heads' outputs match the RNN's.
+Built here at the head sizes the kernels take: RNN heads d_v = 128, KV heads d_v = 64
+(r = 2 per RNN head) with d_k 64 or 128 on either side; also one KV head per RNN head
+with its own key size.  KV head r*h + i follows the routing of RNN head h and holds
+its own cache; each side is normalised per head of its own size and gated per head.
+Compared with the oracle through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import attention_sequence_mixing_amd as ham
+from attention_sequence_mixing_amd.inputs import (make_inputs, make_doc_start, make_router_scores,
+                                                  tau_for_rho)
+from parity import check_forward, check_routing, np_of, rel_err_slices, to_dev, TOL, block_means
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+INF = np.float32(np.inf)
+
+
+def _dt(dtype):
+    return "f32" if dtype == torch.float32 else "bf16"
+
+
+def _i32(x):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, np.int32))).to(DEV)
+
+
+def _tau(inp, rho, scale, n=0):
+    H = inp["q"].shape[2]
+    e = oracle.forward(**inp, tau=np.full(H, INF, np.float32), scale=scale)["e"]
+    if n > 1:
+        return tau_for_rho(block_means(e, n)[:, ::n], rho)
+    return tau_for_rho(e, rho)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,r,dkk,rec,base,blk,docs", [
+    (2, 200, 2, 128, 128, 2, 128, False, 0.0, 0, False),
+    (1, 130, 3, 64, 128, 2, 64, False, 500000.0, 0, False),
+    (2, 150, 2, 128, 128, 2, 64, True, 0.0, 0, False),
+    (1, 256, 2, 128, 128, 2, 128, False, 10000.0, 16, True),
+    (2, 65, 1, 64, 128, 2, 128, False, 0.0, 0, True),
+    (2, 100, 2, 128, 64, 1, 64, False, 0.0, 0, False),
+])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kv_heads_forward(B, T, H, dk, dv, r, dkk, rec, base, blk, docs, dtype):
+    seed = 180 + T + dkk
+    Hk, dvk = r * H, dv // r
+    inp = make_inputs(B, T, H, dk, dv, dtype=_dt(dtype), seed=seed)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype=_dt(dtype), seed=seed + 1)
+    scale = dkk ** -0.5
+    tau = _tau(inp, 0.5, scale, blk)
+    rng = np.random.default_rng(seed)
+    gr = rng.random((B, T, H)).astype(np.float32)
+    gk = rng.random((B, T, Hk)).astype(np.float32)
+    ds = make_doc_start(B, T, 40, seed) if docs else None
+    t, ta = to_dev(inp, dtype, DEV), to_dev(att, dtype, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"],
+                          gate_rnn=torch.from_numpy(gr).to(DEV), gate_kv=torch.from_numpy(gk).to(DEV),
+                          rope_base=base, route_block=blk, doc_start=_i32(ds) if docs else None,
+                          force_recurrent=rec, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    assert tuple(out["o_kv"].shape) == (B, T, Hk, dvk) and tuple(out["count"].shape) == (B, Hk)
+    res = check_forward(out, inp, tau, dtype, scale=scale, gates=(gr, gk), attn=att, rope_base=base,
+                        route_block=blk, doc_start=ds)
+    cnt = out["count"].cpu().numpy()
+    for i in range(r):                                 # KV heads of one RNN head share the routing
+        assert np.array_equal(cnt[:, i::r], res["ref"]["count"][:, i::r])
+        assert np.array_equal(cnt[:, i::r], cnt[:, 0::r])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kv_heads_continuation_and_decode(dtype):
+    """A forward prefix, a continued forward call, then decode steps: every output
+    equals one oracle forward over the whole sequence."""
+    B, H, dk, dv, r, dkk = 2, 2, 128, 128, 2, 64
+    Hk, dvk = r * H, dv // r
+    T1, T2, steps = 96, 70, 12
+    T = T1 + T2 + steps
+    inp = make_inputs(B, T, H, dk, dv, dtype=_dt(dtype), seed=190)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype=_dt(dtype), seed=191)
+    scale = dkk ** -0.5
+    tau = _tau(inp, 0.5, scale)
+    base = 500000.0
+    t, ta = to_dev(inp, dtype, DEV), to_dev(att, dtype, DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+
+    def sl(x, a, b):
+        return {n: v[:, a:b].contiguous() for n, v in x.items()}
+
+    p1, a1 = sl(t, 0, T1), sl(ta, 0, T1)
+    o1 = ham.ham_forward(p1["q"], p1["k"], p1["v"], p1["beta"], p1["g"], tau_d, scale=scale, cap=T,
+                         q_attn=a1["q"], k_attn=a1["k"], v_attn=a1["v"], rope_base=base)
+    cache = {n: o1[n] for n in ("Kc", "Vc", "pos", "count")}
+    p2, a2 = sl(t, T1, T1 + T2), sl(ta, T1, T1 + T2)
+    o2 = ham.ham_forward(p2["q"], p2["k"], p2["v"], p2["beta"], p2["g"], tau_d, scale=scale,
+                         q_attn=a2["q"], k_attn=a2["k"], v_attn=a2["v"], S0=o1["S"].clone(), cache=cache,
+                         t0=T1, rope_base=base)
+    S = o2["S"]
+    plan = ham.DecodePlan(B, H, dk, dv, T, dtype, DEV, scale=scale, rope_base=base, kv_heads=Hk,
+                          dk_kv=dkk, dv_kv=dvk, want_o_kv=True)
+    es, rs, os_, okv = [], [], [], []
+    for s in range(steps):
+        tt = T1 + T2 + s
+        x = {n: t[n][:, tt].contiguous() for n in t}
+        xa = {n: ta[n][:, tt].contiguous() for n in ("q", "k", "v")}
+        plan(x["q"], x["k"], x["v"], x["beta"], x["g"], tau_d, S, cache["Kc"], cache["Vc"], cache["pos"],
+             cache["count"], torch.full((B,), tt, dtype=torch.int32, device=DEV),
+             q_attn=xa["q"], k_attn=xa["k"], v_attn=xa["v"])
+        es.append(plan.e.cpu().numpy()); rs.append(plan.routed.cpu().numpy())
+        os_.append(np_of(plan.o)); okv.append(np_of(plan.o_kv))
+    torch.cuda.synchronize()
+    assert int(plan.status.item()) == 0
+    e_all = np.concatenate([o1["e"].cpu().numpy(), o2["e"].cpu().numpy(), np.stack(es, 1)], 1)
+    r_all = np.concatenate([o1["routed"].cpu().numpy(), o2["routed"].cpu().numpy(), np.stack(rs, 1)], 1)
+    okw = dict(tau=tau, scale=scale, cap=T, rope_base=base, q_attn=att["q"], k_attn=att["k"],
+               v_attn=att["v"])
+    ref = oracle.forward(**inp, **okw)
+    if check_routing(e_all, r_all, ref, tau):
+        ref = oracle.forward(**inp, mask_override=r_all, **okw)
+    assert rel_err_slices(np_of(o2["o"]), ref["o"][:, T1:T1 + T2], 2) < TOL[dtype]
+    assert rel_err_slices(np.stack(os_, 1), ref["o"][:, T1 + T2:], 2) < TOL[dtype]
+    assert rel_err_slices(np.stack(okv, 1), ref["o_kv"][:, T1 + T2:], 2) < TOL[dtype]
+    assert np.array_equal(cache["count"].cpu().numpy(), ref["count"])
+    pos = cache["pos"].cpu().numpy()
+    for b in range(B):
+        for j in range(Hk):
+            c = ref["count"][b, j]
+            assert np.array_equal(pos[b, j, :c], ref["pos"][b, j, :c])
+
+
+def test_kv_heads_one_routed_set_per_layer():
+    """A learned router's per-token score broadcast over the RNN heads with one tau:
+    every KV head of the layer caches the same positions."""
+    B, T, H, dk, dv, r, dkk = 2, 256, 4, 128, 128, 2, 128
+    Hk, dvk = r * H, dv // r
+    inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=195)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype="bf16", seed=196)
+    rs = np.repeat(make_router_scores(B, T, 1, 195), H, axis=2)
+    tau = np.full(H, np.float32(np.quantile(rs[..., 0], 0.5)), np.float32)
+    t, ta = to_dev(inp, torch.bfloat16, DEV), to_dev(att, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=dkk ** -0.5, q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"],
+                          router_scores=torch.from_numpy(rs).to(DEV), want_o_kv=True)
+    torch.cuda.synchronize()
+    check_forward(out, inp, tau, torch.bfloat16, scale=dkk ** -0.5, attn=att, router_score=rs)
+    cnt = out["count"].cpu().numpy()
+    pos = out["pos"].cpu().numpy()
+    assert (cnt == cnt[:, :1]).all()
+    for j in range(1, Hk):
+        assert np.array_equal(pos[:, j, :cnt[0, 0]], pos[:, 0, :cnt[0, 0]])

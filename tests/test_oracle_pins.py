@@ -618,3 +618,53 @@ def test_block_routing_override_and_continuation():
     np.testing.assert_array_equal(bpart["count"], one["count"])
     with pytest.raises(ValueError):
         oracle.forward(**inp, tau=tau, scale=0.5, route_block=n, t0=4)
+
+
+# --- attention heads of their own geometry ("Hybrid Associative Memories" §4, Tab. E.1) ---
+def _rms_rows(x, eps=1e-6):
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+
+
+@pytest.mark.parametrize("H,dk,dv,r,dkk", [(2, 8, 8, 2, 4), (3, 6, 8, 2, 6), (2, 8, 6, 1, 4)])
+def test_kv_head_geometry_dense_reference(H, dk, dv, r, dkk):
+    """r KV heads per RNN head, each with its own q/k/v and dv/r value columns: KV head
+    j attends over the positions routed by RNN head j // r with its own keys; o is the
+    RNN head's normalised readout plus, column by column, the normalised readout of
+    the KV head that owns the column, each gated per head; the RNN side is untouched."""
+    B, T = 2, 45
+    Hk, dvk = r * H, dv // r
+    rng = np.random.default_rng(170 + r + dkk)
+    inp = make_inputs(B, T, H, dk, dv, seed=170 + dk)
+    att = make_inputs(B, T, Hk, dkk, dvk, seed=171 + dk)
+    mask = (rng.random((B, T, H)) < 0.5).astype(np.int8)
+    gr = rng.random((B, T, H))
+    gk = rng.random((B, T, Hk))
+    out = oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5, mask_override=mask,
+                         q_attn=att["q"], k_attn=att["k"], v_attn=att["v"], gate_rnn=gr, gate_kv=gk)
+    plain = oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5, mask_override=mask)
+    for name in ("e", "o_rnn", "S", "routed"):
+        np.testing.assert_array_equal(out[name], plain[name])
+    assert out["o_kv"].shape == (B, T, Hk, dvk) and out["Kc"].shape[:2] == (B, Hk)
+    for b in range(B):
+        for j in range(Hk):
+            m = mask[b, :, j // r].astype(bool)
+            allowed = np.tril(np.ones((T, T), bool)) & m[None, :]
+            ref = masked_softmax_attention(att["q"][b, :, j].astype(np.float64), att["k"][b, :, j].astype(np.float64),
+                                           att["v"][b, :, j].astype(np.float64), allowed, 0.5)
+            np.testing.assert_allclose(out["o_kv"][b, :, j], ref, rtol=1e-12, atol=1e-12)
+            nz = np.nonzero(m)[0]
+            assert out["count"][b, j] == len(nz)
+            assert out["pos"][b, j, :len(nz)].tolist() == nz.tolist()
+            np.testing.assert_array_equal(out["Kc"][b, j, :len(nz)], att["k"][b, nz, j])
+    want = np.empty((B, T, H, dv))
+    rn = _rms_rows(out["o_rnn"])
+    kn = _rms_rows(out["o_kv"])
+    for h in range(H):
+        for c in range(dv):
+            j = h * r + c // dvk
+            want[:, :, h, c] = gr[:, :, h] * rn[:, :, h, c] + gk[:, :, j] * kn[:, :, j, c % dvk]
+    np.testing.assert_allclose(out["o"], want, rtol=1e-12, atol=1e-12)
+    if r > 1:
+        with pytest.raises(ValueError):                                # columns must tile
+            oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5, q_attn=att["q"][:, :, :H],
+                           k_attn=att["k"][:, :, :H], v_attn=att["v"][:, :, :H])
