@@ -195,7 +195,7 @@ def bench_forward(args, dev):
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
-    router = rope = packed = blocks = None
+    router = rope = packed = blocks = kvh = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
         router = bench_router(args, dev, w, t)
@@ -208,24 +208,37 @@ def bench_forward(args, dev):
         means = st["e"].view(w.B, w.T // nb, nb, w.H).mean(dim=2).contiguous()
         tau_b = ham.ham_select_tau(means, w.rho)
         blocks = bench_variant(args, dev, w, t, tau_b, f"block_routing{nb}", route_block=nb)
+        # the paper's head layout at the kernels' sizes: twice the RNN heads as KV heads,
+        # key size 128, value size half the RNN's (their outputs tile the RNN heads')
+        from attention_sequence_mixing_amd.inputs import make_inputs_torch
+        att = make_inputs_torch(w.B, w.T, 2 * w.H, w.d, w.d // 2, dtype="bf16", seed=w.seed + 3,
+                                device=dev)
+        kvh = bench_variant(args, dev, w, t, tau, f"kv_heads{2 * w.H}_dk{w.d}_dv{w.d // 2}", attn=att)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router, rope=rope, packed=packed, blocks=blocks)
+                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh)
 
 
-def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0):
+def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0,
+                  attn=None):
     """The same layer with the fit-error routing, plus RoPE on the attention query and
-    key (rope_base > 0), same-document masking of packed sequences (doc_start [B,T])
-    and/or block-contiguous routing (route_block > 1, with its own tau)."""
+    key (rope_base > 0), same-document masking of packed sequences (doc_start [B,T]),
+    block-contiguous routing (route_block > 1, with its own tau) and/or attention
+    heads of their own geometry (attn: dict q, k, v of the attention path)."""
     import torch
     import attention_sequence_mixing_amd as ham
     from attention_sequence_mixing_amd import _lib
-    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale,
-                           rope_base=rope_base, route_block=route_block)
+    kv = {} if attn is None else dict(kv_heads=attn["q"].shape[2], dk_kv=attn["q"].shape[3],
+                                      dv_kv=attn["v"].shape[3])
+    scale = w.attn_scale if attn is None else attn["q"].shape[3] ** -0.5
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=scale,
+                           rope_base=rope_base, route_block=route_block, **kv)
     ds = None if doc_start is None else torch.from_numpy(doc_start.astype(np.int32)).to(dev)
+    qa, ka, va = (None, None, None) if attn is None else (attn["q"], attn["k"], attn["v"])
 
     def step():
-        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, doc_start=ds)
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, doc_start=ds, q_attn=qa, k_attn=ka,
+             v_attn=va)
 
     for _ in range(args.warmup):
         step()
@@ -241,7 +254,7 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, ro
     ms = e0.elapsed_time(e1) / args.steps
     stages = collect_stages(lib, args.steps)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
-    rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
+    rho = float(plan.count.sum().item()) / (w.B * w.T * plan.count.shape[1])
     log(f"[bench] {label}: {ms:.3f} ms/step, rho {rho:.4f}, "
         f"stages {dict(zip(names, [round(x, 4) for x in stages]))}")
     return dict(workload=f"{w.name}_{label}", ms_per_step=round(ms, 4),
@@ -492,6 +505,7 @@ def main():
         "rope": res["rope"],
         "packed_docs": res["packed"],
         "block_routing": res["blocks"],
+        "kv_heads": res["kvh"],
         "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
