@@ -37,8 +37,11 @@ int check_dims(const ham_dims* d, bool need_T) {
   if (d->H > 4096) return fail(HAM_EUNSUPPORTED, "H must be <= 4096 (H=%d)", d->H);
   if (d->B <= 0 || d->H <= 0 || (need_T && d->T <= 0))
     return fail(HAM_EINVAL, "B, T and H must be positive (B=%d T=%d H=%d)", d->B, d->T, d->H);
-  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
-    return fail(HAM_EUNSUPPORTED, "dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
+  // 64 or 128 each; or the RNN heads of the paper's layer, dk = 256 with dv = 384
+  // (token-serial RNN kernel)
+  if (!(((d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128)) || (d->dk == 256 && d->dv == 384)))
+    return fail(HAM_EUNSUPPORTED, "dk and dv must be 64 or 128, or dk=256 with dv=384 (dk=%d dv=%d)",
+                d->dk, d->dv);
   if (d->io_dtype != HAM_F32 && d->io_dtype != HAM_BF16)
     return fail(HAM_EUNSUPPORTED, "io_dtype must be HAM_F32 or HAM_BF16 (got %d)", d->io_dtype);
   if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES | HAM_TAU_PER_TOKEN))
@@ -56,8 +59,10 @@ int check_dims(const ham_dims* d, bool need_T) {
   {
     const int HK = d->kv_heads > 0 ? d->kv_heads : d->H;
     const int DKK = d->dk_kv > 0 ? d->dk_kv : d->dk, DVK = d->dv_kv > 0 ? d->dv_kv : d->dv;
-    if ((DKK != 64 && DKK != 128) || (DVK != 64 && DVK != 128))
-      return fail(HAM_EUNSUPPORTED, "dk_kv and dv_kv must be 64 or 128 (dk_kv=%d dv_kv=%d)", DKK, DVK);
+    // 64 or 128 each; or the KV heads of the paper's layer, dk_kv = 128 with dv_kv = 192
+    if (!(((DKK == 64 || DKK == 128) && (DVK == 64 || DVK == 128)) || (DKK == 128 && DVK == 192)))
+      return fail(HAM_EUNSUPPORTED, "dk_kv and dv_kv must be 64 or 128, or 128 with 192 (dk_kv=%d "
+                                    "dv_kv=%d)", DKK, DVK);
     if (HK % d->H)
       return fail(HAM_EUNSUPPORTED, "kv_heads (%d) must be a multiple of H (%d)", HK, d->H);
     if ((long long)HK * DVK != (long long)d->H * d->dv)
@@ -135,7 +140,7 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   FwdLayout L{};
   size_t off = 0;
   L.o_rnn32 = off;     off += up256(BTH * d->dv * sizeof(float));
-  L.score = off;       off += up256(BTH * ham::kScoreSlicesMax * sizeof(float4));
+  L.score = off;       off += up256(BTH * (d->dv / 16) * sizeof(float4));
   L.e = off;           off += up256(BTH * sizeof(float));
   L.routed = off;      off += up256(BTH);
   L.chunk_count = off; off += up256(BH * nchunk * sizeof(int32_t));
@@ -146,7 +151,8 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (dk_kv(d) / 2) * sizeof(float2)) : 0;
   L.okv32 = off;       off += (!with_state && split_heads(d)) ? up256(BTH * d->dv * sizeof(float)) : 0;
   L.prep = off;
-  if (d->io_dtype == HAM_BF16 && d->T > ham::kChunk) off += up256(BH * nchunk * ham::kPrepRecordBytes);
+  if (d->T > ham::kChunk && ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv))
+    off += up256(BH * nchunk * ham::kPrepRecordBytes);
   L.seg = seg_plan(d);
   const size_t P = (size_t)L.seg.nseg;
   L.seg_a = off;       off += P > 1 ? up256((P - 1) * BH * d->dk * d->dk * sizeof(float)) : 0;
@@ -167,7 +173,7 @@ DecLayout dec_layout(const ham_dims* d) {
   L.nseg = (d->cap + ham::kDecodeSeg - 1) / ham::kDecodeSeg;
   size_t off = 0;
   L.o_rnn32 = off;     off += up256(BH * d->dv * sizeof(float));
-  L.score = off;       off += up256(BH * ham::kScoreSlicesMax * sizeof(float4));
+  L.score = off;       off += up256(BH * (d->dv / 16) * sizeof(float4));
   L.e = off;           off += up256(BH * sizeof(float));
   L.routed = off;      off += up256(BH);
   L.chunk_count = off; off += up256(BH * sizeof(int32_t));

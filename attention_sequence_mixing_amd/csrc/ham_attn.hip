@@ -16,8 +16,9 @@
 // per-query softmax state lives in the lanes that later hold that query's output
 // column of O^T = V^T P^T: no data movement between the two products.  bf16 I/O
 // (attn_bf16_v5_kernel): 4 waves x 32 queries of one (b,h) per workgroup on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  fp32 I/O (attn_f32_kernel): 4
-// waves x 16 queries on v_mfma_f32_16x16x4f32.
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  fp32 I/O, and bf16 value rows of
+// 192 elements (attn_kernel): 4 waves x 16 queries of one (b,h) per workgroup, on
+// v_mfma_f32_16x16x4f32 (fp32) or v_mfma_f32_16x16x32_bf16 (bf16).
 #include "ham_common.h"
 #include "ham_internal.h"
 
@@ -25,9 +26,25 @@ namespace ham {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// LDS tile of the fp32 kernel: BN cache rows of K and V, rows padded by 4 floats.
+template <class IO>
+struct AttnTile;
+template <>
+struct AttnTile<IoBF16> { static constexpr int BN = 64; };
+template <>
+struct AttnTile<IoF32> { static constexpr int BN = 32; };
+
+template <class IO, int DK, int DV>
+struct AttnSmem;
 template <int DK, int DV>
-struct AttnSmemF32 {
+struct AttnSmem<IoBF16, DK, DV> {
+  static constexpr int BN = 64;
+  static constexpr int KS = DK + 8;   // K row stride (elements), padded
+  static constexpr int VS = BN + 8;   // V^T row stride (elements), padded
+  uint16_t K[BN * KS];
+  uint16_t Vt[DV * VS];
+};
+template <int DK, int DV>
+struct AttnSmem<IoF32, DK, DV> {
   static constexpr int BN = 32;
   static constexpr int KS = DK + 4;
   static constexpr int VS = DV + 4;
@@ -38,9 +55,31 @@ struct AttnSmemF32 {
 // Stage rows [c0, c0+BN) of this head's cache into LDS; rows at or beyond nmax
 // are zero so masked lanes multiply finite values.
 template <int DK, int DV>
-HAM_DEVICE void stage_kv(AttnSmemF32<DK, DV>& sm, const float* Kh, const float* Vh,
+HAM_DEVICE void stage_kv(AttnSmem<IoBF16, DK, DV>& sm, const uint16_t* Kh, const uint16_t* Vh,
                          int c0, int nmax, int tid) {
-  constexpr int BN = AttnSmemF32<DK, DV>::BN, KS = DK + 4, VS = DV + 4;
+  constexpr int BN = 64, KS = DK + 8, VS = BN + 8;
+  constexpr int KU = DK / 8, VU = DV / 8;
+#pragma unroll
+  for (int u = tid; u < BN * KU; u += 256) {
+    const int row = u / KU, col = (u % KU) * 8;
+    u16x8 x = (u16x8)(0);
+    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Kh + (size_t)(c0 + row) * DK + col);
+    *reinterpret_cast<u16x8*>(&sm.K[row * KS + col]) = x;
+  }
+#pragma unroll
+  for (int u = tid; u < BN * VU; u += 256) {
+    const int row = u / VU, col = (u % VU) * 8;
+    u16x8 x = (u16x8)(0);
+    if (c0 + row < nmax) x = *reinterpret_cast<const u16x8*>(Vh + (size_t)(c0 + row) * DV + col);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.Vt[(col + j) * VS + row] = x[j];
+  }
+}
+
+template <int DK, int DV>
+HAM_DEVICE void stage_kv(AttnSmem<IoF32, DK, DV>& sm, const float* Kh, const float* Vh,
+                         int c0, int nmax, int tid) {
+  constexpr int BN = 32, KS = DK + 4, VS = DV + 4;
   constexpr int KU = DK / 4, VU = DV / 4;
 #pragma unroll
   for (int u = tid; u < BN * KU; u += 256) {
@@ -58,13 +97,22 @@ HAM_DEVICE void stage_kv(AttnSmemF32<DK, DV>& sm, const float* Kh, const float* 
   }
 }
 
-// fp32 I/O: 4 waves x 16 queries of one (b,h) per workgroup, exact online softmax.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
-  constexpr int BN = AttnSmemF32<DK, DV>::BN;
+// Query fragments: the B operand of S^T = K Q^T for this lane's query.
+template <int DK>
+struct QFragBF16 { bf16x8 x[DK / 32]; };
+template <int DK>
+struct QFragF32 { float x[DK / 4]; };
+
+// Generic kernel: every fp32 shape, and bf16 shapes the tiled kernel below does not
+// take (value rows that are not a power-of-two number of 16-byte chunks).
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  using E = typename IO::elem;
+  constexpr bool kBF16 = (IO::kBytes == 2);
+  constexpr int BN = AttnTile<IO>::BN;
   constexpr int NT = BN / 16;              // 16-key subtiles per tile
   constexpr int DT = DV / 16;              // 16-wide d tiles of the output
-  __shared__ AttnSmemF32<DK, DV> sm;
+  __shared__ AttnSmem<IO, DK, DV> sm;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, qn = lane & 15;
@@ -75,9 +123,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int qb = nqb - 1 - (lin % nqb);
   const int b = bh / a.H, h = bh % a.H;
 
-  const float* __restrict__ qp = static_cast<const float*>(a.q);
-  const float* __restrict__ Kh = static_cast<const float*>(a.Kc) + (size_t)bh * a.cap * DK;
-  const float* __restrict__ Vh = static_cast<const float*>(a.Vc) + (size_t)bh * a.cap * DV;
+  const E* __restrict__ qp = static_cast<const E*>(a.q);
+  const E* __restrict__ Kh = static_cast<const E*>(a.Kc) + (size_t)bh * a.cap * DK;
+  const E* __restrict__ Vh = static_cast<const E*>(a.Vc) + (size_t)bh * a.cap * DV;
   const int32_t* ntok = a.ntok + (size_t)bh * a.T;
 
   const int t = qb * 64 + wave * 16 + qn;           // this lane's query
@@ -96,28 +144,45 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     for (int o = 1; o < 64; o <<= 1) m = min(m, __shfl_xor(m, o, kWave));
     if (lane == 0) s_lomin[wave] = m;
     __syncthreads();
-    it0 = min(min(s_lomin[0], s_lomin[1]), min(s_lomin[2], s_lomin[3])) / BN;
+    it0 = min(min(s_lomin[0], s_lomin[1]), min(s_lomin[2], s_lomin[3])) / AttnTile<IO>::BN;
   }
   const size_t tok = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
 
-  // this lane's query fragment: the B operand of S^T = K Q^T.  With a rotary
-  // table the query is turned at its position first (pairs of consecutive
-  // elements; the table row of local token t).
-  float qf[DK / 4];
+  // load this lane's query fragment
+  QFragBF16<DK> qfb;
+  QFragF32<DK> qff;
+  // with a rotary table the query is turned at its position first (pairs of
+  // consecutive elements; the table row of local token t)
   const float2* rrow = a.rope ? a.rope + (size_t)(tvalid ? t : 0) * (DK / 2) : nullptr;
-  {
-    const float* qrow = qp + tok * DK;
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      u16x8 x = (u16x8)(0);
+      if (tvalid) x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(qp) + tok * DK + ks * 32 + 8 * g);
+      if (rrow) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
+          rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
+          x[2 * j] = f32_to_bf16(x0);
+          x[2 * j + 1] = f32_to_bf16(x1);
+        }
+      }
+      qfb.x[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  } else {
+    const float* qf = reinterpret_cast<const float*>(qp) + tok * DK;
 #pragma unroll
     for (int ks = 0; ks < DK / 4; ++ks) {
       const int d = ks * 4 + g;
-      float x = tvalid ? qrow[d] : 0.f;
+      float x = tvalid ? qf[d] : 0.f;
       if (rrow && tvalid) {
         // element d of pair d/2; its partner is d ^ 1
-        const float y = qrow[d ^ 1];
+        const float y = qf[d ^ 1];
         const float2 cs = rrow[d >> 1];
         x = (d & 1) ? (y * cs.y + x * cs.x) : (x * cs.x - y * cs.y);
       }
-      qf[ks] = x;
+      qff.x[ks] = x;
     }
   }
 
@@ -138,10 +203,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) {
       st[kt] = (f32x4)(0.f);
+      if constexpr (kBF16) {
 #pragma unroll
-      for (int ks = 0; ks < DK / 4; ++ks) {
-        const float kx = sm.K[(kt * 16 + qn) * (DK + 4) + ks * 4 + g];
-        st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, qf[ks], st[kt], 0, 0, 0);
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const u16x8 kx = *reinterpret_cast<const u16x8*>(&sm.K[(kt * 16 + qn) * (DK + 8) + ks * 32 + 8 * g]);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx), qfb.x[ks], st[kt], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DK / 4; ++ks) {
+          const float kx = sm.K[(kt * 16 + qn) * (DK + 4) + ks * 4 + g];
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, qff.x[ks], st[kt], 0, 0, 0);
+        }
       }
     }
     // st[kt][i] = q_t . k_c for c = c0 + kt*16 + 4g + i (this lane's query t)
@@ -174,15 +247,38 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
 
     // O^T += V^T P^T
+    if constexpr (kBF16) {
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
+      for (int u = 0; u < NT / 2; ++u) {
+        u16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float* vrow = &sm.V[(kt * 16 + 4 * g + i) * (DV + 4)];
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = f32_to_bf16(st[2 * u][i]);
+          pb[4 + i] = f32_to_bf16(st[2 * u + 1][i]);
+        }
+        const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[dt * 16 + qn], st[kt][i], acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vrow = &sm.Vt[(dt * 16 + qn) * (64 + 8)];
+          const u16x4 v0 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 4 * g);
+          const u16x4 v1 = *reinterpret_cast<const u16x4*>(vrow + 32 * u + 16 + 4 * g);
+          u16x8 va;
+          va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+          va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pbf, acc[dt], 0, 0, 0);
+        }
       }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* vrow = &sm.V[(kt * 16 + 4 * g + i) * (DV + 4)];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[dt * 16 + qn], st[kt][i], acc[dt], 0, 0, 0);
+        }
+    }
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
@@ -204,7 +300,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     f32x4 r4 = (f32x4)(0.f);
-    if (tvalid) r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tok * DV + dt * 16 + 4 * g);
+    if (tvalid && a.ornn_bf16) {
+      const u16x4 x = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(a.o_rnn32) +
+                                                       tok * DV + dt * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r4[i] = bf16_to_f32(x[i]);
+    } else if (tvalid) {
+      r4 = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tok * DV + dt * 16 + 4 * g);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       okv[dt][i] = acc[dt][i] * inv_l;
@@ -223,16 +326,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
   const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
   const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
-  float* o = static_cast<float*>(a.o);
+  E* o = static_cast<E*>(a.o);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
     const size_t off = tt * DV + dt * 16 + 4 * g;
-    IoF32::store4(o, off, y);
-    if (a.o_kv) IoF32::store4(static_cast<float*>(a.o_kv), off, okv[dt]);
-    if (a.o_rnn) IoF32::store4(static_cast<float*>(a.o_rnn), off, orn[dt]);
+    IO::store4(o, off, y);
+    if (a.o_kv) IO::store4(static_cast<E*>(a.o_kv), off, okv[dt]);
+    if (a.o_rnn) IO::store4(static_cast<E*>(a.o_rnn), off, orn[dt]);
   }
 }
 
@@ -768,31 +871,35 @@ __global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
 
 hipError_t launch_mix(int io, int dv, const MixArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(((long long)a.ntok * a.H + 3) / 4));
-  if (dv != 128 || a.r != 2) return hipErrorInvalidValue;
-  if (io == 0) hipLaunchKernelGGL((mix_kernel<IoF32, 128, 2>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((mix_kernel<IoBF16, 128, 2>), grid, dim3(256), 0, s, a);
+  if (a.r != 2 || (dv != 128 && dv != 384)) return hipErrorInvalidValue;
+  if (io == 0 && dv == 128) hipLaunchKernelGGL((mix_kernel<IoF32, 128, 2>), grid, dim3(256), 0, s, a);
+  else if (io == 0) hipLaunchKernelGGL((mix_kernel<IoF32, 384, 2>), grid, dim3(256), 0, s, a);
+  else if (dv == 128) hipLaunchKernelGGL((mix_kernel<IoBF16, 128, 2>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((mix_kernel<IoBF16, 384, 2>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DK, int DV>
-static hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
+template <class IO, int DK, int DV>
+static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.T + 63) / 64;
-  hipLaunchKernelGGL((attn_f32_kernel<DK, DV>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<IO, DK, DV>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream_t s) {
+#define HAM_CASE(IOT, DKV, DVV) \
+  if (dk == DKV && dv == DVV) return launch_attn_t<IOT, DKV, DVV>(a, s);
   if (io == 0) {
-    if (dk == 64 && dv == 64) return launch_attn_f32<64, 64>(a, s);
-    if (dk == 64 && dv == 128) return launch_attn_f32<64, 128>(a, s);
-    if (dk == 128 && dv == 64) return launch_attn_f32<128, 64>(a, s);
-    if (dk == 128 && dv == 128) return launch_attn_f32<128, 128>(a, s);
+    HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+    HAM_CASE(IoF32, 128, 192)
   } else {
     if (dk == 64 && dv == 64) return launch_attn_bf16_v5<64, 64>(a, s);
     if (dk == 64 && dv == 128) return launch_attn_bf16_v5<64, 128>(a, s);
     if (dk == 128 && dv == 64) return launch_attn_bf16_v5<128, 64>(a, s);
     if (dk == 128 && dv == 128) return launch_attn_bf16_v5<128, 128>(a, s);
+    HAM_CASE(IoBF16, 128, 192)
   }
+#undef HAM_CASE
   return hipErrorInvalidValue;
 }
 

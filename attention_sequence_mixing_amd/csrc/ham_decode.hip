@@ -23,7 +23,7 @@ template <class IO, int N>
 struct RawRun;
 template <int N>
 struct RawRun<IoBF16, N> {                    // 16-byte runs (8-byte when N = 4)
-  static_assert(N % 8 == 0 || N == 4, "run length");
+  static_assert(N % 4 == 0, "run length");
   static constexpr int W = N % 8 == 0 ? 8 : 4;
   typedef uint16_t vec __attribute__((ext_vector_type(W)));
   vec x[N / W];
@@ -166,8 +166,10 @@ hipError_t launch_decode_attn(int io, int dk, int dv, const DecodeAttnArgs& a, h
   if (dk == DKV && dv == DVV) return launch_dattn_t<IOT, DKV, DVV>(a, s);
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+    HAM_CASE(IoF32, 128, 192)
   } else {
     HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+    HAM_CASE(IoBF16, 128, 192)
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;
@@ -236,6 +238,8 @@ hipError_t launch_decode_combine(int io, int dv, const DecodeCombineArgs& a, hip
   else if (io == 0 && dv == 128) hipLaunchKernelGGL((decode_combine_kernel<IoF32, 128>), grid, dim3(64), 0, s, a);
   else if (io == 1 && dv == 64) hipLaunchKernelGGL((decode_combine_kernel<IoBF16, 64>), grid, dim3(64), 0, s, a);
   else if (io == 1 && dv == 128) hipLaunchKernelGGL((decode_combine_kernel<IoBF16, 128>), grid, dim3(64), 0, s, a);
+  else if (io == 0 && dv == 192) hipLaunchKernelGGL((decode_combine_kernel<IoF32, 192>), grid, dim3(64), 0, s, a);
+  else if (io == 1 && dv == 192) hipLaunchKernelGGL((decode_combine_kernel<IoBF16, 192>), grid, dim3(64), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -10,7 +10,6 @@ namespace ham {
 // Score partials: every RNN kernel writes, per token and per d_v slice, the
 // three sums (p.v, p.p, v.v) of the prediction p = S_{t-1}^T k_t against v_t.
 // The routing kernel adds the slices and forms the cosine.
-constexpr int kScoreSlicesMax = 8;
 
 struct RnnArgs {
   const void* q;

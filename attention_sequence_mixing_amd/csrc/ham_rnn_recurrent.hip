@@ -4,10 +4,12 @@
 // 1/2|S k - v|^2; readout S_t^T q_t) with the gated-DeltaNet decay of App. A.1,
 // and the fit-error score of §2 / App. A.1 ("Router Implementations").
 //
-// One wave owns 64 columns of the fp32 state S (dk x dv) of one head and walks the
-// tokens in order.  Lane (rh, cp) = (lane / 32, lane mod 32) holds columns 2cp, 2cp+1
-// of the wave's block for rows [rh*dk/2, (rh+1)*dk/2), so each row's 64 columns are
-// one contiguous 256-byte run of float2 loads.  Columns of S evolve independently
+// One wave owns a block of columns of the fp32 state S (dk x dv) of one head and
+// walks the tokens in order.  The rows are split into RQ groups (2, or 4 at dk = 256
+// so that a lane keeps 128 floats of state): lane (rq, cp) = (lane / CPW, lane mod
+// CPW) holds columns 2cp, 2cp+1 of the wave's 2*CPW columns (CPW = 64/RQ) for rows
+// [rq*dk/RQ, (rq+1)*dk/RQ), so each row's columns are one contiguous run of float2
+// loads.  Columns of S evolve independently
 // under S <- alpha (I - beta k k^T) S + beta k v^T, so waves need no communication;
 // the routing score only needs three sums per token, written as partials per
 // 16-column slice.  k_t and q_t are staged in LDS as floats each token (every lane
@@ -18,19 +20,26 @@
 
 namespace ham {
 
-constexpr int kRecCols = 64;              // state columns per wave
+// row groups per wave and the resulting state columns per wave
+template <int DK>
+constexpr int rec_groups() { return DK > 128 ? 4 : 2; }
+template <int DK>
+constexpr int rec_cols() { return 128 / rec_groups<DK>(); }
 
 template <class IO, int DK, int DV>
 __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
-  static_assert(DV % kRecCols == 0, "whole 64-column blocks");
+  constexpr int RQ = rec_groups<DK>();     // row groups
+  constexpr int CPW = 64 / RQ;             // column pairs per wave
+  constexpr int kRecCols = 2 * CPW;        // state columns per wave
+  static_assert(DV % kRecCols == 0, "whole column blocks");
   using E = typename IO::elem;
-  constexpr int RH = DK / 2;               // rows per lane
+  constexpr int RH = DK / RQ;              // rows per lane
   constexpr int NS = DV / 16;              // score slices per head
   __shared__ float4 ks4[DK / 4], qs4[DK / 4];
   float* ks = reinterpret_cast<float*>(ks4);
   float* qs = reinterpret_cast<float*>(qs4);
   const int lane = lane_id();
-  const int rh = lane >> 5, cp = lane & 31;
+  const int rh = lane / CPW, cp = lane % CPW;
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int j0 = blk * kRecCols + 2 * cp;  // this lane's first column
   const int bh = b * a.H + h;
@@ -72,8 +81,11 @@ __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
       pb0 = fmaf(S[m + 3].x, kk.w, pb0); pb1 = fmaf(S[m + 3].y, kk.w, pb1);
     }
     float p0 = pa0 + pb0, p1 = pa1 + pb1;
-    p0 += __shfl_xor(p0, 32, kWave);       // the other half of the rows
-    p1 += __shfl_xor(p1, 32, kWave);
+#pragma unroll
+    for (int m = CPW; m < 64; m <<= 1) {   // the other row groups
+      p0 += __shfl_xor(p0, m, kWave);
+      p1 += __shfl_xor(p1, m, kWave);
+    }
 
     // score partials over each 16-column slice (8 lanes of column pairs)
     float pv = p0 * v0 + p1 * v1, pp = p0 * p0 + p1 * p1, vv = v0 * v0 + v1 * v1;
@@ -109,8 +121,11 @@ __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
         ob0 = fmaf(S[m + 3].x, qq.w, ob0); ob1 = fmaf(S[m + 3].y, qq.w, ob1);
       }
       float o0 = oa0 + ob0, o1 = oa1 + ob1;
-      o0 += __shfl_xor(o0, 32, kWave);
-      o1 += __shfl_xor(o1, 32, kWave);
+#pragma unroll
+      for (int m = CPW; m < 64; m <<= 1) {
+        o0 += __shfl_xor(o0, m, kWave);
+        o1 += __shfl_xor(o1, m, kWave);
+      }
       if (rh == 0) *reinterpret_cast<float2*>(a.o_rnn32 + tok * DV + j0) = make_float2(o0, o1);
     }
     __syncthreads();                       // k, q of the next token overwrite LDS
@@ -123,7 +138,7 @@ int rnn_recurrent_slices(int dv) { return dv / 16; }
 
 template <class IO, int DK, int DV>
 static hipError_t launch_t(const RnnArgs& a, hipStream_t s) {
-  dim3 grid(DV / kRecCols, a.H, a.B);
+  dim3 grid(DV / rec_cols<DK>(), a.H, a.B);
   hipLaunchKernelGGL((rnn_recurrent_kernel<IO, DK, DV>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
@@ -133,8 +148,10 @@ hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStr
   if (dk == DKV && dv == DVV) return launch_t<IOT, DKV, DVV>(a, s);
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+    HAM_CASE(IoF32, 256, 384)
   } else {
     HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+    HAM_CASE(IoBF16, 256, 384)
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;

@@ -27,7 +27,7 @@ namespace ham {
 template <int NS>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   extern __shared__ int s_cnt[];            // [H]
-  constexpr int PER = 4;                    // (token, head) pairs per thread and pass
+  constexpr int PER = NS > 8 ? 1 : 4;       // (token, head) pairs per thread and pass
   const int tid = threadIdx.x;
   const int c = blockIdx.x, b = blockIdx.y;
   const int nchunk = gridDim.x;
@@ -130,6 +130,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.e_in) hipLaunchKernelGGL(route_kernel<0>, grid, dim3(256), lds, s, a);
   else if (a.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, a);
   else if (a.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, a);
+  else if (a.slices == 24) hipLaunchKernelGGL(route_kernel<24>, grid, dim3(256), lds, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -268,8 +269,10 @@ hipError_t launch_compact(int io, int dk, int dv, const CompactArgs& a, hipStrea
   if (dk == DKV && dv == DVV) return launch_compact_t<IOT, DKV, DVV>(a, s);
   if (io == 0) {
     HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+    HAM_CASE(IoF32, 128, 192)
   } else {
     HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+    HAM_CASE(IoBF16, 128, 192)
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;

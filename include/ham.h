@@ -31,7 +31,9 @@
  *     cache and the outputs o / o_rnn / o_kv: HAM_F32 (float) or HAM_BF16
  *     (bfloat16 bits; stores round to nearest even).  beta, g, tau, gates, e and
  *     the state are always fp32.
- *   - dk, dv must each be 64 or 128 (likewise dk_kv, dv_kv).  "KV heads" below
+ *   - dk, dv must each be 64 or 128, or dk = 256 with dv = 384 (the RNN heads of
+ *     the paper's layer, run by the token-serial RNN kernel); dk_kv, dv_kv 64 or
+ *     128 each, or 128 with 192 (its KV heads).  "KV heads" below
  *     are the attention heads: kv_heads of them (default H) with sizes dk_kv,
  *     dv_kv (default dk, dv); the cache, gate_kv, o_kv and the attention-path
  *     inputs are shaped by them.
@@ -81,7 +83,7 @@ extern "C" {
 
 typedef struct {
     int B, T, H;      /* batch, new tokens per sequence, heads                   */
-    int dk, dv;       /* key and value head sizes (64 or 128 each)               */
+    int dk, dv;       /* key and value head sizes (64 or 128 each, or 256/384)   */
     int io_dtype;     /* HAM_F32 or HAM_BF16                                      */
     float scale;      /* attention logit scale, > 0 (usually 1/sqrt(dk))         */
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
@@ -127,7 +129,7 @@ typedef struct {
                          side is RMS-normalised per head of its own size and
                          gated per head before the sum.                       */
     int dk_kv, dv_kv; /* 0 (= dk, dv), or the KV heads' key and value sizes (64
-                         or 128).  When kv_heads != H or dk_kv != dk, the
+                         or 128 each, or 128/192).  When kv_heads != H or dk_kv != dk, the
                          attention-path inputs q_attn, k_attn, v_attn are
                          required ([B,T,kv_heads,dk_kv|dv_kv]).              */
 } ham_dims;

@@ -43,8 +43,12 @@ def test_workspace_sizes():
     assert ws >= BTH * 128 * 4 + BTH * 4 + BTH      # o_rnn fp32 + e + routed at least
     assert L.ham_route_stats_workspace_size(ctypes.byref(d)) > ws   # adds the state
     assert L.ham_decode_workspace_size(ctypes.byref(d)) > 0
-    for bad in (dims(dk=96), dims(dv=32), dims(T=0), dims(B=-1), dims(io_dtype=7), dims(cap=0),
-                dims(flags=64)):
+    # the paper's layer: RNN heads 256/384 with twice as many KV heads of 128/192
+    assert L.ham_forward_workspace_size(ctypes.byref(dims(dk=256, dv=384, kv_heads=8, dk_kv=128,
+                                                          dv_kv=192))) > 0
+    for bad in (dims(dk=96), dims(dv=32), dims(dk=256), dims(dv=384), dims(dk=256, dv=384),
+                dims(T=0), dims(B=-1),
+                dims(io_dtype=7), dims(cap=0), dims(flags=64), dims(dk_kv=128, dv_kv=192)):
         assert L.ham_forward_workspace_size(ctypes.byref(bad)) == 0
 
 

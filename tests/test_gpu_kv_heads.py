@@ -3,9 +3,9 @@
 "Hybrid Associative Memories" §4 (model setup) and App. E Tab. E.1: the HAM layer has
 twice as many KV heads as RNN heads, each half the RNN head's size (RNN 256/384, KV
 128/192), the KV value size chosen so that the KV heads' outputs match the RNN's.
-Built here at the head sizes the kernels take: RNN heads d_v = 128, KV heads d_v = 64
-(r = 2 per RNN head) with d_k 64 or 128 on either side; also one KV head per RNN head
-with its own key size.  KV head r*h + i follows the routing of RNN head h and holds
+Cases: RNN heads d_v = 128 with KV heads d_v = 64 (r = 2 per RNN head, d_k 64 or 128 on
+either side), one KV head per RNN head with its own key size, and the paper's own
+sizes (RNN 256/384 on the token-serial RNN kernel, KV 128/192).  KV head r*h + i follows the routing of RNN head h and holds
 its own cache; each side is normalised per head of its own size and gated per head.
 Compared with the oracle through the C ABI.
 """
@@ -156,3 +156,61 @@ def test_kv_heads_one_routed_set_per_layer():
     assert (cnt == cnt[:, :1]).all()
     for j in range(1, Hk):
         assert np.array_equal(pos[:, j, :cnt[0, 0]], pos[:, 0, :cnt[0, 0]])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_paper_head_sizes_forward_and_decode(dtype):
+    """The paper's head sizes: RNN heads of key/value size 256/384 (token-serial RNN
+    kernel) and twice as many KV heads of 128/192, with RoPE base 500K and gates; a
+    forward prefix, then decode steps, against one oracle forward."""
+    B, H, dk, dv, r, dkk = 2, 2, 256, 384, 2, 128
+    Hk, dvk = r * H, dv // r
+    T0, steps = 90, 6
+    T = T0 + steps
+    inp = make_inputs(B, T, H, dk, dv, dtype=_dt(dtype), seed=197)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype=_dt(dtype), seed=198)
+    scale = dkk ** -0.5
+    tau = _tau(inp, 0.5, scale)
+    base = 500000.0
+    rng = np.random.default_rng(197)
+    gr = rng.random((B, T, H)).astype(np.float32)
+    gk = rng.random((B, T, Hk)).astype(np.float32)
+    t, ta = to_dev(inp, dtype, DEV), to_dev(att, dtype, DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+    grd, gkd = torch.from_numpy(gr).to(DEV), torch.from_numpy(gk).to(DEV)
+    pre = {n: x[:, :T0].contiguous() for n, x in t.items()}
+    pa = {n: x[:, :T0].contiguous() for n, x in ta.items()}
+    out = ham.ham_forward(pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"], tau_d, scale=scale, cap=T,
+                          q_attn=pa["q"], k_attn=pa["k"], v_attn=pa["v"], rope_base=base,
+                          gate_rnn=grd[:, :T0].contiguous(), gate_kv=gkd[:, :T0].contiguous(),
+                          want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    pre_np = {n: x[:, :T0] for n, x in inp.items()}
+    att_np = {n: x[:, :T0] for n, x in att.items()}
+    check_forward(out, pre_np, tau, dtype, scale=scale, gates=(gr[:, :T0], gk[:, :T0]), attn=att_np,
+                  rope_base=base, cap=T)
+    S = out["S"]
+    cache = {n: out[n] for n in ("Kc", "Vc", "pos", "count")}
+    plan = ham.DecodePlan(B, H, dk, dv, T, dtype, DEV, scale=scale, rope_base=base, kv_heads=Hk,
+                          dk_kv=dkk, dv_kv=dvk)
+    es, rs, os_ = [], [], []
+    for s in range(steps):
+        tt = T0 + s
+        x = {n: t[n][:, tt].contiguous() for n in t}
+        xa = {n: ta[n][:, tt].contiguous() for n in ("q", "k", "v")}
+        plan(x["q"], x["k"], x["v"], x["beta"], x["g"], tau_d, S, cache["Kc"], cache["Vc"], cache["pos"],
+             cache["count"], torch.full((B,), tt, dtype=torch.int32, device=DEV), q_attn=xa["q"],
+             k_attn=xa["k"], v_attn=xa["v"], gate_rnn=grd[:, tt].contiguous(), gate_kv=gkd[:, tt].contiguous())
+        es.append(plan.e.cpu().numpy()); rs.append(plan.routed.cpu().numpy()); os_.append(np_of(plan.o))
+    torch.cuda.synchronize()
+    assert int(plan.status.item()) == 0
+    e_all = np.concatenate([out["e"].cpu().numpy(), np.stack(es, 1)], 1)
+    r_all = np.concatenate([out["routed"].cpu().numpy(), np.stack(rs, 1)], 1)
+    okw = dict(tau=tau, scale=scale, cap=T, rope_base=base, q_attn=att["q"], k_attn=att["k"],
+               v_attn=att["v"], gate_rnn=gr, gate_kv=gk)
+    ref = oracle.forward(**inp, **okw)
+    if check_routing(e_all, r_all, ref, tau):
+        ref = oracle.forward(**inp, mask_override=r_all, **okw)
+    assert rel_err_slices(np.stack(os_, 1), ref["o"][:, T0:], 2) < TOL[dtype]
+    assert rel_err_slices(np_of(S), ref["S"], 1) < 1e-4
+    assert np.array_equal(cache["count"].cpu().numpy(), ref["count"])
