@@ -32,7 +32,9 @@ bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int check_dims(const ham_dims* d, bool need_T) {
+// attn: the call attends (ham_forward, ham_decode_step), so the KV heads' geometry
+// must be one the kernels take; ham_route_stats runs the RNN alone.
+int check_dims(const ham_dims* d, bool need_T, bool attn = true) {
   if (!d) return fail(HAM_EINVAL, "dims is NULL");
   if (d->H > 4096) return fail(HAM_EUNSUPPORTED, "H must be <= 4096 (H=%d)", d->H);
   if (d->B <= 0 || d->H <= 0 || (need_T && d->T <= 0))
@@ -56,7 +58,7 @@ int check_dims(const ham_dims* d, bool need_T) {
     return fail(HAM_EINVAL, "rope_base must be 0 (none) or a finite positive base");
   if (d->kv_heads < 0 || d->dk_kv < 0 || d->dv_kv < 0)
     return fail(HAM_EINVAL, "kv_heads, dk_kv and dv_kv must be >= 0 (0: as the RNN heads)");
-  {
+  if (attn) {
     const int HK = d->kv_heads > 0 ? d->kv_heads : d->H;
     const int DKK = d->dk_kv > 0 ? d->dk_kv : d->dk, DVK = d->dv_kv > 0 ? d->dv_kv : d->dv;
     // 64 or 128 each; or the KV heads of the paper's layer, dk_kv = 128 with dv_kv = 192
@@ -272,7 +274,7 @@ size_t ham_forward_workspace_size(const ham_dims* d) {
 }
 
 size_t ham_route_stats_workspace_size(const ham_dims* d) {
-  if (check_dims(d, true) != HAM_OK) return 0;
+  if (check_dims(d, true, false) != HAM_OK) return 0;
   return fwd_layout(d, true).total;
 }
 
@@ -446,7 +448,7 @@ int ham_route_stats(const ham_dims* d, const void* q, const void* k, const void*
                     float* e, uint8_t* routed, int32_t* count, int64_t* n_near, float near_band,
                     double* rho_host, void* ws, size_t ws_bytes, void* stream) {
   (void)q;
-  int rc = check_dims(d, true);
+  int rc = check_dims(d, true, false);
   if (rc != HAM_OK) return rc;
   if (d->flags & HAM_EXTERNAL_SCORES)
     return fail(HAM_EUNSUPPORTED, "ham_route_stats takes its scores from the RNN; use ham_select_tau "

@@ -195,7 +195,7 @@ def bench_forward(args, dev):
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
-    router = rope = packed = blocks = kvh = None
+    router = rope = packed = blocks = kvh = paper = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
         router = bench_router(args, dev, w, t)
@@ -214,9 +214,10 @@ def bench_forward(args, dev):
         att = make_inputs_torch(w.B, w.T, 2 * w.H, w.d, w.d // 2, dtype="bf16", seed=w.seed + 3,
                                 device=dev)
         kvh = bench_variant(args, dev, w, t, tau, f"kv_heads{2 * w.H}_dk{w.d}_dv{w.d // 2}", attn=att)
+        paper = bench_paper_heads(args, dev, w)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh)
+                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper)
 
 
 def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0,
@@ -259,6 +260,51 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, ro
         f"stages {dict(zip(names, [round(x, 4) for x in stages]))}")
     return dict(workload=f"{w.name}_{label}", ms_per_step=round(ms, 4),
                 tokens_per_s=round(w.B * w.T / (ms / 1e3), 1), rho_measured=round(rho, 6),
+                stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
+
+
+def bench_paper_heads(args, dev, w, steps=5, warmup=5):
+    """The 800M model's layer geometry ("Hybrid Associative Memories" §4 and Tab. E.1 at
+    hidden size 1792): 5 RNN heads of key/value size 256/384 and 10 KV heads of 128/192,
+    B 8, T 4096, bf16, rho 0.5 per RNN head.  The RNN heads run on the token-serial
+    kernel (the chunked state kernel takes d_k <= 128), so this measures that path."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd import _lib
+    from attention_sequence_mixing_amd.inputs import make_inputs_torch
+    H, dk, dv, HK, dkk, dvk = 5, 256, 384, 10, 128, 192
+    t = make_inputs_torch(w.B, w.T, H, dk, dv, dtype="bf16", seed=w.seed + 5, device=dev)
+    att = make_inputs_torch(w.B, w.T, HK, dkk, dvk, dtype="bf16", seed=w.seed + 6, device=dev)
+    st = ham.ham_route_stats(t["k"], t["v"], t["beta"], t["g"], torch.full((H,), float("inf"), device=dev),
+                             want_rho=False)
+    tau = ham.ham_select_tau(st["e"], w.rho)
+    plan = ham.ForwardPlan(w.B, w.T, H, dk, dv, torch.bfloat16, dev, scale=dkk ** -0.5, kv_heads=HK,
+                           dk_kv=dkk, dv_kv=dvk)
+
+    def step():
+        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, q_attn=att["q"], k_attn=att["k"],
+             v_attn=att["v"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stages = collect_stages(lib, steps)
+    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
+    rho = float(plan.count.sum().item()) / (w.B * w.T * HK)
+    label = f"paper_heads_bf16_B{w.B}_T{w.T}_rnn{H}x{dk}x{dv}_kv{HK}x{dkk}x{dvk}"
+    log(f"[bench] {label}: {ms:.3f} ms/step, rho {rho:.4f}, "
+        f"stages {dict(zip(names, [round(x, 4) for x in stages]))}")
+    return dict(workload=label, ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                rho_measured=round(rho, 6), steps=steps, warmup=warmup,
                 stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
 
 
@@ -506,6 +552,7 @@ def main():
         "packed_docs": res["packed"],
         "block_routing": res["blocks"],
         "kv_heads": res["kvh"],
+        "paper_heads": res["paper"],
         "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",

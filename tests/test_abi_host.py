@@ -214,3 +214,12 @@ def test_kv_head_geometry_checks():
     d = [fake] * 26
     d[5] = None                                        # v_attn of the decode step
     assert L.ham_decode_step(ctypes.byref(dims(kv_heads=8, dv_kv=64)), *d, 1 << 40, None) == _lib.HAM_EINVAL
+
+
+def test_route_stats_ignores_the_kv_geometry():
+    """Routing alone needs no attention heads: the paper's RNN heads (256/384) size a
+    route-statistics workspace without KV sizes, while a forward needs them."""
+    L = _lib.lib()
+    d = dims(dk=256, dv=384)
+    assert L.ham_route_stats_workspace_size(ctypes.byref(d)) > 0
+    assert L.ham_forward_workspace_size(ctypes.byref(d)) == 0 and "dk_kv" in _msg()
