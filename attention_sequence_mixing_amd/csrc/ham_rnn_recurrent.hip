@@ -5,11 +5,11 @@
 // and the fit-error score of §2 / App. A.1 ("Router Implementations").
 //
 // One wave owns a block of columns of the fp32 state S (dk x dv) of one head and
-// walks the tokens in order.  The rows are split into RQ groups (2, or 4 at dk = 256
-// so that a lane keeps 128 floats of state): lane (rq, cp) = (lane / CPW, lane mod
-// CPW) holds columns 2cp, 2cp+1 of the wave's 2*CPW columns (CPW = 64/RQ) for rows
-// [rq*dk/RQ, (rq+1)*dk/RQ), so each row's columns are one contiguous run of float2
-// loads.  Columns of S evolve independently
+// walks the tokens in order.  The rows are split into RQ groups (2; 8 at dk = 256, so
+// that a lane keeps 64 floats of state and a head spreads over twice as many waves):
+// lane (rq, cp) = (lane / CPW, lane mod CPW) holds columns 2cp, 2cp+1 of the wave's
+// 2*CPW columns (CPW = 64/RQ) for rows [rq*dk/RQ, (rq+1)*dk/RQ), so each row's
+// columns are one contiguous run of float2 loads.  Columns of S evolve independently
 // under S <- alpha (I - beta k k^T) S + beta k v^T, so waves need no communication;
 // the routing score only needs three sums per token, written as partials per
 // 16-column slice.  k_t and q_t are staged in LDS as floats each token (every lane
@@ -22,7 +22,7 @@ namespace ham {
 
 // row groups per wave and the resulting state columns per wave
 template <int DK>
-constexpr int rec_groups() { return DK > 128 ? 4 : 2; }
+constexpr int rec_groups() { return DK > 128 ? 8 : 2; }
 template <int DK>
 constexpr int rec_cols() { return 128 / rec_groups<DK>(); }
 
@@ -58,16 +58,39 @@ __global__ __launch_bounds__(64) void rnn_recurrent_kernel(RnnArgs a) {
   }
 
   const bool readout = a.o_rnn32 != nullptr;
+  // The next token's inputs are loaded into registers while the current token is
+  // processed, so the chain from one token to the next waits on LDS, not on memory.
+  constexpr int KL = (DK + 63) / 64;       // key / query elements per lane
+  float kn[KL], qn[KL], vn0 = 0.f, vn1 = 0.f, gn = 0.f, bn = 0.f;
+  auto fetch = [&](int t) {
+    const size_t tok = ((size_t)b * a.T + t) * a.H + h;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int e = lane + 64 * i;
+      kn[i] = e < DK ? IO::load(k, tok * DK + e) : 0.f;
+      qn[i] = (readout && e < DK) ? IO::load(q, tok * DK + e) : 0.f;
+    }
+    vn0 = IO::load(v, tok * DV + j0);
+    vn1 = IO::load(v, tok * DV + j0 + 1);
+    gn = a.g[tok];
+    bn = a.beta[tok];
+  };
+  if (a.T > 0) fetch(0);
   for (int t = 0; t < a.T; ++t) {
     const size_t tok = ((size_t)b * a.T + t) * a.H + h;
-    const float alpha = expf(a.g[tok]);
-    const float beta = a.beta[tok];
-    for (int e = lane; e < DK; e += 64) {
-      ks[e] = IO::load(k, tok * DK + e);
-      if (readout) qs[e] = IO::load(q, tok * DK + e);
+    const float alpha = expf(gn);
+    const float beta = bn;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < DK) {
+        ks[e] = kn[i];
+        if (readout) qs[e] = qn[i];
+      }
     }
-    const float v0 = IO::load(v, tok * DV + j0), v1 = IO::load(v, tok * DV + j0 + 1);
+    const float v0 = vn0, v1 = vn1;
     __syncthreads();
+    if (t + 1 < a.T) fetch(t + 1);
     const float4* kr = ks4 + rh * (RH / 4);
 
     // prediction p_j = sum_i S[i][j] k_i   (S_{t-1}^T k_t), two chains per column
