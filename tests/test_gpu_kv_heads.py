@@ -214,3 +214,51 @@ def test_paper_head_sizes_forward_and_decode(dtype):
     assert rel_err_slices(np.stack(os_, 1), ref["o"][:, T0:], 2) < TOL[dtype]
     assert rel_err_slices(np_of(S), ref["S"], 1) < 1e-4
     assert np.array_equal(cache["count"].cpu().numpy(), ref["count"])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kv_heads_block_routing_decode(dtype):
+    """KV heads of their own geometry with 8-token block routing, RoPE and document
+    masks: a forward prefix of whole blocks, then decode steps ending in an open block."""
+    from parity import spread_block_flags
+    B, H, dk, dv, r, dkk, n = 2, 2, 128, 128, 2, 64, 8
+    Hk, dvk = r * H, dv // r
+    T0, steps = 64, 13
+    T = T0 + steps
+    inp = make_inputs(B, T, H, dk, dv, dtype=_dt(dtype), seed=199)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype=_dt(dtype), seed=200)
+    scale = dkk ** -0.5
+    tau = _tau(inp, 0.5, scale, n)
+    base = 10000.0
+    ds = make_doc_start(B, T, 20, 199)
+    t, ta = to_dev(inp, dtype, DEV), to_dev(att, dtype, DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+    pre = {k: x[:, :T0].contiguous() for k, x in t.items()}
+    pa = {k: x[:, :T0].contiguous() for k, x in ta.items()}
+    o1 = ham.ham_forward(pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"], tau_d, scale=scale, cap=T,
+                         q_attn=pa["q"], k_attn=pa["k"], v_attn=pa["v"], rope_base=base, route_block=n,
+                         doc_start=_i32(ds[:, :T0]))
+    S = o1["S"]
+    cache = {k: o1[k] for k in ("Kc", "Vc", "pos", "count")}
+    plan = ham.DecodePlan(B, H, dk, dv, T, dtype, DEV, scale=scale, rope_base=base, route_block=n,
+                          kv_heads=Hk, dk_kv=dkk, dv_kv=dvk)
+    es, rs, os_ = [], [], []
+    for s in range(steps):
+        tt = T0 + s
+        x = {k: t[k][:, tt].contiguous() for k in t}
+        xa = {k: ta[k][:, tt].contiguous() for k in ("q", "k", "v")}
+        plan(x["q"], x["k"], x["v"], x["beta"], x["g"], tau_d, S, cache["Kc"], cache["Vc"], cache["pos"],
+             cache["count"], torch.full((B,), tt, dtype=torch.int32, device=DEV), q_attn=xa["q"],
+             k_attn=xa["k"], v_attn=xa["v"], doc_start=_i32(ds[:, tt]))
+        es.append(plan.e.cpu().numpy()); rs.append(plan.routed.cpu().numpy()); os_.append(np_of(plan.o))
+    torch.cuda.synchronize()
+    assert int(plan.status.item()) == 0
+    e_all = np.concatenate([o1["e"].cpu().numpy(), np.stack(es, 1)], 1)
+    r_all = np.concatenate([o1["routed"].cpu().numpy(), spread_block_flags(np.stack(rs, 1), n)], 1)
+    okw = dict(tau=tau, scale=scale, cap=T, rope_base=base, route_block=n, doc_start=ds,
+               q_attn=att["q"], k_attn=att["k"], v_attn=att["v"])
+    ref = oracle.forward(**inp, **okw)
+    if check_routing(e_all, r_all, ref, tau, n):
+        ref = oracle.forward(**inp, mask_override=r_all, **okw)
+    assert rel_err_slices(np.stack(os_, 1), ref["o"][:, T0:], 2) < TOL[dtype]
+    assert np.array_equal(cache["count"].cpu().numpy(), ref["count"])
