@@ -64,6 +64,7 @@ struct RouteArgs {
   float* blk_acc;
   const int32_t* t_abs;
   int Hkv;              // KV heads (count, count_in are [B,Hkv]); 0: H
+  int e_lds;            // set by the launcher: block routing keeps the scores in LDS
 };
 
 struct CompactArgs {

@@ -26,7 +26,9 @@ namespace ham {
 // input router's sigma(W_r x_t), App. A.1 "Router Implementations"), read from e_in.
 template <int NS>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  extern __shared__ int s_cnt[];            // [H]
+  extern __shared__ int s_cnt[];            // [H], then (block routing, if it fits)
+                                            // the chunk's scores [64][H]
+  float* s_e = a.blk > 1 && a.e_lds ? reinterpret_cast<float*>(s_cnt + a.H) : nullptr;
   constexpr int PER = NS > 8 ? 1 : 4;       // (token, head) pairs per thread and pass
   const int tid = threadIdx.x;
   const int c = blockIdx.x, b = blockIdx.y;
@@ -74,7 +76,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       }
       const size_t tok = ((size_t)b * a.T + t0 + tl) * H + h;
       if constexpr (NS > 0) a.e[tok] = e;
-      if (a.blk > 1) continue;                                       // decided per block below
+      if (a.blk > 1) {                                               // decided per block below
+        if (s_e) s_e[idx] = e;
+        continue;
+      }
       const bool r = e > a.tau[a.tau_per_token ? tok : (size_t)h];   // strict; NaN never routes
       a.routed[tok] = (uint8_t)r;
       if (r) atomicAdd(&s_cnt[h], 1);
@@ -106,7 +111,13 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         const int j = idx / H, h = idx - j * H;
         const size_t tok0 = ((size_t)b * a.T + t0 + j * a.blk) * H + h;
         float sum = 0.f;
-        for (int i = 0; i < a.blk; ++i) sum += es[tok0 + (size_t)i * H];
+        if (s_e) {
+          // the chunk's scores kept in LDS at (token in chunk) * H + head
+          const int loc0 = j * a.blk * H + h;
+          for (int i = 0; i < a.blk; ++i) sum += s_e[loc0 + i * H];
+        } else {
+          for (int i = 0; i < a.blk; ++i) sum += es[tok0 + (size_t)i * H];
+        }
         const size_t tlast = tok0 + (size_t)(a.blk - 1) * H;
         const bool r = sum * inv > a.tau[a.tau_per_token ? tlast : (size_t)h];
         for (int i = 0; i < a.blk; ++i) a.routed[tok0 + (size_t)i * H] = (uint8_t)r;
@@ -126,11 +137,15 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nchunk = (a.T + kChunk - 1) / kChunk;
   const dim3 grid(nchunk, a.B);
-  const size_t lds = a.H * sizeof(int);
-  if (a.e_in) hipLaunchKernelGGL(route_kernel<0>, grid, dim3(256), lds, s, a);
-  else if (a.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, a);
-  else if (a.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, a);
-  else if (a.slices == 24) hipLaunchKernelGGL(route_kernel<24>, grid, dim3(256), lds, s, a);
+  size_t lds = a.H * sizeof(int);
+  // block routing keeps the chunk's scores in LDS when they fit
+  RouteArgs b = a;
+  b.e_lds = a.blk > 1 && !a.t_abs && a.H <= 192 ? 1 : 0;
+  if (b.e_lds) lds += (size_t)kChunk * a.H * sizeof(float);
+  if (b.e_in) hipLaunchKernelGGL(route_kernel<0>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 24) hipLaunchKernelGGL(route_kernel<24>, grid, dim3(256), lds, s, b);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
