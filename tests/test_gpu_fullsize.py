@@ -6,7 +6,8 @@ pass), and the attention outputs at sampled tokens of sampled heads.
 Workloads: the layer at the 800M-model shape (B=8, H=16, d=128, T=4096, bf16 I/O,
 rho = 0.5 and the two rho limits; rho = 0.5 with RoPE base 500K; rho = 0.5 over packed
 documents with same-document masking and RoPE; rho = 0.5 of 64-token blocks with
-block-contiguous routing); the long-context case (B=1, H=16, T=32768,
+block-contiguous routing; 32 KV heads of 128/64, and the 800M layer's 5 RNN heads of 256/384 with
+10 KV heads of 128/192, at sampled sequence-head pairs); the long-context case (B=1, H=16, T=32768,
 planted repeated pairs, rho = 0.25); the decode case (batch 32, H=16, d=128,
 32K-token prefix, then decode steps).
 """
@@ -289,3 +290,55 @@ def test_decode_maximum_capacity_many_segments():
     got = np.stack(outs, 1)
     assert rel_err_slices(got, ref["o"][:, T0:], 2) < TOL[torch.bfloat16]
     assert rel_err_slices(np_of(plan.S), ref["S"], 1) < 1e-4
+
+
+@pytest.mark.parametrize("H,dk,dv,r,dkk", [(16, 128, 128, 2, 128), (5, 256, 384, 2, 128)])
+def test_kv_heads_fullsize_sampled_heads(H, dk, dv, r, dkk):
+    """The benchmark's head layouts at full size (B 8, T 4096, bf16): 32 KV heads of
+    128/64 over the layer's 16 RNN heads, and the 800M layer's 5 RNN heads of 256/384
+    with 10 KV heads of 128/192.  For sampled (sequence, RNN head) pairs the oracle runs
+    that RNN head and its r KV heads over all tokens: every score, decision, cache entry
+    of both KV heads and the final state, and the outputs at sampled tokens."""
+    B, T = 8, 4096
+    Hk, dvk = r * H, dv // r
+    inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=60 + dk)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype="bf16", seed=61 + dk)
+    tau = np.full(H, 1.0, np.float32)                  # routes about half of the tokens
+    scale = dkk ** -0.5
+    t, ta = to_dev(inp, torch.bfloat16, DEV), to_dev(att, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], want_o_rnn=True,
+                          want_o_kv=True)
+    torch.cuda.synchronize()
+    e_gpu = out["e"].cpu().numpy()
+    r_gpu = out["routed"].cpu().numpy()
+    cnt, pos = out["count"].cpu().numpy(), out["pos"].cpu().numpy()
+    S = np_of(out["S"])
+    rng = np.random.default_rng(62)
+    for (b, h) in [(0, 0), (5, H - 1)]:
+        sub = {n: np.ascontiguousarray(a[b:b + 1, :, h:h + 1]) for n, a in inp.items()}
+        sa = {n: np.ascontiguousarray(a[b:b + 1, :, r * h:r * h + r]) for n, a in att.items()}
+        toks = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
+        emit = np.zeros((1, T, 1), np.int8)
+        emit[0, toks, 0] = 1
+        okw = dict(tau=tau[h:h + 1], scale=scale, emit=emit, q_attn=sa["q"], k_attn=sa["k"], v_attn=sa["v"])
+        ref = oracle.forward(**sub, **okw)
+        de = np.abs(e_gpu[b, :, h] - ref["e"][0, :, 0]).max()
+        assert de < E_TOL, (b, h, de)
+        near = np.abs(ref["e"][0, :, 0] - tau[h]) < NEAR
+        flips = r_gpu[b, :, h].astype(bool) != ref["routed"][0, :, 0].astype(bool)
+        assert not (flips & ~near).any()
+        if flips.any():
+            ref = oracle.forward(**sub, mask_override=r_gpu[b:b + 1, :, h:h + 1], **okw)
+        for i in range(r):
+            j = r * h + i
+            n = int(ref["count"][0, i])
+            assert cnt[b, j] == n and np.array_equal(pos[b, j, :n], ref["pos"][0, i, :n])
+        errS = np.abs(S[b, h] - ref["S"][0, 0]).max() / np.abs(ref["S"][0, 0]).max()
+        assert errS < 1e-4, errS
+        for name, heads in (("o", slice(h, h + 1)), ("o_rnn", slice(h, h + 1)), ("o_kv", slice(r * h, r * h + r))):
+            x = np_of(out[name][b, toks, heads])
+            y = ref[name][0, toks]
+            err = np.abs(x - y).max() / max(np.abs(y).max(), 1e-30)
+            assert err < TOL[torch.bfloat16], (name, b, h, err)
+        print(f"kv heads H={H} dk={dk} dv={dv} (b={b}, h={h}): max|de|={de:.2e} flips={int(flips.sum())}")
