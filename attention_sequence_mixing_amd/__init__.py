@@ -363,3 +363,35 @@ def ham_select_tau(e, rho, *, out=None, stream=None):
                                    _stream(stream))
     check(rc)
     return tau
+
+
+def ham_attention_backward(q_attn, cache, dO, *, scale=None, t0=0, doc_start=None, stream=None):
+    """Gradients of the attention readout o_kv for training: q_attn [B,T,H,dk] (the
+    forward's attention-path queries), cache dict(Kc, Vc, pos, count) as the forward
+    left it, dO [B,T,H,dv] float32 = dL/do_kv.  Returns dict(dq [B,T,H,dk],
+    dKc [B,H,cap,dk], dVc [B,H,cap,dv]) in float32 (cache rows < count)."""
+    B, T, H, dk = q_attn.shape
+    Kc, Vc, pos, count = cache["Kc"], cache["Vc"], cache["pos"], cache["count"]
+    cap, dv = Kc.shape[2], Vc.shape[3]
+    dev, dt = q_attn.device, q_attn.dtype
+    _need("q_attn", q_attn, (B, T, H, dk), dt, dev)
+    _need("Kc", Kc, (B, H, cap, dk), dt, dev)
+    _need("Vc", Vc, (B, H, cap, dv), dt, dev)
+    _need("pos", pos, (B, H, cap), torch.int32, dev)
+    _need("count", count, (B, H), torch.int32, dev)
+    _need("dO", dO, (B, T, H, dv), torch.float32, dev)
+    _need("doc_start", doc_start, (B, T), torch.int32, dev)
+    scale = 1.0 / math.sqrt(dk) if scale is None else scale
+    dims = make_dims(B, T, H, dk, dv, _io_code(dt), scale, 1e-6, cap, t0=t0)
+    L = _lib.lib()
+    ws_bytes = L.ham_attention_backward_workspace_size(ctypes.byref(dims))
+    if ws_bytes == 0:
+        raise HamError(-1, L.ham_last_error().decode())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    dq = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    dKc = torch.zeros((B, H, cap, dk), dtype=torch.float32, device=dev)
+    dVc = torch.zeros((B, H, cap, dv), dtype=torch.float32, device=dev)
+    check(L.ham_attention_backward(ctypes.byref(dims), _vp(q_attn), _vp(Kc), _vp(Vc), _vp(pos), _vp(count),
+                                   _vp(doc_start), _vp(dO), _vp(dq), _vp(dKc), _vp(dVc), _vp(ws), ws.numel(),
+                                   _stream(stream)))
+    return dict(dq=dq, dKc=dKc, dVc=dVc)

@@ -18,7 +18,8 @@ HAM_CONTINUE, HAM_FORCE_RECURRENT, HAM_EXTERNAL_SCORES, HAM_TAU_PER_TOKEN = 1, 2
 # every symbol include/ham.h declares
 EXPORTS = ("ham_version", "ham_last_error", "ham_forward_workspace_size", "ham_forward",
            "ham_decode_workspace_size", "ham_decode_step", "ham_route_stats_workspace_size",
-           "ham_route_stats", "ham_select_tau", "ham_profile_start", "ham_profile_stop")
+           "ham_route_stats", "ham_select_tau", "ham_profile_start", "ham_profile_stop",
+           "ham_attention_backward_workspace_size", "ham_attention_backward")
 HAM_PROFILE_STAGES = 5
 
 
@@ -57,7 +58,7 @@ def lib():
     L.ham_last_error.restype = ctypes.c_char_p
     L.ham_last_error.argtypes = []
     for name in ("ham_forward_workspace_size", "ham_decode_workspace_size",
-                 "ham_route_stats_workspace_size"):
+                 "ham_route_stats_workspace_size", "ham_attention_backward_workspace_size"):
         f = getattr(L, name)
         f.restype = Z
         f.argtypes = [D]
@@ -67,6 +68,8 @@ def lib():
     L.ham_decode_step.argtypes = [D] + [P] * 26 + [Z, P]
     L.ham_route_stats.restype = I
     L.ham_route_stats.argtypes = [D] + [P] * 11 + [ctypes.c_float, P, P, Z, P]
+    L.ham_attention_backward.restype = I
+    L.ham_attention_backward.argtypes = [D] + [P] * 10 + [P, Z, P]
     L.ham_select_tau.restype = I
     L.ham_select_tau.argtypes = [D, P, ctypes.c_double, P, P]
     L.ham_profile_start.restype = I

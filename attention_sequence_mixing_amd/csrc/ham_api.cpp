@@ -264,7 +264,7 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
 
 extern "C" {
 
-int ham_version(void) { return 10300; }
+int ham_version(void) { return 10400; }
 
 const char* ham_last_error(void) { return g_err.c_str(); }
 
@@ -276,6 +276,32 @@ size_t ham_forward_workspace_size(const ham_dims* d) {
 size_t ham_route_stats_workspace_size(const ham_dims* d) {
   if (check_dims(d, true, false) != HAM_OK) return 0;
   return fwd_layout(d, true).total;
+}
+
+size_t ham_attention_backward_workspace_size(const ham_dims* d) {
+  if (check_dims(d, true) != HAM_OK) return 0;
+  return up256((size_t)d->B * d->T * kv_heads(d) * 3 * sizeof(float));
+}
+
+int ham_attention_backward(const ham_dims* d, const void* q_attn, const void* Kc, const void* Vc,
+                           const int32_t* pos, const int32_t* count, const int32_t* doc_start,
+                           const float* dO, float* dq, float* dKc, float* dVc,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != HAM_OK) return rc;
+  if (d->rope_base > 0.f || route_blk(d) || dv_kv(d) > 128)
+    return fail(HAM_EUNSUPPORTED, "ham_attention_backward: no RoPE, no block routing, KV sizes 64 or 128");
+  HAM_REQUIRE(q_attn); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos); HAM_REQUIRE(count);
+  HAM_REQUIRE(dO); HAM_REQUIRE(dq); HAM_REQUIRE(dKc); HAM_REQUIRE(dVc);
+  HAM_ALIGNED(q_attn); HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(dO); HAM_ALIGNED(dq);
+  HAM_ALIGNED(dKc); HAM_ALIGNED(dVc); HAM_ALIGNED(ws);
+  const size_t need = ham_attention_backward_workspace_size(d);
+  if (!ws || ws_bytes < need)
+    return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  ham::AttnBwdArgs a{q_attn, Kc, Vc, pos, count, doc_start, dO, dq, dKc, dVc, static_cast<float*>(ws),
+                     d->scale, d->B, d->T, kv_heads(d), d->cap, d->t0};
+  HAM_HIP(ham::launch_attention_backward(d->io_dtype, dk_kv(d), dv_kv(d), a, static_cast<hipStream_t>(stream)));
+  return HAM_OK;
 }
 
 size_t ham_decode_workspace_size(const ham_dims* d) {

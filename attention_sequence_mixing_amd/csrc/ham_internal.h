@@ -180,7 +180,26 @@ struct MixArgs {
   int ornn_bf16;
 };
 
+// Gradients of the attention over the cache (training): the cache and its positions
+// as the forward left them, the gradient of the attention readout, and fp32 outputs.
+struct AttnBwdArgs {
+  const void* q;            // attention-path queries [B,T,H,dk] (io type)
+  const void* Kc;           // [B,H,cap,dk]
+  const void* Vc;           // [B,H,cap,dv]
+  const int32_t* pos;       // [B,H,cap] ascending positions
+  const int32_t* count;     // [B,H]
+  const int32_t* doc_start; // [B,T] or null
+  const float* dO;          // [B,T,H,dv] dL/do_kv
+  float* dq;                // [B,T,H,dk]
+  float* dKc;               // [B,H,cap,dk] (entries < count)
+  float* dVc;               // [B,H,cap,dv]
+  float* stat;              // [B,T,H][3] scratch: row maximum, 1/row sum, D
+  float scale;
+  int B, T, H, cap, t0;
+};
+
 // launchers (return hipGetLastError() of the launch)
+hipError_t launch_attention_backward(int io, int dk, int dv, const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);
 hipError_t launch_mix(int io, int dv, const MixArgs& a, hipStream_t s);
 int rnn_recurrent_slices(int dv);

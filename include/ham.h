@@ -303,6 +303,35 @@ int ham_route_stats(const ham_dims *dims,
  */
 int ham_select_tau(const ham_dims *dims, const float *e, double rho, float *tau, void *stream);
 
+/* Bytes of device scratch ham_attention_backward needs. */
+size_t ham_attention_backward_workspace_size(const ham_dims *dims);
+
+/*
+ * ham_attention_backward -- gradients of the KV-memory readout for training ([HAM]
+ * §2 KV-memory equation; App. A.1 "FlexAttention and Block Masks" for the visible
+ * set): given dO = dL/do_kv, the gradients of softmax attention over the cache,
+ *   D_t = dO_t . o_kv_t,  dq_t = scale sum_c p_tc (dO_t . v_c - D_t) k_c,
+ *   dk_c = scale sum_t p_tc (dO_t . v_c - D_t) q_t,  dv_c = sum_t p_tc dO_t.
+ * The routing threshold passes no gradient.  The visible set is read from the
+ * cache: query t (position t0 + t) sees the entries at positions <= t0 + t (and,
+ * with doc_start, >= its document's start), so the cache may hold entries of
+ * earlier calls.  Acts on the KV heads (kv_heads, dk_kv, dv_kv: 64 or 128 each).
+ *
+ *   q_attn             [B,T,kv_heads,dk_kv] io dtype: the queries of the forward.
+ *   Kc, Vc, pos, count the cache as the forward left it.
+ *   doc_start          [B,T] int32 or NULL, as in ham_forward.
+ *   dO                 [B,T,kv_heads,dv_kv] fp32: dL/do_kv.
+ *   dq                 [B,T,kv_heads,dk_kv] fp32 out.
+ *   dKc, dVc           [B,kv_heads,cap,dk_kv|dv_kv] fp32 out, entries < count
+ *                      (the caller scatters them to token positions through pos).
+ * Errors: HAM_EINVAL, HAM_EUNSUPPORTED (rope_base > 0, route_block > 1, or KV
+ * sizes other than 64/128), HAM_EWORKSPACE, HAM_EHIP.
+ */
+int ham_attention_backward(const ham_dims *dims, const void *q_attn, const void *Kc, const void *Vc,
+                           const int32_t *pos, const int32_t *count, const int32_t *doc_start,
+                           const float *dO, float *dq, float *dKc, float *dVc,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Instrumentation (not part of the method): HIP-event timing of the kernel
  * stages of the next calls.  ham_profile_start(max_calls) arms recording on the

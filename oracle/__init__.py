@@ -206,3 +206,46 @@ def route_stats(out, tau, near_band=1e-5):
     tau = tau.reshape(1, 1, H) if tau.size == H else tau.reshape(B, T, H)
     n_near = (np.abs(e - tau) < near_band).sum(axis=(0, 1))
     return dict(count=count, rho=rho, n_near=n_near)
+
+
+def attention_backward(q_attn, Kc, Vc, pos, count, dO, *, scale, t0=0, doc_start=None):
+    """Gradients of the attention readout ([HAM] §2 KV-memory equation; the visible
+    set of App. A.1 "FlexAttention and Block Masks"), written out per head from the
+    definition of softmax attention, in float64.  Query t (position t0 + t) sees the
+    cached entries at positions <= t0 + t (and >= doc_start[b, t] if given).  With
+    P = the masked softmax of scale * Q K^T (a row with no visible entry is 0),
+    O = P V, D = rowsum(dO * O):  dP = dO V^T, dS = P * (dP - D),
+    dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.  Returns dict(dq [B,T,H,dk],
+    dKc [B,H,cap,dk], dVc [B,H,cap,dv]); cache rows >= count are 0."""
+    q = np.asarray(q_attn, dtype=np.float64)
+    B, T, H, dk = q.shape
+    Kc = np.asarray(Kc, dtype=np.float64)
+    Vc = np.asarray(Vc, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    cap, dv = Kc.shape[2], Vc.shape[3]
+    dq = np.zeros((B, T, H, dk))
+    dK = np.zeros((B, H, cap, dk))
+    dV = np.zeros((B, H, cap, dv))
+    tpos = t0 + np.arange(T)
+    for b in range(B):
+        for h in range(H):
+            n = int(count[b, h])
+            p_ = np.asarray(pos[b, h, :n], dtype=np.int64)
+            vis = p_[None, :] <= tpos[:, None]
+            if doc_start is not None:
+                vis &= p_[None, :] >= np.asarray(doc_start[b], dtype=np.int64)[:, None]
+            Q, K, V, G = q[b, :, h], Kc[b, h, :n], Vc[b, h, :n], dO[b, :, h]
+            S = np.where(vis, scale * (Q @ K.T), -np.inf)
+            P = np.zeros((T, n))
+            rows = vis.any(axis=1)
+            if rows.any():
+                Sr = S[rows]
+                E = np.exp(Sr - Sr.max(axis=1, keepdims=True))
+                P[rows] = E / E.sum(axis=1, keepdims=True)
+            O = P @ V
+            D = (G * O).sum(axis=1, keepdims=True)
+            dS = P * (G @ V.T - D)
+            dq[b, :, h] = scale * dS @ K
+            dK[b, h, :n] = scale * dS.T @ Q
+            dV[b, h, :n] = P.T @ G
+    return dict(dq=dq, dKc=dK, dVc=dV)

@@ -668,3 +668,57 @@ def test_kv_head_geometry_dense_reference(H, dk, dv, r, dkk):
         with pytest.raises(ValueError):                                # columns must tile
             oracle.forward(**inp, tau=np.zeros(H, np.float32), scale=0.5, q_attn=att["q"][:, :, :H],
                            k_attn=att["k"][:, :, :H], v_attn=att["v"][:, :, :H])
+
+
+# --- gradients of the attention readout (training) -----------------------------------
+def test_attention_backward_matches_finite_differences():
+    """The backward written from the softmax-attention definition agrees with central
+    differences of the token-serial forward's o_kv (loss sum(dO * o_kv)) for the
+    attention query, key and value of every token, routing held fixed, with document
+    masks and a continued cache (entries of an earlier call)."""
+    B, T, H, d = 1, 14, 1, 4
+    T1 = 5
+    inp = make_inputs(B, T, H, d, seed=210)
+    att = {n: x.astype(np.float64) for n, x in make_inputs(B, T, H, d, seed=211).items()}
+    rng = np.random.default_rng(210)
+    mask = (rng.random((B, T, H)) < 0.6).astype(np.int8)
+    mask[0, 6, 0] = 1
+    ds = np.array([[0] * 4 + [4] * 6 + [10] * 4])               # documents of 4, 6, 4 tokens
+    dO = rng.standard_normal((B, T - T1, H, d))
+    scale = 0.7
+
+    def second_call(q_a, k_a, v_a):
+        first = oracle.forward(**{n: x[:, :T1] for n, x in inp.items()}, tau=np.zeros(H, np.float32),
+                               scale=scale, mask_override=mask[:, :T1], cap=T, q_attn=q_a[:, :T1],
+                               k_attn=k_a[:, :T1], v_attn=v_a[:, :T1], doc_start=ds[:, :T1])
+        return oracle.forward(**{n: x[:, T1:] for n, x in inp.items()}, tau=np.zeros(H, np.float32),
+                              scale=scale, mask_override=mask[:, T1:], t0=T1, S0=first["S"],
+                              cache={n: first[n] for n in ("Kc", "Vc", "pos", "count")},
+                              q_attn=q_a[:, T1:], k_attn=k_a[:, T1:], v_attn=v_a[:, T1:],
+                              doc_start=ds[:, T1:])
+
+    base = second_call(att["q"], att["k"], att["v"])
+    g = oracle.attention_backward(att["q"][:, T1:], base["Kc"], base["Vc"], base["pos"], base["count"], dO,
+                                  scale=scale, t0=T1, doc_start=ds[:, T1:])
+    n = int(base["count"][0, 0])
+    pos = base["pos"][0, 0, :n]
+    eps = 1e-6
+    for name in ("q", "k", "v"):
+        num = np.zeros((T, d))
+        for t in range(T):
+            for i in range(d):
+                plus = {k: x.copy() for k, x in att.items()}
+                minus = {k: x.copy() for k, x in att.items()}
+                plus[name][0, t, 0, i] += eps
+                minus[name][0, t, 0, i] -= eps
+                lp = (dO * second_call(plus["q"], plus["k"], plus["v"])["o_kv"]).sum()
+                lm = (dO * second_call(minus["q"], minus["k"], minus["v"])["o_kv"]).sum()
+                num[t, i] = (lp - lm) / (2 * eps)
+        if name == "q":
+            np.testing.assert_allclose(g["dq"][0, :, 0], num[T1:], rtol=1e-6, atol=1e-7)
+            assert np.abs(num[:T1]).max() == 0                  # earlier queries are not in the loss
+        else:
+            ana = np.zeros((T, d))
+            ana[pos] = (g["dKc"] if name == "k" else g["dVc"])[0, 0, :n]
+            np.testing.assert_allclose(ana, num, rtol=1e-6, atol=1e-7)
+    assert np.abs(g["dKc"]).max() > 0 and np.abs(g["dq"]).max() > 0
