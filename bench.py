@@ -195,7 +195,7 @@ def bench_forward(args, dev):
                             achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
         per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
     dom = max(per, key=lambda x: x["ms"])
-    router = rope = packed = blocks = kvh = paper = None
+    router = rope = packed = blocks = kvh = paper = bwd = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
         router = bench_router(args, dev, w, t)
@@ -215,9 +215,10 @@ def bench_forward(args, dev):
                                 device=dev)
         kvh = bench_variant(args, dev, w, t, tau, f"kv_heads{2 * w.H}_dk{w.d}_dv{w.d // 2}", attn=att)
         paper = bench_paper_heads(args, dev, w)
+        bwd = bench_backward(args, dev, w, t, plan, pairs)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper)
+                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper, bwd=bwd)
 
 
 def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0,
@@ -306,6 +307,34 @@ def bench_paper_heads(args, dev, w, steps=5, warmup=5):
     return dict(workload=label, ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
                 rho_measured=round(rho, 6), steps=steps, warmup=warmup,
                 stages_ms=dict(zip(names, [round(x, 4) for x in stages])))
+
+
+def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
+    """Gradients of the attention readout at the layer shape (the cache of the main
+    forward plan, dO ~ N(0,1)): fp32 VALU kernels, priced at 10 d FLOPs per visible
+    pair (the score recompute and the four products of the backward)."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    cache = dict(Kc=plan.Kc, Vc=plan.Vc, pos=plan.pos, count=plan.count)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 9)
+    dO = torch.randn((w.B, w.T, w.H, w.d), generator=gen, device=dev, dtype=torch.float32)
+    for _ in range(warmup):
+        ham.ham_attention_backward(t["q"], cache, dO, scale=w.attn_scale)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ham.ham_attention_backward(t["q"], cache, dO, scale=w.attn_scale)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = pairs * 10 * w.d / (ms / 1e3) / 1e12
+    log(f"[bench] attention backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
+        f"({100 * tflops / PEAK_FP32_TFLOPS:.1f}% of the fp32 vector peak)")
+    return dict(workload=f"{w.name}_attention_backward", ms_per_step=round(ms, 4), steps=steps,
+                warmup=warmup, roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_TFLOPS,
+                                             unit="TFLOP/s", frac=round(tflops / PEAK_FP32_TFLOPS, 4)))
 
 
 def bench_long(args, dev, steps=10, warmup=10):
@@ -553,6 +582,7 @@ def main():
         "block_routing": res["blocks"],
         "kv_heads": res["kvh"],
         "paper_heads": res["paper"],
+        "attention_backward": res["bwd"],
         "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
