@@ -13,8 +13,8 @@
 // Visibility comes from the cache itself: entries are in ascending position, so
 // query t (absolute position t0 + t) sees entries [lo_t, n_t) with n_t = #{pos <=
 // t0 + t} and lo_t = #{pos < doc start}.  Two kernels, both fp32: the query kernel
-// (one wave per four queries) forms the row statistics (m, l, D) and dq; the entry kernel
-// (one wave per four cache entries) walks the queries that see them and forms dk, dv.
+// (one wave per eight queries) forms the row statistics (m, l, D) and dq; the entry kernel
+// (one wave per eight cache entries) walks the queries that see them and forms dk, dv.
 // Each takes 64 items at a time with a lane per item for the dot products (rows read
 // as 16-byte runs), then turns to a lane per output dimension to accumulate, so no
 // lane holds a whole gradient row.
@@ -316,11 +316,11 @@ __global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnBwdArgs a) {
 
 template <class IO, int DK, int DV>
 static hipError_t launch_bwd_t(const AttnBwdArgs& a, hipStream_t s) {
-  constexpr int QB = 4;
+  constexpr int QB = 8;
   hipLaunchKernelGGL((attn_bwd_q_kernel<IO, DK, DV, QB>), dim3((a.T + QB - 1) / QB, a.H, a.B), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int EB = 4;
+  constexpr int EB = 8;
   hipLaunchKernelGGL((attn_bwd_kv_kernel<IO, DK, DV, EB>), dim3((a.cap + EB - 1) / EB, a.H, a.B), dim3(64), 0,
                      s, a);
   return hipGetLastError();
