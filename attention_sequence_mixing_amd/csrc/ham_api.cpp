@@ -65,8 +65,9 @@ int check_dims(const ham_dims* d, bool need_T, bool attn = true) {
     if (!(((DKK == 64 || DKK == 128) && (DVK == 64 || DVK == 128)) || (DKK == 128 && DVK == 192)))
       return fail(HAM_EUNSUPPORTED, "dk_kv and dv_kv must be 64 or 128, or 128 with 192 (dk_kv=%d "
                                     "dv_kv=%d)", DKK, DVK);
-    if (HK % d->H)
-      return fail(HAM_EUNSUPPORTED, "kv_heads (%d) must be a multiple of H (%d)", HK, d->H);
+    // the readout mix across head counts pairs two KV heads with each RNN head
+    if (HK != d->H && HK != 2 * d->H)
+      return fail(HAM_EUNSUPPORTED, "kv_heads (%d) must equal H or 2*H (H=%d)", HK, d->H);
     if ((long long)HK * DVK != (long long)d->H * d->dv)
       return fail(HAM_EUNSUPPORTED, "the KV heads' values must tile the RNN heads' output: kv_heads*dv_kv "
                                     "(%d*%d) != H*dv (%d*%d)", HK, DVK, d->H, d->dv);

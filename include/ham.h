@@ -102,8 +102,8 @@ typedef struct {
                          a workspace table and the rotation runs in float.      */
     int route_block;  /* 0 or 1: every token is routed on its own score.  2, 4,
                          8, 16, 32 or 64: block-contiguous routing ([HAM] §7:
-                         sending contiguous blocks of tokens to the KV cache
-                         against the random access of per-token routing).  The
+                         routing whole runs of adjacent tokens into the cache
+                         to avoid the scattered reads of per-token routing).  The
                          positions are cut into aligned blocks of route_block
                          tokens; a block enters the cache whole when the mean
                          of its tokens' scores (summed in token order in fp32,
@@ -116,8 +116,8 @@ typedef struct {
                          per-token rule.  ham_forward and ham_route_stats take
                          whole blocks (t0 and T multiples of route_block);
                          ham_decode_step keeps the open block pending.        */
-    int kv_heads;     /* 0 (= H), or the number of attention (KV) heads: a
-                         multiple r of H.  The paper's layers have twice as many
+    int kv_heads;     /* 0 (= H), or the number of attention (KV) heads: H or
+                         r*H with r = 2 (other multiples: HAM_EUNSUPPORTED).  The paper's layers have twice as many
                          KV heads as RNN heads, each half the RNN head's size
                          ([HAM] §4 model setup: RNN heads 256/384, KV heads
                          128/192, the value size chosen to match the RNN's

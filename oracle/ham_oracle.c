@@ -46,8 +46,8 @@
  *   the end of the call stays unrouted.
  *   if routed: append (k^a_t, v^a_t, position) to this head's cache
  *   (with a rotary base b > 0 the attention-path query and key are rotated at
- *    their original positions first: RoPE, [HAM] §4 "RoPE with a base of 500K for
- *    all inputs to self-attention", citing Su et al.'s RoFormer: consecutive
+ *    their original positions first: RoPE, [HAM] §4 model setup (rotary base
+ *    500000 on the attention path's inputs), citing Su et al.'s RoFormer: consecutive
  *    pairs (x_2i, x_2i+1) turned by the angle position * b^(-2i/d_k))
  *   o_kv_t  = softmax over the cached keys, scale * q^a_t . k_c, of the cached
  *             values; 0 when no cached key is visible     ([HAM] §2 KV-memory
@@ -70,7 +70,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* RoPE ([HAM] §4: base 500K for all inputs to self-attention; RoFormer, Su et al.):
+/* RoPE ([HAM] §4 model setup: rotary base 500000 on the attention inputs; RoFormer):
  * y_2i = x_2i cos(a_i) - x_2i+1 sin(a_i), y_2i+1 = x_2i sin(a_i) + x_2i+1 cos(a_i),
  * a_i = pos * base^(-2i/d).  y may not alias x. */
 static void rope_rotate(const double *x, double *y, int d, double pos, double base)

@@ -202,6 +202,10 @@ def test_kv_head_geometry_checks():
         L.ham_forward_workspace_size(ctypes.byref(dims()))           # the readout scratch
     assert L.ham_decode_workspace_size(ctypes.byref(dims(kv_heads=8, dk_kv=64, dv_kv=64))) > 0
     for bad, code in ((dims(kv_heads=6, dv_kv=64), _lib.HAM_EUNSUPPORTED),     # not a multiple of H
+                      # values tile the RNN heads, but only two KV heads per RNN head are mixed
+                      (dims(H=5, dk=256, dv=384, kv_heads=15, dk_kv=128, dv_kv=128), _lib.HAM_EUNSUPPORTED),
+                      (dims(H=5, dk=256, dv=384, kv_heads=30, dk_kv=64, dv_kv=64), _lib.HAM_EUNSUPPORTED),
+                      (dims(kv_heads=16, dk_kv=64, dv_kv=32), _lib.HAM_EUNSUPPORTED),
                       (dims(kv_heads=8), _lib.HAM_EUNSUPPORTED),               # 8*128 != 4*128
                       (dims(dk_kv=96), _lib.HAM_EUNSUPPORTED),
                       (dims(kv_heads=-1), _lib.HAM_EINVAL)):

@@ -161,6 +161,68 @@ def test_score_invariants():
     np.testing.assert_array_equal(o4["e"], 1.0)
 
 
+# --- the decision rule at the threshold: strict, NaN never routes --------------------
+def test_score_equal_to_tau_does_not_route():
+    """A token is stored when its score exceeds the threshold ([HAM] App. A.1 "Forward
+    Pass"), so a score equal to tau stays out.  From a zero state e_0 = 1 exactly
+    (cos := 0), so tau = 1.0 keeps token 0 out and the next float below 1.0 lets it
+    in; the same holds for every token when v = 0 (e = 1 throughout)."""
+    inp = make_inputs(2, 24, 3, 8, seed=19)
+    at = oracle.forward(**inp, tau=np.full(3, 1.0, np.float32), scale=0.5)
+    below = oracle.forward(**inp, tau=np.full(3, np.nextafter(np.float32(1.0), np.float32(0.0)), np.float32),
+                           scale=0.5)
+    assert np.all(at["e"][:, 0, :] == 1.0)
+    assert not at["routed"][:, 0, :].any()
+    assert below["routed"][:, 0, :].all()
+    zero_v = dict(inp); zero_v["v"] = np.zeros_like(inp["v"])
+    z_at = oracle.forward(**zero_v, tau=np.full(3, 1.0, np.float32), scale=0.5)
+    z_below = oracle.forward(**zero_v, tau=np.full(3, np.nextafter(np.float32(1.0), np.float32(0.0)), np.float32),
+                             scale=0.5)
+    assert z_at["count"].sum() == 0 and not z_at["routed"].any()
+    assert z_below["routed"].all() and np.all(z_below["count"] == 24)
+
+
+def test_router_score_ties_and_nan_do_not_route():
+    """Learned-router scores equal to tau or NaN stay out of the cache; the next float
+    above tau goes in.  Checked per token, per threshold schedule, and with blocks
+    whose mean score equals tau exactly (block-contiguous routing, mean in fp32)."""
+    B, T, H, d = 1, 32, 2, 8
+    inp = make_inputs(B, T, H, d, seed=20)
+    tau = np.array([0.5, 0.25], np.float32)
+    rs = np.full((B, T, H), 0.125, np.float32)
+    rs[0, 0::4, :] = tau                                     # exact ties
+    rs[0, 1::4, :] = np.nan
+    rs[0, 2::4, :] = np.nextafter(tau, np.float32(np.inf))   # just above
+    out = oracle.forward(**inp, tau=tau, scale=0.5, router_score=rs)
+    want = np.zeros((B, T, H), np.int8)
+    want[0, 2::4, :] = 1
+    np.testing.assert_array_equal(out["routed"], want)
+    assert np.all(out["count"] == T // 4)
+    sched = np.broadcast_to(tau, (B, T, H)).copy()
+    out_s = oracle.forward(**inp, tau=sched, scale=0.5, router_score=rs)
+    np.testing.assert_array_equal(out_s["routed"], want)
+    # blocks of 4: scores (t, t, t, t) have mean exactly t in fp32
+    rb = np.repeat(np.array([0.5, 0.75, 0.5, 0.25], np.float32), T // 4)[None, :, None].repeat(H, 2)
+    rb = np.ascontiguousarray(rb)
+    ob = oracle.forward(**inp, tau=np.full(H, 0.5, np.float32), scale=0.5, router_score=rb, route_block=4)
+    np.testing.assert_array_equal(ob["routed"][0, :, 0], (rb[0, :, 0] > 0.5).astype(np.int8))
+
+
+def test_emit_all_ones_equals_no_emit():
+    """The emit mask only skips the readout of unselected tokens: with every token
+    selected the result is the plain forward's, bit for bit."""
+    inp = make_inputs(2, 40, 2, 8, seed=21)
+    tau = np.full(2, 0.9, np.float32)
+    base = oracle.forward(**inp, tau=tau, scale=0.5)
+    allon = oracle.forward(**inp, tau=tau, scale=0.5, emit=np.ones((2, 40, 2), bool))
+    for n in ("e", "routed", "o", "o_rnn", "o_kv", "S", "Kc", "Vc", "pos", "count"):
+        np.testing.assert_array_equal(allon[n], base[n])
+    some = np.zeros((2, 40, 2), bool); some[:, ::3] = True
+    part = oracle.forward(**inp, tau=tau, scale=0.5, emit=some)
+    np.testing.assert_array_equal(part["o"][some], base["o"][some])
+    np.testing.assert_array_equal(part["o"][~some], 0.0)
+
+
 # --- threshold, compaction, attention ----------------------------------------------
 def test_tau_plus_inf_is_pure_gated_deltanet():
     inp = make_inputs(2, 64, 2, 16, seed=6)
