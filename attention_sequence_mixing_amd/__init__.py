@@ -220,8 +220,12 @@ class DecodePlan:
 
     def __init__(self, B, H, dk, dv, cap, dtype, device, *, scale=None, norm_eps=1e-6,
                  rope_base=0.0, route_block=0, kv_heads=0, dk_kv=0, dv_kv=0, want_o_rnn=False,
-                 want_o_kv=False):
+                 want_o_kv=False, noalloc=False):
+        """noalloc: call ham_decode_step_noalloc, whose scratch is the library's fixed
+        per-GPU array (no workspace is allocated here; steps that need more than it
+        holds are rejected)."""
         device = torch.device(device)
+        self.noalloc = noalloc
         self.io = _io_code(dtype)
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(dk) if scale is None else scale
@@ -237,7 +241,7 @@ class DecodePlan:
         ws_bytes = L.ham_decode_workspace_size(ctypes.byref(self.dims))
         if ws_bytes == 0:
             raise HamError(-1, L.ham_last_error().decode())
-        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.ws = None if noalloc else torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.o = torch.empty((B, H, dv), dtype=dtype, device=device)
         self.o_rnn = torch.empty((B, H, dv), dtype=dtype, device=device) if want_o_rnn else None
         self.o_kv = (torch.empty((B, self.kv[0], self.kv[2]), dtype=dtype, device=device)
@@ -280,13 +284,15 @@ class DecodePlan:
         _need("block_score", block_score, (B, H), torch.float32, dev)
         self.dims.flags = (HAM_EXTERNAL_SCORES if router_scores is not None else 0) | tf
         e = router_scores if router_scores is not None else self.e
-        rc = _lib.lib().ham_decode_step(
-            ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
-            _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start),
-            _vp(block_score), _vp(S), _vp(Kc), _vp(Vc),
-            _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
-            _vp(e), _vp(self.routed), _vp(self.status), _vp(self.ws), self.ws.numel(),
-            _stream(stream))
+        args = [ctypes.byref(self.dims), _vp(q), _vp(k), _vp(v), _vp(q_attn), _vp(k_attn), _vp(v_attn),
+                _vp(beta), _vp(g), _vp(tau), _vp(gate_rnn), _vp(gate_kv), _vp(doc_start),
+                _vp(block_score), _vp(S), _vp(Kc), _vp(Vc),
+                _vp(pos), _vp(count), _vp(t_abs), _vp(self.o), _vp(self.o_rnn), _vp(self.o_kv),
+                _vp(e), _vp(self.routed), _vp(self.status)]
+        if self.noalloc:
+            rc = _lib.lib().ham_decode_step_noalloc(*args, _stream(stream))
+        else:
+            rc = _lib.lib().ham_decode_step(*args, _vp(self.ws), self.ws.numel(), _stream(stream))
         check(rc)
         return self
 

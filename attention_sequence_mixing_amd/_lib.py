@@ -19,7 +19,8 @@ HAM_CONTINUE, HAM_FORCE_RECURRENT, HAM_EXTERNAL_SCORES, HAM_TAU_PER_TOKEN = 1, 2
 EXPORTS = ("ham_version", "ham_last_error", "ham_forward_workspace_size", "ham_forward",
            "ham_decode_workspace_size", "ham_decode_step", "ham_route_stats_workspace_size",
            "ham_route_stats", "ham_select_tau", "ham_profile_start", "ham_profile_stop",
-           "ham_attention_backward_workspace_size", "ham_attention_backward")
+           "ham_attention_backward_workspace_size", "ham_attention_backward",
+           "ham_decode_step_noalloc", "ham_decode_noalloc_scratch_bytes")
 HAM_PROFILE_STAGES = 5
 
 
@@ -66,6 +67,10 @@ def lib():
     L.ham_forward.argtypes = [D] + [P] * 24 + [Z, P]
     L.ham_decode_step.restype = I
     L.ham_decode_step.argtypes = [D] + [P] * 26 + [Z, P]
+    L.ham_decode_step_noalloc.restype = I
+    L.ham_decode_step_noalloc.argtypes = [D] + [P] * 25 + [P]
+    L.ham_decode_noalloc_scratch_bytes.restype = Z
+    L.ham_decode_noalloc_scratch_bytes.argtypes = []
     L.ham_route_stats.restype = I
     L.ham_route_stats.argtypes = [D] + [P] * 11 + [ctypes.c_float, P, P, Z, P]
     L.ham_attention_backward.restype = I

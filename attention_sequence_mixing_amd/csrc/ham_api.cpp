@@ -263,9 +263,14 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
 
 }  // namespace
 
+namespace ham {
+// The error path of entry points defined in other translation units.
+int api_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace ham
+
 extern "C" {
 
-int ham_version(void) { return 10400; }
+int ham_version(void) { return 10500; }
 
 const char* ham_last_error(void) { return g_err.c_str(); }
 

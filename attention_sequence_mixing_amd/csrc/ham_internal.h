@@ -198,6 +198,10 @@ struct AttnBwdArgs {
   int B, T, H, cap, t0;
 };
 
+// Records msg as this thread's ham_last_error() and returns code (for entry points
+// defined outside ham_api.cpp).
+int api_fail(int code, const char* msg);
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_attention_backward(int io, int dk, int dv, const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);

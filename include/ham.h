@@ -256,6 +256,35 @@ int ham_decode_step(const ham_dims *dims,
                     float *e, uint8_t *routed, int32_t *status,
                     void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * ham_decode_step_noalloc -- ham_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, semantics, errors and kernels as
+ * ham_decode_step, without (ws, ws_bytes): the scratch is a fixed array of
+ * HAM_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, which the library
+ * holds from the first call on that GPU until the process ends.  Nothing is
+ * allocated or freed by the call.
+ *   - A step whose ham_decode_workspace_size() exceeds HAM_NOALLOC_SCRATCH_BYTES
+ *     is rejected with HAM_EWORKSPACE before anything is enqueued (the split-K
+ *     partials need B * kv_heads * ceil(cap / 1024) * (dv_kv + 2) * 4 bytes,
+ *     about 9 MiB for batch 32, 16 heads of 128 and a 33K-entry cache).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on the
+ *     same GPU (different streams or threads) race and give wrong results.
+ *     Calls on one stream are ordered and safe.
+ */
+#define HAM_NOALLOC_SCRATCH_BYTES 33554432   /* 32 MiB per GPU */
+size_t ham_decode_noalloc_scratch_bytes(void);
+int ham_decode_step_noalloc(const ham_dims *dims,
+                            const void *q, const void *k, const void *v,
+                            const void *q_attn, const void *k_attn, const void *v_attn,
+                            const float *beta, const float *g, const float *tau,
+                            const float *gate_rnn, const float *gate_kv,
+                            const int32_t *doc_start, float *block_score,
+                            float *S, void *Kc, void *Vc, int32_t *pos, int32_t *count,
+                            const int32_t *t_abs,
+                            void *o, void *o_rnn, void *o_kv,
+                            float *e, uint8_t *routed, int32_t *status, void *stream);
+
 /* Bytes of device scratch ham_route_stats needs. */
 size_t ham_route_stats_workspace_size(const ham_dims *dims);
 
