@@ -27,7 +27,12 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
+# The library is built with packed fp32 instructions disabled, so its VALU kernels
+# can reach half the published vector rate: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA)
+# x 2.4 GHz.
+PEAK_FP32_VALU_TFLOPS = 78.6
 CHUNK = 64
+STAGES = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
 
 
 def log(*a):
@@ -47,6 +52,63 @@ def copy_calibration(dev):
         y.copy_(x)
     torch.cuda.synchronize()
     log(f"[bench] copy calibration: 3 copies of {n} bytes")
+
+
+def device_info(dev):
+    """Name, architecture, compute units and clock of the GPU, and the host's CPU model
+    and core counts (rocminfo for the GPU agent, /proc/cpuinfo for the host)."""
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = dict(name=p.name, arch=getattr(p, "gcnArchName", ""), cus=p.multi_processor_count,
+                mem_gib=round(p.total_memory / 2 ** 30, 1))
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        for blk in txt.split("*******"):
+            if "gfx950" in blk and "Compute Unit" in blk:
+                for ln in blk.splitlines():
+                    if "Max Clock Freq" in ln:
+                        info["max_clock_mhz"] = int(ln.split(":")[1].split()[0])
+                    if ln.strip().startswith("Compute Unit:"):
+                        info["rocminfo_cus"] = int(ln.split(":")[1])
+                break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    info.update(cpu_model=model, nproc=os.cpu_count(), cpu_affinity=avail)
+    return info
+
+
+def stream_copy_gbs(dev, nbytes=1 << 30, reps=5):
+    """Achieved bandwidth of a plain device-to-device copy (bytes read + written per
+    second): the practical ceiling next to the 8 TB/s published figure."""
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * nbytes / sec / 1e9
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_layer_bf16_B8_H16_T4096_d128.md")
@@ -121,11 +183,115 @@ def collect_stages(lib, n):
     return [float(x) for x in arr.astype(np.float64).mean(axis=0)]   # ms per stage
 
 
+def time_steps(step, steps, warmup):
+    """Run warmup untimed steps, then time exactly `steps` steps between two events
+    on torch's current stream (the launch stream); the library records per-kernel
+    HIP events on that stream during the timed steps.  Returns (ms per step, stage
+    times in ms)."""
+    import torch
+    from attention_sequence_mixing_amd import _lib
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, collect_stages(lib, steps)
+
+
+def visible_pairs(routed):
+    """Sum over queries of the routed tokens at or before them (the attention's exact
+    (query, key) pair count for per-token routing without a continued cache)."""
+    import torch
+    return float(torch.cumsum(routed.to(torch.int64), dim=1).sum().item())
+
+
+def stage_report(stages, B, T, H, d, pairs, nroute):
+    """Per-kernel achieved rate against the roof of the arithmetic each kernel runs:
+    the prep kernel's Gram products are a small share of its HBM traffic (67 FLOP/B);
+    the state kernel and attention run bf16 MFMA (the state kernel's fp32-accurate
+    products as split bf16 terms; only algorithmic FLOPs are counted)."""
+    BTH = B * T * H
+    state_flops = BTH * rnn_state_flops_per_token_head(d)
+    att_flops = pairs * attn_flops_per_pair(d)
+    # algorithmic bytes (inputs read once, outputs written once)
+    bytes_ = {"rnn_prep": BTH * (2 * d * 2 + 8),                # q, k bf16; beta, g fp32
+              "route": BTH * (16 * (d // 16) + 4 + 1),          # score partials in; e, routed out
+              "compact": BTH * (1 + 4) + nroute * (2 * (2 * d * 2) + 4)}
+    per = []
+    for i, nm in enumerate(STAGES):
+        sec = max(stages[i], 1e-9) / 1e3
+        if nm in ("rnn_state", "attention"):
+            f = state_flops if nm == "rnn_state" else att_flops
+            per.append(dict(stage=nm, ms=stages[i], bound="mfma", unit="TFLOP/s",
+                            achieved=f / sec / 1e12, peak=PEAK_BF16_TFLOPS))
+        else:
+            per.append(dict(stage=nm, ms=stages[i], bound="hbm", unit="GB/s",
+                            achieved=bytes_[nm] / sec / 1e9, peak=PEAK_HBM_GBS))
+        per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
+    return per
+
+
+def rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def bench_rho_sweep(args, dev, w, t, e_scores, rhos):
+    """The layer at the same inputs for each targeted KV fraction rho (tau per head
+    from the fit-error scores of the RNN-only pass): rho = 0 routes nothing (pure
+    gated DeltaNet plus an empty attention), rho = 1 routes every token (full causal
+    attention next to the RNN)."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd.inputs import tau_for_rho
+    out = []
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.bfloat16, dev, scale=w.attn_scale)
+    for rho in rhos:
+        tau = torch.from_numpy(tau_for_rho(e_scores, rho)).to(dev)
+        ms, stages = time_steps(lambda: plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau),
+                                args.steps, args.warmup)
+        pairs = visible_pairs(plan.routed)
+        nroute = float(plan.count.sum().item())
+        per = stage_report(stages, w.B, w.T, w.H, w.d, pairs, nroute)
+        rho_m = nroute / (w.B * w.T * w.H)
+        log(f"[bench] rho sweep {rho}: {ms:.3f} ms/step, rho {rho_m:.4f}, pairs {pairs:.3e}, "
+            f"stages {dict(zip(STAGES, [round(x, 4) for x in stages]))}")
+        out.append(dict(workload=f"{w.name}_rho{rho}", rho_target=rho, rho_measured=round(rho_m, 6),
+                        ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                        visible_pairs=pairs, stages=[rounded(x) for x in per]))
+    return out
+
+
+def bench_small(args, dev):
+    """The small fp32 workload (B 1, H 2, T 256, d 64, scale 1/8, rho 0.5): launch-latency
+    bound; reported as time per forward."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    from attention_sequence_mixing_amd.inputs import SMALL, make_workload, tau_for_rho
+    w = SMALL
+    inp = make_workload(w)
+    t = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+    st = ham.ham_route_stats(t["k"], t["v"], t["beta"], t["g"],
+                             torch.full((w.H,), float("inf"), device=dev), want_rho=False)
+    tau = torch.from_numpy(tau_for_rho(st["e"].cpu().numpy(), w.rho)).to(dev)
+    plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, torch.float32, dev, scale=w.attn_scale)
+    ms, stages = time_steps(lambda: plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau),
+                            max(args.steps, 50), max(args.warmup, 20))
+    rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
+    log(f"[bench] {w.name}: {ms * 1e3:.1f} us/step, stages {dict(zip(STAGES, [round(x, 4) for x in stages]))}")
+    return dict(workload=w.name, us_per_step=round(ms * 1e3, 2), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                rho_measured=round(rho, 6), stages_ms=dict(zip(STAGES, [round(x, 4) for x in stages])))
+
+
 def bench_forward(args, dev):
     import torch
     import attention_sequence_mixing_amd as ham
-    from attention_sequence_mixing_amd import _lib
-    from attention_sequence_mixing_amd.inputs import LAYER, make_workload, tau_for_rho
+    from attention_sequence_mixing_amd.inputs import LAYER, RHO_SWEEP, make_workload, tau_for_rho
 
     w = LAYER
     t0 = time.time()
@@ -137,64 +303,33 @@ def bench_forward(args, dev):
     log(f"[bench] inputs {w.name} drawn in {time.time() - t0:.1f}s")
     st = ham.ham_route_stats(t["k"], t["v"], t["beta"], t["g"],
                              torch.full((w.H,), float("inf"), device=dev), want_rho=False)
-    tau_np = tau_for_rho(st["e"].cpu().numpy(), w.rho)
+    e_scores = st["e"].cpu().numpy()
+    tau_np = tau_for_rho(e_scores, w.rho)
     tau = torch.from_numpy(tau_np).to(dev)
+    # The rho sweep runs first: besides its own numbers it brings the GPU clock to its
+    # loaded steady state before the headline measurement.
+    sweep = None if args.main_only else bench_rho_sweep(args, dev, w, t, e_scores,
+                                                        [r for r in RHO_SWEEP if r != w.rho])
     plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, dt, dev, scale=w.attn_scale)
-
-    def step():
-        plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # The timed steps themselves carry the per-kernel HIP events (recorded by the
-    # library on the launch stream, which is torch's current stream here).
-    lib = _lib.lib()
-    lib.ham_profile_start(args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms, stages = time_steps(lambda: plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau),
+                            args.steps, args.warmup)
     wall = time.perf_counter() - t_start
-    ms = e0.elapsed_time(e1) / args.steps
-    stages = collect_stages(lib, args.steps)
 
-    routed = plan.routed
     count = plan.count
     rho = float(count.sum().item()) / (w.B * w.T * w.H)
-    n_t = torch.cumsum(routed.to(torch.int64), dim=1)          # visible keys per query
-    pairs = float(n_t.sum().item())
-    BTH = w.B * w.T * w.H
-    d = w.d
-    rnn_flops = BTH * rnn_flops_per_token_head(d)
-    state_flops = BTH * rnn_state_flops_per_token_head(d)
-    att_flops = pairs * attn_flops_per_pair(d)
+    pairs = visible_pairs(plan.routed)
     nroute = float(count.sum().item())
-    # algorithmic bytes (inputs read once, outputs written once)
-    prep_bytes = BTH * (2 * d * 2 + 8)                          # q, k bf16; beta, g fp32
-    route_bytes = BTH * (16 * 8 + 4 + 1)                        # score partials in; e, routed out
-    compact_bytes = BTH * (1 + 4) + nroute * (2 * (2 * d * 2) + 4)
-    # Each kernel is priced against the roof of the arithmetic it runs: the prep
-    # kernel's Gram products are a small share of its HBM traffic (67 FLOP/B); the
-    # state kernel and attention run bf16 MFMA (the state kernel's fp32-accurate
-    # products as split bf16 terms; only algorithmic FLOPs are counted).
-    names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
-    per = []
-    for i, nm in enumerate(names):
-        sec = stages[i] / 1e3
-        if nm in ("rnn_state", "attention"):
-            f = state_flops if nm == "rnn_state" else att_flops
-            per.append(dict(stage=nm, ms=stages[i], bound="mfma", unit="TFLOP/s",
-                            achieved=f / sec / 1e12, peak=PEAK_BF16_TFLOPS))
-        else:
-            b = {"rnn_prep": prep_bytes, "route": route_bytes, "compact": compact_bytes}[nm]
-            per.append(dict(stage=nm, ms=stages[i], bound="hbm", unit="GB/s",
-                            achieved=b / sec / 1e9, peak=PEAK_HBM_GBS))
-        per[-1]["frac"] = per[-1]["achieved"] / per[-1]["peak"]
+    BTH = w.B * w.T * w.H
+    rnn_flops = BTH * rnn_flops_per_token_head(w.d)
+    att_flops = pairs * attn_flops_per_pair(w.d)
+    per = stage_report(stages, w.B, w.T, w.H, w.d, pairs, nroute)
     dom = max(per, key=lambda x: x["ms"])
+    if sweep is not None:
+        sweep.insert([r for r in RHO_SWEEP].index(w.rho),
+                     dict(workload=f"{w.name}_rho{w.rho}", rho_target=w.rho, rho_measured=round(rho, 6),
+                          ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
+                          visible_pairs=pairs, stages=[rounded(x) for x in per], note="the headline run"))
     router = rope = packed = blocks = kvh = paper = bwd = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
@@ -218,7 +353,8 @@ def bench_forward(args, dev):
         bwd = bench_backward(args, dev, w, t, plan, pairs)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
-                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper, bwd=bwd)
+                router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper, bwd=bwd,
+                sweep=sweep)
 
 
 def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0,
@@ -331,10 +467,10 @@ def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
     ms = e0.elapsed_time(e1) / steps
     tflops = pairs * 10 * w.d / (ms / 1e3) / 1e12
     log(f"[bench] attention backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
-        f"({100 * tflops / PEAK_FP32_TFLOPS:.1f}% of the fp32 vector peak)")
+        f"({100 * tflops / PEAK_FP32_VALU_TFLOPS:.1f}% of the fp32 VALU peak without packed instructions)")
     return dict(workload=f"{w.name}_attention_backward", ms_per_step=round(ms, 4), steps=steps,
-                warmup=warmup, roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_TFLOPS,
-                                             unit="TFLOP/s", frac=round(tflops / PEAK_FP32_TFLOPS, 4)))
+                warmup=warmup, roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
+                                             unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4)))
 
 
 def bench_long(args, dev, steps=10, warmup=10):
@@ -452,14 +588,27 @@ def bench_decode(args, dev):
     dplan = ham.DecodePlan(B, H, d, d, cap, dt, dev, scale=d ** -0.5)
     t_abs = [torch.full((B,), T0 + s, dtype=torch.int32, device=dev) for s in range(steps)]
 
-    def run_all():
+    # (b, h) heads sampled for the oracle's decode from the GPU prefill
+    sample = [(0, 0), (B // 3, H // 2), (2 * B // 3, H - 1), (B - 1, 3 % H)]
+    bs = torch.tensor([b for b, _ in sample], device=dev)
+    hs = torch.tensor([h for _, h in sample], device=dev)
+    pre_host = dict(S=S0[bs, hs].cpu().numpy(), count=count0[bs, hs].cpu().numpy(),
+                    Kc=Kc[bs, hs].float().cpu().numpy(), Vc=Vc[bs, hs].float().cpu().numpy(),
+                    pos=pos[bs, hs].cpu().numpy(), tau=tau[hs].cpu().numpy(),
+                    x={n: x[n][:, bs, hs].float().cpu().numpy() for n in x})
+    o_sampled = []
+
+    def run_all(collect=False):
         for s in range(steps):
             dplan(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s], tau, S, Kc, Vc, pos,
                   count, t_abs[s])
+            if collect:
+                o_sampled.append(dplan.o[bs, hs].float())
 
     cache_keys0 = float(count0.sum().item())
-    run_all()                               # warm-up pass over the same steps
+    run_all(collect=True)                   # warm-up pass over the same steps
     torch.cuda.synchronize()
+    pre_host["o_gpu"] = torch.stack(o_sampled, 1).cpu().numpy()      # [4, steps, d]
     S.copy_(S0); count.copy_(count0)
     lib = _lib.lib()
     lib.ham_profile_start(steps)            # per-kernel HIP events on the timed steps
@@ -478,7 +627,8 @@ def bench_decode(args, dev):
     roof = dict(stage="decode_attention", ms=float(stg[3]), bound="hbm", unit="GB/s",
                 achieved=cache_bytes / attn_sec / 1e9, peak=PEAK_HBM_GBS)
     roof["frac"] = roof["achieved"] / PEAK_HBM_GBS
-    return dict(us_per_step=us, tokens_per_s=B / (us / 1e6), steps=steps, prefix=T0,
+    return dict(us_per_step=us, tokens_per_s=B / (us / 1e6), steps=steps, prefix=T0, sampled=pre_host,
+                sample_heads=sample, B=B, H=H, d=d,
                 cache_keys_mean=mean_keys, step_bytes=cache_bytes + state_bytes,
                 step_gbs=(cache_bytes + state_bytes) / (us / 1e6) / 1e9,
                 stages_ms=dict(zip(["rnn", "route", "append", "attention", "combine"],
@@ -499,6 +649,7 @@ def cpu_baseline(res, nbatch):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
+    # the GPU machine allots 16 host CPUs to each GPU, whatever nproc shows
     threads = max(1, min(16, w.H * nb, avail))
     oracle.forward(**{n: a[:1, :64] for n, a in sub.items()}, tau=tau, scale=w.attn_scale,
                    threads=threads)   # load outside the timing
@@ -509,6 +660,38 @@ def cpu_baseline(res, nbatch):
     return dict(value=tokens / sec, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"sequences 0..{nb - 1} of {w.name} (all {w.H} heads, all {w.T} tokens, "
                        f"same tau), fp64 C oracle, {sec:.1f}s wall on {threads} threads")
+
+
+def cpu_decode_baseline(dec, threads):
+    """The fp64 oracle's decode of the sampled (b, h) heads from the GPU-produced prefill
+    (state and cache copied to the host): all decode steps, the same inputs and
+    thresholds, as the continuation of a forward (each sampled head as its own
+    sequence).  Returns the timing and the largest per-head relative difference of the
+    GPU's decode outputs from the oracle's."""
+    import oracle
+    sp = dec["sampled"]
+    n, steps, d = len(dec["sample_heads"]), dec["steps"], dec["d"]
+    xs = {k: np.ascontiguousarray(np.swapaxes(v, 0, 1)[:, :, None]) for k, v in sp["x"].items()}  # [n,steps,1,..]
+    tau = np.ascontiguousarray(np.broadcast_to(sp["tau"].reshape(n, 1, 1), (n, steps, 1)))
+    cap = sp["Kc"].shape[1]
+    cache = dict(Kc=sp["Kc"][:, None], Vc=sp["Vc"][:, None], pos=sp["pos"][:, None].astype(np.int64),
+                 count=sp["count"].reshape(n, 1).astype(np.int64))
+    thr = max(1, min(threads, n))
+    t0 = time.perf_counter()
+    ref = oracle.forward(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], tau, scale=d ** -0.5,
+                         S0=sp["S"][:, None], cache=cache, cap=cap, t0=dec["prefix"], threads=thr)
+    sec = time.perf_counter() - t0
+    err = 0.0
+    for i in range(n):
+        y = ref["o"][i, :, 0]
+        err = max(err, float(np.abs(sp["o_gpu"][i] - y).max() / max(np.abs(y).max(), 1e-30)))
+    us_head_step = sec / steps / n * thr * 1e6
+    return dict(value=round(us_head_step, 1), unit="us per decode step per (b,h) head, one thread",
+                cores=thr, kind="oracle",
+                sample=f"{n} (b,h) heads of the decode workload, {steps} steps from the GPU prefill "
+                       f"(mean {float(sp['count'].mean()):.0f} cached keys), {sec:.1f}s wall on {thr} threads",
+                whole_batch_us_per_step_16_threads=round(us_head_step * dec["B"] * dec["H"] / 16, 1),
+                max_rel_err_gpu_vs_oracle=err)
 
 
 def main():
@@ -537,9 +720,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
         return
-    p = torch.cuda.get_device_properties(dev)
-    log(f"[bench] device {p.name} {getattr(p, 'gcnArchName', '')} CUs={p.multi_processor_count} "
-        f"mem={p.total_memory / 2**30:.0f} GiB")
+    info = device_info(dev)
+    info["stream_copy_GBps"] = round(stream_copy_gbs(dev), 1)
+    log(f"[bench] device {info}")
+    small = None if args.main_only else bench_small(args, dev)
     res = bench_forward(args, dev)
     for s in res["stages"]:
         log(f"[bench] stage {s['stage']:10s} {s['ms']:8.3f} ms  {s['achieved']:9.1f} {s['unit']} "
@@ -550,6 +734,12 @@ def main():
         dec = bench_decode(args, dev)
         log(f"[bench] decode {dec['us_per_step']:.1f} us/step, stages {dec['stages_ms']}")
     cpu = None if args.no_cpu else cpu_baseline(res, args.cpu_batch)
+    if cpu is not None:
+        cpu.update(cpu_model=info.get("cpu_model"), nproc=info.get("nproc"), affinity=info.get("cpu_affinity"))
+    dec_cpu = None
+    if dec is not None and not args.no_cpu:
+        dec_cpu = cpu_decode_baseline(dec, 16)
+        log(f"[bench] decode oracle: {dec_cpu}")
     w = res["w"]
     dom = res["dom"]
     traffic = measured_traffic(dom["stage"])
@@ -576,6 +766,9 @@ def main():
         "visible_pairs": res["pairs"],
         "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
                    for s in res["stages"]],
+        "device": info,
+        "rho_sweep": res["sweep"],
+        "small_f32": small,
         "learned_router": res["router"],
         "rope": res["rope"],
         "packed_docs": res["packed"],
@@ -589,7 +782,8 @@ def main():
             "us_per_step": round(dec["us_per_step"], 2), "tokens_per_s": round(dec["tokens_per_s"], 1),
             "steps": dec["steps"], "stages_ms": {k: round(v, 4) for k, v in dec["stages_ms"].items()},
             "step_GBps": round(dec["step_gbs"], 1),
-            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec["roofline"].items()}},
+            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec["roofline"].items()},
+            "cpu_baseline": dec_cpu},
     }
     print(json.dumps(out), flush=True)
 
