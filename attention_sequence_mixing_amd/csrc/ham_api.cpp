@@ -121,7 +121,7 @@ struct SegPlan {
 };
 SegPlan seg_plan(const ham_dims* d) {
   const int nchunk = (d->T + ham::kChunk - 1) / ham::kChunk;
-  if (!use_chunked(d)) return {1, nchunk};
+  if (!use_chunked(d) || d->dk > 128) return {1, nchunk};   // segments: d_k <= 128 only
   const long long nwg = (long long)d->B * d->H * (d->dv / 64);
   if (nwg > 128) return {1, nchunk};
   const long long p = std::max<long long>(1, std::min<long long>(256 / nwg, nchunk / 8));

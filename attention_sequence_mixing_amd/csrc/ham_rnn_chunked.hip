@@ -422,9 +422,15 @@ struct ChunkLayout {
   static constexpr int RV = NW * 16 * 2;             // bytes per V-slice row
   static constexpr int NCV = NW * 2;
   static constexpr int KB = kC * RK, VB = kC * RV;
-  // a stage holds K, Q, the workgroup's V columns and the chunk record
-  static constexpr int OFF_K = 0, OFF_Q = KB, OFF_V = 2 * KB, OFF_R = 2 * KB + VB;
-  static constexpr int STAGE = OFF_R + (int)kPrepRecordBytes;
+  // A stage holds K, Q, the workgroup's V columns and the chunk record.  Up to
+  // d_k = 128 two whole stages fit in LDS.  At d_k = 256 (SPLIT) they would need
+  // 214 KB, so only K keeps two stages (it is read at both ends of a chunk); Q, V
+  // and the record have one buffer each, reloaded for the next chunk as soon as the
+  // last read of the current one is behind a barrier (139 KB).
+  static constexpr bool SPLIT = DK > 128;
+  static constexpr int OFF_K = 0, OFF_Q = SPLIT ? 0 : KB, OFF_V = OFF_Q + KB, OFF_R = OFF_V + VB;
+  static constexpr int STAGE = SPLIT ? KB : OFF_R + (int)kPrepRecordBytes;
+  static constexpr int SINGLE = SPLIT ? OFF_R + (int)kPrepRecordBytes : 16;   // Q, V, record
   static constexpr int KI = KB / 1024 / NW;          // 1 KiB loads per wave: K (and Q), V
   static constexpr int VI = VB / 1024 / NW;
   static constexpr int RI = (int)(kPrepRecordBytes / 1024);
@@ -452,6 +458,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // of the current stage do not depend on the direct loads into the other one.
   __shared__ __attribute__((aligned(16))) char stage0[LY::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[LY::STAGE];
+  __shared__ __attribute__((aligned(16))) char single[LY::SINGLE];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -517,9 +524,15 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
   for (int j = 0; j < LY::VI; ++j) voff[j] = v_off(j, kC - 1);
 
-  // part 1: K, Q and V tiles; part 2: the chunk record.  The two parts are issued
-  // at different points of the chunk (measured: issuing all loads at once stalls
-  // the loop more than spreading them).
+  // The LDS buffers of a stage: K, Q, V and the record (with SPLIT, K from the stage
+  // and the other three from the single buffer).
+  auto kbuf = [&](char* st) { return st + LY::OFF_K; };
+  auto qbuf = [&](char* st) { return (LY::SPLIT ? single : st) + LY::OFF_Q; };
+  auto vbuf = [&](char* st) { return (LY::SPLIT ? single : st) + LY::OFF_V; };
+  auto rbuf = [&](char* st) { return (LY::SPLIT ? single : st) + LY::OFF_R; };
+  // part 1: K (and, without SPLIT, Q and V) tiles; part 2: the chunk record; part 4
+  // (SPLIT): Q and V tiles.  The parts are issued at different points of the chunk
+  // (measured: issuing all loads at once stalls the loop more than spreading them).
   auto issue_chunk = [&](int cc, char* dst, int part) {
     const int t0 = cc * kC;
     const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
@@ -530,20 +543,30 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const uint32_t lo = (uint32_t)lane * 16u;
     const bool full = t0 + kC <= a.T;
 #if defined(__HIP_DEVICE_COMPILE__)
+    const bool kq = LY::SPLIT ? (part & 4) != 0 : (part & 1) != 0;   // Q and V go with this part
     if (part & 1) {
 #pragma unroll
     for (int j = 0; j < LY::KI; ++j) {
       const uint32_t ko = full ? koff[j] : k_off(j, a.T - 1 - t0);
       const int blk = (wave + NW * j) * 1024;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + ko), dst + LY::OFF_K + blk, 16, 0, 0);
-      if (RO) __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qc + ko), dst + LY::OFF_Q + blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + ko), kbuf(dst) + blk, 16, 0, 0);
+    }
+    }
+    if (kq) {
+    if (RO) {
+#pragma unroll
+    for (int j = 0; j < LY::KI; ++j) {
+      const uint32_t ko = full ? koff[j] : k_off(j, a.T - 1 - t0);
+      const int blk = (wave + NW * j) * 1024;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qc + ko), qbuf(dst) + blk, 16, 0, 0);
+    }
     }
     if (MODE != 2) {
 #pragma unroll
     for (int j = 0; j < LY::VI; ++j) {
       const uint32_t vo = full ? voff[j] : v_off(j, a.T - 1 - t0);
       const int blk = (wave + NW * j) * 1024;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), dst + LY::OFF_V + blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + vo), vbuf(dst) + blk, 16, 0, 0);
     }
     }
     }
@@ -552,11 +575,11 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     for (int j = 0; j < (LY::RI + NW - 1) / NW; ++j) {
       const int blk = (wave + NW * j) * 1024;
       if (wave + NW * j < LY::RI)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rc + blk + lo), dst + LY::OFF_R + blk, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rc + blk + lo), rbuf(dst) + blk, 16, 0, 0);
     }
     }
 #else
-    (void)kc; (void)qc; (void)vc; (void)rc; (void)lo; (void)full; (void)dst;
+    (void)kc; (void)qc; (void)vc; (void)rc; (void)lo; (void)full; (void)dst; (void)part;
 #endif
   };
 
@@ -567,7 +590,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const int s_tok = 16 * (n >> 2) + 4 * g + (n & 3);
   const uint32_t s_lane = (uint32_t)(s_tok * a.H * NSL + slice);
 
-  auto chunk_step = [&](int c, const char* stg, char* nxt) {
+  auto chunk_step = [&](int c, char* stg, char* nxt) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
     __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
@@ -575,7 +598,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     // this lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads)
     u32x2 vraw[4] = {};
     if (MODE != 2) {
-      const char* Vs = stg + LY::OFF_V;
+      const char* Vs = vbuf(stg);
       const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -590,9 +613,9 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       return f;
     };
     if (c + 1 < c_end) issue_chunk(c + 1, nxt, 1);    // the next chunk's tiles
-    const char* Ks = stg + LY::OFF_K;
-    const char* Qs = stg + LY::OFF_Q;
-    const char* rec = stg + LY::OFF_R;
+    const char* Ks = kbuf(stg);
+    const char* Qs = qbuf(stg);
+    const char* rec = rbuf(stg);
     const u32x4* Af = reinterpret_cast<const u32x4*>(rec + kRecA);
     const u32x2* Afh = reinterpret_cast<const u32x2*>(rec + kRecAh);
     const u32x4* QKf = reinterpret_cast<const u32x4*>(rec + kRecQK);
@@ -641,7 +664,13 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
       }
     }
-    if (c + 1 < c_end) issue_chunk(c + 1, nxt, 2);    // the next chunk's record
+    if (LY::SPLIT) {
+      // every wave is done with this chunk's Q and V (V is in registers): reload them
+      __syncthreads();
+      if (c + 1 < c_end) issue_chunk(c + 1, nxt, 4);
+    } else if (c + 1 < c_end) {
+      issue_chunk(c + 1, nxt, 2);                     // the next chunk's record
+    }
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
 #pragma unroll
@@ -770,11 +799,23 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
 
     // ---- S <- gamma_C S + K^T diag(exp(G_C - G)) D ----
+    f32x4 wdv[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      wdv[s][0] = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 4 * g]);
+      wdv[s][1] = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 16 + 4 * g]);
+    }
+    const float gl = gam[kC - 1];
+    if (LY::SPLIT) {
+      // every wave is done with this chunk's record: reload it for the next chunk
+      __syncthreads();
+      if (c + 1 < c_end) issue_chunk(c + 1, nxt, 2);
+    }
     bf16x8 eh[2], em[2], el[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 4 * g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&wdec[32 * s + 16 + 4 * g]);
+      const f32x4 wa = wdv[s][0];
+      const f32x4 wb = wdv[s][1];
       u32x2 h0, m0, l0, h1, m1, l1;
       split4(D[2 * s] * wa, h0, m0, l0);
       split4(D[2 * s + 1] * wb, h1, m1, l1);
@@ -782,7 +823,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       em[s] = as8(cat(m0, m1));
       el[s] = as8(cat(l0, l1));
     }
-    const float gl = gam[kC - 1];
     const int kr4 = n >> 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -803,7 +843,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     }
   };
 
-  issue_chunk(c_begin, stage0, 3);
+  issue_chunk(c_begin, stage0, 7);
   for (int c = c_begin; c < c_end; c += 2) {
     chunk_step(c, stage0, stage1);
     if (c + 1 < c_end) chunk_step(c + 1, stage1, stage0);
@@ -882,6 +922,8 @@ hipError_t launch_state_t(const RnnArgs& a, int mode, int nseg, hipStream_t s) {
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true, 0>), grid, dim3(64 * NW), 0, s, a);
   else if (mode == 0)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false, 0>), grid, dim3(64 * NW), 0, s, a);
+  else if constexpr (DK > 128)            // the segmented passes take d_k <= 128
+    return hipErrorInvalidValue;
   else if (mode == 1)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false, 1>), grid, dim3(64 * NW), 0, s, a);
   else if constexpr (DK == DV)
@@ -894,7 +936,7 @@ hipError_t launch_state_t(const RnnArgs& a, int mode, int nseg, hipStream_t s) {
 }  // namespace chunked
 
 bool rnn_chunked_supported(int io, int dk, int dv) {
-  return io == 1 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+  return io == 1 && (((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) || (dk == 256 && dv == 384));
 }
 
 int rnn_chunked_slices(int dv) { return dv / 16; }
@@ -903,6 +945,7 @@ hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t
   if (io != 1) return hipErrorInvalidValue;
   if (dk == 64) return chunked::launch_prep_t<64>(a, s);
   if (dk == 128) return chunked::launch_prep_t<128>(a, s);
+  if (dk == 256) return chunked::launch_prep_t<256>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -913,6 +956,8 @@ hipError_t launch_rnn_chunked_state_seg(int io, int dk, int dv, int mode, int ns
   if (dk == 64 && dv == 128) return chunked::launch_state_t<64, 128>(a, mode, nseg, s);
   if (dk == 128 && dv == 64) return chunked::launch_state_t<128, 64>(a, mode, nseg, s);
   if (dk == 128 && dv == 128) return chunked::launch_state_t<128, 128>(a, mode, nseg, s);
+  // the paper's RNN heads: only the one-segment full pass
+  if (dk == 256 && dv == 384 && mode == 0 && nseg == 1) return chunked::launch_state_t<256, 384>(a, 0, 1, s);
   return hipErrorInvalidValue;
 }
 

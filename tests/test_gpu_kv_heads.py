@@ -5,7 +5,8 @@ twice as many KV heads as RNN heads, each half the RNN head's size (RNN 256/384,
 128/192), the KV value size chosen so that the KV heads' outputs match the RNN's.
 Cases: RNN heads d_v = 128 with KV heads d_v = 64 (r = 2 per RNN head, d_k 64 or 128 on
 either side), one KV head per RNN head with its own key size, and the paper's own
-sizes (RNN 256/384 on the token-serial RNN kernel, KV 128/192).  KV head r*h + i follows the routing of RNN head h and holds
+sizes (RNN 256/384, KV 128/192; the RNN heads run on the chunked state pass for bf16
+with T > 64 and on the token-serial kernel otherwise).  KV head r*h + i follows the routing of RNN head h and holds
 its own cache; each side is normalised per head of its own size and gated per head.
 Compared with the oracle through the C ABI.
 """
@@ -158,10 +159,38 @@ def test_kv_heads_one_routed_set_per_layer():
         assert np.array_equal(pos[:, j, :cnt[0, 0]], pos[:, 0, :cnt[0, 0]])
 
 
+@pytest.mark.parametrize("T", [65, 127, 200, 321])
+def test_paper_rnn_heads_chunked(T):
+    """The paper's RNN heads (256/384) on the chunked state pass (bf16, T > 64): every
+    score, decision and cache entry, the final state and the outputs against the
+    oracle, at lengths on either side of the 64-token chunk and with a ragged tail;
+    the chunked and token-serial paths agree on the state and scores."""
+    B, H, dk, dv, r, dkk = 2, 2, 256, 384, 2, 128
+    Hk, dvk = r * H, dv // r
+    inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=400 + T)
+    att = make_inputs(B, T, Hk, dkk, dvk, dtype="bf16", seed=401 + T)
+    scale = dkk ** -0.5
+    tau = _tau(inp, 0.4, scale)
+    rng = np.random.default_rng(T)
+    S0 = (0.2 * rng.standard_normal((B, H, dk, dv))).astype(np.float32) if T == 200 else None
+    t, ta = to_dev(inp, torch.bfloat16, DEV), to_dev(att, torch.bfloat16, DEV)
+    tau_d = torch.from_numpy(tau).to(DEV)
+    S0d = None if S0 is None else torch.from_numpy(S0).to(DEV)
+    print(f"paper RNN heads chunked: T={T} S0={'yes' if S0 is not None else 'no'}", flush=True)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau_d, scale=scale, S0=S0d,
+                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], want_o_rnn=True, want_o_kv=True)
+    ser = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau_d, scale=scale, S0=S0d,
+                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], force_recurrent=True)
+    torch.cuda.synchronize()
+    check_forward(out, inp, tau, torch.bfloat16, scale=scale, attn=att, S0=S0)
+    assert np.abs(out["e"].cpu().numpy() - ser["e"].cpu().numpy()).max() < 1e-5
+    assert rel_err_slices(np_of(out["S"]), np_of(ser["S"]), 1) < 1e-4
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_paper_head_sizes_forward_and_decode(dtype):
-    """The paper's head sizes: RNN heads of key/value size 256/384 (token-serial RNN
-    kernel) and twice as many KV heads of 128/192, with RoPE base 500K and gates; a
+    """The paper's head sizes: RNN heads of key/value size 256/384 (chunked state pass for
+    the bf16 prefix, token-serial kernel for fp32 and the decode steps) and twice as many KV heads of 128/192, with RoPE base 500K and gates; a
     forward prefix, then decode steps, against one oracle forward."""
     B, H, dk, dv, r, dkk = 2, 2, 256, 384, 2, 128
     Hk, dvk = r * H, dv // r
