@@ -413,7 +413,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   constexpr int KI = KB / 1024, VI = VB / 1024;            // 1 KiB load instructions per tile
   static_assert((KI + VI) % NWV == 0, "tile loads must split evenly over the waves");
   constexpr int LPW = (KI + VI) / NWV;                     // load instructions per wave per tile
-  constexpr int RBK = DK * 2, RBV = DV * 2;                // row bytes
+  constexpr int RBK = DK * 2, RBV = DV * 2;                // row bytes (in memory)
+  // In LDS a V tile is kept as column parts of power-of-two width (192 = 128 + 64), each
+  // row-major with its own swizzle, so every part has power-of-two rows.
+  constexpr int DV1 = DV > 128 ? 128 : DV, DV2 = DV - DV1;
+  static_assert((DV1 & (DV1 - 1)) == 0 && (DV2 & (DV2 - 1)) == 0, "value parts must be powers of two");
+  constexpr int RB1 = DV1 * 2, RB2 = DV2 * 2;              // LDS row bytes of the parts
+  constexpr int VI1 = BN * RB1 / 1024;                     // load instructions of part 1
+  constexpr int V2OFF = KB + BN * RB1;                     // LDS offset of part 2 in a stage
   // two ring stages as separate LDS objects, so that reads of one stage are known
   // not to alias the direct loads in flight into the other
   __shared__ __attribute__((aligned(16))) char stage0[KB + VB];
@@ -473,15 +480,24 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // into the descriptor base.
   static_assert(KI % NWV == 0, "K and V loads must not share a wave step");
   constexpr int PK = (DK / 8) * RBK / 1024 > 1 ? (DK / 8) * RBK / 1024 : 1;
-  constexpr int PV = (DV / 16) * RBV / 1024 > 1 ? (DV / 16) * RBV / 1024 : 1;
-  static_assert(NWV % PK == 0 && NWV % PV == 0, "swizzle period must divide the wave count");
-  const int jK = wave % PK, jV = wave % PV;
-  int ldK, ldV;
+  constexpr int PV1 = (DV1 / 16) * RB1 / 1024 > 1 ? (DV1 / 16) * RB1 / 1024 : 1;
+  constexpr int PV2 = DV2 && (DV2 / 16) * RB2 / 1024 > 1 ? (DV2 / 16) * RB2 / 1024 : 1;
+  static_assert(NWV % PK == 0 && NWV % PV1 == 0 && NWV % PV2 == 0, "swizzle period must divide the wave count");
+  static_assert(KI % NWV == 0 && VI1 % NWV == 0, "K, V part 1 and V part 2 loads must not share a wave step");
+  // wave w issues the load instructions i = 4k + w of each tensor part; jX is the
+  // instruction of its period that the per-lane offset ldX was computed for
+  const int jK = wave % PK, jV1 = wave % PV1, jV2 = wave % PV2;
+  int ldK, ldV1, ldV2 = 0;
   {
     const int pk = jK * 1024 + lane * 16, rk = pk / RBK;
     ldK = rk * RBK + ((((pk % RBK) >> 4) ^ swz_k<DK>(rk)) << 4);
-    const int pv = jV * 1024 + lane * 16, rv = pv / RBV;
-    ldV = rv * RBV + ((((pv % RBV) >> 4) ^ swz_v<DV>(rv)) << 4);
+    // V parts: LDS rows of RBp bytes, memory rows of RBV bytes
+    const int p1 = jV1 * 1024 + lane * 16, r1 = p1 / RB1;
+    ldV1 = r1 * RBV + ((((p1 % RB1) >> 4) ^ swz_v<DV1>(r1)) << 4);
+    if constexpr (DV2 > 0) {
+      const int p2 = jV2 * 1024 + lane * 16, r2 = p2 / RB2;
+      ldV2 = r2 * RBV + RB1 + ((((p2 % RB2) >> 4) ^ swz_v<DV2>(r2)) << 4);
+    }
   }
   auto issue_tile = [&](int it, char* st) {
     const int c0 = it * BN;
@@ -491,9 +507,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       if (k < KI / NWV) {
         const int i = k * NWV + wave, sh = (i - jK) * 1024;
         buffer_to_lds(Kh + (size_t)c0 * RBK + sh, max(rows * RBK - sh, 0), ldK, st + i * 1024);
+      } else if (k < (KI + VI1) / NWV) {
+        // part 1 instruction i covers LDS rows from (i * 1024 / RB1) on
+        const int i = (k - KI / NWV) * NWV + wave, sh = (i - jV1) * (1024 / RB1) * RBV;
+        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV1, st + KB + i * 1024);
       } else {
-        const int i = (k - KI / NWV) * NWV + wave, sh = (i - jV) * 1024;
-        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV, st + KB + i * 1024);
+        const int i = (k - (KI + VI1) / NWV) * NWV + wave, sh = (i - jV2) * (1024 / (RB2 ? RB2 : 1)) * RBV;
+        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV2, st + V2OFF + i * 1024);
       }
     }
   };
@@ -517,8 +537,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   {
     const int ry = 4 * g + r4;                             // tile row of this lane's V run (mod 16)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      voff[dt] = KB + ry * RBV + (((2 * dt + (c4 >> 1)) ^ swz_v<DV>(ry)) << 4) + (c4 & 1) * 8;
+    for (int dt = 0; dt < DT; ++dt) {
+      if (dt < DV1 / 16)
+        voff[dt] = KB + ry * RB1 + (((2 * dt + (c4 >> 1)) ^ swz_v<DV1>(ry)) << 4) + (c4 & 1) * 8;
+      else
+        voff[dt] = V2OFF + ry * RB2 + (((2 * (dt - DV1 / 16) + (c4 >> 1)) ^ swz_v<DV2 ? DV2 : 16>(ry)) << 4) +
+                   (c4 & 1) * 8;
+    }
   }
 
   const int ntiles = (nhi + BN - 1) / BN;
@@ -664,8 +689,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     for (int u = 0; u < NKT / 2; ++u) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const short4v lo = lds_read_tr16(Vt, voff[dt] + 32 * u * RBV);
-        const short4v hi = lds_read_tr16(Vt, voff[dt] + (32 * u + 16) * RBV);
+        const int rbl = dt < DV1 / 16 ? RB1 : RB2;         // LDS row bytes of dt's part
+        const short4v lo = lds_read_tr16(Vt, voff[dt] + 32 * u * rbl);
+        const short4v hi = lds_read_tr16(Vt, voff[dt] + (32 * u + 16) * rbl);
         short8v va;
         va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
         va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
@@ -687,7 +713,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   constexpr int OCH = DV * 2 / 16;                         // 16-byte chunks per row
   constexpr int OWB = BMW * DV * 2;                        // one wave's rows, bytes
   // (not with document masks: that variant has no registers to spare for it)
-  constexpr bool kOrnnLds = !DOC && NWV * OWB <= KB + VB;  // they fit in a stage
+  constexpr bool kOrnnLds = !DOC && NWV * OWB <= KB + VB && (OCH & (OCH - 1)) == 0;  // they fit in a stage
   const char* ornn_st = nullptr;
   auto issue_ornn = [&](char* st) {
     const int rstride = a.H * DV * 2;
@@ -818,7 +844,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
 
 template <int DK, int DV>
 static hipError_t launch_attn_bf16_v5(const AttnArgs& a, hipStream_t s) {
-  constexpr int QT = 2, BM = 4 * 16 * QT;
+  // two 16-query tiles per wave; one at d_v = 192, where two would not fit the
+  // register file of two workgroups per CU
+  constexpr int QT = DV > 128 ? 1 : 2, BM = 4 * 16 * QT;
   const int nqb = (a.T + BM - 1) / BM;
   if (a.lo)
     hipLaunchKernelGGL((attn_bf16_v5_kernel<DK, DV, QT, true>), dim3(nqb * a.B * a.H), dim3(256), 0, s, a);
@@ -897,7 +925,7 @@ hipError_t launch_attention(int io, int dk, int dv, const AttnArgs& a, hipStream
     if (dk == 64 && dv == 128) return launch_attn_bf16_v5<64, 128>(a, s);
     if (dk == 128 && dv == 64) return launch_attn_bf16_v5<128, 64>(a, s);
     if (dk == 128 && dv == 128) return launch_attn_bf16_v5<128, 128>(a, s);
-    HAM_CASE(IoBF16, 128, 192)
+    if (dk == 128 && dv == 192) return launch_attn_bf16_v5<128, 192>(a, s);
   }
 #undef HAM_CASE
   return hipErrorInvalidValue;

@@ -159,12 +159,14 @@ def test_kv_heads_one_routed_set_per_layer():
         assert np.array_equal(pos[:, j, :cnt[0, 0]], pos[:, 0, :cnt[0, 0]])
 
 
-@pytest.mark.parametrize("T", [65, 127, 200, 321])
-def test_paper_rnn_heads_chunked(T):
-    """The paper's RNN heads (256/384) on the chunked state pass (bf16, T > 64): every
-    score, decision and cache entry, the final state and the outputs against the
-    oracle, at lengths on either side of the 64-token chunk and with a ragged tail;
-    the chunked and token-serial paths agree on the state and scores."""
+@pytest.mark.parametrize("T,docs", [(65, False), (127, False), (200, False), (321, False), (257, True)])
+def test_paper_rnn_heads_chunked(T, docs):
+    """The paper's RNN heads (256/384) on the chunked state pass (bf16, T > 64) with KV
+    heads of 128/192 on the tiled attention kernel: every score, decision and cache
+    entry, the final state and the outputs against the oracle, at lengths on either
+    side of the 64-token chunk and the query blocks, with a ragged tail, and once
+    over packed documents with RoPE; the chunked and token-serial paths agree on the
+    state and scores."""
     B, H, dk, dv, r, dkk = 2, 2, 256, 384, 2, 128
     Hk, dvk = r * H, dv // r
     inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=400 + T)
@@ -176,13 +178,18 @@ def test_paper_rnn_heads_chunked(T):
     t, ta = to_dev(inp, torch.bfloat16, DEV), to_dev(att, torch.bfloat16, DEV)
     tau_d = torch.from_numpy(tau).to(DEV)
     S0d = None if S0 is None else torch.from_numpy(S0).to(DEV)
-    print(f"paper RNN heads chunked: T={T} S0={'yes' if S0 is not None else 'no'}", flush=True)
+    ds = make_doc_start(B, T, 60, T) if docs else None
+    base = 500000.0 if docs else 0.0
+    dsd = None if ds is None else _i32(ds)
+    print(f"paper RNN heads chunked: T={T} S0={'yes' if S0 is not None else 'no'} docs={docs}", flush=True)
     out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau_d, scale=scale, S0=S0d,
-                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], want_o_rnn=True, want_o_kv=True)
+                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], doc_start=dsd, rope_base=base,
+                          want_o_rnn=True, want_o_kv=True)
     ser = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau_d, scale=scale, S0=S0d,
-                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], force_recurrent=True)
+                          q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], doc_start=dsd, rope_base=base,
+                          force_recurrent=True)
     torch.cuda.synchronize()
-    check_forward(out, inp, tau, torch.bfloat16, scale=scale, attn=att, S0=S0)
+    check_forward(out, inp, tau, torch.bfloat16, scale=scale, attn=att, S0=S0, doc_start=ds, rope_base=base)
     assert np.abs(out["e"].cpu().numpy() - ser["e"].cpu().numpy()).max() < 1e-5
     assert rel_err_slices(np_of(out["S"]), np_of(ser["S"]), 1) < 1e-4
 
