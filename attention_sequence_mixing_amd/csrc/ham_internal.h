@@ -42,7 +42,7 @@ struct SegArgs {
 };
 
 // Bytes of one chunk record written by the chunked path's prep kernel.
-constexpr size_t kPrepRecordBytes = 35840;
+constexpr size_t kPrepRecordBytes = 30720;
 
 struct RouteArgs {
   const float4* score;  // [B,T,H][slices]

@@ -21,10 +21,13 @@
 // S_{t-1}^T k_t)^T over the chunk.
 //
 // Precision: K, Q, V are bf16 inputs, so K K^T and Q K^T are exact on bf16 MFMA
-// (fp32 accumulate).  Every product with an fp32 operand (S, D, A, T') splits the
-// fp32 value into three bf16 terms hi+mid+lo (24 significant bits) and keeps the
-// cross terms down to 2^-16 relative, which is fp32-level accuracy; the routing
-// score needs it.  The readout O only feeds bf16 outputs and keeps two terms.
+// (fp32 accumulate).  Every product with an fp32 operand (S, D, A, T') on the path
+// of the state and the routing score splits the fp32 value into three bf16 terms
+// hi+mid+lo (24 significant bits) and keeps the cross terms down to 2^-16 relative,
+// which is fp32-level accuracy; the routing score needs it.  The readout O only
+// feeds bf16 outputs: Q S takes the leading term of S, and (Gamma o Q K^T) D the
+// leading term of Gamma o Q K^T against two terms of D (about 2^-9 relative, the
+// size of the bf16 rounding of the outputs themselves).
 //
 // Layout: one workgroup = NW waves = one head's 16*NW state columns.  The fp32 state
 // lives in MFMA accumulators (rows of S on the 16x16 tile's M axis).  Products
@@ -89,16 +92,16 @@ HAM_DEVICE void split_pair3(const f32x4& lo, const f32x4& hi, bf16x8& h, bf16x8&
 // of each 32x32 block inverse.
 //   [0, 12288)       A, full pairs (1,0) (2,0) (3,0) (3,1): 3 bf16 terms x 64 lanes x 16 B
 //   [12288, 15360)   A, half pairs (0,0) (2,1): 3 terms x 64 lanes x 8 B
-//   [15360, 23552)   Gamma o QK^T, full pairs: 2 terms x 64 x 16 B
-//   [23552, 25600)   Gamma o QK^T, half pairs: 2 terms x 64 x 8 B
-//   [25600, 31744)   T'_I = (I + diag(beta) A_II)^-1 diag(beta), 32x32 block I = 0, 1,
+//   [15360, 19456)   Gamma o QK^T, full pairs: 1 term x 64 x 16 B
+//   [19456, 20480)   Gamma o QK^T, half pairs: 1 term x 64 x 8 B
+//   [20480, 26624)   T'_I = (I + diag(beta) A_II)^-1 diag(beta), 32x32 block I = 0, 1,
 //                    second row tile: 3 terms x 64 x 16 B
-//   [31744, 34816)   first row tile of T'_I (its 16 nonzero columns): 3 terms x 64 x 8 B
-//   [34816, 35072)   gamma_t = exp(G_t)                (fp32 x 64)
-//   [35072, 35328)   w_t = exp(G_last - G_t)           (fp32 x 64)
-//   [35328, 35840)   padding to whole 1 KiB blocks
-constexpr int kRecA = 0, kRecAh = 12288, kRecQK = 15360, kRecQKh = 23552, kRecT = 25600, kRecTh = 31744,
-              kRecGam = 34816, kRecW = 35072;
+//   [26624, 29696)   first row tile of T'_I (its 16 nonzero columns): 3 terms x 64 x 8 B
+//   [29696, 29952)   gamma_t = exp(G_t)                (fp32 x 64)
+//   [29952, 30208)   w_t = exp(G_last - G_t)           (fp32 x 64)
+//   [30208, 30720)   padding to whole 1 KiB blocks
+constexpr int kRecA = 0, kRecAh = 12288, kRecQK = 15360, kRecQKh = 19456, kRecT = 20480, kRecTh = 26624,
+              kRecGam = 29696, kRecW = 29952;
 static_assert(kPrepRecordBytes % 1024 == 0 && kRecW + 256 <= (int)kPrepRecordBytes, "record layout");
 
 // Index of the (row tile mt, k-step s) pair among the six with s <= mt/2.
@@ -198,22 +201,15 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
   }
   const int pi = pair_index(mt, s);
   if (kQK) {
-    bf16x8 h8, m8;
+    bf16x8 h8;                                  // the readout's one term
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = val[i >> 2][i & 3];
-      const __bf16 xh = to_bf16(x);
-      h8[i] = xh;
-      m8[i] = to_bf16(x - from_bf16(xh));
-    }
+    for (int i = 0; i < 8; ++i) h8[i] = to_bf16(val[i >> 2][i & 3]);
     if (pair_is_half(pi)) {
-      bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecQKh) + half_slot(pi) * 2 * kWave + lane;
+      bf16x4* dst = reinterpret_cast<bf16x4*>(rec + kRecQKh) + half_slot(pi) * kWave + lane;
       dst[0] = __builtin_shufflevector(h8, h8, 0, 1, 2, 3);
-      dst[kWave] = __builtin_shufflevector(m8, m8, 0, 1, 2, 3);
     } else {
-      bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecQK) + full_slot(pi) * 2 * kWave + lane;
+      bf16x8* dst = reinterpret_cast<bf16x8*>(rec + kRecQK) + full_slot(pi) * kWave + lane;
       dst[0] = h8;
-      dst[kWave] = m8;
     }
   } else {
     bf16x8 h8, m8, l8;
@@ -657,11 +653,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         P[mt] = mfma_bf16(af, sl, P[mt]);
         P[mt] = mfma_bf16(af, smd, P[mt]);
         P[mt] = mfma_bf16(af, sh, P[mt]);
-        if (RO) {
-          const bf16x8 qa = as8(qf[ks & 1][mt]);
-          O[mt] = mfma_bf16(qa, smd, O[mt]);
-          O[mt] = mfma_bf16(qa, sh, O[mt]);
-        }
+        if (RO) O[mt] = mfma_bf16(as8(qf[ks & 1][mt]), sh, O[mt]);
       }
     }
     if (LY::SPLIT) {
@@ -729,7 +721,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     P[3] = mma6(mfma_bf16, A_at(3, 1, 0), A_at(3, 1, 1), A_at(3, 1, 2),
                 as8(dB[1][0]), as8(dB[1][1]), as8(dB[1][2]), P[3] + R3);
 
-    // ---- readout O += (Gamma o Q K^T o lower_incl) D  (bf16 outputs: 3 terms) ----
+    // ---- readout O += (Gamma o Q K^T o lower_incl) D  (bf16 outputs: 2 terms) ----
     if (RO) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -742,17 +734,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
             // products on the same accumulator, and that back-to-back pairing of the two
             // shapes gave wrong rows 4g, 4g+1 (g = 0, 1) of the tile at d_k = 64 in some
             // builds; with one shape throughout, every build checked gives exact rows.
-            const u32x2 qh2 = QKfh[(half_slot(pi) * 2 + 0) * kWave + lane];
-            const u32x2 qm2 = QKfh[(half_slot(pi) * 2 + 1) * kWave + lane];
+            const u32x2 qh2 = QKfh[half_slot(pi) * kWave + lane];
             const bf16x8 qh = as8(u32x4{qh2[0], qh2[1], 0u, 0u});
-            const bf16x8 qm = as8(u32x4{qm2[0], qm2[1], 0u, 0u});
-            O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
             O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
             O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
           } else {
-            const bf16x8 qh = as8(QKf[(full_slot(pi) * 2 + 0) * kWave + lane]);
-            const bf16x8 qm = as8(QKf[(full_slot(pi) * 2 + 1) * kWave + lane]);
-            O[mt] = mfma_bf16(qm, as8(dB[s][0]), O[mt]);
+            const bf16x8 qh = as8(QKf[full_slot(pi) * kWave + lane]);
             O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
             O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
           }
