@@ -432,9 +432,16 @@ struct ChunkLayout {
   static constexpr int RI = (int)(kPrepRecordBytes / 1024);
   static_assert(KB % (1024 * NW) == 0 && VB % (1024 * NW) == 0, "tiles must split evenly over the waves");
   static_assert(kPrepRecordBytes % 1024 == 0, "record must be whole 1 KiB blocks");
-  // byte offset of 16-byte chunk c of row r in a tile with nch chunks per row,
-  // chunks XOR-swizzled by row
-  HAM_DEVICE static int swz(int r, int c, int rowbytes, int nch) { return r * rowbytes + ((c ^ (r & (nch - 1))) << 4); }
+  // Byte offset of 16-byte chunk c of row r of a K / Q tile and of a V tile.  The
+  // chunks are XOR-swizzled by the row.  K and Q are read two ways: 16-byte row
+  // fragments (8 consecutive rows per LDS pass, same chunk) and, for K, transposing
+  // 8-byte reads (4 consecutive rows x 4 consecutive chunks per pass).  Taking the
+  // row's low three bits rotated by one keeps the first conflict free and the second
+  // at two ways, the least a fixed half-chunk allows (the plain row bits gave four).
+  // V is read transposed only: 2 (r mod 4) spreads 4 rows x 2 chunks over all banks.
+  HAM_DEVICE static int swzk(int r) { return (r & (NCK - 1) & ~7) | ((r & 1) << 2) | ((r >> 1) & 3); }
+  HAM_DEVICE static int koff(int r, int c) { return r * RK + ((c ^ swzk(r)) << 4); }
+  HAM_DEVICE static int voff(int r, int c) { return r * RV + ((c ^ (2 * (r & (NCV / 2 - 1)))) << 4); }
 };
 
 // MODE 0: the full pass (score partials; readout when RO).  MODE 1: the final state
@@ -506,12 +513,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // vectors are zero because beta = 0 there), so full chunks reuse precomputed ones.
   auto k_off = [&](int j, int tlast) {
     const int tp = (wave + NW * j) * 1024 + lane * 16;
-    const int r = tp / LY::RK, c = ((tp % LY::RK) >> 4) ^ (r & (LY::NCK - 1));
+    const int r = tp / LY::RK, c = ((tp % LY::RK) >> 4) ^ LY::swzk(r);
     return (uint32_t)(min(r, tlast) * a.H * (DK * 2) + c * 16);
   };
   auto v_off = [&](int j, int tlast) {
     const int tp = (wave + NW * j) * 1024 + lane * 16;
-    const int r = tp / LY::RV, c = ((tp % LY::RV) >> 4) ^ (r & (LY::NCV - 1));
+    const int r = tp / LY::RV, c = ((tp % LY::RV) >> 4) ^ (2 * (r & (LY::NCV / 2 - 1)));
     return (uint32_t)(min(r, tlast) * a.H * (DV * 2) + colbase * 2 + c * 16);
   };
   uint32_t koff[LY::KI], voff[LY::VI];
@@ -598,7 +605,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       const int vr = n >> 2, vc = wave * 16 + 4 * (n & 3);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        vraw[mt] = lds_tr16(Vs, LY::swz(16 * mt + 4 * g + vr, vc >> 3, LY::RV, LY::NCV) + (vc & 7) * 2);
+        vraw[mt] = lds_tr16(Vs, LY::voff(16 * mt + 4 * g + vr, vc >> 3) + (vc & 7) * 2);
     }
     auto v4_at = [&](int mt) {
       f32x4 f;
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     auto load_frags = [&](int ks, int buf) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int oa = LY::swz(16 * mt + n, 4 * ks + g, LY::RK, LY::NCK);
+        const int oa = LY::koff(16 * mt + n, 4 * ks + g);
         kf[buf][mt] = *reinterpret_cast<const u32x4*>(Ks + oa);
         if (RO) qf[buf][mt] = *reinterpret_cast<const u32x4*>(Qs + oa);
       }
@@ -820,8 +827,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int ra = 32 * s + 4 * g + kr4, rb = ra + 16;
-        const u32x2 ka = lds_tr16(Ks, LY::swz(ra, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
-        const u32x2 kb = lds_tr16(Ks, LY::swz(rb, dcol >> 3, LY::RK, LY::NCK) + (dcol & 7) * 2);
+        const u32x2 ka = lds_tr16(Ks, LY::koff(ra, dcol >> 3) + (dcol & 7) * 2);
+        const u32x2 kb = lds_tr16(Ks, LY::koff(rb, dcol >> 3) + (dcol & 7) * 2);
         const bf16x8 kt = as8(cat(ka, kb));
         S[mt] = mfma_bf16(kt, el[s], S[mt]);
         S[mt] = mfma_bf16(kt, em[s], S[mt]);
