@@ -17,11 +17,11 @@ import torch
 
 from . import _lib
 from ._lib import (HAM_BF16, HAM_CONTINUE, HAM_EXTERNAL_SCORES, HAM_F32, HAM_FORCE_RECURRENT,
-                   HAM_TAU_PER_TOKEN, HamDims, HamError, check)
+                   HAM_OVERLAP, HAM_TAU_PER_TOKEN, HamDims, HamError, check)
 
 __all__ = ["ham_forward", "ham_decode_step", "ham_route_stats", "ham_select_tau", "ForwardPlan",
            "DecodePlan", "HamError", "HAM_CONTINUE", "HAM_FORCE_RECURRENT", "HAM_EXTERNAL_SCORES",
-           "HAM_TAU_PER_TOKEN", "library_path"]
+           "HAM_TAU_PER_TOKEN", "HAM_OVERLAP", "library_path"]
 
 library_path = _lib.LIB_PATH
 
@@ -172,7 +172,7 @@ class ForwardPlan:
 def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q_attn=None,
                 k_attn=None, v_attn=None, gate_rnn=None, gate_kv=None, S0=None, cache=None,
                 t0=0, force_recurrent=False, router_scores=None, rope_base=0.0, doc_start=None,
-                route_block=0, want_o_rnn=False, want_o_kv=False, stream=None):
+                route_block=0, want_o_rnn=False, want_o_kv=False, overlap=False, stream=None):
     """One HAM layer over q, k, v [B,T,H,d] (float32 or bfloat16, on the GPU).
 
     tau: [H] float32 thresholds per head, or [B,T,H] per token and head (a schedule
@@ -187,14 +187,16 @@ def ham_forward(q, k, v, beta, g, tau, *, scale=None, norm_eps=1e-6, cap=None, q
     positions of the tokens' documents (same-document masking of a packed batch).
     route_block: 0 (per-token routing), or 2..64 (a power of two) for block-contiguous
     routing: aligned blocks route whole on their mean score and become visible from
-    their last token on; t0 and T must then be multiples of it.  Returns a dict with
+    their last token on; t0 and T must then be multiples of it.  overlap: with
+    router_scores, run the RNN on the library's second stream beside the routing and
+    attention (HAM_OVERLAP).  Returns a dict with
     o, e, routed, S, Kc, Vc, pos, count (and o_rnn / o_kv if asked); e is the routing
     score used.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     flags = ((HAM_FORCE_RECURRENT if force_recurrent else 0) | (HAM_CONTINUE if cache is not None else 0)
-             | (HAM_EXTERNAL_SCORES if router_scores is not None else 0))
+             | (HAM_EXTERNAL_SCORES if router_scores is not None else 0) | (HAM_OVERLAP if overlap else 0))
     if cache is not None:
         cap = cache["Kc"].shape[2]
     # the attention heads take the geometry of the attention-path inputs

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libham.so")
 
 HAM_OK, HAM_EINVAL, HAM_EUNSUPPORTED, HAM_ECAPACITY, HAM_EHIP, HAM_EWORKSPACE = 0, -1, -2, -3, -4, -5
 HAM_F32, HAM_BF16 = 0, 1
-HAM_CONTINUE, HAM_FORCE_RECURRENT, HAM_EXTERNAL_SCORES, HAM_TAU_PER_TOKEN = 1, 2, 4, 8
+HAM_CONTINUE, HAM_FORCE_RECURRENT, HAM_EXTERNAL_SCORES, HAM_TAU_PER_TOKEN, HAM_OVERLAP = 1, 2, 4, 8, 16
 
 # every symbol include/ham.h declares
 EXPORTS = ("ham_version", "ham_last_error", "ham_forward_workspace_size", "ham_forward",

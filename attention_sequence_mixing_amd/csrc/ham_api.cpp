@@ -46,7 +46,7 @@ int check_dims(const ham_dims* d, bool need_T, bool attn = true) {
                 d->dk, d->dv);
   if (d->io_dtype != HAM_F32 && d->io_dtype != HAM_BF16)
     return fail(HAM_EUNSUPPORTED, "io_dtype must be HAM_F32 or HAM_BF16 (got %d)", d->io_dtype);
-  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES | HAM_TAU_PER_TOKEN))
+  if (d->flags & ~(HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES | HAM_TAU_PER_TOKEN | HAM_OVERLAP))
     return fail(HAM_EUNSUPPORTED, "unknown flag bits 0x%x", d->flags);
   if (d->cap <= 0) return fail(HAM_EINVAL, "cap must be positive (cap=%d)", d->cap);
   // the attention kernels address one head's cache rows with 32-bit byte offsets
@@ -109,6 +109,9 @@ bool use_chunked(const ham_dims* d) {
          ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv);
 }
 
+struct SegPlan;
+SegPlan seg_plan(const ham_dims* d);
+
 // Segments of the chunked state pass.  Its workgroups (one per 64 state columns of a
 // head) walk the chunks in order, one per CU; with few heads most CUs would idle, so
 // the chunk sequence is cut into segments that run side by side: each segment's
@@ -121,12 +124,20 @@ struct SegPlan {
 };
 SegPlan seg_plan(const ham_dims* d) {
   const int nchunk = (d->T + ham::kChunk - 1) / ham::kChunk;
+  if (d->flags & HAM_OVERLAP) return {1, nchunk};          // the overlapped path is one segment
   if (!use_chunked(d) || d->dk > 128) return {1, nchunk};   // segments: d_k <= 128 only
   const long long nwg = (long long)d->B * d->H * (d->dv / 64);
   if (nwg > 128) return {1, nchunk};
   const long long p = std::max<long long>(1, std::min<long long>(256 / nwg, nchunk / 8));
   const int per = (int)((nchunk + p - 1) / p);
   return {(nchunk + per - 1) / per, per};                  // every segment non-empty
+}
+
+// The overlapped learned-router forward (HAM_OVERLAP with HAM_EXTERNAL_SCORES on the
+// chunked path): the RNN runs on a second stream beside routing, compaction and
+// attention, which write their readout to scratch; the mix follows the join.
+bool overlapped(const ham_dims* d) {
+  return (d->flags & HAM_OVERLAP) && (d->flags & HAM_EXTERNAL_SCORES) && use_chunked(d);
 }
 
 // Scratch regions of ham_forward / ham_route_stats (each 256-byte aligned).
@@ -152,7 +163,9 @@ FwdLayout fwd_layout(const ham_dims* d, bool with_state) {
   L.lo = off;          off += with_state ? 0 : up256(BTK * sizeof(int32_t));
   L.state = off;       off += with_state ? up256(BH * d->dk * d->dv * sizeof(float)) : 0;
   L.rope = off;        off += (!with_state && d->rope_base > 0.f) ? up256((size_t)d->T * (dk_kv(d) / 2) * sizeof(float2)) : 0;
-  L.okv32 = off;       off += (!with_state && split_heads(d)) ? up256(BTH * d->dv * sizeof(float)) : 0;
+  // the attention's own readout (fp32), when the mix runs in its own pass: KV heads of
+  // another geometry, or the overlapped learned-router forward
+  L.okv32 = off;       off += (!with_state && (split_heads(d) || overlapped(d))) ? up256(BTH * d->dv * sizeof(float)) : 0;
   L.prep = off;
   if (d->T > ham::kChunk && ham::rnn_chunked_supported(d->io_dtype, d->dk, d->dv))
     off += up256(BH * nchunk * ham::kPrepRecordBytes);
@@ -194,12 +207,14 @@ struct Profiler {
   std::mutex mu;
   bool armed = false;
   int max_calls = 0, used = 0;
-  std::vector<hipEvent_t> ev;      // max_calls x (HAM_PROFILE_STAGES + 1)
-  std::vector<int> kinds, nstage;
+  std::vector<hipEvent_t> ev;      // max_calls x HAM_PROFILE_STAGES x (begin, end)
+  std::vector<int> kinds, done;    // done: bit i set when stage i has both events
 };
 Profiler g_prof;
 
-// One call's recorder: claims a slot when armed; mark() records after a stage.
+// One call's recorder: claims a slot when armed.  Stages run one after another on
+// the call's stream (mark() ends the current stage and begins the next), or on
+// other streams (begin / end name the stage and the stream).
 struct CallTimer {
   int slot = -1, stage = 0;
   hipStream_t s;
@@ -208,18 +223,53 @@ struct CallTimer {
     if (!g_prof.armed || g_prof.used >= g_prof.max_calls) return;
     slot = g_prof.used++;
     g_prof.kinds[slot] = kind;
-    (void)hipEventRecord(g_prof.ev[(size_t)slot * (HAM_PROFILE_STAGES + 1)], s);
+    g_prof.done[slot] = 0;
+    begin(0, s);
+  }
+  hipEvent_t ev(int st, int which) const { return g_prof.ev[((size_t)slot * HAM_PROFILE_STAGES + st) * 2 + which]; }
+  void begin(int st, hipStream_t str) {
+    if (slot >= 0 && st < HAM_PROFILE_STAGES) (void)hipEventRecord(ev(st, 0), str);
+  }
+  void end(int st, hipStream_t str) {
+    if (slot < 0 || st >= HAM_PROFILE_STAGES) return;
+    (void)hipEventRecord(ev(st, 1), str);
+    g_prof.done[slot] |= 1 << st;
   }
   void mark() {
     if (slot < 0 || stage >= HAM_PROFILE_STAGES) return;
+    end(stage, s);
     ++stage;
-    (void)hipEventRecord(g_prof.ev[(size_t)slot * (HAM_PROFILE_STAGES + 1) + stage], s);
-    g_prof.nstage[slot] = stage;
+    begin(stage, s);
   }
 };
 
 template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// A second stream per device for the overlapped forward, with a fork and a join
+// event.  Created on first use (default priority, non-blocking) and kept for the
+// process.  The mutex is held from the fork to the join so that calls from several
+// host threads do not interleave their event records and waits.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  std::mutex mu;
+  hipStream_t st[kMaxDevices] = {};
+  hipEvent_t fork[kMaxDevices] = {}, join[kMaxDevices] = {};
+};
+SideStream g_side;
+
+int side_stream(int* dev_out) {
+  int dev = -1;
+  HAM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HAM_EUNSUPPORTED, "device index beyond %d", kMaxDevices - 1);
+  if (!g_side.st[dev]) {
+    HAM_HIP(hipStreamCreateWithFlags(&g_side.st[dev], hipStreamNonBlocking));
+    HAM_HIP(hipEventCreateWithFlags(&g_side.fork[dev], hipEventDisableTiming));
+    HAM_HIP(hipEventCreateWithFlags(&g_side.join[dev], hipEventDisableTiming));
+  }
+  *dev_out = dev;
+  return HAM_OK;
+}
 
 // The RNN pass shared by ham_forward and ham_route_stats; returns the slice count.
 // Two timer stages: the chunk prep (empty on the token-serial path) and the state pass.
@@ -239,7 +289,7 @@ int run_rnn(const ham_dims* d, const ham::RnnArgs& ra, hipStream_t s, int* slice
       float* Sin = at<float>(ws, L.seg_s);
       // zero-start states and transitions of segments 0 .. P-2
       ham::RnnArgs rb = ra;
-      rb.S0 = nullptr; rb.S_out = Bm; rb.o_rnn32 = nullptr;
+      rb.S0 = nullptr; rb.S_out = Bm; rb.o_rnn32 = nullptr; rb.variant = 0;
       rb.seg_chunks = per; rb.seg_stride = BH * d->dk * d->dv;
       HAM_HIP(ham::launch_rnn_chunked_state_seg(d->io_dtype, d->dk, d->dv, 1, P - 1, rb, s));
       ham::RnnArgs rh = rb;
@@ -351,11 +401,35 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
   int32_t* ntok = at<int32_t>(ws, L.ntok);
 
   CallTimer tm(0, s);
-  // with learned-router scores the RNN's score partials are computed and left unused
+  // with learned-router scores the state pass leaves out the score partials
   ham::RnnArgs ra{q, k, v, beta, g, S0, S_out, o_rnn32, score, at<char>(ws, L.prep), d->B, d->T, d->H};
+  const bool ovl = overlapped(d);
+  if (ext && use_chunked(d) && L.seg.nseg == 1) ra.variant = ovl ? 3 : 1;
   int slices = 0;
-  rc = run_rnn(d, ra, s, &slices, tm, L, ws);
-  if (rc != HAM_OK) return rc;
+  std::unique_lock<std::mutex> side_lk;
+  hipStream_t s2 = nullptr;
+  int dev = 0;
+  if (ovl) {
+    // fork: the RNN on the side stream, beside routing, compaction and attention
+    side_lk = std::unique_lock<std::mutex>(g_side.mu);
+    rc = side_stream(&dev);
+    if (rc != HAM_OK) return rc;
+    s2 = g_side.st[dev];
+    HAM_HIP(hipEventRecord(g_side.fork[dev], s));
+    HAM_HIP(hipStreamWaitEvent(s2, g_side.fork[dev], 0));
+    tm.begin(0, s2);
+    HAM_HIP(ham::launch_rnn_chunked_prep(d->io_dtype, d->dk, ra, s2));
+    tm.end(0, s2);
+    tm.begin(1, s2);
+    HAM_HIP(ham::launch_rnn_chunked_state(d->io_dtype, d->dk, d->dv, ra, s2));
+    tm.end(1, s2);
+    HAM_HIP(hipEventRecord(g_side.join[dev], s2));
+    tm.stage = 2;
+    tm.begin(2, s);
+  } else {
+    rc = run_rnn(d, ra, s, &slices, tm, L, ws);
+    if (rc != HAM_OK) return rc;
+  }
 
   ham::RouteArgs ro{score, slices, tau, ext ? nullptr : e_buf, r_buf, chunk_count,
                     (d->flags & HAM_CONTINUE) ? count : nullptr, count_in, d->B, d->T, d->H,
@@ -382,20 +456,26 @@ int ham_forward(const ham_dims* d, const void* q, const void* k, const void* v,
                       route_blk(d)};
     HAM_HIP(ham::launch_doc_lo(da, s));
   }
-  // With KV heads of another geometry the attention writes its readout to scratch and
-  // the mix of the two headwise-normalised readouts runs afterwards.
-  const bool split = split_heads(d);
-  float* okv32 = split ? at<float>(ws, L.okv32) : nullptr;
-  ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, split ? nullptr : o_rnn32, gate_rnn, gate_kv, o,
+  // With KV heads of another geometry, or on the overlapped path, the attention writes
+  // its readout to scratch and the mix of the two headwise-normalised readouts runs
+  // afterwards.
+  const bool sep = split_heads(d) || ovl;
+  float* okv32 = sep ? at<float>(ws, L.okv32) : nullptr;
+  ham::AttnArgs aa{q_attn ? q_attn : q, Kc, Vc, ntok, sep ? nullptr : o_rnn32, gate_rnn, gate_kv, o,
                    o_rnn, o_kv, d->scale, d->norm_eps, d->B, d->T, HK, d->cap, rope,
-                   (!split && use_chunked(d)) ? 1 : 0, lo, okv32};
+                   (!sep && use_chunked(d)) ? 1 : 0, lo, okv32};
   HAM_HIP(ham::launch_attention(d->io_dtype, dk_kv(d), dv_kv(d), aa, s));
-  if (split) {
+  if (ovl) {
+    tm.end(4, s);                            // attention alone; the join and mix follow
+    HAM_HIP(hipStreamWaitEvent(s, g_side.join[dev], 0));
+    side_lk.unlock();
+  }
+  if (sep) {
     ham::MixArgs mx{o_rnn32, okv32, gate_rnn, gate_kv, o, o_rnn, o_kv, d->norm_eps, d->B * d->T, d->H,
                     HK / d->H, use_chunked(d) ? 1 : 0};
     HAM_HIP(ham::launch_mix(d->io_dtype, d->dv, mx, s));
   }
-  tm.mark();
+  if (!ovl) tm.mark();
   return HAM_OK;
 }
 
@@ -546,10 +626,10 @@ int ham_profile_start(int max_calls) {
   if (max_calls <= 0 || max_calls > (1 << 20)) return fail(HAM_EINVAL, "max_calls out of range");
   std::lock_guard<std::mutex> lk(g_prof.mu);
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
-  g_prof.ev.assign((size_t)max_calls * (HAM_PROFILE_STAGES + 1), nullptr);
+  g_prof.ev.assign((size_t)max_calls * HAM_PROFILE_STAGES * 2, nullptr);
   for (auto& e : g_prof.ev) HAM_HIP(hipEventCreate(&e));
   g_prof.kinds.assign(max_calls, -1);
-  g_prof.nstage.assign(max_calls, 0);
+  g_prof.done.assign(max_calls, 0);
   g_prof.max_calls = max_calls;
   g_prof.used = 0;
   g_prof.armed = true;
@@ -564,15 +644,16 @@ int ham_profile_stop(float* stage_ms, int max_values, int* n_calls, int* kinds) 
   if (n_calls) *n_calls = used;
   for (int c = 0; c < used; ++c) {
     if (kinds) kinds[c] = g_prof.kinds[c];
-    const size_t base = (size_t)c * (HAM_PROFILE_STAGES + 1);
-    const int ns = g_prof.nstage[c];
-    if (ns > 0) HAM_HIP(hipEventSynchronize(g_prof.ev[base + ns]));
+    const size_t base = (size_t)c * HAM_PROFILE_STAGES * 2;
+    const int done = g_prof.done[c];
     for (int st = 0; st < HAM_PROFILE_STAGES; ++st) {
       const long idx = (long)c * HAM_PROFILE_STAGES + st;
-      if (!stage_ms || idx >= max_values) continue;
       float ms = 0.f;
-      if (st < ns) HAM_HIP(hipEventElapsedTime(&ms, g_prof.ev[base + st], g_prof.ev[base + st + 1]));
-      stage_ms[idx] = ms;
+      if (done & (1 << st)) {
+        HAM_HIP(hipEventSynchronize(g_prof.ev[base + 2 * st + 1]));
+        HAM_HIP(hipEventElapsedTime(&ms, g_prof.ev[base + 2 * st], g_prof.ev[base + 2 * st + 1]));
+      }
+      if (stage_ms && idx < max_values) stage_ms[idx] = ms;
     }
   }
   return HAM_OK;

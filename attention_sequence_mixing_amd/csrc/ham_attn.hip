@@ -899,12 +899,14 @@ __global__ __launch_bounds__(256) void mix_kernel(MixArgs a) {
 
 hipError_t launch_mix(int io, int dv, const MixArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(((long long)a.ntok * a.H + 3) / 4));
-  if (a.r != 2 || (dv != 128 && dv != 384)) return hipErrorInvalidValue;
-  if (io == 0 && dv == 128) hipLaunchKernelGGL((mix_kernel<IoF32, 128, 2>), grid, dim3(256), 0, s, a);
-  else if (io == 0) hipLaunchKernelGGL((mix_kernel<IoF32, 384, 2>), grid, dim3(256), 0, s, a);
-  else if (dv == 128) hipLaunchKernelGGL((mix_kernel<IoBF16, 128, 2>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((mix_kernel<IoBF16, 384, 2>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+#define HAM_MIX(IOT, DVV, RR) \
+  if (dv == DVV && a.r == RR) { hipLaunchKernelGGL((mix_kernel<IOT, DVV, RR>), grid, dim3(256), 0, s, a); return hipGetLastError(); }
+  // r = 2: KV heads of half the RNN heads' value size; r = 1: the overlapped forward
+  if (io == 0) { HAM_MIX(IoF32, 128, 2) HAM_MIX(IoF32, 384, 2) HAM_MIX(IoF32, 64, 1) HAM_MIX(IoF32, 128, 1) }
+  else { HAM_MIX(IoBF16, 128, 2) HAM_MIX(IoBF16, 384, 2) HAM_MIX(IoBF16, 64, 1) HAM_MIX(IoBF16, 128, 1)
+         HAM_MIX(IoBF16, 384, 1) }
+#undef HAM_MIX
+  return hipErrorInvalidValue;
 }
 
 template <class IO, int DK, int DV>

@@ -29,6 +29,10 @@ struct RnnArgs {
   // ends in S_out + p*seg_stride (full pass: only the last segment stores S_out there).
   int seg_chunks;
   size_t seg_stride;
+  // chunked full pass, one segment: 0, or 1 (no score partials: the routing scores
+  // are the caller's) or 3 (no score partials and the LDS-lean layout that leaves
+  // room for an attention workgroup on each CU)
+  int variant;
 };
 
 // Entering states of the segments of a segmented state pass: S_in[0] = S0 (or 0),

@@ -411,7 +411,7 @@ HAM_DEVICE void split4(const f32x4& x, u32x2& h, u32x2& m, u32x2& l) {
   l = u32x2{l0, l1};
 }
 
-template <int DK, int NW>
+template <int DK, int NW, bool LEAN = false>
 struct ChunkLayout {
   static constexpr int RK = DK * 2;                  // bytes per K / Q row
   static constexpr int NCK = DK / 8;                 // 16-byte chunks per K / Q row
@@ -422,8 +422,10 @@ struct ChunkLayout {
   // d_k = 128 two whole stages fit in LDS.  At d_k = 256 (SPLIT) they would need
   // 214 KB, so only K keeps two stages (it is read at both ends of a chunk); Q, V
   // and the record have one buffer each, reloaded for the next chunk as soon as the
-  // last read of the current one is behind a barrier (139 KB).
-  static constexpr bool SPLIT = DK > 128;
+  // last read of the current one is behind a barrier (139 KB).  LEAN asks for the
+  // same layout at d_k <= 128 (86 KB at 128), so that an attention workgroup fits
+  // on the CU beside the state pass; its extra barriers cost about 15% alone.
+  static constexpr bool SPLIT = LEAN || DK > 128;
   static constexpr int OFF_K = 0, OFF_Q = SPLIT ? 0 : KB, OFF_V = OFF_Q + KB, OFF_R = OFF_V + VB;
   static constexpr int STAGE = SPLIT ? KB : OFF_R + (int)kPrepRecordBytes;
   static constexpr int SINGLE = SPLIT ? OFF_R + (int)kPrepRecordBytes : 16;   // Q, V, record
@@ -448,11 +450,15 @@ struct ChunkLayout {
 // only.  MODE 2: the homogeneous pass (V = 0 from S0 = I, DV = DK), whose final
 // "state" is the product of the chunk transitions of a segment.  With a.seg_chunks
 // set, the grid covers several segments of the chunk sequence (see RnnArgs).
-template <int DK, int DV, int NW, bool RO, int MODE>
+// VAR (full pass only): bit 0 leaves out the score partials (the routing scores are
+// the caller's, from a learned router); bit 1 takes the LEAN LDS layout.
+constexpr int kVarNoScore = 1, kVarLean = 2;
+template <int DK, int DV, int NW, bool RO, int MODE, int VAR = 0>
 __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   static_assert(MODE == 0 || !RO, "the readout belongs to the full pass");
+  static_assert(MODE == 0 || VAR == 0, "variants of the full pass only");
   static_assert(MODE != 2 || DK == DV, "the transition is dk x dk");
-  using LY = ChunkLayout<DK, NW>;
+  using LY = ChunkLayout<DK, NW, (VAR & kVarLean) != 0>;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
   constexpr int NSL = DV / 16;    // score slices
@@ -755,7 +761,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
 
     // ---- score partials of this 16-column slice, and the readout ----
     const bool full = nvalid == kC;
-    if (MODE == 0) {
+    if (MODE == 0 && !(VAR & kVarNoScore)) {
       float xpv[16], xpp[16], xvv[16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -912,7 +918,14 @@ template <int DK, int DV>
 hipError_t launch_state_t(const RnnArgs& a, int mode, int nseg, hipStream_t s) {
   constexpr int NW = 4;
   dim3 grid((DV / (16 * NW)) * a.H * a.B * nseg);
-  if (mode == 0 && a.o_rnn32)
+  if (mode == 0 && a.o_rnn32 && a.variant == kVarNoScore)
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true, 0, kVarNoScore>), grid, dim3(64 * NW), 0, s, a);
+  else if (mode == 0 && a.o_rnn32 && a.variant == (kVarNoScore | kVarLean))
+    hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true, 0, kVarNoScore | kVarLean>), grid, dim3(64 * NW), 0,
+                       s, a);
+  else if (a.variant != 0)
+    return hipErrorInvalidValue;
+  else if (mode == 0 && a.o_rnn32)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, true, 0>), grid, dim3(64 * NW), 0, s, a);
   else if (mode == 0)
     hipLaunchKernelGGL((rnn_chunked_kernel<DK, DV, NW, false, 0>), grid, dim3(64 * NW), 0, s, a);

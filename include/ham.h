@@ -74,6 +74,18 @@ extern "C" {
                                   prediction error; tau is in the same units.  The RNN
                                   still reads every token.  ham_forward and
                                   ham_decode_step only. */
+#define HAM_OVERLAP 16         /* with HAM_EXTERNAL_SCORES (ham_forward, bf16, T > 64):
+                                  the RNN does not feed the routing, so it runs on a
+                                  second stream of the library's own (one per device,
+                                  created on first use) beside routing, compaction and
+                                  attention ([HAM] §7: with a learned router the two
+                                  memories need not wait for each other); the streams
+                                  join before the mix of the two readouts.  The call
+                                  still only enqueues work on the caller's stream, which
+                                  waits for the second one before the mix.  Calls with
+                                  this flag on one device serialise their RNN work on
+                                  that second stream.  Ignored without
+                                  HAM_EXTERNAL_SCORES or off the chunked path. */
 #define HAM_TAU_PER_TOKEN 8    /* tau holds one threshold per token and head:
                                   [B,T,H] (ham_forward, ham_route_stats) or [B,H]
                                   (ham_decode_step) instead of [H].  A schedule
@@ -89,7 +101,7 @@ typedef struct {
     float norm_eps;   /* eps of the two headwise RMS norms of the mix            */
     int cap;          /* KV-cache capacity per (b,h), in tokens, 1..4194304       */
     int flags;        /* HAM_CONTINUE | HAM_FORCE_RECURRENT | HAM_EXTERNAL_SCORES
-                         | HAM_TAU_PER_TOKEN                                      */
+                         | HAM_TAU_PER_TOKEN | HAM_OVERLAP                        */
     int t0;           /* absolute position of token 0 (recorded in pos)          */
     float rope_base;  /* 0, or the base of a rotary position embedding (RoPE)
                          applied to the attention-path query and key at their

@@ -153,3 +153,60 @@ def test_router_one_routed_set_per_layer(dtype):
     for b in range(B):
         assert (pos[b, :, :cnt[b, 0]] == pos[b, :1, :cnt[b, 0]]).all()
     check_forward(out, inp, tau, dtype, scale=d ** -0.5, router_score=rs)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,kv", [(2, 200, 3, 128, 128, None), (1, 130, 2, 64, 128, None),
+                                            (2, 150, 2, 128, 128, (4, 128, 64)),
+                                            (1, 257, 2, 256, 384, (4, 128, 192))])
+def test_router_overlap_forward(B, T, H, dk, dv, kv):
+    """HAM_OVERLAP: with learned-router scores the RNN runs on the library's second
+    stream beside routing, compaction and attention, joined before the mix.  Routing,
+    cache and state against the oracle exactly / at 1e-4, outputs at the bf16
+    tolerance, and the same results as the serial learned-router path up to the
+    rounding of the separate mix pass."""
+    seed = 90 + T + dk
+    inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=seed)
+    rs = _router_scores(B, T, H, seed)
+    tau = oracle.select_tau(rs, 0.5)
+    gr, gk = make_gates(B, T, H, seed)
+    att = None
+    kw = {}
+    if kv is not None:
+        Hk, dkk, dvk = kv
+        att = make_inputs(B, T, Hk, dkk, dvk, dtype="bf16", seed=seed + 1)
+        ta = to_dev(att, torch.bfloat16, DEV)
+        kw = dict(q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"])
+        gk = np.random.default_rng(seed).random((B, T, Hk)).astype(np.float32)
+    scale = (kv[1] if kv else dk) ** -0.5
+    t = to_dev(inp, torch.bfloat16, DEV)
+    args = (t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV))
+    common = dict(scale=scale, gate_rnn=torch.from_numpy(gr).to(DEV), gate_kv=torch.from_numpy(gk).to(DEV),
+                  router_scores=torch.from_numpy(rs).to(DEV), want_o_rnn=True, want_o_kv=True, **kw)
+    print(f"overlap: B={B} T={T} H={H} {dk}/{dv} kv={kv}", flush=True)
+    ovl = ham.ham_forward(*args, overlap=True, **common)
+    ser = ham.ham_forward(*args, overlap=False, **common)
+    torch.cuda.synchronize()
+    check_forward(ovl, inp, tau, torch.bfloat16, scale=scale, gates=(gr, gk), router_score=rs, attn=att)
+    for n in ("routed", "count", "pos", "Kc", "Vc"):
+        assert torch.equal(ovl[n], ser[n]), n
+    assert torch.equal(ovl["S"], ser["S"])
+    assert rel_err_slices(np_of(ovl["o"]), np_of(ser["o"]), 2) < 1e-2
+
+
+def test_router_overlap_calls_in_a_row():
+    """Overlapped calls back to back on one stream, on two shapes, each against the
+    serial path (the second stream and its events are reused)."""
+    outs = []
+    for (B, T, H, d, seed) in ((2, 300, 2, 128, 95), (1, 100, 3, 64, 96), (2, 300, 2, 128, 97)):
+        inp = make_inputs(B, T, H, d, dtype="bf16", seed=seed)
+        rs = _router_scores(B, T, H, seed)
+        tau = torch.from_numpy(oracle.select_tau(rs, 0.3)).to(DEV)
+        t = to_dev(inp, torch.bfloat16, DEV)
+        r = torch.from_numpy(rs).to(DEV)
+        a = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, router_scores=r, overlap=True)
+        b = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, router_scores=r, overlap=False)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in outs:
+        assert torch.equal(a["S"], b["S"]) and torch.equal(a["count"], b["count"])
+        assert rel_err_slices(np_of(a["o"]), np_of(b["o"]), 2) < 1e-2
