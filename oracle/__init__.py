@@ -18,6 +18,7 @@ invariants, textbook linear algebra and brute force.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -249,3 +250,54 @@ def attention_backward(q_attn, Kc, Vc, pos, count, dO, *, scale, t0=0, doc_start
             dK[b, h, :n] = scale * dS.T @ Q
             dV[b, h, :n] = P.T @ G
     return dict(dq=dq, dKc=dK, dVc=dV)
+
+
+def rnn_backward(q, k, v, beta, g, dO, *, S0=None, dS_T=None):
+    """Gradients of the gated delta-rule RNN readout ([HAM] §2 DeltaNet update and
+    linear-attention readout, App. A.1 gated DeltaNet), written out per head in
+    float64 by reverse-mode differentiation of the token-serial recurrence.
+
+    Forward (per head):  p_t = S_{t-1}^T k_t,  r_t = v_t - alpha_t p_t,
+    S_t = alpha_t S_{t-1} + beta_t k_t r_t^T,  o_t = S_t^T q_t,  alpha_t = exp(g_t).
+    Given dO = dL/do_rnn [B,T,H,dv] and dS_T = dL/dS_T [B,H,dk,dv] (None: 0), with
+    G = dL/dS_t accumulated from the end:
+      G += q_t dO_t^T;  dq_t = S_t dO_t;  u_t = G^T k_t;
+      dv_t = beta_t u_t;  dbeta_t = u_t . r_t;
+      dk_t = beta_t (G r_t - alpha_t S_{t-1} u_t);
+      dalpha_t = <G, S_{t-1}> - beta_t u_t . p_t;  dg_t = alpha_t dalpha_t;
+      G <- alpha_t (G - beta_t k_t u_t^T)   (dL/dS_{t-1});   dS0 = G at the end.
+    The routing decision passes no gradient (a hard threshold).  Returns dict(dq,
+    dk [B,T,H,dk], dv [B,T,H,dv], dbeta, dg [B,T,H], dS0 [B,H,dk,dv])."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    beta, g = np.asarray(beta, np.float64), np.asarray(g, np.float64)
+    dO = np.asarray(dO, np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)), dv=np.zeros((B, T, H, dv)),
+               dbeta=np.zeros((B, T, H)), dg=np.zeros((B, T, H)), dS0=np.zeros((B, H, dk, dv)))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            states = [S]                                   # S_{-1} = S0, then S_0 .. S_{T-1}
+            for t in range(T):
+                a = math.exp(g[b, t, h])
+                p = S.T @ k[b, t, h]
+                S = a * S + beta[b, t, h] * np.outer(k[b, t, h], v[b, t, h] - a * p)
+                states.append(S)
+            G = np.zeros((dk, dv)) if dS_T is None else np.array(dS_T[b, h], dtype=np.float64)
+            for t in range(T - 1, -1, -1):
+                a, bt = math.exp(g[b, t, h]), beta[b, t, h]
+                kt, qt, vt, do = k[b, t, h], q[b, t, h], v[b, t, h], dO[b, t, h]
+                Sp, St = states[t], states[t + 1]
+                G = G + np.outer(qt, do)
+                out["dq"][b, t, h] = St @ do
+                p = Sp.T @ kt
+                r = vt - a * p
+                u = G.T @ kt
+                out["dv"][b, t, h] = bt * u
+                out["dbeta"][b, t, h] = u @ r
+                out["dk"][b, t, h] = bt * (G @ r - a * (Sp @ u))
+                out["dg"][b, t, h] = a * (np.sum(G * Sp) - bt * (u @ p))
+                G = a * (G - bt * np.outer(kt, u))
+            out["dS0"][b, h] = G
+    return out

@@ -784,3 +784,56 @@ def test_attention_backward_matches_finite_differences():
             ana[pos] = (g["dKc"] if name == "k" else g["dVc"])[0, 0, :n]
             np.testing.assert_allclose(ana, num, rtol=1e-6, atol=1e-7)
     assert np.abs(g["dKc"]).max() > 0 and np.abs(g["dq"]).max() > 0
+
+
+# --- gradients of the gated delta-rule RNN ---------------------------------------------
+def _rnn_loss(inp, S0, W, WS):
+    """A linear functional of the RNN outputs: sum <W_t, o_rnn_t> + <WS, S_T>, from the
+    C forward (no routing: tau = +inf)."""
+    H = inp["q"].shape[2]
+    out = oracle.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], np.full(H, INF, np.float32),
+                         scale=1.0, S0=S0)
+    return float(np.sum(W * out["o_rnn"]) + np.sum(WS * out["S"]))
+
+
+def test_rnn_backward_matches_finite_differences():
+    """Every element of dq, dk, dv, dbeta, dg and dS0 against central differences of
+    the token-serial forward (fp64), for a loss linear in o_rnn and S_T."""
+    rng = np.random.default_rng(71)
+    B, T, H, dk, dv = 1, 6, 2, 4, 3
+    inp = {n: np.asarray(a, np.float64) for n, a in make_inputs(B, T, H, dk, dv, seed=71).items()}
+    S0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    W = rng.standard_normal((B, T, H, dv))
+    WS = rng.standard_normal((B, H, dk, dv))
+    grad = oracle.rnn_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], W, S0=S0, dS_T=WS)
+    eps = 1e-6
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "g": "dg"}
+    for n, gn in names.items():
+        x = inp[n]
+        for idx in np.ndindex(x.shape):
+            up = {m: a.copy() for m, a in inp.items()}; dn = {m: a.copy() for m, a in inp.items()}
+            up[n][idx] += eps; dn[n][idx] -= eps
+            fd = (_rnn_loss(up, S0, W, WS) - _rnn_loss(dn, S0, W, WS)) / (2 * eps)
+            assert abs(fd - grad[gn][idx]) < 1e-7 * max(1.0, abs(fd)), (n, idx, fd, grad[gn][idx])
+    for idx in np.ndindex(S0.shape):
+        up = S0.copy(); dn = S0.copy()
+        up[idx] += eps; dn[idx] -= eps
+        fd = (_rnn_loss(inp, up, W, WS) - _rnn_loss(inp, dn, W, WS)) / (2 * eps)
+        assert abs(fd - grad["dS0"][idx]) < 1e-7 * max(1.0, abs(fd)), ("S0", idx)
+
+
+def test_rnn_backward_pure_decay_closed_form():
+    """beta = 0: S_t = (prod_{s<=t} alpha_s) S0, so dq_t = S_t dO_t, dv = 0 and
+    dS0 = sum_t (prod_{s<=t} alpha_s) q_t dO_t^T."""
+    rng = np.random.default_rng(72)
+    T, dk, dv = 9, 5, 4
+    q = rng.standard_normal((1, T, 1, dk)); k = rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv)); g = -rng.random((1, T, 1))
+    S0 = rng.standard_normal((1, 1, dk, dv)); dO = rng.standard_normal((1, T, 1, dv))
+    grad = oracle.rnn_backward(q, k, v, np.zeros((1, T, 1)), g, dO, S0=S0)
+    decay = np.exp(np.cumsum(g[0, :, 0]))
+    for t in range(T):
+        np.testing.assert_allclose(grad["dq"][0, t, 0], decay[t] * S0[0, 0] @ dO[0, t, 0], atol=1e-12)
+    np.testing.assert_allclose(grad["dv"], 0.0, atol=0)
+    want = sum(decay[t] * np.outer(q[0, t, 0], dO[0, t, 0]) for t in range(T))
+    np.testing.assert_allclose(grad["dS0"][0, 0], want, atol=1e-12)
