@@ -403,3 +403,37 @@ def ham_attention_backward(q_attn, cache, dO, *, scale=None, t0=0, doc_start=Non
                                    _vp(doc_start), _vp(dO), _vp(dq), _vp(dKc), _vp(dVc), _vp(ws), ws.numel(),
                                    _stream(stream)))
     return dict(dq=dq, dKc=dKc, dVc=dVc)
+
+
+def ham_rnn_backward(q, k, v, beta, g, dO, *, S0=None, dS_T=None, stream=None):
+    """Gradients of the gated delta-rule RNN for training: q, k [B,T,H,dk], v [B,T,H,dv]
+    (float32 or bfloat16), beta, g [B,T,H] float32 (the forward's inputs), S0 the
+    forward's entering state or None, dO = dL/do_rnn [B,T,H,dv] float32, dS_T = dL/dS_T
+    [B,H,dk,dv] or None.  Returns dict(dq, dk, dv, dbeta, dg, dS0) in float32."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need("k", k, (B, T, H, dk), dt, dev)
+    _need("v", v, (B, T, H, dv), dt, dev)
+    for n, t in (("beta", beta), ("g", g)):
+        _need(n, t, (B, T, H), torch.float32, dev)
+    _need("dO", dO, (B, T, H, dv), torch.float32, dev)
+    _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    _need("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
+    dims = make_dims(B, T, H, dk, dv, _io_code(dt), 1.0, 1e-6, max(T, 1))
+    L = _lib.lib()
+    ws_bytes = L.ham_rnn_backward_workspace_size(ctypes.byref(dims))
+    if ws_bytes == 0:
+        raise HamError(-2, L.ham_last_error().decode())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = dict(dq=torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               dk=torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               dv=torch.empty((B, T, H, dv), dtype=torch.float32, device=dev),
+               dbeta=torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               dg=torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+    check(L.ham_rnn_backward(ctypes.byref(dims), _vp(q), _vp(k), _vp(v), _vp(beta), _vp(g), _vp(S0),
+                             _vp(dO), _vp(dS_T), _vp(out["dq"]), _vp(out["dk"]), _vp(out["dv"]),
+                             _vp(out["dbeta"]), _vp(out["dg"]), _vp(out["dS0"]), _vp(ws), ws.numel(),
+                             _stream(stream)))
+    return out

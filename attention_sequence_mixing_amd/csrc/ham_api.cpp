@@ -360,6 +360,42 @@ int ham_attention_backward(const ham_dims* d, const void* q_attn, const void* Kc
   return HAM_OK;
 }
 
+size_t ham_rnn_backward_workspace_size(const ham_dims* d) {
+  if (check_dims(d, true, false) != HAM_OK) return 0;
+  if (!ham::rnn_backward_supported(d->dk, d->dv)) {
+    fail(HAM_EUNSUPPORTED, "ham_rnn_backward: dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
+    return 0;
+  }
+  const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
+  const size_t total = ham::rnn_backward_scratch_floats(d->B, d->H, d->T, d->dk, d->dv);
+  const size_t ck = total / (nchunk + ham::kChunk) * nchunk;      // the checkpoints come first
+  return up256(ck * sizeof(float)) + up256((total - ck) * sizeof(float));
+}
+
+int ham_rnn_backward(const ham_dims* d, const void* q, const void* k, const void* v, const float* beta,
+                     const float* g, const float* S0, const float* dO, const float* dS_T, float* dq,
+                     float* dk, float* dv, float* dbeta, float* dg, float* dS0, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_dims(d, true, false);
+  if (rc != HAM_OK) return rc;
+  if (!ham::rnn_backward_supported(d->dk, d->dv))
+    return fail(HAM_EUNSUPPORTED, "ham_rnn_backward: dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
+  HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g); HAM_REQUIRE(dO);
+  HAM_REQUIRE(dq); HAM_REQUIRE(dk); HAM_REQUIRE(dv); HAM_REQUIRE(dbeta); HAM_REQUIRE(dg); HAM_REQUIRE(dS0);
+  HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(S0); HAM_ALIGNED(dO); HAM_ALIGNED(dS_T);
+  HAM_ALIGNED(dq); HAM_ALIGNED(dk); HAM_ALIGNED(dv); HAM_ALIGNED(dS0); HAM_ALIGNED(ws);
+  const size_t need = ham_rnn_backward_workspace_size(d);
+  if (!ws || ws_bytes < need)
+    return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
+  const size_t total = ham::rnn_backward_scratch_floats(d->B, d->H, d->T, d->dk, d->dv);
+  const size_t ck = total / (nchunk + ham::kChunk) * nchunk;
+  ham::RnnBwdArgs a{q, k, v, beta, g, S0, dO, dS_T, dq, dk, dv, dbeta, dg, dS0, static_cast<float*>(ws),
+                    at<float>(ws, up256(ck * sizeof(float))), d->B, d->T, d->H};
+  HAM_HIP(ham::launch_rnn_backward(d->io_dtype, d->dk, d->dv, a, static_cast<hipStream_t>(stream)));
+  return HAM_OK;
+}
+
 size_t ham_decode_workspace_size(const ham_dims* d) {
   if (check_dims(d, false) != HAM_OK) return 0;
   return dec_layout(d).total;

@@ -206,6 +206,32 @@ struct AttnBwdArgs {
 // defined outside ham_api.cpp).
 int api_fail(int code, const char* msg);
 
+// Gradients of the gated delta-rule RNN: inputs of the forward, dL/do_rnn and
+// dL/dS_T; fp32 outputs; scratch for the chunk-start checkpoints and one chunk's
+// states per wave.
+struct RnnBwdArgs {
+  const void* q;        // [B,T,H,dk] io type
+  const void* k;
+  const void* v;        // [B,T,H,dv]
+  const float* beta;    // [B,T,H]
+  const float* g;
+  const float* S0;      // [B,H,dk,dv] or null
+  const float* dO;      // [B,T,H,dv] dL/do_rnn
+  const float* dS_T;    // [B,H,dk,dv] or null
+  float* dq;            // [B,T,H,dk]
+  float* dk;
+  float* dv;            // [B,T,H,dv]
+  float* dbeta;         // [B,T,H]
+  float* dg;
+  float* dS0;           // [B,H,dk,dv]
+  float* ckpt;          // scratch: per wave, the state slab at every chunk start
+  float* states;        // scratch: per wave, the states of one chunk
+  int B, T, H;
+};
+size_t rnn_backward_scratch_floats(int B, int H, int T, int dk, int dv);
+bool rnn_backward_supported(int dk, int dv);
+hipError_t launch_rnn_backward(int io, int dk, int dv, const RnnBwdArgs& a, hipStream_t s);
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_attention_backward(int io, int dk, int dv, const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_rnn_recurrent(int io, int dk, int dv, const RnnArgs& a, hipStream_t s);

@@ -373,6 +373,41 @@ int ham_attention_backward(const ham_dims *dims, const void *q_attn, const void 
                            const float *dO, float *dq, float *dKc, float *dVc,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of device scratch ham_rnn_backward needs (0 on bad or unsupported dims). */
+size_t ham_rnn_backward_workspace_size(const ham_dims *dims);
+
+/*
+ * ham_rnn_backward -- gradients of the gated delta-rule RNN for training ([HAM]
+ * §2 DeltaNet update and linear-attention readout, App. A.1 gated DeltaNet; the
+ * pages train the layer end to end).  Per head, with alpha_t = exp(g_t),
+ *   p_t = S_{t-1}^T k_t, r_t = v_t - alpha_t p_t, S_t = alpha_t S_{t-1} + beta_t k_t r_t^T,
+ *   o_rnn_t = S_t^T q_t,
+ * given dO = dL/do_rnn and dS_T = dL/dS_T, the gradients with respect to q, k, v,
+ * beta, g and the entering state (reverse mode of that recurrence, fp32).  The
+ * routing decision passes no gradient; the gradient of the mix (norms, gates) and of
+ * the attention (ham_attention_backward) are separate.
+ *
+ *   dims               B, T, H, dk, dv (64 or 128 each), io_dtype; other fields
+ *                      are not read.
+ *   q, k, v            [B,T,H,dk|dv] io dtype: the forward's RNN inputs.
+ *   beta, g            [B,T,H] fp32.
+ *   S0                 [B,H,dk,dv] fp32 entering state of the forward, or NULL (0).
+ *   dO                 [B,T,H,dv] fp32, required.
+ *   dS_T               [B,H,dk,dv] fp32 or NULL (0).
+ *   dq, dk, dv         [B,T,H,dk|dv] fp32 out;  dbeta, dg [B,T,H] fp32 out;
+ *   dS0                [B,H,dk,dv] fp32 out: dL/dS0.
+ *   ws, ws_bytes       scratch of ham_rnn_backward_workspace_size(dims) bytes: the
+ *                      state at every 64-token chunk start and one chunk's states
+ *                      per 16 state columns (about 2 x T/64 + 64 states per head).
+ * Errors: HAM_EINVAL, HAM_EUNSUPPORTED (dk or dv not 64/128), HAM_EWORKSPACE,
+ * HAM_EHIP.
+ */
+int ham_rnn_backward(const ham_dims *dims, const void *q, const void *k, const void *v,
+                     const float *beta, const float *g, const float *S0,
+                     const float *dO, const float *dS_T,
+                     float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dS0,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Instrumentation (not part of the method): HIP-event timing of the kernel
  * stages of the next calls.  ham_profile_start(max_calls) arms recording on the
