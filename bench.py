@@ -330,7 +330,7 @@ def bench_forward(args, dev):
                      dict(workload=f"{w.name}_rho{w.rho}", rho_target=w.rho, rho_measured=round(rho, 6),
                           ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
                           visible_pairs=pairs, stages=[rounded(x) for x in per], note="the headline run"))
-    router = rope = packed = blocks = kvh = paper = bwd = None
+    router = rope = packed = blocks = kvh = paper = bwd = rbwd = None
     if not args.main_only:
         from attention_sequence_mixing_amd.inputs import make_doc_start
         router = bench_router(args, dev, w, t)
@@ -351,10 +351,11 @@ def bench_forward(args, dev):
         kvh = bench_variant(args, dev, w, t, tau, f"kv_heads{2 * w.H}_dk{w.d}_dv{w.d // 2}", attn=att)
         paper = bench_paper_heads(args, dev, w)
         bwd = bench_backward(args, dev, w, t, plan, pairs)
+        rbwd = bench_rnn_backward(args, dev, w, t)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
                 router=router, rope=rope, packed=packed, blocks=blocks, kvh=kvh, paper=paper, bwd=bwd,
-                sweep=sweep)
+                rbwd=rbwd, sweep=sweep)
 
 
 def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, route_block=0,
@@ -471,6 +472,39 @@ def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
     return dict(workload=f"{w.name}_attention_backward", ms_per_step=round(ms, 4), steps=steps,
                 warmup=warmup, roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
                                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4)))
+
+
+def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):
+    """Gradients of the gated delta-rule RNN at the layer shape (dO = dL/do_rnn and
+    dS_T ~ N(0,1)): a token-serial fp32 kernel, priced at 20 d_k d_v FLOPs per token
+    and head (two forward passes of the recurrence, 4 d_k d_v each, and the reverse
+    step, 12 d_k d_v) against the VALU rate the build can reach."""
+    import torch
+    import attention_sequence_mixing_amd as ham
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 11)
+    dO = torch.randn((w.B, w.T, w.H, w.d), generator=gen, device=dev, dtype=torch.float32)
+    dST = torch.randn((w.B, w.H, w.d, w.d), generator=gen, device=dev, dtype=torch.float32)
+
+    def run():
+        ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], dO, dS_T=dST)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = w.B * w.T * w.H * 20 * w.d * w.d / (ms / 1e3) / 1e12
+    log(f"[bench] rnn backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
+        f"({100 * tflops / PEAK_FP32_VALU_TFLOPS:.1f}% of the fp32 VALU peak without packed instructions)")
+    return dict(workload=f"{w.name}_rnn_backward", ms_per_step=round(ms, 4), steps=steps, warmup=warmup,
+                roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
+                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4)))
 
 
 def bench_long(args, dev, steps=10, warmup=10):
@@ -788,6 +822,7 @@ def main():
         "kv_heads": res["kvh"],
         "paper_heads": res["paper"],
         "attention_backward": res["bwd"],
+        "rnn_backward": res["rbwd"],
         "long_context": long_ctx,
         "decode": None if dec is None else {
             "workload": f"decode_bf16_B32_H16_d128_prefix{dec['prefix']}_rho0.5",
