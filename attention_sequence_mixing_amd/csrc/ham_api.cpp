@@ -334,9 +334,30 @@ size_t ham_route_stats_workspace_size(const ham_dims* d) {
   return fwd_layout(d, true).total;
 }
 
+// Scratch of the attention backward: per-query statistics (32 bytes per token-head);
+// with bf16 inputs also the visible range of each 64-query tile and the two bf16 terms
+// of dO.
+struct AttnBwdLayout {
+  size_t stat = 0, rng = 0, dOh = 0, dOl = 0, total = 0;
+};
+static AttnBwdLayout attn_bwd_layout(const ham_dims* d) {
+  AttnBwdLayout L;
+  const size_t ntok = (size_t)d->B * d->T * kv_heads(d);
+  L.total = up256(ntok * 8 * sizeof(float));
+  if (d->io_dtype == HAM_BF16) {
+    L.rng = L.total;
+    L.total += up256((size_t)d->B * kv_heads(d) * ((d->T + 63) / 64) * 2 * sizeof(int32_t));
+    L.dOh = L.total;
+    L.total += up256(ntok * dv_kv(d) * 2);
+    L.dOl = L.total;
+    L.total += up256(ntok * dv_kv(d) * 2);
+  }
+  return L;
+}
+
 size_t ham_attention_backward_workspace_size(const ham_dims* d) {
   if (check_dims(d, true) != HAM_OK) return 0;
-  return up256((size_t)d->B * d->T * kv_heads(d) * 3 * sizeof(float));
+  return attn_bwd_layout(d).total;
 }
 
 int ham_attention_backward(const ham_dims* d, const void* q_attn, const void* Kc, const void* Vc,
@@ -354,7 +375,12 @@ int ham_attention_backward(const ham_dims* d, const void* q_attn, const void* Kc
   const size_t need = ham_attention_backward_workspace_size(d);
   if (!ws || ws_bytes < need)
     return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
-  ham::AttnBwdArgs a{q_attn, Kc, Vc, pos, count, doc_start, dO, dq, dKc, dVc, static_cast<float*>(ws),
+  const AttnBwdLayout L = attn_bwd_layout(d);
+  char* w = static_cast<char*>(ws);
+  ham::AttnBwdArgs a{q_attn, Kc, Vc, pos, count, doc_start, dO, dq, dKc, dVc, reinterpret_cast<float*>(w + L.stat),
+                     L.rng ? reinterpret_cast<int2*>(w + L.rng) : nullptr,
+                     L.dOh ? reinterpret_cast<uint16_t*>(w + L.dOh) : nullptr,
+                     L.dOl ? reinterpret_cast<uint16_t*>(w + L.dOl) : nullptr,
                      d->scale, d->B, d->T, kv_heads(d), d->cap, d->t0};
   HAM_HIP(ham::launch_attention_backward(d->io_dtype, dk_kv(d), dv_kv(d), a, static_cast<hipStream_t>(stream)));
   return HAM_OK;

@@ -387,18 +387,6 @@ HAM_DEVICE int swz_k(int r) { return r & (D / 8 - 1); }
 template <int D>
 HAM_DEVICE int swz_v(int r) { return 2 * (r & (D / 16 - 1)); }
 
-// One 16-byte-per-lane buffer load from `base` + voff with `range_bytes` valid bytes,
-// written to LDS at `lds` + 16 * lane; offsets at or past the range read zero.
-HAM_DEVICE void buffer_to_lds(const void* base, int range_bytes, int voff, char* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                                               range_bytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
-#else
-  (void)base; (void)range_bytes; (void)voff; (void)lds;
-#endif
-}
-
 // DOC: same-document masking (a.lo set): query t sees keys lo_t <= c < ntok_t; the
 // block starts at the tile of its smallest lo.  The queries' (lo, ntok) ranges wait
 // in LDS for the tiles that need a mask (registers are at their limit here), and a

@@ -75,6 +75,20 @@ HAM_DEVICE float wave_max(float x) {
 
 HAM_DEVICE int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// One 16-byte-per-lane buffer load from `base` + voff with `range_bytes` valid bytes,
+// written straight to LDS at `lds` + 16 * lane (`lds` the same for the whole wave);
+// offsets at or past the range read zero.  Completion is tracked by vmcnt: wait on it
+// (and take a barrier for other waves' loads) before reading the bytes from LDS.
+HAM_DEVICE void buffer_to_lds(const void* base, int range_bytes, int voff, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                               range_bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#else
+  (void)base; (void)range_bytes; (void)voff; (void)lds;
+#endif
+}
+
 // Sum over the 16 lanes of a DPP row (lanes 16r..16r+15), result in every lane of
 // the row: swap neighbours, swap pairs (quad permutes), then mirror within 8 and 16
 // lanes.  Pure VALU (no LDS crossbar traffic).

@@ -197,7 +197,10 @@ struct AttnBwdArgs {
   float* dq;                // [B,T,H,dk]
   float* dKc;               // [B,H,cap,dk] (entries < count)
   float* dVc;               // [B,H,cap,dv]
-  float* stat;              // [B,T,H][3] scratch: row maximum, 1/row sum, D
+  float* stat;              // [B,T,H][8] scratch: row maximum, 1/row sum, D, -, lo_t, n_t, -, -
+  int2* tile_rng;           // bf16: [B,H,ceil(T/64)] scratch, visible entry range per query tile
+  uint16_t* dOh;            // bf16: [B,T,H,dv] scratch, dO = dOh + dOl in bf16 terms
+  uint16_t* dOl;
   float scale;
   int B, T, H, cap, t0;
 };

@@ -448,8 +448,9 @@ def bench_paper_heads(args, dev, w, steps=5, warmup=5):
 
 def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
     """Gradients of the attention readout at the layer shape (the cache of the main
-    forward plan, dO ~ N(0,1)): fp32 VALU kernels, priced at 10 d FLOPs per visible
-    pair (the score recompute and the four products of the backward)."""
+    forward plan, dO ~ N(0,1)): bf16 MFMA kernels with the fp32 operands (dO, P, dS) as
+    two bf16 terms, priced at 10 d FLOPs per visible pair (the score recompute and the
+    four products of the backward) against the bf16 MFMA peak."""
     import torch
     import attention_sequence_mixing_amd as ham
     cache = dict(Kc=plan.Kc, Vc=plan.Vc, pos=plan.pos, count=plan.count)
@@ -468,10 +469,10 @@ def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
     ms = e0.elapsed_time(e1) / steps
     tflops = pairs * 10 * w.d / (ms / 1e3) / 1e12
     log(f"[bench] attention backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
-        f"({100 * tflops / PEAK_FP32_VALU_TFLOPS:.1f}% of the fp32 VALU peak without packed instructions)")
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of the bf16 MFMA peak)")
     return dict(workload=f"{w.name}_attention_backward", ms_per_step=round(ms, 4), steps=steps,
-                warmup=warmup, roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
-                                             unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4)))
+                warmup=warmup, roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS,
+                                             unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4)))
 
 
 def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):

@@ -31,6 +31,8 @@ def _dev(x, dtype):
     (1, 200, 3, 128, 128, 0, True),
     (2, 97, 2, 64, 128, 40, False),
     (1, 130, 2, 128, 64, 60, True),
+    (1, 700, 2, 128, 128, 0, False),                  # several 64-query and 64-entry tiles
+    (2, 451, 2, 64, 128, 90, True),
 ])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_attention_backward(B, T, H, dk, dv, t1, docs, dtype):
