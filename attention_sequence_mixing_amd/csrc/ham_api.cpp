@@ -318,6 +318,33 @@ namespace ham {
 int api_fail(int code, const char* msg) { return fail(code, "%s", msg); }
 }  // namespace ham
 
+namespace ham {
+
+// The host checks of a decode step's dims and arguments (everything but the workspace).
+int decode_check(const ham_dims* d, const void* q, const void* k, const void* v, const void* q_attn,
+                      const void* k_attn, const void* v_attn, const float* beta, const float* g,
+                      const float* tau, const float* block_score, const float* S, const void* Kc,
+                      const void* Vc, const int32_t* pos, const int32_t* count, const int32_t* t_abs,
+                      const void* o, const void* o_rnn, const void* o_kv, const float* e) {
+  int rc = check_dims(d, false);
+  if (rc != HAM_OK) return rc;
+  HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g);
+  HAM_REQUIRE(tau); HAM_REQUIRE(S); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos);
+  HAM_REQUIRE(count); HAM_REQUIRE(t_abs); HAM_REQUIRE(o);
+  if (route_blk(d)) HAM_REQUIRE(block_score);
+  if (own_attn_inputs(d) && !(q_attn && k_attn && v_attn))
+    return fail(HAM_EINVAL, "the KV heads' geometry differs from the RNN heads': q_attn, k_attn and "
+                            "v_attn are required");
+  HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
+  HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
+  HAM_ALIGNED(Kc); HAM_ALIGNED(Vc);
+  if ((d->flags & HAM_EXTERNAL_SCORES) && !e)
+    return fail(HAM_EINVAL, "HAM_EXTERNAL_SCORES needs the scores in e (NULL)");
+  return HAM_OK;
+}
+
+}  // namespace ham
+
 extern "C" {
 
 int ham_version(void) { return 10500; }
@@ -549,20 +576,11 @@ int ham_decode_step(const ham_dims* d, const void* q, const void* k, const void*
                     const int32_t* t_abs, void* o, void* o_rnn, void* o_kv,
                     float* e, uint8_t* routed, int32_t* status,
                     void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_dims(d, false);
+  const int rc = ham::decode_check(d, q, k, v, q_attn, k_attn, v_attn, beta, g, tau, block_score, S, Kc, Vc, pos,
+                                   count, t_abs, o, o_rnn, o_kv, e);
   if (rc != HAM_OK) return rc;
-  HAM_REQUIRE(q); HAM_REQUIRE(k); HAM_REQUIRE(v); HAM_REQUIRE(beta); HAM_REQUIRE(g);
-  HAM_REQUIRE(tau); HAM_REQUIRE(S); HAM_REQUIRE(Kc); HAM_REQUIRE(Vc); HAM_REQUIRE(pos);
-  HAM_REQUIRE(count); HAM_REQUIRE(t_abs); HAM_REQUIRE(o);
-  if (route_blk(d)) HAM_REQUIRE(block_score);
-  if (own_attn_inputs(d) && !(q_attn && k_attn && v_attn))
-    return fail(HAM_EINVAL, "the KV heads' geometry differs from the RNN heads': q_attn, k_attn and "
-                            "v_attn are required");
-  HAM_ALIGNED(q); HAM_ALIGNED(k); HAM_ALIGNED(v); HAM_ALIGNED(q_attn); HAM_ALIGNED(k_attn);
-  HAM_ALIGNED(v_attn); HAM_ALIGNED(S); HAM_ALIGNED(o); HAM_ALIGNED(o_rnn); HAM_ALIGNED(o_kv);
-  HAM_ALIGNED(Kc); HAM_ALIGNED(Vc); HAM_ALIGNED(ws);
+  HAM_ALIGNED(ws);
   const bool ext = (d->flags & HAM_EXTERNAL_SCORES) != 0;
-  if (ext && !e) return fail(HAM_EINVAL, "HAM_EXTERNAL_SCORES needs the scores in e (NULL)");
   const DecLayout L = dec_layout(d);
   if (!ws || ws_bytes < L.total)
     return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);

@@ -124,43 +124,35 @@ __global__ __launch_bounds__(64) void attn_bwd_q_kernel(AttnBwdArgs a) {
     }
   };
 
-  // pass 1: running maximum and sum of each query's scaled scores
-  float m[QB], l[QB];
+  // pass 1: running maximum and sum of each query's scaled scores, and D = sum_c p_c
+  // (g . v_c) accumulated against the same running maximum
+  float m[QB], l[QB], D[QB];
 #pragma unroll
-  for (int j = 0; j < QB; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
-  for (int c0 = cmin; c0 < cmax; c0 += 64) {
-    const int c = c0 + lane;
-    float sc[QB], gv[QB];
-    if (c < cmax) scores(c, sc, gv, false);
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const float s = (c >= lo[j] && c < n[j]) ? a.scale * sc[j] : -INFINITY;
-      const float mn = fmaxf(m[j], wave_max<64>(s));
-      if (mn == -INFINITY) continue;                       // nothing visible yet (uniform)
-      l[j] = l[j] * expf(m[j] - mn) + wave_sum<64>(s == -INFINITY ? 0.f : expf(s - mn));
-      m[j] = mn;
-    }
-  }
-  float inv_l[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) inv_l[j] = l[j] > 0.f ? 1.f / l[j] : 0.f;
-
-  // pass 2: D = sum_c p_c (g . v_c)
-  float D[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) D[j] = 0.f;
+  for (int j = 0; j < QB; ++j) { m[j] = -INFINITY; l[j] = 0.f; D[j] = 0.f; }
   for (int c0 = cmin; c0 < cmax; c0 += 64) {
     const int c = c0 + lane;
     float sc[QB], gv[QB];
     if (c < cmax) scores(c, sc, gv, true);
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      const float x = (c >= lo[j] && c < n[j]) ? expf(a.scale * sc[j] - m[j]) * inv_l[j] * gv[j] : 0.f;
-      D[j] += wave_sum<64>(x);
+      const float s = (c >= lo[j] && c < n[j]) ? a.scale * sc[j] : -INFINITY;
+      const float mn = fmaxf(m[j], wave_max<64>(s));
+      if (mn == -INFINITY) continue;                       // nothing visible yet (uniform)
+      const float corr = expf(m[j] - mn);
+      const float x = s == -INFINITY ? 0.f : expf(s - mn);
+      l[j] = l[j] * corr + wave_sum<64>(x);
+      D[j] = D[j] * corr + wave_sum<64>(x * gv[j]);
+      m[j] = mn;
     }
   }
+  float inv_l[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    inv_l[j] = l[j] > 0.f ? 1.f / l[j] : 0.f;
+    D[j] *= inv_l[j];
+  }
 
-  // pass 3: dq = scale * sum_c p_c (g . v_c - D) k_c; the weights of 64 entries go
+  // pass 2: dq = scale * sum_c p_c (g . v_c - D) k_c; the weights of 64 entries go
   // through LDS, then each lane accumulates its own dimensions for all QB queries
   float dq[QB][PK];
 #pragma unroll

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ham.h"
+
 namespace ham {
 
 // Score partials: every RNN kernel writes, per token and per d_v slice, the
@@ -208,6 +210,14 @@ struct AttnBwdArgs {
 // Records msg as this thread's ham_last_error() and returns code (for entry points
 // defined outside ham_api.cpp).
 int api_fail(int code, const char* msg);
+
+// The host checks of ham_decode_step's dims and arguments, workspace aside: HAM_OK or
+// the error code (with its message recorded), as ham_decode_step would return it.
+int decode_check(const ham_dims* d, const void* q, const void* k, const void* v, const void* q_attn,
+                 const void* k_attn, const void* v_attn, const float* beta, const float* g, const float* tau,
+                 const float* block_score, const float* S, const void* Kc, const void* Vc, const int32_t* pos,
+                 const int32_t* count, const int32_t* t_abs, const void* o, const void* o_rnn,
+                 const void* o_kv, const float* e);
 
 // Gradients of the gated delta-rule RNN: inputs of the forward, dL/do_rnn and
 // dL/dS_T; fp32 outputs; scratch for the chunk-start checkpoints and one chunk's

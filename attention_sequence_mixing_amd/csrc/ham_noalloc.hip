@@ -55,11 +55,11 @@ extern "C" int ham_decode_step_noalloc(const ham_dims* d, const void* q, const v
                                        void* Kc, void* Vc, int32_t* pos, int32_t* count,
                                        const int32_t* t_abs, void* o, void* o_rnn, void* o_kv,
                                        float* e, uint8_t* routed, int32_t* status, void* stream) {
+  // the argument checks of ham_decode_step come first, before any device query
+  const int arc = ham::decode_check(d, q, k, v, q_attn, k_attn, v_attn, beta, g, tau, block_score, S, Kc, Vc, pos,
+                                    count, t_abs, o, o_rnn, o_kv, e);
+  if (arc != HAM_OK) return arc;
   const size_t need = ham_decode_workspace_size(d);
-  if (need == 0)   // bad dims: ham_decode_step reports them before it touches a workspace
-    return ham_decode_step(d, q, k, v, q_attn, k_attn, v_attn, beta, g, tau, gate_rnn, gate_kv, doc_start,
-                           block_score, S, Kc, Vc, pos, count, t_abs, o, o_rnn, o_kv, e, routed, status,
-                           nullptr, 0, stream);
   if (need > (size_t)HAM_NOALLOC_SCRATCH_BYTES) {
     char msg[256];
     snprintf(msg, sizeof msg,
