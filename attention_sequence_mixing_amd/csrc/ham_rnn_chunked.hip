@@ -651,15 +651,28 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         if (RO) qf[buf][mt] = *reinterpret_cast<const u32x4*>(Qs + oa);
       }
     };
-    load_frags(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      if (ks + 1 < KSD) load_frags(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);      // keep those reads ahead of this step's products
+    // the three bf16 terms of S rows 32ks..32ks+31 (the B operand of k-step ks)
+    bf16x8 spl[2][3];
+    auto split_step = [&](int ks, int buf) {
       u32x2 h0, m0, l0, h1, m1, l1;
       split4(S[2 * ks], h0, m0, l0);
       split4(S[2 * ks + 1], h1, m1, l1);
-      const bf16x8 sh = as8(cat(h0, h1)), smd = as8(cat(m0, m1)), sl = as8(cat(l0, l1));
+      spl[buf][0] = as8(cat(h0, h1));
+      spl[buf][1] = as8(cat(m0, m1));
+      spl[buf][2] = as8(cat(l0, l1));
+    };
+    load_frags(0, 0);
+    split_step(0, 0);
+    // Each k-step's products run while the next step's fragments are read and its S
+    // terms are split: the scheduler is asked for the step's LDS reads first, then one
+    // MFMA to three VALU instructions.
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      if (ks + 1 < KSD) {
+        load_frags(ks + 1, (ks + 1) & 1);
+        split_step(ks + 1, (ks + 1) & 1);
+      }
+      const bf16x8 sh = spl[ks & 1][0], smd = spl[ks & 1][1], sl = spl[ks & 1][2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 af = as8(kf[ks & 1][mt]);
@@ -668,6 +681,15 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         P[mt] = mfma_bf16(af, sh, P[mt]);
         if (RO) O[mt] = mfma_bf16(as8(qf[ks & 1][mt]), sh, O[mt]);
       }
+      if (ks + 1 < KSD) {
+        __builtin_amdgcn_sched_group_barrier(0x100, RO ? 8 : 4, 0);     // the next step's LDS reads
+#pragma unroll
+        for (int i = 0; i < (RO ? 16 : 12); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);            // three VALU
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (LY::SPLIT) {
       // every wave is done with this chunk's Q and V (V is in registers): reload them
@@ -675,6 +697,33 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       if (c + 1 < c_end) issue_chunk(c + 1, nxt, 4);
     } else if (c + 1 < c_end) {
       issue_chunk(c + 1, nxt, 2);                     // the next chunk's record
+    }
+    // The record fragments of the block substitution and the prediction below, read
+    // ahead of the serial chain of products that consumes them.
+    u32x2 pTh[2][3], pAh[2][3];
+    u32x4 pT[2][3], pA[4][3];
+    {
+      const u32x4* Tf = reinterpret_cast<const u32x4*>(rec + kRecT);
+      const u32x2* Tfh = reinterpret_cast<const u32x2*>(rec + kRecTh);
+#pragma unroll
+      for (int z = 0; z < 3; ++z) {
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+          pTh[I][z] = Tfh[(I * 3 + z) * kWave + lane];
+          pT[I][z] = Tf[(I * 3 + z) * kWave + lane];
+          pAh[I][z] = Afh[(I * 3 + z) * kWave + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pA[j][z] = Af[(j * 3 + z) * kWave + lane];
+      }
+    }
+    u32x4 pQK[4];
+    u32x2 pQKh[2];
+    if (RO) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pQK[j] = QKf[j * kWave + lane];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pQKh[j] = QKfh[j * kWave + lane];
     }
     // X = V - gamma K S ; P, O start as gamma K S, gamma Q S
     f32x4 X[4];
@@ -690,12 +739,10 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     // ---- block forward substitution over the two 32-token blocks ----
     //   D_0 = T'_0 X_0,   D_1 = T'_1 (X_1 - A_10 D_0),   P += A D (strictly lower A)
     // dB[s][z]: B-operand fragments (k-step s, term z) of D rows 32s..32s+31.
-    const u32x4* Tf = reinterpret_cast<const u32x4*>(rec + kRecT);
-    const u32x2* Tfh = reinterpret_cast<const u32x2*>(rec + kRecTh);
     auto mf16 = [](const bf16x4& x, const bf16x4& y, const f32x4& c) { return mfma_bf16_k16(x, y, c); };
     auto lo4 = [](const u32x4& x) { return as4(u32x2{x[0], x[1]}); };
-    auto A_at = [&](int mt, int s, int z) { return as8(Af[(full_slot(pair_index(mt, s)) * 3 + z) * kWave + lane]); };
-    auto Ah_at = [&](int mt, int s, int z) { return as4(Afh[(half_slot(pair_index(mt, s)) * 3 + z) * kWave + lane]); };
+    auto A_at = [&](int mt, int s, int z) { return as8(pA[full_slot(pair_index(mt, s))][z]); };
+    auto Ah_at = [&](int mt, int s, int z) { return as4(pAh[half_slot(pair_index(mt, s))][z]); };
     u32x4 dB[2][3];
     f32x4 D[4];
     auto solve_block = [&](int I, const f32x4& x0, const f32x4& x1) {
@@ -703,15 +750,10 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       split4(x0, h0, m0, l0);
       split4(x1, h1, m1, l1);
       const bf16x8 rh = as8(cat(h0, h1)), rm = as8(cat(m0, m1)), rl = as8(cat(l0, l1));
-      {
-        const u32x2* t = Tfh + (I * 3) * kWave + lane;          // first row tile: 16 columns
-        D[2 * I] = mma6(mf16, as4(t[0]), as4(t[kWave]), as4(t[2 * kWave]), as4(h0), as4(m0), as4(l0),
-                        (f32x4)(0.f));
-      }
-      {
-        const u32x4* t = Tf + (I * 3) * kWave + lane;
-        D[2 * I + 1] = mma6(mfma_bf16, as8(t[0]), as8(t[kWave]), as8(t[2 * kWave]), rh, rm, rl, (f32x4)(0.f));
-      }
+      // first row tile: 16 columns
+      D[2 * I] = mma6(mf16, as4(pTh[I][0]), as4(pTh[I][1]), as4(pTh[I][2]), as4(h0), as4(m0), as4(l0),
+                      (f32x4)(0.f));
+      D[2 * I + 1] = mma6(mfma_bf16, as8(pT[I][0]), as8(pT[I][1]), as8(pT[I][2]), rh, rm, rl, (f32x4)(0.f));
       split4(D[2 * I], h0, m0, l0);
       split4(D[2 * I + 1], h1, m1, l1);
       dB[I][0] = cat(h0, h1);
@@ -724,6 +766,26 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
     const f32x4 R3 = mma6(mfma_bf16, A_at(3, 0, 0), A_at(3, 0, 1), A_at(3, 0, 2),
                           as8(dB[0][0]), as8(dB[0][1]), as8(dB[0][2]), (f32x4)(0.f));
     solve_block(1, X[2] - R2, X[3] - R3);
+    // K^T fragments of the state update (below), read here so that their latency
+    // falls behind the prediction and the readout (up to d_k = 128: 64 registers)
+    const int kr4 = n >> 2;
+    auto kt_frag = [&](int mt, int s) {
+      // output lane 4c + i needs column srow(mt, c, i); lane (k, c) of the transposing
+      // read addresses row k, columns srow(mt, c, 0..3)
+      const int dcol = 32 * (mt >> 1) + 8 * (n & 3) + 4 * (mt & 1);
+      const int ra = 32 * s + 4 * g + kr4, rb = ra + 16;
+      const u32x2 ka = lds_tr16(Ks, LY::koff(ra, dcol >> 3) + (dcol & 7) * 2);
+      const u32x2 kb = lds_tr16(Ks, LY::koff(rb, dcol >> 3) + (dcol & 7) * 2);
+      return cat(ka, kb);
+    };
+    constexpr bool kKtAhead = DK <= 128;
+    u32x4 ktf[kKtAhead ? MT : 1][2];
+    if constexpr (kKtAhead) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ktf[mt][s] = kt_frag(mt, s);
+    }
     // the prediction P = gamma K S + A D
     P[0] = mma6(mf16, Ah_at(0, 0, 0), Ah_at(0, 0, 1), Ah_at(0, 0, 2),
                 lo4(dB[0][0]), lo4(dB[0][1]), lo4(dB[0][2]), P[0]);
@@ -747,12 +809,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
             // products on the same accumulator, and that back-to-back pairing of the two
             // shapes gave wrong rows 4g, 4g+1 (g = 0, 1) of the tile at d_k = 64 in some
             // builds; with one shape throughout, every build checked gives exact rows.
-            const u32x2 qh2 = QKfh[half_slot(pi) * kWave + lane];
+            const u32x2 qh2 = pQKh[half_slot(pi)];
             const bf16x8 qh = as8(u32x4{qh2[0], qh2[1], 0u, 0u});
             O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
             O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
           } else {
-            const bf16x8 qh = as8(QKf[full_slot(pi) * kWave + lane]);
+            const bf16x8 qh = as8(pQK[full_slot(pi)]);
             O[mt] = mfma_bf16(qh, as8(dB[s][1]), O[mt]);
             O[mt] = mfma_bf16(qh, as8(dB[s][0]), O[mt]);
           }
@@ -823,19 +885,14 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       em[s] = as8(cat(m0, m1));
       el[s] = as8(cat(l0, l1));
     }
-    const int kr4 = n >> 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       S[mt] *= gl;
-      // K^T fragment: output lane 4c + i needs column srow(mt, c, i); lane (k, c) of
-      // the transposing read addresses row k, columns srow(mt, c, 0..3)
-      const int dcol = 32 * (mt >> 1) + 8 * (n & 3) + 4 * (mt & 1);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int ra = 32 * s + 4 * g + kr4, rb = ra + 16;
-        const u32x2 ka = lds_tr16(Ks, LY::koff(ra, dcol >> 3) + (dcol & 7) * 2);
-        const u32x2 kb = lds_tr16(Ks, LY::koff(rb, dcol >> 3) + (dcol & 7) * 2);
-        const bf16x8 kt = as8(cat(ka, kb));
+        bf16x8 kt;
+        if constexpr (kKtAhead) kt = as8(ktf[mt][s]);
+        else kt = as8(kt_frag(mt, s));
         S[mt] = mfma_bf16(kt, el[s], S[mt]);
         S[mt] = mfma_bf16(kt, em[s], S[mt]);
         S[mt] = mfma_bf16(kt, eh[s], S[mt]);
