@@ -35,6 +35,14 @@ CHUNK = 64
 STAGES = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
 
 
+LEGS = ("small", "sweep", "router", "rope", "packed", "blocks", "kv_heads", "paper", "backward",
+        "rnn_backward", "long")
+
+
+def want(args, leg):
+    return leg in getattr(args, "leg_set", set(LEGS))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -308,8 +316,8 @@ def bench_forward(args, dev):
     tau = torch.from_numpy(tau_np).to(dev)
     # The rho sweep runs first: besides its own numbers it brings the GPU clock to its
     # loaded steady state before the headline measurement.
-    sweep = None if args.main_only else bench_rho_sweep(args, dev, w, t, e_scores,
-                                                        [r for r in RHO_SWEEP if r != w.rho])
+    sweep = bench_rho_sweep(args, dev, w, t, e_scores, [r for r in RHO_SWEEP if r != w.rho]) \
+        if want(args, "sweep") else None
     plan = ham.ForwardPlan(w.B, w.T, w.H, w.d, w.d, dt, dev, scale=w.attn_scale)
     t_start = time.perf_counter()
     ms, stages = time_steps(lambda: plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau),
@@ -331,26 +339,32 @@ def bench_forward(args, dev):
                           ms_per_step=round(ms, 4), tokens_per_s=round(w.B * w.T / (ms / 1e3), 1),
                           visible_pairs=pairs, stages=[rounded(x) for x in per], note="the headline run"))
     router = rope = packed = blocks = kvh = paper = bwd = rbwd = None
-    if not args.main_only:
-        from attention_sequence_mixing_amd.inputs import make_doc_start
+    from attention_sequence_mixing_amd.inputs import make_doc_start, make_inputs_torch
+    if want(args, "router"):
         router = bench_router(args, dev, w, t)
+    if want(args, "rope"):
         rope = bench_variant(args, dev, w, t, tau, "rope500000", rope_base=500000.0)
+    if want(args, "packed"):
         packed = bench_variant(args, dev, w, t, tau, "packed_docs_mean1024_rope500000",
                                rope_base=500000.0, doc_start=make_doc_start(w.B, w.T, 1024, w.seed))
+    if want(args, "blocks"):
         # block-contiguous routing: 64-token blocks, tau per head for half of the
         # blocks on their mean score
         nb = 64
         means = st["e"].view(w.B, w.T // nb, nb, w.H).mean(dim=2).contiguous()
         tau_b = ham.ham_select_tau(means, w.rho)
         blocks = bench_variant(args, dev, w, t, tau_b, f"block_routing{nb}", route_block=nb)
+    if want(args, "kv_heads"):
         # the paper's head layout at the kernels' sizes: twice the RNN heads as KV heads,
         # key size 128, value size half the RNN's (their outputs tile the RNN heads')
-        from attention_sequence_mixing_amd.inputs import make_inputs_torch
         att = make_inputs_torch(w.B, w.T, 2 * w.H, w.d, w.d // 2, dtype="bf16", seed=w.seed + 3,
                                 device=dev)
         kvh = bench_variant(args, dev, w, t, tau, f"kv_heads{2 * w.H}_dk{w.d}_dv{w.d // 2}", attn=att)
+    if want(args, "paper"):
         paper = bench_paper_heads(args, dev, w)
+    if want(args, "backward"):
         bwd = bench_backward(args, dev, w, t, plan, pairs)
+    if want(args, "rnn_backward"):
         rbwd = bench_rnn_backward(args, dev, w, t)
     return dict(w=w, ms=ms, wall=wall, tokens_per_s=w.B * w.T / (ms / 1e3), stages=per, dom=dom,
                 rho=rho, pairs=pairs, tau=tau_np, inp=inp, rnn_flops=rnn_flops, att_flops=att_flops,
@@ -750,7 +764,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--main-only", action="store_true",
-                    help="only the layer forward (no learned-router, RoPE or packed-document legs)")
+                    help="only the layer forward (no other leg; same as --legs none)")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs to run besides the layer forward and decode: "
+                         + ",".join(LEGS) + " (or all, none)")
     ap.add_argument("--decode-prefix", type=int, default=0)
     ap.add_argument("--cpu-batch", type=int, default=8,
                     help="sequences of the layer workload the CPU oracle baseline runs")
@@ -758,6 +775,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    legs = set(LEGS) if args.legs == "all" else set() if args.legs == "none" else set(args.legs.split(","))
+    unknown = legs - set(LEGS)
+    if unknown:
+        ap.error("unknown legs: " + ",".join(sorted(unknown)))
+    args.leg_set = set() if args.main_only else legs
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the HAM layer on a single MI355X "
               "(heads shard across GPUs without communication; see the design notes).", file=sys.stderr)
@@ -770,12 +792,12 @@ def main():
     info = device_info(dev)
     info["stream_copy_GBps"] = round(stream_copy_gbs(dev), 1)
     log(f"[bench] device {info}")
-    small = None if args.main_only else bench_small(args, dev)
+    small = bench_small(args, dev) if want(args, "small") else None
     res = bench_forward(args, dev)
     for s in res["stages"]:
         log(f"[bench] stage {s['stage']:10s} {s['ms']:8.3f} ms  {s['achieved']:9.1f} {s['unit']} "
             f"({100 * s['frac']:.1f}% of {s['peak']})")
-    long_ctx = None if args.main_only else bench_long(args, dev)
+    long_ctx = bench_long(args, dev) if want(args, "long") else None
     dec = None
     if not args.no_decode:
         dec = bench_decode(args, dev)
