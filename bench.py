@@ -482,11 +482,14 @@ def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     tflops = pairs * 10 * w.d / (ms / 1e3) / 1e12
+    tq, tkv = measured_traffic("attn_bwd_q"), measured_traffic("attn_bwd_kv")
+    traffic = None if tq is None or tkv is None else tq + tkv      # HBM bytes of the two kernels
     log(f"[bench] attention backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of the bf16 MFMA peak)")
     return dict(workload=f"{w.name}_attention_backward", ms_per_step=round(ms, 4), steps=steps,
                 warmup=warmup, roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS,
-                                             unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4)))
+                                             unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4),
+                                             traffic=traffic))
 
 
 def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):
@@ -519,7 +522,8 @@ def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):
         f"({100 * tflops / PEAK_FP32_VALU_TFLOPS:.1f}% of the fp32 VALU peak without packed instructions)")
     return dict(workload=f"{w.name}_rnn_backward", ms_per_step=round(ms, 4), steps=steps, warmup=warmup,
                 roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
-                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4)))
+                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4),
+                              traffic=measured_traffic("rnn_bwd")))
 
 
 def bench_long(args, dev, steps=10, warmup=10):
@@ -688,6 +692,7 @@ def bench_decode(args, dev):
     roof = dict(stage="decode_attention", ms=float(stg[3]), bound="hbm", unit="GB/s",
                 achieved=cache_bytes / attn_sec / 1e9, peak=PEAK_HBM_GBS)
     roof["frac"] = roof["achieved"] / PEAK_HBM_GBS
+    roof["traffic"] = measured_traffic("decode_attention")
     return dict(us_per_step=us, tokens_per_s=B / (us / 1e6), steps=steps, prefix=T0, sampled=pre_host,
                 sample_heads=sample, B=B, H=H, d=d,
                 cache_keys_mean=mean_keys, step_bytes=cache_bytes + state_bytes,
