@@ -193,23 +193,29 @@ def collect_stages(lib, n):
 
 def time_steps(step, steps, warmup):
     """Run warmup untimed steps, then time exactly `steps` steps between two events
-    on torch's current stream (the launch stream); the library records per-kernel
-    HIP events on that stream during the timed steps.  Returns (ms per step, stage
+    on torch's current stream (the launch stream), with nothing else recorded; then
+    run `steps` more with the library recording HIP events on that stream around each
+    kernel, for the per-stage times (those events add about 20 us to a step at the
+    layer shape, so they stay out of the timed steps).  Returns (ms per step, stage
     times in ms)."""
     import torch
     from attention_sequence_mixing_amd import _lib
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    lib = _lib.lib()
-    lib.ham_profile_start(steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, collect_stages(lib, steps)
+    ms = e0.elapsed_time(e1) / steps
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return ms, collect_stages(lib, steps)
 
 
 def visible_pairs(routed):
@@ -380,7 +386,6 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, ro
     heads of their own geometry (attn: dict q, k, v of the attention path)."""
     import torch
     import attention_sequence_mixing_amd as ham
-    from attention_sequence_mixing_amd import _lib
     kv = {} if attn is None else dict(kv_heads=attn["q"].shape[2], dk_kv=attn["q"].shape[3],
                                       dv_kv=attn["v"].shape[3])
     scale = w.attn_scale if attn is None else attn["q"].shape[3] ** -0.5
@@ -393,19 +398,7 @@ def bench_variant(args, dev, w, t, tau, label, rope_base=0.0, doc_start=None, ro
         plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, doc_start=ds, q_attn=qa, k_attn=ka,
              v_attn=va)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    lib = _lib.lib()
-    lib.ham_profile_start(args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    stages = collect_stages(lib, args.steps)
+    ms, stages = time_steps(step, args.steps, args.warmup)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
     rho = float(plan.count.sum().item()) / (w.B * w.T * plan.count.shape[1])
     log(f"[bench] {label}: {ms:.3f} ms/step, rho {rho:.4f}, "
@@ -422,7 +415,6 @@ def bench_paper_heads(args, dev, w, steps=5, warmup=5):
     kernel (the chunked state kernel takes d_k <= 128), so this measures that path."""
     import torch
     import attention_sequence_mixing_amd as ham
-    from attention_sequence_mixing_amd import _lib
     from attention_sequence_mixing_amd.inputs import make_inputs_torch
     H, dk, dv, HK, dkk, dvk = 5, 256, 384, 10, 128, 192
     t = make_inputs_torch(w.B, w.T, H, dk, dv, dtype="bf16", seed=w.seed + 5, device=dev)
@@ -437,19 +429,7 @@ def bench_paper_heads(args, dev, w, steps=5, warmup=5):
         plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, q_attn=att["q"], k_attn=att["k"],
              v_attn=att["v"])
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    lib = _lib.lib()
-    lib.ham_profile_start(steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    stages = collect_stages(lib, steps)
+    ms, stages = time_steps(step, steps, warmup)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
     rho = float(plan.count.sum().item()) / (w.B * w.T * HK)
     label = f"paper_heads_bf16_B{w.B}_T{w.T}_rnn{H}x{dk}x{dv}_kv{HK}x{dkk}x{dvk}"
@@ -531,7 +511,6 @@ def bench_long(args, dev, steps=10, warmup=10):
     heads the chunked state pass runs in segments side by side."""
     import torch
     import attention_sequence_mixing_amd as ham
-    from attention_sequence_mixing_amd import _lib
     from attention_sequence_mixing_amd.inputs import LONG, make_workload, tau_for_rho
     w = LONG
     inp = make_workload(w)
@@ -546,19 +525,7 @@ def bench_long(args, dev, steps=10, warmup=10):
     def step():
         plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    lib = _lib.lib()
-    lib.ham_profile_start(steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    stages = collect_stages(lib, steps)
+    ms, stages = time_steps(step, steps, warmup)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
     rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
     log(f"[bench] long context: {ms:.3f} ms/step, stages {dict(zip(names, [round(x, 4) for x in stages]))}")
@@ -573,7 +540,6 @@ def bench_router(args, dev, w, t):
     fraction comes from ham_select_tau on the GPU."""
     import torch
     import attention_sequence_mixing_amd as ham
-    from attention_sequence_mixing_amd import _lib
     from attention_sequence_mixing_amd.inputs import make_router_scores
     rs = torch.from_numpy(make_router_scores(w.B, w.T, w.H, w.seed)).to(dev)
     tau = ham.ham_select_tau(rs, w.rho)
@@ -591,18 +557,7 @@ def bench_router(args, dev, w, t):
     def step():
         plan(t["q"], t["k"], t["v"], t["beta"], t["g"], tau, router_scores=rs)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    lib = _lib.lib()
-    lib.ham_profile_start(args.steps)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    stages = collect_stages(lib, args.steps)
+    ms, stages = time_steps(step, args.steps, args.warmup)
     rho = float(plan.count.sum().item()) / (w.B * w.T * w.H)
     names = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
     log(f"[bench] learned router: {ms:.3f} ms/step, select_tau {sel_us:.1f} us, rho {rho:.4f}, "
@@ -675,16 +630,19 @@ def bench_decode(args, dev):
     torch.cuda.synchronize()
     pre_host["o_gpu"] = torch.stack(o_sampled, 1).cpu().numpy()      # [4, steps, d]
     S.copy_(S0); count.copy_(count0)
-    lib = _lib.lib()
-    lib.ham_profile_start(steps)            # per-kernel HIP events on the timed steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    run_all()
+    run_all()                               # the timed pass: nothing else recorded
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    stg = collect_stages(lib, steps)
     cache_keys1 = float(count.sum().item())
+    S.copy_(S0); count.copy_(count0)
+    lib = _lib.lib()
+    lib.ham_profile_start(steps)            # per-kernel HIP events on a second pass over the same steps
+    run_all()
+    torch.cuda.synchronize()
+    stg = collect_stages(lib, steps)
     mean_keys = 0.5 * (cache_keys0 + cache_keys1)
     cache_bytes = mean_keys * 2 * d * 2                     # K and V rows, bf16
     state_bytes = B * H * d * d * 4 * 2                     # S read + write
