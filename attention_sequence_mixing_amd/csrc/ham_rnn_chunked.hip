@@ -249,17 +249,27 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const size_t tok0 = ((size_t)b * a.T + t0) * a.H + h;
 
-  // stage K and Q rows (16-byte units, token-major), zero past T
-  for (int u = tid; u < kC * (DK / 8); u += 256) {
-    const int row = u % kC, cu = (u / kC) * 8;
-    u16x8 kx = (u16x8)(0), qx = (u16x8)(0);
+  // stage K and Q rows (16-byte units, token-major), zero past T: every load of the
+  // thread is issued before the first LDS store, so the tile costs one memory latency
+  constexpr int NU = kC * (DK / 8) / 256;
+  static_assert(kC * (DK / 8) % 256 == 0, "staging units must split evenly over the threads");
+  u16x8 kx[NU], qx[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = tid + 256 * i, row = u % kC, cu = (u / kC) * 8;
+    kx[i] = (u16x8)(0);
+    qx[i] = (u16x8)(0);
     if (row < nvalid) {
       const size_t off = (tok0 + (size_t)row * a.H) * DK + cu;
-      kx = *reinterpret_cast<const u16x8*>(kp + off);
-      if (readout) qx = *reinterpret_cast<const u16x8*>(qp + off);
+      kx[i] = *reinterpret_cast<const u16x8*>(kp + off);
+      if (readout) qx[i] = *reinterpret_cast<const u16x8*>(qp + off);
     }
-    *reinterpret_cast<u16x8*>(&sm.K[SM::at(row, cu >> 3)]) = kx;
-    *reinterpret_cast<u16x8*>(&sm.Q[SM::at(row, cu >> 3)]) = qx;
+  }
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = tid + 256 * i, row = u % kC, cu = (u / kC) * 8;
+    *reinterpret_cast<u16x8*>(&sm.K[SM::at(row, cu >> 3)]) = kx[i];
+    *reinterpret_cast<u16x8*>(&sm.Q[SM::at(row, cu >> 3)]) = qx[i];
   }
   if (wave == 0) {
     float gv = 0.f, bv = 0.f;
