@@ -561,7 +561,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     it0 = __builtin_amdgcn_readfirstlane(mn / BN);
     lmax = __builtin_amdgcn_readfirstlane(mx);
   }
-  __builtin_amdgcn_s_waitcnt(0);                          // query fragments are in
+  // The first tile's loads go out while the query fragments are still in flight (the
+  // compiler waits for those registers where they are first used; every step waits
+  // for all memory before it reads the stage).
   if (it0 < ntiles) issue_tile(it0, stage0);
 
   f32x4 st[QT][NKT];
