@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
 times, against the CPU oracle on everything it can afford: every routing score,
 routing decision, compaction entry and final state of every head (RNN-only oracle
-pass), and the attention outputs at sampled tokens of sampled heads.
+pass), and the attention outputs at sampled tokens of sampled heads -- at the
+headline layer at rho = 0.5, every output element of every head.
 
 Workloads: the layer at the 800M-model shape (B=8, H=16, d=128, T=4096, bf16 I/O,
 rho = 0.5 and the two rho limits; rho = 0.5 with RoPE base 500K; rho = 0.5 over packed
@@ -119,6 +120,32 @@ def test_layer_fullsize(rho):
     worst = _check_sampled_outputs(out, inp, tau, scale, [(0, 0), (3, 7), (7, 15)], 24,
                                    torch.bfloat16, 40, r_gpu)
     print(f"layer rho={rho}: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
+
+
+def test_layer_fullsize_every_output():
+    """The headline layer (B=8, H=16, T=4096, d=128, bf16, rho = 0.5) with every
+    output element compared: the oracle's full forward (all heads, all tokens) runs
+    with the GPU's routing mask, so near-threshold flips do not matter, and o, o_rnn
+    and o_kv of every (b, h) slice must meet the bf16 tolerance; the scores, cache
+    and state are checked for every head as above."""
+    w = LAYER
+    inp = make_workload(w)
+    scale = w.attn_scale
+    base = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(base["e"], 0.5)
+    ref_rnn = _rnn_only_oracle(inp, tau, scale)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    nflip, de = _check_all_heads(out, ref_rnn, tau)
+    r_gpu = out["routed"].cpu().numpy()
+    ref = oracle.forward(**inp, tau=tau, scale=scale, mask_override=r_gpu)
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"layer, every output: max|de|={de:.2e} near-band flips={nflip} worst slice errors {worst}")
 
 
 def test_layer_fullsize_rope():
