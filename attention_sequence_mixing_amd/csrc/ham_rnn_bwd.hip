@@ -19,7 +19,9 @@
 // needed in reverse order: a first pass runs the recurrence forward and stores the
 // state at every 64-token chunk start; then, chunk by chunk from the end, the chunk's
 // states are recomputed from its checkpoint into a per-wave scratch and the reverse
-// recurrence walks back through them.  fp32 throughout.
+// recurrence walks back through them.  Each token's inputs (and, walking back, its
+// stored state) are loaded while the previous token is processed, so a token waits on
+// its arithmetic and the barrier rather than on memory.  fp32 throughout.
 #include "ham_common.h"
 #include "ham_internal.h"
 
@@ -93,24 +95,36 @@ __global__ __launch_bounds__(64 * (DV / kCols)) void rnn_bwd_kernel(RnnBwdArgs a
   float* st = a.states + (size_t)(bh * NW + wave) * kC * SLAB;
 
   auto tok_of = [&](int t) { return ((size_t)b * a.T + t) * a.H + h; };
-  // this lane's rows of k_t (and q_t), and the wave's 16 columns of a row vector as
-  // uniform values (lanes 0..15 load, then every lane reads them)
-  auto load_rows = [&](const E* p, int t, float (&out)[R]) {
-#pragma unroll
-    for (int m = 0; m < R; ++m) out[m] = IO::load(p, tok_of(t) * DK + lane + 64 * m);
+  // One token's inputs as loaded: this lane's rows of k_t and q_t, lane j < 16 holding
+  // column j of the wave's v_t and dO_t (spread to every lane where they are used), g, beta.
+  struct TokIn {
+    float kr[R], qr[R], vx, dox, g, beta;
   };
-  auto load_cols = [&](int t, float (&vj)[kCols]) {
-    const float x = lane < kCols ? IO::load(vp, tok_of(t) * DV + c0 + lane) : 0.f;
+  auto load_in = [&](int t, bool with_q) {
+    TokIn in;
+    const size_t tok = tok_of(t);
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+      in.kr[m] = IO::load(kp, tok * DK + lane + 64 * m);
+      in.qr[m] = with_q ? IO::load(qp, tok * DK + lane + 64 * m) : 0.f;
+    }
+    in.vx = lane < kCols ? IO::load(vp, tok * DV + c0 + lane) : 0.f;
+    in.dox = (with_q && lane < kCols) ? a.dO[tok * DV + c0 + lane] : 0.f;
+    in.g = a.g[tok];
+    in.beta = a.beta[tok];
+    return in;
+  };
+  auto spread = [&](float x, float (&out)[kCols]) {
 #pragma unroll
     for (int j = 0; j < kCols; ++j)
-      vj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
+      out[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
   };
   // one forward step S <- alpha S + beta k (v - alpha S^T k)^T on the slab
-  auto forward_step = [&](Slab<R>& S, int t) {
-    float kr[R], vj[kCols], x[kCols], p[kCols];
-    load_rows(kp, t, kr);
-    load_cols(t, vj);
-    const float alpha = expf(a.g[tok_of(t)]), beta = a.beta[tok_of(t)];
+  auto forward_step = [&](Slab<R>& S, const TokIn& in) {
+    float vj[kCols], x[kCols], p[kCols];
+    const float* kr = in.kr;
+    spread(in.vx, vj);
+    const float alpha = expf(in.g), beta = in.beta;
 #pragma unroll
     for (int j = 0; j < kCols; ++j) {
       float acc = 0.f;
@@ -134,9 +148,14 @@ __global__ __launch_bounds__(64 * (DV / kCols)) void rnn_bwd_kernel(RnnBwdArgs a
 #pragma unroll
     for (int j = 0; j < kCols; ++j)
       S.x[m][j] = a.S0 ? a.S0[(size_t)bh * DK * DV + (size_t)(lane + 64 * m) * DV + c0 + j] : 0.f;
-  for (int t = 0; t < a.T; ++t) {
-    if (t % kC == 0) slab_store(ck + (size_t)(t / kC) * SLAB, S);
-    forward_step(S, t);
+  {
+    TokIn cur = load_in(0, false);
+    for (int t = 0; t < a.T; ++t) {
+      const TokIn nxt = load_in(t + 1 < a.T ? t + 1 : t, false);
+      if (t % kC == 0) slab_store(ck + (size_t)(t / kC) * SLAB, S);
+      forward_step(S, cur);
+      cur = nxt;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);              // the checkpoints are in memory before they are read
 
@@ -151,26 +170,34 @@ __global__ __launch_bounds__(64 * (DV / kCols)) void rnn_bwd_kernel(RnnBwdArgs a
   for (int c = nchunk - 1; c >= 0; --c) {
     const int t0 = c * kC, t1 = min(a.T, t0 + kC);
     slab_load(ck + (size_t)c * SLAB, S);
-    for (int t = t0; t < t1; ++t) {
-      slab_store(st + (size_t)(t - t0) * SLAB, S);        // S_{t-1} of token t
-      forward_step(S, t);
+    {
+      TokIn cur = load_in(t0, false);
+      for (int t = t0; t < t1; ++t) {
+        const TokIn nxt = load_in(t + 1 < t1 ? t + 1 : t, false);
+        slab_store(st + (size_t)(t - t0) * SLAB, S);      // S_{t-1} of token t
+        forward_step(S, cur);
+        cur = nxt;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);            // the chunk's states are in memory before they are read
+    Slab<R> Sn;                               // S_{t-1} of the next token walked (t - 1)
+    slab_load(st + (size_t)(t1 - 1 - t0) * SLAB, Sn);
+    TokIn nin = load_in(t1 - 1, true);
     for (int t = t1 - 1; t >= t0; --t) {
       const int buf = t & 1;
       const size_t tok = tok_of(t);
-      slab_load(st + (size_t)(t - t0) * SLAB, S);         // S_{t-1}
-      float kr[R], qr[R], vj[kCols], dOj[kCols];
-      load_rows(kp, t, kr);
-      load_rows(qp, t, qr);
-      load_cols(t, vj);
-      {
-        const float x = lane < kCols ? a.dO[tok * DV + c0 + lane] : 0.f;
-#pragma unroll
-        for (int j = 0; j < kCols; ++j)
-          dOj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
+      S = Sn;                                 // S_{t-1}
+      const TokIn in = nin;
+      if (t > t0) {
+        slab_load(st + (size_t)(t - 1 - t0) * SLAB, Sn);
+        nin = load_in(t - 1, true);
       }
-      const float alpha = expf(a.g[tok]), beta = a.beta[tok];
+      const float* kr = in.kr;
+      const float* qr = in.qr;
+      float vj[kCols], dOj[kCols];
+      spread(in.vx, vj);
+      spread(in.dox, dOj);
+      const float alpha = expf(in.g), beta = in.beta;
       // G += q dO^T  (G is now dL/dS_t)
 #pragma unroll
       for (int m = 0; m < R; ++m)
