@@ -319,7 +319,11 @@ __global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnBwdArgs a) {
 //
 // Tiles come into LDS by direct buffer-to-LDS loads, double-buffered: after the barrier
 // that publishes tile i, the loads of the next tile are issued into the other buffer
-// and tile i is multiplied.  Rows are unpadded and the 16-byte chunk c of row r sits at
+// and tile i is multiplied.  The two buffers are separate LDS objects and the tile loops
+// are unrolled by two, so that every LDS access names its buffer statically: the
+// compiler waits on the loads in flight into one buffer only before reads of that one
+// (with one array indexed at run time it waited on them before every read, and loads
+// never overlapped the products).  Rows are unpadded and the 16-byte chunk c of row r sits at
 // slot c ^ f(r).  The LDS has 64 four-byte banks; a 16-byte read serves 16 consecutive
 // lanes a pass, an 8-byte read 32, and (measured with the bank-conflict counter on
 // probe patterns) the bank of a 16-byte read has its bit 2 flipped by address bit 11,
@@ -418,7 +422,8 @@ __global__ __launch_bounds__(NTH) void attn_bwd_q_mfma(AttnBwdArgs a) {
   constexpr int KSD = DK / 32, VSD = DV / 32, DT = DK / 16;
   constexpr int KB = BT * DK * 2, STAGE = KB + BT * DV * 2;
   constexpr int NKI = DK / 64, NVI = DV / 64;              // direct loads per wave and tile
-  __shared__ __attribute__((aligned(1024))) char smem[2][STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ int s_rng[2][NW];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -494,18 +499,21 @@ __global__ __launch_bounds__(NTH) void attn_bwd_q_mfma(AttnBwdArgs a) {
     for (int k = 0; k < NVI; ++k)
       buffer_to_lds(Vh + (size_t)c0 * DV * 2, rows * DV * 2, voV[k], st + KB + (k * NW + wave) * 1024);
   };
-  // Walks the entry tiles [cfirst, cmax), calling body(c0, K, V) on each.
+  // Walks the entry tiles [cfirst, cmax), calling body(c0, K, V) on each: wait for the
+  // tile's loads, publish it, send the next tile's loads to the other buffer, multiply.
   auto walk = [&](auto&& body) {
     if (cmax <= cfirst) return;
     __syncthreads();                                       // both buffers are free
-    issue(cfirst, smem[0]);
-    int buf = 0;
-    for (int c0 = cfirst; c0 < cmax; c0 += BT) {
+    issue(cfirst, stage0);
+    auto step = [&](int c0, char* cur, char* nxt) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (c0 + BT < cmax) issue(c0 + BT, smem[buf ^ 1]);
-      body(c0, reinterpret_cast<const uint16_t*>(smem[buf]), reinterpret_cast<const uint16_t*>(smem[buf] + KB));
-      buf ^= 1;
+      if (c0 + BT < cmax) issue(c0 + BT, nxt);
+      body(c0, reinterpret_cast<const uint16_t*>(cur), reinterpret_cast<const uint16_t*>(cur + KB));
+    };
+    for (int c0 = cfirst; c0 < cmax; c0 += 2 * BT) {
+      step(c0, stage0, stage1);
+      if (c0 + BT < cmax) step(c0 + BT, stage1, stage0);
     }
   };
 
@@ -615,7 +623,8 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   constexpr int QBY = BT * DK * 2, GBY = BT * DV * 2, SBY = BT * 32;
   constexpr int STAGE = QBY + 2 * GBY + SBY;
   constexpr int NQI = DK / 64, NGI = DV / 64;              // direct loads per wave and tile
-  __shared__ __attribute__((aligned(1024))) char smem[2][STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ uint32_t s_mask[kMaskWords];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   // visibility of the query tiles j0.. (tile j0 holds the query at the first entry's
   // position, the first that may see the block), from the query kernel's tile ranges
   const long long p0 = (long long)ph[cb] - (long long)a.t0;
-  const int j0 = (int)(max(0LL, min((long long)a.T, p0)) / BT);
+  const int j0 = uniform((int)(max(0LL, min((long long)a.T, p0)) / BT));
   const int nt = nq64 - j0;
   for (int base = 0; base < nt; base += NTH) {
     bool vis = false;
@@ -698,18 +707,17 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DTV; ++i) dv[i] = (f32x4)(0.f);
 
-  int jt = next_vis(0);
-  if (jt < nt) issue(jt, smem[0]);
-  int buf = 0;
-  while (jt < nt) {
+  // one visible tile: wait for its loads, publish it, send the next visible tile's
+  // loads to the other buffer, multiply; returns that next tile
+  auto step = [&](int jt, char* cur, char* nxt) {
     const int jn = next_vis(jt + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (jn < nt) issue(jn, smem[buf ^ 1]);
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(smem[buf]);
-    const uint16_t* Gh = reinterpret_cast<const uint16_t*>(smem[buf] + QBY);
-    const uint16_t* Gl = reinterpret_cast<const uint16_t*>(smem[buf] + QBY + GBY);
-    const char* S = smem[buf] + QBY + 2 * GBY;
+    if (jn < nt) issue(jn, nxt);
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(cur);
+    const uint16_t* Gh = reinterpret_cast<const uint16_t*>(cur + QBY);
+    const uint16_t* Gl = reinterpret_cast<const uint16_t*>(cur + QBY + GBY);
+    const char* S = cur + QBY + 2 * GBY;
     f32x4 sc[4], dpt[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -758,8 +766,14 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
         dk[dt] = mma(aq, dl, dk[dt]);
       }
     }
-    buf ^= 1;
-    jt = jn;
+    return jn;
+  };
+  int jt = next_vis(0);
+  if (jt < nt) issue(jt, stage0);
+  while (jt < nt) {
+    jt = step(jt, stage0, stage1);
+    if (jt >= nt) break;
+    jt = step(jt, stage1, stage0);
   }
   if (cv) {
     const size_t row = (size_t)bh * a.cap + c;
