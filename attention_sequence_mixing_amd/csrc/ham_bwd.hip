@@ -425,7 +425,7 @@ __global__ __launch_bounds__(NTH) void attn_bwd_q_mfma(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ int s_rng[2][NW];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int bh = blockIdx.x, qb = gridDim.y - 1 - blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ uint32_t s_mask[kMaskWords];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int bh = blockIdx.x, cb = blockIdx.y * (NW * 16);
   const int b = bh / a.H, h = bh % a.H;
@@ -740,7 +740,7 @@ __global__ __launch_bounds__(NTH) void attn_bwd_kv_mfma(AttnBwdArgs a) {
         const int r = 16 * qt + 4 * g + i;
         const f32x4 sv = *reinterpret_cast<const f32x4*>(S + r * 32);
         const int2 rg = *reinterpret_cast<const int2*>(S + r * 32 + 16);
-        const bool vis = cv && c >= rg.x && c < rg.y;
+        const bool vis = cv & (c >= rg.x) & (c < rg.y);     // no branch per row
         const float e = __builtin_amdgcn_exp2f(sc[qt][i] * sl2 - sv[0]) * sv[1];
         const float p = vis ? e : 0.f;
         P[qt][i] = p;
