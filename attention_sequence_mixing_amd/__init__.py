@@ -405,11 +405,13 @@ def ham_attention_backward(q_attn, cache, dO, *, scale=None, t0=0, doc_start=Non
     return dict(dq=dq, dKc=dKc, dVc=dVc)
 
 
-def ham_rnn_backward(q, k, v, beta, g, dO, *, S0=None, dS_T=None, stream=None):
+def ham_rnn_backward(q, k, v, beta, g, dO, *, S0=None, dS_T=None, force_recurrent=False, stream=None):
     """Gradients of the gated delta-rule RNN for training: q, k [B,T,H,dk], v [B,T,H,dv]
     (float32 or bfloat16), beta, g [B,T,H] float32 (the forward's inputs), S0 the
     forward's entering state or None, dO = dL/do_rnn [B,T,H,dv] float32, dS_T = dL/dS_T
-    [B,H,dk,dv] or None.  Returns dict(dq, dk, dv, dbeta, dg, dS0) in float32."""
+    [B,H,dk,dv] or None.  The chunked form runs unless force_recurrent asks for the
+    token-serial reverse (HAM_FORCE_RECURRENT).  Returns dict(dq, dk, dv, dbeta, dg, dS0)
+    in float32."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -420,7 +422,8 @@ def ham_rnn_backward(q, k, v, beta, g, dO, *, S0=None, dS_T=None, stream=None):
     _need("dO", dO, (B, T, H, dv), torch.float32, dev)
     _need("S0", S0, (B, H, dk, dv), torch.float32, dev)
     _need("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
-    dims = make_dims(B, T, H, dk, dv, _io_code(dt), 1.0, 1e-6, max(T, 1))
+    dims = make_dims(B, T, H, dk, dv, _io_code(dt), 1.0, 1e-6, max(T, 1),
+                     flags=HAM_FORCE_RECURRENT if force_recurrent else 0)
     L = _lib.lib()
     ws_bytes = L.ham_rnn_backward_workspace_size(ctypes.byref(dims))
     if ws_bytes == 0:

@@ -419,6 +419,8 @@ size_t ham_rnn_backward_workspace_size(const ham_dims* d) {
     fail(HAM_EUNSUPPORTED, "ham_rnn_backward: dk and dv must be 64 or 128 (dk=%d dv=%d)", d->dk, d->dv);
     return 0;
   }
+  if (!(d->flags & HAM_FORCE_RECURRENT))
+    return up256(ham::rnn_backward_chunked_scratch_floats(d->B, d->H, d->T, d->dk, d->dv) * sizeof(float));
   const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
   const size_t total = ham::rnn_backward_scratch_floats(d->B, d->H, d->T, d->dk, d->dv);
   const size_t ck = total / (nchunk + ham::kChunk) * nchunk;      // the checkpoints come first
@@ -440,6 +442,12 @@ int ham_rnn_backward(const ham_dims* d, const void* q, const void* k, const void
   const size_t need = ham_rnn_backward_workspace_size(d);
   if (!ws || ws_bytes < need)
     return fail(HAM_EWORKSPACE, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  if (!(d->flags & HAM_FORCE_RECURRENT)) {
+    ham::RnnBwdArgs a{q, k, v, beta, g, S0, dO, dS_T, dq, dk, dv, dbeta, dg, dS0, nullptr, nullptr,
+                      d->B, d->T, d->H, static_cast<float*>(ws)};
+    HAM_HIP(ham::launch_rnn_backward_chunked(d->io_dtype, d->dk, d->dv, a, static_cast<hipStream_t>(stream)));
+    return HAM_OK;
+  }
   const size_t nchunk = ((size_t)d->T + ham::kChunk - 1) / ham::kChunk;
   const size_t total = ham::rnn_backward_scratch_floats(d->B, d->H, d->T, d->dk, d->dv);
   const size_t ck = total / (nchunk + ham::kChunk) * nchunk;

@@ -237,13 +237,16 @@ struct RnnBwdArgs {
   float* dbeta;         // [B,T,H]
   float* dg;
   float* dS0;           // [B,H,dk,dv]
-  float* ckpt;          // scratch: per wave, the state slab at every chunk start
-  float* states;        // scratch: per wave, the states of one chunk
+  float* ckpt;          // token-serial reverse, scratch: per wave, the state slab at every chunk start
+  float* states;        // token-serial reverse, scratch: per wave, the states of one chunk
   int B, T, H;
+  float* scratch;       // chunked reverse: its scratch (rnn_backward_chunked_scratch_floats)
 };
 size_t rnn_backward_scratch_floats(int B, int H, int T, int dk, int dv);
 bool rnn_backward_supported(int dk, int dv);
 hipError_t launch_rnn_backward(int io, int dk, int dv, const RnnBwdArgs& a, hipStream_t s);
+size_t rnn_backward_chunked_scratch_floats(int B, int H, int T, int dk, int dv);
+hipError_t launch_rnn_backward_chunked(int io, int dk, int dv, const RnnBwdArgs& a, hipStream_t s);
 
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_attention_backward(int io, int dk, int dv, const AttnBwdArgs& a, hipStream_t s);

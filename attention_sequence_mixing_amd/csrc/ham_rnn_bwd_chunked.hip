@@ -1,0 +1,662 @@
+// ham_rnn_bwd_chunked.hip -- chunked gradients of the gated delta-rule RNN (training).
+//
+// "Hybrid Associative Memories" App. A.1: the chunked kernel of the RNN memory serves
+// the backward pass as well.  Per head, the forward recurrence (§2 DeltaNet update and
+// linear-attention readout, App. A.1 gated decay) over one 64-token chunk with entering
+// state S, cumulative log decay G_t inside the chunk, gamma_t = e^{G_t},
+// gamma_C = e^{G_last}, w_t = e^{G_last - G_t}, Gamma_ts = e^{G_t - G_s}, reads
+//   X = V - diag(gamma) K S,   (I + diag(beta) A) D = diag(beta) X,
+//   S_C = gamma_C S + K^T diag(w) D,   O = diag(gamma) Q S + M D,
+// with A = strict_lower(Gamma o K K^T) and M = lower(Gamma o Q K^T) (diagonal kept):
+// the residual form of the UT transform that the forward state pass also uses.  Its
+// reverse mode, given dO and dS_C = dL/dS_C, is
+//   dD = M^T dO + diag(w) K dS_C,   dX = T'^T dD  (T' = (I + diag(beta) A)^-1 diag(beta)),
+//   U = dD - A^T dX,   R = X - A D,   dV = dX,   dbeta_t = U_t . R_t,
+//   dS = gamma_C dS_C - K^T diag(gamma) dX + Q^T diag(gamma) dO      (entering state),
+//   dM = lower(dO D^T),   dA = -strict_lower(dX D^T),
+//   dQ = diag(gamma) dO S^T + (dM o Gamma) K,
+//   dK = -diag(gamma) dX S^T + diag(w) D dS_C^T + (dM o Gamma)^T Q + (dA o Gamma) K
+//        + (dA o Gamma)^T K,
+//   dG_t = gamma_t sum_j (dO o QS - dX o KS)_tj - w_t sum_j (K dS_C o D)_tj
+//          + sum_s (dM o M + dA o A)_ts - sum_s (dM o M + dA o A)_st,
+//   and the chunk's last token's G also takes gamma_C <S, dS_C> + sum_t w_t (K dS_C o D)_t;
+//   dg_j = sum_{t >= j} dG_t  (G is the running sum of g inside the chunk).
+// Chunks beyond the sequence's end are padded with zero rows, beta = g = 0, which leaves
+// every quantity of the real tokens unchanged.
+//
+// Five kernels, fp32 throughout (products on the fp32 matrix cores, 16x16x4):
+//   cbwd_prep   chunk-parallel: G, A, M, T' per chunk (T' by forward substitution);
+//   cbwd_fwd    sequential over chunks: the entering state of every chunk and D;
+//   cbwd_rev    sequential over chunks, from the end: dS_C of every chunk and dS0;
+//   cbwd_cols   chunk-parallel, 16 value columns per wave: dV, dX and the per-token
+//               partial sums of dbeta, dgamma, dw over those columns;
+//   cbwd_final  chunk-parallel: dM, dA, dQ, dK, dG, dg, dbeta.
+// The state chains keep S (or dS) in matrix-core accumulators, 16 value columns per
+// wave; a product whose contraction index is held by an accumulator takes it in the
+// accumulator's own order (row 16i + 4(lane/16) + r in element r of tile i), and its
+// other operand is read from LDS in that order.
+#include "ham_common.h"
+#include "ham_internal.h"
+
+namespace ham {
+namespace cbwd {
+
+constexpr int kC = 64;          // tokens per chunk
+constexpr int LP = 4;           // LDS row padding (floats)
+constexpr int RW = kC + LP;     // LDS row length of a 64-wide matrix
+
+HAM_DEVICE f32x4 mf(float a, float b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+
+// Scratch regions (floats), each 64-float aligned; see chunk_scratch_floats().
+struct Scratch {
+  size_t G, A, M, T, S, dS, D, dX, part, total;
+};
+__host__ __device__ inline Scratch scratch_layout(int B, int H, int T, int DK, int DV) {
+  auto up = [](size_t x) { return (x + 63) / 64 * 64; };
+  const size_t N = (size_t)(T + kC - 1) / kC, BHN = (size_t)B * H * N;
+  Scratch s{};
+  size_t o = 0;
+  s.G = o;    o += up(BHN * kC);
+  s.A = o;    o += up(BHN * kC * kC);
+  s.M = o;    o += up(BHN * kC * kC);
+  s.T = o;    o += up(BHN * kC * kC);
+  s.S = o;    o += up(BHN * DK * DV);
+  s.dS = o;   o += up(BHN * DK * DV);
+  s.D = o;    o += up(BHN * kC * DV);
+  s.dX = o;   o += up(BHN * kC * DV);
+  s.part = o; o += up(BHN * (DV / 16) * 4 * kC);
+  s.total = o;
+  return s;
+}
+
+struct Ctx {                    // per-workgroup indices of a (b, h, chunk)
+  int b, h, bh, c, N, t0, Cc;
+};
+HAM_DEVICE Ctx ctx(const RnnBwdArgs& a, int bh, int c) {
+  Ctx x;
+  x.bh = bh; x.b = bh / a.H; x.h = bh % a.H; x.c = c;
+  x.N = (a.T + kC - 1) / kC;
+  x.t0 = c * kC;
+  x.Cc = min(kC, a.T - x.t0);
+  return x;
+}
+
+// rows t < Cc of a [B,T,H,D] tensor (columns col0 .. col0 + W - 1) into LDS [64][W + LP]
+// as floats; padded rows are zero
+template <class IO, int D, int W>
+HAM_DEVICE void load_rows(float* dst, const void* src, const RnnBwdArgs& a, const Ctx& x, int col0) {
+  using E = typename IO::elem;
+  const E* p = static_cast<const E*>(src);
+  for (int i = threadIdx.x; i < kC * W / 4; i += blockDim.x) {
+    const int t = i / (W / 4), c4 = (i % (W / 4)) * 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < x.Cc) IO::load4(p, (((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * D + col0 + c4, v);
+    float* q = dst + t * (W + LP) + c4;
+    q[0] = v[0]; q[1] = v[1]; q[2] = v[2]; q[3] = v[3];
+  }
+}
+// a [64][64] fp32 matrix of the chunk from scratch into LDS [64][RW]
+HAM_DEVICE void load_mat(float* dst, const float* src) {
+  for (int i = threadIdx.x; i < kC * kC / 4; i += blockDim.x) {
+    const int t = i / (kC / 4), c4 = (i % (kC / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + t * kC + c4);
+    float* q = dst + t * RW + c4;
+    q[0] = v[0]; q[1] = v[1]; q[2] = v[2]; q[3] = v[3];
+  }
+}
+// columns col0 .. col0 + W - 1 of R rows with row length LD (scratch) into LDS [R][W + LP]
+template <int R, int W>
+HAM_DEVICE void load_block(float* dst, const float* src, int LD, int col0) {
+  for (int i = threadIdx.x; i < R * W / 4; i += blockDim.x) {
+    const int t = i / (W / 4), c4 = (i % (W / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)t * LD + col0 + c4);
+    float* q = dst + t * (W + LP) + c4;
+    q[0] = v[0]; q[1] = v[1]; q[2] = v[2]; q[3] = v[3];
+  }
+}
+
+// ---- cbwd_prep: G, A, M, T' of one chunk -----------------------------------------
+// grid (N, B*H), 256 threads.  Wave w forms row tile w of K K^T and Q K^T.  T' by forward
+// substitution, one column per lane of wave 0: T'_tj = beta_t ([t == j] - sum_{s<t} A_ts T'_sj).
+template <class IO, int DK>
+__global__ __launch_bounds__(256) void cbwd_prep(RnnBwdArgs a, Scratch sc) {
+  constexpr int KW = DK + LP;
+  __shared__ float Ks[kC * KW], Qs[kC * KW], As[kC * RW], Gs[kC], Bs[kC];
+  const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  const size_t cid = (size_t)x.bh * x.N + x.c;
+  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
+  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+  if (wave == 0) {
+    const bool real = lane < x.Cc;
+    const size_t tok = ((size_t)x.b * a.T + x.t0 + (real ? lane : 0)) * a.H + x.h;
+    float G = real ? a.g[tok] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(G, o, kWave);
+      if (lane >= o) G += y;
+    }
+    Gs[lane] = G;
+    Bs[lane] = real ? a.beta[tok] : 0.f;
+    a.scratch[sc.G + cid * kC + lane] = G;
+  }
+  __syncthreads();
+  float* Ag = a.scratch + sc.A + cid * kC * kC;
+  float* Mg = a.scratch + sc.M + cid * kC * kC;
+#pragma unroll
+  for (int si = 0; si < 4; ++si) {
+    f32x4 kk = (f32x4)(0.f), qk = (f32x4)(0.f);
+    for (int d = 0; d < DK; d += 4) {
+      const float kb = Ks[(16 * si + n) * KW + d + g4];
+      kk = mf(Ks[(16 * wave + n) * KW + d + g4], kb, kk);
+      qk = mf(Qs[(16 * wave + n) * KW + d + g4], kb, qk);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * g4 + r, s = 16 * si + n;
+      const float gam = s <= t ? __expf(Gs[t] - Gs[s]) : 0.f;
+      const float av = s < t ? gam * kk[r] : 0.f;
+      const float mv = gam * qk[r];
+      Ag[t * kC + s] = av;
+      Mg[t * kC + s] = mv;
+      As[t * RW + s] = av;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int j = lane;
+    float col[kC];
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;      // four partial sums for ILP
+#pragma unroll
+      for (int s = 0; s + 3 < t; s += 4) {
+        p0 = fmaf(As[t * RW + s], col[s], p0);
+        p1 = fmaf(As[t * RW + s + 1], col[s + 1], p1);
+        p2 = fmaf(As[t * RW + s + 2], col[s + 2], p2);
+        p3 = fmaf(As[t * RW + s + 3], col[s + 3], p3);
+      }
+#pragma unroll
+      for (int s = t & ~3; s < t; ++s) p0 = fmaf(As[t * RW + s], col[s], p0);
+      col[t] = Bs[t] * ((t == j ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3)));
+    }
+    float* Tg = a.scratch + sc.T + cid * kC * kC;
+#pragma unroll
+    for (int t = 0; t < kC; ++t) Tg[t * kC + j] = col[t];
+  }
+}
+
+// ---- cbwd_fwd: the entering state of every chunk, and D --------------------------
+// grid (B*H, DV/64), 256 threads: wave w owns value columns 64 y + 16 w .. + 15.
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void cbwd_fwd(RnnBwdArgs a, Scratch sc) {
+  constexpr int KW = DK + LP, RT = DK / 16;
+  __shared__ float Ks[kC * KW], Vs[kC * RW], Ts[kC * RW], Gs[kC];
+  const int bh = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  const int cb0 = blockIdx.y * 64, col = cb0 + 16 * wave + n;
+  Ctx x = ctx(a, bh, 0);
+  f32x4 S[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[rt][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] : 0.f;
+  for (int c = 0; c < x.N; ++c) {
+    x = ctx(a, bh, c);
+    const size_t cid = (size_t)bh * x.N + c;
+    float* Sg = a.scratch + sc.S + cid * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sg[(size_t)(16 * rt + 4 * g4 + r) * DV + col] = S[rt][r];
+    __syncthreads();                                        // the previous chunk's LDS reads
+    load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
+    load_rows<IO, DV, 64>(Vs, a.v, a, x, cb0);
+    load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
+    if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+    __syncthreads();
+    // Y = K S
+    f32x4 Y[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      Y[tt] = (f32x4)(0.f);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[tt] = mf(Ks[(16 * tt + n) * KW + 16 * rt + 4 * g4 + r], S[rt][r], Y[tt]);
+    }
+    // X = V - diag(gamma) Y
+    f32x4 X[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        X[tt][r] = Vs[t * RW + 16 * wave + n] - __expf(Gs[t]) * Y[tt][r];
+      }
+    // D = T' X (T' lower triangular)
+    f32x4 D[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      D[tt] = (f32x4)(0.f);
+#pragma unroll
+      for (int u = 0; u <= tt; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) D[tt] = mf(Ts[(16 * tt + n) * RW + 16 * u + 4 * g4 + r], X[u][r], D[tt]);
+    }
+    float* Dg = a.scratch + sc.D + cid * kC * DV;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Dg[(size_t)(16 * tt + 4 * g4 + r) * DV + col] = D[tt][r];
+    // S <- gamma_C S + K^T diag(w) D
+    const float GL = Gs[kC - 1], gC = __expf(GL);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) S[rt] *= gC;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        const float wd = __expf(GL - Gs[t]) * D[tt][r];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) S[rt] = mf(Ks[t * KW + 16 * rt + n], wd, S[rt]);
+      }
+  }
+}
+
+// ---- cbwd_rev: dS_C of every chunk (from the end), and dS0 -----------------------
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
+  constexpr int KW = DK + LP, RT = DK / 16;
+  __shared__ float Ks[kC * KW], Qs[kC * KW], Ms[kC * RW], Ts[kC * RW], dOs[kC * RW], Gs[kC];
+  const int bh = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  const int cb0 = blockIdx.y * 64, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
+  Ctx x = ctx(a, bh, 0);
+  f32x4 dS[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dS[rt][r] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] : 0.f;
+  for (int c = x.N - 1; c >= 0; --c) {
+    x = ctx(a, bh, c);
+    const size_t cid = (size_t)bh * x.N + c;
+    float* dSg = a.scratch + sc.dS + cid * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dSg[(size_t)(16 * rt + 4 * g4 + r) * DV + col] = dS[rt][r];
+    __syncthreads();
+    load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
+    load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+    load_mat(Ms, a.scratch + sc.M + cid * kC * kC);
+    load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
+    load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
+    if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+    __syncthreads();
+    const float GL = Gs[kC - 1], gC = __expf(GL);
+    // dD = M^T dO + diag(w) K dS   (M^T upper triangular)
+    f32x4 dD[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 kd = (f32x4)(0.f), md = (f32x4)(0.f);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kd = mf(Ks[(16 * tt + n) * KW + 16 * rt + 4 * g4 + r], dS[rt][r], kd);
+#pragma unroll
+      for (int u = tt; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = 16 * u + 4 * g4 + r;
+          md = mf(Ms[s * RW + 16 * tt + n], dOs[s * RW + cw], md);
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        dD[tt][r] = md[r] + __expf(GL - Gs[t]) * kd[r];
+      }
+    }
+    // dX = T'^T dD   (T'^T upper triangular)
+    f32x4 dX[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      dX[tt] = (f32x4)(0.f);
+#pragma unroll
+      for (int u = tt; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dX[tt] = mf(Ts[(16 * u + 4 * g4 + r) * RW + 16 * tt + n], dD[u][r], dX[tt]);
+    }
+    // dS <- gamma_C dS - K^T diag(gamma) dX + Q^T diag(gamma) dO
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) dS[rt] *= gC;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * g4 + r;
+        const float gt = __expf(Gs[t]);
+        const float bx = -gt * dX[tt][r], bo = gt * dOs[t * RW + cw];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          dS[rt] = mf(Ks[t * KW + 16 * rt + n], bx, dS[rt]);
+          dS[rt] = mf(Qs[t * KW + 16 * rt + n], bo, dS[rt]);
+        }
+      }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a.dS0[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] = dS[rt][r];
+}
+
+// ---- cbwd_cols: dV, dX and per-token partial sums, 16 value columns per wave -----
+// grid (N, B*H, DV/64), 256 threads.  Partials over the wave's columns: [0] U . R
+// (dbeta), [1] dO . QS - dX . KS (dgamma), [2] K dS . D (dw); [3][0] <S, dS> (dgamma_C).
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
+  constexpr int KW = DK + LP, RT = DK / 16;
+  __shared__ float Ks[kC * KW], Qs[kC * KW], As[kC * RW], Ms[kC * RW], Ts[kC * RW], Vs[kC * RW],
+      dOs[kC * RW], Gs[kC];
+  const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  const int cb0 = blockIdx.z * 64, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
+  const size_t cid = (size_t)x.bh * x.N + x.c;
+  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
+  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+  load_mat(As, a.scratch + sc.A + cid * kC * kC);
+  load_mat(Ms, a.scratch + sc.M + cid * kC * kC);
+  load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
+  load_rows<IO, DV, 64>(Vs, a.v, a, x, cb0);
+  load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
+  if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+  const float* Sg = a.scratch + sc.S + cid * DK * DV;
+  const float* dSg = a.scratch + sc.dS + cid * DK * DV;
+  const float* Dg = a.scratch + sc.D + cid * kC * DV;
+  f32x4 S[RT], dS[RT], D[4];
+  float sds = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t o = (size_t)(16 * rt + 4 * g4 + r) * DV + col;
+      S[rt][r] = Sg[o];
+      dS[rt][r] = dSg[o];
+      sds = fmaf(S[rt][r], dS[rt][r], sds);
+    }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) D[tt][r] = Dg[(size_t)(16 * tt + 4 * g4 + r) * DV + col];
+  __syncthreads();
+  const float GL = Gs[kC - 1];
+  f32x4 Y[4], QS[4], KdS[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    Y[tt] = (f32x4)(0.f); QS[tt] = (f32x4)(0.f); KdS[tt] = (f32x4)(0.f);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kcol = 16 * rt + 4 * g4 + r;
+        const float ka = Ks[(16 * tt + n) * KW + kcol];
+        Y[tt] = mf(ka, S[rt][r], Y[tt]);
+        KdS[tt] = mf(ka, dS[rt][r], KdS[tt]);
+        QS[tt] = mf(Qs[(16 * tt + n) * KW + kcol], S[rt][r], QS[tt]);
+      }
+  }
+  // dD = M^T dO + diag(w) K dS;  dX = T'^T dD;  U = dD - A^T dX;  R = X - A D
+  f32x4 dD[4], dX[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f32x4 md = (f32x4)(0.f);
+#pragma unroll
+    for (int u = tt; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * u + 4 * g4 + r;
+        md = mf(Ms[s * RW + 16 * tt + n], dOs[s * RW + cw], md);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dD[tt][r] = md[r] + __expf(GL - Gs[16 * tt + 4 * g4 + r]) * KdS[tt][r];
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    dX[tt] = (f32x4)(0.f);
+#pragma unroll
+    for (int u = tt; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dX[tt] = mf(Ts[(16 * u + 4 * g4 + r) * RW + 16 * tt + n], dD[u][r], dX[tt]);
+  }
+  float pb[16], pg[16], pw[16];
+  float* dXg = a.scratch + sc.dX + cid * kC * DV;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f32x4 atdx = (f32x4)(0.f), ad = (f32x4)(0.f);
+#pragma unroll
+    for (int u = tt; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) atdx = mf(As[(16 * u + 4 * g4 + r) * RW + 16 * tt + n], dX[u][r], atdx);
+#pragma unroll
+    for (int u = 0; u <= tt; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ad = mf(As[(16 * tt + n) * RW + 16 * u + 4 * g4 + r], D[u][r], ad);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tt + 4 * g4 + r;
+      const float X = Vs[t * RW + cw] - __expf(Gs[t]) * Y[tt][r];
+      const float U = dD[tt][r] - atdx[r], R = X - ad[r];
+      pb[4 * tt + r] = U * R;
+      pg[4 * tt + r] = dOs[t * RW + cw] * QS[tt][r] - dX[tt][r] * Y[tt][r];
+      pw[4 * tt + r] = KdS[tt][r] * D[tt][r];
+      dXg[(size_t)t * DV + col] = dX[tt][r];
+      if (t < x.Cc) a.dv[(((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DV + col] = dX[tt][r];
+    }
+  }
+  // lane (g4, n) receives the column sums of value index n: token 16 (n/4) + 4 g4 + n%4
+  const float sb = row16_transpose_sum(pb, n), sg = row16_transpose_sum(pg, n), sw = row16_transpose_sum(pw, n);
+  const int tok = 16 * (n >> 2) + 4 * g4 + (n & 3);
+  float* P = a.scratch + sc.part + (cid * (DV / 16) + blockIdx.z * 4 + wave) * 4 * kC;
+  P[tok] = sb;
+  P[kC + tok] = sg;
+  P[2 * kC + tok] = sw;
+  sds = wave_sum<64>(sds);
+  if (lane == 0) P[3 * kC] = sds;
+}
+
+// ---- cbwd_final: dM, dA, dQ, dK, dG -> dg, dbeta ---------------------------------
+// grid (N, B*H), 256 threads.  dQ and dK are formed transposed (dk rows x tokens):
+// wave w owns dk rows DK/4 * w .. + DK/4 - 1.  Phase 1 runs over the value columns in
+// blocks of 64 (dO, D, dX, S, dS of the block in LDS); phase 2 takes the Gram terms.
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
+  constexpr int KW = DK + LP, WR = DK / 4, WT = WR / 16;     // dk rows and row tiles per wave
+  constexpr int P1 = 3 * kC * RW + 2 * DK * RW;                // phase-1 floats
+  constexpr int P2 = 2 * kC * KW + 3 * kC * RW;                // phase-2 floats
+  __shared__ float L[P1 > P2 ? P1 : P2];
+  __shared__ float Gs[kC], rsum[kC], csum[kC];
+  const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  const size_t cid = (size_t)x.bh * x.N + x.c;
+  if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+  const float* Sg = a.scratch + sc.S + cid * DK * DV;
+  const float* dSg = a.scratch + sc.dS + cid * DK * DV;
+  const float* Dg = a.scratch + sc.D + cid * kC * DV;
+  const float* dXg = a.scratch + sc.dX + cid * kC * DV;
+  f32x4 dM[4], dA[4], dQT[WT][4], dKT[WT][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dM[i] = (f32x4)(0.f); dA[i] = (f32x4)(0.f);
+#pragma unroll
+    for (int kt = 0; kt < WT; ++kt) { dQT[kt][i] = (f32x4)(0.f); dKT[kt][i] = (f32x4)(0.f); }
+  }
+  float* dOs = L;
+  float* Ds = L + kC * RW;
+  float* dXs = L + 2 * kC * RW;
+  float* Ss = L + 3 * kC * RW;
+  float* dSs = Ss + DK * RW;
+  for (int cb0 = 0; cb0 < DV; cb0 += 64) {
+    __syncthreads();
+    load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
+    load_block<kC, 64>(Ds, Dg, DV, cb0);
+    load_block<kC, 64>(dXs, dXg, DV, cb0);
+    load_block<DK, 64>(Ss, Sg, DV, cb0);
+    load_block<DK, 64>(dSs, dSg, DV, cb0);
+    __syncthreads();
+    const float gl = Gs[kC - 1];
+    for (int d = 0; d < 64; d += 4) {
+      // dM, dA row tile `wave`: sum over the block's columns of dO D^T, dX D^T
+      const float o_a = dOs[(16 * wave + n) * RW + d + g4], x_a = dXs[(16 * wave + n) * RW + d + g4];
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        const float db = Ds[(16 * si + n) * RW + d + g4];
+        dM[si] = mf(o_a, db, dM[si]);
+        dA[si] = mf(x_a, db, dA[si]);
+      }
+      // dQ^T += S diag(gamma) dO^T;  dK^T += -S (diag(gamma) dX)^T + dS (diag(w) D)^T
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + n;
+        const float gt = __expf(Gs[t]), wt = __expf(gl - Gs[t]);
+        const float bo = gt * dOs[t * RW + d + g4], bx = -gt * dXs[t * RW + d + g4], bd = wt * Ds[t * RW + d + g4];
+#pragma unroll
+        for (int kt = 0; kt < WT; ++kt) {
+          const int row = WR * wave + 16 * kt + n;
+          const float sa = Ss[row * RW + d + g4], dsa = dSs[row * RW + d + g4];
+          dQT[kt][tt] = mf(sa, bo, dQT[kt][tt]);
+          dKT[kt][tt] = mf(sa, bx, dKT[kt][tt]);
+          dKT[kt][tt] = mf(dsa, bd, dKT[kt][tt]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // phase 2: dM o Gamma, dA o Gamma and dM o M + dA o A in LDS; K and Q rows
+  float* Ks = L;
+  float* Qs = L + kC * KW;
+  float* dMG = L + 2 * kC * KW;
+  float* dAG = dMG + kC * RW;
+  float* dGG = dAG + kC * RW;
+  const float* Ag = a.scratch + sc.A + cid * kC * kC;
+  const float* Mg = a.scratch + sc.M + cid * kC * kC;
+#pragma unroll
+  for (int si = 0; si < 4; ++si)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * g4 + r, s = 16 * si + n;
+      const float gam = s <= t ? __expf(Gs[t] - Gs[s]) : 0.f;
+      const float dm = s <= t ? dM[si][r] : 0.f, da = s < t ? -dA[si][r] : 0.f;
+      dMG[t * RW + s] = dm * gam;
+      dAG[t * RW + s] = da * gam;
+      dGG[t * RW + s] = dm * Mg[t * kC + s] + da * Ag[t * kC + s];
+    }
+  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
+  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+  __syncthreads();
+  if (threadIdx.x < kC) {                                   // row sums
+    float s = 0.f;
+    for (int j = 0; j < kC; ++j) s += dGG[threadIdx.x * RW + j];
+    rsum[threadIdx.x] = s;
+  } else if (threadIdx.x < 2 * kC) {                        // column sums
+    const int j = threadIdx.x - kC;
+    float s = 0.f;
+    for (int t = 0; t < kC; ++t) s += dGG[t * RW + j];
+    csum[j] = s;
+  }
+  // dQ^T += K^T (dM o Gamma)^T;  dK^T += Q^T (dM o Gamma) + K^T (dA o Gamma)^T + K^T (dA o Gamma)
+  for (int s0 = 0; s0 < kC; s0 += 4) {
+    const int s = s0 + g4;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int t = 16 * tt + n;
+      const float mgT = dMG[t * RW + s], mg = dMG[s * RW + t];
+      const float agT = dAG[t * RW + s], ag = dAG[s * RW + t];
+#pragma unroll
+      for (int kt = 0; kt < WT; ++kt) {
+        const int row = WR * wave + 16 * kt + n;
+        const float ka = Ks[s * KW + row], qa = Qs[s * KW + row];
+        dQT[kt][tt] = mf(ka, mgT, dQT[kt][tt]);
+        dKT[kt][tt] = mf(qa, mg, dKT[kt][tt]);
+        dKT[kt][tt] = mf(ka, agT + ag, dKT[kt][tt]);
+      }
+    }
+  }
+  // dQ^T / dK^T tiles: lane (g4, n) holds dk rows WR w + 16 kt + 4 g4 + r of token 16 tt + n
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = 16 * tt + n;
+    if (t < x.Cc) {
+      const size_t o = (((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DK;
+#pragma unroll
+      for (int kt = 0; kt < WT; ++kt) {
+        const int row = WR * wave + 16 * kt + 4 * g4;
+        *reinterpret_cast<f32x4*>(a.dq + o + row) = dQT[kt][tt];
+        *reinterpret_cast<f32x4*>(a.dk + o + row) = dKT[kt][tt];
+      }
+    }
+  }
+  __syncthreads();
+  // dG, then dg = reverse cumulative sum over the real tokens; dbeta
+  if (wave == 0) {
+    const int t = lane;
+    const float* P = a.scratch + sc.part + cid * (DV / 16) * 4 * kC;
+    float db = 0.f, dgam = 0.f, dw = 0.f, dgC = 0.f;
+    for (int cb = 0; cb < DV / 16; ++cb) {
+      db += P[cb * 4 * kC + t];
+      dgam += P[cb * 4 * kC + kC + t];
+      dw += P[cb * 4 * kC + 2 * kC + t];
+      dgC += P[cb * 4 * kC + 3 * kC];
+    }
+    const bool real = t < x.Cc;
+    const float G = Gs[t], GLr = Gs[kC - 1];
+    const float wt = __expf(GLr - G);
+    float dG = real ? __expf(G) * dgam - wt * dw + rsum[t] - csum[t] : 0.f;
+    const float tail = wave_sum<64>(real ? wt * dw : 0.f);
+    if (t == x.Cc - 1) dG += __expf(GLr) * dgC + tail;
+    // reverse inclusive scan: dg_t = sum_{j >= t} dG_j
+    float acc = dG;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(acc, o, kWave);
+      if (lane + o < 64) acc += y;
+    }
+    if (real) {
+      const size_t tok = ((size_t)x.b * a.T + x.t0 + t) * a.H + x.h;
+      a.dg[tok] = acc;
+      a.dbeta[tok] = db;
+    }
+  }
+}
+
+template <class IO, int DK, int DV>
+hipError_t launch_t(const RnnBwdArgs& a, hipStream_t s) {
+  const Scratch sc = scratch_layout(a.B, a.H, a.T, DK, DV);
+  const int N = (a.T + kC - 1) / kC, BH = a.B * a.H;
+  hipLaunchKernelGGL((cbwd_prep<IO, DK>), dim3(N, BH), dim3(256), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_fwd<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_rev<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / 64), dim3(256), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(256), 0, s, a, sc);
+  return hipGetLastError();
+}
+
+}  // namespace cbwd
+
+size_t rnn_backward_chunked_scratch_floats(int B, int H, int T, int dk, int dv) {
+  return cbwd::scratch_layout(B, H, T, dk, dv).total;
+}
+
+hipError_t launch_rnn_backward_chunked(int io, int dk, int dv, const RnnBwdArgs& a, hipStream_t s) {
+#define HAM_CASE(IOT, DKV, DVV) \
+  if (dk == DKV && dv == DVV) return cbwd::launch_t<IOT, DKV, DVV>(a, s);
+  if (io == 0) {
+    HAM_CASE(IoF32, 64, 64) HAM_CASE(IoF32, 64, 128) HAM_CASE(IoF32, 128, 64) HAM_CASE(IoF32, 128, 128)
+  } else {
+    HAM_CASE(IoBF16, 64, 64) HAM_CASE(IoBF16, 64, 128) HAM_CASE(IoBF16, 128, 64) HAM_CASE(IoBF16, 128, 128)
+  }
+#undef HAM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ham

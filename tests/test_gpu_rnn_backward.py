@@ -22,15 +22,18 @@ def _rel(x, y, axes):
     return rel_err_slices(x, y, axes)
 
 
+@pytest.mark.parametrize("recurrent", [False, True], ids=["chunked", "token_serial"])
 @pytest.mark.parametrize("B,T,H,dk,dv,dtype,s0,dst", [
     (2, 37, 2, 64, 64, torch.float32, False, False),
     (1, 130, 3, 128, 128, torch.bfloat16, True, True),
     (2, 65, 1, 64, 128, torch.float32, True, False),
     (1, 200, 2, 128, 64, torch.bfloat16, False, True),
     (1, 1, 2, 128, 128, torch.float32, True, True),
+    (1, 64, 1, 64, 64, torch.float32, True, True),
+    (1, 128, 2, 128, 128, torch.float32, False, True),
     (2, 1024, 2, 128, 128, torch.bfloat16, True, True),
 ])
-def test_rnn_backward(B, T, H, dk, dv, dtype, s0, dst):
+def test_rnn_backward(B, T, H, dk, dv, dtype, s0, dst, recurrent):
     seed = 500 + T + dk
     inp = make_inputs(B, T, H, dk, dv, dtype="f32" if dtype == torch.float32 else "bf16", seed=seed)
     rng = np.random.default_rng(seed)
@@ -39,8 +42,10 @@ def test_rnn_backward(B, T, H, dk, dv, dtype, s0, dst):
     dS_T = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if dst else None
     t = to_dev(inp, dtype, DEV)
     dev = lambda x: None if x is None else torch.from_numpy(x).to(DEV)
-    print(f"rnn backward: B={B} T={T} H={H} {dk}/{dv} {dtype} S0={s0} dS_T={dst}", flush=True)
-    got = ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], dev(dO), S0=dev(S0), dS_T=dev(dS_T))
+    print(f"rnn backward ({'token-serial' if recurrent else 'chunked'}): B={B} T={T} H={H} {dk}/{dv} {dtype} "
+          f"S0={s0} dS_T={dst}", flush=True)
+    got = ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], dev(dO), S0=dev(S0), dS_T=dev(dS_T),
+                               force_recurrent=recurrent)
     torch.cuda.synchronize()
     ref = oracle.rnn_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], dO, S0=S0, dS_T=dS_T)
     errs = {n: _rel(np_of(got[n]), ref[n], 2) for n in ("dq", "dk", "dv")}
