@@ -27,10 +27,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
-# The library is built with packed fp32 instructions disabled.  That does not halve the
-# vector rate: a plain fp32 FMA of a 64-lane wave issues about every 2 cycles on a SIMD
-# (32 lanes per clock), so the published 157.3 TFLOP/s is the roof of the VALU kernels.
-PEAK_FP32_VALU_TFLOPS = PEAK_FP32_TFLOPS
+# (The library is built with packed fp32 instructions disabled.  That does not halve the
+# vector rate: a plain fp32 FMA of a 64-lane wave issues about every 2 cycles on a SIMD,
+# 32 lanes per clock, so 157.3 TFLOP/s is the fp32 roof of vector and matrix-core work.)
 CHUNK = 64
 STAGES = ["rnn_prep", "rnn_state", "route", "compact", "attention"]
 
@@ -474,9 +473,11 @@ def bench_backward(args, dev, w, t, plan, pairs, steps=3, warmup=1):
 
 def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):
     """Gradients of the gated delta-rule RNN at the layer shape (dO = dL/do_rnn and
-    dS_T ~ N(0,1)): a token-serial fp32 kernel, priced at 20 d_k d_v FLOPs per token
-    and head (two forward passes of the recurrence, 4 d_k d_v each, and the reverse
-    step, 12 d_k d_v) against the VALU rate the build can reach."""
+    dS_T ~ N(0,1)): the chunked form (chunk prep, the forward and reverse state chains
+    over chunks, two chunk-parallel gradient kernels) on the fp32 matrix cores, priced
+    at 20 d_k d_v FLOPs per token and head (two forward passes of the recurrence,
+    4 d_k d_v each, and the reverse step, 12 d_k d_v) against the fp32 peak.  The
+    token-serial reverse (HAM_FORCE_RECURRENT) is timed once beside it."""
     import torch
     import attention_sequence_mixing_amd as ham
     gen = torch.Generator(device=dev)
@@ -484,26 +485,34 @@ def bench_rnn_backward(args, dev, w, t, steps=3, warmup=1):
     dO = torch.randn((w.B, w.T, w.H, w.d), generator=gen, device=dev, dtype=torch.float32)
     dST = torch.randn((w.B, w.H, w.d, w.d), generator=gen, device=dev, dtype=torch.float32)
 
-    def run():
-        ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], dO, dS_T=dST)
+    def run(serial=False):
+        ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], dO, dS_T=dST, force_recurrent=serial)
+
+    def timed(n, serial=False):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            run(serial)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
+    ms = timed(steps)
+    run(True)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms_serial = timed(1, True)
     tflops = w.B * w.T * w.H * 20 * w.d * w.d / (ms / 1e3) / 1e12
-    log(f"[bench] rnn backward: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s algorithmic "
-        f"({100 * tflops / PEAK_FP32_VALU_TFLOPS:.1f}% of the fp32 vector peak)")
+    log(f"[bench] rnn backward: {ms:.3f} ms/step (token-serial reverse {ms_serial:.3f} ms), {tflops:.1f} TFLOP/s "
+        f"algorithmic ({100 * tflops / PEAK_FP32_TFLOPS:.1f}% of the fp32 peak)")
+    parts = [measured_traffic(k) for k in ("cbwd_prep", "cbwd_fwd", "cbwd_rev", "cbwd_cols", "cbwd_final")]
     return dict(workload=f"{w.name}_rnn_backward", ms_per_step=round(ms, 4), steps=steps, warmup=warmup,
-                roofline=dict(bound="alu", achieved=round(tflops, 3), peak=PEAK_FP32_VALU_TFLOPS,
-                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_VALU_TFLOPS, 4),
-                              traffic=measured_traffic("rnn_bwd")))
+                token_serial_ms=round(ms_serial, 3),
+                roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_FP32_TFLOPS,
+                              unit="TFLOP/s", frac=round(tflops / PEAK_FP32_TFLOPS, 4),
+                              traffic=None if None in parts else sum(parts)))
 
 
 def bench_long(args, dev, steps=10, warmup=10):
