@@ -115,18 +115,104 @@ HAM_DEVICE void load_block(float* dst, const float* src, int LD, int col0) {
   }
 }
 
+// One thread's share (16-byte pieces) of a chunk's rows [64][W] of a [B,T,H,D] tensor
+// (columns col0 .., padded rows zero), held in registers from the moment the loads
+// are issued until they are written to LDS as floats [64][W + LP]: the state chains
+// fetch the next chunk's inputs while the current chunk computes.
+template <class IO, int D, int W>
+struct RowsPre {
+  static constexpr int EPP = 16 / IO::kBytes, PPR = W / EPP, NP = kC * PPR / 256;
+  static_assert(kC * PPR % 256 == 0, "whole pieces per thread");
+  uint4 x[NP];
+  HAM_DEVICE void load(const void* src, const RnnBwdArgs& a, const Ctx& c, int col0) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = threadIdx.x + 256 * j, t = p / PPR, e0 = (p % PPR) * EPP;
+      x[j] = t < c.Cc ? *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                        ((((size_t)c.b * a.T + c.t0 + t) * a.H + c.h) * D + col0 + e0) * IO::kBytes)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  }
+  HAM_DEVICE void store(float* dst) const {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = threadIdx.x + 256 * j, t = p / PPR, e0 = (p % PPR) * EPP;
+      float* q = dst + t * (W + LP) + e0;
+      const uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+      if constexpr (IO::kBytes == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q[2 * i] = __uint_as_float(w[i] << 16);
+          q[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = __uint_as_float(w[i]);
+      }
+    }
+  }
+};
+// the same for a [64][64] fp32 matrix of the chunk in scratch
+struct MatPre {
+  static constexpr int NP = kC * 16 / 256;
+  float4 x[NP];
+  HAM_DEVICE void load(const float* src) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) x[j] = reinterpret_cast<const float4*>(src)[threadIdx.x + 256 * j];
+  }
+  HAM_DEVICE void store(float* dst) const {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = threadIdx.x + 256 * j, t = p / 16, c4 = (p % 16) * 4;
+      float* q = dst + t * RW + c4;
+      q[0] = x[j].x; q[1] = x[j].y; q[2] = x[j].z; q[3] = x[j].w;
+    }
+  }
+};
+
+// rows t < Cc of a [B,T,H,D] tensor into LDS in their own element type, rows D + 16 bytes
+// apart (padded rows zero); ldf reads one element as a float
+template <class IO, int D>
+HAM_DEVICE void load_rows_raw(typename IO::elem* dst, const void* src, const RnnBwdArgs& a, const Ctx& x) {
+  constexpr int EPP = 16 / IO::kBytes, PPR = D / EPP, RS = D + EPP;
+  for (int i = threadIdx.x; i < kC * PPR; i += blockDim.x) {
+    const int t = i / PPR, e0 = (i % PPR) * EPP;
+    const uint4 v = t < x.Cc ? *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                               ((((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * D + e0) * IO::kBytes)
+                             : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(dst + t * RS + e0) = v;
+  }
+}
+// columns col0 .. col0 + W - 1 of the same, rows W + 16 bytes apart
+template <class IO, int D, int W>
+HAM_DEVICE void load_cols_raw(typename IO::elem* dst, const void* src, const RnnBwdArgs& a, const Ctx& x, int col0) {
+  constexpr int EPP = 16 / IO::kBytes, PPR = W / EPP, RS = W + EPP;
+  for (int i = threadIdx.x; i < kC * PPR; i += blockDim.x) {
+    const int t = i / PPR, e0 = (i % PPR) * EPP;
+    const uint4 v = t < x.Cc ? *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                               ((((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * D + col0 + e0) * IO::kBytes)
+                             : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(dst + t * RS + e0) = v;
+  }
+}
+HAM_DEVICE float ldf(const float* p, int i) { return p[i]; }
+HAM_DEVICE float ldf(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+
 // ---- cbwd_prep: G, A, M, T' of one chunk -----------------------------------------
 // grid (N, B*H), 256 threads.  Wave w forms row tile w of K K^T and Q K^T.  T' by forward
 // substitution, one column per lane of wave 0: T'_tj = beta_t ([t == j] - sum_{s<t} A_ts T'_sj).
 template <class IO, int DK>
 __global__ __launch_bounds__(256) void cbwd_prep(RnnBwdArgs a, Scratch sc) {
-  constexpr int KW = DK + LP;
-  __shared__ float Ks[kC * KW], Qs[kC * KW], As[kC * RW], Gs[kC], Bs[kC];
+  using E = typename IO::elem;
+  constexpr int KW = DK + 16 / IO::kBytes;                 // K and Q rows in their input type
+  __shared__ __attribute__((aligned(16))) E Ks[kC * KW];
+  __shared__ __attribute__((aligned(16))) E Qs[kC * KW];
+  __shared__ float As[kC * RW], Gs[kC], Bs[kC];
   const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
   const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
   const size_t cid = (size_t)x.bh * x.N + x.c;
-  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
-  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+  load_rows_raw<IO, DK>(Ks, a.k, a, x);
+  load_rows_raw<IO, DK>(Qs, a.q, a, x);
   if (wave == 0) {
     const bool real = lane < x.Cc;
     const size_t tok = ((size_t)x.b * a.T + x.t0 + (real ? lane : 0)) * a.H + x.h;
@@ -147,9 +233,9 @@ __global__ __launch_bounds__(256) void cbwd_prep(RnnBwdArgs a, Scratch sc) {
   for (int si = 0; si < 4; ++si) {
     f32x4 kk = (f32x4)(0.f), qk = (f32x4)(0.f);
     for (int d = 0; d < DK; d += 4) {
-      const float kb = Ks[(16 * si + n) * KW + d + g4];
-      kk = mf(Ks[(16 * wave + n) * KW + d + g4], kb, kk);
-      qk = mf(Qs[(16 * wave + n) * KW + d + g4], kb, qk);
+      const float kb = ldf(Ks, (16 * si + n) * KW + d + g4);
+      kk = mf(ldf(Ks, (16 * wave + n) * KW + d + g4), kb, kk);
+      qk = mf(ldf(Qs, (16 * wave + n) * KW + d + g4), kb, qk);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -201,6 +287,19 @@ __global__ __launch_bounds__(256) void cbwd_fwd(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       S[rt][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] : 0.f;
+  RowsPre<IO, DK, DK> pk;
+  RowsPre<IO, DV, 64> pv;
+  MatPre pt;
+  float pg = 0.f;
+  auto fetch = [&](int c) {                                 // chunk c's inputs into registers
+    const Ctx y = ctx(a, bh, c);
+    const size_t cid = (size_t)bh * y.N + c;
+    pk.load(a.k, a, y, 0);
+    pv.load(a.v, a, y, cb0);
+    pt.load(a.scratch + sc.T + cid * kC * kC);
+    if (threadIdx.x < kC) pg = a.scratch[sc.G + cid * kC + threadIdx.x];
+  };
+  fetch(0);
   for (int c = 0; c < x.N; ++c) {
     x = ctx(a, bh, c);
     const size_t cid = (size_t)bh * x.N + c;
@@ -210,11 +309,12 @@ __global__ __launch_bounds__(256) void cbwd_fwd(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Sg[(size_t)(16 * rt + 4 * g4 + r) * DV + col] = S[rt][r];
     __syncthreads();                                        // the previous chunk's LDS reads
-    load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
-    load_rows<IO, DV, 64>(Vs, a.v, a, x, cb0);
-    load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
-    if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+    pk.store(Ks);
+    pv.store(Vs);
+    pt.store(Ts);
+    if (threadIdx.x < kC) Gs[threadIdx.x] = pg;
     __syncthreads();
+    if (c + 1 < x.N) fetch(c + 1);                          // in flight under this chunk's products
     // Y = K S
     f32x4 Y[4];
 #pragma unroll
@@ -279,6 +379,21 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       dS[rt][r] = a.dS_T ? a.dS_T[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] : 0.f;
+  RowsPre<IO, DK, DK> pk, pq;
+  RowsPre<IoF32, DV, 64> po;
+  MatPre pm, pt;
+  float pg = 0.f;
+  auto fetch = [&](int c) {                                 // chunk c's inputs into registers
+    const Ctx y = ctx(a, bh, c);
+    const size_t cid = (size_t)bh * y.N + c;
+    pk.load(a.k, a, y, 0);
+    pq.load(a.q, a, y, 0);
+    po.load(a.dO, a, y, cb0);
+    pm.load(a.scratch + sc.M + cid * kC * kC);
+    pt.load(a.scratch + sc.T + cid * kC * kC);
+    if (threadIdx.x < kC) pg = a.scratch[sc.G + cid * kC + threadIdx.x];
+  };
+  fetch(x.N - 1);
   for (int c = x.N - 1; c >= 0; --c) {
     x = ctx(a, bh, c);
     const size_t cid = (size_t)bh * x.N + c;
@@ -288,13 +403,14 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dSg[(size_t)(16 * rt + 4 * g4 + r) * DV + col] = dS[rt][r];
     __syncthreads();
-    load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
-    load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
-    load_mat(Ms, a.scratch + sc.M + cid * kC * kC);
-    load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
-    load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
-    if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
+    pk.store(Ks);
+    pq.store(Qs);
+    po.store(dOs);
+    pm.store(Ms);
+    pt.store(Ts);
+    if (threadIdx.x < kC) Gs[threadIdx.x] = pg;
     __syncthreads();
+    if (c > 0) fetch(c - 1);                                // in flight under this chunk's products
     const float GL = Gs[kC - 1], gC = __expf(GL);
     // dD = M^T dO + diag(w) K dS   (M^T upper triangular)
     f32x4 dD[4];
@@ -352,24 +468,35 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
 }
 
 // ---- cbwd_cols: dV, dX and per-token partial sums, 16 value columns per wave -----
-// grid (N, B*H, DV/64), 256 threads.  Partials over the wave's columns: [0] U . R
-// (dbeta), [1] dO . QS - dX . KS (dgamma), [2] K dS . D (dw); [3][0] <S, dS> (dgamma_C).
+// grid (N, B*H, DV/CW), 64 CW/16 threads: a workgroup takes CW value columns (all of
+// them with bf16 inputs, whose K, Q and V rows stay bf16 in LDS; 64 with fp32 inputs),
+// so the chunk's K, Q, A, M and T' are staged once for its columns.  Partials over the
+// wave's columns: [0] U . R (dbeta), [1] dO . QS - dX . KS (dgamma), [2] K dS . D (dw);
+// [3][0] <S, dS> (dgamma_C).
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
-  constexpr int KW = DK + LP, RT = DK / 16;
-  __shared__ float Ks[kC * KW], Qs[kC * KW], As[kC * RW], Ms[kC * RW], Ts[kC * RW], Vs[kC * RW],
-      dOs[kC * RW], Gs[kC];
+struct ColsGeom {
+  static constexpr int CW = IO::kBytes == 2 ? DV : 64, NW = CW / 16;
+};
+template <class IO, int DK, int DV>
+__global__ __launch_bounds__(512) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
+  using E = typename IO::elem;
+  constexpr int CW = ColsGeom<IO, DK, DV>::CW, NW = ColsGeom<IO, DK, DV>::NW;
+  constexpr int KW = DK + 16 / IO::kBytes, VW = CW + 16 / IO::kBytes, OW = CW + LP, RT = DK / 16;
+  __shared__ __attribute__((aligned(16))) E Ks[kC * KW];
+  __shared__ __attribute__((aligned(16))) E Qs[kC * KW];
+  __shared__ __attribute__((aligned(16))) E Vs[kC * VW];
+  __shared__ float As[kC * RW], Ms[kC * RW], Ts[kC * RW], dOs[kC * OW], Gs[kC];
   const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
   const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
-  const int cb0 = blockIdx.z * 64, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
+  const int cb0 = blockIdx.z * CW, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
   const size_t cid = (size_t)x.bh * x.N + x.c;
-  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
-  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
+  load_rows_raw<IO, DK>(Ks, a.k, a, x);
+  load_rows_raw<IO, DK>(Qs, a.q, a, x);
   load_mat(As, a.scratch + sc.A + cid * kC * kC);
   load_mat(Ms, a.scratch + sc.M + cid * kC * kC);
   load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
-  load_rows<IO, DV, 64>(Vs, a.v, a, x, cb0);
-  load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
+  load_cols_raw<IO, DV, CW>(Vs, a.v, a, x, cb0);
+  load_rows<IoF32, DV, CW>(dOs, a.dO, a, x, cb0);
   if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
   const float* Sg = a.scratch + sc.S + cid * DK * DV;
   const float* dSg = a.scratch + sc.dS + cid * DK * DV;
@@ -400,10 +527,10 @@ __global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kcol = 16 * rt + 4 * g4 + r;
-        const float ka = Ks[(16 * tt + n) * KW + kcol];
+        const float ka = ldf(Ks, (16 * tt + n) * KW + kcol);
         Y[tt] = mf(ka, S[rt][r], Y[tt]);
         KdS[tt] = mf(ka, dS[rt][r], KdS[tt]);
-        QS[tt] = mf(Qs[(16 * tt + n) * KW + kcol], S[rt][r], QS[tt]);
+        QS[tt] = mf(ldf(Qs, (16 * tt + n) * KW + kcol), S[rt][r], QS[tt]);
       }
   }
   // dD = M^T dO + diag(w) K dS;  dX = T'^T dD;  U = dD - A^T dX;  R = X - A D
@@ -416,7 +543,7 @@ __global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * u + 4 * g4 + r;
-        md = mf(Ms[s * RW + 16 * tt + n], dOs[s * RW + cw], md);
+        md = mf(Ms[s * RW + 16 * tt + n], dOs[s * OW + cw], md);
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) dD[tt][r] = md[r] + __expf(GL - Gs[16 * tt + 4 * g4 + r]) * KdS[tt][r];
@@ -445,10 +572,10 @@ __global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tt + 4 * g4 + r;
-      const float X = Vs[t * RW + cw] - __expf(Gs[t]) * Y[tt][r];
+      const float X = ldf(Vs, t * VW + cw) - __expf(Gs[t]) * Y[tt][r];
       const float U = dD[tt][r] - atdx[r], R = X - ad[r];
       pb[4 * tt + r] = U * R;
-      pg[4 * tt + r] = dOs[t * RW + cw] * QS[tt][r] - dX[tt][r] * Y[tt][r];
+      pg[4 * tt + r] = dOs[t * OW + cw] * QS[tt][r] - dX[tt][r] * Y[tt][r];
       pw[4 * tt + r] = KdS[tt][r] * D[tt][r];
       dXg[(size_t)t * DV + col] = dX[tt][r];
       if (t < x.Cc) a.dv[(((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DV + col] = dX[tt][r];
@@ -457,7 +584,7 @@ __global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
   // lane (g4, n) receives the column sums of value index n: token 16 (n/4) + 4 g4 + n%4
   const float sb = row16_transpose_sum(pb, n), sg = row16_transpose_sum(pg, n), sw = row16_transpose_sum(pw, n);
   const int tok = 16 * (n >> 2) + 4 * g4 + (n & 3);
-  float* P = a.scratch + sc.part + (cid * (DV / 16) + blockIdx.z * 4 + wave) * 4 * kC;
+  float* P = a.scratch + sc.part + (cid * (DV / 16) + blockIdx.z * NW + wave) * 4 * kC;
   P[tok] = sb;
   P[kC + tok] = sg;
   P[2 * kC + tok] = sw;
@@ -466,11 +593,11 @@ __global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
 }
 
 // ---- cbwd_final: dM, dA, dQ, dK, dG -> dg, dbeta ---------------------------------
-// grid (N, B*H), 256 threads.  dQ and dK are formed transposed (dk rows x tokens):
-// wave w owns dk rows DK/4 * w .. + DK/4 - 1.  Phase 1 runs over the value columns in
+// grid (N, B*H), 512 threads.  dQ and dK are formed transposed (dk rows x tokens):
+// wave w owns dk rows DK/4 * (w mod 4) .. + DK/4 - 1 of the token tiles 2 (w / 4), + 1.  Phase 1 runs over the value columns in
 // blocks of 64 (dO, D, dX, S, dS of the block in LDS); phase 2 takes the Gram terms.
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
+__global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
   constexpr int KW = DK + LP, WR = DK / 4, WT = WR / 16;     // dk rows and row tiles per wave
   constexpr int P1 = 3 * kC * RW + 2 * DK * RW;                // phase-1 floats
   constexpr int P2 = 2 * kC * KW + 3 * kC * RW;                // phase-2 floats
@@ -478,15 +605,18 @@ __global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
   __shared__ float Gs[kC], rsum[kC], csum[kC];
   const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
   const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
+  // wave: row tile (and dk row group) qw of dM, dA (dQ^T, dK^T); half hw of the column
+  // (token) tiles: 2 hw and 2 hw + 1
+  const int qw = wave & 3, hw = wave >> 2;
   const size_t cid = (size_t)x.bh * x.N + x.c;
   if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
   const float* Sg = a.scratch + sc.S + cid * DK * DV;
   const float* dSg = a.scratch + sc.dS + cid * DK * DV;
   const float* Dg = a.scratch + sc.D + cid * kC * DV;
   const float* dXg = a.scratch + sc.dX + cid * kC * DV;
-  f32x4 dM[4], dA[4], dQT[WT][4], dKT[WT][4];
+  f32x4 dM[2], dA[2], dQT[WT][2], dKT[WT][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     dM[i] = (f32x4)(0.f); dA[i] = (f32x4)(0.f);
 #pragma unroll
     for (int kt = 0; kt < WT; ++kt) { dQT[kt][i] = (f32x4)(0.f); dKT[kt][i] = (f32x4)(0.f); }
@@ -506,27 +636,27 @@ __global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
     __syncthreads();
     const float gl = Gs[kC - 1];
     for (int d = 0; d < 64; d += 4) {
-      // dM, dA row tile `wave`: sum over the block's columns of dO D^T, dX D^T
-      const float o_a = dOs[(16 * wave + n) * RW + d + g4], x_a = dXs[(16 * wave + n) * RW + d + g4];
+      // dM, dA tiles (qw, 2 hw + j): sum over the block's columns of dO D^T, dX D^T
+      const float o_a = dOs[(16 * qw + n) * RW + d + g4], x_a = dXs[(16 * qw + n) * RW + d + g4];
 #pragma unroll
-      for (int si = 0; si < 4; ++si) {
-        const float db = Ds[(16 * si + n) * RW + d + g4];
-        dM[si] = mf(o_a, db, dM[si]);
-        dA[si] = mf(x_a, db, dA[si]);
+      for (int j = 0; j < 2; ++j) {
+        const float db = Ds[(16 * (2 * hw + j) + n) * RW + d + g4];
+        dM[j] = mf(o_a, db, dM[j]);
+        dA[j] = mf(x_a, db, dA[j]);
       }
       // dQ^T += S diag(gamma) dO^T;  dK^T += -S (diag(gamma) dX)^T + dS (diag(w) D)^T
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + n;
+      for (int j = 0; j < 2; ++j) {
+        const int t = 16 * (2 * hw + j) + n;
         const float gt = __expf(Gs[t]), wt = __expf(gl - Gs[t]);
         const float bo = gt * dOs[t * RW + d + g4], bx = -gt * dXs[t * RW + d + g4], bd = wt * Ds[t * RW + d + g4];
 #pragma unroll
         for (int kt = 0; kt < WT; ++kt) {
-          const int row = WR * wave + 16 * kt + n;
+          const int row = WR * qw + 16 * kt + n;
           const float sa = Ss[row * RW + d + g4], dsa = dSs[row * RW + d + g4];
-          dQT[kt][tt] = mf(sa, bo, dQT[kt][tt]);
-          dKT[kt][tt] = mf(sa, bx, dKT[kt][tt]);
-          dKT[kt][tt] = mf(dsa, bd, dKT[kt][tt]);
+          dQT[kt][j] = mf(sa, bo, dQT[kt][j]);
+          dKT[kt][j] = mf(sa, bx, dKT[kt][j]);
+          dKT[kt][j] = mf(dsa, bd, dKT[kt][j]);
         }
       }
     }
@@ -541,12 +671,12 @@ __global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
   const float* Ag = a.scratch + sc.A + cid * kC * kC;
   const float* Mg = a.scratch + sc.M + cid * kC * kC;
 #pragma unroll
-  for (int si = 0; si < 4; ++si)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * g4 + r, s = 16 * si + n;
+      const int t = 16 * qw + 4 * g4 + r, s = 16 * (2 * hw + j) + n;
       const float gam = s <= t ? __expf(Gs[t] - Gs[s]) : 0.f;
-      const float dm = s <= t ? dM[si][r] : 0.f, da = s < t ? -dA[si][r] : 0.f;
+      const float dm = s <= t ? dM[j][r] : 0.f, da = s < t ? -dA[j][r] : 0.f;
       dMG[t * RW + s] = dm * gam;
       dAG[t * RW + s] = da * gam;
       dGG[t * RW + s] = dm * Mg[t * kC + s] + da * Ag[t * kC + s];
@@ -568,31 +698,32 @@ __global__ __launch_bounds__(256) void cbwd_final(RnnBwdArgs a, Scratch sc) {
   for (int s0 = 0; s0 < kC; s0 += 4) {
     const int s = s0 + g4;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int t = 16 * tt + n;
+    for (int j = 0; j < 2; ++j) {
+      const int t = 16 * (2 * hw + j) + n;
       const float mgT = dMG[t * RW + s], mg = dMG[s * RW + t];
       const float agT = dAG[t * RW + s], ag = dAG[s * RW + t];
 #pragma unroll
       for (int kt = 0; kt < WT; ++kt) {
-        const int row = WR * wave + 16 * kt + n;
+        const int row = WR * qw + 16 * kt + n;
         const float ka = Ks[s * KW + row], qa = Qs[s * KW + row];
-        dQT[kt][tt] = mf(ka, mgT, dQT[kt][tt]);
-        dKT[kt][tt] = mf(qa, mg, dKT[kt][tt]);
-        dKT[kt][tt] = mf(ka, agT + ag, dKT[kt][tt]);
+        dQT[kt][j] = mf(ka, mgT, dQT[kt][j]);
+        dKT[kt][j] = mf(qa, mg, dKT[kt][j]);
+        dKT[kt][j] = mf(ka, agT + ag, dKT[kt][j]);
       }
     }
   }
-  // dQ^T / dK^T tiles: lane (g4, n) holds dk rows WR w + 16 kt + 4 g4 + r of token 16 tt + n
+  // dQ^T / dK^T tiles: lane (g4, n) holds dk rows WR qw + 16 kt + 4 g4 + r of token
+  // 16 (2 hw + j) + n
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int t = 16 * tt + n;
+  for (int j = 0; j < 2; ++j) {
+    const int t = 16 * (2 * hw + j) + n;
     if (t < x.Cc) {
       const size_t o = (((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DK;
 #pragma unroll
       for (int kt = 0; kt < WT; ++kt) {
-        const int row = WR * wave + 16 * kt + 4 * g4;
-        *reinterpret_cast<f32x4*>(a.dq + o + row) = dQT[kt][tt];
-        *reinterpret_cast<f32x4*>(a.dk + o + row) = dKT[kt][tt];
+        const int row = WR * qw + 16 * kt + 4 * g4;
+        *reinterpret_cast<f32x4*>(a.dq + o + row) = dQT[kt][j];
+        *reinterpret_cast<f32x4*>(a.dk + o + row) = dKT[kt][j];
       }
     }
   }
@@ -636,8 +767,9 @@ hipError_t launch_t(const RnnBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((cbwd_prep<IO, DK>), dim3(N, BH), dim3(256), 0, s, a, sc);
   hipLaunchKernelGGL((cbwd_fwd<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
   hipLaunchKernelGGL((cbwd_rev<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
-  hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / 64), dim3(256), 0, s, a, sc);
-  hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(256), 0, s, a, sc);
+  using CG = ColsGeom<IO, DK, DV>;
+  hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / CG::CW), dim3(64 * CG::NW), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(512), 0, s, a, sc);
   return hipGetLastError();
 }
 
