@@ -593,20 +593,26 @@ __global__ __launch_bounds__(512) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
 }
 
 // ---- cbwd_final: dM, dA, dQ, dK, dG -> dg, dbeta ---------------------------------
-// grid (N, B*H), 512 threads.  dQ and dK are formed transposed (dk rows x tokens):
-// wave w owns dk rows DK/4 * (w mod 4) .. + DK/4 - 1 of the token tiles 2 (w / 4), + 1.  Phase 1 runs over the value columns in
-// blocks of 64 (dO, D, dX, S, dS of the block in LDS); phase 2 takes the Gram terms.
+// grid (N, B*H), 64 NWF threads.  dQ and dK are formed transposed (dk rows x tokens):
+// wave w owns dk rows DK/4 * (w mod 4) .. + DK/4 - 1 of JT token tiles, and the dM, dA
+// tiles (w mod 4, same JT column tiles).  Phase 1 runs over the value columns in blocks
+// of 32 (dO, D, dX, S, dS of the block in LDS); phase 2 takes the Gram terms, with K and
+// Q rows in LDS in their input type.  At bf16 two workgroups share a CU, so one stages
+// its rows while the other multiplies.
+constexpr int NWF = 4;
 template <class IO, int DK, int DV>
-__global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
-  constexpr int KW = DK + LP, WR = DK / 4, WT = WR / 16;     // dk rows and row tiles per wave
-  constexpr int P1 = 3 * kC * RW + 2 * DK * RW;                // phase-1 floats
-  constexpr int P2 = 2 * kC * KW + 3 * kC * RW;                // phase-2 floats
-  __shared__ float L[P1 > P2 ? P1 : P2];
-  __shared__ float Gs[kC], rsum[kC], csum[kC];
+__global__ __launch_bounds__(64 * NWF) void cbwd_final(RnnBwdArgs a, Scratch sc) {
+  using E = typename IO::elem;
+  constexpr int NH = NWF / 4, JT = 4 / NH;                    // wave halves, tiles per wave
+  constexpr int WR = DK / 4, WT = WR / 16;                    // dk rows and row tiles per wave
+  constexpr int CB = 32, BW = CB + LP;                        // phase-1 column block
+  constexpr int KW = DK + 16 / IO::kBytes;                    // K, Q rows in their input type
+  constexpr int P1 = (3 * kC + 2 * DK) * BW * 4;              // phase-1 bytes
+  constexpr int P2 = 2 * kC * KW * IO::kBytes + 2 * kC * RW * 4;
+  __shared__ __attribute__((aligned(16))) char L[P1 > P2 ? P1 : P2];
+  __shared__ float Gs[kC], rpart[NH][kC], cpart[4][kC];
   const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
   const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
-  // wave: row tile (and dk row group) qw of dM, dA (dQ^T, dK^T); half hw of the column
-  // (token) tiles: 2 hw and 2 hw + 1
   const int qw = wave & 3, hw = wave >> 2;
   const size_t cid = (size_t)x.bh * x.N + x.c;
   if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
@@ -614,46 +620,46 @@ __global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
   const float* dSg = a.scratch + sc.dS + cid * DK * DV;
   const float* Dg = a.scratch + sc.D + cid * kC * DV;
   const float* dXg = a.scratch + sc.dX + cid * kC * DV;
-  f32x4 dM[2], dA[2], dQT[WT][2], dKT[WT][2];
+  f32x4 dM[JT], dA[JT], dQT[WT][JT], dKT[WT][JT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < JT; ++i) {
     dM[i] = (f32x4)(0.f); dA[i] = (f32x4)(0.f);
 #pragma unroll
     for (int kt = 0; kt < WT; ++kt) { dQT[kt][i] = (f32x4)(0.f); dKT[kt][i] = (f32x4)(0.f); }
   }
-  float* dOs = L;
-  float* Ds = L + kC * RW;
-  float* dXs = L + 2 * kC * RW;
-  float* Ss = L + 3 * kC * RW;
-  float* dSs = Ss + DK * RW;
-  for (int cb0 = 0; cb0 < DV; cb0 += 64) {
+  float* dOs = reinterpret_cast<float*>(L);
+  float* Ds = dOs + kC * BW;
+  float* dXs = Ds + kC * BW;
+  float* Ss = dXs + kC * BW;
+  float* dSs = Ss + DK * BW;
+  for (int cb0 = 0; cb0 < DV; cb0 += CB) {
     __syncthreads();
-    load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
-    load_block<kC, 64>(Ds, Dg, DV, cb0);
-    load_block<kC, 64>(dXs, dXg, DV, cb0);
-    load_block<DK, 64>(Ss, Sg, DV, cb0);
-    load_block<DK, 64>(dSs, dSg, DV, cb0);
+    load_rows<IoF32, DV, CB>(dOs, a.dO, a, x, cb0);
+    load_block<kC, CB>(Ds, Dg, DV, cb0);
+    load_block<kC, CB>(dXs, dXg, DV, cb0);
+    load_block<DK, CB>(Ss, Sg, DV, cb0);
+    load_block<DK, CB>(dSs, dSg, DV, cb0);
     __syncthreads();
     const float gl = Gs[kC - 1];
-    for (int d = 0; d < 64; d += 4) {
-      // dM, dA tiles (qw, 2 hw + j): sum over the block's columns of dO D^T, dX D^T
-      const float o_a = dOs[(16 * qw + n) * RW + d + g4], x_a = dXs[(16 * qw + n) * RW + d + g4];
+    for (int d = 0; d < CB; d += 4) {
+      // dM, dA tiles (qw, JT hw + j): sum over the block's columns of dO D^T, dX D^T
+      const float o_a = dOs[(16 * qw + n) * BW + d + g4], x_a = dXs[(16 * qw + n) * BW + d + g4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float db = Ds[(16 * (2 * hw + j) + n) * RW + d + g4];
+      for (int j = 0; j < JT; ++j) {
+        const float db = Ds[(16 * (JT * hw + j) + n) * BW + d + g4];
         dM[j] = mf(o_a, db, dM[j]);
         dA[j] = mf(x_a, db, dA[j]);
       }
       // dQ^T += S diag(gamma) dO^T;  dK^T += -S (diag(gamma) dX)^T + dS (diag(w) D)^T
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = 16 * (2 * hw + j) + n;
+      for (int j = 0; j < JT; ++j) {
+        const int t = 16 * (JT * hw + j) + n;
         const float gt = __expf(Gs[t]), wt = __expf(gl - Gs[t]);
-        const float bo = gt * dOs[t * RW + d + g4], bx = -gt * dXs[t * RW + d + g4], bd = wt * Ds[t * RW + d + g4];
+        const float bo = gt * dOs[t * BW + d + g4], bx = -gt * dXs[t * BW + d + g4], bd = wt * Ds[t * BW + d + g4];
 #pragma unroll
         for (int kt = 0; kt < WT; ++kt) {
           const int row = WR * qw + 16 * kt + n;
-          const float sa = Ss[row * RW + d + g4], dsa = dSs[row * RW + d + g4];
+          const float sa = Ss[row * BW + d + g4], dsa = dSs[row * BW + d + g4];
           dQT[kt][j] = mf(sa, bo, dQT[kt][j]);
           dKT[kt][j] = mf(sa, bx, dKT[kt][j]);
           dKT[kt][j] = mf(dsa, bd, dKT[kt][j]);
@@ -662,50 +668,53 @@ __global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
     }
   }
   __syncthreads();
-  // phase 2: dM o Gamma, dA o Gamma and dM o M + dA o A in LDS; K and Q rows
-  float* Ks = L;
-  float* Qs = L + kC * KW;
-  float* dMG = L + 2 * kC * KW;
+  // phase 2: dM o Gamma and dA o Gamma in LDS, K and Q rows; the row and column sums of
+  // dM o M + dA o A by wave reductions
+  E* Ks = reinterpret_cast<E*>(L);
+  E* Qs = Ks + kC * KW;
+  float* dMG = reinterpret_cast<float*>(Qs + kC * KW);
   float* dAG = dMG + kC * RW;
-  float* dGG = dAG + kC * RW;
   const float* Ag = a.scratch + sc.A + cid * kC * kC;
   const float* Mg = a.scratch + sc.M + cid * kC * kC;
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < JT; ++j) {
+    float cs = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * qw + 4 * g4 + r, s = 16 * (2 * hw + j) + n;
+      const int t = 16 * qw + 4 * g4 + r, s = 16 * (JT * hw + j) + n;
       const float gam = s <= t ? __expf(Gs[t] - Gs[s]) : 0.f;
       const float dm = s <= t ? dM[j][r] : 0.f, da = s < t ? -dA[j][r] : 0.f;
       dMG[t * RW + s] = dm * gam;
       dAG[t * RW + s] = da * gam;
-      dGG[t * RW + s] = dm * Mg[t * kC + s] + da * Ag[t * kC + s];
+      const float gg = dm * Mg[t * kC + s] + da * Ag[t * kC + s];
+      rs[r] += gg;
+      cs += gg;
     }
-  load_rows<IO, DK, DK>(Ks, a.k, a, x, 0);
-  load_rows<IO, DK, DK>(Qs, a.q, a, x, 0);
-  __syncthreads();
-  if (threadIdx.x < kC) {                                   // row sums
-    float s = 0.f;
-    for (int j = 0; j < kC; ++j) s += dGG[threadIdx.x * RW + j];
-    rsum[threadIdx.x] = s;
-  } else if (threadIdx.x < 2 * kC) {                        // column sums
-    const int j = threadIdx.x - kC;
-    float s = 0.f;
-    for (int t = 0; t < kC; ++t) s += dGG[t * RW + j];
-    csum[j] = s;
+    cs += __shfl_xor(cs, 16, kWave);                        // over the four 4-row groups
+    cs += __shfl_xor(cs, 32, kWave);
+    if (g4 == 0) cpart[qw][16 * (JT * hw + j) + n] = cs;
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float v = row16_sum(rs[r]);                       // over the 16 columns of the row
+    if (n == 0) rpart[hw][16 * qw + 4 * g4 + r] = v;
+  }
+  load_rows_raw<IO, DK>(Ks, a.k, a, x);
+  load_rows_raw<IO, DK>(Qs, a.q, a, x);
+  __syncthreads();
   // dQ^T += K^T (dM o Gamma)^T;  dK^T += Q^T (dM o Gamma) + K^T (dA o Gamma)^T + K^T (dA o Gamma)
   for (int s0 = 0; s0 < kC; s0 += 4) {
     const int s = s0 + g4;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = 16 * (2 * hw + j) + n;
+    for (int j = 0; j < JT; ++j) {
+      const int t = 16 * (JT * hw + j) + n;
       const float mgT = dMG[t * RW + s], mg = dMG[s * RW + t];
       const float agT = dAG[t * RW + s], ag = dAG[s * RW + t];
 #pragma unroll
       for (int kt = 0; kt < WT; ++kt) {
         const int row = WR * qw + 16 * kt + n;
-        const float ka = Ks[s * KW + row], qa = Qs[s * KW + row];
+        const float ka = ldf(Ks, s * KW + row), qa = ldf(Qs, s * KW + row);
         dQT[kt][j] = mf(ka, mgT, dQT[kt][j]);
         dKT[kt][j] = mf(qa, mg, dKT[kt][j]);
         dKT[kt][j] = mf(ka, agT + ag, dKT[kt][j]);
@@ -713,10 +722,10 @@ __global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
     }
   }
   // dQ^T / dK^T tiles: lane (g4, n) holds dk rows WR qw + 16 kt + 4 g4 + r of token
-  // 16 (2 hw + j) + n
+  // 16 (JT hw + j) + n
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = 16 * (2 * hw + j) + n;
+  for (int j = 0; j < JT; ++j) {
+    const int t = 16 * (JT * hw + j) + n;
     if (t < x.Cc) {
       const size_t o = (((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DK;
 #pragma unroll
@@ -727,7 +736,6 @@ __global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
       }
     }
   }
-  __syncthreads();
   // dG, then dg = reverse cumulative sum over the real tokens; dbeta
   if (wave == 0) {
     const int t = lane;
@@ -739,10 +747,15 @@ __global__ __launch_bounds__(512) void cbwd_final(RnnBwdArgs a, Scratch sc) {
       dw += P[cb * 4 * kC + 2 * kC + t];
       dgC += P[cb * 4 * kC + 3 * kC];
     }
+    float rsum = 0.f, csum = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) rsum += rpart[h2][t];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) csum += cpart[q4][t];
     const bool real = t < x.Cc;
     const float G = Gs[t], GLr = Gs[kC - 1];
     const float wt = __expf(GLr - G);
-    float dG = real ? __expf(G) * dgam - wt * dw + rsum[t] - csum[t] : 0.f;
+    float dG = real ? __expf(G) * dgam - wt * dw + rsum - csum : 0.f;
     const float tail = wave_sum<64>(real ? wt * dw : 0.f);
     if (t == x.Cc - 1) dG += __expf(GLr) * dgC + tail;
     // reverse inclusive scan: dg_t = sum_{j >= t} dG_j
@@ -769,7 +782,7 @@ hipError_t launch_t(const RnnBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((cbwd_rev<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
   using CG = ColsGeom<IO, DK, DV>;
   hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / CG::CW), dim3(64 * CG::NW), 0, s, a, sc);
-  hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(512), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(64 * NWF), 0, s, a, sc);
   return hipGetLastError();
 }
 
