@@ -27,9 +27,10 @@
 // Five kernels, fp32 throughout (products on the fp32 matrix cores, 16x16x4):
 //   cbwd_prep   chunk-parallel: G, A, M, T' per chunk (T' by forward substitution);
 //   cbwd_fwd    sequential over chunks: the entering state of every chunk and D;
-//   cbwd_rev    sequential over chunks, from the end: dS_C of every chunk and dS0;
-//   cbwd_cols   chunk-parallel, 16 value columns per wave: dV, dX and the per-token
-//               partial sums of dbeta, dgamma, dw over those columns;
+//   cbwd_rev    sequential over chunks, from the end: dS_C of every chunk and dS0, and
+//               each chunk's K dS_C, dD and dX = dV;
+//   cbwd_cols   chunk-parallel, 16 value columns per wave: the per-token partial sums
+//               of dbeta, dgamma, dw over those columns;
 //   cbwd_final  chunk-parallel: dM, dA, dQ, dK, dG, dg, dbeta.
 // The state chains keep S (or dS) in matrix-core accumulators, 16 value columns per
 // wave; a product whose contraction index is held by an accumulator takes it in the
@@ -49,7 +50,7 @@ HAM_DEVICE f32x4 mf(float a, float b, f32x4 c) { return __builtin_amdgcn_mfma_f3
 
 // Scratch regions (floats), each 64-float aligned; see chunk_scratch_floats().
 struct Scratch {
-  size_t G, A, M, T, S, dS, D, dX, part, total;
+  size_t G, A, M, T, S, dS, D, dX, dD, KdS, part, total;
 };
 __host__ __device__ inline Scratch scratch_layout(int B, int H, int T, int DK, int DV) {
   auto up = [](size_t x) { return (x + 63) / 64 * 64; };
@@ -64,6 +65,8 @@ __host__ __device__ inline Scratch scratch_layout(int B, int H, int T, int DK, i
   s.dS = o;   o += up(BHN * DK * DV);
   s.D = o;    o += up(BHN * kC * DV);
   s.dX = o;   o += up(BHN * kC * DV);
+  s.dD = o;   o += up(BHN * kC * DV);
+  s.KdS = o;  o += up(BHN * kC * DV);
   s.part = o; o += up(BHN * (DV / 16) * 4 * kC);
   s.total = o;
   return s;
@@ -413,14 +416,15 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
     if (c > 0) fetch(c - 1);                                // in flight under this chunk's products
     const float GL = Gs[kC - 1], gC = __expf(GL);
     // dD = M^T dO + diag(w) K dS   (M^T upper triangular)
-    f32x4 dD[4];
+    f32x4 dD[4], kd[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      f32x4 kd = (f32x4)(0.f), md = (f32x4)(0.f);
+      f32x4 md = (f32x4)(0.f);
+      kd[tt] = (f32x4)(0.f);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) kd = mf(Ks[(16 * tt + n) * KW + 16 * rt + 4 * g4 + r], dS[rt][r], kd);
+        for (int r = 0; r < 4; ++r) kd[tt] = mf(Ks[(16 * tt + n) * KW + 16 * rt + 4 * g4 + r], dS[rt][r], kd[tt]);
 #pragma unroll
       for (int u = tt; u < 4; ++u)
 #pragma unroll
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * g4 + r;
-        dD[tt][r] = md[r] + __expf(GL - Gs[t]) * kd[r];
+        dD[tt][r] = md[r] + __expf(GL - Gs[t]) * kd[tt][r];
       }
     }
     // dX = T'^T dD   (T'^T upper triangular)
@@ -443,6 +447,22 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
       for (int u = tt; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dX[tt] = mf(Ts[(16 * u + 4 * g4 + r) * RW + 16 * tt + n], dD[u][r], dX[tt]);
+    }
+    // K dS_C, dD and dX of the chunk for the column kernel; dV = dX
+    {
+      float* dDg = a.scratch + sc.dD + cid * kC * DV;
+      float* dXg = a.scratch + sc.dX + cid * kC * DV;
+      float* kdg = a.scratch + sc.KdS + cid * kC * DV;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * tt + 4 * g4 + r;
+          dDg[(size_t)t * DV + col] = dD[tt][r];
+          dXg[(size_t)t * DV + col] = dX[tt][r];
+          kdg[(size_t)t * DV + col] = kd[tt][r];
+          if (t < x.Cc) a.dv[(((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DV + col] = dX[tt][r];
+        }
     }
     // dS <- gamma_C dS - K^T diag(gamma) dX + Q^T diag(gamma) dO
 #pragma unroll
@@ -467,41 +487,33 @@ __global__ __launch_bounds__(256) void cbwd_rev(RnnBwdArgs a, Scratch sc) {
     for (int r = 0; r < 4; ++r) a.dS0[((size_t)bh * DK + 16 * rt + 4 * g4 + r) * DV + col] = dS[rt][r];
 }
 
-// ---- cbwd_cols: dV, dX and per-token partial sums, 16 value columns per wave -----
-// grid (N, B*H, DV/CW), 64 CW/16 threads: a workgroup takes CW value columns (all of
-// them with bf16 inputs, whose K, Q and V rows stay bf16 in LDS; 64 with fp32 inputs),
-// so the chunk's K, Q, A, M and T' are staged once for its columns.  Partials over the
-// wave's columns: [0] U . R (dbeta), [1] dO . QS - dX . KS (dgamma), [2] K dS . D (dw);
-// [3][0] <S, dS> (dgamma_C).
+// ---- cbwd_cols: per-token partial sums over 16 value columns per wave -----------
+// grid (N, B*H, DV/64), 256 threads.  K dS_C, dD and dX come from the reverse chain;
+// this kernel forms KS, QS, A^T dX and A D and the partial sums over the wave's
+// columns: [0] U . R (dbeta), [1] dO . QS - dX . KS (dgamma), [2] K dS_C . D (dw);
+// [3][0] <S, dS_C> (dgamma_C).  K and Q rows stay in their input type in LDS, so two
+// workgroups share a CU.
 template <class IO, int DK, int DV>
-struct ColsGeom {
-  static constexpr int CW = IO::kBytes == 2 ? DV : 64, NW = CW / 16;
-};
-template <class IO, int DK, int DV>
-__global__ __launch_bounds__(512) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
+__global__ __launch_bounds__(256) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
   using E = typename IO::elem;
-  constexpr int CW = ColsGeom<IO, DK, DV>::CW, NW = ColsGeom<IO, DK, DV>::NW;
-  constexpr int KW = DK + 16 / IO::kBytes, VW = CW + 16 / IO::kBytes, OW = CW + LP, RT = DK / 16;
+  constexpr int KW = DK + 16 / IO::kBytes, VW = 64 + 16 / IO::kBytes, RT = DK / 16;
   __shared__ __attribute__((aligned(16))) E Ks[kC * KW];
   __shared__ __attribute__((aligned(16))) E Qs[kC * KW];
   __shared__ __attribute__((aligned(16))) E Vs[kC * VW];
-  __shared__ float As[kC * RW], Ms[kC * RW], Ts[kC * RW], dOs[kC * OW], Gs[kC];
+  __shared__ float As[kC * RW], dOs[kC * RW], Gs[kC];
   const Ctx x = ctx(a, blockIdx.y, blockIdx.x);
   const int lane = lane_id(), wave = threadIdx.x >> 6, g4 = lane >> 4, n = lane & 15;
-  const int cb0 = blockIdx.z * CW, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
+  const int cb0 = blockIdx.z * 64, col = cb0 + 16 * wave + n, cw = 16 * wave + n;
   const size_t cid = (size_t)x.bh * x.N + x.c;
   load_rows_raw<IO, DK>(Ks, a.k, a, x);
   load_rows_raw<IO, DK>(Qs, a.q, a, x);
+  load_cols_raw<IO, DV, 64>(Vs, a.v, a, x, cb0);
+  load_rows<IoF32, DV, 64>(dOs, a.dO, a, x, cb0);
   load_mat(As, a.scratch + sc.A + cid * kC * kC);
-  load_mat(Ms, a.scratch + sc.M + cid * kC * kC);
-  load_mat(Ts, a.scratch + sc.T + cid * kC * kC);
-  load_cols_raw<IO, DV, CW>(Vs, a.v, a, x, cb0);
-  load_rows<IoF32, DV, CW>(dOs, a.dO, a, x, cb0);
   if (threadIdx.x < kC) Gs[threadIdx.x] = a.scratch[sc.G + cid * kC + threadIdx.x];
   const float* Sg = a.scratch + sc.S + cid * DK * DV;
   const float* dSg = a.scratch + sc.dS + cid * DK * DV;
-  const float* Dg = a.scratch + sc.D + cid * kC * DV;
-  f32x4 S[RT], dS[RT], D[4];
+  f32x4 S[RT], D[4], dD[4], dX[4], kd[4];
   float sds = 0.f;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -509,55 +521,40 @@ __global__ __launch_bounds__(512) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
     for (int r = 0; r < 4; ++r) {
       const size_t o = (size_t)(16 * rt + 4 * g4 + r) * DV + col;
       S[rt][r] = Sg[o];
-      dS[rt][r] = dSg[o];
-      sds = fmaf(S[rt][r], dS[rt][r], sds);
+      sds = fmaf(S[rt][r], dSg[o], sds);
     }
+  {
+    const float* Dg = a.scratch + sc.D + cid * kC * DV;
+    const float* dDg = a.scratch + sc.dD + cid * kC * DV;
+    const float* dXg = a.scratch + sc.dX + cid * kC * DV;
+    const float* kdg = a.scratch + sc.KdS + cid * kC * DV;
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) D[tt][r] = Dg[(size_t)(16 * tt + 4 * g4 + r) * DV + col];
+      for (int r = 0; r < 4; ++r) {
+        const size_t o = (size_t)(16 * tt + 4 * g4 + r) * DV + col;
+        D[tt][r] = Dg[o];
+        dD[tt][r] = dDg[o];
+        dX[tt][r] = dXg[o];
+        kd[tt][r] = kdg[o];
+      }
+  }
   __syncthreads();
-  const float GL = Gs[kC - 1];
-  f32x4 Y[4], QS[4], KdS[4];
+  f32x4 Y[4], QS[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    Y[tt] = (f32x4)(0.f); QS[tt] = (f32x4)(0.f); KdS[tt] = (f32x4)(0.f);
+    Y[tt] = (f32x4)(0.f); QS[tt] = (f32x4)(0.f);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kcol = 16 * rt + 4 * g4 + r;
-        const float ka = ldf(Ks, (16 * tt + n) * KW + kcol);
-        Y[tt] = mf(ka, S[rt][r], Y[tt]);
-        KdS[tt] = mf(ka, dS[rt][r], KdS[tt]);
+        Y[tt] = mf(ldf(Ks, (16 * tt + n) * KW + kcol), S[rt][r], Y[tt]);
         QS[tt] = mf(ldf(Qs, (16 * tt + n) * KW + kcol), S[rt][r], QS[tt]);
       }
   }
-  // dD = M^T dO + diag(w) K dS;  dX = T'^T dD;  U = dD - A^T dX;  R = X - A D
-  f32x4 dD[4], dX[4];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    f32x4 md = (f32x4)(0.f);
-#pragma unroll
-    for (int u = tt; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = 16 * u + 4 * g4 + r;
-        md = mf(Ms[s * RW + 16 * tt + n], dOs[s * OW + cw], md);
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dD[tt][r] = md[r] + __expf(GL - Gs[16 * tt + 4 * g4 + r]) * KdS[tt][r];
-  }
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    dX[tt] = (f32x4)(0.f);
-#pragma unroll
-    for (int u = tt; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dX[tt] = mf(Ts[(16 * u + 4 * g4 + r) * RW + 16 * tt + n], dD[u][r], dX[tt]);
-  }
+  // U = dD - A^T dX;  R = X - A D with X = V - diag(gamma) KS
   float pb[16], pg[16], pw[16];
-  float* dXg = a.scratch + sc.dX + cid * kC * DV;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f32x4 atdx = (f32x4)(0.f), ad = (f32x4)(0.f);
@@ -575,16 +572,14 @@ __global__ __launch_bounds__(512) void cbwd_cols(RnnBwdArgs a, Scratch sc) {
       const float X = ldf(Vs, t * VW + cw) - __expf(Gs[t]) * Y[tt][r];
       const float U = dD[tt][r] - atdx[r], R = X - ad[r];
       pb[4 * tt + r] = U * R;
-      pg[4 * tt + r] = dOs[t * OW + cw] * QS[tt][r] - dX[tt][r] * Y[tt][r];
-      pw[4 * tt + r] = KdS[tt][r] * D[tt][r];
-      dXg[(size_t)t * DV + col] = dX[tt][r];
-      if (t < x.Cc) a.dv[(((size_t)x.b * a.T + x.t0 + t) * a.H + x.h) * DV + col] = dX[tt][r];
+      pg[4 * tt + r] = dOs[t * RW + cw] * QS[tt][r] - dX[tt][r] * Y[tt][r];
+      pw[4 * tt + r] = kd[tt][r] * D[tt][r];
     }
   }
   // lane (g4, n) receives the column sums of value index n: token 16 (n/4) + 4 g4 + n%4
   const float sb = row16_transpose_sum(pb, n), sg = row16_transpose_sum(pg, n), sw = row16_transpose_sum(pw, n);
   const int tok = 16 * (n >> 2) + 4 * g4 + (n & 3);
-  float* P = a.scratch + sc.part + (cid * (DV / 16) + blockIdx.z * NW + wave) * 4 * kC;
+  float* P = a.scratch + sc.part + (cid * (DV / 16) + blockIdx.z * 4 + wave) * 4 * kC;
   P[tok] = sb;
   P[kC + tok] = sg;
   P[2 * kC + tok] = sw;
@@ -780,8 +775,7 @@ hipError_t launch_t(const RnnBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((cbwd_prep<IO, DK>), dim3(N, BH), dim3(256), 0, s, a, sc);
   hipLaunchKernelGGL((cbwd_fwd<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
   hipLaunchKernelGGL((cbwd_rev<IO, DK, DV>), dim3(BH, DV / 64), dim3(256), 0, s, a, sc);
-  using CG = ColsGeom<IO, DK, DV>;
-  hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / CG::CW), dim3(64 * CG::NW), 0, s, a, sc);
+  hipLaunchKernelGGL((cbwd_cols<IO, DK, DV>), dim3(N, BH, DV / 64), dim3(256), 0, s, a, sc);
   hipLaunchKernelGGL((cbwd_final<IO, DK, DV>), dim3(N, BH), dim3(64 * NWF), 0, s, a, sc);
   return hipGetLastError();
 }
