@@ -383,12 +383,16 @@ size_t ham_rnn_backward_workspace_size(const ham_dims *dims);
  *   p_t = S_{t-1}^T k_t, r_t = v_t - alpha_t p_t, S_t = alpha_t S_{t-1} + beta_t k_t r_t^T,
  *   o_rnn_t = S_t^T q_t,
  * given dO = dL/do_rnn and dS_T = dL/dS_T, the gradients with respect to q, k, v,
- * beta, g and the entering state (reverse mode of that recurrence, fp32).  The
- * routing decision passes no gradient; the gradient of the mix (norms, gates) and of
- * the attention (ham_attention_backward) are separate.
+ * beta, g and the entering state (reverse mode of that recurrence, fp32).  It runs
+ * chunked ([HAM] App. A.1: the chunked kernel also serves the backward pass): reverse
+ * mode of the 64-token chunk form of the forward state pass, a forward and a reverse
+ * chain over the chunks and chunk-parallel gradient terms; with HAM_FORCE_RECURRENT
+ * in dims->flags, token by token instead.  The routing decision passes no gradient;
+ * the gradient of the mix (norms, gates) and of the attention
+ * (ham_attention_backward) are separate.
  *
- *   dims               B, T, H, dk, dv (64 or 128 each), io_dtype; other fields
- *                      are not read.
+ *   dims               B, T, H, dk, dv (64 or 128 each), io_dtype, flags
+ *                      (HAM_FORCE_RECURRENT or 0); other fields are not read.
  *   q, k, v            [B,T,H,dk|dv] io dtype: the forward's RNN inputs.
  *   beta, g            [B,T,H] fp32.
  *   S0                 [B,H,dk,dv] fp32 entering state of the forward, or NULL (0).
@@ -396,9 +400,12 @@ size_t ham_rnn_backward_workspace_size(const ham_dims *dims);
  *   dS_T               [B,H,dk,dv] fp32 or NULL (0).
  *   dq, dk, dv         [B,T,H,dk|dv] fp32 out;  dbeta, dg [B,T,H] fp32 out;
  *   dS0                [B,H,dk,dv] fp32 out: dL/dS0.
- *   ws, ws_bytes       scratch of ham_rnn_backward_workspace_size(dims) bytes: the
- *                      state at every 64-token chunk start and one chunk's states
- *                      per 16 state columns (about 2 x T/64 + 64 states per head).
+ *   ws, ws_bytes       scratch of ham_rnn_backward_workspace_size(dims) bytes
+ *                      (the same flags): chunked, the entering state and its
+ *                      gradient at every chunk and per-chunk matrices (about
+ *                      2 x T/64 states and (4 d_v + 192) T floats per head);
+ *                      token by token, the state at every chunk start and one
+ *                      chunk's states per 16 state columns.
  * Errors: HAM_EINVAL, HAM_EUNSUPPORTED (dk or dv not 64/128), HAM_EWORKSPACE,
  * HAM_EHIP.
  */
