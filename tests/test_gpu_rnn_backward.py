@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import attention_sequence_mixing_amd as ham
-from attention_sequence_mixing_amd.inputs import make_inputs
+from attention_sequence_mixing_amd.inputs import LAYER, make_inputs, make_workload
 from parity import np_of, rel_err_slices, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -53,6 +53,32 @@ def test_rnn_backward(B, T, H, dk, dv, dtype, s0, dst, recurrent):
     errs["dS0"] = _rel(np_of(got["dS0"]), ref["dS0"], 1)
     print("   errors", {k: f"{v:.2e}" for k, v in errs.items()})
     assert all(v < TOL for v in errs.values()), errs
+
+
+def test_rnn_backward_layer_shape_sampled_heads():
+    """The chunked gradients at the headline layer shape (B 8, T 4096, H 16, d 128, bf16
+    inputs, dO and dS_T ~ N(0,1)), every head computed on the GPU; three (b, h) slices
+    compared with the oracle, which runs on those slices alone (heads are independent)."""
+    w = LAYER
+    inp = make_workload(w)
+    rng = np.random.default_rng(77)
+    dO = rng.standard_normal((w.B, w.T, w.H, w.d)).astype(np.float32)
+    dS_T = rng.standard_normal((w.B, w.H, w.d, w.d)).astype(np.float32)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    print(f"rnn backward at the layer shape: B={w.B} T={w.T} H={w.H} d={w.d}", flush=True)
+    got = ham.ham_rnn_backward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(dO).to(DEV),
+                               dS_T=torch.from_numpy(dS_T).to(DEV))
+    torch.cuda.synchronize()
+    got = {n: np_of(x) for n, x in got.items()}
+    for b, h in [(0, 0), (3, 7), (7, 15)]:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        ref = oracle.rnn_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["g"]),
+                                  sl(dO), dS_T=np.ascontiguousarray(dS_T[b:b + 1, h:h + 1]))
+        errs = {n: _rel(sl(got[n]), ref[n], 2) for n in ("dq", "dk", "dv")}
+        errs.update({n: _rel(sl(got[n])[..., None], ref[n][..., None], 2) for n in ("dbeta", "dg")})
+        errs["dS0"] = _rel(got["dS0"][b:b + 1, h:h + 1], ref["dS0"], 1)
+        print(f"   (b, h) = ({b}, {h}) errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+        assert all(v < TOL for v in errs.values()), (b, h, errs)
 
 
 def test_rnn_backward_rejects_other_head_sizes():
