@@ -123,8 +123,8 @@ HAM_DEVICE float row16_transpose_sum(const float (&x)[16], int n) {
 }
 
 // ---- rotary position embedding ------------------------------------------------------
-// "Hybrid Associative Memories" §4: RoPE with base 500K on all inputs to
-// self-attention (RoFormer, Su et al.): pair (x_2i, x_2i+1) of a d-dimensional vector
+// "Hybrid Associative Memories" §4 model setup: a rotary embedding of base 500000 turns
+// the attention path's queries and keys (RoFormer, Su et al.): pair (x_2i, x_2i+1) of a d-dimensional vector
 // at absolute position pos turns by pos * base^(-2i/d).  The angle is formed and
 // reduced to [-pi, pi] in double precision (at positions in the millions a float
 // angle would be off by a good fraction of a radian), then cos and sin are rounded

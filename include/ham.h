@@ -105,8 +105,8 @@ typedef struct {
     int t0;           /* absolute position of token 0 (recorded in pos)          */
     float rope_base;  /* 0, or the base of a rotary position embedding (RoPE)
                          applied to the attention-path query and key at their
-                         absolute positions: [HAM] §4 uses base 500000 for all
-                         inputs to self-attention.  Pairs of consecutive elements
+                         absolute positions ([HAM] §4 model setup: base 500000
+                         on the attention path).  Pairs of consecutive elements
                          (x_2i, x_2i+1) turn by pos * rope_base^(-2i/dk) (RoFormer);
                          the cache then holds rotated keys.  The RNN path is not
                          rotated.  Angles are formed and reduced in double
