@@ -381,6 +381,31 @@ HAM_DEVICE short4v lds_read_tr16(const char* base, int byte_off) {
 #endif
 }
 
+// Direct-to-LDS load of 16 bytes per lane at voff + soff of a buffer of range_bytes
+// from base (bytes at or past the range read as zero; the scalar offset is part of
+// the range check and does not move the LDS address).
+HAM_DEVICE void buffer_to_lds_so(const void* base, int range_bytes, int voff, int soff, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                               range_bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#else
+  (void)base; (void)range_bytes; (void)voff; (void)soff; (void)lds;
+#endif
+}
+
+// Scheduling pattern: NM matrix products in L groups, one vector-memory instruction
+// after each group (the first NM mod L groups hold one product more).
+template <int NM, int L, int K = 0>
+HAM_DEVICE void interleave_loads() {
+  if constexpr (K < L) {
+    constexpr int n = NM / L + (K < NM % L ? 1 : 0);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, 0);
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    interleave_loads<NM, L, K + 1>();
+  }
+}
+
 // Chunk slot swizzles of the K and V tiles (D = row length in elements).
 template <int D>
 HAM_DEVICE int swz_k(int r) { return r & (D / 8 - 1); }
@@ -464,8 +489,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // (K rows first, then V rows); wave w issues i = 4k + w.  Lane l writes 16 bytes at
   // i*1024 + 16*l, which hold chunk (slot ^ swizzle) of its tile row.  The swizzle
   // repeats every PK (PV) instructions, a divisor of 4, so one per-lane offset per
-  // tensor serves all of a wave's loads; the rest of each instruction's offset goes
-  // into the descriptor base.
+  // tensor serves all of a wave's loads, each adding a constant step.
   static_assert(KI % NWV == 0, "K and V loads must not share a wave step");
   constexpr int PK = (DK / 8) * RBK / 1024 > 1 ? (DK / 8) * RBK / 1024 : 1;
   constexpr int PV1 = (DV1 / 16) * RB1 / 1024 > 1 ? (DV1 / 16) * RB1 / 1024 : 1;
@@ -487,23 +511,41 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       ldV2 = r2 * RBV + RB1 + ((((p2 % RB2) >> 4) ^ swz_v<DV2>(r2)) << 4);
     }
   }
-  auto issue_tile = [&](int it, char* st) {
+  // One descriptor per tensor and tile (base: the tile's first row; range: its rows
+  // still visible to the block).  An instruction's place in the tile goes into the
+  // scalar offset, which the range check includes, so rows past the last visible key
+  // read as zero; the wave's share of the offset is folded into the per-lane offsets.
+  ldK += (wave - jK) * 1024;
+  ldV1 += (wave - jV1) * (1024 / RB1) * RBV;
+  if constexpr (DV2 > 0) ldV2 += (wave - jV2) * (1024 / RB2) * RBV;
+  // load k (of LPW) of this wave for tile it into stage st; woff = 1024 * wave (the
+  // caller hides its value from the compiler, which otherwise keeps every load's LDS
+  // address in a register of its own and runs out of scalar registers)
+  auto issue_load = [&](int k, int it, char* st, int woff) {
     const int c0 = it * BN;
-    const int rows = nhi - c0;                             // > 0 for every issued tile
-#pragma unroll
-    for (int k = 0; k < LPW; ++k) {
-      if (k < KI / NWV) {
-        const int i = k * NWV + wave, sh = (i - jK) * 1024;
-        buffer_to_lds(Kh + (size_t)c0 * RBK + sh, max(rows * RBK - sh, 0), ldK, st + i * 1024);
-      } else if (k < (KI + VI1) / NWV) {
-        // part 1 instruction i covers LDS rows from (i * 1024 / RB1) on
-        const int i = (k - KI / NWV) * NWV + wave, sh = (i - jV1) * (1024 / RB1) * RBV;
-        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV1, st + KB + i * 1024);
-      } else {
-        const int i = (k - (KI + VI1) / NWV) * NWV + wave, sh = (i - jV2) * (1024 / (RB2 ? RB2 : 1)) * RBV;
-        buffer_to_lds(Vh + (size_t)c0 * RBV + sh, max(rows * RBV - sh, 0), ldV2, st + V2OFF + i * 1024);
-      }
+    const int rows = min(nhi - c0, BN);                    // > 0 for every issued tile
+    if (k < KI / NWV) {
+      buffer_to_lds_so(Kh + (size_t)c0 * RBK, rows * RBK, ldK, k * NWV * 1024, st + woff + k * NWV * 1024);
+    } else if (k < (KI + VI1) / NWV) {
+      // part 1 instruction i = kk * NWV + wave covers LDS rows from (i * 1024 / RB1) on
+      const int kk = k - KI / NWV;
+      buffer_to_lds_so(Vh + (size_t)c0 * RBV, rows * RBV, ldV1, kk * NWV * (1024 / RB1) * RBV,
+                       st + KB + woff + kk * NWV * 1024);
+    } else {
+      const int kk = k - (KI + VI1) / NWV;
+      buffer_to_lds_so(Vh + (size_t)c0 * RBV, rows * RBV, ldV2, kk * NWV * (1024 / (RB2 ? RB2 : 1)) * RBV,
+                       st + V2OFF + woff + kk * NWV * 1024);
     }
+  };
+  auto opaque_woff = [&]() {
+    int w = wave * 1024;
+    asm volatile("" : "+s"(w));
+    return w;
+  };
+  auto issue_tile = [&](int it, char* st) {
+    const int woff = opaque_woff();
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) issue_load(k, it, st, woff);
   };
 
   const float sl2 = a.scale * kLog2e;
@@ -567,8 +609,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   if (it0 < ntiles) issue_tile(it0, stage0);
 
   f32x4 st[QT][NKT];
-  // S^T = K Q^T for the tile in `stage`
-  auto do_scores = [&](const char* Kt) {
+  // S^T = K Q^T for the tile in `Kt`.  With `load` set, the loads of tile `itn` into
+  // stage `nx` go out between the products (about one per NM / LPW of them), so the
+  // texture path takes them spread over the phase rather than all at once after the
+  // barrier, where the waves stalled on their issue.
+  auto do_scores = [&](const char* Kt, bool load, char* nx, int itn) {
+    constexpr int NM = KSD * NKT * QT;                     // products of the phase
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -582,6 +628,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
         for (int qt = 0; qt < QT; ++qt)
           st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
       }
+    if (load) {
+      const int woff = opaque_woff();
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) issue_load(k, itn, nx, woff);
+      // order: the fragment reads, then the products in LPW groups, a load after each
+      __builtin_amdgcn_sched_group_barrier(0x100, KSD * NKT, 0);
+      interleave_loads<NM, LPW>();
+    }
   };
   // keys at or past a query's visible count get -inf
   auto do_mask = [&](int c0) {
@@ -716,16 +770,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       buffer_to_lds(base, range, r * rstride + c * 16, st + wave * OWB + j * 1024);
     }
   };
-  auto step = [&](int it, char* cur, char* nxt) {
+  auto step = [&](int it, char* cur, char* nxt, bool last) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < ntiles) {
-      issue_tile(it + 1, nxt);
-    } else if (kOrnnLds && a.ornn_bf16) {
+    if (last && kOrnnLds && a.ornn_bf16) {
       issue_ornn(nxt);
       ornn_st = nxt;
     }
-    do_scores(cur);
+    do_scores(cur, !last, nxt, it + 1);
     do_mask(it * BN);
     // the first tile is exact; with document masks, every tile in which a row meets
     // its first visible key is (the row has no running maximum before it)
@@ -748,7 +800,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       }
       if (__any(over)) {
         exact = true;
-        do_scores(cur);
+        do_scores(cur, false, nxt, 0);
         do_mask(it * BN);
       } else {
 #pragma unroll
@@ -758,9 +810,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     if (exact) do_exact();
     do_pv(cur);
   };
-  for (int it = it0; it < ntiles; it += 2) {
-    step(it, stage0, stage1);
-    if (it + 1 < ntiles) step(it + 1, stage1, stage0);
+  // tile it sits in stage (it - it0) mod 2; the last tile's step loads no tile.  The
+  // loop body holds only steps that load (a choice inside it would let the compiler
+  // share the products of both kinds and leave the loads in a block of their own).
+  int it = it0;
+  for (; it + 2 < ntiles; it += 2) {
+    step(it, stage0, stage1, false);
+    step(it + 1, stage1, stage0, false);
+  }
+  if (it + 1 < ntiles) {
+    step(it, stage0, stage1, false);
+    step(it + 1, stage1, stage0, true);
+  } else if (it < ntiles) {
+    step(it, stage0, stage1, true);
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
