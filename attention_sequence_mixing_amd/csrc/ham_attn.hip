@@ -762,7 +762,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   auto issue_ornn = [&](char* st) {
     const int rstride = a.H * DV * 2;
     const char* base = reinterpret_cast<const char*>(a.o_rnn32) + (((size_t)b * a.T + qb0) * a.H + h) * DV * 2;
-    const int range = max(0, min(a.T - qb0, BM)) * rstride;   // rows past T read zero
+    // rows past T read zero (kept in a scalar register: a clamp the compiler forms on the
+    // vector unit would make the descriptor look divergent and wrap each load in a loop)
+    const int range = __builtin_amdgcn_readfirstlane(max(0, min(a.T - qb0, BM)) * rstride);
 #pragma unroll
     for (int j = 0; j < OCH / 2; ++j) {
       const int r = wave * BMW + j * (64 / OCH) + lane / OCH;
@@ -826,70 +828,146 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: normalise, mix with the RNN readout, store ----------------------
-  if (kOrnnLds && ornn_st) __builtin_amdgcn_s_waitcnt(0);   // this wave's readout rows are in LDS
+  // Straight-line per source, so that all of a wave's reads go out before the first
+  // use; reciprocals and reciprocal square roots by the hardware instructions (about
+  // one unit in the last place of fp32, far below the bf16 rounding of the outputs).
+  float inv_l[QT];
+  size_t tt[QT];
+  bool tvalid[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = l_run[qt];                       // full row sum in every lane
-    const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int t = tq[qt];
-    const bool tvalid = t < a.T;
-    const size_t tt = ((size_t)b * a.T + (tvalid ? t : 0)) * a.H + h;
-    if (a.okv32) {
-      // KV heads of another geometry than the RNN's: the readout alone, mixed later
-      if (tvalid) {
+    inv_l[qt] = (l_run[qt] > 0.f) ? __builtin_amdgcn_rcpf(l_run[qt]) : 0.f;   // row sum in every lane
+    tvalid[qt] = tq[qt] < a.T;
+    tt[qt] = ((size_t)b * a.T + (tvalid[qt] ? tq[qt] : 0)) * a.H + h;
+  }
+  if (a.okv32) {
+    // KV heads of another geometry than the RNN's: the readout alone, mixed later
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+      if (tvalid[qt]) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(a.okv32 + tt * DV + dt * 16 + 4 * g) = acc[qt][dt] * inv_l;
+          *reinterpret_cast<f32x4*>(a.okv32 + tt[qt] * DV + dt * 16 + 4 * g) = acc[qt][dt] * inv_l[qt];
       }
-      continue;
-    }
-    float okv[DT][4], orn[DT][4];
-    float ssk = 0.f, ssr = 0.f;
+    return;
+  }
+  float orn[QT][DT][4];
+  if (kOrnnLds && ornn_st) {
+    __builtin_amdgcn_s_waitcnt(0);                       // this wave's readout rows are in LDS
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 r4v;
-      if (kOrnnLds && ornn_st) {
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
         // row 16 qt + n of this wave's rows; columns dt*16 + 4g .. +3 are half of chunk 2dt + g/2
         const int rr = 16 * qt + qn;
         const int c = (2 * dt + (g >> 1)) ^ ((wave * BMW + rr) & (OCH - 1));
         const u16x4 x = *reinterpret_cast<const u16x4*>(ornn_st + wave * OWB + rr * (DV * 2) + c * 16 + (g & 1) * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r4v[i] = bf16_to_f32(x[i]);
-      } else if (a.ornn_bf16) {
-        const u16x4 x = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(a.o_rnn32) +
-                                                         tt * DV + dt * 16 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r4v[i] = bf16_to_f32(x[i]);
-      } else {
-        r4v = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt * DV + dt * 16 + 4 * g);
+        for (int i = 0; i < 4; ++i) orn[qt][dt][i] = bf16_to_f32(x[i]);
       }
+  } else if (a.ornn_bf16) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u16x4 x = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(a.o_rnn32) +
+                                                         tt[qt] * DV + dt * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orn[qt][dt][i] = bf16_to_f32(x[i]);
+      }
+  } else {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(a.o_rnn32 + tt[qt] * DV + dt * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orn[qt][dt][i] = x[i];
+      }
+  }
+  // With the readout rows in LDS, the bf16 results of each wave go over its own rows
+  // there, in the layout they were read in, and leave as whole rows (16 bytes per
+  // lane, four 256-byte rows per instruction); else 8 bytes per lane from registers.
+  const bool staged = kOrnnLds && ornn_st;
+  auto stage_put = [&](int qt, int dt, const float (&x)[4]) {
+    // row 16 qt + n of this wave's rows; columns dt*16 + 4g .. +3 are half of chunk 2dt + g/2
+    const int rr = 16 * qt + qn;
+    const int c = (2 * dt + (g >> 1)) ^ ((wave * BMW + rr) & (OCH - 1));
+    u16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(x[i]);
+    *reinterpret_cast<u16x4*>(const_cast<char*>(ornn_st) + wave * OWB + rr * (DV * 2) + c * 16 + (g & 1) * 8) = v;
+  };
+  auto stage_store = [&](void* dst) {
+    constexpr int RPI = 64 / OCH, NI = BMW / RPI;          // rows per instruction, instructions
+    const int cc = lane % OCH;
+    u16x8 v[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {                         // all reads before the first store
+      const int r = j * RPI + lane / OCH;
+      const int c = cc ^ ((wave * BMW + r) & (OCH - 1));
+      v[j] = *reinterpret_cast<const u16x8*>(ornn_st + wave * OWB + r * (DV * 2) + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int t = qb0 + wave * BMW + j * RPI + lane / OCH;
+      if (t < a.T)
+        *reinterpret_cast<u16x8*>(static_cast<char*>(dst) + (((size_t)b * a.T + t) * a.H + h) * (DV * 2) + cc * 16) = v[j];
+    }
+  };
+  float okv[QT][DT][4];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float ssk = 0.f, ssr = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        okv[dt][i] = acc[qt][dt][i] * inv_l;
-        orn[dt][i] = r4v[i];
-        ssk += okv[dt][i] * okv[dt][i];
-        ssr += orn[dt][i] * orn[dt][i];
+        okv[qt][dt][i] = acc[qt][dt][i] * inv_l[qt];
+        ssk += okv[qt][dt][i] * okv[qt][dt][i];
+        ssr += orn[qt][dt][i] * orn[qt][dt][i];
       }
-    }
     ssk += __shfl_xor(ssk, 16, kWave);
     ssk += __shfl_xor(ssk, 32, kWave);
     ssr += __shfl_xor(ssr, 16, kWave);
     ssr += __shfl_xor(ssr, 32, kWave);
-    if (!tvalid) continue;
-    const float gr = a.gate_rnn ? a.gate_rnn[tt] : 1.f;
-    const float gk = a.gate_kv ? a.gate_kv[tt] : 1.f;
-    const float ir = gr / sqrtf(ssr / (float)DV + a.eps);
-    const float ik = gk / sqrtf(ssk / (float)DV + a.eps);
+    if (!staged && !tvalid[qt]) continue;
+    const float gr = a.gate_rnn ? a.gate_rnn[tt[qt]] : 1.f;
+    const float gk = a.gate_kv ? a.gate_kv[tt[qt]] : 1.f;
+    const float ir = gr * __builtin_amdgcn_rsqf(ssr * (1.f / DV) + a.eps);
+    const float ik = gk * __builtin_amdgcn_rsqf(ssk * (1.f / DV) + a.eps);
     uint16_t* o = static_cast<uint16_t*>(a.o);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       float y[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = orn[dt][i] * ir + okv[dt][i] * ik;
-      const size_t off = tt * DV + dt * 16 + 4 * g;
-      IoBF16::store4(o, off, y);
-      if (a.o_kv) IoBF16::store4(static_cast<uint16_t*>(a.o_kv), off, okv[dt]);
-      if (a.o_rnn) IoBF16::store4(static_cast<uint16_t*>(a.o_rnn), off, orn[dt]);
+      for (int i = 0; i < 4; ++i) y[i] = orn[qt][dt][i] * ir + okv[qt][dt][i] * ik;
+      if (staged) {
+        stage_put(qt, dt, y);
+      } else {
+        const size_t off = tt[qt] * DV + dt * 16 + 4 * g;
+        IoBF16::store4(o, off, y);
+        if (a.o_kv) IoBF16::store4(static_cast<uint16_t*>(a.o_kv), off, okv[qt][dt]);
+        if (a.o_rnn) IoBF16::store4(static_cast<uint16_t*>(a.o_rnn), off, orn[qt][dt]);
+      }
+    }
+  }
+  if (staged) {
+    // each wave reads back only what it wrote (LDS operations of a wave stay in order)
+    stage_store(a.o);
+    if (a.o_kv) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) stage_put(qt, dt, okv[qt][dt]);
+      stage_store(a.o_kv);
+    }
+    if (a.o_rnn) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) stage_put(qt, dt, orn[qt][dt]);
+      stage_store(a.o_rnn);
     }
   }
 }
