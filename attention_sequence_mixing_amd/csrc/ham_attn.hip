@@ -394,6 +394,15 @@ HAM_DEVICE void buffer_to_lds_so(const void* base, int range_bytes, int voff, in
 #endif
 }
 
+// A wave-uniform pointer pinned to scalar registers (a buffer descriptor built from
+// vector registers makes the compiler wrap each load in a loop over lanes).
+HAM_DEVICE const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Scheduling pattern: NM matrix products in L groups, one vector-memory instruction
 // after each group (the first NM mod L groups hold one product more).
 template <int NM, int L, int K = 0>
@@ -444,11 +453,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   const int g = lane >> 4, qn = lane & 15;
   const int nqb = (a.T + BM - 1) / BM;
   // global longest-first: all heads' last query block first
+  // (the integer divisions run on the vector unit; the results are pinned to scalar
+  // registers so that the buffer descriptors built from them stay scalar)
   const int lin = blockIdx.x;
   const int nbh = gridDim.x / nqb;
-  const int bh = lin % nbh;
-  const int qb = nqb - 1 - (lin / nbh);
-  const int b = bh / a.H, h = bh % a.H;
+  const int bh = __builtin_amdgcn_readfirstlane(lin % nbh);
+  const int qb = __builtin_amdgcn_readfirstlane(nqb - 1 - (lin / nbh));
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.H), h = __builtin_amdgcn_readfirstlane(bh % a.H);
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const char* Kh = static_cast<const char*>(a.Kc) + (size_t)bh * a.cap * RBK;
@@ -459,6 +470,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   const int nlo = ntok[qb0];
   const int nhi = ntok[min(a.T - 1, qb0 + BM - 1)];
 
+  // The query fragments carry the logit scale in log2 units (one more bf16 rounding of
+  // each query element, the size of the rounding the probabilities get anyway), so the
+  // products give scaled logits directly.
+  const float sl2 = a.scale * kLog2e;
   int tq[QT], nq[QT];
   bf16x8 qf[QT][KSD];
 #pragma unroll
@@ -467,23 +482,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     const bool ok = tq[qt] < a.T;
     nq[qt] = ok ? ntok[tq[qt]] : 0;
     const size_t tok = ((size_t)b * a.T + (ok ? tq[qt] : 0)) * a.H + h;
-    // with a rotary table the query is turned at its position (consecutive pairs)
-    const float2* rrow = a.rope ? a.rope + (size_t)(ok ? tq[qt] : 0) * (DK / 2) : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      u16x8 x = *reinterpret_cast<const u16x8*>(qp + tok * DK + ks * 32 + 8 * g);
-      if (rrow) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
-          rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
-          x[2 * j] = f32_to_bf16(x0);
-          x[2 * j + 1] = f32_to_bf16(x1);
-        }
-      }
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int ks = 0; ks < KSD; ++ks)
+      qf[qt][ks] = *reinterpret_cast<const bf16x8*>(qp + tok * DK + ks * 32 + 8 * g);
   }
+  // The query fragments are turned and scaled after the first tile's loads have gone
+  // out (work on them waits for their loads).
+  auto prep_queries = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      // with a rotary table the query is turned at its position (consecutive pairs)
+      const float2* rrow = a.rope ? a.rope + (size_t)(tq[qt] < a.T ? tq[qt] : 0) * (DK / 2) : nullptr;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        u16x8 x = __builtin_bit_cast(u16x8, qf[qt][ks]);
+        if (rrow) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x0 = bf16_to_f32(x[2 * j]), x1 = bf16_to_f32(x[2 * j + 1]);
+            rope_pair(x0, x1, rrow[(ks * 32 + 8 * g) / 2 + j]);
+            x[2 * j] = f32_to_bf16(x0 * sl2);
+            x[2 * j + 1] = f32_to_bf16(x1 * sl2);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = f32_to_bf16(bf16_to_f32(x[j]) * sl2);
+        }
+        qf[qt][ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  };
 
   // Tile loads: 1 KiB instruction i covers bytes [i*1024, i*1024 + 1024) of a stage
   // (K rows first, then V rows); wave w issues i = 4k + w.  Lane l writes 16 bytes at
@@ -548,7 +576,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     for (int k = 0; k < LPW; ++k) issue_load(k, it, st, woff);
   };
 
-  const float sl2 = a.scale * kLog2e;
   float m_run[QT], l_run[QT];
   f32x4 acc[QT][DT];
 #pragma unroll
@@ -607,6 +634,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // compiler waits for those registers where they are first used; every step waits
   // for all memory before it reads the stage).
   if (it0 < ntiles) issue_tile(it0, stage0);
+  prep_queries();
 
   f32x4 st[QT][NKT];
   // S^T = K Q^T for the tile in `Kt`.  With `load` set, the loads of tile `itn` into
@@ -615,10 +643,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // barrier, where the waves stalled on their issue.
   auto do_scores = [&](const char* Kt, bool load, char* nx, int itn) {
     constexpr int NM = KSD * NKT * QT;                     // products of the phase
+    // the products accumulate onto minus the running maximum (0 while it is -inf), so
+    // they end as scaled logits relative to it
+    f32x4 c0v[QT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) st[qt][kt] = (f32x4)(0.f);
+    for (int qt = 0; qt < QT; ++qt) c0v[qt] = (f32x4)(m_run[qt] == -INFINITY ? 0.f : -m_run[qt]);
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
@@ -626,7 +655,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
         const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Kt + koff[ks] + kt * 16 * RBK);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], st[qt][kt], 0, 0, 0);
+          st[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qf[qt][ks], ks == 0 ? c0v[qt] : st[qt][kt], 0, 0, 0);
       }
     if (load) {
       const int woff = opaque_woff();
@@ -666,18 +695,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // probabilities against the current maximum, rounded to bf16: the B operand of
   // O^T += V^T P^T.  Within each 32-key half u, B's row k = 8g + j holds key
   // 32u + 4g + j (j < 4) or 32u + 16 + 4g + j - 4 (j >= 4); the V^T fragments
-  // follow the same order.
+  // follow the same order.  The scores are relative to the maximum they were formed
+  // against; off[qt] moves them to the current one (the exact path only).
   bf16x8 pb[NKT / 2][QT];
-  auto do_probs = [&]() {
+  auto do_probs = [&](const float (&off)[QT], bool shift) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float mneg = (m_run[qt] == -INFINITY) ? 0.f : -m_run[qt];
 #pragma unroll
       for (int u = 0; u < NKT / 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[u][qt][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[qt][2 * u][i], sl2, mneg)));
-          pb[u][qt][4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(st[qt][2 * u + 1][i], sl2, mneg)));
+          const float s0 = shift ? st[qt][2 * u][i] + off[qt] : st[qt][2 * u][i];
+          const float s1 = shift ? st[qt][2 * u + 1][i] + off[qt] : st[qt][2 * u + 1][i];
+          pb[u][qt][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s0));
+          pb[u][qt][4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s1));
         }
     }
   };
@@ -698,14 +729,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // exact path: row maxima, rescale, probabilities against the new maximum
   auto do_exact = [&]() {
     bool grow = false;
-    float m_loc[QT];
+    float m_loc[QT], mref[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
+      mref[qt] = m_run[qt] == -INFINITY ? 0.f : m_run[qt];   // what the scores are relative to
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
         tmax = fmaxf(tmax, fmaxf(fmaxf(st[qt][kt][0], st[qt][kt][1]), fmaxf(st[qt][kt][2], st[qt][kt][3])));
-      m_loc[qt] = tmax * sl2;
+      m_loc[qt] = tmax + mref[qt];
       grow |= m_loc[qt] > m_run[qt] + kLazyRescale;
     }
     if (__any(grow)) {
@@ -721,7 +753,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
         m_run[qt] = mn;
       }
     }
-    do_probs();
+    float off[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) off[qt] = m_run[qt] == -INFINITY ? 0.f : mref[qt] - m_run[qt];
+    do_probs(off, true);
     float ls[QT];
     do_rowsum(ls);
 #pragma unroll
@@ -761,7 +796,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   const char* ornn_st = nullptr;
   auto issue_ornn = [&](char* st) {
     const int rstride = a.H * DV * 2;
-    const char* base = reinterpret_cast<const char*>(a.o_rnn32) + (((size_t)b * a.T + qb0) * a.H + h) * DV * 2;
+    const char* base = uniform_ptr(reinterpret_cast<const char*>(a.o_rnn32) + (((size_t)b * a.T + qb0) * a.H + h) * DV * 2);
     // rows past T read zero (kept in a scalar register: a clamp the compiler forms on the
     // vector unit would make the descriptor look divergent and wrap each load in a loop)
     const int range = __builtin_amdgcn_readfirstlane(max(0, min(a.T - qb0, BM)) * rstride);
@@ -785,7 +820,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     // its first visible key is (the row has no running maximum before it)
     bool exact = !DOC && it == 0;
     if (!exact) {
-      do_probs();
+      const float zero[QT] = {};
+      do_probs(zero, false);
       float ls[QT];
       do_rowsum(ls);
       bool over = false;
