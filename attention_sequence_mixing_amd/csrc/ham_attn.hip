@@ -549,9 +549,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // load k (of LPW) of this wave for tile it into stage st; woff = 1024 * wave (the
   // caller hides its value from the compiler, which otherwise keeps every load's LDS
   // address in a register of its own and runs out of scalar registers)
-  auto issue_load = [&](int k, int it, char* st, int woff) {
+  auto issue_load = [&](int k, int it, char* st, int woff, int rows) {
     const int c0 = it * BN;
-    const int rows = min(nhi - c0, BN);                    // > 0 for every issued tile
     if (k < KI / NWV) {
       buffer_to_lds_so(Kh + (size_t)c0 * RBK, rows * RBK, ldK, k * NWV * 1024, st + woff + k * NWV * 1024);
     } else if (k < (KI + VI1) / NWV) {
@@ -570,10 +569,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     asm volatile("" : "+s"(w));
     return w;
   };
-  auto issue_tile = [&](int it, char* st) {
+  auto issue_tile = [&](int it, char* st, int rows) {
     const int woff = opaque_woff();
 #pragma unroll
-    for (int k = 0; k < LPW; ++k) issue_load(k, it, st, woff);
+    for (int k = 0; k < LPW; ++k) issue_load(k, it, st, woff, rows);
   };
 
   float m_run[QT], l_run[QT];
@@ -632,9 +631,34 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   }
   // The first tile's loads go out while the query fragments are still in flight (the
   // compiler waits for those registers where they are first used; every step waits
-  // for all memory before it reads the stage).
-  if (it0 < ntiles) issue_tile(it0, stage0);
+  // for all memory before it reads the stage).  Without document masks the first tile
+  // is tile 0 and its loads do not wait for the block's visible-key counts either: they
+  // take every row the cache holds (up to 64), and once the counts are known the rows
+  // past the last visible key, which may be stale, are cleared in the V tile (their
+  // scores are masked; a stale value row times probability 0 could still be NaN).
+  if constexpr (DOC) {
+    if (it0 < ntiles) issue_tile(it0, stage0, min(nhi - it0 * BN, BN));
+  } else {
+    issue_tile(0, stage0, min(a.cap, BN));
+  }
   prep_queries();
+  if constexpr (!DOC) {
+    const int rmax = min(a.cap, BN);
+    if (ntiles == 0) {
+      __builtin_amdgcn_s_waitcnt(0);                       // no step waits for the early tile
+    } else if (nhi < rmax) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int tid = threadIdx.x;
+      for (int i = tid; i < (rmax - nhi) * (RB1 / 16); i += 64 * NWV)
+        *reinterpret_cast<f32x4*>(stage0 + KB + (nhi + i / (RB1 / 16)) * RB1 + (i % (RB1 / 16)) * 16) = (f32x4)(0.f);
+      if constexpr (DV2 > 0) {
+        for (int i = tid; i < (rmax - nhi) * (RB2 / 16); i += 64 * NWV)
+          *reinterpret_cast<f32x4*>(stage0 + V2OFF + (nhi + i / (RB2 / 16)) * RB2 + (i % (RB2 / 16)) * 16) =
+              (f32x4)(0.f);
+      }
+    }
+  }
 
   f32x4 st[QT][NKT];
   // S^T = K Q^T for the tile in `Kt`.  With `load` set, the loads of tile `itn` into
@@ -660,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
     if (load) {
       const int woff = opaque_woff();
 #pragma unroll
-      for (int k = 0; k < LPW; ++k) issue_load(k, itn, nx, woff);
+      for (int k = 0; k < LPW; ++k) issue_load(k, itn, nx, woff, min(nhi - itn * BN, BN));
       // order: the fragment reads, then the products in LPW groups, a load after each
       __builtin_amdgcn_sched_group_barrier(0x100, KSD * NKT, 0);
       interleave_loads<NM, LPW>();
