@@ -10,8 +10,9 @@
 namespace ham {
 
 // Score partials: every RNN kernel writes, per token and per d_v slice, the
-// three sums (p.v, p.p, v.v) of the prediction p = S_{t-1}^T k_t against v_t.
-// The routing kernel adds the slices and forms the cosine.
+// three sums (p.v, p.p, v.v) of the prediction p = S_{t-1}^T k_t against v_t
+// (slices of 16 columns from the token-serial kernel, of 64 from the chunked state
+// pass).  The routing kernel adds the slices and forms the cosine.
 
 struct RnnArgs {
   const void* q;

@@ -471,13 +471,19 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   using LY = ChunkLayout<DK, NW, (VAR & kVarLean) != 0>;
   constexpr int MT = DK / 16;     // 16-row tiles of S
   constexpr int KSD = DK / 32;    // 32-wide k-steps over d
-  constexpr int NSL = DV / 16;    // score slices
+  constexpr int NSL = DV / (16 * NW);   // score slices per token: one per column block
   // Two stages as separate LDS objects: the chunk loop is unrolled by two, so
   // every access names its stage statically and the compiler can tell that reads
   // of the current stage do not depend on the direct loads into the other one.
   __shared__ __attribute__((aligned(16))) char stage0[LY::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[LY::STAGE];
   __shared__ __attribute__((aligned(16))) char single[LY::SINGLE];
+  // Score partials of the waves' 16-column slices, two chunks deep: a chunk's are
+  // summed over the workgroup's waves after the next chunk's barrier, so one float4
+  // per token and column block goes to memory.
+  constexpr bool kScore = MODE == 0 && !(VAR & kVarNoScore);
+  static_assert(NW * 16 == kC, "one wave per 16 tokens of a chunk in the score sums");
+  __shared__ __attribute__((aligned(16))) float4 sred[kScore ? 2 * NW * kC : 1];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -492,7 +498,6 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   const int h = bh % a.H, b = bh / a.H;
   const int colbase = cb * 16 * NW;
   const int col = colbase + wave * 16 + n;
-  const int slice = cb * NW + wave;
 
   // State tiles: element i of tile mt in lane (g, n) is S[srow(mt, g, i)][col] with
   // srow = 32 (mt/2) + 8g + 4 (mt mod 2) + i.  With this row order the k-slots
@@ -607,13 +612,32 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   // token whose row totals this lane ends with after the transposed reduction)
   const uint32_t o_lane = (uint32_t)((4 * g * a.H + h) * DV + col);
   const int s_tok = 16 * (n >> 2) + 4 * g + (n & 3);
-  const uint32_t s_lane = (uint32_t)(s_tok * a.H * NSL + slice);
+  // the waves' partials of chunk cc summed in wave order (lanes 0..15 of wave w take
+  // tokens 16w .. 16w + 15) and stored as the column block's slice
+  auto flush_scores = [&](int cc) {
+    if constexpr (kScore) {
+      const int tt = 16 * wave + lane, t0 = cc * kC;
+      if (lane < 16 && t0 + tt < a.T) {
+        const float4* sr = sred + (cc & 1) * NW * kC + tt;
+        float4 acc = sr[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          const float4 x = sr[w * kC];
+          acc.x += x.x;
+          acc.y += x.y;
+          acc.z += x.z;
+        }
+        a.score[(((size_t)b * a.T + t0 + tt) * a.H + h) * NSL + cb] = acc;
+      }
+    }
+  };
 
   auto chunk_step = [&](int c, char* stg, char* nxt) {
     const int t0 = c * kC;
     const int nvalid = min(kC, a.T - t0);
     __builtin_amdgcn_s_waitcnt(0);            // this chunk's tiles and record have arrived
     __syncthreads();                          // ... for every wave; the other stage is free
+    if (c > c_begin) flush_scores(c - 1);     // every wave's partials of the last chunk are in
     // this lane's V values V[16mt + 4g + i][wave*16 + n] (transposing reads)
     u32x2 vraw[4] = {};
     if (MODE != 2) {
@@ -831,7 +855,8 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         }
     }
 
-    // ---- score partials of this 16-column slice, and the readout ----
+    // ---- score partials of this 16-column slice (summed over the workgroup after
+    //      the next barrier), and the readout ----
     const bool full = nvalid == kC;
     if (MODE == 0 && !(VAR & kVarNoScore)) {
       float xpv[16], xpp[16], xvv[16];
@@ -848,8 +873,7 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       const float pv = row16_transpose_sum(xpv, n);
       const float pp = row16_transpose_sum(xpp, n);
       const float vv = row16_transpose_sum(xvv, n);
-      float4* sc = a.score + (((size_t)b * a.T + t0) * a.H + h) * NSL;
-      if (full || s_tok < nvalid) sc[s_lane] = make_float4(pv, pp, vv, 0.f);
+      sred[(c & 1) * NW * kC + wave * kC + s_tok] = make_float4(pv, pp, vv, 0.f);
     }
     if (RO) {
       // the readout feeds the bf16 mix and the bf16 o_rnn output: stored as bf16
@@ -914,6 +938,10 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
   for (int c = c_begin; c < c_end; c += 2) {
     chunk_step(c, stage0, stage1);
     if (c + 1 < c_end) chunk_step(c + 1, stage1, stage0);
+  }
+  if (kScore && c_end > c_begin) {
+    __syncthreads();
+    flush_scores(c_end - 1);
   }
   // the full pass stores the state after the last chunk (its last segment only); the
   // partial passes store each segment's result in its own block
@@ -1013,7 +1041,8 @@ bool rnn_chunked_supported(int io, int dk, int dv) {
   return io == 1 && (((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) || (dk == 256 && dv == 384));
 }
 
-int rnn_chunked_slices(int dv) { return dv / 16; }
+// one score slice per four-wave workgroup (64 state columns)
+int rnn_chunked_slices(int dv) { return dv / 64; }
 
 hipError_t launch_rnn_chunked_prep(int io, int dk, const RnnArgs& a, hipStream_t s) {
   if (io != 1) return hipErrorInvalidValue;

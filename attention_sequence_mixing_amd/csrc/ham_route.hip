@@ -143,6 +143,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   b.e_lds = a.blk > 1 && !a.t_abs && a.H <= 192 ? 1 : 0;
   if (b.e_lds) lds += (size_t)kChunk * a.H * sizeof(float);
   if (b.e_in) hipLaunchKernelGGL(route_kernel<0>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 1) hipLaunchKernelGGL(route_kernel<1>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 2) hipLaunchKernelGGL(route_kernel<2>, grid, dim3(256), lds, s, b);
+  else if (b.slices == 6) hipLaunchKernelGGL(route_kernel<6>, grid, dim3(256), lds, s, b);
   else if (b.slices == 8) hipLaunchKernelGGL(route_kernel<8>, grid, dim3(256), lds, s, b);
   else if (b.slices == 4) hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), lds, s, b);
   else if (b.slices == 24) hipLaunchKernelGGL(route_kernel<24>, grid, dim3(256), lds, s, b);

@@ -234,7 +234,8 @@ def stage_report(stages, B, T, H, d, pairs, nroute):
     att_flops = pairs * attn_flops_per_pair(d)
     # algorithmic bytes (inputs read once, outputs written once)
     bytes_ = {"rnn_prep": BTH * (2 * d * 2 + 8),                # q, k bf16; beta, g fp32
-              "route": BTH * (16 * (d // 16) + 4 + 1),          # score partials in; e, routed out
+              "route": BTH * (16 * (d // 64) + 4 + 1),          # score partials (one float4 per 64
+                                                                # state columns) in; e, routed out
               "compact": BTH * (1 + 4) + nroute * (2 * (2 * d * 2) + 4)}
     per = []
     for i, nm in enumerate(STAGES):
