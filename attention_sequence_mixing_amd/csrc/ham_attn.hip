@@ -665,8 +665,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   // stage `nx` go out between the products (about one per NM / LPW of them), so the
   // texture path takes them spread over the phase rather than all at once after the
   // barrier, where the waves stalled on their issue.
+  // The matrix phases (scores, P V) run at raised wave priority: with two waves per
+  // SIMD in different phases, the one issuing products is served first and the
+  // other's softmax instructions fill its gaps (attention 0.298 -> 0.291 ms at the
+  // layer shape, same box).
   auto do_scores = [&](const char* Kt, bool load, char* nx, int itn) {
     constexpr int NM = KSD * NKT * QT;                     // products of the phase
+    __builtin_amdgcn_s_setprio(1);
     // the products accumulate onto minus the running maximum (0 while it is -inf), so
     // they end as scaled logits relative to it
     f32x4 c0v[QT];
@@ -689,6 +694,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, KSD * NKT, 0);
       interleave_loads<NM, LPW>();
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // keys at or past a query's visible count get -inf
   auto do_mask = [&](int c0) {
@@ -788,6 +794,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
   };
   // O^T += V^T P^T for the tile in `stage`
   auto do_pv = [&](const char* Vt) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < NKT / 2; ++u) {
 #pragma unroll
@@ -804,6 +811,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_v5_kernel(AttnArgs a) {
           acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u][qt], acc[qt][dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Step it: tile it has landed in `cur` (wait, then barrier: every wave is also
