@@ -10,7 +10,7 @@ documents with same-document masking and RoPE; rho = 0.5 of 64-token blocks with
 block-contiguous routing; 32 KV heads of 128/64, and the 800M layer's 5 RNN heads of 256/384 with
 10 KV heads of 128/192, at sampled sequence-head pairs); the long-context case (B=1, H=16, T=32768,
 planted repeated pairs, rho = 0.25); the decode case (batch 32, H=16, d=128,
-32K-token prefix, then decode steps).
+32K-token prefix, then 16 decode steps, 64 sampled sequence-head pairs).
 """
 import numpy as np
 import pytest
@@ -233,7 +233,11 @@ def test_long_context_fullsize():
 
 
 def test_decode_fullsize_sampled_heads():
-    B, H, d, T0, steps = DECODE_B, DECODE_H, DECODE_D, DECODE_PREFIX, 8
+    """Decode at the full workload (batch 32, H=16, d=128, 32K-token prefix): 16 decode
+    steps, then 64 sampled (sequence, head) pairs -- four of every head index, spread over
+    the batch -- against one oracle pass over their whole prefix and steps (the pairs
+    stacked along the oracle's batch axis, so its threads take one each)."""
+    B, H, d, T0, steps = DECODE_B, DECODE_H, DECODE_D, DECODE_PREFIX, 16
     scale = d ** -0.5
     tau = np.full(H, 1.0, np.float32)        # a fixed threshold near the median score
     pre = make_inputs_torch(B, T0, H, d, dtype="bf16", seed=4, device=DEV)
@@ -251,29 +255,31 @@ def test_decode_fullsize_sampled_heads():
     assert int(dplan.status.item()) == 0
     e_pre = plan.e.cpu().numpy()
     r_pre = plan.routed.cpu().numpy()
-    for (b, h) in [(0, 0), (5, 3), (17, 11), (31, 15)]:
-        sub = {n: np.concatenate([np_of(pre[n][b:b + 1, :, h:h + 1]),
-                                  np_of(x[n][:, b, h]).reshape((1, steps, 1) + x[n].shape[3:])], axis=1)
-               for n in ("q", "k", "v", "beta", "g")}
-        T = T0 + steps
-        emit = np.zeros((1, T, 1), np.int8)
-        emit[0, T0:, 0] = 1
-        e_all = np.concatenate([e_pre[b, :, h], np.array([e[b, h] for e in es])])
-        r_all = np.concatenate([r_pre[b, :, h], np.array([r[b, h] for r in rs])]).astype(np.int8)
-        ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit)
-        assert np.abs(e_all - ref["e"][0, :, 0]).max() < E_TOL
-        near = np.abs(ref["e"][0, :, 0] - tau[h]) < NEAR
-        assert not ((r_all.astype(bool) != ref["routed"][0, :, 0].astype(bool)) & ~near).any()
-        if not np.array_equal(r_all, ref["routed"][0, :, 0]):
-            ref = oracle.forward(**sub, tau=tau[h:h + 1], scale=scale, emit=emit,
-                                 mask_override=r_all.reshape(1, T, 1))
-        assert int(plan.count[b, h].item()) == int(ref["count"][0, 0])
+    pairs = [((7 * h + 3 + 8 * j) % B, h) for h in range(H) for j in range(4)]
+    n, T = len(pairs), T0 + steps
+    sub = {nm: np.concatenate([np.concatenate([np_of(pre[nm][b:b + 1, :, h:h + 1]),
+                                               np_of(x[nm][:, b, h]).reshape((1, steps, 1) + x[nm].shape[3:])],
+                                              axis=1) for (b, h) in pairs], axis=0)
+           for nm in ("q", "k", "v", "beta", "g")}
+    emit = np.zeros((n, T, 1), np.int8)
+    emit[:, T0:, 0] = 1
+    e_all = np.stack([np.concatenate([e_pre[b, :, h], np.array([e[b, h] for e in es])]) for (b, h) in pairs])
+    r_all = np.stack([np.concatenate([r_pre[b, :, h], np.array([r[b, h] for r in rs])])
+                      for (b, h) in pairs]).astype(np.int8)
+    ref = oracle.forward(**sub, tau=tau[:1], scale=scale, emit=emit)
+    assert np.abs(e_all - ref["e"][:, :, 0]).max() < E_TOL
+    near = np.abs(ref["e"][:, :, 0] - tau[0]) < NEAR
+    assert not ((r_all.astype(bool) != ref["routed"][:, :, 0].astype(bool)) & ~near).any()
+    if not np.array_equal(r_all, ref["routed"][:, :, 0]):
+        ref = oracle.forward(**sub, tau=tau[:1], scale=scale, emit=emit, mask_override=r_all.reshape(n, T, 1))
+    for i, (b, h) in enumerate(pairs):
+        assert int(plan.count[b, h].item()) == int(ref["count"][i, 0])
         o_dec = np.stack([o[b, h] for o in outs])
-        y = ref["o"][0, T0:, 0]
+        y = ref["o"][i, T0:, 0]
         err = np.abs(o_dec - y).max() / np.abs(y).max()
         assert err < TOL[torch.bfloat16], (b, h, err)
-        errS = np.abs(np_of(plan.S[b, h]) - ref["S"][0, 0]).max() / np.abs(ref["S"][0, 0]).max()
-        assert errS < 1e-4, errS
+        errS = np.abs(np_of(plan.S[b, h]) - ref["S"][i, 0]).max() / np.abs(ref["S"][i, 0]).max()
+        assert errS < 1e-4, (b, h, errS)
 
 
 def test_decode_maximum_capacity_many_segments():
