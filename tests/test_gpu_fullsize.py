@@ -232,6 +232,28 @@ def test_long_context_fullsize():
     print(f"long: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
 
 
+def test_long_context_every_output():
+    """The long-context case (B=1, H=16, T=32768, rho = 0.25, the segmented state pass)
+    with every output element compared: the oracle's full forward runs with the GPU's
+    routing mask, and o, o_rnn and o_kv of every head must meet the bf16 tolerance."""
+    w = LONG
+    inp = make_workload(w)
+    scale = w.attn_scale
+    base = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(base["e"], w.rho)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    r_gpu = out["routed"].cpu().numpy()
+    ref = oracle.forward(**inp, tau=tau, scale=scale, mask_override=r_gpu)
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"long, every output: worst slice errors {worst}")
+
+
 def test_decode_fullsize_sampled_heads():
     """Decode at the full workload (batch 32, H=16, d=128, 32K-token prefix): 16 decode
     steps, then 64 sampled (sequence, head) pairs -- four of every head index, spread over
