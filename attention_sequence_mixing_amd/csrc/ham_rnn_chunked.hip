@@ -25,9 +25,9 @@
 // of the state and the routing score splits the fp32 value into three bf16 terms
 // hi+mid+lo (24 significant bits) and keeps the cross terms down to 2^-16 relative,
 // which is fp32-level accuracy; the routing score needs it.  The readout O only
-// feeds bf16 outputs: Q S takes the leading term of S, and (Gamma o Q K^T) D the
-// leading term of Gamma o Q K^T against two terms of D (about 2^-9 relative, the
-// size of the bf16 rounding of the outputs themselves).
+// feeds bf16 outputs: Q S takes the leading term of S (the first two at d_k = 256),
+// and (Gamma o Q K^T) D the leading term of Gamma o Q K^T against two terms of D
+// (about 2^-9 relative, the size of the bf16 rounding of the outputs themselves).
 //
 // Layout: one workgroup = NW waves = one head's 16*NW state columns.  The fp32 state
 // lives in MFMA accumulators (rows of S on the 16x16 tile's M axis).  Products
@@ -685,7 +685,13 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         if (RO) qf[buf][mt] = *reinterpret_cast<const u32x4*>(Qs + oa);
       }
     };
-    // the three bf16 terms of S rows 32ks..32ks+31 (the B operand of k-step ks)
+    // the three bf16 terms of S rows 32ks..32ks+31 (the B operand of k-step ks).  The
+    // readout's Q S takes the leading term, and at d_k = 256 the first two: the mix
+    // normalises each readout row by its own RMS, so a row of small norm (the first
+    // tokens of a chunk, early in the sequence) carries the product's rounding relative
+    // to the row, and over 256 terms the one-term product left 2.2% in the worst row of
+    // the paper's head layout against 1% at d_k = 128.
+    constexpr bool kQS2 = DK > 128;
     bf16x8 spl[2][3];
     auto split_step = [&](int ks, int buf) {
       u32x2 h0, m0, l0, h1, m1, l1;
@@ -713,12 +719,13 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
         P[mt] = mfma_bf16(af, sl, P[mt]);
         P[mt] = mfma_bf16(af, smd, P[mt]);
         P[mt] = mfma_bf16(af, sh, P[mt]);
+        if (RO && kQS2) O[mt] = mfma_bf16(as8(qf[ks & 1][mt]), smd, O[mt]);
         if (RO) O[mt] = mfma_bf16(as8(qf[ks & 1][mt]), sh, O[mt]);
       }
       if (ks + 1 < KSD) {
         __builtin_amdgcn_sched_group_barrier(0x100, RO ? 8 : 4, 0);     // the next step's LDS reads
 #pragma unroll
-        for (int i = 0; i < (RO ? 16 : 12); ++i) {
+        for (int i = 0; i < 4 * (3 + (RO ? (kQS2 ? 2 : 1) : 0)); ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);            // three VALU
         }

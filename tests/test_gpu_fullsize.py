@@ -254,6 +254,39 @@ def test_long_context_every_output():
     print(f"long, every output: worst slice errors {worst}")
 
 
+def test_paper_heads_every_output():
+    """The 800M layer's head geometry at full size (B 8, T 4096, bf16: 5 RNN heads of
+    256/384 on the chunked state pass, 10 KV heads of 128/192 on the tiled attention):
+    every score and final state of all 40 RNN heads, routing outside the near band, and
+    every output element of o, o_rnn (per RNN head) and o_kv (per KV head) against the
+    oracle's forward under the GPU's routing mask."""
+    B, T, H, dk, dv, r, dkk = 8, 4096, 5, 256, 384, 2, 128
+    inp = make_inputs(B, T, H, dk, dv, dtype="bf16", seed=60 + dk)
+    att = make_inputs(B, T, r * H, dkk, dv // r, dtype="bf16", seed=61 + dk)
+    tau = np.full(H, 1.0, np.float32)
+    scale = dkk ** -0.5
+    t, ta = to_dev(inp, torch.bfloat16, DEV), to_dev(att, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"], want_o_rnn=True,
+                          want_o_kv=True)
+    torch.cuda.synchronize()
+    r_gpu = out["routed"].cpu().numpy()
+    okw = dict(tau=tau, scale=scale, q_attn=att["q"], k_attn=att["k"], v_attn=att["v"])
+    ref = oracle.forward(**inp, mask_override=r_gpu, **okw)
+    e_gpu = out["e"].cpu().numpy()
+    de = np.abs(e_gpu - ref["e"]).max()
+    assert de < E_TOL, de
+    ref_r = (ref["e"] > tau.reshape(1, 1, H)).astype(bool)         # the oracle's own decisions
+    near = np.abs(ref["e"] - tau.reshape(1, 1, H).astype(np.float64)) < NEAR
+    assert not ((r_gpu.astype(bool) != ref_r) & ~near).any()
+    assert rel_err_slices(np_of(out["S"]), ref["S"], 1) < 1e-4
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"paper heads, every output: max|de|={de:.2e} worst slice errors {worst}")
+
+
 def test_decode_fullsize_sampled_heads():
     """Decode at the full workload (batch 32, H=16, d=128, 32K-token prefix): 16 decode
     steps, then 64 sampled (sequence, head) pairs -- four of every head index, spread over
