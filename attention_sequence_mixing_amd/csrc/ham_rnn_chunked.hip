@@ -25,8 +25,9 @@
 // of the state and the routing score splits the fp32 value into three bf16 terms
 // hi+mid+lo (24 significant bits) and keeps the cross terms down to 2^-16 relative,
 // which is fp32-level accuracy; the routing score needs it.  The readout O only
-// feeds bf16 outputs: Q S takes the leading term of S (the first two at d_k = 256),
-// and (Gamma o Q K^T) D the leading term of Gamma o Q K^T against two terms of D
+// feeds bf16 outputs: Q S takes the first two terms of S (the mix normalises each
+// readout row, so a row of small norm needs the product accurate relative to the
+// row), and (Gamma o Q K^T) D the leading term of Gamma o Q K^T against two terms of D
 // (about 2^-9 relative, the size of the bf16 rounding of the outputs themselves).
 //
 // Layout: one workgroup = NW waves = one head's 16*NW state columns.  The fp32 state
@@ -686,12 +687,12 @@ __global__ __launch_bounds__(64 * NW) void rnn_chunked_kernel(RnnArgs a) {
       }
     };
     // the three bf16 terms of S rows 32ks..32ks+31 (the B operand of k-step ks).  The
-    // readout's Q S takes the leading term, and at d_k = 256 the first two: the mix
-    // normalises each readout row by its own RMS, so a row of small norm (the first
-    // tokens of a chunk, early in the sequence) carries the product's rounding relative
-    // to the row, and over 256 terms the one-term product left 2.2% in the worst row of
-    // the paper's head layout against 1% at d_k = 128.
-    constexpr bool kQS2 = DK > 128;
+    // readout's Q S takes the first two: the mix normalises each readout row by its own
+    // RMS, so a row of small norm (the first tokens of a chunk, early in the sequence)
+    // carries the product's rounding relative to the row.  With the leading term alone
+    // the worst output slice was 2.2% off at d_k = 256 and 1.6% at d_k = 128 (32 KV
+    // heads of 128/64), against the 2% bound; with two, under 0.5%.
+    constexpr bool kQS2 = true;
     bf16x8 spl[2][3];
     auto split_step = [&](int ks, int buf) {
       u32x2 h0, m0, l0, h1, m1, l1;

@@ -232,6 +232,52 @@ def test_long_context_fullsize():
     print(f"long: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
 
 
+@pytest.mark.parametrize("variant", ["rope", "packed", "blocks", "kv32"])
+def test_layer_variants_every_output(variant):
+    """The benchmark's layer variants at full size (B 8, H 16, T 4096, bf16) with every
+    output element compared: RoPE base 500K; packed documents (mean 1024) with RoPE;
+    64-token block routing; 32 KV heads of 128/64 over the 16 RNN heads (the split-head
+    mix).  The oracle's full forward runs with the GPU's routing mask; o, o_rnn and o_kv
+    of every head must meet the bf16 tolerance."""
+    w = LAYER
+    scale = w.attn_scale
+    kw, okw = {}, {}
+    if variant == "kv32":
+        inp = make_inputs(w.B, w.T, w.H, 128, 128, dtype="bf16", seed=188)
+        att = make_inputs(w.B, w.T, 2 * w.H, 128, 64, dtype="bf16", seed=189)
+        tau = np.full(w.H, 1.0, np.float32)
+        ta = to_dev(att, torch.bfloat16, DEV)
+        kw = dict(q_attn=ta["q"], k_attn=ta["k"], v_attn=ta["v"])
+        okw = dict(q_attn=att["q"], k_attn=att["k"], v_attn=att["v"])
+    else:
+        inp = make_workload(w)
+        base_e = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+        if variant == "blocks":
+            tau = tau_for_rho(block_means(base_e["e"], 64)[:, ::64], 0.5)
+            kw = okw = dict(route_block=64)
+        else:
+            tau = tau_for_rho(base_e["e"], 0.5)
+            kw = dict(rope_base=500000.0)
+            okw = dict(rope_base=500000.0)
+            if variant == "packed":
+                ds = make_doc_start(w.B, w.T, 1024, 43)
+                kw["doc_start"] = torch.from_numpy(ds.astype(np.int32)).to(DEV)
+                okw["doc_start"] = ds
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True, **kw)
+    torch.cuda.synchronize()
+    r_gpu = out["routed"].cpu().numpy()
+    ref = oracle.forward(**inp, tau=tau, scale=scale, mask_override=r_gpu, **okw)
+    de = np.abs(out["e"].cpu().numpy() - ref["e"]).max()
+    assert de < E_TOL, de
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"layer {variant}, every output: max|de|={de:.2e} worst slice errors {worst}")
+
+
 def test_long_context_every_output():
     """The long-context case (B=1, H=16, T=32768, rho = 0.25, the segmented state pass)
     with every output element compared: the oracle's full forward runs with the GPU's
