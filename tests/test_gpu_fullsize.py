@@ -232,6 +232,31 @@ def test_long_context_fullsize():
     print(f"long: max|de|={de:.2e} near-band flips={nflip} sampled errors {worst}")
 
 
+@pytest.mark.parametrize("rho", [0.1, 1.0])
+def test_layer_rho_every_output(rho):
+    """The headline layer at the rho sweep's sparse and full ends (rho = 0.1, and 1.0:
+    every token cached, full causal attention beside the RNN) with every output element
+    of every head compared against the oracle's forward under the GPU's routing mask."""
+    w = LAYER
+    inp = make_workload(w)
+    scale = w.attn_scale
+    base = _rnn_only_oracle(inp, np.full(w.H, INF, np.float32), scale)
+    tau = tau_for_rho(base["e"], rho)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, want_o_rnn=True, want_o_kv=True)
+    torch.cuda.synchronize()
+    r_gpu = out["routed"].cpu().numpy()
+    if rho == 1.0:
+        assert r_gpu.all()
+    ref = oracle.forward(**inp, tau=tau, scale=scale, mask_override=r_gpu)
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"layer rho={rho}, every output: worst slice errors {worst}")
+
+
 @pytest.mark.parametrize("variant", ["rope", "packed", "blocks", "kv32"])
 def test_layer_variants_every_output(variant):
     """The benchmark's layer variants at full size (B 8, H 16, T 4096, bf16) with every
