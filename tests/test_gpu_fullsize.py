@@ -20,7 +20,8 @@ import oracle
 import attention_sequence_mixing_amd as ham
 from attention_sequence_mixing_amd.inputs import (LAYER, LONG, DECODE_B, DECODE_D, DECODE_H,
                                                   DECODE_PREFIX, make_doc_start, make_inputs,
-                                                  make_inputs_torch, make_workload, tau_for_rho)
+                                                  make_inputs_torch, make_router_scores,
+                                                  make_workload, tau_for_rho)
 from parity import E_TOL, NEAR, TOL, block_means, np_of, rel_err_slices, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -255,6 +256,35 @@ def test_layer_rho_every_output(rho):
         worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
         assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
     print(f"layer rho={rho}, every output: worst slice errors {worst}")
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_learned_router_every_output(overlap):
+    """The headline layer with a learned router's scores (synthetic sigmoid scores, one
+    per token and head) as the routing score, thresholds for rho = 0.5: the score-free
+    state pass, alone or beside the attention chain on a second stream.  Routing must
+    equal score > tau exactly, and every output element of every head must meet the bf16
+    tolerance against the oracle."""
+    w = LAYER
+    inp = make_workload(w)
+    scale = w.attn_scale
+    rs = make_router_scores(w.B, w.T, w.H, 77).copy()
+    tau = oracle.select_tau(rs, 0.5)
+    t = to_dev(inp, torch.bfloat16, DEV)
+    out = ham.ham_forward(t["q"], t["k"], t["v"], t["beta"], t["g"], torch.from_numpy(tau).to(DEV),
+                          scale=scale, router_scores=torch.from_numpy(rs).to(DEV), want_o_rnn=True,
+                          want_o_kv=True, overlap=overlap)
+    torch.cuda.synchronize()
+    r_gpu = out["routed"].cpu().numpy().astype(bool)
+    assert np.array_equal(r_gpu, rs > tau.reshape(1, 1, w.H))
+    ref = oracle.forward(**inp, tau=tau, scale=scale, router_score=rs)
+    assert np.array_equal(out["count"].cpu().numpy(), ref["count"])
+    assert rel_err_slices(np_of(out["S"]), ref["S"], 1) < 1e-4
+    worst = {}
+    for name in ("o", "o_rnn", "o_kv"):
+        worst[name] = rel_err_slices(np_of(out[name]), ref[name], 2)
+        assert worst[name] < TOL[torch.bfloat16], (name, worst[name])
+    print(f"learned router (overlap={overlap}), every output: worst slice errors {worst}")
 
 
 @pytest.mark.parametrize("variant", ["rope", "packed", "blocks", "kv32"])
