@@ -144,18 +144,17 @@ HAM_DEVICE f32x4 mma6(F mf, const V& ah, const V& am, const V& al, const V& bh, 
 // Prep kernel: one workgroup (4 waves) per (b, h, chunk); chunks are independent.
 // Decayed Gram matrices (S2), their diagonal-block inverses (S3), gamma and the
 // state-update decays (S1).
-// 39 KiB at d_k = 128, so four workgroups share a CU: K and Q rows are unpadded with
-// their 16-byte chunks XOR-swizzled by row, and the block-inverse scratch reuses Q's
-// space once the Gram fragments are done.
+// About 23 KiB at d_k = 128: K rows are unpadded with their 16-byte chunks XOR-swizzled
+// by row, the Q rows of the Q K^T products go from memory straight into registers, and
+// the block-inverse scratch reuses K's space once the Gram fragments are done.
 template <int DK>
 struct PrepSmem {
-  static constexpr int NCH = DK / 8;       // 16-byte chunks per K / Q row
+  static constexpr int NCH = DK / 8;       // 16-byte chunks per K row
   // element offset of chunk c of row r: the 16 rows one fragment read touches fall in
   // different banks
   HAM_DEVICE static int at(int r, int c) { return r * DK + ((c ^ (r & (NCH - 1))) << 3); }
-  uint16_t K[kC * DK];
   union {
-    uint16_t Q[kC * DK];                   // until the Gram fragments are done
+    uint16_t K[kC * DK];                   // until the Gram fragments are done
     struct {
       alignas(16) float Td[4][16][20];     // (I + Ld)^-1 diag(beta)
       float W[2][16][17];                  // Aoff T'_{2I}
@@ -172,9 +171,9 @@ struct PrepSmem {
 // transposed so that the MFMA output already sits in A-operand order: lane (g,n)
 // ends with entries (t = 16mt + n, j = 32s + 16h + 4g + i) for half h, i = 0..3.
 template <int DK, bool kQK>
-HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g, int n, int lane) {
+HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g, int n, int lane,
+                              const u16x8 (&qrow)[DK / 32]) {
   using SM = PrepSmem<DK>;
-  const uint16_t* rowsT = kQK ? sm.Q : sm.K;
   float val[2][4];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -184,7 +183,9 @@ HAM_DEVICE void gram_fragment(PrepSmem<DK>& sm, char* rec, int mt, int s, int g,
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[SM::at(16 * jt + n, 4 * ks + g)]));
-        const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&rowsT[SM::at(16 * mt + n, 4 * ks + g)]));
+        // K K^T reads row 16 mt + n of K from LDS; Q K^T takes that row of Q from registers
+        const bf16x8 bf = kQK ? __builtin_bit_cast(bf16x8, qrow[ks])
+                              : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&sm.K[SM::at(16 * mt + n, 4 * ks + g)]));
         acc = mfma_bf16(af, bf, acc);
       }
     }
@@ -254,23 +255,39 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
   // thread is issued before the first LDS store, so the tile costs one memory latency
   constexpr int NU = kC * (DK / 8) / 256;
   static_assert(kC * (DK / 8) % 256 == 0, "staging units must split evenly over the threads");
-  u16x8 kx[NU], qx[NU];
+  u16x8 kx[NU];
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int u = tid + 256 * i, row = u % kC, cu = (u / kC) * 8;
     kx[i] = (u16x8)(0);
-    qx[i] = (u16x8)(0);
     if (row < nvalid) {
       const size_t off = (tok0 + (size_t)row * a.H) * DK + cu;
       kx[i] = *reinterpret_cast<const u16x8*>(kp + off);
-      if (readout) qx[i] = *reinterpret_cast<const u16x8*>(qp + off);
+    }
+  }
+  // The Q K^T fragments this wave computes (fragments f = wave + 4 rep with f >= 6 of
+  // the twelve below) take their Q rows straight from memory into registers, in the
+  // B-operand order of the products: lane (g, n) holds row 16 mt + n, d = 32 ks + 8g ..
+  // +7.  Q never goes through LDS, and the block-inverse scratch reuses K's space, so a
+  // workgroup needs about 23 KiB and five share a CU.
+  constexpr int KSD = DK / 32;
+  auto frag_mt = [](int pi) { return pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3; };
+  u16x8 qrow[2][KSD];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int f = wave + 4 * (rr + 1);
+    const int row = 16 * frag_mt(f % 6) + n;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      qrow[rr][ks] = (u16x8)(0);
+      if (readout && f >= 6 && row < nvalid)
+        qrow[rr][ks] = *reinterpret_cast<const u16x8*>(qp + (tok0 + (size_t)row * a.H) * DK + 32 * ks + 8 * g);
     }
   }
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int u = tid + 256 * i, row = u % kC, cu = (u / kC) * 8;
     *reinterpret_cast<u16x8*>(&sm.K[SM::at(row, cu >> 3)]) = kx[i];
-    *reinterpret_cast<u16x8*>(&sm.Q[SM::at(row, cu >> 3)]) = qx[i];
   }
   if (wave == 0) {
     float gv = 0.f, bv = 0.f;
@@ -301,8 +318,8 @@ __global__ __launch_bounds__(256) void rnn_prep_kernel(RnnArgs a) {
     const int pi = f % 6;
     const int mt = pi == 0 ? 0 : pi == 1 ? 1 : pi < 4 ? 2 : 3;
     const int s = pi < 2 ? 0 : (pi - 2) & 1;
-    if (f < 6) gram_fragment<DK, false>(sm, rec, mt, s, g, n, lane);
-    else gram_fragment<DK, true>(sm, rec, mt, s, g, n, lane);
+    if (f < 6) gram_fragment<DK, false>(sm, rec, mt, s, g, n, lane, qrow[0]);
+    else gram_fragment<DK, true>(sm, rec, mt, s, g, n, lane, qrow[rep == 1 ? 0 : 1]);
   }
   __syncthreads();
 
